@@ -1,0 +1,217 @@
+/*
+ * pmqa.h -- C ABI of libpmqa, paged FP8 MQA logits and threshold Top-k select
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (definitions on the pages cited per entry point):
+ *   pmqa_mqa_logits           logits[b*next_n+t, p] =
+ *                               s_p * sum_h w[b*next_n+t, h] * relu(q[b,t,h,:] . k_p)
+ *   pmqa_indexer_topk         one-pass threshold select over a logits matrix,
+ *                             with last-CTA radix-select repair and Top-k finalize
+ *   pmqa_fused_logits_select  both in one launch; no score matrix is written
+ *
+ * Conventions shared by every entry point:
+ *   - All buffer pointers are DEVICE pointers on the device that owns `stream`
+ *     (a hipStream_t; NULL is the null stream).  The caller owns every buffer:
+ *     the library never allocates, frees or synchronises the host, and each
+ *     call is one kernel launch on `stream` (so it can be captured in a HIP
+ *     graph).
+ *   - Rows: R = batch_size * next_n, row r = b*next_n + t pairs with q[b, t].
+ *     Row r sees KV positions 0 .. e_r - 1 with e_r = seq_lens[b] - next_n + t + 1
+ *     (at least 0): slot t = next_n-1 is the newest draft position and sees the
+ *     whole sequence (page "flashinfer.attn_scores", Note and Returns).
+ *   - Arguments the host can check are checked before anything is launched and
+ *     a status other than PMQA_OK is returned with nothing written.
+ *   - Device-content preconditions are the caller's: every seq_lens[b] at most
+ *     max_seq_len (max_context for the select calls), block table row b valid
+ *     for its first ceil(seq_lens[b]/block_size) entries with ids in
+ *     [0, num_blocks), counters zeroed, arrivals zeroed.  A violation is
+ *     undefined behaviour (an out-of-bounds read or write), as on the pages
+ *     (fp8_paged_mqa_logits, block_tables and max_seq_len).  With the
+ *     environment variable PMQA_VALIDATE=1 the library copies those buffers to
+ *     the host and returns PMQA_ERR_CONTENT on a violation; that check
+ *     synchronises the stream and is skipped while the stream is capturing.
+ *   - Launch failures return PMQA_ERR_LAUNCH.
+ *   - v1 kernels support num_heads == 64, head_dim == 128, next_n in 1..4 and
+ *     block_size in {32, 64, 128}; other shapes return PMQA_ERR_UNSUPPORTED.
+ */
+#ifndef PMQA_H
+#define PMQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pmqa_status {
+  PMQA_OK = 0,
+  PMQA_ERR_NULL = 1,        /* a required pointer is NULL (or an optional one is given without its partner) */
+  PMQA_ERR_SHAPE = 2,       /* a size or count is out of range */
+  PMQA_ERR_STRIDE = 3,      /* a stride is negative, too small, or rows would overlap */
+  PMQA_ERR_UNSUPPORTED = 4, /* a shape the kernels are not built for */
+  PMQA_ERR_ALIGN = 5,       /* a pointer is not aligned as its entry point requires */
+  PMQA_ERR_OVERFLOW = 6,    /* an output offset would not fit the 32-bit range */
+  PMQA_ERR_LAUNCH = 7,      /* the HIP launch failed (no device, bad stream, ...) */
+  PMQA_ERR_CONTENT = 8      /* PMQA_VALIDATE=1 found a device-content precondition violated */
+} pmqa_status;
+
+/* Static string naming a status; never NULL. */
+const char* pmqa_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t pmqa_version(void);
+
+/* Minimum column count of a logits output buffer for max_seq_len: max_seq_len
+ * rounded up to a multiple of 256 (the kernels store whole 64-column groups up
+ * to round_up(seq_len, 64) and write those padding columns unconditionally).
+ * 8000 -> 8192 as in the Example of page "flashinfer.attn_scores".  Returns -1
+ * for a negative argument. */
+int32_t pmqa_padded_seq_len(int32_t max_seq_len);
+
+/* Minimum block-table width for a sequence length: ceil(seq_len / block_size)
+ * (page "flashinfer.attn_scores", block_tables; 8000, 32 -> 250).  Returns -1
+ * for a negative seq_len or a non-positive block_size. */
+int32_t pmqa_min_block_table_width(int32_t seq_len, int32_t block_size);
+
+/*
+ * pmqa_mqa_logits -- FP8 paged MQA logits (page "flashinfer.attn_scores",
+ * fp8_paged_mqa_logits: the formula and its parameters).
+ *
+ *   q            [batch_size, next_n, num_heads, head_dim] e4m3fn bytes,
+ *                contiguous, 16-byte aligned.
+ *   kv_fused     [num_blocks, block_size*(head_dim+4)] bytes, 16-byte aligned.
+ *                Block j: bytes [0, block_size*head_dim) hold the e4m3 values
+ *                token-major (token i at i*head_dim); bytes
+ *                [block_size*head_dim, end) hold block_size little-endian f32
+ *                per-token scales (token i's at block_size*head_dim + 4*i).
+ *   weights      [batch_size*next_n, num_heads] f32, contiguous, 16-byte aligned.
+ *   block_tables int32, row b at block_tables + b*block_table_stride, entries
+ *                contiguous; block_table_stride >= 0 is free (a row-strided view
+ *                is fine).  block_table_width is the number of columns (used by
+ *                PMQA_VALIDATE only; the kernel never reads row b past
+ *                ceil(seq_lens[b]/block_size) entries).
+ *   seq_lens     int32 at seq_lens + b*seq_lens_stride (any stride >= 0).
+ *   max_seq_len  >= every seq_lens[b]; sizes the output rows.
+ *   out          f32, row r at out + r*out_stride, out_stride >=
+ *                pmqa_padded_seq_len(max_seq_len), 4-byte aligned, and
+ *                R*out_stride < 2^31.  Row r is written for columns
+ *                [0, round_up(seq_lens[b], 64)) of every request with
+ *                seq_lens[b] > 0; columns at or past e_r hold unspecified values
+ *                (no mask is applied) and rows of requests with seq_lens[b] == 0
+ *                are never written.
+ */
+pmqa_status pmqa_check_logits_args(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_seq_len,
+    const float* out, int64_t out_stride);
+
+pmqa_status pmqa_mqa_logits(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_seq_len,
+    float* out, int64_t out_stride, void* stream);
+
+/*
+ * Select arguments shared by pmqa_indexer_topk and pmqa_fused_logits_select
+ * (page "flashinfer.sdsa.indexer_threshold_select", the description and the
+ * parameters thresholds, counters, candidates, max_context, top_k, arrivals,
+ * ranges).  A query tile is one request: its next_n rows.
+ *
+ *   max_context  the most keys a row sees (>= every seq_lens[b]); sizes the grid.
+ *   thresholds   [R] f32, in/out.  A key p < e_r of row r scoring above
+ *                thresholds[r] is a candidate; one scoring neither above nor
+ *                below it (equal, or NaN) is a tie.  A repaired row gets its new
+ *                threshold: its min(e_r, top_k)-th largest score.
+ *   counters     [R, 2] int32, zeroed by the caller, 8-byte aligned: the row's
+ *                candidate and tie counts (all of them, also past the slots).
+ *   candidates   [R, top_k + capacity, 2] int32, 8-byte aligned, output.  The
+ *                n-th candidate goes to slot top_k + n if n < capacity, the n-th
+ *                tie to slot top_k - 1 - n if n < top_k; each slot holds (key
+ *                index, score bits).  Slot order within a class is unspecified.
+ *                Stored score bits: for a candidate s - t when t > 0 and s <= 2t
+ *                (exact, and order-keeping), else s; for a tie s - t.
+ *   capacity     >= 0 candidate slots per row.
+ *   top_k        >= 1; also the number of tie slots.
+ *   arrivals     [batch_size] int32 or NULL.  Zeroed once by the caller and left
+ *                zeroed by every call.  With arrivals, the last CTA of each tile
+ *                re-selects every row that does not fit (n_cand > capacity or
+ *                n_cand + min(n_tie, top_k) < min(e_r, top_k)) at its
+ *                radix-selected min(e_r, top_k)-th largest score; with
+ *                capacity >= top_k - 1 every row then fits.  Without arrivals no
+ *                repair runs and ranges/topk_idx must be NULL.
+ *   ranges       [2, R] int32, required with arrivals, output: slots
+ *                [ranges[0][r], ranges[1][r]) hold the row's ties and candidates
+ *                (ranges[0][r] = top_k - min(n_tie, top_k),
+ *                 ranges[1][r] = top_k + min(n_cand, capacity)).
+ *   topk_idx     [R, top_k] int32 or NULL (needs arrivals and capacity >=
+ *                top_k - 1), output: the row's exact Top-min(e_r, top_k) key
+ *                indices in unspecified order, then -1 entries.  Among keys
+ *                scoring exactly the k-th largest score any may be chosen.
+ */
+pmqa_status pmqa_check_select_args(
+    const float* logits, int64_t logits_stride,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t max_context,
+    const float* thresholds, const int32_t* counters, const int32_t* candidates,
+    int32_t capacity, int32_t top_k,
+    const int32_t* arrivals, const int32_t* ranges, const int32_t* topk_idx);
+
+/*
+ * pmqa_indexer_topk -- the select over a logits matrix (row r at
+ * logits + r*logits_stride, 4-byte aligned, logits_stride >= max_context),
+ * e.g. the output of pmqa_mqa_logits.  Only columns p < e_r are read.  The
+ * repair re-reads the logits rows it repairs.
+ */
+pmqa_status pmqa_indexer_topk(
+    const float* logits, int64_t logits_stride,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t max_context,
+    float* thresholds, int32_t* counters, int32_t* candidates,
+    int32_t capacity, int32_t top_k,
+    int32_t* arrivals, int32_t* ranges, int32_t* topk_idx, void* stream);
+
+/*
+ * pmqa_fused_logits_select -- logits and select in one launch: each CTA scores
+ * its share of a request's keys exactly as pmqa_mqa_logits does (same
+ * arithmetic, bit for bit) and selects them without storing the scores; the
+ * repair recomputes the scores of the request it repairs.  Arguments as in
+ * pmqa_mqa_logits (minus out/out_stride/max_seq_len) and the select arguments
+ * above; block_table_width >= ceil(max_context / block_size) ("the block table
+ * must cover it", page "flashinfer.sdsa.indexer_threshold_select",
+ * max_context).
+ */
+pmqa_status pmqa_check_fused_args(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_context,
+    const float* thresholds, const int32_t* counters, const int32_t* candidates,
+    int32_t capacity, int32_t top_k,
+    const int32_t* arrivals, const int32_t* ranges, const int32_t* topk_idx);
+
+pmqa_status pmqa_fused_logits_select(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_context,
+    float* thresholds, int32_t* counters, int32_t* candidates,
+    int32_t capacity, int32_t top_k,
+    int32_t* arrivals, int32_t* ranges, int32_t* topk_idx, void* stream);
+
+/* Keys scored per CTA by the logits/fused kernels and selected per CTA by the
+ * indexer_topk kernel (grid = batch_size x ceil(max_context / keys)). */
+int32_t pmqa_keys_per_cta(int32_t which /* 0 logits, 1 indexer_topk, 2 fused */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMQA_H */

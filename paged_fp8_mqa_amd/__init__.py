@@ -1,0 +1,155 @@
+"""Python binding of libpmqa: paged FP8 MQA logits and threshold Top-k select
+on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libpmqa.so (built in-tree by ``python -m paged_fp8_mqa_amd.build``).
+PyTorch supplies device memory and the current stream.  Loading fails loudly
+when the library has not been built; there is no fallback.
+
+Entry points mirror the C ABI in include/pmqa.h:
+  mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None)
+  indexer_topk(logits, seq_lens, next_n, max_context, thresholds, counters,
+               candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None)
+  fused_logits_select(q, kv_fused, weights, block_tables, seq_lens, max_context,
+               thresholds, counters, candidates, capacity, top_k,
+               arrivals=None, ranges=None, topk_idx=None)
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpmqa.so")
+
+STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_NULL", 2: "PMQA_ERR_SHAPE", 3: "PMQA_ERR_STRIDE",
+          4: "PMQA_ERR_UNSUPPORTED", 5: "PMQA_ERR_ALIGN", 6: "PMQA_ERR_OVERFLOW",
+          7: "PMQA_ERR_LAUNCH", 8: "PMQA_ERR_CONTENT"}
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+_PAGED = [_P, _P, _P, _P, _I64, _I32, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64]
+_SELECT_OUT = [_P, _P, _P, _I32, _I32, _P, _P, _P]
+SIGNATURES = {
+    "pmqa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "pmqa_version": ([], _I32),
+    "pmqa_padded_seq_len": ([_I32], _I32),
+    "pmqa_min_block_table_width": ([_I32, _I32], _I32),
+    "pmqa_keys_per_cta": ([_I32], _I32),
+    "pmqa_check_logits_args": (_PAGED + [_I32, _P, _I64], ctypes.c_int),
+    "pmqa_mqa_logits": (_PAGED + [_I32, _P, _I64, _P], ctypes.c_int),
+    "pmqa_check_select_args": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT, ctypes.c_int),
+    "pmqa_indexer_topk": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT + [_P], ctypes.c_int),
+    "pmqa_check_fused_args": (_PAGED + [_I32] + _SELECT_OUT, ctypes.c_int),
+    "pmqa_fused_logits_select": (_PAGED + [_I32] + _SELECT_OUT + [_P], ctypes.c_int),
+}
+
+_lib = None
+
+
+class PmqaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+def lib():
+    """The loaded libpmqa (ctypes.CDLL); raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libpmqa.so is not built ({LIB_PATH}); run python -m paged_fp8_mqa_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def padded_seq_len(max_seq_len: int) -> int:
+    return int(lib().pmqa_padded_seq_len(int(max_seq_len)))
+
+
+def min_block_table_width(seq_len: int, block_size: int) -> int:
+    return int(lib().pmqa_min_block_table_width(int(seq_len), int(block_size)))
+
+
+def keys_per_cta(which: str) -> int:
+    return int(lib().pmqa_keys_per_cta({"logits": 0, "indexer_topk": 1, "fused": 2}[which]))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, where):
+    if status != 0:
+        raise PmqaError(status, where)
+
+
+def _paged(q, kv_fused, weights, block_tables, seq_lens, block_size):
+    """Pointers and sizes of the paged inputs (pages' shapes accepted)."""
+    B, nn, H, D = q.shape
+    if kv_fused.dim() == 4:
+        bs = kv_fused.shape[1]
+    else:
+        if block_size is None:
+            raise ValueError("block_size is needed for a 2-D kv_fused")
+        bs = block_size
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be 2-D with contiguous rows")
+    if not q.is_contiguous() or not weights.is_contiguous() or not kv_fused.is_contiguous():
+        raise ValueError("q, weights and kv_fused must be contiguous")
+    return [_ptr(q), _ptr(kv_fused), _ptr(weights), _ptr(block_tables), block_tables.stride(0),
+            block_tables.shape[1], _ptr(seq_lens), seq_lens.stride(0), B, nn, H, D, bs,
+            kv_fused.shape[0]], B, nn
+
+
+def mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None, block_size=None,
+               stream=None):
+    """FP8 paged MQA logits; returns the [B*next_n, max_seq_len] view of `out`."""
+    import torch
+    args, B, nn = _paged(q, kv_fused, weights, block_tables, seq_lens, block_size)
+    if out is None:
+        out = torch.empty(B * nn, padded_seq_len(max_seq_len), dtype=torch.float32, device=q.device)
+    if out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    _check(lib().pmqa_mqa_logits(*args, int(max_seq_len), _ptr(out), out.stride(0), _stream(stream)),
+           "pmqa_mqa_logits")
+    return out[: B * nn, :max_seq_len]
+
+
+def _select_out(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx):
+    return [_ptr(thresholds), _ptr(counters), _ptr(candidates), int(capacity), int(top_k),
+            _ptr(arrivals), _ptr(ranges), _ptr(topk_idx)]
+
+
+def indexer_topk(logits, seq_lens, next_n, max_context, thresholds, counters, candidates, capacity, top_k,
+                 arrivals=None, ranges=None, topk_idx=None, stream=None):
+    """Threshold select over a logits matrix (rows contiguous)."""
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    B = seq_lens.shape[0]
+    _check(lib().pmqa_indexer_topk(_ptr(logits), logits.stride(0), _ptr(seq_lens), seq_lens.stride(0), B,
+                                   int(next_n), int(max_context),
+                                   *_select_out(thresholds, counters, candidates, capacity, top_k, arrivals,
+                                                ranges, topk_idx), _stream(stream)),
+           "pmqa_indexer_topk")
+
+
+def fused_logits_select(q, kv_fused, weights, block_tables, seq_lens, max_context, thresholds, counters,
+                        candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None,
+                        block_size=None, stream=None):
+    """Logits and select in one launch (no score matrix)."""
+    args, B, nn = _paged(q, kv_fused, weights, block_tables, seq_lens, block_size)
+    _check(lib().pmqa_fused_logits_select(*args, int(max_context),
+                                          *_select_out(thresholds, counters, candidates, capacity, top_k,
+                                                       arrivals, ranges, topk_idx), _stream(stream)),
+           "pmqa_fused_logits_select")

@@ -1,0 +1,789 @@
+// libpmqa device code and entry points: paged FP8 MQA logits, threshold Top-k
+// select with last-CTA radix-select repair, and the fused one-launch path, for
+// gfx950 (MI355X).
+//
+// What is computed (page "flashinfer.attn_scores", fp8_paged_mqa_logits):
+//   E[r, p] = s_p * sum_h w[r, h] * relu(q[b, t, h, :] . k_p),   r = b*next_n + t
+// and the select (page "flashinfer.sdsa.indexer_threshold_select"): keys above
+// a row's threshold are candidates, keys neither above nor below it are ties,
+// both counted and stored in the row's slots; the last CTA of a tile repairs
+// rows that do not fit at their radix-selected k-th largest score.
+//
+// Work layout.  A CTA is 4 waves and covers a contiguous chunk of one
+// request's key positions for all next_n rows.  A wave scores 64 keys at a time:
+// four 16-key column tiles of the 16x16x128 FP8 MFMA, with the 64 heads as four
+// 16-row tiles on the M axis and head_dim 128 as the MFMA's K.  Each lane loads
+// its own B operand -- 32 bytes of one key -- straight from the page, so one
+// wave's 64 lanes read one 2 KiB stretch of a page's value region per tile.
+// The C layout leaves 16 heads of one key in each lane, so the ReLU and the
+// weighted head sum run in-lane; a two-step reduce-scatter across the four lane
+// groups then leaves lane l holding the score of key p0 + l, which is
+// multiplied by that key's scale (region 2 of its page).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <vector>
+
+#include "pmqa_internal.h"
+
+namespace pmqa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroupKeys = 64;                  // keys a wave scores per step
+constexpr int kCtaStep = kGroupKeys * kWaves;   // keys a CTA advances per step
+constexpr int kRadixBins = 2048;                // 11-bit digits: 11 + 11 + 10
+
+struct PagedArgs {
+  const uint8_t* q;
+  const uint8_t* kv;
+  const float* w;
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* seq_lens;
+  int64_t sl_stride;
+  int32_t bs_shift;     // log2(block_size)
+  int32_t block_bytes;  // block_size * (head_dim + 4)
+  int32_t scale_off;    // block_size * head_dim: start of region 2
+};
+
+struct LogitsArgs {
+  const float* logits;
+  int64_t ld;
+  const int32_t* seq_lens;
+  int64_t sl_stride;
+};
+
+struct SelectArgs {
+  float* thresholds;
+  int32_t* counters;
+  int32_t* candidates;
+  int32_t* arrivals;
+  int32_t* ranges;
+  int32_t* topk_idx;
+  int32_t capacity;
+  int32_t top_k;
+  int32_t rows;
+};
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+__device__ __forceinline__ v8i load32(const uint8_t* p) {
+  const int4 lo = *reinterpret_cast<const int4*>(p);
+  const int4 hi = *reinterpret_cast<const int4*>(p + 16);
+  return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// One 16x16x128 e4m3 x e4m3 -> f32 MFMA from a zero accumulator.  Lane l holds
+// row/column l % 16 and 32 of the 128 K values (the same K values for A and B);
+// the result gives lane l rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+// x[j] is this lane's partial for column tile j; returns, in lane (g, n), the
+// sum over the four lane groups of tile g's partials for column n.
+__device__ __forceinline__ float reduce_scatter4(float x0, float x1, float x2, float x3, int g) {
+  const bool hi2 = (g & 2) != 0;
+  const float keep_a = hi2 ? x2 : x0, keep_b = hi2 ? x3 : x1;
+  const float send_a = hi2 ? x0 : x2, send_b = hi2 ? x1 : x3;
+  const float y0 = keep_a + __shfl_xor(send_a, 32);
+  const float y1 = keep_b + __shfl_xor(send_b, 32);
+  const bool hi1 = (g & 1) != 0;
+  const float keep = hi1 ? y1 : y0, send = hi1 ? y0 : y1;
+  return keep + __shfl_xor(send, 16);
+}
+
+// ---------------------------------------------------------------- score sources
+
+// Scores computed from the paged KV pool.
+template <int NT>
+struct KvSource {
+  struct Group {
+    v8i k[4];
+    float s;
+  };
+  v8i qa[NT][4];        // A operands: rows t, head tiles mt
+  float wt[NT][16];     // weight of head 16*mt + 4*g + i at [4*mt + i]
+  const uint8_t* kv;
+  const int32_t* bt_row;
+  int bs_shift, bs_mask, block_bytes, scale_off;
+  int lane, n, g;
+
+  __device__ __forceinline__ void init(const PagedArgs& a, int b) {
+    lane = lane_id();
+    n = lane & 15;
+    g = lane >> 4;
+    kv = a.kv;
+    bt_row = a.bt + static_cast<int64_t>(b) * a.bt_stride;
+    bs_shift = a.bs_shift;
+    bs_mask = (1 << a.bs_shift) - 1;
+    block_bytes = a.block_bytes;
+    scale_off = a.scale_off;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = static_cast<int64_t>(b) * NT + t;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        qa[t][mt] = load32(a.q + ((row * kHeads + 16 * mt + n) * kDim + 32 * g));
+        const float4 wv = *reinterpret_cast<const float4*>(a.w + row * kHeads + 16 * mt + 4 * g);
+        wt[t][4 * mt + 0] = wv.x;
+        wt[t][4 * mt + 1] = wv.y;
+        wt[t][4 * mt + 2] = wv.z;
+        wt[t][4 * mt + 3] = wv.w;
+      }
+    }
+  }
+
+  // Issue the loads of the 64 keys at p0 (a multiple of 64).  Column tiles at or
+  // past L are not read (their pages may not exist); partly valid tiles read
+  // only their own page.
+  __device__ __forceinline__ void load(Group& gr, int p0, int L) const {
+    // p0 is a multiple of 64: tiles 0,1 share one page and tiles 2,3 share one
+    // (the same page unless block_size == 32).
+    const int page_a = p0 < L ? bt_row[p0 >> bs_shift] : 0;
+    const int page_b = p0 + 32 < L ? bt_row[(p0 + 32) >> bs_shift] : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ps = p0 + 16 * j;
+      if (ps < L) {
+        const int page = j < 2 ? page_a : page_b;
+        gr.k[j] = load32(kv + static_cast<int64_t>(page) * block_bytes + ((ps & bs_mask) + n) * kDim + 32 * g);
+      } else {
+        gr.k[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+    const int mine = p0 + 16 * g;
+    const int page = g < 2 ? page_a : page_b;
+    gr.s = mine < L ? *reinterpret_cast<const float*>(kv + static_cast<int64_t>(page) * block_bytes + scale_off +
+                                                      ((p0 + lane) & bs_mask) * 4)
+                    : 0.f;
+  }
+
+  // E[t] = score of key p0 + lane for row t.  Fixed operation order, shared by
+  // every kernel, so the logits, fused and repair paths agree bit for bit.
+  __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
+    float part[NT][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float sum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const v4f acc = mfma_fp8(qa[t][mt], gr.k[j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum = __builtin_fmaf(fmaxf(acc[i], 0.f), wt[t][4 * mt + i], sum);
+        }
+        part[t][j] = sum;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) E[t] = reduce_scatter4(part[t][0], part[t][1], part[t][2], part[t][3], g) * gr.s;
+  }
+};
+
+// Scores read from a logits matrix (only columns below each row's end).
+template <int NT>
+struct LogitsSource {
+  struct Group {
+    float v[NT];
+  };
+  const float* rows;
+  int64_t ld;
+  int end[NT];
+  int lane;
+
+  __device__ __forceinline__ void init(const LogitsArgs& a, int b, const int (&e)[NT]) {
+    lane = lane_id();
+    ld = a.ld;
+    rows = a.logits + static_cast<int64_t>(b) * NT * a.ld;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) end[t] = e[t];
+  }
+  __device__ __forceinline__ void load(Group& gr, int p0, int /*L*/) const {
+    const int p = p0 + lane;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) gr.v[t] = p < end[t] ? rows[t * ld + p] : 0.f;
+  }
+  __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) E[t] = gr.v[t];
+  }
+};
+
+// Runs f(p0, E) over every 64-key group of [begin, end) assigned to this wave
+// (groups wave, wave + 4, ...), loading one group ahead.
+template <int NT, class Src, class F>
+__device__ __forceinline__ void sweep(const Src& src, int begin, int end, int L, F&& f) {
+  typename Src::Group cur, nxt;
+  int p0 = begin + kGroupKeys * wave_id();
+  if (p0 >= end) return;
+  src.load(cur, p0, L);
+  for (; p0 < end; p0 += kCtaStep) {
+    if (p0 + kCtaStep < end) src.load(nxt, p0 + kCtaStep, L);
+    float E[NT];
+    src.score(cur, E);
+    f(p0, E);
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------- select pieces
+
+// Stored score of a candidate: s - t where that is exact and order-keeping
+// (t > 0 and t < s <= 2t, Sterbenz), else s.  Ties store s - t.
+__device__ __forceinline__ float enc_cand(float s, float t) { return (t > 0.f && s <= 2.f * t) ? s - t : s; }
+__device__ __forceinline__ float dec_cand(float v, float t) { return (t > 0.f && v <= t) ? v + t : v; }
+
+// Order-preserving radix key: larger score -> larger key, -0 == +0, NaN -> 0.
+__device__ __forceinline__ uint32_t radix_key(float x) {
+  if (x != x) return 0u;
+  const uint32_t u = x == 0.f ? 0u : __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  if (k == 0u) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
+  *reinterpret_cast<int2*>(slot) = int2{idx, static_cast<int>(__float_as_uint(v))};
+}
+
+// Candidate / tie append of one wave's 64 keys for all rows, counting with one
+// ballot and one atomic per class per wave.  Counts go to `cnt` (global
+// counters or LDS counters of the repairing CTA).
+template <int NT, bool kLds>
+__device__ __forceinline__ void append(const SelectArgs& s, int b, int p0, const float (&E)[NT],
+                                       const float (&thr)[NT], const int (&end)[NT], int32_t* cnt,
+                                       uint32_t row_mask) {
+  const int lane = lane_id();
+  const int p = p0 + lane;
+  const int stride = s.top_k + s.capacity;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(row_mask & (1u << t))) continue;
+    const int r = b * NT + t;
+    const float e = E[t], th = thr[t];
+    const bool valid = p < end[t];
+    const bool cand = valid && (e > th);
+    const bool tie = valid && !(e > th) && !(e < th);
+    const uint64_t mc = __ballot(cand);
+    const uint64_t mt = __ballot(tie);
+    int32_t* row_slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
+    if (mc) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(cnt + 2 * t, __popcll(mc));
+      base = __shfl(base, 0);
+      const int k = base + lanes_below(mc);
+      if (cand && k < s.capacity) store_pair(row_slots + 2 * (s.top_k + k), p, enc_cand(e, th));
+    }
+    if (mt) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(cnt + 2 * t + 1, __popcll(mt));
+      base = __shfl(base, 0);
+      const int k = base + lanes_below(mt);
+      if (tie && k < s.top_k) store_pair(row_slots + 2 * (s.top_k - 1 - k), p, e - th);
+    }
+  }
+}
+
+// Shared memory of the CTA that finishes a tile.
+template <int NT>
+struct TileShared {
+  uint32_t hist[NT][kRadixBins];
+  uint32_t pfx[NT];
+  uint32_t krem[NT];
+  int32_t cnt[NT][2];
+  int32_t nc[NT];
+  int32_t nt[NT];
+  float thr[NT];
+  uint32_t repair_mask;
+  int32_t is_last;
+  int32_t pos[2];
+};
+
+// One wave finds the digit holding the krem-th largest entry of hist[0..nb) and
+// the rank left inside it.  The histogram's total is at least krem.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_t krem, uint32_t* digit,
+                                           uint32_t* rem) {
+  const int lane = lane_id();
+  const int per = nb / 64;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += hist[lane * per + i];
+  uint32_t incl = local;  // sum over lanes >= this lane
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(incl, off);
+    if (lane + off < 64) incl += y;
+  }
+  const uint32_t excl = incl - local;
+  if (excl < krem && krem <= incl) {
+    uint32_t acc = excl;
+    for (int i = per - 1; i >= 0; --i) {
+      const uint32_t h = hist[lane * per + i];
+      if (acc + h >= krem) {
+        *digit = static_cast<uint32_t>(lane * per + i);
+        *rem = krem - acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+}
+
+// Radix pass layout: 11 bits, 11 bits, 10 bits from the top of the key.
+__device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ int pass_bits(int pass) { return pass == 2 ? 10 : 11; }
+
+// Work of the last CTA of tile (request) b: fit test, repair of the rows that
+// do not fit, ranges, Top-k finalize, and the arrivals reset.
+template <int NT, class Src>
+__device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, const int (&end)[NT],
+                            const float (&thr_in)[NT], TileShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int stride = s.top_k + s.capacity;
+  if (tid == 0) sh.repair_mask = 0u;
+  __syncthreads();
+  if (tid < NT) {
+    const int r = b * NT + tid;
+    const int nc = __hip_atomic_load(s.counters + 2 * r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int nt = __hip_atomic_load(s.counters + 2 * r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int k = min(end[tid], s.top_k);
+    const bool fit = nc <= s.capacity && nc + min(nt, s.top_k) >= k;
+    sh.nc[tid] = nc;
+    sh.nt[tid] = nt;
+    sh.thr[tid] = thr_in[tid];
+    if (!fit) atomicOr(&sh.repair_mask, 1u << tid);
+  }
+  __syncthreads();
+  const uint32_t mask = sh.repair_mask;
+  if (mask) {
+    if (tid < NT) {
+      sh.pfx[tid] = 0u;
+      sh.krem[tid] = static_cast<uint32_t>(min(end[tid], s.top_k));
+    }
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass_shift(pass);
+      const int bits = pass_bits(pass);
+      for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.hist[0][0])[i] = 0u;
+      __syncthreads();
+      uint32_t pfx[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) pfx[t] = sh.pfx[t];
+      sweep<NT>(src, 0, L, L, [&](int p0, const float(&E)[NT]) {
+        const int p = p0 + lane;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (!(mask & (1u << t)) || p >= end[t]) continue;
+          const uint32_t key = radix_key(E[t]);
+          if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
+          atomicAdd(&sh.hist[t][(key >> shift) & ((1u << bits) - 1u)], 1u);
+        }
+      });
+      __syncthreads();
+      if (wave < NT && (mask & (1u << wave))) {
+        uint32_t d = 0, rem = 0;
+        find_digit(sh.hist[wave], 1 << bits, sh.krem[wave], &d, &rem);
+        // exactly one lane found the digit; lane 0 publishes after a wave-wide max
+        uint32_t dd = d, rr = rem;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          dd = max(dd, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dd), off)));
+          rr = max(rr, static_cast<uint32_t>(__shfl_xor(static_cast<int>(rr), off)));
+        }
+        if (lane == 0) {
+          sh.pfx[wave] = pass == 0 ? dd : ((sh.pfx[wave] << bits) | dd);
+          sh.krem[wave] = rr;
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < NT && (mask & (1u << tid))) {
+      const float t2 = key_to_float(sh.pfx[tid]);
+      sh.thr[tid] = t2;
+      s.thresholds[b * NT + tid] = t2;
+      sh.cnt[tid][0] = 0;
+      sh.cnt[tid][1] = 0;
+    }
+    __syncthreads();
+    float thr2[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) thr2[t] = sh.thr[t];
+    sweep<NT>(src, 0, L, L, [&](int p0, const float(&E)[NT]) {
+      append<NT, true>(s, b, p0, E, thr2, end, &sh.cnt[0][0], mask);
+    });
+    __syncthreads();
+    if (tid < NT && (mask & (1u << tid))) {
+      const int r = b * NT + tid;
+      s.counters[2 * r] = sh.cnt[tid][0];
+      s.counters[2 * r + 1] = sh.cnt[tid][1];
+      sh.nc[tid] = sh.cnt[tid][0];
+      sh.nt[tid] = sh.cnt[tid][1];
+    }
+    __syncthreads();
+  }
+  if (tid < NT) {
+    const int r = b * NT + tid;
+    s.ranges[r] = s.top_k - min(sh.nt[tid], s.top_k);
+    s.ranges[s.rows + r] = s.top_k + min(sh.nc[tid], s.capacity);
+  }
+  if (s.topk_idx) {
+    for (int t = 0; t < NT; ++t) {
+      const int r = b * NT + t;
+      const int k = min(end[t], s.top_k);
+      const int nc = sh.nc[t];
+      const int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
+      int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
+      for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
+      if (nc <= k) {
+        for (int i = tid; i < k; i += kThreads)
+          out[i] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
+        continue;
+      }
+      // More candidates than k: radix-select the k-th largest decoded score.
+      const float th = sh.thr[t];
+      if (tid == 0) {
+        sh.pfx[0] = 0u;
+        sh.krem[0] = static_cast<uint32_t>(k);
+        sh.pos[0] = 0;
+        sh.pos[1] = 0;
+      }
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass_shift(pass);
+        const int bits = pass_bits(pass);
+        for (int i = tid; i < kRadixBins; i += kThreads) sh.hist[0][i] = 0u;
+        __syncthreads();
+        const uint32_t pf = sh.pfx[0];
+        for (int i = tid; i < nc; i += kThreads) {
+          const uint32_t key = radix_key(dec_cand(__int_as_float(slots[2 * (s.top_k + i) + 1]), th));
+          if (pass > 0 && (key >> (shift + bits)) != pf) continue;
+          atomicAdd(&sh.hist[0][(key >> shift) & ((1u << bits) - 1u)], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+          uint32_t d = 0, rem = 0;
+          find_digit(sh.hist[0], 1 << bits, sh.krem[0], &d, &rem);
+          uint32_t dd = d, rr = rem;
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) {
+            dd = max(dd, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dd), off)));
+            rr = max(rr, static_cast<uint32_t>(__shfl_xor(static_cast<int>(rr), off)));
+          }
+          if (lane == 0) {
+            sh.pfx[0] = pass == 0 ? dd : ((sh.pfx[0] << bits) | dd);
+            sh.krem[0] = rr;
+          }
+        }
+        __syncthreads();
+      }
+      const uint32_t kstar = sh.pfx[0];
+      const int n_eq = static_cast<int>(sh.krem[0]);
+      const int n_gt = k - n_eq;
+      for (int i = tid; i < nc; i += kThreads) {
+        const uint32_t key = radix_key(dec_cand(__int_as_float(slots[2 * (s.top_k + i) + 1]), th));
+        if (key > kstar) {
+          out[atomicAdd(&sh.pos[0], 1)] = slots[2 * (s.top_k + i)];
+        } else if (key == kstar) {
+          const int e = atomicAdd(&sh.pos[1], 1);
+          if (e < n_eq) out[n_gt + e] = slots[2 * (s.top_k + i)];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) s.arrivals[b] = 0;
+}
+
+// Tile arrival: every thread releases its slot stores at agent scope, then one
+// thread counts the CTA in; the CTA that completes the count acquires and
+// finishes the tile.
+template <int NT>
+__device__ __forceinline__ bool arrive_last(const SelectArgs& s, int b, int expected, TileShared<NT>& sh) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(s.arrivals + b, 1);
+    sh.is_last = old == expected - 1;
+  }
+  __syncthreads();
+  if (!sh.is_last) return false;
+  __threadfence();
+  return true;
+}
+
+// ---------------------------------------------------------------- kernels
+
+template <int NT>
+__global__ void __launch_bounds__(kThreads) logits_kernel(PagedArgs a, float* out, int64_t ld) {
+  const int b = blockIdx.y;
+  const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+  const int c0 = blockIdx.x * kLogitsKeysPerCta;
+  if (c0 >= L) return;
+  const int cend = min(c0 + kLogitsKeysPerCta, L);
+  KvSource<NT> src;
+  src.init(a, b);
+  float* row0 = out + static_cast<int64_t>(b) * NT * ld;
+  const int lane = lane_id();
+  sweep<NT>(src, c0, cend, L, [&](int p0, const float(&E)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) row0[t * ld + p0 + lane] = E[t];
+  });
+}
+
+template <int NT>
+__global__ void __launch_bounds__(kThreads) fused_kernel(PagedArgs a, SelectArgs s) {
+  __shared__ TileShared<NT> sh;
+  const int b = blockIdx.y;
+  const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+  const int expected = L > 0 ? static_cast<int>(ceil_div(L, kFusedKeysPerCta)) : 1;
+  if (static_cast<int>(blockIdx.x) >= expected) return;
+  const int c0 = blockIdx.x * kFusedKeysPerCta;
+  const int cend = min(c0 + kFusedKeysPerCta, L);
+  float thr[NT];
+  int end[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    thr[t] = s.thresholds[b * NT + t];
+    end[t] = max(0, L - NT + t + 1);
+  }
+  KvSource<NT> src;
+  src.init(a, b);
+  sweep<NT>(src, c0, cend, L, [&](int p0, const float(&E)[NT]) {
+    append<NT, false>(s, b, p0, E, thr, end, s.counters + 2 * b * NT, (1u << NT) - 1u);
+  });
+  if (!s.arrivals) return;
+  if (!arrive_last<NT>(s, b, expected, sh)) return;
+  finish_tile<NT>(src, s, b, L, end, thr, sh);
+}
+
+template <int NT>
+__global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectArgs s) {
+  __shared__ TileShared<NT> sh;
+  const int b = blockIdx.y;
+  const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+  const int expected = L > 0 ? static_cast<int>(ceil_div(L, kSelectKeysPerCta)) : 1;
+  if (static_cast<int>(blockIdx.x) >= expected) return;
+  const int c0 = blockIdx.x * kSelectKeysPerCta;
+  const int cend = min(c0 + kSelectKeysPerCta, L);
+  float thr[NT];
+  int end[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    thr[t] = s.thresholds[b * NT + t];
+    end[t] = max(0, L - NT + t + 1);
+  }
+  LogitsSource<NT> src;
+  src.init(a, b, end);
+  sweep<NT>(src, c0, cend, L, [&](int p0, const float(&E)[NT]) {
+    append<NT, false>(s, b, p0, E, thr, end, s.counters + 2 * b * NT, (1u << NT) - 1u);
+  });
+  if (!s.arrivals) return;
+  if (!arrive_last<NT>(s, b, expected, sh)) return;
+  finish_tile<NT>(src, s, b, L, end, thr, sh);
+}
+
+// ---------------------------------------------------------------- host side
+
+namespace {
+
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+bool validate_enabled() {
+  const char* v = std::getenv("PMQA_VALIDATE");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+bool stream_capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return true;
+  return cs != hipStreamCaptureStatusNone;
+}
+
+template <class T>
+bool copy_span(std::vector<T>& host, const T* dev, int64_t count, hipStream_t st) {
+  host.resize(static_cast<size_t>(count));
+  if (count == 0) return true;
+  return hipMemcpyAsync(host.data(), dev, sizeof(T) * count, hipMemcpyDeviceToHost, st) == hipSuccess;
+}
+
+// PMQA_VALIDATE=1: device-content preconditions, checked on a host copy.
+pmqa_status validate_content(hipStream_t st, const int32_t* seq_lens, int64_t sl_stride, int32_t B,
+                             int32_t limit, const int32_t* bt, int64_t bt_stride, int32_t bt_width,
+                             int32_t bs, int64_t num_blocks, const int32_t* counters, int64_t rows,
+                             const int32_t* arrivals) {
+  if (!validate_enabled() || stream_capturing(st) || B == 0) return PMQA_OK;
+  std::vector<int32_t> L, T, C, A;
+  bool ok = copy_span(L, seq_lens, (B - 1) * sl_stride + 1, st);
+  if (bt) ok = ok && copy_span(T, bt, (B - 1) * bt_stride + bt_width, st);
+  if (counters) ok = ok && copy_span(C, counters, 2 * rows, st);
+  if (arrivals) ok = ok && copy_span(A, arrivals, static_cast<int64_t>(B), st);
+  if (!ok || hipStreamSynchronize(st) != hipSuccess) return PMQA_ERR_LAUNCH;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t len = L[static_cast<size_t>(b * sl_stride)];
+    if (len < 0 || len > limit) return PMQA_ERR_CONTENT;
+    if (!bt) continue;
+    const int64_t pages = ceil_div(len, bs);
+    if (pages > bt_width) return PMQA_ERR_CONTENT;
+    for (int64_t j = 0; j < pages; ++j) {
+      const int32_t id = T[static_cast<size_t>(b * bt_stride + j)];
+      if (id < 0 || id >= num_blocks) return PMQA_ERR_CONTENT;
+    }
+  }
+  for (int32_t v : C)
+    if (v != 0) return PMQA_ERR_CONTENT;
+  for (int32_t v : A)
+    if (v != 0) return PMQA_ERR_CONTENT;
+  return PMQA_OK;
+}
+
+PagedArgs paged_args(const uint8_t* q, const uint8_t* kv, const float* w, const int32_t* bt,
+                     int64_t bt_stride, const int32_t* sl, int64_t sl_stride, int32_t bs) {
+  PagedArgs a;
+  a.q = q;
+  a.kv = kv;
+  a.w = w;
+  a.bt = bt;
+  a.bt_stride = bt_stride;
+  a.seq_lens = sl;
+  a.sl_stride = sl_stride;
+  a.bs_shift = log2_exact(bs);
+  a.block_bytes = bs * (kDim + 4);
+  a.scale_off = bs * kDim;
+  return a;
+}
+
+SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int32_t top_k, int32_t* arr,
+                       int32_t* ranges, int32_t* topk, int32_t rows) {
+  SelectArgs s;
+  s.thresholds = thr;
+  s.counters = cnt;
+  s.candidates = cand;
+  s.arrivals = arr;
+  s.ranges = ranges;
+  s.topk_idx = topk;
+  s.capacity = cap;
+  s.top_k = top_k;
+  s.rows = rows;
+  return s;
+}
+
+pmqa_status launched() { return hipGetLastError() == hipSuccess ? PMQA_OK : PMQA_ERR_LAUNCH; }
+
+template <template <int> class K, class... Args>
+void launch_nt(int nt, dim3 grid, hipStream_t st, Args... args) {
+  switch (nt) {
+    case 1: hipLaunchKernelGGL(K<1>::fn, grid, dim3(kThreads), 0, st, args...); break;
+    case 2: hipLaunchKernelGGL(K<2>::fn, grid, dim3(kThreads), 0, st, args...); break;
+    case 3: hipLaunchKernelGGL(K<3>::fn, grid, dim3(kThreads), 0, st, args...); break;
+    default: hipLaunchKernelGGL(K<4>::fn, grid, dim3(kThreads), 0, st, args...); break;
+  }
+}
+
+template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT>; };
+template <int NT> struct FusedK { static constexpr auto fn = fused_kernel<NT>; };
+template <int NT> struct SelectK { static constexpr auto fn = select_kernel<NT>; };
+
+}  // namespace
+}  // namespace pmqa
+
+using namespace pmqa;
+
+extern "C" {
+
+pmqa_status pmqa_mqa_logits(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+                            const int32_t* block_tables, int64_t block_table_stride,
+                            int32_t block_table_width, const int32_t* seq_lens, int64_t seq_lens_stride,
+                            int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+                            int32_t block_size, int64_t num_blocks, int32_t max_seq_len, float* out,
+                            int64_t out_stride, void* stream) {
+  pmqa_status st = pmqa_check_logits_args(q, kv_fused, weights, block_tables, block_table_stride,
+                                          block_table_width, seq_lens, seq_lens_stride, batch_size, next_n,
+                                          num_heads, head_dim, block_size, num_blocks, max_seq_len, out,
+                                          out_stride);
+  if (st != PMQA_OK) return st;
+  if (batch_size > 65535) return PMQA_ERR_SHAPE;
+  const int64_t gx = ceil_div(max_seq_len, kLogitsKeysPerCta);
+  if (batch_size == 0 || gx == 0) return PMQA_OK;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_seq_len, block_tables,
+                        block_table_stride, block_table_width, block_size, num_blocks, nullptr, 0, nullptr);
+  if (st != PMQA_OK) return st;
+  const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
+                                 seq_lens_stride, block_size);
+  launch_nt<LogitsK>(next_n, dim3(static_cast<unsigned>(gx), batch_size), hs, a, out, out_stride);
+  return launched();
+}
+
+pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const int32_t* seq_lens,
+                              int64_t seq_lens_stride, int32_t batch_size, int32_t next_n, int32_t max_context,
+                              float* thresholds, int32_t* counters, int32_t* candidates, int32_t capacity,
+                              int32_t top_k, int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
+                              void* stream) {
+  pmqa_status st = pmqa_check_select_args(logits, logits_stride, seq_lens, seq_lens_stride, batch_size, next_n,
+                                          max_context, thresholds, counters, candidates, capacity, top_k,
+                                          arrivals, ranges, topk_idx);
+  if (st != PMQA_OK) return st;
+  if (batch_size > 65535) return PMQA_ERR_SHAPE;
+  if (batch_size == 0) return PMQA_OK;
+  const int64_t gx = std::max<int64_t>(1, ceil_div(max_context, kSelectKeysPerCta));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int64_t rows = static_cast<int64_t>(batch_size) * next_n;
+  st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_context, nullptr, 0, 0, 1, 0, counters,
+                        rows, arrivals);
+  if (st != PMQA_OK) return st;
+  LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride};
+  const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
+                                   static_cast<int32_t>(rows));
+  launch_nt<SelectK>(next_n, dim3(static_cast<unsigned>(gx), batch_size), hs, a, s);
+  return launched();
+}
+
+pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+                                     const int32_t* block_tables, int64_t block_table_stride,
+                                     int32_t block_table_width, const int32_t* seq_lens, int64_t seq_lens_stride,
+                                     int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+                                     int32_t block_size, int64_t num_blocks, int32_t max_context,
+                                     float* thresholds, int32_t* counters, int32_t* candidates, int32_t capacity,
+                                     int32_t top_k, int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
+                                     void* stream) {
+  pmqa_status st = pmqa_check_fused_args(q, kv_fused, weights, block_tables, block_table_stride,
+                                         block_table_width, seq_lens, seq_lens_stride, batch_size, next_n,
+                                         num_heads, head_dim, block_size, num_blocks, max_context, thresholds,
+                                         counters, candidates, capacity, top_k, arrivals, ranges, topk_idx);
+  if (st != PMQA_OK) return st;
+  if (batch_size > 65535) return PMQA_ERR_SHAPE;
+  if (batch_size == 0) return PMQA_OK;
+  const int64_t gx = std::max<int64_t>(1, ceil_div(max_context, kFusedKeysPerCta));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int64_t rows = static_cast<int64_t>(batch_size) * next_n;
+  st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_context, block_tables, block_table_stride,
+                        block_table_width, block_size, num_blocks, counters, rows, arrivals);
+  if (st != PMQA_OK) return st;
+  const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
+                                 seq_lens_stride, block_size);
+  const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
+                                   static_cast<int32_t>(rows));
+  launch_nt<FusedK>(next_n, dim3(static_cast<unsigned>(gx), batch_size), hs, a, s);
+  return launched();
+}
+
+}  // extern "C"

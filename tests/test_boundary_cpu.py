@@ -1,0 +1,138 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and every host-checkable argument error maps to its documented
+status without touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_fp8_mqa_amd as pm
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pmqa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pmqa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pm.lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pmqa.h but not exported"
+    assert set(names) == set(pm.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_helpers():
+    assert pm.padded_seq_len(8000) == 8192
+    assert pm.padded_seq_len(0) == 0 and pm.padded_seq_len(256) == 256 and pm.padded_seq_len(257) == 512
+    assert pm.min_block_table_width(8000, 32) == 250
+    assert pm.min_block_table_width(0, 64) == 0 and pm.min_block_table_width(65, 64) == 2
+    assert pm.lib().pmqa_padded_seq_len(-1) == -1 and pm.lib().pmqa_min_block_table_width(5, 0) == -1
+    assert pm.lib().pmqa_version() >= 10000
+    for s in range(9):
+        assert pm.lib().pmqa_status_string(s).startswith(b"PMQA")
+    assert pm.keys_per_cta("fused") > 0
+
+
+A = 0x10000   # a fake 64 KiB-aligned "device" address: the checks never dereference it
+
+
+def P(off=0):
+    return ctypes.c_void_p(A + off)
+
+
+def logits_args(**kw):
+    a = dict(q=P(), kv=P(), w=P(), bt=P(), bts=250, btw=250, sl=P(), sls=1, B=2, nn=3, H=64, D=128, bs=32,
+             nb=500, msl=8000, out=P(), outs=8192)
+    a.update(kw)
+    return [a["q"], a["kv"], a["w"], a["bt"], a["bts"], a["btw"], a["sl"], a["sls"], a["B"], a["nn"], a["H"],
+            a["D"], a["bs"], a["nb"], a["msl"], a["out"], a["outs"]]
+
+
+def select_args(**kw):
+    a = dict(lg=P(), lgs=8192, sl=P(), sls=1, B=2, nn=3, mc=8000, thr=P(), cnt=P(), cand=P(), cap=512, k=512,
+             arr=P(), rng=P(), topk=P())
+    a.update(kw)
+    return [a["lg"], a["lgs"], a["sl"], a["sls"], a["B"], a["nn"], a["mc"], a["thr"], a["cnt"], a["cand"],
+            a["cap"], a["k"], a["arr"], a["rng"], a["topk"]]
+
+
+def fused_args(**kw):
+    a = dict(q=P(), kv=P(), w=P(), bt=P(), bts=250, btw=250, sl=P(), sls=1, B=2, nn=3, H=64, D=128, bs=32,
+             nb=500, mc=8000, thr=P(), cnt=P(), cand=P(), cap=512, k=512, arr=P(), rng=P(), topk=P())
+    a.update(kw)
+    return [a["q"], a["kv"], a["w"], a["bt"], a["bts"], a["btw"], a["sl"], a["sls"], a["B"], a["nn"], a["H"],
+            a["D"], a["bs"], a["nb"], a["mc"], a["thr"], a["cnt"], a["cand"], a["cap"], a["k"], a["arr"],
+            a["rng"], a["topk"]]
+
+
+OK, NULL, SHAPE, STRIDE, UNSUP, ALIGN, OVERFLOW = 0, 1, 2, 3, 4, 5, 6
+
+LOGITS_CASES = [
+    ({}, OK),
+    ({"B": 0, "q": None, "out": None}, OK),
+    ({"q": None}, NULL), ({"kv": None}, NULL), ({"w": None}, NULL), ({"bt": None}, NULL),
+    ({"sl": None}, NULL), ({"out": None}, NULL),
+    ({"H": 32}, UNSUP), ({"D": 64}, UNSUP), ({"nn": 0}, UNSUP), ({"nn": 5}, UNSUP), ({"bs": 16}, UNSUP),
+    ({"bs": 256}, UNSUP),
+    ({"B": -1}, SHAPE), ({"nb": 0}, SHAPE), ({"msl": -1}, SHAPE), ({"btw": 0}, SHAPE),
+    ({"outs": 8000}, STRIDE), ({"bts": -1}, STRIDE), ({"sls": -2}, STRIDE),
+    ({"kv": P(8)}, ALIGN), ({"q": P(4)}, ALIGN), ({"w": P(4)}, ALIGN), ({"out": P(2)}, ALIGN),
+    ({"B": 40000, "nn": 4, "outs": 16384, "msl": 16384}, OVERFLOW),
+]
+
+
+@pytest.mark.parametrize("kw,want", LOGITS_CASES)
+def test_check_logits_args(kw, want):
+    assert pm.lib().pmqa_check_logits_args(*logits_args(**kw)) == want
+
+
+SELECT_CASES = [
+    ({}, OK),
+    ({"arr": None, "rng": None, "topk": None}, OK),
+    ({"topk": None}, OK),
+    ({"lg": None}, NULL), ({"thr": None}, NULL), ({"cnt": None}, NULL), ({"cand": None}, NULL),
+    ({"rng": None}, NULL), ({"arr": None}, NULL),
+    ({"nn": 0}, UNSUP), ({"nn": 5}, UNSUP),
+    ({"k": 0}, SHAPE), ({"cap": -1}, SHAPE), ({"cap": 100}, SHAPE), ({"mc": -1}, SHAPE), ({"B": -1}, SHAPE),
+    ({"lgs": 7999}, STRIDE), ({"sls": -1}, STRIDE),
+    ({"cnt": P(4)}, ALIGN), ({"cand": P(4)}, ALIGN), ({"thr": P(2)}, ALIGN),
+    ({"k": 2 ** 30, "cap": 2 ** 30}, OVERFLOW),
+    ({"B": 60000, "nn": 4, "lgs": 16384, "mc": 16384}, OVERFLOW),
+]
+
+
+@pytest.mark.parametrize("kw,want", SELECT_CASES)
+def test_check_select_args(kw, want):
+    assert pm.lib().pmqa_check_select_args(*select_args(**kw)) == want
+
+
+FUSED_CASES = [
+    ({}, OK),
+    ({"q": None}, NULL), ({"thr": None}, NULL), ({"rng": None}, NULL),
+    ({"arr": None, "rng": None, "topk": P()}, NULL),
+    ({"H": 128}, UNSUP), ({"bs": 48}, UNSUP),
+    ({"btw": 249}, SHAPE), ({"k": 0}, SHAPE), ({"cap": 10}, SHAPE),
+    ({"kv": P(4)}, ALIGN), ({"cnt": P(4)}, ALIGN),
+]
+
+
+@pytest.mark.parametrize("kw,want", FUSED_CASES)
+def test_check_fused_args(kw, want):
+    assert pm.lib().pmqa_check_fused_args(*fused_args(**kw)) == want
+
+
+def test_entry_points_reject_before_launch():
+    """Invalid arguments return their status from the entry points too, before
+    any device call (this container has no GPU)."""
+    lib = pm.lib()
+    assert lib.pmqa_mqa_logits(*logits_args(H=32), None) == UNSUP
+    assert lib.pmqa_indexer_topk(*select_args(k=0), None) == SHAPE
+    assert lib.pmqa_fused_logits_select(*fused_args(q=None), None) == NULL
+    # a zero batch is a no-op that needs no device either
+    assert lib.pmqa_fused_logits_select(*fused_args(B=0), None) == OK

@@ -1,0 +1,198 @@
+"""GPU parity of the select paths: pmqa_indexer_topk (exact, against the
+oracle's select on the same float32 scores), pmqa_fused_logits_select (against
+the float64 oracle within tau, and bit for bit against the unfused pair)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_fp8_mqa_amd as pm
+import workloads as W
+from gpu_util import dev, golden_thresholds, run_fused, run_logits, run_select, slot_sets
+from oracle.checker import check_row
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(wl, res, repair, scores32=None, scores64=None, tau=None, rows=None, capacity=None):
+    cap = wl.capacity if capacity is None else capacity
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    errs = []
+    for r in (range(wl.rows) if rows is None else rows):
+        errs += check_row(
+            r, e_r=int(ends[r]), top_k=wl.top_k, capacity=cap, threshold_in=res["thr_in"][r],
+            threshold_out=res["thr"][r], counters=res["counters"][r], cand_row=res["cand"][r],
+            rng=None if res["ranges"] is None else res["ranges"][:, r],
+            topk_row=None if res["topk"] is None else res["topk"][r], repair=repair,
+            scores32=None if scores32 is None else scores32[r],
+            scores64=None if scores64 is None else scores64[r], tau=0.0 if tau is None else float(tau[r]))
+    if res["arrivals"] is not None:
+        assert np.all(res["arrivals"] == 0), "arrivals not left zeroed"
+    assert not errs, "\n".join(errs[:20])
+
+
+def _synthetic_logits(seed, R, cols, ends, tie_frac=0.3):
+    """Seeded float32 scores with many exact repeats (ties), NaN past each row's end."""
+    g = np.random.default_rng(seed)
+    x = g.normal(size=(R, cols)).astype(np.float32) * 4
+    pool = g.normal(size=8).astype(np.float32) * 4
+    rep = g.random((R, cols)) < tie_frac
+    x[rep] = pool[g.integers(0, 8, size=int(rep.sum()))]
+    for r in range(R):
+        x[r, ends[r]:] = np.nan
+    return x
+
+
+SEL_CASES = [
+    # seed, seq_lens, next_n, top_k, capacity, threshold mode
+    (1, [5000, 20, 0, 9000], 2, 64, 128, "sigma"),
+    (2, [5000, 20, 0, 9000], 2, 64, 63, "inf"),
+    (3, [3000, 8000], 3, 512, 1024, "low"),
+    (4, [100, 4096, 4097, 1], 4, 256, 255, "sigma"),
+    (5, [17000], 1, 2048, 4096, "mixed"),
+    (6, [300, 300, 300], 1, 1024, 2048, "low"),   # row_end < top_k
+]
+
+
+def _thresholds(mode, scores, ends, top_k, seed):
+    g = np.random.default_rng(seed)
+    thr = np.zeros(len(ends), np.float32)
+    for r, e in enumerate(ends):
+        if e == 0:
+            continue
+        s = np.sort(scores[r, :e])[::-1]
+        k = min(e, top_k)
+        m = mode if mode != "mixed" else ["sigma", "inf", "low", "high"][r % 4]
+        thr[r] = {"sigma": s[k - 1], "inf": np.inf, "low": -np.inf,
+                  "high": s[max(0, k // 8 - 1)]}[m] if m != "low" else s[-1] - 1
+    return thr
+
+
+@pytest.mark.parametrize("seed,seq_lens,next_n,top_k,cap,mode", SEL_CASES)
+def test_indexer_topk_exact(seed, seq_lens, next_n, top_k, cap, mode):
+    B = len(seq_lens)
+    R = B * next_n
+    ends = oracle.row_ends(np.array(seq_lens), next_n)
+    cols = max(max(seq_lens), 1)
+    x = _synthetic_logits(seed, R, cols + 7, ends)
+    thr = _thresholds(mode, x, ends, top_k, seed)
+    wl = W.Workload(name="syn", q=None, kv_fused=np.zeros((1, 1), np.uint8), weights=None, block_tables=None,
+                    seq_lens=np.array(seq_lens, np.int32), max_seq_len=cols, block_size=64, next_n=next_n,
+                    top_k=top_k, capacity=cap, threshold_recipe="", description="")
+    logits = torch.from_numpy(x).to("cuda")
+    res = run_select(wl, logits, thr)
+    _check(wl, res, True, scores32=x)
+    # without arrivals: a single pass, no repair
+    res2 = run_select(wl, logits, thr, arrivals=False)
+    _check(wl, res2, False, scores32=x)
+
+
+def _oracle_rows(wl, rows):
+    ref = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
+                                  wl.max_seq_len, rows=rows)
+    tau = oracle.row_tolerance(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
+                               rows=rows)
+    return ref, tau
+
+
+def _sigma_thresholds(ref, ends, top_k, mode):
+    thr = np.zeros(len(ends), np.float32)
+    for r, e in enumerate(ends):
+        if e == 0:
+            continue
+        k = min(int(e), top_k)
+        s = np.sort(ref[r, :e])[::-1]
+        thr[r] = np.float32(np.inf) if mode == "inf" else np.float32(s[k - 1])
+    return thr
+
+
+@pytest.mark.parametrize("cfg,mode", [(1, "inf"), (1, "sigma"), (2, "inf"), (2, "sigma")])
+def test_fused_small_configs_vs_oracle(cfg, mode):
+    wl = W.make(cfg)
+    ref, tau = _oracle_rows(wl, None)
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    thr = _sigma_thresholds(ref, ends, wl.top_k, mode)
+    d = dev(wl)
+    res = run_fused(wl, d, thr)
+    _check(wl, res, True, scores64=ref, tau=tau)
+
+
+FUSED_EDGE = [
+    (31, [1, 17, 64, 65, 200], 1, 32, 16, 32),
+    (32, [0, 2, 3, 130, 1000], 3, 64, 64, 63),
+    (33, [127, 128, 129, 0, 4096], 2, 128, 100, 200),
+    (34, [5, 63, 64, 2049, 3], 4, 64, 512, 511),
+    (35, [0, 0], 2, 64, 8, 8),
+]
+
+
+@pytest.mark.parametrize("seed,seq_lens,next_n,bs,top_k,cap", FUSED_EDGE)
+@pytest.mark.parametrize("mode", ["inf", "sigma"])
+def test_fused_edge_vs_oracle_and_unfused(seed, seq_lens, next_n, bs, top_k, cap, mode):
+    wl = W.small_random(seed, seq_lens, next_n, bs, top_k=top_k, capacity=cap)
+    ref, tau = _oracle_rows(wl, None)
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    thr = _sigma_thresholds(ref, ends, wl.top_k, mode)
+    d = dev(wl)
+    fused = run_fused(wl, d, thr)
+    _check(wl, fused, True, scores64=ref, tau=tau)
+    # the unfused pair on the same inputs gives the same bits
+    out, _ = run_logits(wl, d)
+    unf = run_select(wl, out, thr, max_context=wl.max_seq_len)
+    _same(wl, fused, unf)
+
+
+def _same(wl, a, b, capacity=None):
+    cap = wl.capacity if capacity is None else capacity
+    assert np.array_equal(a["thr"].view(np.int32), b["thr"].view(np.int32)), "thresholds differ"
+    assert np.array_equal(a["counters"], b["counters"]), "counters differ"
+    if a["ranges"] is not None:
+        assert np.array_equal(a["ranges"], b["ranges"]), "ranges differ"
+    for r in range(wl.rows):
+        ca, ta = slot_sets(a, r, wl.top_k, cap)
+        cb, tb = slot_sets(b, r, wl.top_k, cap)
+        if int(a["counters"][r, 0]) <= cap:
+            assert ca == cb, f"row {r}: candidate slots differ"
+        if int(a["counters"][r, 1]) <= wl.top_k:
+            assert ta == tb, f"row {r}: tie slots differ"
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_fused_large_configs(cfg):
+    wl = W.make(cfg)
+    gold, thr = golden_thresholds(cfg)
+    assert gold["fingerprint"] == W.fingerprint(wl), "input generator drifted from the golden thresholds"
+    d = dev(wl)
+    res = run_fused(wl, d, thr)
+    _check(wl, res, True)                               # contract on every row
+    rng = np.random.default_rng(cfg)
+    rows = sorted(set(rng.choice(wl.rows, size=2, replace=False).tolist()) | {0, wl.rows - 1})
+    rows = [r for r in rows if gold["row_ends"][r] > 0]
+    ref, tau = _oracle_rows(wl, rows)
+    _check(wl, res, True, scores64=ref, tau=tau, rows=rows)
+    if cfg == 5:
+        assert np.sum(res["thr"].view(np.int32) != thr.view(np.int32)) >= 7   # the too-high rows repaired
+        res2 = run_fused(wl, d, thr, capacity=wl.top_k - 1)
+        _check(wl, res2, True, capacity=wl.top_k - 1)
+        _check(wl, res2, True, scores64=ref, tau=tau, rows=rows, capacity=wl.top_k - 1)
+
+
+def test_fused_repeated_calls_reuse_arrivals():
+    wl = W.small_random(41, [3000, 5000], 2, 64, top_k=128, capacity=256)
+    ref, tau = _oracle_rows(wl, None)
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    thr = _sigma_thresholds(ref, ends, wl.top_k, "inf")
+    d = dev(wl)
+    import gpu_util
+    sb = gpu_util.SelectBuffers(wl.rows, wl.batch, wl.top_k, wl.capacity, thr)
+    first = None
+    for it in range(3):
+        sb.counters.zero_()
+        sb.thr.copy_(sb.thr_in)
+        pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], wl.max_seq_len, **sb.kwargs())
+        h = sb.host()
+        _check(wl, h, True, scores64=ref, tau=tau)
+        if first is None:
+            first = h
+        else:
+            _same(wl, first, h)
