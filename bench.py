@@ -1,0 +1,245 @@
+"""Benchmark of the paged FP8 MQA logits + threshold Top-k select hot path.
+
+One step = one pmqa_fused_logits_select launch over the whole batch of a
+synthetic workload (logits, candidate/tie select, last-CTA repair, ranges and
+exact Top-k finalize), with every input already resident in HBM.  Each step
+gets its own pre-zeroed counters and pristine thresholds (prepared before the
+timed region) and cycles through `--replicas` copies of the KV pool, so no
+step finds its pool in the 256 MiB Infinity Cache.
+
+Prints one JSON line:
+  value          pairs/s: sum over rows of visible KV positions, per second
+  rows_per_s     rows selected (and finalized) per second
+  roofline       the fused kernel's algorithmic HBM bytes per launch over its
+                 average launch time (HIP events on its stream) against 8 TB/s
+  cpu_baseline   the float64 CPU oracle on a bounded sample of the workload
+
+    python bench.py [--steps K] [--warmup W] [--workload 3|4|5] [--path fused|unfused]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_fp8_mqa_amd as pm  # noqa: E402
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "paged_fp8_mqa_amd", "csrc", "pmqa_device.hip")
+METRIC = "scored (row,KV position) pairs/sec and rows top-k selected/sec; % roofline"
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_thresholds(cfg, wl):
+    d = json.load(open(os.path.join(GOLDEN, f"thresholds_cfg{cfg}.json")))
+    if d["fingerprint"] != W.fingerprint(wl):
+        raise SystemExit(f"workload {wl.name} does not match its stored thresholds (generator drift)")
+    return np.array(d["threshold_bits"], dtype=np.int32).view(np.float32)
+
+
+def algorithmic_bytes(wl, path):
+    """HBM bytes one launch must move at least: every visible KV position's 132
+    bytes once per request, q and weights, the row thresholds/counters/ranges,
+    and (unfused) the logits write and read."""
+    kv = int(wl.seq_lens.astype(np.int64).sum()) * 132
+    qw = wl.q.size + wl.weights.size * 4
+    rows = wl.rows * (4 + 8 + 8)
+    pairs = int(wl.row_ends().sum())
+    extra = 8 * pairs if path == "unfused" else 0
+    return kv + qw + rows + extra
+
+
+def traffic_from_profiles(cfg, path):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    f = os.path.join(PROFILES, "fused_traffic.json")
+    if not os.path.exists(f):
+        return None
+    d = json.load(open(f))
+    e = d.get(f"cfg{cfg}_{path}")
+    if not e or e.get("kernel_src_sha") != kernel_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, thresholds, budget_s):
+    """The oracle (float64 scores, full-sort Top-k) on the first requests of the
+    workload, until about budget_s seconds of CPU work."""
+    import oracle
+    from oracle.select import select_with_repair
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    ends = wl.row_ends()
+    pairs = 0
+    rows = 0
+    reqs = 0
+    t0 = time.perf_counter()
+    for b in range(wl.batch):
+        L = int(wl.seq_lens[b])
+        if L == 0:
+            continue
+        k, s = oracle.gather_request(wl.kv_fused, wl.block_tables[b], L, wl.block_size, 128)
+        sc = oracle.request_scores(wl.q[b], k, s, wl.weights[b * wl.next_n:(b + 1) * wl.next_n])
+        for t in range(wl.next_n):
+            r = b * wl.next_n + t
+            e = int(ends[r])
+            select_with_repair(sc[t, :e].astype(np.float32), e, thresholds[r], wl.top_k, wl.capacity)
+            pairs += e
+            rows += 1
+        reqs += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": int(cores), "kind": "oracle",
+            "rows_per_s": rows / dt,
+            "sample": f"first {reqs} of {wl.batch} requests of {wl.name} ({pairs} pairs, {rows} rows) in {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[3, 4, 5])
+    ap.add_argument("--path", default="fused", choices=["fused", "unfused"])
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    pm.lib()
+
+    wl = W.make(args.workload)
+    thr0 = load_thresholds(args.workload, wl)
+    R, B = wl.rows, wl.batch
+    ends = wl.row_ends()
+    pairs = int(ends.sum())
+
+    q = torch.from_numpy(wl.q).to(dev)
+    w = torch.from_numpy(wl.weights).to(dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    kv_host = torch.from_numpy(wl.kv_fused)
+    kvs = [kv_host.to(dev).view(wl.num_blocks, wl.block_size, 1, 132) for _ in range(args.replicas)]
+    del kv_host
+
+    total = args.warmup + args.steps
+    thr_all = torch.from_numpy(np.tile(thr0, (total, 1))).to(dev)
+    cnt_all = torch.zeros(total, R, 2, dtype=torch.int32, device=dev)
+    cand = torch.empty(R, wl.top_k + wl.capacity, 2, dtype=torch.int32, device=dev)
+    arrivals = torch.zeros(B, dtype=torch.int32, device=dev)
+    ranges = torch.empty(2, R, dtype=torch.int32, device=dev)
+    topk = torch.empty(R, wl.top_k, dtype=torch.int32, device=dev)
+    logits = None
+    if args.path == "unfused":
+        logits = torch.empty(R, pm.padded_seq_len(wl.max_seq_len), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kv = kvs[i % len(kvs)]
+        if args.path == "fused":
+            pm.fused_logits_select(q, kv, w, bt, sl, wl.max_seq_len, thr_all[i], cnt_all[i], cand, wl.capacity,
+                                   wl.top_k, arrivals, ranges, topk)
+        else:
+            pm.mqa_logits(q, kv, w, bt, sl, wl.max_seq_len, out=logits)
+            pm.indexer_topk(logits, sl, wl.next_n, wl.max_seq_len, thr_all[i], cnt_all[i], cand, wl.capacity,
+                            wl.top_k, arrivals, ranges, topk)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for j in range(args.steps):
+        ev[j][0].record(stream)
+        step(args.warmup + j)
+        ev[j][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_step = ms_total / args.steps
+
+    assert int(arrivals.abs().sum()) == 0, "arrivals not left zeroed"
+    repaired = int((thr_all[-1].cpu().numpy().view(np.int32) != thr0.view(np.int32)).sum())
+
+    # one warm (same pool every step) measurement as context
+    warm = []
+    thr_dev = torch.from_numpy(thr0).to(dev)
+    for j in range(5):
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cnt_all[0].zero_()
+        thr_all[0].copy_(thr_dev)
+        a.record(stream)
+        step(0)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        warm.append(a.elapsed_time(b_))
+
+    alg = algorithmic_bytes(wl, args.path)
+    mean_launch_s = float(launch_ms.mean()) / 1e3
+    achieved = alg / mean_launch_s / 1e9
+    flops = 2.0 * 64 * 128 * pairs
+    out = {
+        "metric": METRIC,
+        "value": pairs / (ms_step / 1e3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp8_e4m3 -> f32",
+        "data": "synthetic (seeded generators, workloads/)",
+        "config": {"workload": wl.name, "path": args.path, "batch": B, "next_n": wl.next_n,
+                   "block_size": wl.block_size, "top_k": wl.top_k, "capacity": wl.capacity,
+                   "pairs": pairs, "rows": R, "kv_replicas": args.replicas, "parallelism": "single GPU"},
+        "rows_per_s": R / (ms_step / 1e3),
+        "repaired_rows": repaired,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(args.workload, args.path),
+                     "algorithmic_bytes_per_launch": alg,
+                     "launch_ms": {"mean": float(launch_ms.mean()), "p10": float(np.percentile(launch_ms, 10)),
+                                   "p50": float(np.percentile(launch_ms, 50)),
+                                   "p90": float(np.percentile(launch_ms, 90))},
+                     "mfma_frac": flops / mean_launch_s / 1e12 / FP8_PEAK_TFLOPS},
+        "warm_ms_per_step": float(np.median(warm)),
+        "kernel_src_sha": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, thr0, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

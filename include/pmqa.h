@@ -165,8 +165,9 @@ pmqa_status pmqa_check_select_args(
 /*
  * pmqa_indexer_topk -- the select over a logits matrix (row r at
  * logits + r*logits_stride, 4-byte aligned, logits_stride >= max_context),
- * e.g. the output of pmqa_mqa_logits.  Only columns p < e_r are read.  The
- * repair re-reads the logits rows it repairs.
+ * e.g. the output of pmqa_mqa_logits.  Columns p < seq_lens[b] of request b's
+ * rows may be read; only those below e_r are selected.  The repair re-reads the
+ * logits rows it repairs.
  */
 pmqa_status pmqa_indexer_topk(
     const float* logits, int64_t logits_stride,

@@ -26,6 +26,8 @@ def command(out=LIB):
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # keep packed-FP32 VALU instructions out of the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results in VGPRs, read by the epilogue without AGPR copies
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         "-o", out,
     ] + [os.path.join(CSRC, s) for s in SOURCES]

@@ -35,8 +35,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupKeys = 64;                  // keys a wave scores per step
-constexpr int kCtaStep = kGroupKeys * kWaves;   // keys a CTA advances per step
+constexpr int kChunk = kGroupKeys * kWaves * 4;  // keys a CTA scores per chunk
 constexpr int kRadixBins = 2048;                // 11-bit digits: 11 + 11 + 10
+constexpr int kFinalizeLds = 4096;              // candidate keys the finalize keeps in LDS
 
 struct PagedArgs {
   const uint8_t* q;
@@ -49,6 +50,8 @@ struct PagedArgs {
   int32_t bs_shift;     // log2(block_size)
   int32_t block_bytes;  // block_size * (head_dim + 4)
   int32_t scale_off;    // block_size * head_dim: start of region 2
+  int32_t batch;
+  int32_t locate;       // 1-D grid over live chunks (else a batch x chunks grid)
 };
 
 struct LogitsArgs {
@@ -56,6 +59,8 @@ struct LogitsArgs {
   int64_t ld;
   const int32_t* seq_lens;
   int64_t sl_stride;
+  int32_t batch;
+  int32_t locate;
 };
 
 struct SelectArgs {
@@ -91,6 +96,10 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
   const v4f z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
+
+// max(x, 0) as one integer max on the bit pattern: a float with the sign bit
+// set is a negative int32 and becomes +0; any other value passes unchanged.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // x[j] is this lane's partial for column tile j; returns, in lane (g, n), the
 // sum over the four lane groups of tile g's partials for column n.
@@ -146,29 +155,20 @@ struct KvSource {
     }
   }
 
-  // Issue the loads of the 64 keys at p0 (a multiple of 64).  Column tiles at or
-  // past L are not read (their pages may not exist); partly valid tiles read
-  // only their own page.
+  // Issue the loads of the 64 keys at p0 (a multiple of 64, below L).  A column
+  // tile at or past L re-reads slots of a page the request owns (values never
+  // used), so every load is unconditional and inside the pool: no block-table
+  // entry past ceil(L / block_size) is read.
   __device__ __forceinline__ void load(Group& gr, int p0, int L) const {
-    // p0 is a multiple of 64: tiles 0,1 share one page and tiles 2,3 share one
-    // (the same page unless block_size == 32).
-    const int page_a = p0 < L ? bt_row[p0 >> bs_shift] : 0;
-    const int page_b = p0 + 32 < L ? bt_row[(p0 + 32) >> bs_shift] : 0;
+    const int pb = (p0 + 32 < L) ? p0 + 32 : p0;
+    const uint8_t* base_a = kv + static_cast<int64_t>(bt_row[p0 >> bs_shift]) * block_bytes;
+    const uint8_t* base_b = kv + static_cast<int64_t>(bt_row[pb >> bs_shift]) * block_bytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ps = p0 + 16 * j;
-      if (ps < L) {
-        const int page = j < 2 ? page_a : page_b;
-        gr.k[j] = load32(kv + static_cast<int64_t>(page) * block_bytes + ((ps & bs_mask) + n) * kDim + 32 * g);
-      } else {
-        gr.k[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      gr.k[j] = load32((j < 2 ? base_a : base_b) + ((ps & bs_mask) + n) * kDim + 32 * g);
     }
-    const int mine = p0 + 16 * g;
-    const int page = g < 2 ? page_a : page_b;
-    gr.s = mine < L ? *reinterpret_cast<const float*>(kv + static_cast<int64_t>(page) * block_bytes + scale_off +
-                                                      ((p0 + lane) & bs_mask) * 4)
-                    : 0.f;
+    gr.s = *reinterpret_cast<const float*>((g < 2 ? base_a : base_b) + scale_off + ((p0 + lane) & bs_mask) * 4);
   }
 
   // E[t] = score of key p0 + lane for row t.  Fixed operation order, shared by
@@ -177,15 +177,20 @@ struct KvSource {
     float part[NT][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      // all of the tile's MFMAs first, into separate accumulators, so their
+      // latencies overlap; then the in-lane epilogue
+      v4f acc[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mfma_fp8(qa[t][mt], gr.k[j]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         float sum = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const v4f acc = mfma_fp8(qa[t][mt], gr.k[j]);
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sum = __builtin_fmaf(fmaxf(acc[i], 0.f), wt[t][4 * mt + i], sum);
-        }
+          for (int i = 0; i < 4; ++i) sum = __builtin_fmaf(relu(acc[t][mt][i]), wt[t][4 * mt + i], sum);
         part[t][j] = sum;
       }
     }
@@ -194,7 +199,8 @@ struct KvSource {
   }
 };
 
-// Scores read from a logits matrix (only columns below each row's end).
+// Scores read from a logits matrix.  Columns at or past L are clamped to L - 1
+// (read, never used); only columns below each row's end are selected.
 template <int NT>
 struct LogitsSource {
   struct Group {
@@ -202,20 +208,17 @@ struct LogitsSource {
   };
   const float* rows;
   int64_t ld;
-  int end[NT];
   int lane;
 
-  __device__ __forceinline__ void init(const LogitsArgs& a, int b, const int (&e)[NT]) {
+  __device__ __forceinline__ void init(const LogitsArgs& a, int b) {
     lane = lane_id();
     ld = a.ld;
     rows = a.logits + static_cast<int64_t>(b) * NT * a.ld;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) end[t] = e[t];
   }
-  __device__ __forceinline__ void load(Group& gr, int p0, int /*L*/) const {
-    const int p = p0 + lane;
+  __device__ __forceinline__ void load(Group& gr, int p0, int L) const {
+    const int p = min(p0 + lane, L - 1);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) gr.v[t] = p < end[t] ? rows[t * ld + p] : 0.f;
+    for (int t = 0; t < NT; ++t) gr.v[t] = rows[t * ld + p];
   }
   __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
 #pragma unroll
@@ -223,20 +226,46 @@ struct LogitsSource {
   }
 };
 
-// Runs f(p0, E) over every 64-key group of [begin, end) assigned to this wave
-// (groups wave, wave + 4, ...), loading one group ahead.
+// Scores one chunk [c0, cend) of at most kChunk keys (c0 < cend <= L): wave w
+// takes the groups at c0 + 64*(w + 4i), i = 0..3, double-buffered so the next
+// group's loads are in flight while the current one is scored.  f(p0, E) runs
+// for the groups below cend; the loads of a group past cend re-read the
+// chunk's first group.
 template <int NT, class Src, class F>
-__device__ __forceinline__ void sweep(const Src& src, int begin, int end, int L, F&& f) {
-  typename Src::Group cur, nxt;
-  int p0 = begin + kGroupKeys * wave_id();
-  if (p0 >= end) return;
-  src.load(cur, p0, L);
-  for (; p0 < end; p0 += kCtaStep) {
-    if (p0 + kCtaStep < end) src.load(nxt, p0 + kCtaStep, L);
+__device__ __forceinline__ void score_chunk(const Src& src, int c0, int cend, int L, F&& f) {
+  const int w = wave_id();
+  int p[4];
+  bool v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = c0 + kGroupKeys * (w + kWaves * i);
+    v[i] = q < cend;
+    p[i] = v[i] ? q : c0;
+  }
+  typename Src::Group ga, gb;
+  src.load(ga, p[0], L);
+  src.load(gb, p[1], L);
+  if (v[0]) {
     float E[NT];
-    src.score(cur, E);
-    f(p0, E);
-    cur = nxt;
+    src.score(ga, E);
+    f(p[0], E);
+  }
+  src.load(ga, p[2], L);
+  if (v[1]) {
+    float E[NT];
+    src.score(gb, E);
+    f(p[1], E);
+  }
+  src.load(gb, p[3], L);
+  if (v[2]) {
+    float E[NT];
+    src.score(ga, E);
+    f(p[2], E);
+  }
+  if (v[3]) {
+    float E[NT];
+    src.score(gb, E);
+    f(p[3], E);
   }
 }
 
@@ -258,52 +287,35 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// A slot store is an agent-scope (relaxed) atomic store: the L2 of the
+// storing XCD writes it through, so no dirty slot line is left in any XCD's L2.
+// The tile's last CTA (on any XCD) can then read the slots after its acquire,
+// and its own later stores to the same slots cannot be overwritten by a stale
+// write-back -- without the L2-wide write-back an agent-scope release fence
+// costs on every CTA.
 __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
-  *reinterpret_cast<int2*>(slot) = int2{idx, static_cast<int>(__float_as_uint(v))};
+  const uint64_t packed = (static_cast<uint64_t>(__float_as_uint(v)) << 32) | static_cast<uint32_t>(idx);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(slot), packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Candidate / tie append of one wave's 64 keys for all rows, counting with one
-// ballot and one atomic per class per wave.  Counts go to `cnt` (global
-// counters or LDS counters of the repairing CTA).
-template <int NT, bool kLds>
-__device__ __forceinline__ void append(const SelectArgs& s, int b, int p0, const float (&E)[NT],
-                                       const float (&thr)[NT], const int (&end)[NT], int32_t* cnt,
-                                       uint32_t row_mask) {
-  const int lane = lane_id();
-  const int p = p0 + lane;
-  const int stride = s.top_k + s.capacity;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (!(row_mask & (1u << t))) continue;
-    const int r = b * NT + t;
-    const float e = E[t], th = thr[t];
-    const bool valid = p < end[t];
-    const bool cand = valid && (e > th);
-    const bool tie = valid && !(e > th) && !(e < th);
-    const uint64_t mc = __ballot(cand);
-    const uint64_t mt = __ballot(tie);
-    int32_t* row_slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
-    if (mc) {
-      int base = 0;
-      if (lane == 0) base = atomicAdd(cnt + 2 * t, __popcll(mc));
-      base = __shfl(base, 0);
-      const int k = base + lanes_below(mc);
-      if (cand && k < s.capacity) store_pair(row_slots + 2 * (s.top_k + k), p, enc_cand(e, th));
-    }
-    if (mt) {
-      int base = 0;
-      if (lane == 0) base = atomicAdd(cnt + 2 * t + 1, __popcll(mt));
-      base = __shfl(base, 0);
-      const int k = base + lanes_below(mt);
-      if (tie && k < s.top_k) store_pair(row_slots + 2 * (s.top_k - 1 - k), p, e - th);
-    }
-  }
-}
+// s_waitcnt vmcnt(0): this wave's loads and stores have completed.
+__device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Shared memory of the CTA that finishes a tile.
+// Shared memory of a CTA.  The union's members are live in different phases:
+// the chunk's scores (main pass, repair append), the per-row radix histograms
+// (repair), and one row's candidate keys (finalize).
 template <int NT>
-struct TileShared {
-  uint32_t hist[NT][kRadixBins];
+struct CtaShared {
+  union {
+    float score[NT][kChunk];
+    uint32_t hist[NT][kRadixBins];
+    struct {
+      uint32_t hist[kRadixBins];
+      uint32_t key[kFinalizeLds];
+    } fin;
+  } u;
+  int32_t wcnt[NT][kWaves][2];
+  int32_t wbase[NT][kWaves][2];
   uint32_t pfx[NT];
   uint32_t krem[NT];
   int32_t cnt[NT][2];
@@ -315,8 +327,82 @@ struct TileShared {
   int32_t pos[2];
 };
 
+// Candidate / tie append of one scored chunk [c0, cend) held in sh.u.score, for
+// the rows in row_mask.  Each wave counts its 256 keys with ballots; one
+// thread per row adds the CTA's totals to cnt[2t], cnt[2t+1] (global counters,
+// or the LDS counters of a repairing CTA) with one atomic per class, and the
+// waves then store their slots at the returned base plus their prefix.
+template <int NT>
+__device__ void select_chunk(const SelectArgs& s, int b, int c0, int cend, const float (&thr)[NT],
+                             const int (&end)[NT], CtaShared<NT>& sh, int32_t* cnt, uint32_t row_mask) {
+  const int w = wave_id();
+  const int lane = lane_id();
+  const int tid = threadIdx.x;
+  const int stride = s.top_k + s.capacity;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(row_mask & (1u << t))) continue;
+    const int lim = min(cend, end[t]);
+    const float th = thr[t];
+    int nc = 0, ntie = 0;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = 256 * w + 64 * it + lane;
+      const float e = sh.u.score[t][i];
+      const bool valid = c0 + i < lim;
+      nc += __popcll(__ballot(valid && (e > th)));
+      ntie += __popcll(__ballot(valid && !(e > th) && !(e < th)));
+    }
+    if (lane == 0) {
+      sh.wcnt[t][w][0] = nc;
+      sh.wcnt[t][w][1] = ntie;
+    }
+  }
+  __syncthreads();
+  if (tid < NT && (row_mask & (1u << tid))) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      int tot = 0;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) tot += sh.wcnt[tid][q][c];
+      int base = tot ? atomicAdd(cnt + 2 * tid + c, tot) : 0;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) {
+        sh.wbase[tid][q][c] = base;
+        base += sh.wcnt[tid][q][c];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(row_mask & (1u << t))) continue;
+    const int lim = min(cend, end[t]);
+    const float th = thr[t];
+    int32_t* slots = s.candidates + static_cast<int64_t>(b * NT + t) * stride * 2;
+    int rc = sh.wbase[t][w][0], rt = sh.wbase[t][w][1];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = 256 * w + 64 * it + lane;
+      const float e = sh.u.score[t][i];
+      const bool valid = c0 + i < lim;
+      const bool cand = valid && (e > th);
+      const bool tie = valid && !(e > th) && !(e < th);
+      const uint64_t mc = __ballot(cand);
+      const uint64_t mt = __ballot(tie);
+      const int kc = rc + lanes_below(mc);
+      const int kt = rt + lanes_below(mt);
+      if (cand && kc < s.capacity) store_pair(slots + 2 * (s.top_k + kc), c0 + i, enc_cand(e, th));
+      if (tie && kt < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - kt), c0 + i, e - th);
+      rc += __popcll(mc);
+      rt += __popcll(mt);
+    }
+  }
+}
+
 // One wave finds the digit holding the krem-th largest entry of hist[0..nb) and
-// the rank left inside it.  The histogram's total is at least krem.
+// the rank left inside it, and returns both in every lane.  The histogram's
+// total is at least krem.
 __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_t krem, uint32_t* digit,
                                            uint32_t* rem) {
   const int lane = lane_id();
@@ -330,33 +416,110 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_
     if (lane + off < 64) incl += y;
   }
   const uint32_t excl = incl - local;
+  uint32_t d = 0, r = 0;
   if (excl < krem && krem <= incl) {
     uint32_t acc = excl;
     for (int i = per - 1; i >= 0; --i) {
       const uint32_t h = hist[lane * per + i];
       if (acc + h >= krem) {
-        *digit = static_cast<uint32_t>(lane * per + i);
-        *rem = krem - acc;
+        d = static_cast<uint32_t>(lane * per + i);
+        r = krem - acc;
         break;
       }
       acc += h;
     }
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    d = max(d, static_cast<uint32_t>(__shfl_xor(static_cast<int>(d), off)));
+    r = max(r, static_cast<uint32_t>(__shfl_xor(static_cast<int>(r), off)));
+  }
+  *digit = d;
+  *rem = r;
 }
 
 // Radix pass layout: 11 bits, 11 bits, 10 bits from the top of the key.
 __device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ int pass_bits(int pass) { return pass == 2 ? 10 : 11; }
 
+// Exact Top-k of one fitting row from its slots: every candidate when there are
+// at most k, topped up with ties from the tie slots; otherwise the k largest
+// candidates by decoded score, found by a 3-pass radix select over keys kept in
+// LDS (read from the slots once).  Entries past k are -1.
+template <int NT>
+__device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
+  int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
+  for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
+  if (nc <= k) {
+    for (int i = tid; i < k; i += kThreads)
+      out[i] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
+    return;
+  }
+  const bool in_lds = nc <= kFinalizeLds;
+  uint32_t* hist = sh.u.fin.hist;
+  uint32_t* keys = sh.u.fin.key;
+  const int32_t* cand = slots + 2 * s.top_k;
+  if (in_lds) {
+#pragma unroll 4
+    for (int i = tid; i < nc; i += kThreads) keys[i] = radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
+  }
+  if (tid == 0) {
+    sh.pfx[0] = 0u;
+    sh.krem[0] = static_cast<uint32_t>(k);
+    sh.pos[0] = 0;
+    sh.pos[1] = 0;
+  }
+  auto key_of = [&](int i) -> uint32_t {
+    return in_lds ? keys[i] : radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
+  };
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass_shift(pass);
+    const int bits = pass_bits(pass);
+    for (int i = tid; i < kRadixBins; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+    const uint32_t pf = sh.pfx[0];
+    for (int i = tid; i < nc; i += kThreads) {
+      const uint32_t key = key_of(i);
+      if (pass > 0 && (key >> (shift + bits)) != pf) continue;
+      atomicAdd(&hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
+    }
+    __syncthreads();
+    if (wave_id() == 0) {
+      uint32_t d = 0, rem = 0;
+      find_digit(hist, 1 << bits, sh.krem[0], &d, &rem);
+      if (lane == 0) {
+        sh.pfx[0] = pass == 0 ? d : ((sh.pfx[0] << bits) | d);
+        sh.krem[0] = rem;
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t kstar = sh.pfx[0];
+  const int n_eq = static_cast<int>(sh.krem[0]);
+  const int n_gt = k - n_eq;
+  for (int i = tid; i < nc; i += kThreads) {
+    const uint32_t key = key_of(i);
+    if (key > kstar) {
+      out[atomicAdd(&sh.pos[0], 1)] = cand[2 * i];
+    } else if (key == kstar) {
+      const int e = atomicAdd(&sh.pos[1], 1);
+      if (e < n_eq) out[n_gt + e] = cand[2 * i];
+    }
+  }
+  __syncthreads();
+}
+
 // Work of the last CTA of tile (request) b: fit test, repair of the rows that
 // do not fit, ranges, Top-k finalize, and the arrivals reset.
 template <int NT, class Src>
 __device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, const int (&end)[NT],
-                            const float (&thr_in)[NT], TileShared<NT>& sh) {
+                            const float (&thr_in)[NT], CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   const int wave = wave_id();
   const int lane = lane_id();
-  const int stride = s.top_k + s.capacity;
   if (tid == 0) sh.repair_mask = 0u;
   __syncthreads();
   if (tid < NT) {
@@ -373,6 +536,8 @@ __device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, c
   __syncthreads();
   const uint32_t mask = sh.repair_mask;
   if (mask) {
+    // k-th largest score of each repaired row: three radix passes, each a
+    // re-scoring sweep over the request with per-row LDS histograms.
     if (tid < NT) {
       sh.pfx[tid] = 0u;
       sh.krem[tid] = static_cast<uint32_t>(min(end[tid], s.top_k));
@@ -380,35 +545,30 @@ __device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, c
     for (int pass = 0; pass < 3; ++pass) {
       const int shift = pass_shift(pass);
       const int bits = pass_bits(pass);
-      for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.hist[0][0])[i] = 0u;
+      for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
       __syncthreads();
       uint32_t pfx[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) pfx[t] = sh.pfx[t];
-      sweep<NT>(src, 0, L, L, [&](int p0, const float(&E)[NT]) {
-        const int p = p0 + lane;
+      for (int c = 0; c < L; c += kChunk) {
+        score_chunk<NT>(src, c, min(c + kChunk, L), L, [&](int p0, const float(&E)[NT]) {
+          const int p = p0 + lane;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (!(mask & (1u << t)) || p >= end[t]) continue;
-          const uint32_t key = radix_key(E[t]);
-          if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
-          atomicAdd(&sh.hist[t][(key >> shift) & ((1u << bits) - 1u)], 1u);
-        }
-      });
+          for (int t = 0; t < NT; ++t) {
+            if (!(mask & (1u << t)) || p >= end[t]) continue;
+            const uint32_t key = radix_key(E[t]);
+            if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
+            atomicAdd(&sh.u.hist[t][(key >> shift) & ((1u << bits) - 1u)], 1u);
+          }
+        });
+      }
       __syncthreads();
       if (wave < NT && (mask & (1u << wave))) {
         uint32_t d = 0, rem = 0;
-        find_digit(sh.hist[wave], 1 << bits, sh.krem[wave], &d, &rem);
-        // exactly one lane found the digit; lane 0 publishes after a wave-wide max
-        uint32_t dd = d, rr = rem;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          dd = max(dd, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dd), off)));
-          rr = max(rr, static_cast<uint32_t>(__shfl_xor(static_cast<int>(rr), off)));
-        }
+        find_digit(sh.u.hist[wave], 1 << bits, sh.krem[wave], &d, &rem);
         if (lane == 0) {
-          sh.pfx[wave] = pass == 0 ? dd : ((sh.pfx[wave] << bits) | dd);
-          sh.krem[wave] = rr;
+          sh.pfx[wave] = pass == 0 ? d : ((sh.pfx[wave] << bits) | d);
+          sh.krem[wave] = rem;
         }
       }
       __syncthreads();
@@ -424,10 +584,17 @@ __device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, c
     float thr2[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) thr2[t] = sh.thr[t];
-    sweep<NT>(src, 0, L, L, [&](int p0, const float(&E)[NT]) {
-      append<NT, true>(s, b, p0, E, thr2, end, &sh.cnt[0][0], mask);
-    });
-    __syncthreads();
+    // select the repaired rows again at their new thresholds, counting in LDS
+    for (int c = 0; c < L; c += kChunk) {
+      const int cend = min(c + kChunk, L);
+      score_chunk<NT>(src, c, cend, L, [&](int p0, const float(&E)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
+      });
+      __syncthreads();
+      select_chunk<NT>(s, b, c, cend, thr2, end, sh, &sh.cnt[0][0], mask);
+      __syncthreads();
+    }
     if (tid < NT && (mask & (1u << tid))) {
       const int r = b * NT + tid;
       s.counters[2 * r] = sh.cnt[tid][0];
@@ -443,78 +610,18 @@ __device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, c
     s.ranges[s.rows + r] = s.top_k + min(sh.nc[tid], s.capacity);
   }
   if (s.topk_idx) {
-    for (int t = 0; t < NT; ++t) {
-      const int r = b * NT + t;
-      const int k = min(end[t], s.top_k);
-      const int nc = sh.nc[t];
-      const int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
-      int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
-      for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
-      if (nc <= k) {
-        for (int i = tid; i < k; i += kThreads)
-          out[i] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
-        continue;
-      }
-      // More candidates than k: radix-select the k-th largest decoded score.
-      const float th = sh.thr[t];
-      if (tid == 0) {
-        sh.pfx[0] = 0u;
-        sh.krem[0] = static_cast<uint32_t>(k);
-        sh.pos[0] = 0;
-        sh.pos[1] = 0;
-      }
-      for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass_shift(pass);
-        const int bits = pass_bits(pass);
-        for (int i = tid; i < kRadixBins; i += kThreads) sh.hist[0][i] = 0u;
-        __syncthreads();
-        const uint32_t pf = sh.pfx[0];
-        for (int i = tid; i < nc; i += kThreads) {
-          const uint32_t key = radix_key(dec_cand(__int_as_float(slots[2 * (s.top_k + i) + 1]), th));
-          if (pass > 0 && (key >> (shift + bits)) != pf) continue;
-          atomicAdd(&sh.hist[0][(key >> shift) & ((1u << bits) - 1u)], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) {
-          uint32_t d = 0, rem = 0;
-          find_digit(sh.hist[0], 1 << bits, sh.krem[0], &d, &rem);
-          uint32_t dd = d, rr = rem;
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) {
-            dd = max(dd, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dd), off)));
-            rr = max(rr, static_cast<uint32_t>(__shfl_xor(static_cast<int>(rr), off)));
-          }
-          if (lane == 0) {
-            sh.pfx[0] = pass == 0 ? dd : ((sh.pfx[0] << bits) | dd);
-            sh.krem[0] = rr;
-          }
-        }
-        __syncthreads();
-      }
-      const uint32_t kstar = sh.pfx[0];
-      const int n_eq = static_cast<int>(sh.krem[0]);
-      const int n_gt = k - n_eq;
-      for (int i = tid; i < nc; i += kThreads) {
-        const uint32_t key = radix_key(dec_cand(__int_as_float(slots[2 * (s.top_k + i) + 1]), th));
-        if (key > kstar) {
-          out[atomicAdd(&sh.pos[0], 1)] = slots[2 * (s.top_k + i)];
-        } else if (key == kstar) {
-          const int e = atomicAdd(&sh.pos[1], 1);
-          if (e < n_eq) out[n_gt + e] = slots[2 * (s.top_k + i)];
-        }
-      }
-      __syncthreads();
-    }
+    for (int t = 0; t < NT; ++t) finalize_topk<NT>(s, b * NT + t, min(end[t], s.top_k), sh.nc[t], sh.thr[t], sh);
   }
   if (tid == 0) s.arrivals[b] = 0;
 }
 
-// Tile arrival: every thread releases its slot stores at agent scope, then one
-// thread counts the CTA in; the CTA that completes the count acquires and
-// finishes the tile.
+// Tile arrival: each wave waits until its slot stores (agent-scope, written
+// through) and counter atomics have completed, then one thread counts the CTA
+// in; the CTA that completes the count acquires at agent scope and finishes
+// the tile.
 template <int NT>
-__device__ __forceinline__ bool arrive_last(const SelectArgs& s, int b, int expected, TileShared<NT>& sh) {
-  __threadfence();
+__device__ __forceinline__ bool arrive_last(const SelectArgs& s, int b, int expected, CtaShared<NT>& sh) {
+  wait_vm_done();
   __syncthreads();
   if (threadIdx.x == 0) {
     const int old = atomicAdd(s.arrivals + b, 1);
@@ -522,79 +629,136 @@ __device__ __forceinline__ bool arrive_last(const SelectArgs& s, int b, int expe
   }
   __syncthreads();
   if (!sh.is_last) return false;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return true;
+}
+
+// ---------------------------------------------------------------- work items
+
+// A CTA's work item: chunk c of request b (seq_len L, n chunks in all).
+struct Item {
+  int b, c, L, n;
+};
+
+// Launches with a 1-D grid number every request's chunks request-major, so all
+// CTAs past the last live chunk sit at the end of the dispatch order instead of
+// between live ones.  Each wave derives its item from a scan over
+// ceil(seq_lens[b] / keys_per_cta) (a request with seq_len 0 owns one item when
+// `empty_item` is set, so its tile still finishes).  Otherwise the grid is
+// chunks x batch and the item is (blockIdx.y, blockIdx.x).
+__device__ __forceinline__ bool find_item(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
+                                          int keys_per_cta, bool empty_item, Item& it) {
+  const int lane = lane_id();
+  auto chunks_of = [&](int L) { return L > 0 ? static_cast<int>(ceil_div(L, keys_per_cta)) : (empty_item ? 1 : 0); };
+  if (!locate) {
+    it.b = blockIdx.y;
+    it.c = blockIdx.x;
+    it.L = seq_lens[static_cast<int64_t>(it.b) * sl_stride];
+    it.n = chunks_of(it.L);
+    return it.c < it.n;
+  }
+  const int i = blockIdx.x;
+  int base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int b = b0 + lane;
+    const int L = b < batch ? seq_lens[static_cast<int64_t>(b) * sl_stride] : 0;
+    const int n = b < batch ? chunks_of(L) : 0;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int total = __shfl(incl, 63);
+    if (i < base + total) {
+      const uint64_t m = __ballot(base + incl > i);
+      const int l = __ffsll(static_cast<long long>(m)) - 1;
+      it.b = b0 + l;
+      it.L = __shfl(L, l);
+      it.n = __shfl(n, l);
+      it.c = i - base - (__shfl(incl, l) - it.n);
+      it.b = __builtin_amdgcn_readfirstlane(it.b);
+      it.L = __builtin_amdgcn_readfirstlane(it.L);
+      it.n = __builtin_amdgcn_readfirstlane(it.n);
+      it.c = __builtin_amdgcn_readfirstlane(it.c);
+      return true;
+    }
+    base += total;
+  }
+  return false;
 }
 
 // ---------------------------------------------------------------- kernels
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) logits_kernel(PagedArgs a, float* out, int64_t ld) {
-  const int b = blockIdx.y;
-  const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
-  const int c0 = blockIdx.x * kLogitsKeysPerCta;
-  if (c0 >= L) return;
+  Item it;
+  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kLogitsKeysPerCta, false, it)) return;
+  const int b = it.b;
+  const int L = it.L;
+  const int c0 = it.c * kLogitsKeysPerCta;
   const int cend = min(c0 + kLogitsKeysPerCta, L);
   KvSource<NT> src;
   src.init(a, b);
   float* row0 = out + static_cast<int64_t>(b) * NT * ld;
   const int lane = lane_id();
-  sweep<NT>(src, c0, cend, L, [&](int p0, const float(&E)[NT]) {
+  for (int c = c0; c < cend; c += kChunk) {
+    score_chunk<NT>(src, c, min(c + kChunk, cend), L, [&](int p0, const float(&E)[NT]) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) row0[t * ld + p0 + lane] = E[t];
-  });
+      for (int t = 0; t < NT; ++t) row0[t * ld + p0 + lane] = E[t];
+    });
+  }
+}
+
+// Main pass shared by the fused and the logits-select kernels: score this
+// CTA's chunk(s) into LDS and append them, then count the CTA in and, if it
+// is the tile's last, finish the tile.
+template <int NT, int kKeysPerCta, class Src>
+__device__ __forceinline__ void select_tile_part(const Src& src, const SelectArgs& s, int b, int L, int chunk,
+                                                 int expected, CtaShared<NT>& sh) {
+  const int c0 = chunk * kKeysPerCta;
+  const int cend = min(c0 + kKeysPerCta, L);
+  const int lane = lane_id();
+  float thr[NT];
+  int end[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    thr[t] = s.thresholds[b * NT + t];
+    end[t] = max(0, L - NT + t + 1);
+  }
+  for (int c = c0; c < cend; c += kChunk) {
+    const int ce = min(c + kChunk, cend);
+    score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
+    });
+    __syncthreads();
+    select_chunk<NT>(s, b, c, ce, thr, end, sh, s.counters + 2 * b * NT, (1u << NT) - 1u);
+    __syncthreads();
+  }
+  if (!s.arrivals) return;
+  if (!arrive_last<NT>(s, b, expected, sh)) return;
+  finish_tile<NT>(src, s, b, L, end, thr, sh);
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) fused_kernel(PagedArgs a, SelectArgs s) {
-  __shared__ TileShared<NT> sh;
-  const int b = blockIdx.y;
-  const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
-  const int expected = L > 0 ? static_cast<int>(ceil_div(L, kFusedKeysPerCta)) : 1;
-  if (static_cast<int>(blockIdx.x) >= expected) return;
-  const int c0 = blockIdx.x * kFusedKeysPerCta;
-  const int cend = min(c0 + kFusedKeysPerCta, L);
-  float thr[NT];
-  int end[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    thr[t] = s.thresholds[b * NT + t];
-    end[t] = max(0, L - NT + t + 1);
-  }
+  __shared__ CtaShared<NT> sh;
+  Item it;
+  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kFusedKeysPerCta, true, it)) return;
   KvSource<NT> src;
-  src.init(a, b);
-  sweep<NT>(src, c0, cend, L, [&](int p0, const float(&E)[NT]) {
-    append<NT, false>(s, b, p0, E, thr, end, s.counters + 2 * b * NT, (1u << NT) - 1u);
-  });
-  if (!s.arrivals) return;
-  if (!arrive_last<NT>(s, b, expected, sh)) return;
-  finish_tile<NT>(src, s, b, L, end, thr, sh);
+  src.init(a, it.b);
+  select_tile_part<NT, kFusedKeysPerCta>(src, s, it.b, it.L, it.c, it.n, sh);
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectArgs s) {
-  __shared__ TileShared<NT> sh;
-  const int b = blockIdx.y;
-  const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
-  const int expected = L > 0 ? static_cast<int>(ceil_div(L, kSelectKeysPerCta)) : 1;
-  if (static_cast<int>(blockIdx.x) >= expected) return;
-  const int c0 = blockIdx.x * kSelectKeysPerCta;
-  const int cend = min(c0 + kSelectKeysPerCta, L);
-  float thr[NT];
-  int end[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    thr[t] = s.thresholds[b * NT + t];
-    end[t] = max(0, L - NT + t + 1);
-  }
+  __shared__ CtaShared<NT> sh;
+  Item it;
+  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kSelectKeysPerCta, true, it)) return;
   LogitsSource<NT> src;
-  src.init(a, b, end);
-  sweep<NT>(src, c0, cend, L, [&](int p0, const float(&E)[NT]) {
-    append<NT, false>(s, b, p0, E, thr, end, s.counters + 2 * b * NT, (1u << NT) - 1u);
-  });
-  if (!s.arrivals) return;
-  if (!arrive_last<NT>(s, b, expected, sh)) return;
-  finish_tile<NT>(src, s, b, L, end, thr, sh);
+  src.init(a, it.b);
+  select_tile_part<NT, kSelectKeysPerCta>(src, s, it.b, it.L, it.c, it.n, sh);
 }
 
 // ---------------------------------------------------------------- host side
@@ -655,9 +819,20 @@ pmqa_status validate_content(hipStream_t st, const int32_t* seq_lens, int64_t sl
   return PMQA_OK;
 }
 
+// Batches up to this size use the 1-D located grid (each CTA scans the batch's
+// seq_lens once); larger ones use a chunks x batch grid.
+constexpr int kLocateMaxBatch = 1024;
+
+dim3 grid_for(int32_t batch, int64_t chunks_per_request, bool locate) {
+  return locate ? dim3(static_cast<unsigned>(chunks_per_request * batch), 1)
+                : dim3(static_cast<unsigned>(chunks_per_request), static_cast<unsigned>(batch));
+}
+
 PagedArgs paged_args(const uint8_t* q, const uint8_t* kv, const float* w, const int32_t* bt,
-                     int64_t bt_stride, const int32_t* sl, int64_t sl_stride, int32_t bs) {
+                     int64_t bt_stride, const int32_t* sl, int64_t sl_stride, int32_t bs, int32_t batch) {
   PagedArgs a;
+  a.batch = batch;
+  a.locate = batch <= kLocateMaxBatch;
   a.q = q;
   a.kv = kv;
   a.w = w;
@@ -728,8 +903,8 @@ pmqa_status pmqa_mqa_logits(const uint8_t* q, const uint8_t* kv_fused, const flo
                         block_table_stride, block_table_width, block_size, num_blocks, nullptr, 0, nullptr);
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
-                                 seq_lens_stride, block_size);
-  launch_nt<LogitsK>(next_n, dim3(static_cast<unsigned>(gx), batch_size), hs, a, out, out_stride);
+                                 seq_lens_stride, block_size, batch_size);
+  launch_nt<LogitsK>(next_n, grid_for(batch_size, gx, a.locate), hs, a, out, out_stride);
   return launched();
 }
 
@@ -750,10 +925,10 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
   st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_context, nullptr, 0, 0, 1, 0, counters,
                         rows, arrivals);
   if (st != PMQA_OK) return st;
-  LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride};
+  LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, batch_size <= kLocateMaxBatch};
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
                                    static_cast<int32_t>(rows));
-  launch_nt<SelectK>(next_n, dim3(static_cast<unsigned>(gx), batch_size), hs, a, s);
+  launch_nt<SelectK>(next_n, grid_for(batch_size, gx, a.locate), hs, a, s);
   return launched();
 }
 
@@ -779,10 +954,10 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
                         block_table_width, block_size, num_blocks, counters, rows, arrivals);
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
-                                 seq_lens_stride, block_size);
+                                 seq_lens_stride, block_size, batch_size);
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
                                    static_cast<int32_t>(rows));
-  launch_nt<FusedK>(next_n, dim3(static_cast<unsigned>(gx), batch_size), hs, a, s);
+  launch_nt<FusedK>(next_n, grid_for(batch_size, gx, a.locate), hs, a, s);
   return launched();
 }
 

@@ -88,6 +88,15 @@ EDGE = [
 ]
 
 
+def test_logits_large_batch_grid():
+    """More than 1024 requests: the batch x chunks grid instead of the located one."""
+    rng = np.random.default_rng(5)
+    seq = [int(x) for x in rng.integers(0, 300, size=1100)]
+    wl = W.small_random(18, seq, 2, 32, top_k=16, capacity=32)
+    out, _ = run_logits(wl, dev(wl))
+    _check_logits(wl, out, rows=list(range(0, wl.rows, 7)) + [wl.rows - 1])
+
+
 @pytest.mark.parametrize("seed,seq_lens,next_n,bs", EDGE)
 def test_logits_edge_cases(seed, seq_lens, next_n, bs):
     wl = W.small_random(seed, seq_lens, next_n, bs, top_k=16, capacity=32)

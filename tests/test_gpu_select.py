@@ -177,6 +177,23 @@ def test_fused_large_configs(cfg):
         _check(wl, res2, True, scores64=ref, tau=tau, rows=rows, capacity=wl.top_k - 1)
 
 
+def test_fused_large_batch_grid():
+    """More than 1024 requests (batch x chunks grid), fused against unfused bit for bit."""
+    rng = np.random.default_rng(6)
+    seq = [int(x) for x in rng.integers(0, 2000, size=1100)]
+    wl = W.small_random(42, seq, 1, 64, top_k=32, capacity=64)
+    thr = np.full(wl.rows, np.inf, np.float32)
+    d = dev(wl)
+    fused = run_fused(wl, d, thr)
+    _check(wl, fused, True)
+    out, _ = run_logits(wl, d)
+    unf = run_select(wl, out, thr, max_context=wl.max_seq_len)
+    _same(wl, fused, unf)
+    rows = [0, 1, 500, wl.rows - 1]
+    ref, tau = _oracle_rows(wl, rows)
+    _check(wl, fused, True, scores64=ref, tau=tau, rows=rows)
+
+
 def test_fused_repeated_calls_reuse_arrivals():
     wl = W.small_random(41, [3000, 5000], 2, 64, top_k=128, capacity=256)
     ref, tau = _oracle_rows(wl, None)
