@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (for HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -201,6 +203,17 @@ def main():
         b_.record(stream)
         torch.cuda.synchronize()
         warm.append(a.elapsed_time(b_))
+
+    if args.calib_copy_mib:
+        # a plain elementwise kernel that reads and writes exactly calib_copy_mib MiB
+        # (torch's same-dtype copy_ may go to a DMA engine instead of a kernel)
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     alg = algorithmic_bytes(wl, args.path)
     mean_launch_s = float(launch_ms.mean()) / 1e3
