@@ -154,6 +154,7 @@ def main():
     arrivals = torch.zeros(B, dtype=torch.int32, device=dev)
     ranges = torch.empty(2, R, dtype=torch.int32, device=dev)
     topk = torch.empty(R, wl.top_k, dtype=torch.int32, device=dev)
+    ws = pm.make_workspace(B, wl.next_n, dev)
     logits = None
     if args.path == "unfused":
         logits = torch.empty(R, pm.padded_seq_len(wl.max_seq_len), dtype=torch.float32, device=dev)
@@ -164,11 +165,11 @@ def main():
         kv = kvs[i % len(kvs)]
         if args.path == "fused":
             pm.fused_logits_select(q, kv, w, bt, sl, wl.max_seq_len, thr_all[i], cnt_all[i], cand, wl.capacity,
-                                   wl.top_k, arrivals, ranges, topk)
+                                   wl.top_k, arrivals, ranges, topk, workspace=ws)
         else:
             pm.mqa_logits(q, kv, w, bt, sl, wl.max_seq_len, out=logits)
             pm.indexer_topk(logits, sl, wl.next_n, wl.max_seq_len, thr_all[i], cnt_all[i], cand, wl.capacity,
-                            wl.top_k, arrivals, ranges, topk)
+                            wl.top_k, arrivals, ranges, topk, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -189,6 +190,7 @@ def main():
     ms_step = ms_total / args.steps
 
     assert int(arrivals.abs().sum()) == 0, "arrivals not left zeroed"
+    assert int((ws != 0).sum()) == 0, "workspace not left zeroed"
     repaired = int((thr_all[-1].cpu().numpy().view(np.int32) != thr0.view(np.int32)).sum())
 
     # one warm (same pool every step) measurement as context

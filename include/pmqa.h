@@ -153,14 +153,30 @@ pmqa_status pmqa_mqa_logits(
  *                top_k - 1), output: the row's exact Top-min(e_r, top_k) key
  *                indices in unspecified order, then -1 entries.  Among keys
  *                scoring exactly the k-th largest score any may be chosen.
+ *   workspace    pmqa_workspace_bytes(batch_size, next_n) bytes of device
+ *                memory, 8-byte aligned, required with arrivals (NULL
+ *                without), zeroed once by the caller and left zeroed by every
+ *                call.  It holds the repair: a tile's last CTA publishes a
+ *                job for its rows that do not fit (per-row radix histogram
+ *                passes, then a collect pass into a per-row bucket buffer, or
+ *                an exact re-select), and a second kernel, launched by the same
+ *                call on the same stream with as many CTAs as fit on the
+ *                device, splits every job into items of a few thousand keys
+ *                and runs them grid-wide.  Calls that share a workspace or
+ *                arrivals must not run concurrently.
  */
+
+/* Bytes of the repair workspace for batch_size requests of next_n rows. */
+size_t pmqa_workspace_bytes(int32_t batch_size, int32_t next_n);
+
 pmqa_status pmqa_check_select_args(
     const float* logits, int64_t logits_stride,
     const int32_t* seq_lens, int64_t seq_lens_stride,
     int32_t batch_size, int32_t next_n, int32_t max_context,
     const float* thresholds, const int32_t* counters, const int32_t* candidates,
     int32_t capacity, int32_t top_k,
-    const int32_t* arrivals, const int32_t* ranges, const int32_t* topk_idx);
+    const int32_t* arrivals, const int32_t* ranges, const int32_t* topk_idx,
+    const void* workspace, size_t workspace_bytes);
 
 /*
  * pmqa_indexer_topk -- the select over a logits matrix (row r at
@@ -175,7 +191,8 @@ pmqa_status pmqa_indexer_topk(
     int32_t batch_size, int32_t next_n, int32_t max_context,
     float* thresholds, int32_t* counters, int32_t* candidates,
     int32_t capacity, int32_t top_k,
-    int32_t* arrivals, int32_t* ranges, int32_t* topk_idx, void* stream);
+    int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pmqa_fused_logits_select -- logits and select in one launch: each CTA scores
@@ -195,7 +212,8 @@ pmqa_status pmqa_check_fused_args(
     int32_t block_size, int64_t num_blocks, int32_t max_context,
     const float* thresholds, const int32_t* counters, const int32_t* candidates,
     int32_t capacity, int32_t top_k,
-    const int32_t* arrivals, const int32_t* ranges, const int32_t* topk_idx);
+    const int32_t* arrivals, const int32_t* ranges, const int32_t* topk_idx,
+    const void* workspace, size_t workspace_bytes);
 
 pmqa_status pmqa_fused_logits_select(
     const uint8_t* q, const uint8_t* kv_fused, const float* weights,
@@ -205,10 +223,11 @@ pmqa_status pmqa_fused_logits_select(
     int32_t block_size, int64_t num_blocks, int32_t max_context,
     float* thresholds, int32_t* counters, int32_t* candidates,
     int32_t capacity, int32_t top_k,
-    int32_t* arrivals, int32_t* ranges, int32_t* topk_idx, void* stream);
+    int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Keys scored per CTA by the logits/fused kernels and selected per CTA by the
- * indexer_topk kernel (grid = batch_size x ceil(max_context / keys)). */
+ * indexer_topk kernel (at most batch_size x ceil(max_context / keys) CTAs). */
 int32_t pmqa_keys_per_cta(int32_t which /* 0 logits, 1 indexer_topk, 2 fused */);
 
 #ifdef __cplusplus

@@ -9,10 +9,12 @@ when the library has not been built; there is no fallback.
 Entry points mirror the C ABI in include/pmqa.h:
   mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None)
   indexer_topk(logits, seq_lens, next_n, max_context, thresholds, counters,
-               candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None)
+               candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None,
+               workspace=None)
   fused_logits_select(q, kv_fused, weights, block_tables, seq_lens, max_context,
                thresholds, counters, candidates, capacity, top_k,
-               arrivals=None, ranges=None, topk_idx=None)
+               arrivals=None, ranges=None, topk_idx=None, workspace=None)
+  make_workspace(batch_size, next_n)  -> zeroed repair workspace (required with arrivals)
 """
 import ctypes
 import os
@@ -26,15 +28,17 @@ STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_NULL", 2: "PMQA_ERR_SHAPE", 3: "PMQA_ERR_ST
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
 
 _PAGED = [_P, _P, _P, _P, _I64, _I32, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64]
-_SELECT_OUT = [_P, _P, _P, _I32, _I32, _P, _P, _P]
+_SELECT_OUT = [_P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ]
 SIGNATURES = {
     "pmqa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pmqa_version": ([], _I32),
     "pmqa_padded_seq_len": ([_I32], _I32),
     "pmqa_min_block_table_width": ([_I32, _I32], _I32),
     "pmqa_keys_per_cta": ([_I32], _I32),
+    "pmqa_workspace_bytes": ([_I32, _I32], _SZ),
     "pmqa_check_logits_args": (_PAGED + [_I32, _P, _I64], ctypes.c_int),
     "pmqa_mqa_logits": (_PAGED + [_I32, _P, _I64, _P], ctypes.c_int),
     "pmqa_check_select_args": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT, ctypes.c_int),
@@ -73,6 +77,16 @@ def padded_seq_len(max_seq_len: int) -> int:
 
 def min_block_table_width(seq_len: int, block_size: int) -> int:
     return int(lib().pmqa_min_block_table_width(int(seq_len), int(block_size)))
+
+
+def workspace_bytes(batch_size: int, next_n: int) -> int:
+    return int(lib().pmqa_workspace_bytes(int(batch_size), int(next_n)))
+
+
+def make_workspace(batch_size: int, next_n: int, device="cuda"):
+    """A zeroed repair workspace; calls leave it zeroed, so it can be reused."""
+    import torch
+    return torch.zeros(workspace_bytes(batch_size, next_n), dtype=torch.uint8, device=device)
 
 
 def keys_per_cta(which: str) -> int:
@@ -126,30 +140,33 @@ def mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=No
     return out[: B * nn, :max_seq_len]
 
 
-def _select_out(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx):
+def _select_out(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx, workspace):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return [_ptr(thresholds), _ptr(counters), _ptr(candidates), int(capacity), int(top_k),
-            _ptr(arrivals), _ptr(ranges), _ptr(topk_idx)]
+            _ptr(arrivals), _ptr(ranges), _ptr(topk_idx), _ptr(workspace), nbytes]
 
 
 def indexer_topk(logits, seq_lens, next_n, max_context, thresholds, counters, candidates, capacity, top_k,
-                 arrivals=None, ranges=None, topk_idx=None, stream=None):
-    """Threshold select over a logits matrix (rows contiguous)."""
+                 arrivals=None, ranges=None, topk_idx=None, workspace=None, stream=None):
+    """Threshold select over a logits matrix (rows contiguous).  With arrivals,
+    pass a workspace from make_workspace()."""
     if logits.stride(1) != 1:
         raise ValueError("logits rows must be contiguous")
     B = seq_lens.shape[0]
     _check(lib().pmqa_indexer_topk(_ptr(logits), logits.stride(0), _ptr(seq_lens), seq_lens.stride(0), B,
                                    int(next_n), int(max_context),
                                    *_select_out(thresholds, counters, candidates, capacity, top_k, arrivals,
-                                                ranges, topk_idx), _stream(stream)),
+                                                ranges, topk_idx, workspace), _stream(stream)),
            "pmqa_indexer_topk")
 
 
 def fused_logits_select(q, kv_fused, weights, block_tables, seq_lens, max_context, thresholds, counters,
                         candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None,
-                        block_size=None, stream=None):
-    """Logits and select in one launch (no score matrix)."""
+                        workspace=None, block_size=None, stream=None):
+    """Logits and select in one launch (no score matrix).  With arrivals, pass
+    a workspace from make_workspace()."""
     args, B, nn = _paged(q, kv_fused, weights, block_tables, seq_lens, block_size)
     _check(lib().pmqa_fused_logits_select(*args, int(max_context),
                                           *_select_out(thresholds, counters, candidates, capacity, top_k,
-                                                       arrivals, ranges, topk_idx), _stream(stream)),
+                                                       arrivals, ranges, topk_idx, workspace), _stream(stream)),
            "pmqa_fused_logits_select")

@@ -32,21 +32,26 @@ pmqa_status check_paged_inputs(const uint8_t* q, const uint8_t* kv_fused, const 
   return PMQA_OK;
 }
 
-pmqa_status check_select_outputs(int64_t rows, const float* thresholds, const int32_t* counters,
+pmqa_status check_select_outputs(int64_t batch, int64_t rows, const float* thresholds, const int32_t* counters,
                                  const int32_t* candidates, int32_t capacity, int32_t top_k,
                                  const int32_t* arrivals, const int32_t* ranges,
-                                 const int32_t* topk_idx) {
+                                 const int32_t* topk_idx, const void* workspace, size_t workspace_bytes) {
   if (top_k < 1 || capacity < 0) return PMQA_ERR_SHAPE;
   if (static_cast<int64_t>(top_k) + capacity > INT32_MAX / 2) return PMQA_ERR_OVERFLOW;
   if (rows == 0) return PMQA_OK;
   if (!thresholds || !counters || !candidates) return PMQA_ERR_NULL;
-  if (arrivals && !ranges) return PMQA_ERR_NULL;
+  if (arrivals && (!ranges || !workspace)) return PMQA_ERR_NULL;
   if (!arrivals && (ranges || topk_idx)) return PMQA_ERR_NULL;
   if (topk_idx && capacity < top_k - 1) return PMQA_ERR_SHAPE;
   if (!aligned(thresholds, 4) || !aligned(counters, 8) || !aligned(candidates, 8)) return PMQA_ERR_ALIGN;
   if ((arrivals && !aligned(arrivals, 4)) || (ranges && !aligned(ranges, 4)) ||
       (topk_idx && !aligned(topk_idx, 4)))
     return PMQA_ERR_ALIGN;
+  if (workspace) {
+    if (!arrivals) return PMQA_ERR_NULL;
+    if (!aligned(workspace, 8)) return PMQA_ERR_ALIGN;
+    if (static_cast<int64_t>(workspace_bytes) < 4 * workspace_words(batch, rows)) return PMQA_ERR_SHAPE;
+  }
   return PMQA_OK;
 }
 
@@ -80,6 +85,11 @@ int32_t pmqa_padded_seq_len(int32_t max_seq_len) {
 int32_t pmqa_min_block_table_width(int32_t seq_len, int32_t block_size) {
   if (seq_len < 0 || block_size <= 0) return -1;
   return static_cast<int32_t>(ceil_div(seq_len, block_size));
+}
+
+size_t pmqa_workspace_bytes(int32_t batch_size, int32_t next_n) {
+  if (batch_size < 0 || next_n < 1 || next_n > kMaxNextN) return 0;
+  return static_cast<size_t>(4 * workspace_words(batch_size, static_cast<int64_t>(batch_size) * next_n));
 }
 
 int32_t pmqa_keys_per_cta(int32_t which) {
@@ -118,12 +128,13 @@ pmqa_status pmqa_check_select_args(const float* logits, int64_t logits_stride,
                                    const float* thresholds, const int32_t* counters,
                                    const int32_t* candidates, int32_t capacity, int32_t top_k,
                                    const int32_t* arrivals, const int32_t* ranges,
-                                   const int32_t* topk_idx) {
+                                   const int32_t* topk_idx, const void* workspace,
+                                   size_t workspace_bytes) {
   if (batch_size < 0 || max_context < 0) return PMQA_ERR_SHAPE;
   if (next_n < 1 || next_n > kMaxNextN) return PMQA_ERR_UNSUPPORTED;
   const int64_t rows = static_cast<int64_t>(batch_size) * next_n;
-  pmqa_status st = check_select_outputs(rows, thresholds, counters, candidates, capacity, top_k,
-                                        arrivals, ranges, topk_idx);
+  pmqa_status st = check_select_outputs(batch_size, rows, thresholds, counters, candidates, capacity, top_k,
+                                        arrivals, ranges, topk_idx, workspace, workspace_bytes);
   if (st != PMQA_OK || rows == 0) return st;
   if (!logits || !seq_lens) return PMQA_ERR_NULL;
   if (!aligned(logits, 4) || !aligned(seq_lens, 4)) return PMQA_ERR_ALIGN;
@@ -140,15 +151,16 @@ pmqa_status pmqa_check_fused_args(const uint8_t* q, const uint8_t* kv_fused, con
                                   int64_t num_blocks, int32_t max_context, const float* thresholds,
                                   const int32_t* counters, const int32_t* candidates,
                                   int32_t capacity, int32_t top_k, const int32_t* arrivals,
-                                  const int32_t* ranges, const int32_t* topk_idx) {
+                                  const int32_t* ranges, const int32_t* topk_idx, const void* workspace,
+                                  size_t workspace_bytes) {
   pmqa_status st = check_paged_inputs(q, kv_fused, weights, block_tables, block_table_stride,
                                       block_table_width, seq_lens, seq_lens_stride, batch_size,
                                       next_n, num_heads, head_dim, block_size, num_blocks);
   if (st != PMQA_OK) return st;
   if (max_context < 0) return PMQA_ERR_SHAPE;
   const int64_t rows = static_cast<int64_t>(batch_size) * next_n;
-  st = check_select_outputs(rows, thresholds, counters, candidates, capacity, top_k, arrivals,
-                            ranges, topk_idx);
+  st = check_select_outputs(batch_size, rows, thresholds, counters, candidates, capacity, top_k, arrivals,
+                            ranges, topk_idx, workspace, workspace_bytes);
   if (st != PMQA_OK || rows == 0) return st;
   if (block_table_width < ceil_div(max_context, block_size)) return PMQA_ERR_SHAPE;
   return PMQA_OK;

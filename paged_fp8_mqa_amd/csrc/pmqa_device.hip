@@ -1,13 +1,13 @@
 // libpmqa device code and entry points: paged FP8 MQA logits, threshold Top-k
-// select with last-CTA radix-select repair, and the fused one-launch path, for
-// gfx950 (MI355X).
+// select with a grid-wide radix-select repair, and the fused path (logits and
+// select in one kernel, plus the repair kernel), for gfx950 (MI355X).
 //
 // What is computed (page "flashinfer.attn_scores", fp8_paged_mqa_logits):
 //   E[r, p] = s_p * sum_h w[r, h] * relu(q[b, t, h, :] . k_p),   r = b*next_n + t
 // and the select (page "flashinfer.sdsa.indexer_threshold_select"): keys above
 // a row's threshold are candidates, keys neither above nor below it are ties,
-// both counted and stored in the row's slots; the last CTA of a tile repairs
-// rows that do not fit at their radix-selected k-th largest score.
+// both counted and stored in the row's slots; rows that do not fit are
+// selected again at their radix-selected k-th largest score.
 //
 // Work layout.  A CTA is 4 waves and covers a contiguous chunk of one
 // request's key positions for all next_n rows.  A wave scores 64 keys at a time:
@@ -21,8 +21,11 @@
 // multiplied by that key's scale (region 2 of its page).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "pmqa_internal.h"
@@ -36,8 +39,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupKeys = 64;                  // keys a wave scores per step
 constexpr int kChunk = kGroupKeys * kWaves * 4;  // keys a CTA scores per chunk
-constexpr int kRadixBins = 2048;                // 11-bit digits: 11 + 11 + 10
-constexpr int kFinalizeLds = 4096;              // candidate keys the finalize keeps in LDS
 
 struct PagedArgs {
   const uint8_t* q;
@@ -70,9 +71,11 @@ struct SelectArgs {
   int32_t* arrivals;
   int32_t* ranges;
   int32_t* topk_idx;
+  uint32_t* ws;         // repair workspace (with arrivals)
   int32_t capacity;
   int32_t top_k;
   int32_t rows;
+  int32_t per_request;  // CTAs per request when the grid is not located by a scan
 };
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -301,18 +304,18 @@ __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
 // s_waitcnt vmcnt(0): this wave's loads and stores have completed.
 __device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Shared memory of a CTA.  The union's members are live in different phases:
-// the chunk's scores (main pass, repair append), the per-row radix histograms
-// (repair), and one row's candidate keys (finalize).
+// Shared memory of a CTA: a union of the scores of the chunk being selected,
+// per-row radix histograms (repair passes) and one row's keys (final radix
+// selects), which are live at different times.
 template <int NT>
 struct CtaShared {
   union {
-    float score[NT][kChunk];
-    uint32_t hist[NT][kRadixBins];
+    float score[NT][kChunk];        // the chunk being selected
+    uint32_t hist[NT][kRadixBins];  // per-row radix histograms
     struct {
       uint32_t hist[kRadixBins];
       uint32_t key[kFinalizeLds];
-    } fin;
+    } fin;                          // one row's keys for a final radix select
   } u;
   int32_t wcnt[NT][kWaves][2];
   int32_t wbase[NT][kWaves][2];
@@ -325,6 +328,8 @@ struct CtaShared {
   uint32_t repair_mask;
   int32_t is_last;
   int32_t pos[2];
+  int32_t job[3];      // claimed repair item: tile (or -1: none open, -2: leave), stage, index
+  int32_t next_stage;
 };
 
 // Candidate / tie append of one scored chunk [c0, cend) held in sh.u.score, for
@@ -408,6 +413,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_
   const int lane = lane_id();
   const int per = nb / 64;
   uint32_t local = 0;
+#pragma unroll 4
   for (int i = 0; i < per; ++i) local += hist[lane * per + i];
   uint32_t incl = local;  // sum over lanes >= this lane
 #pragma unroll
@@ -419,6 +425,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_
   uint32_t d = 0, r = 0;
   if (excl < krem && krem <= incl) {
     uint32_t acc = excl;
+#pragma unroll 1
     for (int i = per - 1; i >= 0; --i) {
       const uint32_t h = hist[lane * per + i];
       if (acc + h >= krem) {
@@ -442,46 +449,29 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_
 __device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ int pass_bits(int pass) { return pass == 2 ? 10 : 11; }
 
-// Exact Top-k of one fitting row from its slots: every candidate when there are
-// at most k, topped up with ties from the tie slots; otherwise the k largest
-// candidates by decoded score, found by a 3-pass radix select over keys kept in
-// LDS (read from the slots once).  Entries past k are -1.
-template <int NT>
-__device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, CtaShared<NT>& sh) {
+// The k-th largest of n radix keys key_of(0..n) (1 <= k <= n), by a 3-pass
+// LDS radix select over `hist` (kRadixBins words).  Leaves the key in sh.pfx[0]
+// and, in sh.krem[0], how many entries equal to it the k largest hold; resets
+// sh.pos[0..1] for the caller.
+template <int NT, class KeyOf>
+__device__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
-  int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
-  for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
-  if (nc <= k) {
-    for (int i = tid; i < k; i += kThreads)
-      out[i] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
-    return;
-  }
-  const bool in_lds = nc <= kFinalizeLds;
-  uint32_t* hist = sh.u.fin.hist;
-  uint32_t* keys = sh.u.fin.key;
-  const int32_t* cand = slots + 2 * s.top_k;
-  if (in_lds) {
-#pragma unroll 4
-    for (int i = tid; i < nc; i += kThreads) keys[i] = radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
-  }
   if (tid == 0) {
     sh.pfx[0] = 0u;
     sh.krem[0] = static_cast<uint32_t>(k);
     sh.pos[0] = 0;
     sh.pos[1] = 0;
   }
-  auto key_of = [&](int i) -> uint32_t {
-    return in_lds ? keys[i] : radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
-  };
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass_shift(pass);
     const int bits = pass_bits(pass);
+    #pragma unroll 1
     for (int i = tid; i < kRadixBins; i += kThreads) hist[i] = 0u;
     __syncthreads();
     const uint32_t pf = sh.pfx[0];
-    for (int i = tid; i < nc; i += kThreads) {
+    #pragma unroll 1
+    for (int i = tid; i < n; i += kThreads) {
       const uint32_t key = key_of(i);
       if (pass > 0 && (key >> (shift + bits)) != pf) continue;
       atomicAdd(&hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
@@ -497,9 +487,40 @@ __device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float t
     }
     __syncthreads();
   }
+}
+
+// Exact Top-k of one fitting row from its slots: every candidate when there are
+// at most k, topped up with ties from the tie slots; otherwise the k largest
+// candidates by decoded score, found by a 3-pass radix select over keys kept in
+// LDS (read from the slots once).  Entries past k are -1.
+template <int NT>
+__device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
+  int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
+  for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
+  if (nc <= k) {
+    #pragma unroll 1
+    for (int i = tid; i < k; i += kThreads)
+      out[i] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
+    return;
+  }
+  const bool in_lds = nc <= kFinalizeLds;
+  uint32_t* hist = sh.u.fin.hist;
+  uint32_t* keys = sh.u.fin.key;
+  const int32_t* cand = slots + 2 * s.top_k;
+  if (in_lds) {
+#pragma unroll 1
+    for (int i = tid; i < nc; i += kThreads) keys[i] = radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
+  }
+  auto key_of = [&](int i) -> uint32_t {
+    return in_lds ? keys[i] : radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
+  };
+  cta_radix_select(key_of, nc, k, hist, sh);
   const uint32_t kstar = sh.pfx[0];
   const int n_eq = static_cast<int>(sh.krem[0]);
   const int n_gt = k - n_eq;
+  #pragma unroll 1
   for (int i = tid; i < nc; i += kThreads) {
     const uint32_t key = key_of(i);
     if (key > kstar) {
@@ -512,14 +533,12 @@ __device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float t
   __syncthreads();
 }
 
-// Work of the last CTA of tile (request) b: fit test, repair of the rows that
-// do not fit, ranges, Top-k finalize, and the arrivals reset.
-template <int NT, class Src>
-__device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, const int (&end)[NT],
-                            const float (&thr_in)[NT], CtaShared<NT>& sh) {
+// Fit test of tile b from its counters: fills sh.nc, sh.nt, sh.thr and returns
+// the mask of rows that do not fit.
+template <int NT>
+__device__ uint32_t tile_fit(const SelectArgs& s, int b, const int (&end)[NT], const float (&thr_in)[NT],
+                             CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
-  const int wave = wave_id();
-  const int lane = lane_id();
   if (tid == 0) sh.repair_mask = 0u;
   __syncthreads();
   if (tid < NT) {
@@ -534,76 +553,16 @@ __device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, c
     if (!fit) atomicOr(&sh.repair_mask, 1u << tid);
   }
   __syncthreads();
-  const uint32_t mask = sh.repair_mask;
-  if (mask) {
-    // k-th largest score of each repaired row: three radix passes, each a
-    // re-scoring sweep over the request with per-row LDS histograms.
-    if (tid < NT) {
-      sh.pfx[tid] = 0u;
-      sh.krem[tid] = static_cast<uint32_t>(min(end[tid], s.top_k));
-    }
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass_shift(pass);
-      const int bits = pass_bits(pass);
-      for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
-      __syncthreads();
-      uint32_t pfx[NT];
+  return sh.repair_mask;
+}
+
+// ranges, Top-k finalize and the arrivals reset of tile b, from sh.nc/nt/thr.
+template <int NT>
+__device__ void tile_outputs(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  int end[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) pfx[t] = sh.pfx[t];
-      for (int c = 0; c < L; c += kChunk) {
-        score_chunk<NT>(src, c, min(c + kChunk, L), L, [&](int p0, const float(&E)[NT]) {
-          const int p = p0 + lane;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            if (!(mask & (1u << t)) || p >= end[t]) continue;
-            const uint32_t key = radix_key(E[t]);
-            if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
-            atomicAdd(&sh.u.hist[t][(key >> shift) & ((1u << bits) - 1u)], 1u);
-          }
-        });
-      }
-      __syncthreads();
-      if (wave < NT && (mask & (1u << wave))) {
-        uint32_t d = 0, rem = 0;
-        find_digit(sh.u.hist[wave], 1 << bits, sh.krem[wave], &d, &rem);
-        if (lane == 0) {
-          sh.pfx[wave] = pass == 0 ? d : ((sh.pfx[wave] << bits) | d);
-          sh.krem[wave] = rem;
-        }
-      }
-      __syncthreads();
-    }
-    if (tid < NT && (mask & (1u << tid))) {
-      const float t2 = key_to_float(sh.pfx[tid]);
-      sh.thr[tid] = t2;
-      s.thresholds[b * NT + tid] = t2;
-      sh.cnt[tid][0] = 0;
-      sh.cnt[tid][1] = 0;
-    }
-    __syncthreads();
-    float thr2[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) thr2[t] = sh.thr[t];
-    // select the repaired rows again at their new thresholds, counting in LDS
-    for (int c = 0; c < L; c += kChunk) {
-      const int cend = min(c + kChunk, L);
-      score_chunk<NT>(src, c, cend, L, [&](int p0, const float(&E)[NT]) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
-      });
-      __syncthreads();
-      select_chunk<NT>(s, b, c, cend, thr2, end, sh, &sh.cnt[0][0], mask);
-      __syncthreads();
-    }
-    if (tid < NT && (mask & (1u << tid))) {
-      const int r = b * NT + tid;
-      s.counters[2 * r] = sh.cnt[tid][0];
-      s.counters[2 * r + 1] = sh.cnt[tid][1];
-      sh.nc[tid] = sh.cnt[tid][0];
-      sh.nt[tid] = sh.cnt[tid][1];
-    }
-    __syncthreads();
-  }
+  for (int t = 0; t < NT; ++t) end[t] = max(0, L - NT + t + 1);
   if (tid < NT) {
     const int r = b * NT + tid;
     s.ranges[r] = s.top_k - min(sh.nt[tid], s.top_k);
@@ -613,6 +572,7 @@ __device__ void finish_tile(const Src& src, const SelectArgs& s, int b, int L, c
     for (int t = 0; t < NT; ++t) finalize_topk<NT>(s, b * NT + t, min(end[t], s.top_k), sh.nc[t], sh.thr[t], sh);
   }
   if (tid == 0) s.arrivals[b] = 0;
+  __syncthreads();
 }
 
 // Tile arrival: each wave waits until its slot stores (agent-scope, written
@@ -633,6 +593,474 @@ __device__ __forceinline__ bool arrive_last(const SelectArgs& s, int b, int expe
   return true;
 }
 
+// ---------------------------------------------------------------- repair
+
+// Rows that do not fit are repaired by a second kernel, launched right after
+// the select kernel on the same stream, so it starts with every repair job
+// published and every main-pass slot and counter in memory.  A tile's last CTA
+// in the select kernel publishes a job: the mask of the tile's rows to repair,
+// their state words, and the tile's index appended to the job list.  A job runs
+// in stages, each split into items of kItemKeys keys of the request:
+//   stages 1-3  radix histogram pass 0/1/2 (11/11/10 bits) of the repaired
+//               rows' keys, into per-row global histograms;
+//   stage 4     collect: keys above the selected bucket become candidates
+//               (stored raw), keys inside it go to a per-row bucket buffer;
+//   stage 5     select again at the now exact k-th largest score.
+// After a histogram pass the digit holding each row's k-th largest key is
+// found; if every row's bucket fits the bucket buffer the job moves to stage 4,
+// if every key bit is known to stage 5, else to the next pass.  An item is
+// claimed by a 64-bit fetch-and-add on the job's (stage, next item) word: a
+// returned index below the stage's item count is the caller's item, a larger
+// one claims nothing.  Whoever completes a stage's last item runs the stage
+// change, which rewrites the word to (next stage, 0), or after stage 4 or 5
+// finishes the tile.  A CTA that finds no open item waits (a bounded number of
+// polls) while some job is still in a histogram stage, whose change will open
+// new items, and leaves otherwise; the wait only adds hands, since each job is
+// carried to its end by the CTA that completes each of its stages.  Shared
+// words are written with agent-scope atomic (write-through) stores or atomic
+// adds and read with agent-scope atomic loads.  The last CTA to leave clears
+// the jobs, so the workspace is zero again at the end of the call.
+constexpr int kStageHist0 = 1;
+constexpr int kStageCollect = 4;
+constexpr int kStageSelect = 5;
+constexpr int kIdlePolls = 20000;  // bound on a CTA's polls without an item
+
+struct Ws {
+  uint32_t* base;
+  int batch, rows;
+  __device__ uint32_t* hdr() const { return base; }  // [0] jobs listed, [1] repair CTAs gone
+  __device__ uint32_t* list(int j) const { return base + 16 + j; }
+  // [0,1] claim word, [2] row mask, [3 + stage] items done in the stage
+  __device__ uint32_t* job(int b) const { return base + 16 + job_list_words(batch) + kJobWords * b; }
+  __device__ uint64_t* claim(int b) const { return reinterpret_cast<uint64_t*>(job(b)); }
+  // [0] digit prefix [1] rank left [2] bits known [3] bucket count
+  __device__ uint32_t* row(int r) const { return job(batch) + kRowWords * r; }
+  __device__ uint32_t* hist(int r) const { return job(batch) + kRowWords * rows + static_cast<int64_t>(kRadixBins) * r; }
+  __device__ int32_t* bucket(int r) const {
+    return reinterpret_cast<int32_t*>(job(batch) + (kRowWords + kRadixBins) * rows) +
+           static_cast<int64_t>(2) * kFinalizeLds * r;
+  }
+};
+
+__device__ __forceinline__ uint32_t ld_ag(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_ag64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_wt(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_wt64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int kItemKeys>
+__device__ __forceinline__ int items_of(int L) {
+  return max(1, static_cast<int>(ceil_div(L, kItemKeys)));
+}
+
+// The tile's last CTA (select kernel) hands the rows in `mask` to the repair
+// kernel.  Plain stores: the repair kernel starts after this kernel ends.
+template <int NT>
+__device__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int (&end)[NT], uint32_t mask) {
+  const int tid = threadIdx.x;
+  if (tid < NT && (mask & (1u << tid))) ws.row(b * NT + tid)[1] = static_cast<uint32_t>(min(end[tid], s.top_k));
+  if (tid == 0) {
+    ws.job(b)[2] = mask;
+    *ws.claim(b) = static_cast<uint64_t>(kStageHist0) << 32;
+    *ws.list(static_cast<int>(atomicAdd(ws.hdr(), 1u))) = static_cast<uint32_t>(b);
+  }
+}
+
+// Stage 4 on one scored chunk (scores in sh.u.score): keys of the repaired rows
+// above the bucket are appended as candidates (raw scores; re-encoded once the
+// threshold is known), keys inside it go to the row's bucket buffer.
+template <int NT>
+__device__ void collect_chunk(const SelectArgs& s, const Ws& ws, int b, int c0, int cend, const int (&end)[NT],
+                              const uint32_t (&pfx)[NT], int known, CtaShared<NT>& sh, uint32_t mask) {
+  const int w = wave_id();
+  const int lane = lane_id();
+  const int tid = threadIdx.x;
+  const int stride = s.top_k + s.capacity;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(mask & (1u << t))) continue;
+    const int lim = min(cend, end[t]);
+    int na = 0, ni = 0;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = 256 * w + 64 * it + lane;
+      const bool valid = c0 + i < lim;
+      const uint32_t top = radix_key(sh.u.score[t][i]) >> (32 - known);
+      na += __popcll(__ballot(valid && top > pfx[t]));
+      ni += __popcll(__ballot(valid && top == pfx[t]));
+    }
+    if (lane == 0) {
+      sh.wcnt[t][w][0] = na;
+      sh.wcnt[t][w][1] = ni;
+    }
+  }
+  __syncthreads();
+  if (tid < NT && (mask & (1u << tid))) {
+    const int r = b * NT + tid;
+    int tot[2] = {0, 0};
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+      tot[0] += sh.wcnt[tid][q][0];
+      tot[1] += sh.wcnt[tid][q][1];
+    }
+    int base[2];
+    base[0] = tot[0] ? atomicAdd(s.counters + 2 * r, tot[0]) : 0;
+    base[1] = tot[1] ? static_cast<int>(atomicAdd(ws.row(r) + 3, static_cast<uint32_t>(tot[1]))) : 0;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+      sh.wbase[tid][q][0] = base[0];
+      sh.wbase[tid][q][1] = base[1];
+      base[0] += sh.wcnt[tid][q][0];
+      base[1] += sh.wcnt[tid][q][1];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(mask & (1u << t))) continue;
+    const int r = b * NT + t;
+    const int lim = min(cend, end[t]);
+    int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
+    int32_t* bucket = ws.bucket(r);
+    int ra = sh.wbase[t][w][0], ri = sh.wbase[t][w][1];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = 256 * w + 64 * it + lane;
+      const float e = sh.u.score[t][i];
+      const bool valid = c0 + i < lim;
+      const uint32_t top = radix_key(e) >> (32 - known);
+      const bool above = valid && top > pfx[t];
+      const bool in = valid && top == pfx[t];
+      const uint64_t ma = __ballot(above);
+      const uint64_t mi = __ballot(in);
+      const int ka = ra + lanes_below(ma);
+      const int ki = ri + lanes_below(mi);
+      if (above && ka < s.capacity) store_pair(slots + 2 * (s.top_k + ka), c0 + i, e);
+      if (in && ki < kFinalizeLds) store_pair(bucket + 2 * ki, c0 + i, e);
+      ra += __popcll(ma);
+      ri += __popcll(mi);
+    }
+  }
+}
+
+// Stage change after histogram pass `pass` of tile b's job (run by the CTA that
+// completed the pass's last item).
+template <int NT>
+__device__ __noinline__ void job_next_stage(SelectArgs s, Ws ws, int b, int pass, uint32_t mask, CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int shift = pass_shift(pass);
+  const int bits = pass_bits(pass);
+  const int nb = 1 << bits;
+  if (wave < NT && (mask & (1u << wave))) {
+    uint32_t* gh = ws.hist(b * NT + wave);
+    for (int i = lane; i < nb; i += 64) {
+      sh.u.hist[wave][i] = ld_ag(gh + i);
+      st_wt(gh + i, 0u);
+    }
+  }
+  __syncthreads();
+  if (wave < NT && (mask & (1u << wave))) {
+    uint32_t* row = ws.row(b * NT + wave);
+    const uint32_t pfx = ld_ag(row + 0);
+    uint32_t d = 0, rem = 0;
+    find_digit(sh.u.hist[wave], nb, ld_ag(row + 1), &d, &rem);
+    if (lane == 0) {
+      sh.pfx[wave] = pass == 0 ? d : ((pfx << bits) | d);
+      sh.krem[wave] = rem;
+      sh.cnt[wave][0] = static_cast<int32_t>(sh.u.hist[wave][d]);
+    }
+  }
+  __syncthreads();
+  const int known = 32 - shift;
+  if (tid == 0) {
+    bool small = true;
+    for (int t = 0; t < NT; ++t)
+      if ((mask & (1u << t)) && sh.cnt[t][0] > kFinalizeLds) small = false;
+    sh.next_stage = known == 32 ? kStageSelect : (small ? kStageCollect : kStageHist0 + pass + 1);
+  }
+  __syncthreads();
+  const int next = sh.next_stage;
+  if (tid < NT && (mask & (1u << tid))) {
+    const int r = b * NT + tid;
+    uint32_t* row = ws.row(r);
+    st_wt(row + 0, sh.pfx[tid]);
+    st_wt(row + 1, sh.krem[tid]);
+    st_wt(row + 2, static_cast<uint32_t>(known));
+    if (next >= kStageCollect) {
+      st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, 0u);
+      st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, 0u);
+      st_wt(row + 3, 0u);
+    }
+    if (next == kStageSelect) st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(key_to_float(sh.pfx[tid])));
+  }
+  wait_vm_done();
+  __syncthreads();
+  if (tid == 0) st_wt64(ws.claim(b), static_cast<uint64_t>(next) << 32);
+}
+
+// After the collect stage: each repaired row's exact k-th largest key among its
+// bucket (kept in LDS), the bucket's candidates and ties appended, the raw
+// candidates re-encoded against the new threshold.
+template <int NT>
+__device__ __noinline__ void job_resolve_buckets(SelectArgs s, Ws ws, int b, uint32_t mask, CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int stride = s.top_k + s.capacity;
+  for (int t = 0; t < NT; ++t) {
+    if (!(mask & (1u << t))) continue;
+    const int r = b * NT + t;
+    uint32_t* row = ws.row(r);
+    // the bucket holds the keys of one digit, at most kFinalizeLds by the stage
+    // change's test
+    const int nin = min(static_cast<int>(ld_ag(row + 3)), kFinalizeLds);
+    const int krem = static_cast<int>(ld_ag(row + 1));
+    const int nabove = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+    int32_t* bucket = ws.bucket(r);
+    uint32_t* keys = sh.u.fin.key;
+    #pragma unroll 1
+    for (int i = tid; i < nin; i += kThreads) keys[i] = radix_key(__int_as_float(bucket[2 * i + 1]));
+    __syncthreads();
+    cta_radix_select([&](int i) { return keys[i]; }, nin, krem, sh.u.fin.hist, sh);
+    const uint32_t kstar = sh.pfx[0];
+    const float t2 = key_to_float(kstar);
+    int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
+    // each bucket entry is cleared once used (the workspace stays zeroed)
+    #pragma unroll 1
+    for (int i = tid; i < nin; i += kThreads) {
+      const uint32_t key = keys[i];
+      const int32_t idx = bucket[2 * i];
+      const float e = __int_as_float(bucket[2 * i + 1]);
+      st_wt64(reinterpret_cast<uint64_t*>(bucket + 2 * i), 0u);
+      if (key > kstar) {
+        const int k = nabove + atomicAdd(&sh.pos[0], 1);
+        if (k < s.capacity) store_pair(slots + 2 * (s.top_k + k), idx, enc_cand(e, t2));
+      } else if (key == kstar) {
+        const int k = atomicAdd(&sh.pos[1], 1);
+        if (k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), idx, e - t2);
+      }
+    }
+    #pragma unroll 1
+    for (int i = tid; i < min(nabove, s.capacity); i += kThreads) {
+      int32_t* sl = slots + 2 * (s.top_k + i);
+      store_pair(sl, sl[0], enc_cand(__int_as_float(sl[1]), t2));
+    }
+    __syncthreads();
+    if (tid == 0) {
+      st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, static_cast<uint32_t>(nabove + sh.pos[0]));
+      st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(sh.pos[1]));
+      st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
+    }
+    __syncthreads();
+  }
+}
+
+// Last step of a job: ranges, Top-k and the arrivals reset of the whole tile.
+template <int NT>
+__device__ __noinline__ void job_finish(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  wait_vm_done();
+  __syncthreads();
+  if (tid < NT) {
+    const int r = b * NT + tid;
+    sh.nc[tid] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+    sh.nt[tid] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
+    sh.thr[tid] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
+  }
+  __syncthreads();
+  tile_outputs<NT>(s, b, L, sh);
+}
+
+// Repair item `idx` of stage `stage` of tile b's job: keys [c0, cend) scored
+// again, then their histogram, collect or select pass, then the stage
+// bookkeeping.
+template <int NT, int kItemKeys, class Src>
+__device__ void run_item(const Src& src, const SelectArgs& s, const Ws& ws, int b, int L, int stage, int idx,
+                         CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const uint32_t mask = ld_ag(ws.job(b) + 2);
+  int end[NT];
+  uint32_t pfx[NT];
+  float thr2[NT];
+  int known = 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    end[t] = max(0, L - NT + t + 1);
+    const int r = b * NT + t;
+    const bool m = (mask & (1u << t)) != 0;
+    pfx[t] = m ? ld_ag(ws.row(r) + 0) : 0u;
+    thr2[t] = m ? __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r)) : 0.f;
+    if (m) known = static_cast<int>(ld_ag(ws.row(r) + 2));
+  }
+  const int c0 = idx * kItemKeys;
+  const int cend = min(c0 + kItemKeys, L);
+  if (stage < kStageCollect) {
+    // histogram straight from the scores in registers
+    const int pass = stage - kStageHist0;
+    const int shift = pass_shift(pass);
+    const int bits = pass_bits(pass);
+    const uint32_t low = (1u << bits) - 1u;
+    for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
+    __syncthreads();
+    for (int c = c0; c < cend; c += kChunk) {
+      const int ce = min(c + kChunk, cend);
+      score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
+        const int p = p0 + lane;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (!(mask & (1u << t)) || p >= min(ce, end[t])) continue;
+          const uint32_t key = radix_key(E[t]);
+          if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
+          atomicAdd(&sh.u.hist[t][(key >> shift) & low], 1u);
+        }
+      });
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (!(mask & (1u << t))) continue;
+      uint32_t* gh = ws.hist(b * NT + t);
+      for (int i = tid; i <= static_cast<int>(low); i += kThreads) {
+        const uint32_t h = sh.u.hist[t][i];
+        if (h) atomicAdd(gh + i, h);
+      }
+    }
+  } else {
+    for (int c = c0; c < cend; c += kChunk) {
+      const int ce = min(c + kChunk, cend);
+      score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
+      });
+      __syncthreads();
+      if (stage == kStageCollect)
+        collect_chunk<NT>(s, ws, b, c, ce, end, pfx, known, sh, mask);
+      else
+        select_chunk<NT>(s, b, c, ce, thr2, end, sh, s.counters + 2 * b * NT, mask);
+      __syncthreads();
+    }
+  }
+  wait_vm_done();
+  __syncthreads();
+  if (tid == 0) sh.is_last = atomicAdd(ws.job(b) + 3 + stage, 1u) + 1 == static_cast<uint32_t>(items_of<kItemKeys>(L));
+  __syncthreads();
+  if (!sh.is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (stage < kStageCollect) {
+    job_next_stage<NT>(s, ws, b, stage - kStageHist0, mask, sh);
+  } else {
+    if (stage == kStageCollect) job_resolve_buckets<NT>(s, ws, b, mask, sh);
+    job_finish<NT>(s, b, L, sh);
+  }
+}
+
+// Wave 0 claims an item of a listed job; the result goes to sh.job: (tile,
+// stage, item), tile -1 when none is open but some job is in a histogram stage
+// (more items will open), -2 when the CTA should leave.
+template <int NT, int kItemKeys, class Args>
+__device__ void claim_item(const Args& a, const Ws& ws, int njobs, int& idle, CtaShared<NT>& sh) {
+  if (wave_id() == 0) {
+    const int lane = lane_id();
+    int got = -1, stage = 0, idx = 0;
+    bool pending = false;
+    for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
+      const int j = j0 + lane;
+      int b = 0, items = 0;
+      uint64_t w = 0;
+      if (j < njobs) {
+        b = min(static_cast<int>(ld_ag(ws.list(j))), ws.batch - 1);
+        w = ld_ag64(ws.claim(b));
+        items = items_of<kItemKeys>(a.seq_lens[static_cast<int64_t>(b) * a.sl_stride]);
+      }
+      const uint32_t st = static_cast<uint32_t>(w >> 32);
+      const bool open = st >= kStageHist0 && st <= kStageSelect && static_cast<uint32_t>(w) < static_cast<uint32_t>(items);
+      pending = pending || __ballot(st >= kStageHist0 && st < kStageCollect) != 0;
+      uint64_t m = __ballot(open);
+      const int rot = static_cast<int>(blockIdx.x & 63);  // spread CTAs over the open jobs
+      while (m) {
+        const uint64_t hi = m & (~0ull << rot);
+        const int l = __ffsll(static_cast<long long>(hi ? hi : m)) - 1;
+        m &= ~(1ull << l);
+        const int bl = __shfl(b, l);
+        const int il = __shfl(items, l);
+        unsigned long long old = 0;
+        if (lane == 0) old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.claim(bl)), 1ull);
+        old = __shfl(old, 0);
+        const uint32_t st2 = static_cast<uint32_t>(old >> 32);
+        const uint32_t i2 = static_cast<uint32_t>(old);
+        if (st2 >= kStageHist0 && st2 <= kStageSelect && i2 < static_cast<uint32_t>(il)) {
+          got = bl;
+          stage = static_cast<int>(st2);
+          idx = static_cast<int>(i2);
+          break;
+        }
+      }
+    }
+    if (got < 0 && (!pending || ++idle > kIdlePolls)) got = -2;
+    if (lane == 0) {
+      sh.job[0] = got;
+      sh.job[1] = stage;
+      sh.job[2] = idx;
+    }
+  }
+  __syncthreads();
+}
+
+// The repair kernel's CTA body: claim and run items until nothing is left,
+// then count out; the last CTA out clears the jobs.
+template <int NT, int kItemKeys, class Src, class Args>
+__device__ __forceinline__ void repair_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
+  const Ws ws{s.ws, a.batch, s.rows};
+  // (a workspace that was not left zeroed gives wrong results, not stray accesses)
+  const int njobs = min(static_cast<int>(ld_ag(ws.hdr())), a.batch);
+  if (njobs == 0) return;
+  const int tid = threadIdx.x;
+  Src src;
+  int idle = 0;
+  while (true) {
+    claim_item<NT, kItemKeys>(a, ws, njobs, idle, sh);
+    const int b = sh.job[0];
+    const int stage = sh.job[1];
+    const int idx = sh.job[2];
+    __syncthreads();
+    if (b == -2) break;
+    if (b < 0) {
+      __builtin_amdgcn_s_sleep(8);
+      continue;
+    }
+    idle = 0;
+    const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+    src.init(a, b);
+    run_item<NT, kItemKeys>(src, s, ws, b, L, stage, idx, sh);
+    __syncthreads();
+  }
+  wait_vm_done();
+  if (tid == 0) sh.is_last = atomicAdd(ws.hdr() + 1, 1u) + 1 == gridDim.x;
+  __syncthreads();
+  if (!sh.is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int j = tid; j < njobs; j += kThreads) {
+    uint32_t* lj = ws.list(j);
+    const int b = min(static_cast<int>(ld_ag(lj)), ws.batch - 1);
+    for (int i = 0; i < kJobWords; ++i) st_wt(ws.job(b) + i, 0u);
+    for (int t = 0; t < NT; ++t)
+      for (int i = 0; i < 4; ++i) st_wt(ws.row(b * NT + t) + i, 0u);
+    st_wt(lj, 0u);
+  }
+  if (tid == 0) {
+    st_wt(ws.hdr(), 0u);
+    st_wt(ws.hdr() + 1, 0u);
+  }
+}
+
 // ---------------------------------------------------------------- work items
 
 // A CTA's work item: chunk c of request b (seq_len L, n chunks in all).
@@ -647,12 +1075,13 @@ struct Item {
 // `empty_item` is set, so its tile still finishes).  Otherwise the grid is
 // chunks x batch and the item is (blockIdx.y, blockIdx.x).
 __device__ __forceinline__ bool find_item(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
-                                          int keys_per_cta, bool empty_item, Item& it) {
+                                          int keys_per_cta, bool empty_item, int per_request, Item& it) {
   const int lane = lane_id();
   auto chunks_of = [&](int L) { return L > 0 ? static_cast<int>(ceil_div(L, keys_per_cta)) : (empty_item ? 1 : 0); };
   if (!locate) {
-    it.b = blockIdx.y;
-    it.c = blockIdx.x;
+    // a chunks x batch grid, or a 1-D grid of per_request items per request
+    it.b = per_request > 0 ? blockIdx.x / per_request : blockIdx.y;
+    it.c = per_request > 0 ? blockIdx.x % per_request : blockIdx.x;
     it.L = seq_lens[static_cast<int64_t>(it.b) * sl_stride];
     it.n = chunks_of(it.L);
     return it.c < it.n;
@@ -693,7 +1122,7 @@ __device__ __forceinline__ bool find_item(const int32_t* seq_lens, int64_t sl_st
 template <int NT>
 __global__ void __launch_bounds__(kThreads) logits_kernel(PagedArgs a, float* out, int64_t ld) {
   Item it;
-  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kLogitsKeysPerCta, false, it)) return;
+  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kLogitsKeysPerCta, false, 0, it)) return;
   const int b = it.b;
   const int L = it.L;
   const int c0 = it.c * kLogitsKeysPerCta;
@@ -710,55 +1139,72 @@ __global__ void __launch_bounds__(kThreads) logits_kernel(PagedArgs a, float* ou
   }
 }
 
-// Main pass shared by the fused and the logits-select kernels: score this
-// CTA's chunk(s) into LDS and append them, then count the CTA in and, if it
-// is the tile's last, finish the tile.
-template <int NT, int kKeysPerCta, class Src>
-__device__ __forceinline__ void select_tile_part(const Src& src, const SelectArgs& s, int b, int L, int chunk,
-                                                 int expected, CtaShared<NT>& sh) {
-  const int c0 = chunk * kKeysPerCta;
-  const int cend = min(c0 + kKeysPerCta, L);
+// The select kernels' CTA body: score and select the chunks of the CTA's work
+// item (one request's keys [c, c + keys per CTA)), each scored into LDS and
+// passed over from there; then count the CTA in at the request's tile and, if
+// last, finish the tile or publish its repair job.
+template <int NT, int kKeysPerCta, class Src, class Args>
+__device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
+  Item it;
+  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kKeysPerCta, true, s.per_request, it)) return;
   const int lane = lane_id();
   float thr[NT];
   int end[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    thr[t] = s.thresholds[b * NT + t];
-    end[t] = max(0, L - NT + t + 1);
+    thr[t] = s.thresholds[it.b * NT + t];
+    end[t] = max(0, it.L - NT + t + 1);
   }
+  const int c0 = it.c * kKeysPerCta;
+  const int cend = min(c0 + kKeysPerCta, it.L);
+  Src src;
+  src.init(a, it.b);
   for (int c = c0; c < cend; c += kChunk) {
     const int ce = min(c + kChunk, cend);
-    score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
+    score_chunk<NT>(src, c, ce, it.L, [&](int p0, const float(&E)[NT]) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
     });
     __syncthreads();
-    select_chunk<NT>(s, b, c, ce, thr, end, sh, s.counters + 2 * b * NT, (1u << NT) - 1u);
+    select_chunk<NT>(s, it.b, c, ce, thr, end, sh, s.counters + 2 * it.b * NT, (1u << NT) - 1u);
     __syncthreads();
   }
   if (!s.arrivals) return;
-  if (!arrive_last<NT>(s, b, expected, sh)) return;
-  finish_tile<NT>(src, s, b, L, end, thr, sh);
+  if (!arrive_last<NT>(s, it.b, it.n, sh)) return;
+  const uint32_t mask = tile_fit<NT>(s, it.b, end, thr, sh);
+  if (mask)
+    publish_job<NT>(s, Ws{s.ws, a.batch, s.rows}, it.b, end, mask);
+  else
+    tile_outputs<NT>(s, it.b, it.L, sh);
 }
 
+// Waves per SIMD each variant is built for (VGPR budget 512 / waves).
 template <int NT>
-__global__ void __launch_bounds__(kThreads) fused_kernel(PagedArgs a, SelectArgs s) {
+constexpr int kFusedWaves = NT == 1 ? 3 : (NT == 2 ? 2 : 1);
+
+template <int NT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
+fused_kernel(PagedArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
-  Item it;
-  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kFusedKeysPerCta, true, it)) return;
-  KvSource<NT> src;
-  src.init(a, it.b);
-  select_tile_part<NT, kFusedKeysPerCta>(src, s, it.b, it.L, it.c, it.n, sh);
+  select_body<NT, kFusedKeysPerCta, KvSource<NT>>(a, s, sh);
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
-  Item it;
-  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kSelectKeysPerCta, true, it)) return;
-  LogitsSource<NT> src;
-  src.init(a, it.b);
-  select_tile_part<NT, kSelectKeysPerCta>(src, s, it.b, it.L, it.c, it.n, sh);
+  select_body<NT, kSelectKeysPerCta, LogitsSource<NT>>(a, s, sh);
+}
+
+template <int NT>
+__global__ void __launch_bounds__(kThreads) fused_repair_kernel(PagedArgs a, SelectArgs s) {
+  __shared__ CtaShared<NT> sh;
+  repair_body<NT, kFusedItemKeys, KvSource<NT>>(a, s, sh);
+}
+
+template <int NT>
+__global__ void __launch_bounds__(kThreads) select_repair_kernel(LogitsArgs a, SelectArgs s) {
+  __shared__ CtaShared<NT> sh;
+  repair_body<NT, kSelectItemKeys, LogitsSource<NT>>(a, s, sh);
 }
 
 // ---------------------------------------------------------------- host side
@@ -819,9 +1265,6 @@ pmqa_status validate_content(hipStream_t st, const int32_t* seq_lens, int64_t sl
   return PMQA_OK;
 }
 
-// Batches up to this size use the 1-D located grid (each CTA scans the batch's
-// seq_lens once); larger ones use a chunks x batch grid.
-constexpr int kLocateMaxBatch = 1024;
 
 dim3 grid_for(int32_t batch, int64_t chunks_per_request, bool locate) {
   return locate ? dim3(static_cast<unsigned>(chunks_per_request * batch), 1)
@@ -846,8 +1289,26 @@ PagedArgs paged_args(const uint8_t* q, const uint8_t* kv, const float* w, const 
   return a;
 }
 
+// CTAs of kernel `fn` that fit on the device at once (a repair grid).
+int resident_ctas(const void* fn) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, fn);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) per_cu = 1;
+  const int n = std::max(1, cus) * std::max(1, per_cu);
+  cache[key] = n;
+  return n;
+}
+
 SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int32_t top_k, int32_t* arr,
-                       int32_t* ranges, int32_t* topk, int32_t rows) {
+                       int32_t* ranges, int32_t* topk, int32_t rows, void* workspace, int64_t per_request) {
   SelectArgs s;
   s.thresholds = thr;
   s.counters = cnt;
@@ -855,9 +1316,11 @@ SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int
   s.arrivals = arr;
   s.ranges = ranges;
   s.topk_idx = topk;
+  s.ws = arr ? static_cast<uint32_t*>(workspace) : nullptr;
   s.capacity = cap;
   s.top_k = top_k;
   s.rows = rows;
+  s.per_request = static_cast<int32_t>(per_request);
   return s;
 }
 
@@ -873,9 +1336,26 @@ void launch_nt(int nt, dim3 grid, hipStream_t st, Args... args) {
   }
 }
 
+// One launch of K<nt> with as many CTAs as fit on the device at once.
+template <template <int> class K, class... Args>
+void launch_resident(int nt, hipStream_t st, Args... args) {
+  auto go = [&](auto fn) {
+    const int g = resident_ctas(reinterpret_cast<const void*>(fn));
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st, args...);
+  };
+  switch (nt) {
+    case 1: go(K<1>::fn); break;
+    case 2: go(K<2>::fn); break;
+    case 3: go(K<3>::fn); break;
+    default: go(K<4>::fn); break;
+  }
+}
+
 template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT>; };
 template <int NT> struct FusedK { static constexpr auto fn = fused_kernel<NT>; };
 template <int NT> struct SelectK { static constexpr auto fn = select_kernel<NT>; };
+template <int NT> struct FusedRepairK { static constexpr auto fn = fused_repair_kernel<NT>; };
+template <int NT> struct SelectRepairK { static constexpr auto fn = select_repair_kernel<NT>; };
 
 }  // namespace
 }  // namespace pmqa
@@ -912,10 +1392,10 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
                               int64_t seq_lens_stride, int32_t batch_size, int32_t next_n, int32_t max_context,
                               float* thresholds, int32_t* counters, int32_t* candidates, int32_t capacity,
                               int32_t top_k, int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
-                              void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream) {
   pmqa_status st = pmqa_check_select_args(logits, logits_stride, seq_lens, seq_lens_stride, batch_size, next_n,
                                           max_context, thresholds, counters, candidates, capacity, top_k,
-                                          arrivals, ranges, topk_idx);
+                                          arrivals, ranges, topk_idx, workspace, workspace_bytes);
   if (st != PMQA_OK) return st;
   if (batch_size > 65535) return PMQA_ERR_SHAPE;
   if (batch_size == 0) return PMQA_OK;
@@ -927,8 +1407,9 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
   if (st != PMQA_OK) return st;
   LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, batch_size <= kLocateMaxBatch};
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   static_cast<int32_t>(rows));
-  launch_nt<SelectK>(next_n, grid_for(batch_size, gx, a.locate), hs, a, s);
+                                   static_cast<int32_t>(rows), workspace, gx);
+  launch_nt<SelectK>(next_n, grid_for(batch_size, gx, true), hs, a, s);
+  if (s.ws) launch_resident<SelectRepairK>(next_n, hs, a, s);
   return launched();
 }
 
@@ -939,11 +1420,12 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
                                      int32_t block_size, int64_t num_blocks, int32_t max_context,
                                      float* thresholds, int32_t* counters, int32_t* candidates, int32_t capacity,
                                      int32_t top_k, int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
-                                     void* stream) {
+                                     void* workspace, size_t workspace_bytes, void* stream) {
   pmqa_status st = pmqa_check_fused_args(q, kv_fused, weights, block_tables, block_table_stride,
                                          block_table_width, seq_lens, seq_lens_stride, batch_size, next_n,
                                          num_heads, head_dim, block_size, num_blocks, max_context, thresholds,
-                                         counters, candidates, capacity, top_k, arrivals, ranges, topk_idx);
+                                         counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
+                                         workspace, workspace_bytes);
   if (st != PMQA_OK) return st;
   if (batch_size > 65535) return PMQA_ERR_SHAPE;
   if (batch_size == 0) return PMQA_OK;
@@ -956,8 +1438,9 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size);
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   static_cast<int32_t>(rows));
-  launch_nt<FusedK>(next_n, grid_for(batch_size, gx, a.locate), hs, a, s);
+                                   static_cast<int32_t>(rows), workspace, gx);
+  launch_nt<FusedK>(next_n, grid_for(batch_size, gx, true), hs, a, s);
+  if (s.ws) launch_resident<FusedRepairK>(next_n, hs, a, s);
   return launched();
 }
 

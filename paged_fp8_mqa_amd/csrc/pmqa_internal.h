@@ -14,6 +14,23 @@ constexpr int kLogitsKeysPerCta = 1024;
 constexpr int kFusedKeysPerCta = 1024;
 constexpr int kSelectKeysPerCta = 4096;
 constexpr int kOutColumnGranule = 256;  // padded_seq_len rounding
+constexpr int kRadixBins = 2048;        // 11-bit radix digits: 11 + 11 + 10
+constexpr int kFinalizeLds = 4096;      // keys a CTA keeps in LDS for a final radix select
+constexpr int kJobWords = 16;           // repair workspace: words per tile job
+constexpr int kRowWords = 16;           // repair workspace: words per row state
+constexpr int kFusedItemKeys = 1024;    // keys per repair item, recomputed from the KV pages
+constexpr int kSelectItemKeys = 4096;   // keys per repair item, re-read from a logits row
+constexpr int kLocateMaxBatch = 1024;   // larger batches: a fixed number of CTAs per request
+
+// Repair job list: one word per tile, rounded up to keep the jobs 64-byte aligned.
+constexpr int64_t job_list_words(int64_t batch) { return (batch + 15) / 16 * 16; }
+
+// Repair workspace size in words: a header, the job list, one job per tile,
+// and per row its state, a radix histogram and a bucket buffer of (index,
+// score) pairs.
+constexpr int64_t workspace_words(int64_t batch, int64_t rows) {
+  return 16 + job_list_words(batch) + kJobWords * batch + (kRowWords + kRadixBins + 2 * kFinalizeLds) * rows;
+}
 
 constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

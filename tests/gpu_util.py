@@ -47,10 +47,12 @@ class SelectBuffers:
         self.arrivals = torch.zeros(batch, dtype=torch.int32, device=device) if arrivals else None
         self.ranges = torch.full((2, rows), SENTINEL_I32, dtype=torch.int32, device=device) if arrivals else None
         self.topk = torch.full((rows, top_k), SENTINEL_I32, dtype=torch.int32, device=device) if (arrivals and topk) else None
+        self.ws = pm.make_workspace(batch, rows // batch if batch else 1, device) if arrivals else None
 
     def kwargs(self):
         return dict(thresholds=self.thr, counters=self.counters, candidates=self.cand, capacity=self.capacity,
-                    top_k=self.top_k, arrivals=self.arrivals, ranges=self.ranges, topk_idx=self.topk)
+                    top_k=self.top_k, arrivals=self.arrivals, ranges=self.ranges, topk_idx=self.topk,
+                    workspace=self.ws)
 
     def host(self):
         torch.cuda.synchronize()
@@ -60,6 +62,9 @@ class SelectBuffers:
             "arrivals": None if self.arrivals is None else self.arrivals.cpu().numpy(),
             "ranges": None if self.ranges is None else self.ranges.cpu().numpy(),
             "topk": None if self.topk is None else self.topk.cpu().numpy(),
+            "ws_nonzero": None if self.ws is None else int((self.ws != 0).sum().item()),
+            "ws_words": None if self.ws is None else
+            torch.nonzero(self.ws.view(torch.int32) != 0).flatten()[:16].cpu().tolist(),
         }
 
 

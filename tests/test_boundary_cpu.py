@@ -27,6 +27,14 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pm.SIGNATURES), "binding signatures out of sync with the header"
 
 
+def test_workspace_bytes():
+    lib = pm.lib()
+    b2 = lib.pmqa_workspace_bytes(2, 3)
+    assert b2 > 0 and b2 % 8 == 0 and b2 <= WS
+    assert lib.pmqa_workspace_bytes(64, 1) < lib.pmqa_workspace_bytes(64, 2)
+    assert lib.pmqa_workspace_bytes(2, 0) == 0 and lib.pmqa_workspace_bytes(-1, 1) == 0
+
+
 def test_helpers():
     assert pm.padded_seq_len(8000) == 8192
     assert pm.padded_seq_len(0) == 0 and pm.padded_seq_len(256) == 256 and pm.padded_seq_len(257) == 512
@@ -54,21 +62,25 @@ def logits_args(**kw):
             a["D"], a["bs"], a["nb"], a["msl"], a["out"], a["outs"]]
 
 
+WS = 1 << 20
+
+
 def select_args(**kw):
     a = dict(lg=P(), lgs=8192, sl=P(), sls=1, B=2, nn=3, mc=8000, thr=P(), cnt=P(), cand=P(), cap=512, k=512,
-             arr=P(), rng=P(), topk=P())
+             arr=P(), rng=P(), topk=P(), ws=P(), wsb=WS)
     a.update(kw)
     return [a["lg"], a["lgs"], a["sl"], a["sls"], a["B"], a["nn"], a["mc"], a["thr"], a["cnt"], a["cand"],
-            a["cap"], a["k"], a["arr"], a["rng"], a["topk"]]
+            a["cap"], a["k"], a["arr"], a["rng"], a["topk"], a["ws"], a["wsb"]]
 
 
 def fused_args(**kw):
     a = dict(q=P(), kv=P(), w=P(), bt=P(), bts=250, btw=250, sl=P(), sls=1, B=2, nn=3, H=64, D=128, bs=32,
-             nb=500, mc=8000, thr=P(), cnt=P(), cand=P(), cap=512, k=512, arr=P(), rng=P(), topk=P())
+             nb=500, mc=8000, thr=P(), cnt=P(), cand=P(), cap=512, k=512, arr=P(), rng=P(), topk=P(), ws=P(),
+             wsb=WS)
     a.update(kw)
     return [a["q"], a["kv"], a["w"], a["bt"], a["bts"], a["btw"], a["sl"], a["sls"], a["B"], a["nn"], a["H"],
             a["D"], a["bs"], a["nb"], a["mc"], a["thr"], a["cnt"], a["cand"], a["cap"], a["k"], a["arr"],
-            a["rng"], a["topk"]]
+            a["rng"], a["topk"], a["ws"], a["wsb"]]
 
 
 OK, NULL, SHAPE, STRIDE, UNSUP, ALIGN, OVERFLOW = 0, 1, 2, 3, 4, 5, 6
@@ -94,16 +106,20 @@ def test_check_logits_args(kw, want):
 
 SELECT_CASES = [
     ({}, OK),
-    ({"arr": None, "rng": None, "topk": None}, OK),
+    ({"arr": None, "rng": None, "topk": None, "ws": None, "wsb": 0}, OK),
+    ({"ws": None, "wsb": 0}, NULL),
+    ({"arr": None, "rng": None, "topk": None}, NULL),
+    ({"wsb": 1000}, SHAPE),
+    ({"ws": P(4)}, ALIGN),
     ({"topk": None}, OK),
     ({"lg": None}, NULL), ({"thr": None}, NULL), ({"cnt": None}, NULL), ({"cand": None}, NULL),
-    ({"rng": None}, NULL), ({"arr": None}, NULL),
+    ({"rng": None}, NULL), ({"arr": None, "ws": None}, NULL),
     ({"nn": 0}, UNSUP), ({"nn": 5}, UNSUP),
     ({"k": 0}, SHAPE), ({"cap": -1}, SHAPE), ({"cap": 100}, SHAPE), ({"mc": -1}, SHAPE), ({"B": -1}, SHAPE),
     ({"lgs": 7999}, STRIDE), ({"sls": -1}, STRIDE),
     ({"cnt": P(4)}, ALIGN), ({"cand": P(4)}, ALIGN), ({"thr": P(2)}, ALIGN),
     ({"k": 2 ** 30, "cap": 2 ** 30}, OVERFLOW),
-    ({"B": 60000, "nn": 4, "lgs": 16384, "mc": 16384}, OVERFLOW),
+    ({"B": 60000, "nn": 4, "lgs": 16384, "mc": 16384, "wsb": 1 << 40}, OVERFLOW),
 ]
 
 
@@ -115,7 +131,7 @@ def test_check_select_args(kw, want):
 FUSED_CASES = [
     ({}, OK),
     ({"q": None}, NULL), ({"thr": None}, NULL), ({"rng": None}, NULL),
-    ({"arr": None, "rng": None, "topk": P()}, NULL),
+    ({"arr": None, "rng": None, "topk": P(), "ws": None}, NULL), ({"ws": None}, NULL), ({"wsb": 100}, SHAPE),
     ({"H": 128}, UNSUP), ({"bs": 48}, UNSUP),
     ({"btw": 249}, SHAPE), ({"k": 0}, SHAPE), ({"cap": 10}, SHAPE),
     ({"kv": P(4)}, ALIGN), ({"cnt": P(4)}, ALIGN),

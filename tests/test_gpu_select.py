@@ -29,6 +29,8 @@ def _check(wl, res, repair, scores32=None, scores64=None, tau=None, rows=None, c
     if res["arrivals"] is not None:
         assert np.all(res["arrivals"] == 0), "arrivals not left zeroed"
     assert not errs, "\n".join(errs[:20])
+    if res.get("ws_nonzero") is not None:
+        assert res["ws_nonzero"] == 0, f"workspace not left zeroed (nonzero words at {res['ws_words']})"
 
 
 def _synthetic_logits(seed, R, cols, ends, tie_frac=0.3):
