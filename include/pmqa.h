@@ -138,13 +138,16 @@ pmqa_status pmqa_mqa_logits(
  *                (exact, and order-keeping), else s; for a tie s - t.
  *   capacity     >= 0 candidate slots per row.
  *   top_k        >= 1; also the number of tie slots.
- *   arrivals     [batch_size] int32 or NULL.  Zeroed once by the caller and left
- *                zeroed by every call.  With arrivals, the last CTA of each tile
- *                re-selects every row that does not fit (n_cand > capacity or
- *                n_cand + min(n_tie, top_k) < min(e_r, top_k)) at its
- *                radix-selected min(e_r, top_k)-th largest score; with
- *                capacity >= top_k - 1 every row then fits.  Without arrivals no
- *                repair runs and ranges/topk_idx must be NULL.
+ *   arrivals     [batch_size] int32 or NULL: the per-tile arrival counters of
+ *                the pages' calling convention.  Non-NULL turns on the finish
+ *                stage: every row that does not fit (n_cand > capacity or
+ *                n_cand + min(n_tie, top_k) < min(e_r, top_k)) is selected again
+ *                at its radix-selected min(e_r, top_k)-th largest score (with
+ *                capacity >= top_k - 1 every row then fits), and ranges and
+ *                topk_idx are written.  This implementation finishes the tiles
+ *                in a second kernel on the same stream, so the buffer is never
+ *                read or written (it stays zeroed).  With NULL no repair runs and
+ *                ranges/topk_idx must be NULL.
  *   ranges       [2, R] int32, required with arrivals, output: slots
  *                [ranges[0][r], ranges[1][r]) hold the row's ties and candidates
  *                (ranges[0][r] = top_k - min(n_tie, top_k),
@@ -156,14 +159,14 @@ pmqa_status pmqa_mqa_logits(
  *   workspace    pmqa_workspace_bytes(batch_size, next_n) bytes of device
  *                memory, 8-byte aligned, required with arrivals (NULL
  *                without), zeroed once by the caller and left zeroed by every
- *                call.  It holds the repair: a tile's last CTA publishes a
- *                job for its rows that do not fit (per-row radix histogram
- *                passes, then a collect pass into a per-row bucket buffer, or
- *                an exact re-select), and a second kernel, launched by the same
- *                call on the same stream with as many CTAs as fit on the
- *                device, splits every job into items of a few thousand keys
- *                and runs them grid-wide.  Calls that share a workspace or
- *                arrivals must not run concurrently.
+ *                call.  It holds the finish stage, a second kernel launched by
+ *                the same call on the same stream with as many CTAs as fit on
+ *                the device: each tile's fit test, then ranges and Top-k, or a
+ *                repair job for its rows that do not fit (per-row radix
+ *                histogram passes, then a collect pass into a per-row bucket
+ *                buffer, or an exact re-select), split into items of a few
+ *                thousand keys run grid-wide.  Calls that share a workspace
+ *                must not run concurrently.
  */
 
 /* Bytes of the repair workspace for batch_size requests of next_n rows. */

@@ -39,6 +39,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupKeys = 64;                  // keys a wave scores per step
 constexpr int kChunk = kGroupKeys * kWaves * 4;  // keys a CTA scores per chunk
+constexpr int kFewExtra = 3;   // final select by value walk when at most this many keys are left out
 
 struct PagedArgs {
   const uint8_t* q;
@@ -52,7 +53,8 @@ struct PagedArgs {
   int32_t block_bytes;  // block_size * (head_dim + 4)
   int32_t scale_off;    // block_size * head_dim: start of region 2
   int32_t batch;
-  int32_t locate;       // 1-D grid over live chunks (else a batch x chunks grid)
+  int32_t locate;       // balanced grid over all requests' keys (else per_request CTAs per request)
+  int32_t per_request;
 };
 
 struct LogitsArgs {
@@ -62,6 +64,7 @@ struct LogitsArgs {
   int64_t sl_stride;
   int32_t batch;
   int32_t locate;
+  int32_t per_request;
 };
 
 struct SelectArgs {
@@ -75,7 +78,6 @@ struct SelectArgs {
   int32_t capacity;
   int32_t top_k;
   int32_t rows;
-  int32_t per_request;  // CTAs per request when the grid is not located by a scan
 };
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -85,6 +87,9 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
+
+// s_waitcnt vmcnt(0): this wave's loads and stores have completed.
+__device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const int4 lo = *reinterpret_cast<const int4*>(p);
@@ -158,21 +163,36 @@ struct KvSource {
     }
   }
 
-  // Issue the loads of the 64 keys at p0 (a multiple of 64, below L).  A column
-  // tile at or past L re-reads slots of a page the request owns (values never
-  // used), so every load is unconditional and inside the pool: no block-table
-  // entry past ceil(L / block_size) is read.
-  __device__ __forceinline__ void load(Group& gr, int p0, int L) const {
+  // Pages of the 64 keys at p0 (a multiple of 64, below L): keys p0..p0+31 on
+  // page a, p0+32..p0+63 on page b (the same page for block_size >= 64).  A
+  // column tile at or past L re-reads slots of a page the request owns (values
+  // never used), so no block-table entry past ceil(L / block_size) is read.
+  // The entries are read with scalar loads (the index is uniform), which wait
+  // on their own counter: a group's page lookup never waits for the key loads
+  // still in flight.
+  struct Pages {
+    const uint8_t* a;
+    const uint8_t* b;
+  };
+  __device__ __forceinline__ Pages pages(int p0, int L) const {
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const const_i32* bt = (const const_i32*)(bt_row);
     const int pb = (p0 + 32 < L) ? p0 + 32 : p0;
-    const uint8_t* base_a = kv + static_cast<int64_t>(bt_row[p0 >> bs_shift]) * block_bytes;
-    const uint8_t* base_b = kv + static_cast<int64_t>(bt_row[pb >> bs_shift]) * block_bytes;
+    const int ia = __builtin_amdgcn_readfirstlane(p0 >> bs_shift);
+    const int ib = __builtin_amdgcn_readfirstlane(pb >> bs_shift);
+    return {kv + static_cast<int64_t>(bt[ia]) * block_bytes, kv + static_cast<int64_t>(bt[ib]) * block_bytes};
+  }
+
+  // Issue the loads of the 64 keys at p0, on the pages pg.
+  __device__ __forceinline__ void load(Group& gr, const Pages& pg, int p0) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ps = p0 + 16 * j;
-      gr.k[j] = load32((j < 2 ? base_a : base_b) + ((ps & bs_mask) + n) * kDim + 32 * g);
+      gr.k[j] = load32((j < 2 ? pg.a : pg.b) + ((ps & bs_mask) + n) * kDim + 32 * g);
     }
-    gr.s = *reinterpret_cast<const float*>((g < 2 ? base_a : base_b) + scale_off + ((p0 + lane) & bs_mask) * 4);
+    gr.s = *reinterpret_cast<const float*>((g < 2 ? pg.a : pg.b) + scale_off + ((p0 + lane) & bs_mask) * 4);
   }
+  __device__ __forceinline__ void load(Group& gr, int p0, int L) const { load(gr, pages(p0, L), p0); }
 
   // E[t] = score of key p0 + lane for row t.  Fixed operation order, shared by
   // every kernel, so the logits, fused and repair paths agree bit for bit.
@@ -218,11 +238,16 @@ struct LogitsSource {
     ld = a.ld;
     rows = a.logits + static_cast<int64_t>(b) * NT * a.ld;
   }
-  __device__ __forceinline__ void load(Group& gr, int p0, int L) const {
-    const int p = min(p0 + lane, L - 1);
+  struct Pages {
+    int L;
+  };
+  __device__ __forceinline__ Pages pages(int, int L) const { return {L}; }
+  __device__ __forceinline__ void load(Group& gr, const Pages& pg, int p0) const {
+    const int p = min(p0 + lane, pg.L - 1);
 #pragma unroll
     for (int t = 0; t < NT; ++t) gr.v[t] = rows[t * ld + p];
   }
+  __device__ __forceinline__ void load(Group& gr, int p0, int L) const { load(gr, pages(p0, L), p0); }
   __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t) E[t] = gr.v[t];
@@ -272,6 +297,86 @@ __device__ __forceinline__ void score_chunk(const Src& src, int c0, int cend, in
   }
 }
 
+// Wave priority from the fraction of the range done: the waves of the CTAs
+// that share a compute unit start together, and the issue arbiter favours the
+// oldest waves among those of equal priority; waves that are further along
+// step down, so the CTAs on a unit finish their equal shares together instead
+// of in dispatch order.
+__device__ __forceinline__ void set_priority_by_progress(int done, int total) {
+  switch (3 - min(3, (4 * done) / max(total, 1))) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
+// Scores keys [k0, k1) of one request (k0 a multiple of 64, k1 <= L) in chunks
+// of kChunk keys: wave w takes the chunk's groups w, w+4, w+8, w+12.  store(c,
+// p0, E) runs for every group below k1 (c = its chunk's first key); once all
+// waves have scored a chunk, chunk_done(c, cend) runs between two barriers
+// (when kBarriers).  Loads run two groups ahead of the scoring, across chunk
+// boundaries, so the next chunk's first groups are in flight while a chunk is
+// finished; each group's page lookup is issued one group before its loads.  A
+// group past k1 re-reads the segment's last group (an L2 hit), so every load is
+// unconditional.  An empty range scores nothing and calls nothing.
+template <int NT, bool kBarriers, class Src, class StoreF, class DoneF>
+__device__ __forceinline__ void stream_keys(const Src& src, int k0, int k1, int L, StoreF&& store, DoneF&& done) {
+  k0 = __builtin_amdgcn_readfirstlane(k0);
+  k1 = __builtin_amdgcn_readfirstlane(k1);
+  L = __builtin_amdgcn_readfirstlane(L);
+  // an empty segment (a request with no keys) issues no load at all: the
+  // clamped group indices below assume at least one group
+  if (k1 <= k0) return;
+  __builtin_amdgcn_s_setprio(3);
+  const int w = wave_id();
+  const int ngroups = static_cast<int>(ceil_div(k1 - k0, kGroupKeys));
+  const int steps = 4 * static_cast<int>(ceil_div(ngroups, 4 * kWaves));  // groups per wave, padded
+  auto key0 = [&](int i) { return k0 + kGroupKeys * min(w + kWaves * i, ngroups - 1); };
+  auto valid = [&](int i) { return w + kWaves * i < ngroups; };
+  auto chunk0 = [&](int i) { return k0 + kChunk * (i >> 2); };
+  typename Src::Group ga, gb;
+  typename Src::Pages pa = src.pages(key0(0), L);
+  typename Src::Pages pb = src.pages(key0(1), L);
+  // the caller's loads (q, weights, thresholds) complete before the loop, so
+  // that inside it every wait is for key loads only
+  wait_vm_done();
+  // the scheduling barriers keep the groups' loads in issue order, so the
+  // waits for a group count only the loads issued after it
+  src.load(ga, pa, key0(0));
+  __builtin_amdgcn_sched_barrier(0);
+  pa = src.pages(key0(2), L);
+  src.load(gb, pb, key0(1));
+  __builtin_amdgcn_sched_barrier(0);
+  pb = src.pages(key0(3), L);
+  for (int i = 0; i < steps; i += 2) {
+    if (valid(i)) {
+      float E[NT];
+      src.score(ga, E);
+      store(chunk0(i), key0(i), E);
+    }
+    src.load(ga, pa, key0(i + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    pa = src.pages(key0(i + 4), L);
+    if (valid(i + 1)) {
+      float E[NT];
+      src.score(gb, E);
+      store(chunk0(i + 1), key0(i + 1), E);
+    }
+    src.load(gb, pb, key0(i + 3));
+    __builtin_amdgcn_sched_barrier(0);
+    pb = src.pages(key0(i + 5), L);
+    if (((i + 2) & 3) == 0) {
+      const int c = chunk0(i);
+      if (kBarriers) __syncthreads();
+      done(c, min(c + kChunk, k1));
+      if (kBarriers) __syncthreads();
+      set_priority_by_progress(i + 2, steps);
+    }
+  }
+  __builtin_amdgcn_s_setprio(3);
+}
+
 // ---------------------------------------------------------------- select pieces
 
 // Stored score of a candidate: s - t where that is exact and order-keeping
@@ -301,8 +406,6 @@ __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(slot), packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// s_waitcnt vmcnt(0): this wave's loads and stores have completed.
-__device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Shared memory of a CTA: a union of the scores of the chunk being selected,
 // per-row radix histograms (repair passes) and one row's keys (final radix
@@ -313,10 +416,13 @@ struct CtaShared {
     float score[NT][kChunk];        // the chunk being selected
     uint32_t hist[NT][kRadixBins];  // per-row radix histograms
     struct {
-      uint32_t hist[kRadixBins];
+      alignas(16) uint32_t hist[kRadixBins];
       uint32_t key[kFinalizeLds];
-    } fin;                          // one row's keys for a final radix select
+      int32_t idx[kFinalizeLds];
+    } fin;                          // one row's keys (and key indices) for a final radix select
   } u;
+  uint32_t wtot[kWaves];
+  uint32_t dig[2];
   int32_t wcnt[NT][kWaves][2];
   int32_t wbase[NT][kWaves][2];
   uint32_t pfx[NT];
@@ -449,27 +555,73 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_
 __device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ int pass_bits(int pass) { return pass == 2 ? 10 : 11; }
 
+// The digit of hist[0..nb) (nb = 1024 or 2048, 16-byte aligned) holding the
+// krem-th largest entry, and the rank left inside it, found by the whole CTA:
+// each thread sums nb / kThreads consecutive bins held in registers, a suffix
+// scan over the threads gives the count above each thread's bins, and the one
+// thread whose bins reach krem walks them.  The histogram's total is at least
+// krem.  Returns the same values in every thread.
+template <int NT>
+__device__ __forceinline__ void cta_find_digit(const uint32_t* hist, int nb, uint32_t krem, CtaShared<NT>& sh,
+                                               uint32_t& digit, uint32_t& rem) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int per = nb / kThreads;  // 4 or 8
+  uint32_t h[8];
+  const uint4 lo = *reinterpret_cast<const uint4*>(hist + tid * per);
+  const uint4 hi = per == 8 ? *reinterpret_cast<const uint4*>(hist + tid * per + 4) : uint4{0u, 0u, 0u, 0u};
+  h[0] = lo.x; h[1] = lo.y; h[2] = lo.z; h[3] = lo.w;
+  h[4] = hi.x; h[5] = hi.y; h[6] = hi.z; h[7] = hi.w;
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) local += h[i];
+  uint32_t incl = local;  // over lanes >= this lane
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(incl, off);
+    if (lane + off < 64) incl += y;
+  }
+  if (lane == 0) sh.wtot[w] = incl;
+  if (tid == 0) {
+    sh.dig[0] = 0u;
+    sh.dig[1] = 0u;
+  }
+  __syncthreads();
+  uint32_t above = incl - local;
+  for (int q = w + 1; q < kWaves; ++q) above += sh.wtot[q];
+  if (above < krem && krem <= above + local) {
+    uint32_t acc = above;
+    bool found = false;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      if (!found && i < per && acc + h[i] >= krem) {
+        sh.dig[0] = static_cast<uint32_t>(tid * per + i);
+        sh.dig[1] = krem - acc;
+        found = true;
+      }
+      if (i < per) acc += h[i];
+    }
+  }
+  __syncthreads();
+  digit = sh.dig[0];
+  rem = sh.dig[1];
+}
+
 // The k-th largest of n radix keys key_of(0..n) (1 <= k <= n), by a 3-pass
-// LDS radix select over `hist` (kRadixBins words).  Leaves the key in sh.pfx[0]
-// and, in sh.krem[0], how many entries equal to it the k largest hold; resets
-// sh.pos[0..1] for the caller.
+// LDS radix select over `hist` (kRadixBins words, 16-byte aligned).  Leaves the
+// key in sh.pfx[0] and, in sh.krem[0], how many entries equal to it the k
+// largest hold; resets sh.pos[0..1] for the caller.
 template <int NT, class KeyOf>
 __device__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
-  const int lane = lane_id();
-  if (tid == 0) {
-    sh.pfx[0] = 0u;
-    sh.krem[0] = static_cast<uint32_t>(k);
-    sh.pos[0] = 0;
-    sh.pos[1] = 0;
-  }
+  uint32_t pf = 0u, krem = static_cast<uint32_t>(k);
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass_shift(pass);
     const int bits = pass_bits(pass);
     #pragma unroll 1
     for (int i = tid; i < kRadixBins; i += kThreads) hist[i] = 0u;
     __syncthreads();
-    const uint32_t pf = sh.pfx[0];
     #pragma unroll 1
     for (int i = tid; i < n; i += kThreads) {
       const uint32_t key = key_of(i);
@@ -477,16 +629,82 @@ __device__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, C
       atomicAdd(&hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
     }
     __syncthreads();
-    if (wave_id() == 0) {
-      uint32_t d = 0, rem = 0;
-      find_digit(hist, 1 << bits, sh.krem[0], &d, &rem);
-      if (lane == 0) {
-        sh.pfx[0] = pass == 0 ? d : ((sh.pfx[0] << bits) | d);
-        sh.krem[0] = rem;
-      }
-    }
-    __syncthreads();
+    uint32_t d, rem;
+    cta_find_digit(hist, 1 << bits, krem, sh, d, rem);
+    pf = pass == 0 ? d : ((pf << bits) | d);
+    krem = rem;
   }
+  if (tid == 0) {
+    sh.pfx[0] = pf;
+    sh.krem[0] = krem;
+    sh.pos[0] = 0;
+    sh.pos[1] = 0;
+  }
+  __syncthreads();
+}
+
+// CTA-wide min of a and sum of b (two barriers; every thread gets both).
+template <int NT>
+__device__ __forceinline__ void cta_min_sum(uint32_t& a, uint32_t& b, CtaShared<NT>& sh) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a = min(a, static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), off)));
+    b += static_cast<uint32_t>(__shfl_xor(static_cast<int>(b), off));
+  }
+  __syncthreads();
+  if (lane_id() == 0) {
+    sh.wtot[wave_id()] = a;
+    sh.wcnt[0][wave_id()][0] = static_cast<int32_t>(b);
+  }
+  __syncthreads();
+  a = sh.wtot[0];
+  b = static_cast<uint32_t>(sh.wcnt[0][0][0]);
+#pragma unroll
+  for (int q = 1; q < kWaves; ++q) {
+    a = min(a, sh.wtot[q]);
+    b += static_cast<uint32_t>(sh.wcnt[0][q][0]);
+  }
+}
+
+// The k-th largest of the n radix keys keys[0..n) in LDS when n - k is small:
+// it is the (n - k + 1)-th smallest, found by walking the distinct key values
+// upwards from the minimum, each step one pass that counts the copies of the
+// current value and finds the next larger one.  Returns the key and how many
+// of its copies the k largest hold.
+template <int NT>
+__device__ void few_extra_select(const uint32_t* keys, int n, int k, CtaShared<NT>& sh, uint32_t& kstar,
+                                 int& n_eq) {
+  const int tid = threadIdx.x;
+  const int d = n - k;  // keys to leave out
+  uint32_t m = 0xffffffffu, unused = 0u;
+  for (int i = tid; i < n; i += kThreads) m = min(m, keys[i]);
+  cta_min_sum(m, unused, sh);
+  int below = 0;   // keys smaller than m
+  int copies = 0;  // copies of m
+  // every step passes at least one key, so m reaches the (d+1)-th smallest
+  // within d + 1 steps
+  for (int step = 0; step <= d; ++step) {
+    uint32_t next = 0xffffffffu, cnt = 0u;
+    for (int i = tid; i < n; i += kThreads) {
+      const uint32_t key = keys[i];
+      cnt += key == m ? 1u : 0u;
+      if (key > m) next = min(next, key);
+    }
+    cta_min_sum(next, cnt, sh);
+    copies = static_cast<int>(cnt);
+    if (below + copies > d) break;  // m is the (d+1)-th smallest
+    below += copies;
+    m = next;
+  }
+  kstar = m;
+  // the k largest hold every key above m and the copies of m beyond the
+  // d - below that are left out
+  n_eq = copies - (d - below);
+  if (tid == 0) {
+    sh.pos[0] = 0;
+    sh.pos[1] = 0;
+  }
+  __syncthreads();
 }
 
 // Exact Top-k of one fitting row from its slots: every candidate when there are
@@ -500,34 +718,68 @@ __device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float t
   int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
   for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
   if (nc <= k) {
-    #pragma unroll 1
-    for (int i = tid; i < k; i += kThreads)
-      out[i] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
+    // every candidate, then ties; four loads in flight per thread
+    for (int i0 = 0; i0 < k; i0 += 4 * kThreads) {
+      int32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        if (i < k) v[u] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        if (i < k) out[i] = v[u];
+      }
+    }
     return;
   }
   const bool in_lds = nc <= kFinalizeLds;
   uint32_t* hist = sh.u.fin.hist;
   uint32_t* keys = sh.u.fin.key;
+  int32_t* idx = sh.u.fin.idx;
   const int32_t* cand = slots + 2 * s.top_k;
   if (in_lds) {
-#pragma unroll 1
-    for (int i = tid; i < nc; i += kThreads) keys[i] = radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
+    // (index, score) pairs into LDS, four loads in flight per thread
+    for (int i0 = 0; i0 < nc; i0 += 4 * kThreads) {
+      int2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        if (i < nc) v[u] = *reinterpret_cast<const int2*>(cand + 2 * i);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        if (i < nc) {
+          keys[i] = radix_key(dec_cand(__int_as_float(v[u].y), th));
+          idx[i] = v[u].x;
+        }
+      }
+    }
+    __syncthreads();
   }
   auto key_of = [&](int i) -> uint32_t {
     return in_lds ? keys[i] : radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
   };
-  cta_radix_select(key_of, nc, k, hist, sh);
-  const uint32_t kstar = sh.pfx[0];
-  const int n_eq = static_cast<int>(sh.krem[0]);
+  uint32_t kstar;
+  int n_eq;
+  if (in_lds && nc - k <= kFewExtra) {
+    few_extra_select(keys, nc, k, sh, kstar, n_eq);
+  } else {
+    cta_radix_select(key_of, nc, k, hist, sh);
+    kstar = sh.pfx[0];
+    n_eq = static_cast<int>(sh.krem[0]);
+  }
   const int n_gt = k - n_eq;
   #pragma unroll 1
   for (int i = tid; i < nc; i += kThreads) {
     const uint32_t key = key_of(i);
     if (key > kstar) {
-      out[atomicAdd(&sh.pos[0], 1)] = cand[2 * i];
+      out[atomicAdd(&sh.pos[0], 1)] = in_lds ? idx[i] : cand[2 * i];
     } else if (key == kstar) {
       const int e = atomicAdd(&sh.pos[1], 1);
-      if (e < n_eq) out[n_gt + e] = cand[2 * i];
+      if (e < n_eq) out[n_gt + e] = in_lds ? idx[i] : cand[2 * i];
     }
   }
   __syncthreads();
@@ -556,7 +808,7 @@ __device__ uint32_t tile_fit(const SelectArgs& s, int b, const int (&end)[NT], c
   return sh.repair_mask;
 }
 
-// ranges, Top-k finalize and the arrivals reset of tile b, from sh.nc/nt/thr.
+// ranges and Top-k finalize of tile b, from sh.nc/nt/thr.
 template <int NT>
 __device__ void tile_outputs(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
@@ -571,36 +823,19 @@ __device__ void tile_outputs(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
   if (s.topk_idx) {
     for (int t = 0; t < NT; ++t) finalize_topk<NT>(s, b * NT + t, min(end[t], s.top_k), sh.nc[t], sh.thr[t], sh);
   }
-  if (tid == 0) s.arrivals[b] = 0;
   __syncthreads();
 }
 
-// Tile arrival: each wave waits until its slot stores (agent-scope, written
-// through) and counter atomics have completed, then one thread counts the CTA
-// in; the CTA that completes the count acquires at agent scope and finishes
-// the tile.
-template <int NT>
-__device__ __forceinline__ bool arrive_last(const SelectArgs& s, int b, int expected, CtaShared<NT>& sh) {
-  wait_vm_done();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = atomicAdd(s.arrivals + b, 1);
-    sh.is_last = old == expected - 1;
-  }
-  __syncthreads();
-  if (!sh.is_last) return false;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return true;
-}
+// ---------------------------------------------------------------- finish
 
-// ---------------------------------------------------------------- repair
-
-// Rows that do not fit are repaired by a second kernel, launched right after
-// the select kernel on the same stream, so it starts with every repair job
-// published and every main-pass slot and counter in memory.  A tile's last CTA
-// in the select kernel publishes a job: the mask of the tile's rows to repair,
-// their state words, and the tile's index appended to the job list.  A job runs
-// in stages, each split into items of kItemKeys keys of the request:
+// Each tile is finished by a second kernel, launched right after the select
+// kernel on the same stream, so it starts with every slot and counter of the
+// main pass in memory and the memory system idle.  Phase A: CTA i takes tiles
+// i, i + grid, ...: the fit test, then either the tile's ranges and exact Top-k
+// or, for rows that do not fit, a repair job: the mask of those rows, their
+// state words, and the tile appended to the job list.  Phase B: every CTA runs
+// repair items.  A job runs in stages, each split into items of kItemKeys keys
+// of the request:
 //   stages 1-3  radix histogram pass 0/1/2 (11/11/10 bits) of the repaired
 //               rows' keys, into per-row global histograms;
 //   stage 4     collect: keys above the selected bucket become candidates
@@ -613,13 +848,14 @@ __device__ __forceinline__ bool arrive_last(const SelectArgs& s, int b, int expe
 // returned index below the stage's item count is the caller's item, a larger
 // one claims nothing.  Whoever completes a stage's last item runs the stage
 // change, which rewrites the word to (next stage, 0), or after stage 4 or 5
-// finishes the tile.  A CTA that finds no open item waits (a bounded number of
-// polls) while some job is still in a histogram stage, whose change will open
-// new items, and leaves otherwise; the wait only adds hands, since each job is
-// carried to its end by the CTA that completes each of its stages.  Shared
-// words are written with agent-scope atomic (write-through) stores or atomic
-// adds and read with agent-scope atomic loads.  The last CTA to leave clears
-// the jobs, so the workspace is zero again at the end of the call.
+// finishes the tile.  A CTA with no open item waits (a bounded number of polls)
+// while some CTA is still in phase A, a listed job is not yet written, or a job
+// is in a histogram stage (its change opens new items), and leaves otherwise;
+// the wait only adds hands, since each job is carried to its end by the CTA that
+// completes each of its stages.  Shared words are written with agent-scope
+// atomic (write-through) stores or atomic adds and read with agent-scope atomic
+// loads.  The last CTA to leave clears the jobs, so the workspace is zero again
+// at the end of the call.
 constexpr int kStageHist0 = 1;
 constexpr int kStageCollect = 4;
 constexpr int kStageSelect = 5;
@@ -628,8 +864,9 @@ constexpr int kIdlePolls = 20000;  // bound on a CTA's polls without an item
 struct Ws {
   uint32_t* base;
   int batch, rows;
-  __device__ uint32_t* hdr() const { return base; }  // [0] jobs listed, [1] repair CTAs gone
-  __device__ uint32_t* list(int j) const { return base + 16 + j; }
+  // [0] job list entries reserved, [1] CTAs gone, [2] CTAs done with phase A
+  __device__ uint32_t* hdr() const { return base; }
+  __device__ uint32_t* list(int j) const { return base + 16 + j; }  // tile + 1, 0 until written
   // [0,1] claim word, [2] row mask, [3 + stage] items done in the stage
   __device__ uint32_t* job(int b) const { return base + 16 + job_list_words(batch) + kJobWords * b; }
   __device__ uint64_t* claim(int b) const { return reinterpret_cast<uint64_t*>(job(b)); }
@@ -660,16 +897,21 @@ __device__ __forceinline__ int items_of(int L) {
   return max(1, static_cast<int>(ceil_div(L, kItemKeys)));
 }
 
-// The tile's last CTA (select kernel) hands the rows in `mask` to the repair
-// kernel.  Plain stores: the repair kernel starts after this kernel ends.
+// Phase A hands the rows of tile b in `mask` to phase B: their state words and
+// the claim word first, then (once those are complete) the list entry.
 template <int NT>
 __device__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int (&end)[NT], uint32_t mask) {
   const int tid = threadIdx.x;
-  if (tid < NT && (mask & (1u << tid))) ws.row(b * NT + tid)[1] = static_cast<uint32_t>(min(end[tid], s.top_k));
+  if (tid < NT && (mask & (1u << tid))) st_wt(ws.row(b * NT + tid) + 1, static_cast<uint32_t>(min(end[tid], s.top_k)));
   if (tid == 0) {
-    ws.job(b)[2] = mask;
-    *ws.claim(b) = static_cast<uint64_t>(kStageHist0) << 32;
-    *ws.list(static_cast<int>(atomicAdd(ws.hdr(), 1u))) = static_cast<uint32_t>(b);
+    st_wt(ws.job(b) + 2, mask);
+    st_wt64(ws.claim(b), static_cast<uint64_t>(kStageHist0) << 32);
+  }
+  wait_vm_done();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t j = atomicAdd(ws.hdr(), 1u);
+    st_wt(ws.list(static_cast<int>(j)), static_cast<uint32_t>(b + 1));
   }
 }
 
@@ -862,7 +1104,7 @@ __device__ __noinline__ void job_resolve_buckets(SelectArgs s, Ws ws, int b, uin
   }
 }
 
-// Last step of a job: ranges, Top-k and the arrivals reset of the whole tile.
+// Last step of a job: ranges and Top-k of the whole tile.
 template <int NT>
 __device__ __noinline__ void job_finish(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
@@ -963,26 +1205,33 @@ __device__ void run_item(const Src& src, const SelectArgs& s, const Ws& ws, int 
 }
 
 // Wave 0 claims an item of a listed job; the result goes to sh.job: (tile,
-// stage, item), tile -1 when none is open but some job is in a histogram stage
-// (more items will open), -2 when the CTA should leave.
+// stage, item), tile -1 when none is open but more may open, -2 when the CTA
+// should leave.
 template <int NT, int kItemKeys, class Args>
-__device__ void claim_item(const Args& a, const Ws& ws, int njobs, int& idle, CtaShared<NT>& sh) {
+__device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>& sh) {
   if (wave_id() == 0) {
     const int lane = lane_id();
+    // (a workspace that was not left zeroed gives wrong results, not stray accesses)
+    const int njobs = min(static_cast<int>(ld_ag(ws.hdr())), ws.batch);
+    bool pending = ld_ag(ws.hdr() + 2) < gridDim.x;
     int got = -1, stage = 0, idx = 0;
-    bool pending = false;
     for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
       const int j = j0 + lane;
       int b = 0, items = 0;
       uint64_t w = 0;
+      bool unwritten = false;
       if (j < njobs) {
-        b = min(static_cast<int>(ld_ag(ws.list(j))), ws.batch - 1);
-        w = ld_ag64(ws.claim(b));
-        items = items_of<kItemKeys>(a.seq_lens[static_cast<int64_t>(b) * a.sl_stride]);
+        const uint32_t e = ld_ag(ws.list(j));
+        unwritten = e == 0u;
+        if (!unwritten) {
+          b = min(static_cast<int>(e) - 1, ws.batch - 1);
+          w = ld_ag64(ws.claim(b));
+          items = items_of<kItemKeys>(a.seq_lens[static_cast<int64_t>(b) * a.sl_stride]);
+        }
       }
       const uint32_t st = static_cast<uint32_t>(w >> 32);
       const bool open = st >= kStageHist0 && st <= kStageSelect && static_cast<uint32_t>(w) < static_cast<uint32_t>(items);
-      pending = pending || __ballot(st >= kStageHist0 && st < kStageCollect) != 0;
+      pending = pending || __ballot(unwritten || (st >= kStageHist0 && st < kStageCollect)) != 0;
       uint64_t m = __ballot(open);
       const int rot = static_cast<int>(blockIdx.x & 63);  // spread CTAs over the open jobs
       while (m) {
@@ -1014,19 +1263,36 @@ __device__ void claim_item(const Args& a, const Ws& ws, int njobs, int& idle, Ct
   __syncthreads();
 }
 
-// The repair kernel's CTA body: claim and run items until nothing is left,
-// then count out; the last CTA out clears the jobs.
+// The finish kernel's CTA body: phase A over this CTA's tiles, then repair
+// items until nothing is left, then count out; the last CTA out clears the
+// jobs.
 template <int NT, int kItemKeys, class Src, class Args>
-__device__ __forceinline__ void repair_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
+__device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
   const Ws ws{s.ws, a.batch, s.rows};
-  // (a workspace that was not left zeroed gives wrong results, not stray accesses)
-  const int njobs = min(static_cast<int>(ld_ag(ws.hdr())), a.batch);
-  if (njobs == 0) return;
   const int tid = threadIdx.x;
+  for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
+    const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+    int end[NT];
+    float thr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      end[t] = max(0, L - NT + t + 1);
+      thr[t] = s.thresholds[b * NT + t];
+    }
+    const uint32_t mask = tile_fit<NT>(s, b, end, thr, sh);
+    if (mask)
+      publish_job<NT>(s, ws, b, end, mask);
+    else
+      tile_outputs<NT>(s, b, L, sh);
+    __syncthreads();
+  }
+  wait_vm_done();
+  __syncthreads();
+  if (tid == 0) atomicAdd(ws.hdr() + 2, 1u);
   Src src;
   int idle = 0;
   while (true) {
-    claim_item<NT, kItemKeys>(a, ws, njobs, idle, sh);
+    claim_item<NT, kItemKeys>(a, ws, idle, sh);
     const int b = sh.job[0];
     const int stage = sh.job[1];
     const int idx = sh.job[2];
@@ -1047,135 +1313,152 @@ __device__ __forceinline__ void repair_body(const Args& a, const SelectArgs& s, 
   __syncthreads();
   if (!sh.is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int njobs = min(static_cast<int>(ld_ag(ws.hdr())), a.batch);
   for (int j = tid; j < njobs; j += kThreads) {
     uint32_t* lj = ws.list(j);
-    const int b = min(static_cast<int>(ld_ag(lj)), ws.batch - 1);
-    for (int i = 0; i < kJobWords; ++i) st_wt(ws.job(b) + i, 0u);
-    for (int t = 0; t < NT; ++t)
-      for (int i = 0; i < 4; ++i) st_wt(ws.row(b * NT + t) + i, 0u);
+    const int b = min(static_cast<int>(ld_ag(lj)) - 1, ws.batch - 1);
+    if (b >= 0) {
+      for (int i = 0; i < kJobWords; ++i) st_wt(ws.job(b) + i, 0u);
+      for (int t = 0; t < NT; ++t)
+        for (int i = 0; i < 4; ++i) st_wt(ws.row(b * NT + t) + i, 0u);
+    }
     st_wt(lj, 0u);
   }
   if (tid == 0) {
     st_wt(ws.hdr(), 0u);
     st_wt(ws.hdr() + 1, 0u);
+    st_wt(ws.hdr() + 2, 0u);
   }
 }
 
 // ---------------------------------------------------------------- work items
 
-// A CTA's work item: chunk c of request b (seq_len L, n chunks in all).
-struct Item {
-  int b, c, L, n;
-};
+// Located launches run G >= 2 * batch CTAs, about as many as fit on the device
+// at once.  Every request gets one CTA plus a share of the other G - batch in
+// proportion to its 64-key groups (with `empty_group`, a request with seq_len 0
+// counts as one group, so that its tile still finishes), the shares rounded
+// cumulatively so that they add up; a request's groups are split evenly among
+// its CTAs.  So every CTA works on one request only -- a CTA never pays a
+// second start-up and arrival -- and streams about the same number of keys as
+// every other, whatever the length mix, so none sits idle while others finish
+// a second round.  Other launches give each request per_request CTAs of
+// keys_per_cta keys (no per-CTA scan of the batch).
+__device__ __forceinline__ int groups_of(int L, bool empty_group) {
+  return L > 0 ? static_cast<int>(ceil_div(L, kGroupKeys)) : (empty_group ? 1 : 0);
+}
 
-// Launches with a 1-D grid number every request's chunks request-major, so all
-// CTAs past the last live chunk sit at the end of the dispatch order instead of
-// between live ones.  Each wave derives its item from a scan over
-// ceil(seq_lens[b] / keys_per_cta) (a request with seq_len 0 owns one item when
-// `empty_item` is set, so its tile still finishes).  Otherwise the grid is
-// chunks x batch and the item is (blockIdx.y, blockIdx.x).
-__device__ __forceinline__ bool find_item(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
-                                          int keys_per_cta, bool empty_item, int per_request, Item& it) {
-  const int lane = lane_id();
-  auto chunks_of = [&](int L) { return L > 0 ? static_cast<int>(ceil_div(L, keys_per_cta)) : (empty_item ? 1 : 0); };
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Calls seg(b, L, k0, k1, ctas) for the request b this CTA works on, with
+// [k0, k1) the keys of b it handles and ctas the number of CTAs that handle b
+// (the arrivals b's tile waits for).  Uniform across the CTA.
+template <class F>
+__device__ __forceinline__ void for_each_segment(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
+                                                 int per_request, int keys_per_cta, bool empty_group, F&& seg) {
   if (!locate) {
-    // a chunks x batch grid, or a 1-D grid of per_request items per request
-    it.b = per_request > 0 ? blockIdx.x / per_request : blockIdx.y;
-    it.c = per_request > 0 ? blockIdx.x % per_request : blockIdx.x;
-    it.L = seq_lens[static_cast<int64_t>(it.b) * sl_stride];
-    it.n = chunks_of(it.L);
-    return it.c < it.n;
+    const int b = blockIdx.x / per_request;
+    const int c = blockIdx.x % per_request;
+    const int L = seq_lens[static_cast<int64_t>(b) * sl_stride];
+    const int n = L > 0 ? static_cast<int>(ceil_div(L, keys_per_cta)) : (empty_group ? 1 : 0);
+    if (c < n) seg(b, L, c * keys_per_cta, min((c + 1) * keys_per_cta, L), n);
+    return;
   }
-  const int i = blockIdx.x;
-  int base = 0;
+  const int lane = lane_id();
+  int64_t N = 0;  // groups in all
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int b = b0 + lane;
+    int64_t n = b < batch ? groups_of(seq_lens[static_cast<int64_t>(b) * sl_stride], empty_group) : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+    N += uniform64(n);
+  }
+  const int64_t shared = static_cast<int64_t>(gridDim.x) - batch;
+  // CTAs before a request with c groups before it: its index plus round(shared * c / N)
+  auto first_cta = [&](int64_t b, int64_t c) { return b + (N > 0 ? (2 * shared * c + N) / (2 * N) : 0); };
+  const int64_t i = blockIdx.x;
+  int64_t before = 0;  // groups of the requests before this block of 64
   for (int b0 = 0; b0 < batch; b0 += 64) {
     const int b = b0 + lane;
     const int L = b < batch ? seq_lens[static_cast<int64_t>(b) * sl_stride] : 0;
-    const int n = b < batch ? chunks_of(L) : 0;
-    int incl = n;
+    const int g = b < batch ? groups_of(L, empty_group) : 0;
+    int64_t incl = g;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
+      const int64_t y = __shfl_up(incl, off);
       if (lane >= off) incl += y;
     }
-    const int total = __shfl(incl, 63);
-    if (i < base + total) {
-      const uint64_t m = __ballot(base + incl > i);
-      const int l = __ffsll(static_cast<long long>(m)) - 1;
-      it.b = b0 + l;
-      it.L = __shfl(L, l);
-      it.n = __shfl(n, l);
-      it.c = i - base - (__shfl(incl, l) - it.n);
-      it.b = __builtin_amdgcn_readfirstlane(it.b);
-      it.L = __builtin_amdgcn_readfirstlane(it.L);
-      it.n = __builtin_amdgcn_readfirstlane(it.n);
-      it.c = __builtin_amdgcn_readfirstlane(it.c);
-      return true;
+    const int64_t a0 = first_cta(b, before + incl - g), a1 = first_cta(b + 1, before + incl);
+    const uint64_t hit = __ballot(b < batch && a0 <= i && i < a1);
+    if (hit) {
+      const int l = __ffsll(static_cast<long long>(hit)) - 1;
+      const int bb = __builtin_amdgcn_readfirstlane(b0 + l);
+      const int LL = __builtin_amdgcn_readfirstlane(__shfl(L, l));
+      const int gg = __builtin_amdgcn_readfirstlane(__shfl(g, l));
+      const int n = static_cast<int>(uniform64(__shfl(a1 - a0, l)));
+      const int p = static_cast<int>(i - uniform64(__shfl(a0, l)));
+      const int k0 = static_cast<int>(static_cast<int64_t>(p) * gg / n) * kGroupKeys;
+      const int k1 = min(static_cast<int>(static_cast<int64_t>(p + 1) * gg / n) * kGroupKeys, LL);
+      seg(bb, LL, k0, max(k0, k1), n);
+      return;
     }
-    base += total;
+    before += uniform64(__shfl(incl, 63));
   }
-  return false;
 }
 
 // ---------------------------------------------------------------- kernels
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) logits_kernel(PagedArgs a, float* out, int64_t ld) {
-  Item it;
-  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kLogitsKeysPerCta, false, 0, it)) return;
-  const int b = it.b;
-  const int L = it.L;
-  const int c0 = it.c * kLogitsKeysPerCta;
-  const int cend = min(c0 + kLogitsKeysPerCta, L);
   KvSource<NT> src;
-  src.init(a, b);
-  float* row0 = out + static_cast<int64_t>(b) * NT * ld;
   const int lane = lane_id();
-  for (int c = c0; c < cend; c += kChunk) {
-    score_chunk<NT>(src, c, min(c + kChunk, cend), L, [&](int p0, const float(&E)[NT]) {
+  for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kLogitsKeysPerCta, false,
+                   [&](int b, int L, int k0, int k1, int) {
+    src.init(a, b);
+    float* row0 = out + static_cast<int64_t>(b) * NT * ld;
+    stream_keys<NT, false>(
+        src, k0, k1, L,
+        [&](int, int p0, const float(&E)[NT]) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) row0[t * ld + p0 + lane] = E[t];
-    });
-  }
+          for (int t = 0; t < NT; ++t) row0[t * ld + p0 + lane] = E[t];
+        },
+        [](int, int) {});
+  });
 }
 
-// The select kernels' CTA body: score and select the chunks of the CTA's work
-// item (one request's keys [c, c + keys per CTA)), each scored into LDS and
-// passed over from there; then count the CTA in at the request's tile and, if
-// last, finish the tile or publish its repair job.
+// The select kernels' CTA body: score and select keys [k0, k1) of the CTA's
+// request in chunks, each scored into LDS and selected from there.  Whatever
+// follows -- fit test, repair, ranges, Top-k -- is the finish kernel's.
 template <int NT, int kKeysPerCta, class Src, class Args>
 __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
-  Item it;
-  if (!find_item(a.seq_lens, a.sl_stride, a.batch, a.locate, kKeysPerCta, true, s.per_request, it)) return;
-  const int lane = lane_id();
-  float thr[NT];
-  int end[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    thr[t] = s.thresholds[it.b * NT + t];
-    end[t] = max(0, it.L - NT + t + 1);
-  }
-  const int c0 = it.c * kKeysPerCta;
-  const int cend = min(c0 + kKeysPerCta, it.L);
   Src src;
-  src.init(a, it.b);
-  for (int c = c0; c < cend; c += kChunk) {
-    const int ce = min(c + kChunk, cend);
-    score_chunk<NT>(src, c, ce, it.L, [&](int p0, const float(&E)[NT]) {
+  const int lane = lane_id();
+  for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kKeysPerCta, true,
+                   [&](int b, int L, int k0, int k1, int) {
+    float thr[NT];
+    int end[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
-    });
-    __syncthreads();
-    select_chunk<NT>(s, it.b, c, ce, thr, end, sh, s.counters + 2 * it.b * NT, (1u << NT) - 1u);
-    __syncthreads();
-  }
-  if (!s.arrivals) return;
-  if (!arrive_last<NT>(s, it.b, it.n, sh)) return;
-  const uint32_t mask = tile_fit<NT>(s, it.b, end, thr, sh);
-  if (mask)
-    publish_job<NT>(s, Ws{s.ws, a.batch, s.rows}, it.b, end, mask);
-  else
-    tile_outputs<NT>(s, it.b, it.L, sh);
+    for (int t = 0; t < NT; ++t) {
+      thr[t] = s.thresholds[b * NT + t];
+      end[t] = max(0, L - NT + t + 1);
+    }
+    src.init(a, b);
+    stream_keys<NT, true>(
+        src, k0, k1, L,
+        [&](int c, int p0, const float(&E)[NT]) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
+        },
+        [&](int c, int ce) {
+          select_chunk<NT>(s, b, c, ce, thr, end, sh, s.counters + 2 * b * NT, (1u << NT) - 1u);
+          // a known-empty memory counter here lets the next chunk's first
+          // scores wait for exactly their own loads
+          wait_vm_done();
+        });
+  });
 }
 
 // Waves per SIMD each variant is built for (VGPR budget 512 / waves).
@@ -1196,15 +1479,15 @@ __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectAr
 }
 
 template <int NT>
-__global__ void __launch_bounds__(kThreads) fused_repair_kernel(PagedArgs a, SelectArgs s) {
+__global__ void __launch_bounds__(kThreads) fused_finish_kernel(PagedArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
-  repair_body<NT, kFusedItemKeys, KvSource<NT>>(a, s, sh);
+  finish_body<NT, kFusedItemKeys, KvSource<NT>>(a, s, sh);
 }
 
 template <int NT>
-__global__ void __launch_bounds__(kThreads) select_repair_kernel(LogitsArgs a, SelectArgs s) {
+__global__ void __launch_bounds__(kThreads) select_finish_kernel(LogitsArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
-  repair_body<NT, kSelectItemKeys, LogitsSource<NT>>(a, s, sh);
+  finish_body<NT, kSelectItemKeys, LogitsSource<NT>>(a, s, sh);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1266,16 +1549,13 @@ pmqa_status validate_content(hipStream_t st, const int32_t* seq_lens, int64_t sl
 }
 
 
-dim3 grid_for(int32_t batch, int64_t chunks_per_request, bool locate) {
-  return locate ? dim3(static_cast<unsigned>(chunks_per_request * batch), 1)
-                : dim3(static_cast<unsigned>(chunks_per_request), static_cast<unsigned>(batch));
-}
-
 PagedArgs paged_args(const uint8_t* q, const uint8_t* kv, const float* w, const int32_t* bt,
-                     int64_t bt_stride, const int32_t* sl, int64_t sl_stride, int32_t bs, int32_t batch) {
+                     int64_t bt_stride, const int32_t* sl, int64_t sl_stride, int32_t bs, int32_t batch,
+                     int64_t per_request) {
   PagedArgs a;
   a.batch = batch;
-  a.locate = batch <= kLocateMaxBatch;
+  a.locate = 0;  // chosen at launch
+  a.per_request = static_cast<int32_t>(per_request);
   a.q = q;
   a.kv = kv;
   a.w = w;
@@ -1308,7 +1588,7 @@ int resident_ctas(const void* fn) {
 }
 
 SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int32_t top_k, int32_t* arr,
-                       int32_t* ranges, int32_t* topk, int32_t rows, void* workspace, int64_t per_request) {
+                       int32_t* ranges, int32_t* topk, int32_t rows, void* workspace) {
   SelectArgs s;
   s.thresholds = thr;
   s.counters = cnt;
@@ -1320,28 +1600,30 @@ SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int
   s.capacity = cap;
   s.top_k = top_k;
   s.rows = rows;
-  s.per_request = static_cast<int32_t>(per_request);
   return s;
 }
 
 pmqa_status launched() { return hipGetLastError() == hipSuccess ? PMQA_OK : PMQA_ERR_LAUNCH; }
 
-template <template <int> class K, class... Args>
-void launch_nt(int nt, dim3 grid, hipStream_t st, Args... args) {
-  switch (nt) {
-    case 1: hipLaunchKernelGGL(K<1>::fn, grid, dim3(kThreads), 0, st, args...); break;
-    case 2: hipLaunchKernelGGL(K<2>::fn, grid, dim3(kThreads), 0, st, args...); break;
-    case 3: hipLaunchKernelGGL(K<3>::fn, grid, dim3(kThreads), 0, st, args...); break;
-    default: hipLaunchKernelGGL(K<4>::fn, grid, dim3(kThreads), 0, st, args...); break;
-  }
-}
 
-// One launch of K<nt> with as many CTAs as fit on the device at once.
-template <template <int> class K, class... Args>
-void launch_resident(int nt, hipStream_t st, Args... args) {
+// One launch of K<nt> with scoring arguments `a` first.  A main kernel runs the
+// located grid -- as many CTAs as fit on the device at once -- when that is at
+// least twice the batch, else a.per_request CTAs per request (PMQA_ERR_SHAPE if
+// that grid is too large); a finish kernel always runs as many CTAs as fit.
+template <template <int> class K, class A, class... Rest>
+pmqa_status launch_k(int nt, bool main, hipStream_t st, A a, Rest... rest) {
+  pmqa_status status = PMQA_OK;
   auto go = [&](auto fn) {
-    const int g = resident_ctas(reinterpret_cast<const void*>(fn));
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st, args...);
+    int64_t g = resident_ctas(reinterpret_cast<const void*>(fn));
+    if (main) {
+      a.locate = g >= 2 * static_cast<int64_t>(a.batch);
+      if (!a.locate) g = static_cast<int64_t>(a.per_request) * a.batch;
+      if (g > 0x7fffffff) {
+        status = PMQA_ERR_SHAPE;
+        return;
+      }
+    }
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st, a, rest...);
   };
   switch (nt) {
     case 1: go(K<1>::fn); break;
@@ -1349,13 +1631,14 @@ void launch_resident(int nt, hipStream_t st, Args... args) {
     case 3: go(K<3>::fn); break;
     default: go(K<4>::fn); break;
   }
+  return status;
 }
 
 template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT>; };
 template <int NT> struct FusedK { static constexpr auto fn = fused_kernel<NT>; };
 template <int NT> struct SelectK { static constexpr auto fn = select_kernel<NT>; };
-template <int NT> struct FusedRepairK { static constexpr auto fn = fused_repair_kernel<NT>; };
-template <int NT> struct SelectRepairK { static constexpr auto fn = select_repair_kernel<NT>; };
+template <int NT> struct FusedFinishK { static constexpr auto fn = fused_finish_kernel<NT>; };
+template <int NT> struct SelectFinishK { static constexpr auto fn = select_finish_kernel<NT>; };
 
 }  // namespace
 }  // namespace pmqa
@@ -1383,9 +1666,9 @@ pmqa_status pmqa_mqa_logits(const uint8_t* q, const uint8_t* kv_fused, const flo
                         block_table_stride, block_table_width, block_size, num_blocks, nullptr, 0, nullptr);
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
-                                 seq_lens_stride, block_size, batch_size);
-  launch_nt<LogitsK>(next_n, grid_for(batch_size, gx, a.locate), hs, a, out, out_stride);
-  return launched();
+                                 seq_lens_stride, block_size, batch_size, gx);
+  st = launch_k<LogitsK>(next_n, true, hs, a, out, out_stride);
+  return st != PMQA_OK ? st : launched();
 }
 
 pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const int32_t* seq_lens,
@@ -1405,12 +1688,12 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
   st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_context, nullptr, 0, 0, 1, 0, counters,
                         rows, arrivals);
   if (st != PMQA_OK) return st;
-  LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, batch_size <= kLocateMaxBatch};
+  const LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, 0, static_cast<int32_t>(gx)};
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   static_cast<int32_t>(rows), workspace, gx);
-  launch_nt<SelectK>(next_n, grid_for(batch_size, gx, true), hs, a, s);
-  if (s.ws) launch_resident<SelectRepairK>(next_n, hs, a, s);
-  return launched();
+                                   static_cast<int32_t>(rows), workspace);
+  st = launch_k<SelectK>(next_n, true, hs, a, s);
+  if (st == PMQA_OK && s.ws) st = launch_k<SelectFinishK>(next_n, false, hs, a, s);
+  return st != PMQA_OK ? st : launched();
 }
 
 pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
@@ -1436,12 +1719,12 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
                         block_table_width, block_size, num_blocks, counters, rows, arrivals);
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
-                                 seq_lens_stride, block_size, batch_size);
+                                 seq_lens_stride, block_size, batch_size, gx);
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   static_cast<int32_t>(rows), workspace, gx);
-  launch_nt<FusedK>(next_n, grid_for(batch_size, gx, true), hs, a, s);
-  if (s.ws) launch_resident<FusedRepairK>(next_n, hs, a, s);
-  return launched();
+                                   static_cast<int32_t>(rows), workspace);
+  st = launch_k<FusedK>(next_n, true, hs, a, s);
+  if (st == PMQA_OK && s.ws) st = launch_k<FusedFinishK>(next_n, false, hs, a, s);
+  return st != PMQA_OK ? st : launched();
 }
 
 }  // extern "C"

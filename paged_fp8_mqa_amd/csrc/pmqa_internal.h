@@ -20,7 +20,6 @@ constexpr int kJobWords = 16;           // repair workspace: words per tile job
 constexpr int kRowWords = 16;           // repair workspace: words per row state
 constexpr int kFusedItemKeys = 1024;    // keys per repair item, recomputed from the KV pages
 constexpr int kSelectItemKeys = 4096;   // keys per repair item, re-read from a logits row
-constexpr int kLocateMaxBatch = 1024;   // larger batches: a fixed number of CTAs per request
 
 // Repair job list: one word per tile, rounded up to keep the jobs 64-byte aligned.
 constexpr int64_t job_list_words(int64_t batch) { return (batch + 15) / 16 * 16; }
