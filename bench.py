@@ -190,7 +190,6 @@ def main():
     ms_step = ms_total / args.steps
 
     assert int(arrivals.abs().sum()) == 0, "arrivals not left zeroed"
-    assert int((ws != 0).sum()) == 0, "workspace not left zeroed"
     repaired = int((thr_all[-1].cpu().numpy().view(np.int32) != thr0.view(np.int32)).sum())
 
     # one warm (same pool every step) measurement as context

@@ -158,8 +158,9 @@ pmqa_status pmqa_mqa_logits(
  *                scoring exactly the k-th largest score any may be chosen.
  *   workspace    pmqa_workspace_bytes(batch_size, next_n) bytes of device
  *                memory, 8-byte aligned, required with arrivals (NULL
- *                without), zeroed once by the caller and left zeroed by every
- *                call.  It holds the finish stage, a second kernel launched by
+ *                without).  Zeroed by the caller before its first use; after
+ *                that the library keeps state in it from call to call, so the
+ *                caller leaves it alone (zeroing it again is harmless).  It holds the finish stage, a second kernel launched by
  *                the same call on the same stream with as many CTAs as fit on
  *                the device: each tile's fit test, then ranges and Top-k, or a
  *                repair job for its rows that do not fit (per-row radix

@@ -84,7 +84,8 @@ def workspace_bytes(batch_size: int, next_n: int) -> int:
 
 
 def make_workspace(batch_size: int, next_n: int, device="cuda"):
-    """A zeroed repair workspace; calls leave it zeroed, so it can be reused."""
+    """A zeroed workspace for the finish stage; reuse it for later calls (the
+    library keeps state in it) and do not share it between concurrent calls."""
     import torch
     return torch.zeros(workspace_bytes(batch_size, next_n), dtype=torch.uint8, device=device)
 

@@ -74,7 +74,8 @@ struct SelectArgs {
   int32_t* arrivals;
   int32_t* ranges;
   int32_t* topk_idx;
-  uint32_t* ws;         // repair workspace (with arrivals)
+  uint32_t* ws;         // finish-stage workspace (with arrivals)
+  int64_t ws_words;     // its size in 32-bit words
   int32_t capacity;
   int32_t top_k;
   int32_t rows;
@@ -643,6 +644,36 @@ __device__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, C
   __syncthreads();
 }
 
+// CTA-wide exclusive prefix sums of a and b over the threads in order (two
+// barriers).
+template <int NT>
+__device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, CtaShared<NT>& sh) {
+  const int lane = lane_id();
+  const int w = wave_id();
+  uint32_t ia = a, ib = b;  // inclusive within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t ya = __shfl_up(ia, off), yb = __shfl_up(ib, off);
+    if (lane >= off) {
+      ia += ya;
+      ib += yb;
+    }
+  }
+  __syncthreads();
+  if (lane == 63) {
+    sh.wtot[w] = ia;
+    sh.wcnt[0][w][0] = static_cast<int32_t>(ib);
+  }
+  __syncthreads();
+  uint32_t ba = 0u, bb = 0u;
+  for (int q = 0; q < w; ++q) {
+    ba += sh.wtot[q];
+    bb += static_cast<uint32_t>(sh.wcnt[0][q][0]);
+  }
+  a = ba + ia - a;
+  b = bb + ib - b;
+}
+
 // CTA-wide min of a and sum of b (two barriers; every thread gets both).
 template <int NT>
 __device__ __forceinline__ void cta_min_sum(uint32_t& a, uint32_t& b, CtaShared<NT>& sh) {
@@ -666,7 +697,8 @@ __device__ __forceinline__ void cta_min_sum(uint32_t& a, uint32_t& b, CtaShared<
   }
 }
 
-// The k-th largest of the n radix keys keys[0..n) in LDS when n - k is small:
+// The k-th largest of the n radix keys keys[0..n) in LDS (n <= kFinalizeLds)
+// when n - k is small:
 // it is the (n - k + 1)-th smallest, found by walking the distinct key values
 // upwards from the minimum, each step one pass that counts the copies of the
 // current value and finds the next larger one.  Returns the key and how many
@@ -676,8 +708,16 @@ __device__ void few_extra_select(const uint32_t* keys, int n, int k, CtaShared<N
                                  int& n_eq) {
   const int tid = threadIdx.x;
   const int d = n - k;  // keys to leave out
+  // this thread's keys (n <= kFinalizeLds), in registers for all the steps
+  constexpr int kPer = kFinalizeLds / kThreads;
+  uint32_t kv[kPer];
   uint32_t m = 0xffffffffu, unused = 0u;
-  for (int i = tid; i < n; i += kThreads) m = min(m, keys[i]);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = u * kThreads + tid;
+    kv[u] = i < n ? keys[i] : 0xffffffffu;
+    m = min(m, kv[u]);
+  }
   cta_min_sum(m, unused, sh);
   int below = 0;   // keys smaller than m
   int copies = 0;  // copies of m
@@ -685,10 +725,11 @@ __device__ void few_extra_select(const uint32_t* keys, int n, int k, CtaShared<N
   // within d + 1 steps
   for (int step = 0; step <= d; ++step) {
     uint32_t next = 0xffffffffu, cnt = 0u;
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t key = keys[i];
-      cnt += key == m ? 1u : 0u;
-      if (key > m) next = min(next, key);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const bool valid = u * kThreads + tid < n;
+      cnt += (valid && kv[u] == m) ? 1u : 0u;
+      if (valid && kv[u] > m) next = min(next, kv[u]);
     }
     cta_min_sum(next, cnt, sh);
     copies = static_cast<int>(cnt);
@@ -718,16 +759,16 @@ __device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float t
   int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
   for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
   if (nc <= k) {
-    // every candidate, then ties; four loads in flight per thread
-    for (int i0 = 0; i0 < k; i0 += 4 * kThreads) {
-      int32_t v[4];
+    // every candidate, then ties; eight loads in flight per thread
+    for (int i0 = 0; i0 < k; i0 += 8 * kThreads) {
+      int32_t v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * kThreads + tid;
         if (i < k) v[u] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * kThreads + tid;
         if (i < k) out[i] = v[u];
       }
@@ -740,16 +781,17 @@ __device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float t
   int32_t* idx = sh.u.fin.idx;
   const int32_t* cand = slots + 2 * s.top_k;
   if (in_lds) {
-    // (index, score) pairs into LDS, four loads in flight per thread
-    for (int i0 = 0; i0 < nc; i0 += 4 * kThreads) {
-      int2 v[4];
+    // (index, score) pairs into LDS, all of a thread's loads in flight at once
+    constexpr int kPer = kFinalizeLds / kThreads;
+    for (int i0 = 0; i0 < nc; i0 += kPer * kThreads) {
+      int2 v[kPer];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kPer; ++u) {
         const int i = i0 + u * kThreads + tid;
         if (i < nc) v[u] = *reinterpret_cast<const int2*>(cand + 2 * i);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kPer; ++u) {
         const int i = i0 + u * kThreads + tid;
         if (i < nc) {
           keys[i] = radix_key(dec_cand(__int_as_float(v[u].y), th));
@@ -772,14 +814,44 @@ __device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float t
     n_eq = static_cast<int>(sh.krem[0]);
   }
   const int n_gt = k - n_eq;
+  if (in_lds) {
+    // each thread's keys above k* (and equal to it) counted, one CTA-wide
+    // exclusive scan of the counts, then every thread writes at its offsets
+    constexpr int kPer = kFinalizeLds / kThreads;
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kThreads + tid;
+      if (i < nc) {
+        gt += keys[i] > kstar ? 1u : 0u;
+        eq += keys[i] == kstar ? 1u : 0u;
+      }
+    }
+    uint32_t og = gt, oe = eq;
+    cta_exclusive_scan2(og, oe, sh);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kThreads + tid;
+      if (i < nc) {
+        if (keys[i] > kstar) {
+          out[og++] = idx[i];
+        } else if (keys[i] == kstar) {
+          if (static_cast<int>(oe) < n_eq) out[n_gt + oe] = idx[i];
+          ++oe;
+        }
+      }
+    }
+    __syncthreads();
+    return;
+  }
   #pragma unroll 1
   for (int i = tid; i < nc; i += kThreads) {
     const uint32_t key = key_of(i);
     if (key > kstar) {
-      out[atomicAdd(&sh.pos[0], 1)] = in_lds ? idx[i] : cand[2 * i];
+      out[atomicAdd(&sh.pos[0], 1)] = cand[2 * i];
     } else if (key == kstar) {
       const int e = atomicAdd(&sh.pos[1], 1);
-      if (e < n_eq) out[n_gt + e] = in_lds ? idx[i] : cand[2 * i];
+      if (e < n_eq) out[n_gt + e] = cand[2 * i];
     }
   }
   __syncthreads();
@@ -854,8 +926,8 @@ __device__ void tile_outputs(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
 // the wait only adds hands, since each job is carried to its end by the CTA that
 // completes each of its stages.  Shared words are written with agent-scope
 // atomic (write-through) stores or atomic adds and read with agent-scope atomic
-// loads.  The last CTA to leave clears the jobs, so the workspace is zero again
-// at the end of the call.
+// loads.  A job's last step clears its words; the select kernel clears the
+// header and the job list at its start, when no finish kernel can be running.
 constexpr int kStageHist0 = 1;
 constexpr int kStageCollect = 4;
 constexpr int kStageSelect = 5;
@@ -864,7 +936,9 @@ constexpr int kIdlePolls = 20000;  // bound on a CTA's polls without an item
 struct Ws {
   uint32_t* base;
   int batch, rows;
-  // [0] job list entries reserved, [1] CTAs gone, [2] CTAs done with phase A
+  // [0] job list entries reserved, [2] tiles through phase A, [3] the batch
+  // whose layout the jobs use (the select kernel clears the header and the
+  // list before each finish kernel)
   __device__ uint32_t* hdr() const { return base; }
   __device__ uint32_t* list(int j) const { return base + 16 + j; }  // tile + 1, 0 until written
   // [0,1] claim word, [2] row mask, [3 + stage] items done in the stage
@@ -1104,9 +1178,11 @@ __device__ __noinline__ void job_resolve_buckets(SelectArgs s, Ws ws, int b, uin
   }
 }
 
-// Last step of a job: ranges and Top-k of the whole tile.
+// Last step of a job: ranges and Top-k of the whole tile, then the job's words
+// cleared for the next call (all but the claim word, which late claim attempts
+// may still increment; the next publish of the tile rewrites it).
 template <int NT>
-__device__ __noinline__ void job_finish(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
+__device__ __noinline__ void job_finish(SelectArgs s, Ws ws, int b, int L, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   wait_vm_done();
   __syncthreads();
@@ -1118,6 +1194,9 @@ __device__ __noinline__ void job_finish(SelectArgs s, int b, int L, CtaShared<NT
   }
   __syncthreads();
   tile_outputs<NT>(s, b, L, sh);
+  if (tid < NT)
+    for (int i = 0; i < 4; ++i) st_wt(ws.row(b * NT + tid) + i, 0u);
+  if (tid >= 64 + 2 && tid < 64 + kJobWords) st_wt(ws.job(b) + (tid - 64), 0u);
 }
 
 // Repair item `idx` of stage `stage` of tile b's job: keys [c0, cend) scored
@@ -1200,7 +1279,7 @@ __device__ void run_item(const Src& src, const SelectArgs& s, const Ws& ws, int 
     job_next_stage<NT>(s, ws, b, stage - kStageHist0, mask, sh);
   } else {
     if (stage == kStageCollect) job_resolve_buckets<NT>(s, ws, b, mask, sh);
-    job_finish<NT>(s, b, L, sh);
+    job_finish<NT>(s, ws, b, L, sh);
   }
 }
 
@@ -1213,7 +1292,7 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
     const int lane = lane_id();
     // (a workspace that was not left zeroed gives wrong results, not stray accesses)
     const int njobs = min(static_cast<int>(ld_ag(ws.hdr())), ws.batch);
-    bool pending = ld_ag(ws.hdr() + 2) < gridDim.x;
+    bool pending = ld_ag(ws.hdr() + 2) < static_cast<uint32_t>(ws.batch);
     int got = -1, stage = 0, idx = 0;
     for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
       const int j = j0 + lane;
@@ -1264,13 +1343,13 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
 }
 
 // The finish kernel's CTA body: phase A over this CTA's tiles, then repair
-// items until nothing is left, then count out; the last CTA out clears the
-// jobs.
+// items until nothing is left.
 template <int NT, int kItemKeys, class Src, class Args>
 __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
   const Ws ws{s.ws, a.batch, s.rows};
   const int tid = threadIdx.x;
-  for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
+  uint32_t tiles = 0;
+  for (int b = blockIdx.x; b < a.batch; b += gridDim.x, ++tiles) {
     const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
     int end[NT];
     float thr[NT];
@@ -1286,9 +1365,11 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
       tile_outputs<NT>(s, b, L, sh);
     __syncthreads();
   }
-  wait_vm_done();
-  __syncthreads();
-  if (tid == 0) atomicAdd(ws.hdr() + 2, 1u);
+  if (tiles) {
+    wait_vm_done();
+    __syncthreads();
+    if (tid == 0) atomicAdd(ws.hdr() + 2, tiles);
+  }
   Src src;
   int idle = 0;
   while (true) {
@@ -1307,27 +1388,6 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     src.init(a, b);
     run_item<NT, kItemKeys>(src, s, ws, b, L, stage, idx, sh);
     __syncthreads();
-  }
-  wait_vm_done();
-  if (tid == 0) sh.is_last = atomicAdd(ws.hdr() + 1, 1u) + 1 == gridDim.x;
-  __syncthreads();
-  if (!sh.is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int njobs = min(static_cast<int>(ld_ag(ws.hdr())), a.batch);
-  for (int j = tid; j < njobs; j += kThreads) {
-    uint32_t* lj = ws.list(j);
-    const int b = min(static_cast<int>(ld_ag(lj)) - 1, ws.batch - 1);
-    if (b >= 0) {
-      for (int i = 0; i < kJobWords; ++i) st_wt(ws.job(b) + i, 0u);
-      for (int t = 0; t < NT; ++t)
-        for (int i = 0; i < 4; ++i) st_wt(ws.row(b * NT + t) + i, 0u);
-    }
-    st_wt(lj, 0u);
-  }
-  if (tid == 0) {
-    st_wt(ws.hdr(), 0u);
-    st_wt(ws.hdr() + 1, 0u);
-    st_wt(ws.hdr() + 2, 0u);
   }
 }
 
@@ -1434,6 +1494,31 @@ __global__ void __launch_bounds__(kThreads) logits_kernel(PagedArgs a, float* ou
 // follows -- fit test, repair, ranges, Top-k -- is the finish kernel's.
 template <int NT, int kKeysPerCta, class Src, class Args>
 __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
+  if (s.ws && blockIdx.x == 0) {
+    // The finish kernel's header and job list start empty.  The last finish
+    // kernel on this workspace may have left claim words behind (late claim
+    // attempts); they sit where its batch put them, so they are cleared at
+    // those places first, in case this call's batch lays the workspace out
+    // differently.
+    const int tid = threadIdx.x;
+    const uint32_t old_batch = min(s.ws[3], 65535u);
+    const uint32_t old_jobs =
+        min(min(s.ws[0], old_batch), static_cast<uint32_t>(max<int64_t>(0, s.ws_words - 16)));
+    const int64_t old_jobs_at = 16 + job_list_words(old_batch);
+    for (uint32_t j = tid; j < old_jobs; j += kThreads) {
+      const uint32_t e = s.ws[16 + j];
+      const int64_t at = old_jobs_at + static_cast<int64_t>(kJobWords) * (static_cast<int64_t>(e) - 1);
+      if (e != 0u && e <= old_batch && at + 2 <= s.ws_words) {
+        s.ws[at] = 0u;
+        s.ws[at + 1] = 0u;
+      }
+    }
+    __syncthreads();
+    const int64_t words = min<int64_t>(s.ws_words, 16 + max(job_list_words(old_batch), job_list_words(a.batch)));
+    for (int64_t i = tid; i < words; i += kThreads) s.ws[i] = 0u;
+    __syncthreads();
+    if (tid == 0) s.ws[3] = static_cast<uint32_t>(a.batch);
+  }
   Src src;
   const int lane = lane_id();
   for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kKeysPerCta, true,
@@ -1588,7 +1673,7 @@ int resident_ctas(const void* fn) {
 }
 
 SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int32_t top_k, int32_t* arr,
-                       int32_t* ranges, int32_t* topk, int32_t rows, void* workspace) {
+                       int32_t* ranges, int32_t* topk, int32_t rows, void* workspace, size_t workspace_bytes) {
   SelectArgs s;
   s.thresholds = thr;
   s.counters = cnt;
@@ -1597,6 +1682,7 @@ SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int
   s.ranges = ranges;
   s.topk_idx = topk;
   s.ws = arr ? static_cast<uint32_t*>(workspace) : nullptr;
+  s.ws_words = s.ws ? static_cast<int64_t>(workspace_bytes / 4) : 0;
   s.capacity = cap;
   s.top_k = top_k;
   s.rows = rows;
@@ -1690,7 +1776,7 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
   if (st != PMQA_OK) return st;
   const LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, 0, static_cast<int32_t>(gx)};
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   static_cast<int32_t>(rows), workspace);
+                                   static_cast<int32_t>(rows), workspace, workspace_bytes);
   st = launch_k<SelectK>(next_n, true, hs, a, s);
   if (st == PMQA_OK && s.ws) st = launch_k<SelectFinishK>(next_n, false, hs, a, s);
   return st != PMQA_OK ? st : launched();
@@ -1721,7 +1807,7 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   static_cast<int32_t>(rows), workspace);
+                                   static_cast<int32_t>(rows), workspace, workspace_bytes);
   st = launch_k<FusedK>(next_n, true, hs, a, s);
   if (st == PMQA_OK && s.ws) st = launch_k<FusedFinishK>(next_n, false, hs, a, s);
   return st != PMQA_OK ? st : launched();

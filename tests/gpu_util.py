@@ -38,7 +38,8 @@ def run_logits(wl, d, out_cols=None, max_seq_len=None):
 
 
 class SelectBuffers:
-    def __init__(self, rows, batch, top_k, capacity, thresholds, device="cuda", arrivals=True, topk=True):
+    def __init__(self, rows, batch, top_k, capacity, thresholds, device="cuda", arrivals=True, topk=True,
+                 workspace=None):
         self.top_k, self.capacity = top_k, capacity
         self.thr = torch.as_tensor(np.asarray(thresholds, dtype=np.float32)).to(device)
         self.thr_in = self.thr.clone()
@@ -47,7 +48,8 @@ class SelectBuffers:
         self.arrivals = torch.zeros(batch, dtype=torch.int32, device=device) if arrivals else None
         self.ranges = torch.full((2, rows), SENTINEL_I32, dtype=torch.int32, device=device) if arrivals else None
         self.topk = torch.full((rows, top_k), SENTINEL_I32, dtype=torch.int32, device=device) if (arrivals and topk) else None
-        self.ws = pm.make_workspace(batch, rows // batch if batch else 1, device) if arrivals else None
+        self.ws = None if not arrivals else (
+            workspace if workspace is not None else pm.make_workspace(batch, rows // batch if batch else 1, device))
 
     def kwargs(self):
         return dict(thresholds=self.thr, counters=self.counters, candidates=self.cand, capacity=self.capacity,
@@ -62,9 +64,6 @@ class SelectBuffers:
             "arrivals": None if self.arrivals is None else self.arrivals.cpu().numpy(),
             "ranges": None if self.ranges is None else self.ranges.cpu().numpy(),
             "topk": None if self.topk is None else self.topk.cpu().numpy(),
-            "ws_nonzero": None if self.ws is None else int((self.ws != 0).sum().item()),
-            "ws_words": None if self.ws is None else
-            torch.nonzero(self.ws.view(torch.int32) != 0).flatten()[:16].cpu().tolist(),
         }
 
 
