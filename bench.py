@@ -1,17 +1,20 @@
 """Benchmark of the paged FP8 MQA logits + threshold Top-k select hot path.
 
-One step = one pmqa_fused_logits_select launch over the whole batch of a
-synthetic workload (logits, candidate/tie select, last-CTA repair, ranges and
-exact Top-k finalize), with every input already resident in HBM.  Each step
-gets its own pre-zeroed counters and pristine thresholds (prepared before the
-timed region) and cycles through `--replicas` copies of the KV pool, so no
-step finds its pool in the 256 MiB Infinity Cache.
+One step = one pmqa_fused_logits_select call over the whole batch of a
+synthetic workload: the select kernel (logits and candidate/tie select) and
+the finish kernel (fit test, repair, ranges and exact Top-k), with every input
+already resident in HBM.  Each step gets its own pre-zeroed counters and
+pristine thresholds (prepared before the timed region) and cycles through
+`--replicas` copies of the KV pool, so no step finds its pool in the 256 MiB
+Infinity Cache.
 
 Prints one JSON line:
   value          pairs/s: sum over rows of visible KV positions, per second
   rows_per_s     rows selected (and finalized) per second
-  roofline       the fused kernel's algorithmic HBM bytes per launch over its
-                 average launch time (HIP events on its stream) against 8 TB/s
+  roofline       the select kernel (the dominant one): algorithmic HBM bytes
+                 per launch over its average launch time, from HIP events on
+                 its stream around the same steps run with the finish stage
+                 off, against 8 TB/s
   cpu_baseline   the float64 CPU oracle on a bounded sample of the workload
 
     python bench.py [--steps K] [--warmup W] [--workload 3|4|5] [--path fused|unfused]
@@ -161,15 +164,16 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i, finish=True):
         kv = kvs[i % len(kvs)]
+        fin = dict(arrivals=arrivals, ranges=ranges, topk_idx=topk, workspace=ws) if finish else {}
         if args.path == "fused":
             pm.fused_logits_select(q, kv, w, bt, sl, wl.max_seq_len, thr_all[i], cnt_all[i], cand, wl.capacity,
-                                   wl.top_k, arrivals, ranges, topk, workspace=ws)
+                                   wl.top_k, **fin)
         else:
             pm.mqa_logits(q, kv, w, bt, sl, wl.max_seq_len, out=logits)
             pm.indexer_topk(logits, sl, wl.next_n, wl.max_seq_len, thr_all[i], cnt_all[i], cand, wl.capacity,
-                            wl.top_k, arrivals, ranges, topk, workspace=ws)
+                            wl.top_k, **fin)
 
     for i in range(args.warmup):
         step(i)
@@ -191,6 +195,21 @@ def main():
 
     assert int(arrivals.abs().sum()) == 0, "arrivals not left zeroed"
     repaired = int((thr_all[-1].cpu().numpy().view(np.int32) != thr0.view(np.int32)).sum())
+
+    # the same steps with the finish stage off: the select kernel alone, for
+    # its roofline (fresh counters, same KV replicas in the same order)
+    cnt_all.zero_()
+    thr_all.copy_(torch.from_numpy(np.tile(thr0, (total, 1))).to(dev))
+    for i in range(args.warmup):
+        step(i, finish=False)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for j in range(args.steps):
+        sev[j][0].record(stream)
+        step(args.warmup + j, finish=False)
+        sev[j][1].record(stream)
+    torch.cuda.synchronize()
+    select_ms = np.array([a.elapsed_time(b) for a, b in sev])
 
     # one warm (same pool every step) measurement as context
     warm = []
@@ -217,7 +236,7 @@ def main():
         del src, dst
 
     alg = algorithmic_bytes(wl, args.path)
-    mean_launch_s = float(launch_ms.mean()) / 1e3
+    mean_launch_s = float(select_ms.mean()) / 1e3
     achieved = alg / mean_launch_s / 1e9
     flops = 2.0 * 64 * 128 * pairs
     out = {
@@ -241,10 +260,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(args.workload, args.path),
                      "algorithmic_bytes_per_launch": alg,
-                     "launch_ms": {"mean": float(launch_ms.mean()), "p10": float(np.percentile(launch_ms, 10)),
-                                   "p50": float(np.percentile(launch_ms, 50)),
-                                   "p90": float(np.percentile(launch_ms, 90))},
+                     "kernel": "select (fused logits + candidate/tie select)" if args.path == "fused"
+                     else "mqa_logits + select",
+                     "launch_ms": {"mean": float(select_ms.mean()), "p10": float(np.percentile(select_ms, 10)),
+                                   "p50": float(np.percentile(select_ms, 50)),
+                                   "p90": float(np.percentile(select_ms, 90))},
                      "mfma_frac": flops / mean_launch_s / 1e12 / FP8_PEAK_TFLOPS},
+        "call_ms": {"mean": float(launch_ms.mean()), "p50": float(np.percentile(launch_ms, 50)),
+                    "finish_stage_mean": float(launch_ms.mean() - select_ms.mean())},
         "warm_ms_per_step": float(np.median(warm)),
         "kernel_src_sha": kernel_hash(),
     }
