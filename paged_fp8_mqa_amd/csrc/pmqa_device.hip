@@ -33,12 +33,14 @@
 namespace pmqa {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupKeys = 64;                  // keys a wave scores per step
 constexpr int kChunk = kGroupKeys * kWaves * 4;  // keys a CTA scores per chunk
+constexpr int kStageInt4 = 512;  // a wave's KV staging area: 64 keys x 128 bytes
 constexpr int kFewExtra = 3;   // final select by value walk when at most this many keys are left out
 
 struct PagedArgs {
@@ -125,19 +127,29 @@ __device__ __forceinline__ float reduce_scatter4(float x0, float x1, float x2, f
 
 // ---------------------------------------------------------------- score sources
 
-// Scores computed from the paged KV pool.
+// Scores computed from the paged KV pool.  A wave reads a group's 64 keys with
+// contiguous loads -- lane l takes bytes 16l..16l+15 of each 1 KB run of 8
+// keys -- and turns them into MFMA B operands through an 8 KB LDS area of its
+// own: each lane writes its 16-byte pieces into the keys' 128-byte rows, the
+// row's eight 16-byte columns XOR-swizzled by the row index (so that neither
+// the writes nor the operand reads of 16 rows at one column pile onto one
+// bank), and reads back the 32 bytes of key n its operand needs.
 template <int NT>
 struct KvSource {
   struct Group {
-    v8i k[4];
+    v4i raw[8];   // lane's 16 bytes of keys 8i + lane/8, column lane % 8
     float s;
   };
+  v4i* stage;           // this wave's 8 KB LDS area: 64 rows of 8 16-byte columns
   v8i qa[NT][4];        // A operands: rows t, head tiles mt
   float wt[NT][16];     // weight of head 16*mt + 4*g + i at [4*mt + i]
   const uint8_t* kv;
   const int32_t* bt_row;
   int bs_shift, bs_mask, block_bytes, scale_off;
   int lane, n, g;
+
+  // The wave's staging area (kStageInt4 int4 per wave, kWaves waves).
+  __device__ __forceinline__ void bind(v4i* lds) { stage = lds + wave_id() * kStageInt4; }
 
   __device__ __forceinline__ void init(const PagedArgs& a, int b) {
     lane = lane_id();
@@ -184,12 +196,13 @@ struct KvSource {
     return {kv + static_cast<int64_t>(bt[ia]) * block_bytes, kv + static_cast<int64_t>(bt[ib]) * block_bytes};
   }
 
-  // Issue the loads of the 64 keys at p0, on the pages pg.
+  // Issue the loads of the 64 keys at p0, on the pages pg: eight contiguous
+  // 1 KB runs (keys 8i..8i+7 each, never across a page) and the keys' scales.
   __device__ __forceinline__ void load(Group& gr, const Pages& pg, int p0) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ps = p0 + 16 * j;
-      gr.k[j] = load32((j < 2 ? pg.a : pg.b) + ((ps & bs_mask) + n) * kDim + 32 * g);
+    for (int i = 0; i < 8; ++i) {
+      const uint8_t* run = (i < 4 ? pg.a : pg.b) + ((p0 + 8 * i) & bs_mask) * kDim;
+      gr.raw[i] = *reinterpret_cast<const v4i*>(run + 16 * lane);
     }
     gr.s = *reinterpret_cast<const float*>((g < 2 ? pg.a : pg.b) + scale_off + ((p0 + lane) & bs_mask) * 4);
   }
@@ -198,6 +211,21 @@ struct KvSource {
   // E[t] = score of key p0 + lane for row t.  Fixed operation order, shared by
   // every kernel, so the logits, fused and repair paths agree bit for bit.
   __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
+    // the group into the staging area, then the operands out of it (LDS
+    // operations of one wave complete in order)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      stage[row * 8 + ((lane & 7) ^ (row & 7))] = gr.raw[i];
+    }
+    v8i bk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * j + n;
+      const v4i lo = stage[row * 8 + ((2 * g) ^ (row & 7))];
+      const v4i hi = stage[row * 8 + ((2 * g + 1) ^ (row & 7))];
+      bk[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
     float part[NT][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -207,7 +235,7 @@ struct KvSource {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mfma_fp8(qa[t][mt], gr.k[j]);
+        for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mfma_fp8(qa[t][mt], bk[j]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         float sum = 0.f;
@@ -234,6 +262,7 @@ struct LogitsSource {
   int64_t ld;
   int lane;
 
+  __device__ __forceinline__ void bind(v4i*) {}
   __device__ __forceinline__ void init(const LogitsArgs& a, int b) {
     lane = lane_id();
     ld = a.ld;
@@ -439,14 +468,26 @@ struct CtaShared {
   int32_t next_stage;
 };
 
+// Shared memory of a select kernel CTA: the chunk's scores and the per-wave
+// counts of the slot append (the finish stage's structures stay out, so that
+// three CTAs and their KV staging areas fit on a compute unit).
+template <int NT>
+struct MainShared {
+  union {
+    float score[NT][kChunk];
+  } u;
+  int32_t wcnt[NT][kWaves][2];
+  int32_t wbase[NT][kWaves][2];
+};
+
 // Candidate / tie append of one scored chunk [c0, cend) held in sh.u.score, for
 // the rows in row_mask.  Each wave counts its 256 keys with ballots; one
 // thread per row adds the CTA's totals to cnt[2t], cnt[2t+1] (global counters,
 // or the LDS counters of a repairing CTA) with one atomic per class, and the
 // waves then store their slots at the returned base plus their prefix.
-template <int NT>
+template <int NT, class Sh>
 __device__ void select_chunk(const SelectArgs& s, int b, int c0, int cend, const float (&thr)[NT],
-                             const int (&end)[NT], CtaShared<NT>& sh, int32_t* cnt, uint32_t row_mask) {
+                             const int (&end)[NT], Sh& sh, int32_t* cnt, uint32_t row_mask) {
   const int w = wave_id();
   const int lane = lane_id();
   const int tid = threadIdx.x;
@@ -1345,7 +1386,7 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
 // The finish kernel's CTA body: phase A over this CTA's tiles, then repair
 // items until nothing is left.
 template <int NT, int kItemKeys, class Src, class Args>
-__device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
+__device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh, v4i* stage) {
   const Ws ws{s.ws, a.batch, s.rows};
   const int tid = threadIdx.x;
   uint32_t tiles = 0;
@@ -1371,6 +1412,7 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     if (tid == 0) atomicAdd(ws.hdr() + 2, tiles);
   }
   Src src;
+  src.bind(stage);
   int idle = 0;
   while (true) {
     claim_item<NT, kItemKeys>(a, ws, idle, sh);
@@ -1471,9 +1513,17 @@ __device__ __forceinline__ void for_each_segment(const int32_t* seq_lens, int64_
 
 // ---------------------------------------------------------------- kernels
 
+// Waves per SIMD each variant is built for (VGPR budget 512 / waves).
 template <int NT>
-__global__ void __launch_bounds__(kThreads) logits_kernel(PagedArgs a, float* out, int64_t ld) {
+constexpr int kFusedWaves = NT == 1 ? 3 : (NT == 2 ? 2 : 1);
+
+
+template <int NT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
+logits_kernel(PagedArgs a, float* out, int64_t ld) {
+  __shared__ v4i stage[kWaves * kStageInt4];
   KvSource<NT> src;
+  src.bind(stage);
   const int lane = lane_id();
   for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kLogitsKeysPerCta, false,
                    [&](int b, int L, int k0, int k1, int) {
@@ -1493,7 +1543,7 @@ __global__ void __launch_bounds__(kThreads) logits_kernel(PagedArgs a, float* ou
 // request in chunks, each scored into LDS and selected from there.  Whatever
 // follows -- fit test, repair, ranges, Top-k -- is the finish kernel's.
 template <int NT, int kKeysPerCta, class Src, class Args>
-__device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh) {
+__device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, MainShared<NT>& sh, v4i* stage) {
   if (s.ws && blockIdx.x == 0) {
     // The finish kernel's header and job list start empty.  The last finish
     // kernel on this workspace may have left claim words behind (late claim
@@ -1520,6 +1570,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
     if (tid == 0) s.ws[3] = static_cast<uint32_t>(a.batch);
   }
   Src src;
+  src.bind(stage);
   const int lane = lane_id();
   for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kKeysPerCta, true,
                    [&](int b, int L, int k0, int k1, int) {
@@ -1546,33 +1597,32 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
   });
 }
 
-// Waves per SIMD each variant is built for (VGPR budget 512 / waves).
-template <int NT>
-constexpr int kFusedWaves = NT == 1 ? 3 : (NT == 2 ? 2 : 1);
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
 fused_kernel(PagedArgs a, SelectArgs s) {
-  __shared__ CtaShared<NT> sh;
-  select_body<NT, kFusedKeysPerCta, KvSource<NT>>(a, s, sh);
+  __shared__ MainShared<NT> sh;
+  __shared__ v4i stage[kWaves * kStageInt4];
+  select_body<NT, kFusedKeysPerCta, KvSource<NT>>(a, s, sh, stage);
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectArgs s) {
-  __shared__ CtaShared<NT> sh;
-  select_body<NT, kSelectKeysPerCta, LogitsSource<NT>>(a, s, sh);
+  __shared__ MainShared<NT> sh;
+  select_body<NT, kSelectKeysPerCta, LogitsSource<NT>>(a, s, sh, nullptr);
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) fused_finish_kernel(PagedArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
-  finish_body<NT, kFusedItemKeys, KvSource<NT>>(a, s, sh);
+  __shared__ v4i stage[kWaves * kStageInt4];
+  finish_body<NT, kFusedItemKeys, KvSource<NT>>(a, s, sh, stage);
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) select_finish_kernel(LogitsArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
-  finish_body<NT, kSelectItemKeys, LogitsSource<NT>>(a, s, sh);
+  finish_body<NT, kSelectItemKeys, LogitsSource<NT>>(a, s, sh, nullptr);
 }
 
 // ---------------------------------------------------------------- host side
