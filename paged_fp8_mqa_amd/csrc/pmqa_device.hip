@@ -41,6 +41,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupKeys = 64;                  // keys a wave scores per step
 constexpr int kChunk = kGroupKeys * kWaves * 4;  // keys a CTA scores per chunk
 constexpr int kStageInt4 = 512;  // a wave's KV staging area: 64 keys x 128 bytes
+constexpr int kWaveCand = 256;   // select kernel: a wave's pending candidates per row
+constexpr int kWaveTie = 64;     // select kernel: a wave's pending ties per row
 constexpr int kFewExtra = 3;   // final select by value walk when at most this many keys are left out
 
 struct PagedArgs {
@@ -468,16 +470,16 @@ struct CtaShared {
   int32_t next_stage;
 };
 
-// Shared memory of a select kernel CTA: the chunk's scores and the per-wave
-// counts of the slot append (the finish stage's structures stay out, so that
-// three CTAs and their KV staging areas fit on a compute unit).
+// Shared memory of a select kernel CTA: each wave's candidate and tie lists,
+// per row, of (key index, stored score bits) pairs not yet written to the
+// row's slots (the finish stage's structures stay out, so that three CTAs and
+// their KV staging areas fit on a compute unit).
 template <int NT>
 struct MainShared {
-  union {
-    float score[NT][kChunk];
-  } u;
-  int32_t wcnt[NT][kWaves][2];
-  int32_t wbase[NT][kWaves][2];
+  int2 cand[kWaves][NT][kWaveCand];
+  int2 tie[kWaves][NT][kWaveTie];
+  int32_t count[kWaves][NT][2];  // the waves' list lengths at the end
+  int32_t base[NT][2];           // the CTA's slot bases per row and class
 };
 
 // Candidate / tie append of one scored chunk [c0, cend) held in sh.u.score, for
@@ -1539,9 +1541,12 @@ logits_kernel(PagedArgs a, float* out, int64_t ld) {
   });
 }
 
-// The select kernels' CTA body: score and select keys [k0, k1) of the CTA's
-// request in chunks, each scored into LDS and selected from there.  Whatever
-// follows -- fit test, repair, ranges, Top-k -- is the finish kernel's.
+// The select kernels' CTA body: score keys [k0, k1) of the CTA's request and
+// select each wave's 64-key groups straight from the scores in registers onto
+// the wave's own lists, which reach the slots when nearly full (one counter
+// atomic per list) and at the end (one atomic per row and class for the whole
+// CTA, after the only barrier).  Whatever follows -- fit test,
+// repair, ranges, Top-k -- is the finish kernel's.
 template <int NT, int kKeysPerCta, class Src, class Args>
 __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, MainShared<NT>& sh, v4i* stage) {
   if (s.ws && blockIdx.x == 0) {
@@ -1572,28 +1577,105 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
   Src src;
   src.bind(stage);
   const int lane = lane_id();
+  const int w = wave_id();
   for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kKeysPerCta, true,
                    [&](int b, int L, int k0, int k1, int) {
     float thr[NT];
-    int end[NT];
+    int lim[NT];
+    int ncl[NT], ntl[NT];  // entries in this wave's lists (wave-uniform)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       thr[t] = s.thresholds[b * NT + t];
-      end[t] = max(0, L - NT + t + 1);
+      lim[t] = min(k1, max(0, L - NT + t + 1));
+      ncl[t] = 0;
+      ntl[t] = 0;
     }
+    // A wave's list of row t into the row's slots: one atomic per class for
+    // the base, then the pairs at base + i (dropped past the slots).
+    auto flush = [&](int t) {
+      const int r = b * NT + t;
+      int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
+      if (ncl[t]) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(s.counters + 2 * r, ncl[t]);
+        base = __shfl(base, 0);
+        for (int i = lane; i < ncl[t]; i += 64)
+          if (base + i < s.capacity) *reinterpret_cast<int2*>(slots + 2 * (s.top_k + base + i)) = sh.cand[w][t][i];
+        ncl[t] = 0;
+      }
+      if (ntl[t]) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(s.counters + 2 * r + 1, ntl[t]);
+        base = __shfl(base, 0);
+        for (int i = lane; i < ntl[t]; i += 64)
+          if (base + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - base - i)) = sh.tie[w][t][i];
+        ntl[t] = 0;
+      }
+    };
     src.init(a, b);
-    stream_keys<NT, true>(
+    stream_keys<NT, false>(
         src, k0, k1, L,
-        [&](int c, int p0, const float(&E)[NT]) {
+        [&](int, int p0, const float(&E)[NT]) {
+          // this group's candidates and ties onto the wave's lists, positions
+          // from the ballots
+          const int p = p0 + lane;
+          bool flushed = false;
 #pragma unroll
-          for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
+          for (int t = 0; t < NT; ++t) {
+            const float e = E[t];
+            const bool vis = p < lim[t];
+            const bool cand = vis && e > thr[t];
+            const bool tie = vis && !(e > thr[t]) && !(e < thr[t]);
+            const uint64_t mc = __ballot(cand);
+            const uint64_t mt = __ballot(tie);
+            const int nc = __popcll(mc);
+            const int nt = __popcll(mt);
+            if (ncl[t] + nc > kWaveCand || ntl[t] + nt > kWaveTie) {
+              flush(t);
+              flushed = true;
+            }
+            if (cand) sh.cand[w][t][ncl[t] + lanes_below(mc)] = int2{p, __float_as_int(enc_cand(e, thr[t]))};
+            if (tie) sh.tie[w][t][ntl[t] + lanes_below(mt)] = int2{p, __float_as_int(e - thr[t])};
+            ncl[t] += nc;
+            ntl[t] += nt;
+          }
+          // a flush's stores and atomics complete here, so that the loop's
+          // waits keep counting only key loads
+          if (flushed) wait_vm_done();
         },
-        [&](int c, int ce) {
-          select_chunk<NT>(s, b, c, ce, thr, end, sh, s.counters + 2 * b * NT, (1u << NT) - 1u);
-          // a known-empty memory counter here lets the next chunk's first
-          // scores wait for exactly their own loads
-          wait_vm_done();
-        });
+        [](int, int) {});
+    // the end: the four waves' lists of a row share one counter atomic per
+    // class (with every CTA finishing at about the same time, per-wave atomics
+    // pile up on the rows' counter words)
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        sh.count[w][t][0] = ncl[t];
+        sh.count[w][t][1] = ntl[t];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 2 * NT) {
+      const int t = threadIdx.x >> 1, cls = threadIdx.x & 1;
+      int tot = 0;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) tot += sh.count[q][t][cls];
+      sh.base[t][cls] = tot ? atomicAdd(s.counters + 2 * (b * NT + t) + cls, tot) : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      int bc = sh.base[t][0], bt = sh.base[t][1];
+      for (int q = 0; q < w; ++q) {
+        bc += sh.count[q][t][0];
+        bt += sh.count[q][t][1];
+      }
+      int32_t* slots = s.candidates + static_cast<int64_t>(b * NT + t) * (s.top_k + s.capacity) * 2;
+      for (int i = lane; i < ncl[t]; i += 64)
+        if (bc + i < s.capacity) *reinterpret_cast<int2*>(slots + 2 * (s.top_k + bc + i)) = sh.cand[w][t][i];
+      for (int i = lane; i < ntl[t]; i += 64)
+        if (bt + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - bt - i)) = sh.tie[w][t][i];
+    }
   });
 }
 
