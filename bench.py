@@ -157,7 +157,7 @@ def main():
     arrivals = torch.zeros(B, dtype=torch.int32, device=dev)
     ranges = torch.empty(2, R, dtype=torch.int32, device=dev)
     topk = torch.empty(R, wl.top_k, dtype=torch.int32, device=dev)
-    ws = pm.make_workspace(B, wl.next_n, dev)
+    ws = pm.make_workspace("fused" if args.path == "fused" else "indexer_topk", B, wl.next_n, wl.max_seq_len, dev)
     logits = None
     if args.path == "unfused":
         logits = torch.empty(R, pm.padded_seq_len(wl.max_seq_len), dtype=torch.float32, device=dev)

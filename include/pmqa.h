@@ -7,14 +7,16 @@
  *                               s_p * sum_h w[b*next_n+t, h] * relu(q[b,t,h,:] . k_p)
  *   pmqa_indexer_topk         one-pass threshold select over a logits matrix,
  *                             with last-CTA radix-select repair and Top-k finalize
- *   pmqa_fused_logits_select  both in one launch; no score matrix is written
+ *   pmqa_fused_logits_select  both in one pass over the KV pages; no score
+ *                             matrix is written
  *
  * Conventions shared by every entry point:
  *   - All buffer pointers are DEVICE pointers on the device that owns `stream`
  *     (a hipStream_t; NULL is the null stream).  The caller owns every buffer:
  *     the library never allocates, frees or synchronises the host, and each
- *     call is one kernel launch on `stream` (so it can be captured in a HIP
- *     graph).
+ *     call is one kernel launch on `stream`, two for a select with arrivals
+ *     (the select kernel, then the finish kernel), with no host round trip
+ *     (so it can be captured in a HIP graph).
  *   - Rows: R = batch_size * next_n, row r = b*next_n + t pairs with q[b, t].
  *     Row r sees KV positions 0 .. e_r - 1 with e_r = seq_lens[b] - next_n + t + 1
  *     (at least 0): slot t = next_n-1 is the newest draft position and sees the
@@ -156,22 +158,31 @@ pmqa_status pmqa_mqa_logits(
  *                top_k - 1), output: the row's exact Top-min(e_r, top_k) key
  *                indices in unspecified order, then -1 entries.  Among keys
  *                scoring exactly the k-th largest score any may be chosen.
- *   workspace    pmqa_workspace_bytes(batch_size, next_n) bytes of device
- *                memory, 8-byte aligned, required with arrivals (NULL
- *                without).  Zeroed by the caller before its first use; after
- *                that the library keeps state in it from call to call, so the
- *                caller leaves it alone (zeroing it again is harmless).  It holds the finish stage, a second kernel launched by
- *                the same call on the same stream with as many CTAs as fit on
- *                the device: each tile's fit test, then ranges and Top-k, or a
+ *   workspace    pmqa_workspace_bytes(which, batch_size, next_n, max_context)
+ *                bytes of device memory, 8-byte aligned, required with arrivals
+ *                (NULL without).  Zeroed by the caller before its first use;
+ *                after that the library keeps state in it from call to call,
+ *                so the caller leaves it alone (zeroing it again is harmless).
+ *                It holds the finish stage, a second kernel launched by the
+ *                same call on the same stream with as many CTAs as fit on the
+ *                device: each tile's fit test, then ranges and Top-k, or a
  *                repair job for its rows that do not fit (per-row radix
  *                histogram passes, then a collect pass into a per-row bucket
  *                buffer, or an exact re-select), split into items of a few
- *                thousand keys run grid-wide.  Calls that share a workspace
- *                must not run concurrently.
+ *                thousand keys run grid-wide.  The fused select's repair
+ *                computes a repaired row's scores once, in its first pass, and
+ *                keeps them in the workspace for the later passes.  Calls that
+ *                share a workspace must not run concurrently.
  */
 
-/* Bytes of the repair workspace for batch_size requests of next_n rows. */
-size_t pmqa_workspace_bytes(int32_t batch_size, int32_t next_n);
+/* Bytes of the finish-stage workspace of entry point `which` (1
+ * pmqa_indexer_topk, 2 pmqa_fused_logits_select) for batch_size requests of
+ * next_n rows and max_context keys: the finish stage's state (about 41 KB per
+ * row), plus for the fused select a score buffer of
+ * round_up(max_context, 64) floats per row, where the repair keeps the scores
+ * of the rows it repairs.  Returns 0 for an unknown `which` or a negative
+ * size. */
+size_t pmqa_workspace_bytes(int32_t which, int32_t batch_size, int32_t next_n, int32_t max_context);
 
 pmqa_status pmqa_check_select_args(
     const float* logits, int64_t logits_stride,

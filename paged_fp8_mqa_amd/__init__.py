@@ -14,7 +14,8 @@ Entry points mirror the C ABI in include/pmqa.h:
   fused_logits_select(q, kv_fused, weights, block_tables, seq_lens, max_context,
                thresholds, counters, candidates, capacity, top_k,
                arrivals=None, ranges=None, topk_idx=None, workspace=None)
-  make_workspace(batch_size, next_n)  -> zeroed repair workspace (required with arrivals)
+  make_workspace(which, batch_size, next_n, max_context)
+               -> zeroed finish-stage workspace (required with arrivals)
 """
 import ctypes
 import os
@@ -38,7 +39,7 @@ SIGNATURES = {
     "pmqa_padded_seq_len": ([_I32], _I32),
     "pmqa_min_block_table_width": ([_I32, _I32], _I32),
     "pmqa_keys_per_cta": ([_I32], _I32),
-    "pmqa_workspace_bytes": ([_I32, _I32], _SZ),
+    "pmqa_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
     "pmqa_check_logits_args": (_PAGED + [_I32, _P, _I64], ctypes.c_int),
     "pmqa_mqa_logits": (_PAGED + [_I32, _P, _I64, _P], ctypes.c_int),
     "pmqa_check_select_args": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT, ctypes.c_int),
@@ -79,19 +80,25 @@ def min_block_table_width(seq_len: int, block_size: int) -> int:
     return int(lib().pmqa_min_block_table_width(int(seq_len), int(block_size)))
 
 
-def workspace_bytes(batch_size: int, next_n: int) -> int:
-    return int(lib().pmqa_workspace_bytes(int(batch_size), int(next_n)))
+_WHICH = {"logits": 0, "indexer_topk": 1, "fused": 2}
 
 
-def make_workspace(batch_size: int, next_n: int, device="cuda"):
-    """A zeroed workspace for the finish stage; reuse it for later calls (the
-    library keeps state in it) and do not share it between concurrent calls."""
+def workspace_bytes(which: str, batch_size: int, next_n: int, max_context: int) -> int:
+    """Workspace bytes of entry point `which` ("indexer_topk" or "fused")."""
+    return int(lib().pmqa_workspace_bytes(_WHICH[which], int(batch_size), int(next_n), int(max_context)))
+
+
+def make_workspace(which: str, batch_size: int, next_n: int, max_context: int, device="cuda"):
+    """A zeroed workspace for the finish stage of entry point `which`; reuse it
+    for later calls (the library keeps state in it) and do not share it between
+    concurrent calls."""
     import torch
-    return torch.zeros(workspace_bytes(batch_size, next_n), dtype=torch.uint8, device=device)
+    n = workspace_bytes(which, batch_size, next_n, max_context)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def keys_per_cta(which: str) -> int:
-    return int(lib().pmqa_keys_per_cta({"logits": 0, "indexer_topk": 1, "fused": 2}[which]))
+    return int(lib().pmqa_keys_per_cta(_WHICH[which]))
 
 
 def _ptr(t):

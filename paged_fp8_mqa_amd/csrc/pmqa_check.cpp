@@ -32,7 +32,8 @@ pmqa_status check_paged_inputs(const uint8_t* q, const uint8_t* kv_fused, const 
   return PMQA_OK;
 }
 
-pmqa_status check_select_outputs(int64_t batch, int64_t rows, const float* thresholds, const int32_t* counters,
+pmqa_status check_select_outputs(int64_t batch, int64_t rows, int32_t max_context, bool fused,
+                                 const float* thresholds, const int32_t* counters,
                                  const int32_t* candidates, int32_t capacity, int32_t top_k,
                                  const int32_t* arrivals, const int32_t* ranges,
                                  const int32_t* topk_idx, const void* workspace, size_t workspace_bytes) {
@@ -50,7 +51,8 @@ pmqa_status check_select_outputs(int64_t batch, int64_t rows, const float* thres
   if (workspace) {
     if (!arrivals) return PMQA_ERR_NULL;
     if (!aligned(workspace, 8)) return PMQA_ERR_ALIGN;
-    if (static_cast<int64_t>(workspace_bytes) < 4 * workspace_words(batch, rows)) return PMQA_ERR_SHAPE;
+    if (static_cast<int64_t>(workspace_bytes) < 4 * workspace_words(batch, rows, max_context, fused))
+      return PMQA_ERR_SHAPE;
   }
   return PMQA_OK;
 }
@@ -87,9 +89,10 @@ int32_t pmqa_min_block_table_width(int32_t seq_len, int32_t block_size) {
   return static_cast<int32_t>(ceil_div(seq_len, block_size));
 }
 
-size_t pmqa_workspace_bytes(int32_t batch_size, int32_t next_n) {
-  if (batch_size < 0 || next_n < 1 || next_n > kMaxNextN) return 0;
-  return static_cast<size_t>(4 * workspace_words(batch_size, static_cast<int64_t>(batch_size) * next_n));
+size_t pmqa_workspace_bytes(int32_t which, int32_t batch_size, int32_t next_n, int32_t max_context) {
+  if ((which != 1 && which != 2) || batch_size < 0 || next_n < 1 || next_n > kMaxNextN || max_context < 0) return 0;
+  return static_cast<size_t>(
+      4 * workspace_words(batch_size, static_cast<int64_t>(batch_size) * next_n, max_context, which == 2));
 }
 
 int32_t pmqa_keys_per_cta(int32_t which) {
@@ -133,8 +136,8 @@ pmqa_status pmqa_check_select_args(const float* logits, int64_t logits_stride,
   if (batch_size < 0 || max_context < 0) return PMQA_ERR_SHAPE;
   if (next_n < 1 || next_n > kMaxNextN) return PMQA_ERR_UNSUPPORTED;
   const int64_t rows = static_cast<int64_t>(batch_size) * next_n;
-  pmqa_status st = check_select_outputs(batch_size, rows, thresholds, counters, candidates, capacity, top_k,
-                                        arrivals, ranges, topk_idx, workspace, workspace_bytes);
+  pmqa_status st = check_select_outputs(batch_size, rows, max_context, false, thresholds, counters, candidates,
+                                        capacity, top_k, arrivals, ranges, topk_idx, workspace, workspace_bytes);
   if (st != PMQA_OK || rows == 0) return st;
   if (!logits || !seq_lens) return PMQA_ERR_NULL;
   if (!aligned(logits, 4) || !aligned(seq_lens, 4)) return PMQA_ERR_ALIGN;
@@ -159,8 +162,8 @@ pmqa_status pmqa_check_fused_args(const uint8_t* q, const uint8_t* kv_fused, con
   if (st != PMQA_OK) return st;
   if (max_context < 0) return PMQA_ERR_SHAPE;
   const int64_t rows = static_cast<int64_t>(batch_size) * next_n;
-  st = check_select_outputs(batch_size, rows, thresholds, counters, candidates, capacity, top_k, arrivals,
-                            ranges, topk_idx, workspace, workspace_bytes);
+  st = check_select_outputs(batch_size, rows, max_context, true, thresholds, counters, candidates, capacity, top_k,
+                            arrivals, ranges, topk_idx, workspace, workspace_bytes);
   if (st != PMQA_OK || rows == 0) return st;
   if (block_table_width < ceil_div(max_context, block_size)) return PMQA_ERR_SHAPE;
   return PMQA_OK;

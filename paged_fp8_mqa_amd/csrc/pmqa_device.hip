@@ -80,6 +80,8 @@ struct SelectArgs {
   int32_t* topk_idx;
   uint32_t* ws;         // finish-stage workspace (with arrivals)
   int64_t ws_words;     // its size in 32-bit words
+  float* scores;        // fused repair: the workspace's score buffer, row r at scores + r * score_ld
+  int64_t score_ld;
   int32_t capacity;
   int32_t top_k;
   int32_t rows;
@@ -95,6 +97,22 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 // s_waitcnt vmcnt(0): this wave's loads and stores have completed.
 __device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Words shared between the CTAs of one kernel (on any XCD) are written with
+// agent-scope atomic stores, which the storing XCD's L2 writes through, and
+// read with agent-scope atomic loads.
+__device__ __forceinline__ uint32_t ld_ag(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_ag64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_wt(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_wt64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const int4 lo = *reinterpret_cast<const int4*>(p);
@@ -254,8 +272,10 @@ struct KvSource {
 };
 
 // Scores read from a logits matrix.  Columns at or past L are clamped to L - 1
-// (read, never used); only columns below each row's end are selected.
-template <int NT>
+// (read, never used); only columns below each row's end are selected.  The
+// kShared variant reads scores that other CTAs of the same kernel wrote (the
+// fused repair's score buffer): agent-scope loads, and only the rows in `mask`.
+template <int NT, bool kShared = false>
 struct LogitsSource {
   struct Group {
     float v[NT];
@@ -263,12 +283,20 @@ struct LogitsSource {
   const float* rows;
   int64_t ld;
   int lane;
+  uint32_t mask;
 
   __device__ __forceinline__ void bind(v4i*) {}
   __device__ __forceinline__ void init(const LogitsArgs& a, int b) {
     lane = lane_id();
     ld = a.ld;
     rows = a.logits + static_cast<int64_t>(b) * NT * a.ld;
+    mask = ~0u;
+  }
+  __device__ __forceinline__ void init_rows(const float* r, int64_t row_ld, uint32_t row_mask) {
+    lane = lane_id();
+    ld = row_ld;
+    rows = r;
+    mask = row_mask;
   }
   struct Pages {
     int L;
@@ -277,7 +305,13 @@ struct LogitsSource {
   __device__ __forceinline__ void load(Group& gr, const Pages& pg, int p0) const {
     const int p = min(p0 + lane, pg.L - 1);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) gr.v[t] = rows[t * ld + p];
+    for (int t = 0; t < NT; ++t) {
+      if (!kShared)
+        gr.v[t] = rows[t * ld + p];
+      else
+        gr.v[t] = (mask >> t) & 1u ? __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(rows + t * ld + p)))
+                                   : 0.f;
+    }
   }
   __device__ __forceinline__ void load(Group& gr, int p0, int L) const { load(gr, pages(p0, L), p0); }
   __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
@@ -949,13 +983,17 @@ __device__ void tile_outputs(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
 // i, i + grid, ...: the fit test, then either the tile's ranges and exact Top-k
 // or, for rows that do not fit, a repair job: the mask of those rows, their
 // state words, and the tile appended to the job list.  Phase B: every CTA runs
-// repair items.  A job runs in stages, each split into items of kItemKeys keys
-// of the request:
+// repair items.  A job runs in stages, each split into items of a few thousand
+// keys of the request:
 //   stages 1-3  radix histogram pass 0/1/2 (11/11/10 bits) of the repaired
 //               rows' keys, into per-row global histograms;
 //   stage 4     collect: keys above the selected bucket become candidates
 //               (stored raw), keys inside it go to a per-row bucket buffer;
 //   stage 5     select again at the now exact k-th largest score.
+// The fused repair computes the scores from the KV pages once, in stage 1, and
+// keeps the repaired rows' scores in the workspace's score buffer; its later
+// stages read them back (4 bytes a key instead of 132), as the repair of a
+// select over a logits matrix reads the matrix.
 // After a histogram pass the digit holding each row's k-th largest key is
 // found; if every row's bucket fits the bucket buffer the job moves to stage 4,
 // if every key bit is known to stage 5, else to the next pass.  An item is
@@ -975,12 +1013,14 @@ constexpr int kStageHist0 = 1;
 constexpr int kStageCollect = 4;
 constexpr int kStageSelect = 5;
 constexpr int kIdlePolls = 20000;  // bound on a CTA's polls without an item
+constexpr int kHdrBatch = 3, kHdrNextN = 4, kHdrMagic = 5;  // header words of the layout record
+constexpr uint32_t kLayoutMagic = 0x41514d50u;
 
 struct Ws {
   uint32_t* base;
   int batch, rows;
-  // [0] job list entries reserved, [2] tiles through phase A, [3] the batch
-  // whose layout the jobs use (the select kernel clears the header and the
+  // [0] job list entries reserved, [2] tiles through phase A, [3..5] the
+  // layout of the last finish kernel (the select kernel clears [0..2] and the
   // list before each finish kernel)
   __device__ uint32_t* hdr() const { return base; }
   __device__ uint32_t* list(int j) const { return base + 16 + j; }  // tile + 1, 0 until written
@@ -996,22 +1036,13 @@ struct Ws {
   }
 };
 
-__device__ __forceinline__ uint32_t ld_ag(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_ag64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_wt(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_wt64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int kItemKeys>
-__device__ __forceinline__ int items_of(int L) {
-  return max(1, static_cast<int>(ceil_div(L, kItemKeys)));
+// Items of a stage of a request of L keys: kRescoreItemKeys keys when the
+// scores are computed from the KV pages (stage 1 of the fused repair), else
+// kSelectItemKeys keys read back from a score row.
+template <bool kFused>
+__device__ __forceinline__ int stage_items(int stage, int L) {
+  const int keys = (kFused && stage == kStageHist0) ? kRescoreItemKeys : kSelectItemKeys;
+  return max(1, static_cast<int>(ceil_div(L, keys)));
 }
 
 // Phase A hands the rows of tile b in `mask` to phase B: their state words and
@@ -1242,12 +1273,62 @@ __device__ __noinline__ void job_finish(SelectArgs s, Ws ws, int b, int L, CtaSh
   if (tid >= 64 + 2 && tid < 64 + kJobWords) st_wt(ws.job(b) + (tid - 64), 0u);
 }
 
-// Repair item `idx` of stage `stage` of tile b's job: keys [c0, cend) scored
-// again, then their histogram, collect or select pass, then the stage
-// bookkeeping.
-template <int NT, int kItemKeys, class Src>
-__device__ void run_item(const Src& src, const SelectArgs& s, const Ws& ws, int b, int L, int stage, int idx,
-                         CtaShared<NT>& sh) {
+// Adds the LDS histograms sh.u.hist of pass `pass` of the rows in `mask` to
+// their global histograms (nonzero bins only).
+template <int NT>
+__device__ __forceinline__ void flush_hist(const Ws& ws, int b, int pass, uint32_t mask, CtaShared<NT>& sh) {
+  const int nb = 1 << pass_bits(pass);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(mask & (1u << t))) continue;
+    uint32_t* gh = ws.hist(b * NT + t);
+    for (int i = threadIdx.x; i < nb; i += kThreads) {
+      const uint32_t h = sh.u.hist[t][i];
+      if (h) atomicAdd(gh + i, h);
+    }
+  }
+}
+
+// Stage 1 of the fused repair, item idx: keys [c0, c1) of request b scored
+// again from the KV pages (the select kernel's loop and arithmetic, so the
+// scores are the same bits), the repaired rows' scores written to the score
+// buffer for the later passes, and their first radix histogram pass.
+template <int NT>
+__device__ void rescore_item(const PagedArgs& a, const SelectArgs& s, const Ws& ws, int b, int L, int idx,
+                             uint32_t mask, const int (&end)[NT], CtaShared<NT>& sh, v4i* lds) {
+  const int lane = lane_id();
+  const int shift = pass_shift(0);
+  for (int i = threadIdx.x; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
+  __syncthreads();
+  KvSource<NT> src;
+  src.bind(lds);
+  src.init(a, b);
+  float* rows = s.scores + static_cast<int64_t>(b) * NT * s.score_ld;
+  const int c0 = idx * kRescoreItemKeys;
+  const int c1 = min(c0 + kRescoreItemKeys, L);
+  stream_keys<NT, false>(
+      src, c0, c1, L,
+      [&](int, int p0, const float(&E)[NT]) {
+        const int p = p0 + lane;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (!(mask & (1u << t)) || p >= end[t]) continue;
+          st_wt(reinterpret_cast<uint32_t*>(rows + t * s.score_ld + p), __float_as_uint(E[t]));
+          atomicAdd(&sh.u.hist[t][radix_key(E[t]) >> shift], 1u);
+        }
+      },
+      [](int, int) {});
+  __syncthreads();
+  flush_hist<NT>(ws, b, 0, mask, sh);
+}
+
+// Repair item `idx` of stage `stage` of tile b's job: its keys' scores (read
+// back from the logits matrix or the score buffer, or for stage 1 of the fused
+// repair computed again), then their histogram, collect or select pass, then
+// the stage bookkeeping.
+template <int NT, bool kFused, class Args>
+__device__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b, int L, int stage, int idx,
+                         CtaShared<NT>& sh, v4i* lds) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const uint32_t mask = ld_ag(ws.job(b) + 2);
@@ -1264,57 +1345,64 @@ __device__ void run_item(const Src& src, const SelectArgs& s, const Ws& ws, int 
     thr2[t] = m ? __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r)) : 0.f;
     if (m) known = static_cast<int>(ld_ag(ws.row(r) + 2));
   }
-  const int c0 = idx * kItemKeys;
-  const int cend = min(c0 + kItemKeys, L);
-  if (stage < kStageCollect) {
-    // histogram straight from the scores in registers
-    const int pass = stage - kStageHist0;
-    const int shift = pass_shift(pass);
-    const int bits = pass_bits(pass);
-    const uint32_t low = (1u << bits) - 1u;
-    for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
-    __syncthreads();
-    for (int c = c0; c < cend; c += kChunk) {
-      const int ce = min(c + kChunk, cend);
-      score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
-        const int p = p0 + lane;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (!(mask & (1u << t)) || p >= min(ce, end[t])) continue;
-          const uint32_t key = radix_key(E[t]);
-          if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
-          atomicAdd(&sh.u.hist[t][(key >> shift) & low], 1u);
-        }
-      });
+  bool rescored = false;
+  if constexpr (kFused) {
+    if (stage == kStageHist0) {
+      rescore_item<NT>(a, s, ws, b, L, idx, mask, end, sh, lds);
+      rescored = true;
     }
-    __syncthreads();
+  }
+  if (!rescored) {
+    LogitsSource<NT, kFused> src;
+    if constexpr (kFused)
+      src.init_rows(s.scores + static_cast<int64_t>(b) * NT * s.score_ld, s.score_ld, mask);
+    else
+      src.init(a, b);
+    const int c0 = idx * kSelectItemKeys;
+    const int cend = min(c0 + kSelectItemKeys, L);
+    if (stage < kStageCollect) {
+      // histogram straight from the scores in registers
+      const int pass = stage - kStageHist0;
+      const int shift = pass_shift(pass);
+      const int bits = pass_bits(pass);
+      const uint32_t low = (1u << bits) - 1u;
+      for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
+      __syncthreads();
+      for (int c = c0; c < cend; c += kChunk) {
+        const int ce = min(c + kChunk, cend);
+        score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
+          const int p = p0 + lane;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (!(mask & (1u << t))) continue;
-      uint32_t* gh = ws.hist(b * NT + t);
-      for (int i = tid; i <= static_cast<int>(low); i += kThreads) {
-        const uint32_t h = sh.u.hist[t][i];
-        if (h) atomicAdd(gh + i, h);
+          for (int t = 0; t < NT; ++t) {
+            if (!(mask & (1u << t)) || p >= min(ce, end[t])) continue;
+            const uint32_t key = radix_key(E[t]);
+            if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
+            atomicAdd(&sh.u.hist[t][(key >> shift) & low], 1u);
+          }
+        });
       }
-    }
-  } else {
-    for (int c = c0; c < cend; c += kChunk) {
-      const int ce = min(c + kChunk, cend);
-      score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
+      __syncthreads();
+      flush_hist<NT>(ws, b, pass, mask, sh);
+    } else {
+      for (int c = c0; c < cend; c += kChunk) {
+        const int ce = min(c + kChunk, cend);
+        score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
-      });
-      __syncthreads();
-      if (stage == kStageCollect)
-        collect_chunk<NT>(s, ws, b, c, ce, end, pfx, known, sh, mask);
-      else
-        select_chunk<NT>(s, b, c, ce, thr2, end, sh, s.counters + 2 * b * NT, mask);
-      __syncthreads();
+          for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
+        });
+        __syncthreads();
+        if (stage == kStageCollect)
+          collect_chunk<NT>(s, ws, b, c, ce, end, pfx, known, sh, mask);
+        else
+          select_chunk<NT>(s, b, c, ce, thr2, end, sh, s.counters + 2 * b * NT, mask);
+        __syncthreads();
+      }
     }
   }
   wait_vm_done();
   __syncthreads();
-  if (tid == 0) sh.is_last = atomicAdd(ws.job(b) + 3 + stage, 1u) + 1 == static_cast<uint32_t>(items_of<kItemKeys>(L));
+  if (tid == 0)
+    sh.is_last = atomicAdd(ws.job(b) + 3 + stage, 1u) + 1 == static_cast<uint32_t>(stage_items<kFused>(stage, L));
   __syncthreads();
   if (!sh.is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -1329,7 +1417,7 @@ __device__ void run_item(const Src& src, const SelectArgs& s, const Ws& ws, int 
 // Wave 0 claims an item of a listed job; the result goes to sh.job: (tile,
 // stage, item), tile -1 when none is open but more may open, -2 when the CTA
 // should leave.
-template <int NT, int kItemKeys, class Args>
+template <int NT, bool kFused, class Args>
 __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>& sh) {
   if (wave_id() == 0) {
     const int lane = lane_id();
@@ -1339,7 +1427,7 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
     int got = -1, stage = 0, idx = 0;
     for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
       const int j = j0 + lane;
-      int b = 0, items = 0;
+      int b = 0, len = 0;
       uint64_t w = 0;
       bool unwritten = false;
       if (j < njobs) {
@@ -1348,11 +1436,12 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
         if (!unwritten) {
           b = min(static_cast<int>(e) - 1, ws.batch - 1);
           w = ld_ag64(ws.claim(b));
-          items = items_of<kItemKeys>(a.seq_lens[static_cast<int64_t>(b) * a.sl_stride]);
+          len = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
         }
       }
       const uint32_t st = static_cast<uint32_t>(w >> 32);
-      const bool open = st >= kStageHist0 && st <= kStageSelect && static_cast<uint32_t>(w) < static_cast<uint32_t>(items);
+      const bool open = st >= kStageHist0 && st <= kStageSelect &&
+                        static_cast<uint32_t>(w) < static_cast<uint32_t>(stage_items<kFused>(static_cast<int>(st), len));
       pending = pending || __ballot(unwritten || (st >= kStageHist0 && st < kStageCollect)) != 0;
       uint64_t m = __ballot(open);
       const int rot = static_cast<int>(blockIdx.x & 63);  // spread CTAs over the open jobs
@@ -1361,13 +1450,14 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
         const int l = __ffsll(static_cast<long long>(hi ? hi : m)) - 1;
         m &= ~(1ull << l);
         const int bl = __shfl(b, l);
-        const int il = __shfl(items, l);
+        const int ll = __shfl(len, l);
         unsigned long long old = 0;
         if (lane == 0) old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.claim(bl)), 1ull);
         old = __shfl(old, 0);
         const uint32_t st2 = static_cast<uint32_t>(old >> 32);
         const uint32_t i2 = static_cast<uint32_t>(old);
-        if (st2 >= kStageHist0 && st2 <= kStageSelect && i2 < static_cast<uint32_t>(il)) {
+        if (st2 >= kStageHist0 && st2 <= kStageSelect &&
+            i2 < static_cast<uint32_t>(stage_items<kFused>(static_cast<int>(st2), ll))) {
           got = bl;
           stage = static_cast<int>(st2);
           idx = static_cast<int>(i2);
@@ -1387,10 +1477,16 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
 
 // The finish kernel's CTA body: phase A over this CTA's tiles, then repair
 // items until nothing is left.
-template <int NT, int kItemKeys, class Src, class Args>
-__device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh, v4i* stage) {
+template <int NT, bool kFused, class Args>
+__device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh, v4i* lds) {
   const Ws ws{s.ws, a.batch, s.rows};
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) {
+    // the layout this call's state words use (read by the next select kernel)
+    st_wt(ws.hdr() + kHdrBatch, static_cast<uint32_t>(a.batch));
+    st_wt(ws.hdr() + kHdrNextN, static_cast<uint32_t>(NT));
+    st_wt(ws.hdr() + kHdrMagic, kLayoutMagic);
+  }
   uint32_t tiles = 0;
   for (int b = blockIdx.x; b < a.batch; b += gridDim.x, ++tiles) {
     const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
@@ -1413,11 +1509,9 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     __syncthreads();
     if (tid == 0) atomicAdd(ws.hdr() + 2, tiles);
   }
-  Src src;
-  src.bind(stage);
   int idle = 0;
   while (true) {
-    claim_item<NT, kItemKeys>(a, ws, idle, sh);
+    claim_item<NT, kFused>(a, ws, idle, sh);
     const int b = sh.job[0];
     const int stage = sh.job[1];
     const int idx = sh.job[2];
@@ -1429,10 +1523,36 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     }
     idle = 0;
     const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
-    src.init(a, b);
-    run_item<NT, kItemKeys>(src, s, ws, b, L, stage, idx, sh);
+    run_item<NT, kFused>(a, s, ws, b, L, stage, idx, sh, lds);
     __syncthreads();
   }
+}
+
+// Run by the select kernel, before any finish kernel of this call: the finish
+// stage's header and job list start empty.  Between calls the workspace holds
+// only zeros in its state words (every job clears its own) -- except where a
+// call laid it out differently: the fused repair's score buffer starts right
+// after the state words, so another batch size or next_n puts state words
+// where an earlier call kept scores.  The header records the layout the last
+// finish kernel used (written by that kernel, so every CTA here reads the same
+// value); when this call's layout differs, all CTAs clear its state words.
+template <int NT>
+__device__ void prepare_workspace(const SelectArgs& s, int batch) {
+  const Ws ws{s.ws, batch, s.rows};
+  const bool same = s.ws[kHdrMagic] == kLayoutMagic && s.ws[kHdrBatch] == static_cast<uint32_t>(batch) &&
+                    s.ws[kHdrNextN] == static_cast<uint32_t>(NT);
+  const int tid = threadIdx.x;
+  if (!same) {
+    const int64_t n = workspace_state_words(batch, s.rows) - 16;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + tid; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kThreads)
+      s.ws[16 + i] = 0u;
+  } else if (blockIdx.x == 0) {
+    // the job list (the claim words a late claim attempt incremented sit where
+    // this call's jobs are, and each publish rewrites its job's)
+    for (int i = tid; i < job_list_words(batch); i += kThreads) *ws.list(i) = 0u;
+  }
+  if (blockIdx.x == 0 && tid < 3) s.ws[tid] = 0u;
 }
 
 // ---------------------------------------------------------------- work items
@@ -1549,31 +1669,7 @@ logits_kernel(PagedArgs a, float* out, int64_t ld) {
 // repair, ranges, Top-k -- is the finish kernel's.
 template <int NT, int kKeysPerCta, class Src, class Args>
 __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, MainShared<NT>& sh, v4i* stage) {
-  if (s.ws && blockIdx.x == 0) {
-    // The finish kernel's header and job list start empty.  The last finish
-    // kernel on this workspace may have left claim words behind (late claim
-    // attempts); they sit where its batch put them, so they are cleared at
-    // those places first, in case this call's batch lays the workspace out
-    // differently.
-    const int tid = threadIdx.x;
-    const uint32_t old_batch = min(s.ws[3], 65535u);
-    const uint32_t old_jobs =
-        min(min(s.ws[0], old_batch), static_cast<uint32_t>(max<int64_t>(0, s.ws_words - 16)));
-    const int64_t old_jobs_at = 16 + job_list_words(old_batch);
-    for (uint32_t j = tid; j < old_jobs; j += kThreads) {
-      const uint32_t e = s.ws[16 + j];
-      const int64_t at = old_jobs_at + static_cast<int64_t>(kJobWords) * (static_cast<int64_t>(e) - 1);
-      if (e != 0u && e <= old_batch && at + 2 <= s.ws_words) {
-        s.ws[at] = 0u;
-        s.ws[at + 1] = 0u;
-      }
-    }
-    __syncthreads();
-    const int64_t words = min<int64_t>(s.ws_words, 16 + max(job_list_words(old_batch), job_list_words(a.batch)));
-    for (int64_t i = tid; i < words; i += kThreads) s.ws[i] = 0u;
-    __syncthreads();
-    if (tid == 0) s.ws[3] = static_cast<uint32_t>(a.batch);
-  }
+  if (s.ws) prepare_workspace<NT>(s, a.batch);
   Src src;
   src.bind(stage);
   const int lane = lane_id();
@@ -1698,13 +1794,13 @@ template <int NT>
 __global__ void __launch_bounds__(kThreads) fused_finish_kernel(PagedArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
   __shared__ v4i stage[kWaves * kStageInt4];
-  finish_body<NT, kFusedItemKeys, KvSource<NT>>(a, s, sh, stage);
+  finish_body<NT, true>(a, s, sh, stage);
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) select_finish_kernel(LogitsArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
-  finish_body<NT, kSelectItemKeys, LogitsSource<NT>>(a, s, sh, nullptr);
+  finish_body<NT, false>(a, s, sh, nullptr);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1805,7 +1901,8 @@ int resident_ctas(const void* fn) {
 }
 
 SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int32_t top_k, int32_t* arr,
-                       int32_t* ranges, int32_t* topk, int32_t rows, void* workspace, size_t workspace_bytes) {
+                       int32_t* ranges, int32_t* topk, int32_t batch, int32_t rows, int32_t max_context, bool fused,
+                       void* workspace, size_t workspace_bytes) {
   SelectArgs s;
   s.thresholds = thr;
   s.counters = cnt;
@@ -1815,6 +1912,8 @@ SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int
   s.topk_idx = topk;
   s.ws = arr ? static_cast<uint32_t*>(workspace) : nullptr;
   s.ws_words = s.ws ? static_cast<int64_t>(workspace_bytes / 4) : 0;
+  s.scores = s.ws && fused ? reinterpret_cast<float*>(s.ws + workspace_state_words(batch, rows)) : nullptr;
+  s.score_ld = score_stride(max_context);
   s.capacity = cap;
   s.top_k = top_k;
   s.rows = rows;
@@ -1908,7 +2007,8 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
   if (st != PMQA_OK) return st;
   const LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, 0, static_cast<int32_t>(gx)};
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   static_cast<int32_t>(rows), workspace, workspace_bytes);
+                                   batch_size, static_cast<int32_t>(rows), max_context, false, workspace,
+                                   workspace_bytes);
   st = launch_k<SelectK>(next_n, true, hs, a, s);
   if (st == PMQA_OK && s.ws) st = launch_k<SelectFinishK>(next_n, false, hs, a, s);
   return st != PMQA_OK ? st : launched();
@@ -1939,7 +2039,8 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   static_cast<int32_t>(rows), workspace, workspace_bytes);
+                                   batch_size, static_cast<int32_t>(rows), max_context, true, workspace,
+                                   workspace_bytes);
   st = launch_k<FusedK>(next_n, true, hs, a, s);
   if (st == PMQA_OK && s.ws) st = launch_k<FusedFinishK>(next_n, false, hs, a, s);
   return st != PMQA_OK ? st : launched();

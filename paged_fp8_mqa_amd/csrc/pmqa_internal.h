@@ -18,19 +18,29 @@ constexpr int kRadixBins = 2048;        // 11-bit radix digits: 11 + 11 + 10
 constexpr int kFinalizeLds = 4096;      // keys a CTA keeps in LDS for a final radix select
 constexpr int kJobWords = 16;           // repair workspace: words per tile job
 constexpr int kRowWords = 16;           // repair workspace: words per row state
-constexpr int kFusedItemKeys = 1024;    // keys per repair item, recomputed from the KV pages
-constexpr int kSelectItemKeys = 4096;   // keys per repair item, re-read from a logits row
+constexpr int kRescoreItemKeys = 2048;  // keys per repair item recomputed from the KV pages
+constexpr int kSelectItemKeys = 4096;   // keys per repair item read back as scores
+
+constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Repair job list: one word per tile, rounded up to keep the jobs 64-byte aligned.
 constexpr int64_t job_list_words(int64_t batch) { return (batch + 15) / 16 * 16; }
 
-// Repair workspace size in words: a header, the job list, one job per tile,
-// and per row its state, a radix histogram and a bucket buffer of (index,
-// score) pairs.
-constexpr int64_t workspace_words(int64_t batch, int64_t rows) {
+// Floats per row of the fused repair's score buffer (256-byte rows).
+constexpr int64_t score_stride(int64_t max_context) { return ceil_div(max_context, 64) * 64; }
+
+// Repair workspace: a header, the job list, one job per tile, and per row its
+// state, a radix histogram and a bucket buffer of (index, score) pairs; this
+// much is the finish stage's state (in words).
+constexpr int64_t workspace_state_words(int64_t batch, int64_t rows) {
   return 16 + job_list_words(batch) + kJobWords * batch + (kRowWords + kRadixBins + 2 * kFinalizeLds) * rows;
 }
 
-constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// The whole workspace in words: the fused select's repair adds a score buffer
+// of score_stride(max_context) floats per row (the scores of a repaired row,
+// computed once from the KV pages and read back by the later passes).
+constexpr int64_t workspace_words(int64_t batch, int64_t rows, int64_t max_context, bool fused) {
+  return workspace_state_words(batch, rows) + (fused ? rows * score_stride(max_context) : 0);
+}
 
 }  // namespace pmqa

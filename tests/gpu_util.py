@@ -39,7 +39,7 @@ def run_logits(wl, d, out_cols=None, max_seq_len=None):
 
 class SelectBuffers:
     def __init__(self, rows, batch, top_k, capacity, thresholds, device="cuda", arrivals=True, topk=True,
-                 workspace=None):
+                 workspace=None, which="fused", max_context=0):
         self.top_k, self.capacity = top_k, capacity
         self.thr = torch.as_tensor(np.asarray(thresholds, dtype=np.float32)).to(device)
         self.thr_in = self.thr.clone()
@@ -49,7 +49,8 @@ class SelectBuffers:
         self.ranges = torch.full((2, rows), SENTINEL_I32, dtype=torch.int32, device=device) if arrivals else None
         self.topk = torch.full((rows, top_k), SENTINEL_I32, dtype=torch.int32, device=device) if (arrivals and topk) else None
         self.ws = None if not arrivals else (
-            workspace if workspace is not None else pm.make_workspace(batch, rows // batch if batch else 1, device))
+            workspace if workspace is not None else
+            pm.make_workspace(which, batch, rows // batch if batch else 1, max_context, device))
 
     def kwargs(self):
         return dict(thresholds=self.thr, counters=self.counters, candidates=self.cand, capacity=self.capacity,
@@ -69,16 +70,18 @@ class SelectBuffers:
 
 def run_fused(wl, d, thresholds, capacity=None, arrivals=True, topk=True, max_context=None):
     cap = wl.capacity if capacity is None else capacity
-    sb = SelectBuffers(wl.rows, wl.batch, wl.top_k, cap, thresholds, arrivals=arrivals, topk=topk)
     mc = wl.max_seq_len if max_context is None else max_context
+    sb = SelectBuffers(wl.rows, wl.batch, wl.top_k, cap, thresholds, arrivals=arrivals, topk=topk, which="fused",
+                       max_context=mc)
     pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], mc, **sb.kwargs())
     return sb.host()
 
 
 def run_select(wl, logits, thresholds, capacity=None, arrivals=True, topk=True, max_context=None):
     cap = wl.capacity if capacity is None else capacity
-    sb = SelectBuffers(wl.rows, wl.batch, wl.top_k, cap, thresholds, arrivals=arrivals, topk=topk)
     mc = wl.max_seq_len if max_context is None else max_context
+    sb = SelectBuffers(wl.rows, wl.batch, wl.top_k, cap, thresholds, arrivals=arrivals, topk=topk,
+                       which="indexer_topk", max_context=mc)
     sl = torch.from_numpy(wl.seq_lens).to("cuda")
     pm.indexer_topk(logits, sl, wl.next_n, mc, **sb.kwargs())
     return sb.host()

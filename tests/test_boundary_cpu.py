@@ -29,10 +29,16 @@ def test_library_exports_every_declared_function():
 
 def test_workspace_bytes():
     lib = pm.lib()
-    b2 = lib.pmqa_workspace_bytes(2, 3)
-    assert b2 > 0 and b2 % 8 == 0 and b2 <= WS
-    assert lib.pmqa_workspace_bytes(64, 1) < lib.pmqa_workspace_bytes(64, 2)
-    assert lib.pmqa_workspace_bytes(2, 0) == 0 and lib.pmqa_workspace_bytes(-1, 1) == 0
+    b2 = lib.pmqa_workspace_bytes(1, 2, 3, 8000)
+    f2 = lib.pmqa_workspace_bytes(2, 2, 3, 8000)
+    assert b2 > 0 and b2 % 8 == 0 and f2 <= WS
+    # the fused select adds a score buffer of round_up(max_context, 64) floats per row
+    assert f2 - b2 == 6 * 8000 * 4
+    assert lib.pmqa_workspace_bytes(2, 2, 3, 8001) - b2 == 6 * 8064 * 4
+    assert lib.pmqa_workspace_bytes(1, 2, 3, 1) == b2  # the select over a logits matrix keeps none
+    assert lib.pmqa_workspace_bytes(1, 64, 1, 0) < lib.pmqa_workspace_bytes(1, 64, 2, 0)
+    assert lib.pmqa_workspace_bytes(1, 2, 0, 10) == 0 and lib.pmqa_workspace_bytes(1, -1, 1, 10) == 0
+    assert lib.pmqa_workspace_bytes(0, 2, 3, 10) == 0 and lib.pmqa_workspace_bytes(2, 2, 3, -1) == 0
 
 
 def test_helpers():
@@ -132,6 +138,8 @@ FUSED_CASES = [
     ({}, OK),
     ({"q": None}, NULL), ({"thr": None}, NULL), ({"rng": None}, NULL),
     ({"arr": None, "rng": None, "topk": P(), "ws": None}, NULL), ({"ws": None}, NULL), ({"wsb": 100}, SHAPE),
+    # enough for the select over a logits matrix, not for the fused score buffer
+    ({"wsb": 1 << 18}, SHAPE), ({"wsb": 1 << 18, "mc": 100, "btw": 4}, OK),
     ({"H": 128}, UNSUP), ({"bs": 48}, UNSUP),
     ({"btw": 249}, SHAPE), ({"k": 0}, SHAPE), ({"cap": 10}, SHAPE),
     ({"kv": P(4)}, ALIGN), ({"cnt": P(4)}, ALIGN),

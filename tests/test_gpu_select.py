@@ -201,7 +201,7 @@ def test_fused_repeated_calls_reuse_arrivals():
     thr = _sigma_thresholds(ref, ends, wl.top_k, "inf")
     d = dev(wl)
     import gpu_util
-    sb = gpu_util.SelectBuffers(wl.rows, wl.batch, wl.top_k, wl.capacity, thr)
+    sb = gpu_util.SelectBuffers(wl.rows, wl.batch, wl.top_k, wl.capacity, thr, max_context=wl.max_seq_len)
     first = None
     for it in range(3):
         sb.counters.zero_()
@@ -217,15 +217,19 @@ def test_fused_repeated_calls_reuse_arrivals():
 
 @pytest.mark.gpu
 def test_workspace_reused_across_batch_sizes():
-    """One workspace, sized for the larger call, serves calls of different batch
-    sizes in turn, every row repaired each time (the finish stage keeps state
-    in the workspace between calls, laid out by each call's batch)."""
+    """One workspace, sized for the largest call, serves calls of different
+    batch sizes and next_n in turn, every row repaired each time (the finish
+    stage keeps state in the workspace between calls, laid out by each call's
+    batch and next_n, and the fused repair's score buffer sits right after that
+    state, so each layout's scores cover another layout's state words)."""
     wa = W.small_random(51, [3000, 5000], 2, 64, top_k=128, capacity=256)
     wb = W.small_random(52, [900, 4000, 0, 2500, 7000], 2, 64, top_k=128, capacity=256)
-    ws = torch.zeros(max(pm.workspace_bytes(wa.batch, 2), pm.workspace_bytes(wb.batch, 2)), dtype=torch.uint8,
-                     device="cuda")
+    wc = W.small_random(53, [6000, 2100, 4500], 1, 64, top_k=128, capacity=256)
+    wls = (wa, wb, wc)
+    ws = torch.zeros(max(pm.workspace_bytes("fused", w.batch, w.next_n, w.max_seq_len) for w in wls),
+                     dtype=torch.uint8, device="cuda")
     import gpu_util
-    for wl in (wa, wb, wa, wb):
+    for wl in (wa, wb, wa, wc, wb, wc, wa):
         ref, tau = _oracle_rows(wl, None)
         ends = oracle.row_ends(wl.seq_lens, wl.next_n)
         thr = _sigma_thresholds(ref, ends, wl.top_k, "inf")
