@@ -522,7 +522,7 @@ struct MainShared {
 // or the LDS counters of a repairing CTA) with one atomic per class, and the
 // waves then store their slots at the returned base plus their prefix.
 template <int NT, class Sh>
-__device__ void select_chunk(const SelectArgs& s, int b, int c0, int cend, const float (&thr)[NT],
+__device__ __forceinline__ void select_chunk(const SelectArgs& s, int b, int c0, int cend, const float (&thr)[NT],
                              const int (&end)[NT], Sh& sh, int32_t* cnt, uint32_t row_mask) {
   const int w = wave_id();
   const int lane = lane_id();
@@ -691,7 +691,7 @@ __device__ __forceinline__ void cta_find_digit(const uint32_t* hist, int nb, uin
 // key in sh.pfx[0] and, in sh.krem[0], how many entries equal to it the k
 // largest hold; resets sh.pos[0..1] for the caller.
 template <int NT, class KeyOf>
-__device__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, CtaShared<NT>& sh) {
+__device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   uint32_t pf = 0u, krem = static_cast<uint32_t>(k);
   for (int pass = 0; pass < 3; ++pass) {
@@ -781,7 +781,7 @@ __device__ __forceinline__ void cta_min_sum(uint32_t& a, uint32_t& b, CtaShared<
 // current value and finds the next larger one.  Returns the key and how many
 // of its copies the k largest hold.
 template <int NT>
-__device__ void few_extra_select(const uint32_t* keys, int n, int k, CtaShared<NT>& sh, uint32_t& kstar,
+__device__ __forceinline__ void few_extra_select(const uint32_t* keys, int n, int k, CtaShared<NT>& sh, uint32_t& kstar,
                                  int& n_eq) {
   const int tid = threadIdx.x;
   const int d = n - k;  // keys to leave out
@@ -830,7 +830,7 @@ __device__ void few_extra_select(const uint32_t* keys, int n, int k, CtaShared<N
 // candidates by decoded score, found by a 3-pass radix select over keys kept in
 // LDS (read from the slots once).  Entries past k are -1.
 template <int NT>
-__device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, CtaShared<NT>& sh) {
+__device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   const int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
   int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
@@ -937,7 +937,7 @@ __device__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float t
 // Fit test of tile b from its counters: fills sh.nc, sh.nt, sh.thr and returns
 // the mask of rows that do not fit.
 template <int NT>
-__device__ uint32_t tile_fit(const SelectArgs& s, int b, const int (&end)[NT], const float (&thr_in)[NT],
+__device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, int b, const int (&end)[NT], const float (&thr_in)[NT],
                              CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.repair_mask = 0u;
@@ -957,21 +957,15 @@ __device__ uint32_t tile_fit(const SelectArgs& s, int b, const int (&end)[NT], c
   return sh.repair_mask;
 }
 
-// ranges and Top-k finalize of tile b, from sh.nc/nt/thr.
+// ranges and Top-k finalize of row r (k = min(e_r, top_k)) from its final
+// candidate count nc, tie count nt and threshold th.
 template <int NT>
-__device__ void tile_outputs(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
-  const int tid = threadIdx.x;
-  int end[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) end[t] = max(0, L - NT + t + 1);
-  if (tid < NT) {
-    const int r = b * NT + tid;
-    s.ranges[r] = s.top_k - min(sh.nt[tid], s.top_k);
-    s.ranges[s.rows + r] = s.top_k + min(sh.nc[tid], s.capacity);
+__device__ __forceinline__ void row_outputs(const SelectArgs& s, int r, int k, int nc, int nt, float th, CtaShared<NT>& sh) {
+  if (threadIdx.x == 0) {
+    s.ranges[r] = s.top_k - min(nt, s.top_k);
+    s.ranges[s.rows + r] = s.top_k + min(nc, s.capacity);
   }
-  if (s.topk_idx) {
-    for (int t = 0; t < NT; ++t) finalize_topk<NT>(s, b * NT + t, min(end[t], s.top_k), sh.nc[t], sh.thr[t], sh);
-  }
+  if (s.topk_idx) finalize_topk<NT>(s, r, k, nc, th, sh);
   __syncthreads();
 }
 
@@ -979,31 +973,37 @@ __device__ void tile_outputs(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
 
 // Each tile is finished by a second kernel, launched right after the select
 // kernel on the same stream, so it starts with every slot and counter of the
-// main pass in memory and the memory system idle.  Phase A: CTA i takes tiles
-// i, i + grid, ...: the fit test, then either the tile's ranges and exact Top-k
-// or, for rows that do not fit, a repair job: the mask of those rows, their
-// state words, and the tile appended to the job list.  Phase B: every CTA runs
+// main pass in memory and the memory system idle.  Phase A: CTA i takes rows
+// i, i + grid, ...: the fit test of the row's tile, then either the row's
+// ranges and exact Top-k or, from the CTA with the tile's first row that does
+// not fit, a repair job: the mask of those rows, their state words, and the
+// tile appended to the job list.  Phase B: every CTA runs
 // repair items.  A job runs in stages, each split into items of a few thousand
 // keys of the request:
 //   stages 1-3  radix histogram pass 0/1/2 (11/11/10 bits) of the repaired
 //               rows' keys, into per-row global histograms;
 //   stage 4     collect: keys above the selected bucket become candidates
 //               (stored raw), keys inside it go to a per-row bucket buffer;
-//   stage 5     select again at the now exact k-th largest score.
+//   stage 5     select again at the now exact k-th largest score;
+//   stage 6     one item per row: for a collected row, the exact k-th largest
+//               key from its bucket (the bucket's keys appended, the collected
+//               candidates re-encoded against it), then the row's ranges and
+//               Top-k.
 // The fused repair computes the scores from the KV pages once, in stage 1, and
 // keeps the repaired rows' scores in the workspace's score buffer; its later
 // stages read them back (4 bytes a key instead of 132), as the repair of a
 // select over a logits matrix reads the matrix.
 // After a histogram pass the digit holding each row's k-th largest key is
 // found; if every row's bucket fits the bucket buffer the job moves to stage 4,
-// if every key bit is known to stage 5, else to the next pass.  An item is
+// if every key bit is known to stage 5, else to the next pass; stages 4 and 5
+// lead to stage 6.  An item is
 // claimed by a 64-bit fetch-and-add on the job's (stage, next item) word: a
 // returned index below the stage's item count is the caller's item, a larger
 // one claims nothing.  Whoever completes a stage's last item runs the stage
-// change, which rewrites the word to (next stage, 0), or after stage 4 or 5
-// finishes the tile.  A CTA with no open item waits (a bounded number of polls)
+// change, which rewrites the word to (next stage, 0), or after stage 6 clears
+// the job's words.  A CTA with no open item waits (a bounded number of polls)
 // while some CTA is still in phase A, a listed job is not yet written, or a job
-// is in a histogram stage (its change opens new items), and leaves otherwise;
+// is in a stage before 6 (its change opens new items), and leaves otherwise;
 // the wait only adds hands, since each job is carried to its end by the CTA that
 // completes each of its stages.  Shared words are written with agent-scope
 // atomic (write-through) stores or atomic adds and read with agent-scope atomic
@@ -1012,6 +1012,7 @@ __device__ void tile_outputs(SelectArgs s, int b, int L, CtaShared<NT>& sh) {
 constexpr int kStageHist0 = 1;
 constexpr int kStageCollect = 4;
 constexpr int kStageSelect = 5;
+constexpr int kStageRows = 6;
 constexpr int kIdlePolls = 20000;  // bound on a CTA's polls without an item
 constexpr int kHdrBatch = 3, kHdrNextN = 4, kHdrMagic = 5;  // header words of the layout record
 constexpr uint32_t kLayoutMagic = 0x41514d50u;
@@ -1019,7 +1020,7 @@ constexpr uint32_t kLayoutMagic = 0x41514d50u;
 struct Ws {
   uint32_t* base;
   int batch, rows;
-  // [0] job list entries reserved, [2] tiles through phase A, [3..5] the
+  // [0] job list entries reserved, [2] rows through phase A, [3..5] the
   // layout of the last finish kernel (the select kernel clears [0..2] and the
   // list before each finish kernel)
   __device__ uint32_t* hdr() const { return base; }
@@ -1029,18 +1030,23 @@ struct Ws {
   __device__ uint64_t* claim(int b) const { return reinterpret_cast<uint64_t*>(job(b)); }
   // [0] digit prefix [1] rank left [2] bits known [3] bucket count
   __device__ uint32_t* row(int r) const { return job(batch) + kRowWords * r; }
-  __device__ uint32_t* hist(int r) const { return job(batch) + kRowWords * rows + static_cast<int64_t>(kRadixBins) * r; }
+  // copy c of row r's radix histogram (items add into copy idx % kHistCopies,
+  // which spreads the atomics of a pass over kHistCopies times more lines)
+  __device__ uint32_t* hist(int r, int c) const {
+    return job(batch) + kRowWords * rows + static_cast<int64_t>(kRadixBins) * (kHistCopies * r + c);
+  }
   __device__ int32_t* bucket(int r) const {
-    return reinterpret_cast<int32_t*>(job(batch) + (kRowWords + kRadixBins) * rows) +
+    return reinterpret_cast<int32_t*>(job(batch) + (kRowWords + kHistCopies * kRadixBins) * rows) +
            static_cast<int64_t>(2) * kFinalizeLds * r;
   }
 };
 
 // Items of a stage of a request of L keys: kRescoreItemKeys keys when the
 // scores are computed from the KV pages (stage 1 of the fused repair), else
-// kSelectItemKeys keys read back from a score row.
-template <bool kFused>
+// kSelectItemKeys keys read back from a score row; one per row in stage 6.
+template <int NT, bool kFused>
 __device__ __forceinline__ int stage_items(int stage, int L) {
+  if (stage == kStageRows) return NT;
   const int keys = (kFused && stage == kStageHist0) ? kRescoreItemKeys : kSelectItemKeys;
   return max(1, static_cast<int>(ceil_div(L, keys)));
 }
@@ -1048,7 +1054,7 @@ __device__ __forceinline__ int stage_items(int stage, int L) {
 // Phase A hands the rows of tile b in `mask` to phase B: their state words and
 // the claim word first, then (once those are complete) the list entry.
 template <int NT>
-__device__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int (&end)[NT], uint32_t mask) {
+__device__ __forceinline__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int (&end)[NT], uint32_t mask) {
   const int tid = threadIdx.x;
   if (tid < NT && (mask & (1u << tid))) st_wt(ws.row(b * NT + tid) + 1, static_cast<uint32_t>(min(end[tid], s.top_k)));
   if (tid == 0) {
@@ -1067,7 +1073,7 @@ __device__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int 
 // above the bucket are appended as candidates (raw scores; re-encoded once the
 // threshold is known), keys inside it go to the row's bucket buffer.
 template <int NT>
-__device__ void collect_chunk(const SelectArgs& s, const Ws& ws, int b, int c0, int cend, const int (&end)[NT],
+__device__ __forceinline__ void collect_chunk(const SelectArgs& s, const Ws& ws, int b, int c0, int cend, const int (&end)[NT],
                               const uint32_t (&pfx)[NT], int known, CtaShared<NT>& sh, uint32_t mask) {
   const int w = wave_id();
   const int lane = lane_id();
@@ -1143,18 +1149,36 @@ __device__ void collect_chunk(const SelectArgs& s, const Ws& ws, int b, int c0, 
 // Stage change after histogram pass `pass` of tile b's job (run by the CTA that
 // completed the pass's last item).
 template <int NT>
-__device__ __noinline__ void job_next_stage(SelectArgs s, Ws ws, int b, int pass, uint32_t mask, CtaShared<NT>& sh) {
+__device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws, int b, int pass, uint32_t mask, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   const int wave = wave_id();
   const int lane = lane_id();
   const int shift = pass_shift(pass);
   const int bits = pass_bits(pass);
   const int nb = 1 << bits;
-  if (wave < NT && (mask & (1u << wave))) {
-    uint32_t* gh = ws.hist(b * NT + wave);
-    for (int i = lane; i < nb; i += 64) {
-      sh.u.hist[wave][i] = ld_ag(gh + i);
-      st_wt(gh + i, 0u);
+  // each row's histogram: the sum of its copies, which are cleared for the next
+  // pass (all of a thread's loads in flight at once)
+  for (int t = 0; t < NT; ++t) {
+    if (!(mask & (1u << t))) continue;
+    uint32_t* gh = ws.hist(b * NT + t, 0);
+    constexpr int kJ = kRadixBins / kThreads / 2;  // bins of a thread per half
+#pragma unroll 1
+    for (int i0 = 0; i0 < nb; i0 += kJ * kThreads) {
+      uint32_t v[kJ][kHistCopies];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c) v[j][c] = ld_ag(gh + c * kRadixBins + i0 + j * kThreads + tid);
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        uint32_t sum = 0u;
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c) {
+          sum += v[j][c];
+          if (v[j][c]) st_wt(gh + c * kRadixBins + i0 + j * kThreads + tid, 0u);
+        }
+        sh.u.hist[t][i0 + j * kThreads + tid] = sum;
+      }
     }
   }
   __syncthreads();
@@ -1197,91 +1221,100 @@ __device__ __noinline__ void job_next_stage(SelectArgs s, Ws ws, int b, int pass
   if (tid == 0) st_wt64(ws.claim(b), static_cast<uint64_t>(next) << 32);
 }
 
-// After the collect stage: each repaired row's exact k-th largest key among its
-// bucket (kept in LDS), the bucket's candidates and ties appended, the raw
-// candidates re-encoded against the new threshold.
+// Row r after the collect stage: its exact k-th largest key among its bucket
+// (kept in LDS), the bucket's candidates and ties appended, the raw candidates
+// re-encoded against the new threshold.  Leaves the row's final candidate and
+// tie counts and threshold in sh.nc[0], sh.nt[0], sh.thr[0] (and in counters
+// and thresholds).
 template <int NT>
-__device__ __noinline__ void job_resolve_buckets(SelectArgs s, Ws ws, int b, uint32_t mask, CtaShared<NT>& sh) {
+__device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, int r, CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   const int stride = s.top_k + s.capacity;
-  for (int t = 0; t < NT; ++t) {
-    if (!(mask & (1u << t))) continue;
-    const int r = b * NT + t;
-    uint32_t* row = ws.row(r);
-    // the bucket holds the keys of one digit, at most kFinalizeLds by the stage
-    // change's test
-    const int nin = min(static_cast<int>(ld_ag(row + 3)), kFinalizeLds);
-    const int krem = static_cast<int>(ld_ag(row + 1));
-    const int nabove = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
-    int32_t* bucket = ws.bucket(r);
-    uint32_t* keys = sh.u.fin.key;
-    #pragma unroll 1
-    for (int i = tid; i < nin; i += kThreads) keys[i] = radix_key(__int_as_float(bucket[2 * i + 1]));
-    __syncthreads();
-    cta_radix_select([&](int i) { return keys[i]; }, nin, krem, sh.u.fin.hist, sh);
-    const uint32_t kstar = sh.pfx[0];
-    const float t2 = key_to_float(kstar);
-    int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
-    // each bucket entry is cleared once used (the workspace stays zeroed)
-    #pragma unroll 1
-    for (int i = tid; i < nin; i += kThreads) {
-      const uint32_t key = keys[i];
-      const int32_t idx = bucket[2 * i];
-      const float e = __int_as_float(bucket[2 * i + 1]);
-      st_wt64(reinterpret_cast<uint64_t*>(bucket + 2 * i), 0u);
-      if (key > kstar) {
-        const int k = nabove + atomicAdd(&sh.pos[0], 1);
-        if (k < s.capacity) store_pair(slots + 2 * (s.top_k + k), idx, enc_cand(e, t2));
-      } else if (key == kstar) {
-        const int k = atomicAdd(&sh.pos[1], 1);
-        if (k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), idx, e - t2);
-      }
+  uint32_t* row = ws.row(r);
+  // the bucket holds the keys of one digit, at most kFinalizeLds by the stage
+  // change's test
+  const int nin = min(static_cast<int>(ld_ag(row + 3)), kFinalizeLds);
+  const int krem = static_cast<int>(ld_ag(row + 1));
+  const int nabove = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+  int32_t* bucket = ws.bucket(r);
+  uint32_t* keys = sh.u.fin.key;
+  #pragma unroll 1
+  for (int i = tid; i < nin; i += kThreads) keys[i] = radix_key(__int_as_float(bucket[2 * i + 1]));
+  __syncthreads();
+  cta_radix_select([&](int i) { return keys[i]; }, nin, krem, sh.u.fin.hist, sh);
+  const uint32_t kstar = sh.pfx[0];
+  const float t2 = key_to_float(kstar);
+  int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
+  #pragma unroll 1
+  for (int i = tid; i < nin; i += kThreads) {
+    const uint32_t key = keys[i];
+    const int32_t idx = bucket[2 * i];
+    const float e = __int_as_float(bucket[2 * i + 1]);
+    if (key > kstar) {
+      const int k = nabove + atomicAdd(&sh.pos[0], 1);
+      if (k < s.capacity) store_pair(slots + 2 * (s.top_k + k), idx, enc_cand(e, t2));
+    } else if (key == kstar) {
+      const int k = atomicAdd(&sh.pos[1], 1);
+      if (k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), idx, e - t2);
     }
-    #pragma unroll 1
-    for (int i = tid; i < min(nabove, s.capacity); i += kThreads) {
-      int32_t* sl = slots + 2 * (s.top_k + i);
-      store_pair(sl, sl[0], enc_cand(__int_as_float(sl[1]), t2));
-    }
-    __syncthreads();
-    if (tid == 0) {
-      st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, static_cast<uint32_t>(nabove + sh.pos[0]));
-      st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(sh.pos[1]));
-      st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
-    }
-    __syncthreads();
   }
-}
-
-// Last step of a job: ranges and Top-k of the whole tile, then the job's words
-// cleared for the next call (all but the claim word, which late claim attempts
-// may still increment; the next publish of the tile rewrites it).
-template <int NT>
-__device__ __noinline__ void job_finish(SelectArgs s, Ws ws, int b, int L, CtaShared<NT>& sh) {
-  const int tid = threadIdx.x;
+  #pragma unroll 1
+  for (int i = tid; i < min(nabove, s.capacity); i += kThreads) {
+    int32_t* sl = slots + 2 * (s.top_k + i);
+    store_pair(sl, sl[0], enc_cand(__int_as_float(sl[1]), t2));
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int nc = nabove + sh.pos[0], nt = sh.pos[1];
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, static_cast<uint32_t>(nc));
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(nt));
+    st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
+    sh.nc[0] = nc;
+    sh.nt[0] = nt;
+    sh.thr[0] = t2;
+  }
+  // this CTA's slot stores complete before the Top-k reads the slots back
   wait_vm_done();
   __syncthreads();
-  if (tid < NT) {
-    const int r = b * NT + tid;
-    sh.nc[tid] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
-    sh.nt[tid] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
-    sh.thr[tid] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
+}
+
+// Stage 6 item t of tile b's job: row t, if repaired, resolved (after a
+// collect) and given its ranges and Top-k.  The row's state words are cleared
+// for the next call.
+template <int NT>
+__device__ __forceinline__ void row_end_item(const SelectArgs& s, const Ws& ws, int b, int L, int t, uint32_t mask,
+                             CtaShared<NT>& sh) {
+  if (!(mask & (1u << t))) return;
+  const int tid = threadIdx.x;
+  const int r = b * NT + t;
+  // the collect stage's stores (other CTAs, written through) become visible
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (ld_ag(ws.row(r) + 2) < 32u) {
+    resolve_row<NT>(s, ws, r, sh);
+  } else {
+    // stage 5 selected the row again at its exact threshold
+    if (tid == 0) {
+      sh.nc[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+      sh.nt[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
+      sh.thr[0] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  tile_outputs<NT>(s, b, L, sh);
-  if (tid < NT)
-    for (int i = 0; i < 4; ++i) st_wt(ws.row(b * NT + tid) + i, 0u);
-  if (tid >= 64 + 2 && tid < 64 + kJobWords) st_wt(ws.job(b) + (tid - 64), 0u);
+  const int k = min(max(0, L - NT + t + 1), s.top_k);
+  row_outputs<NT>(s, r, k, sh.nc[0], sh.nt[0], sh.thr[0], sh);
+  if (tid < 4) st_wt(ws.row(r) + tid, 0u);
 }
 
 // Adds the LDS histograms sh.u.hist of pass `pass` of the rows in `mask` to
-// their global histograms (nonzero bins only).
+// copy `copy` of their global histograms (nonzero bins only).
 template <int NT>
-__device__ __forceinline__ void flush_hist(const Ws& ws, int b, int pass, uint32_t mask, CtaShared<NT>& sh) {
+__device__ __forceinline__ void flush_hist(const Ws& ws, int b, int pass, uint32_t mask, int copy,
+                                           CtaShared<NT>& sh) {
   const int nb = 1 << pass_bits(pass);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (!(mask & (1u << t))) continue;
-    uint32_t* gh = ws.hist(b * NT + t);
+    uint32_t* gh = ws.hist(b * NT + t, copy);
     for (int i = threadIdx.x; i < nb; i += kThreads) {
       const uint32_t h = sh.u.hist[t][i];
       if (h) atomicAdd(gh + i, h);
@@ -1294,7 +1327,7 @@ __device__ __forceinline__ void flush_hist(const Ws& ws, int b, int pass, uint32
 // scores are the same bits), the repaired rows' scores written to the score
 // buffer for the later passes, and their first radix histogram pass.
 template <int NT>
-__device__ void rescore_item(const PagedArgs& a, const SelectArgs& s, const Ws& ws, int b, int L, int idx,
+__device__ __forceinline__ void rescore_item(const PagedArgs& a, const SelectArgs& s, const Ws& ws, int b, int L, int idx,
                              uint32_t mask, const int (&end)[NT], CtaShared<NT>& sh, v4i* lds) {
   const int lane = lane_id();
   const int shift = pass_shift(0);
@@ -1319,7 +1352,7 @@ __device__ void rescore_item(const PagedArgs& a, const SelectArgs& s, const Ws& 
       },
       [](int, int) {});
   __syncthreads();
-  flush_hist<NT>(ws, b, 0, mask, sh);
+  flush_hist<NT>(ws, b, 0, mask, idx % kHistCopies, sh);
 }
 
 // Repair item `idx` of stage `stage` of tile b's job: its keys' scores (read
@@ -1327,7 +1360,7 @@ __device__ void rescore_item(const PagedArgs& a, const SelectArgs& s, const Ws& 
 // repair computed again), then their histogram, collect or select pass, then
 // the stage bookkeeping.
 template <int NT, bool kFused, class Args>
-__device__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b, int L, int stage, int idx,
+__device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b, int L, int stage, int idx,
                          CtaShared<NT>& sh, v4i* lds) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -1345,14 +1378,18 @@ __device__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b
     thr2[t] = m ? __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r)) : 0.f;
     if (m) known = static_cast<int>(ld_ag(ws.row(r) + 2));
   }
-  bool rescored = false;
+  bool done = false;
+  if (stage == kStageRows) {
+    row_end_item<NT>(s, ws, b, L, idx, mask, sh);
+    done = true;
+  }
   if constexpr (kFused) {
     if (stage == kStageHist0) {
       rescore_item<NT>(a, s, ws, b, L, idx, mask, end, sh, lds);
-      rescored = true;
+      done = true;
     }
   }
-  if (!rescored) {
+  if (!done) {
     LogitsSource<NT, kFused> src;
     if constexpr (kFused)
       src.init_rows(s.scores + static_cast<int64_t>(b) * NT * s.score_ld, s.score_ld, mask);
@@ -1382,7 +1419,7 @@ __device__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b
         });
       }
       __syncthreads();
-      flush_hist<NT>(ws, b, pass, mask, sh);
+      flush_hist<NT>(ws, b, pass, mask, idx % kHistCopies, sh);
     } else {
       for (int c = c0; c < cend; c += kChunk) {
         const int ce = min(c + kChunk, cend);
@@ -1402,15 +1439,19 @@ __device__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b
   wait_vm_done();
   __syncthreads();
   if (tid == 0)
-    sh.is_last = atomicAdd(ws.job(b) + 3 + stage, 1u) + 1 == static_cast<uint32_t>(stage_items<kFused>(stage, L));
+    sh.is_last = atomicAdd(ws.job(b) + 3 + stage, 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
   __syncthreads();
   if (!sh.is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (stage < kStageCollect) {
     job_next_stage<NT>(s, ws, b, stage - kStageHist0, mask, sh);
+  } else if (stage < kStageRows) {
+    if (tid == 0) st_wt64(ws.claim(b), static_cast<uint64_t>(kStageRows) << 32);
   } else {
-    if (stage == kStageCollect) job_resolve_buckets<NT>(s, ws, b, mask, sh);
-    job_finish<NT>(s, ws, b, L, sh);
+    // the job is done: its words cleared for the next call (all but the claim
+    // word, which late claim attempts may still increment; the next publish of
+    // the tile rewrites it)
+    if (tid >= 2 && tid < kJobWords) st_wt(ws.job(b) + tid, 0u);
   }
 }
 
@@ -1418,12 +1459,12 @@ __device__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b
 // stage, item), tile -1 when none is open but more may open, -2 when the CTA
 // should leave.
 template <int NT, bool kFused, class Args>
-__device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>& sh) {
+__device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>& sh) {
   if (wave_id() == 0) {
     const int lane = lane_id();
     // (a workspace that was not left zeroed gives wrong results, not stray accesses)
     const int njobs = min(static_cast<int>(ld_ag(ws.hdr())), ws.batch);
-    bool pending = ld_ag(ws.hdr() + 2) < static_cast<uint32_t>(ws.batch);
+    bool pending = ld_ag(ws.hdr() + 2) < static_cast<uint32_t>(ws.rows);
     int got = -1, stage = 0, idx = 0;
     for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
       const int j = j0 + lane;
@@ -1440,9 +1481,9 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
         }
       }
       const uint32_t st = static_cast<uint32_t>(w >> 32);
-      const bool open = st >= kStageHist0 && st <= kStageSelect &&
-                        static_cast<uint32_t>(w) < static_cast<uint32_t>(stage_items<kFused>(static_cast<int>(st), len));
-      pending = pending || __ballot(unwritten || (st >= kStageHist0 && st < kStageCollect)) != 0;
+      const bool open = st >= kStageHist0 && st <= kStageRows &&
+                        static_cast<uint32_t>(w) < static_cast<uint32_t>(stage_items<NT, kFused>(static_cast<int>(st), len));
+      pending = pending || __ballot(unwritten || (st >= kStageHist0 && st < kStageRows)) != 0;
       uint64_t m = __ballot(open);
       const int rot = static_cast<int>(blockIdx.x & 63);  // spread CTAs over the open jobs
       while (m) {
@@ -1456,8 +1497,8 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
         old = __shfl(old, 0);
         const uint32_t st2 = static_cast<uint32_t>(old >> 32);
         const uint32_t i2 = static_cast<uint32_t>(old);
-        if (st2 >= kStageHist0 && st2 <= kStageSelect &&
-            i2 < static_cast<uint32_t>(stage_items<kFused>(static_cast<int>(st2), ll))) {
+        if (st2 >= kStageHist0 && st2 <= kStageRows &&
+            i2 < static_cast<uint32_t>(stage_items<NT, kFused>(static_cast<int>(st2), ll))) {
           got = bl;
           stage = static_cast<int>(st2);
           idx = static_cast<int>(i2);
@@ -1475,7 +1516,7 @@ __device__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>
   __syncthreads();
 }
 
-// The finish kernel's CTA body: phase A over this CTA's tiles, then repair
+// The finish kernel's CTA body: phase A over this CTA's rows, then repair
 // items until nothing is left.
 template <int NT, bool kFused, class Args>
 __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh, v4i* lds) {
@@ -1487,27 +1528,30 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     st_wt(ws.hdr() + kHdrNextN, static_cast<uint32_t>(NT));
     st_wt(ws.hdr() + kHdrMagic, kLayoutMagic);
   }
-  uint32_t tiles = 0;
-  for (int b = blockIdx.x; b < a.batch; b += gridDim.x, ++tiles) {
+  uint32_t done_rows = 0;
+  for (int r = blockIdx.x; r < s.rows; r += gridDim.x, ++done_rows) {
+    const int b = r / NT, t = r - b * NT;
     const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
     int end[NT];
     float thr[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      end[t] = max(0, L - NT + t + 1);
-      thr[t] = s.thresholds[b * NT + t];
+    for (int u = 0; u < NT; ++u) {
+      end[u] = max(0, L - NT + u + 1);
+      thr[u] = s.thresholds[b * NT + u];
     }
+    // every CTA working on a row of tile b finds the same mask; the one with
+    // its lowest row publishes the job
     const uint32_t mask = tile_fit<NT>(s, b, end, thr, sh);
-    if (mask)
+    if (!(mask & (1u << t)))
+      row_outputs<NT>(s, r, min(end[t], s.top_k), sh.nc[t], sh.nt[t], sh.thr[t], sh);
+    else if ((mask & ((1u << t) - 1u)) == 0u)
       publish_job<NT>(s, ws, b, end, mask);
-    else
-      tile_outputs<NT>(s, b, L, sh);
     __syncthreads();
   }
-  if (tiles) {
+  if (done_rows) {
     wait_vm_done();
     __syncthreads();
-    if (tid == 0) atomicAdd(ws.hdr() + 2, tiles);
+    if (tid == 0) atomicAdd(ws.hdr() + 2, done_rows);
   }
   int idle = 0;
   while (true) {
@@ -1518,7 +1562,9 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     __syncthreads();
     if (b == -2) break;
     if (b < 0) {
-      __builtin_amdgcn_s_sleep(8);
+      // back off (up to about 2 us between polls), so that waiting CTAs keep
+      // their loads off the job words the working ones update
+      for (int i = 0; i < min(idle, 16); ++i) __builtin_amdgcn_s_sleep(8);
       continue;
     }
     idle = 0;
@@ -1537,7 +1583,7 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
 // finish kernel used (written by that kernel, so every CTA here reads the same
 // value); when this call's layout differs, all CTAs clear its state words.
 template <int NT>
-__device__ void prepare_workspace(const SelectArgs& s, int batch) {
+__device__ __forceinline__ void prepare_workspace(const SelectArgs& s, int batch) {
   const Ws ws{s.ws, batch, s.rows};
   const bool same = s.ws[kHdrMagic] == kLayoutMagic && s.ws[kHdrBatch] == static_cast<uint32_t>(batch) &&
                     s.ws[kHdrNextN] == static_cast<uint32_t>(NT);

@@ -15,6 +15,7 @@ constexpr int kFusedKeysPerCta = 1024;
 constexpr int kSelectKeysPerCta = 4096;
 constexpr int kOutColumnGranule = 256;  // padded_seq_len rounding
 constexpr int kRadixBins = 2048;        // 11-bit radix digits: 11 + 11 + 10
+constexpr int kHistCopies = 8;          // repair workspace: copies of a row's radix histogram
 constexpr int kFinalizeLds = 4096;      // keys a CTA keeps in LDS for a final radix select
 constexpr int kJobWords = 16;           // repair workspace: words per tile job
 constexpr int kRowWords = 16;           // repair workspace: words per row state
@@ -30,10 +31,11 @@ constexpr int64_t job_list_words(int64_t batch) { return (batch + 15) / 16 * 16;
 constexpr int64_t score_stride(int64_t max_context) { return ceil_div(max_context, 64) * 64; }
 
 // Repair workspace: a header, the job list, one job per tile, and per row its
-// state, a radix histogram and a bucket buffer of (index, score) pairs; this
-// much is the finish stage's state (in words).
+// state, kHistCopies copies of a radix histogram and a bucket buffer of (index,
+// score) pairs; this much is the finish stage's state (in words).
 constexpr int64_t workspace_state_words(int64_t batch, int64_t rows) {
-  return 16 + job_list_words(batch) + kJobWords * batch + (kRowWords + kRadixBins + 2 * kFinalizeLds) * rows;
+  return 16 + job_list_words(batch) + kJobWords * batch +
+         (kRowWords + kHistCopies * kRadixBins + 2 * kFinalizeLds) * rows;
 }
 
 // The whole workspace in words: the fused select's repair adds a score buffer

@@ -139,7 +139,7 @@ FUSED_CASES = [
     ({"q": None}, NULL), ({"thr": None}, NULL), ({"rng": None}, NULL),
     ({"arr": None, "rng": None, "topk": P(), "ws": None}, NULL), ({"ws": None}, NULL), ({"wsb": 100}, SHAPE),
     # enough for the select over a logits matrix, not for the fused score buffer
-    ({"wsb": 1 << 18}, SHAPE), ({"wsb": 1 << 18, "mc": 100, "btw": 4}, OK),
+    ({"wsb": "select"}, SHAPE), ({"wsb": "select+", "mc": 100, "btw": 4}, OK),
     ({"H": 128}, UNSUP), ({"bs": 48}, UNSUP),
     ({"btw": 249}, SHAPE), ({"k": 0}, SHAPE), ({"cap": 10}, SHAPE),
     ({"kv": P(4)}, ALIGN), ({"cnt": P(4)}, ALIGN),
@@ -148,6 +148,12 @@ FUSED_CASES = [
 
 @pytest.mark.parametrize("kw,want", FUSED_CASES)
 def test_check_fused_args(kw, want):
+    kw = dict(kw)
+    if isinstance(kw.get("wsb"), str):
+        # the indexer_topk workspace for the same shape (plus room for the
+        # 100-key score buffer with "select+")
+        need = pm.lib().pmqa_workspace_bytes(1, 2, 3, 8000)
+        kw["wsb"] = need + (6 * 128 * 4 if kw["wsb"] == "select+" else 0)
     assert pm.lib().pmqa_check_fused_args(*fused_args(**kw)) == want
 
 
