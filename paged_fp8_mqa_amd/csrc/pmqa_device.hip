@@ -95,6 +95,9 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
 
+// Wavefront minimum (the device library's DPP reduction); every lane gets it.
+extern "C" __device__ uint64_t __ockl_wfred_min_u64(uint64_t);
+
 // s_waitcnt vmcnt(0): this wave's loads and stores have completed.
 __device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -498,10 +501,12 @@ struct CtaShared {
   int32_t nt[NT];
   float thr[NT];
   uint32_t repair_mask;
+  int32_t len;
   int32_t is_last;
   int32_t pos[2];
   int32_t job[3];      // claimed repair item: tile (or -1: none open, -2: leave), stage, index
   int32_t next_stage;
+  uint64_t low[kFewExtra][kWaves];  // few_extra_topk: each wave's smallest (key, position) pair per round
 };
 
 // Shared memory of a select kernel CTA: each wave's candidate and tie lists,
@@ -751,105 +756,125 @@ __device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, Ct
   b = bb + ib - b;
 }
 
-// CTA-wide min of a and sum of b (two barriers; every thread gets both).
+// Top-k of a row whose nc candidates exceed k by d = nc - k <= kFewExtra (the
+// pairs of the slots below npre already in sh.u.fin.idx / sh.u.fin.key): the
+// d smallest candidates (by radix key, ties by slot position) are left out
+// and every other candidate's index is written in slot order.  Each of the d
+// rounds finds the smallest pair not yet left out: a tree over each thread's
+// keys, the wavefront minimum (DPP), and the four waves' minima exchanged
+// through LDS with one barrier; the output then shifts each index past the
+// left-out positions before it, so the stores stay coalesced.
 template <int NT>
-__device__ __forceinline__ void cta_min_sum(uint32_t& a, uint32_t& b, CtaShared<NT>& sh) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    a = min(a, static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), off)));
-    b += static_cast<uint32_t>(__shfl_xor(static_cast<int>(b), off));
-  }
-  __syncthreads();
-  if (lane_id() == 0) {
-    sh.wtot[wave_id()] = a;
-    sh.wcnt[0][wave_id()][0] = static_cast<int32_t>(b);
-  }
-  __syncthreads();
-  a = sh.wtot[0];
-  b = static_cast<uint32_t>(sh.wcnt[0][0][0]);
-#pragma unroll
-  for (int q = 1; q < kWaves; ++q) {
-    a = min(a, sh.wtot[q]);
-    b += static_cast<uint32_t>(sh.wcnt[0][q][0]);
-  }
-}
-
-// The k-th largest of the n radix keys keys[0..n) in LDS (n <= kFinalizeLds)
-// when n - k is small:
-// it is the (n - k + 1)-th smallest, found by walking the distinct key values
-// upwards from the minimum, each step one pass that counts the copies of the
-// current value and finds the next larger one.  Returns the key and how many
-// of its copies the k largest hold.
-template <int NT>
-__device__ __forceinline__ void few_extra_select(const uint32_t* keys, int n, int k, CtaShared<NT>& sh, uint32_t& kstar,
-                                 int& n_eq) {
+__device__ __forceinline__ void few_extra_topk(const int32_t* cand, int32_t* out, int nc, int d, float th, int npre,
+                                               CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
-  const int d = n - k;  // keys to leave out
-  // this thread's keys (n <= kFinalizeLds), in registers for all the steps
   constexpr int kPer = kFinalizeLds / kThreads;
-  uint32_t kv[kPer];
-  uint32_t m = 0xffffffffu, unused = 0u;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = u * kThreads + tid;
-    kv[u] = i < n ? keys[i] : 0xffffffffu;
-    m = min(m, kv[u]);
-  }
-  cta_min_sum(m, unused, sh);
-  int below = 0;   // keys smaller than m
-  int copies = 0;  // copies of m
-  // every step passes at least one key, so m reaches the (d+1)-th smallest
-  // within d + 1 steps
-  for (int step = 0; step <= d; ++step) {
-    uint32_t next = 0xffffffffu, cnt = 0u;
+  uint32_t* key = sh.u.fin.key;
+  int32_t* idx = sh.u.fin.idx;
+  if (npre < nc) {
+    // the pairs not in LDS yet, all of a thread's loads in flight
+    int2 v[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const bool valid = u * kThreads + tid < n;
-      cnt += (valid && kv[u] == m) ? 1u : 0u;
-      if (valid && kv[u] > m) next = min(next, kv[u]);
+      const int i = u * kThreads + tid;
+      if (i >= npre && i < nc) v[u] = *reinterpret_cast<const int2*>(cand + 2 * i);
     }
-    cta_min_sum(next, cnt, sh);
-    copies = static_cast<int>(cnt);
-    if (below + copies > d) break;  // m is the (d+1)-th smallest
-    below += copies;
-    m = next;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kThreads + tid;
+      if (i >= npre && i < nc) {
+        idx[i] = v[u].x;
+        key[i] = static_cast<uint32_t>(v[u].y);
+      }
+    }
   }
-  kstar = m;
-  // the k largest hold every key above m and the copies of m beyond the
-  // d - below that are left out
-  n_eq = copies - (d - below);
-  if (tid == 0) {
-    sh.pos[0] = 0;
-    sh.pos[1] = 0;
+  __syncthreads();
+  // (LDS reads at clamped indices, unconditional, so that they are all in
+  // flight at once instead of one branch and wait each)
+  uint32_t kv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) kv[u] = key[min(u * kThreads + tid, nc - 1)];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) kv[u] = radix_key(dec_cand(__uint_as_float(kv[u]), th));
+  uint32_t p0 = 0xffffffffu, p1 = 0xffffffffu, p2 = 0xffffffffu;
+#pragma unroll 1
+  for (int j = 0; j < d; ++j) {
+    // this thread's smallest pair still in, by a tree over its keys
+    uint64_t m[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t i = static_cast<uint32_t>(u * kThreads + tid);
+      m[u] = (i < static_cast<uint32_t>(nc) && i != p0 && i != p1 && i != p2)
+                 ? ((static_cast<uint64_t>(kv[u]) << 32) | i)
+                 : ~0ull;
+    }
+#pragma unroll
+    for (int w = kPer / 2; w > 0; w >>= 1)
+#pragma unroll
+      for (int u = 0; u < w; ++u) m[u] = min(m[u], m[u + w]);
+    const uint64_t wm = __ockl_wfred_min_u64(m[0]);
+    if (lane_id() == 0) sh.low[j][wave_id()] = wm;
+    __syncthreads();
+    uint64_t g = sh.low[j][0];
+#pragma unroll
+    for (int q = 1; q < kWaves; ++q) g = min(g, sh.low[j][q]);
+    const uint32_t pj = static_cast<uint32_t>(g);
+    if (j == 0) p0 = pj;
+    else if (j == 1) p1 = pj;
+    else p2 = pj;
+  }
+  int32_t iv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) iv[u] = idx[min(u * kThreads + tid, nc - 1)];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const uint32_t i = static_cast<uint32_t>(u * kThreads + tid);
+    if (i < static_cast<uint32_t>(nc) && i != p0 && i != p1 && i != p2)
+      out[i - (i > p0) - (i > p1) - (i > p2)] = iv[u];
   }
   __syncthreads();
 }
 
 // Exact Top-k of one fitting row from its slots: every candidate when there are
 // at most k, topped up with ties from the tie slots; otherwise the k largest
-// candidates by decoded score, found by a 3-pass radix select over keys kept in
-// LDS (read from the slots once).  Entries past k are -1.
+// candidates by decoded score -- all but the few smallest when at most
+// kFewExtra are left out, else by a 3-pass radix select over keys kept in LDS
+// (read from the slots once).  Entries past k are -1.  The first npre
+// candidate pairs may be in sh.u.fin.idx / sh.u.fin.key already.
 template <int NT>
-__device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, CtaShared<NT>& sh) {
+__device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, int npre,
+                                              CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
+  constexpr int kPer = kFinalizeLds / kThreads;
   const int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
   int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
   for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
   if (nc <= k) {
-    // every candidate, then ties; eight loads in flight per thread
-    for (int i0 = 0; i0 < k; i0 += 8 * kThreads) {
-      int32_t v[8];
+    // every candidate, then ties; all of a thread's loads in flight at once
+    // (the preloaded candidates read from LDS at clamped indices, unconditional)
+    const bool lds = nc <= npre;
+    for (int i0 = 0; i0 < k; i0 += kPer * kThreads) {
+      int32_t v[kPer];
+      if (lds && nc > 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kThreads + tid;
-        if (i < k) v[u] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
+        for (int u = 0; u < kPer; ++u) v[u] = sh.u.fin.idx[min(i0 + u * kThreads + tid, nc - 1)];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kPer; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        if (i < k && (i >= nc || !lds))
+          v[u] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
         const int i = i0 + u * kThreads + tid;
         if (i < k) out[i] = v[u];
       }
     }
+    return;
+  }
+  if (nc - k <= kFewExtra && nc <= kFinalizeLds) {
+    few_extra_topk<NT>(slots + 2 * s.top_k, out, nc, nc - k, th, npre, sh);
     return;
   }
   const bool in_lds = nc <= kFinalizeLds;
@@ -881,15 +906,9 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
   auto key_of = [&](int i) -> uint32_t {
     return in_lds ? keys[i] : radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
   };
-  uint32_t kstar;
-  int n_eq;
-  if (in_lds && nc - k <= kFewExtra) {
-    few_extra_select(keys, nc, k, sh, kstar, n_eq);
-  } else {
-    cta_radix_select(key_of, nc, k, hist, sh);
-    kstar = sh.pfx[0];
-    n_eq = static_cast<int>(sh.krem[0]);
-  }
+  cta_radix_select(key_of, nc, k, hist, sh);
+  const uint32_t kstar = sh.pfx[0];
+  const int n_eq = static_cast<int>(sh.krem[0]);
   const int n_gt = k - n_eq;
   if (in_lds) {
     // each thread's keys above k* (and equal to it) counted, one CTA-wide
@@ -934,23 +953,51 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
   __syncthreads();
 }
 
-// Fit test of tile b from its counters: fills sh.nc, sh.nt, sh.thr and returns
-// the mask of rows that do not fit.
+// Fit test of tile b (its request's length at *len) from its counters: fills
+// sh.nc, sh.nt, sh.thr and sh.len and returns the mask of rows that do not
+// fit.  With npre > 0 it also loads the first npre candidate pairs of row
+// r_pre into sh.u.fin.idx / sh.u.fin.key (index, score bits), as
+// finalize_topk takes them.  All of these loads are issued together.
 template <int NT>
-__device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, int b, const int (&end)[NT], const float (&thr_in)[NT],
-                             CtaShared<NT>& sh) {
+__device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, const int32_t* len, int b, CtaShared<NT>& sh,
+                                             int r_pre = 0, int npre = 0) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.repair_mask = 0u;
-  __syncthreads();
+  int nc = 0, nt = 0, L = 0;
+  float th = 0.f;
   if (tid < NT) {
     const int r = b * NT + tid;
-    const int nc = __hip_atomic_load(s.counters + 2 * r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int nt = __hip_atomic_load(s.counters + 2 * r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int k = min(end[tid], s.top_k);
+    nc = __hip_atomic_load(s.counters + 2 * r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    nt = __hip_atomic_load(s.counters + 2 * r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    th = s.thresholds[r];
+    L = *len;
+  }
+  if (npre) {
+    constexpr int kPer = kFinalizeLds / kThreads;
+    const int32_t* cand = s.candidates + (static_cast<int64_t>(r_pre) * (s.top_k + s.capacity) + s.top_k) * 2;
+    int2 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kThreads + tid;
+      if (i < npre) v[u] = *reinterpret_cast<const int2*>(cand + 2 * i);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kThreads + tid;
+      if (i < npre) {
+        sh.u.fin.idx[i] = v[u].x;
+        sh.u.fin.key[i] = static_cast<uint32_t>(v[u].y);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < NT) {
+    const int k = min(max(0, L - NT + tid + 1), s.top_k);
     const bool fit = nc <= s.capacity && nc + min(nt, s.top_k) >= k;
     sh.nc[tid] = nc;
     sh.nt[tid] = nt;
-    sh.thr[tid] = thr_in[tid];
+    sh.thr[tid] = th;
+    if (tid == 0) sh.len = L;
     if (!fit) atomicOr(&sh.repair_mask, 1u << tid);
   }
   __syncthreads();
@@ -958,14 +1005,16 @@ __device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, int b, const i
 }
 
 // ranges and Top-k finalize of row r (k = min(e_r, top_k)) from its final
-// candidate count nc, tie count nt and threshold th.
+// candidate count nc, tie count nt and threshold th (the first npre candidate
+// pairs possibly loaded already, as finalize_topk takes them).
 template <int NT>
-__device__ __forceinline__ void row_outputs(const SelectArgs& s, int r, int k, int nc, int nt, float th, CtaShared<NT>& sh) {
+__device__ __forceinline__ void row_outputs(const SelectArgs& s, int r, int k, int nc, int nt, float th, int npre,
+                                            CtaShared<NT>& sh) {
   if (threadIdx.x == 0) {
     s.ranges[r] = s.top_k - min(nt, s.top_k);
     s.ranges[s.rows + r] = s.top_k + min(nc, s.capacity);
   }
-  if (s.topk_idx) finalize_topk<NT>(s, r, k, nc, th, sh);
+  if (s.topk_idx) finalize_topk<NT>(s, r, k, nc, th, npre, sh);
   __syncthreads();
 }
 
@@ -1301,7 +1350,7 @@ __device__ __forceinline__ void row_end_item(const SelectArgs& s, const Ws& ws, 
     __syncthreads();
   }
   const int k = min(max(0, L - NT + t + 1), s.top_k);
-  row_outputs<NT>(s, r, k, sh.nc[0], sh.nt[0], sh.thr[0], sh);
+  row_outputs<NT>(s, r, k, sh.nc[0], sh.nt[0], sh.thr[0], 0, sh);
   if (tid < 4) st_wt(ws.row(r) + tid, 0u);
 }
 
@@ -1531,19 +1580,19 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
   uint32_t done_rows = 0;
   for (int r = blockIdx.x; r < s.rows; r += gridDim.x, ++done_rows) {
     const int b = r / NT, t = r - b * NT;
-    const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
-    int end[NT];
-    float thr[NT];
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      end[u] = max(0, L - NT + u + 1);
-      thr[u] = s.thresholds[b * NT + u];
-    }
+    // the row's first candidate pairs (all of them when it has at most top_k +
+    // kFewExtra) are loaded together with the fit test's inputs
+    const int npre = s.topk_idx ? min(min(s.capacity, s.top_k + kFewExtra), kFinalizeLds) : 0;
     // every CTA working on a row of tile b finds the same mask; the one with
     // its lowest row publishes the job
-    const uint32_t mask = tile_fit<NT>(s, b, end, thr, sh);
+    const uint32_t mask = tile_fit<NT>(s, a.seq_lens + static_cast<int64_t>(b) * a.sl_stride, b, sh, r, npre);
+    const int L = sh.len;
+    int end[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) end[u] = max(0, L - NT + u + 1);
+    const int k = min(end[t], s.top_k);
     if (!(mask & (1u << t)))
-      row_outputs<NT>(s, r, min(end[t], s.top_k), sh.nc[t], sh.nt[t], sh.thr[t], sh);
+      row_outputs<NT>(s, r, k, sh.nc[t], sh.nt[t], sh.thr[t], npre, sh);
     else if ((mask & ((1u << t) - 1u)) == 0u)
       publish_job<NT>(s, ws, b, end, mask);
     __syncthreads();
@@ -1562,9 +1611,9 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     __syncthreads();
     if (b == -2) break;
     if (b < 0) {
-      // back off (up to about 2 us between polls), so that waiting CTAs keep
-      // their loads off the job words the working ones update
-      for (int i = 0; i < min(idle, 16); ++i) __builtin_amdgcn_s_sleep(8);
+      // back off (up to about half a microsecond between polls), so that
+      // waiting CTAs keep their loads off the job words the working ones update
+      for (int i = 0; i < min(idle, 4); ++i) __builtin_amdgcn_s_sleep(4);
       continue;
     }
     idle = 0;
@@ -1836,8 +1885,11 @@ __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectAr
   select_body<NT, kSelectKeysPerCta, LogitsSource<NT>>(a, s, sh, nullptr);
 }
 
+// For next_n = 1 two CTAs fit on a compute unit (by LDS and, capped here, by
+// registers).
 template <int NT>
-__global__ void __launch_bounds__(kThreads) fused_finish_kernel(PagedArgs a, SelectArgs s) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1, 8)))
+fused_finish_kernel(PagedArgs a, SelectArgs s) {
   __shared__ CtaShared<NT> sh;
   __shared__ v4i stage[kWaves * kStageInt4];
   finish_body<NT, true>(a, s, sh, stage);

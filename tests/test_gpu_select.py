@@ -87,6 +87,34 @@ def test_indexer_topk_exact(seed, seq_lens, next_n, top_k, cap, mode):
     _check(wl, res2, False, scores32=x)
 
 
+@pytest.mark.parametrize("tied", [False, True])
+def test_indexer_topk_few_extra_candidates(tied):
+    """Rows that fit with 1, 2 or 3 candidates more than k (the Top-k leaves the
+    smallest out), with the smallest candidates tied at the k-th value or not,
+    and rows with 0 and 4 extra (the copy and the radix paths beside them)."""
+    top_k, cap, n = 256, 512, 5000
+    extras = [1, 2, 3, 0, 4, 1, 2, 3]
+    R = len(extras)
+    g = np.random.default_rng(77 + tied)
+    x = (g.normal(size=(R, n + 3)) * 4).astype(np.float32)
+    thr = np.zeros(R, np.float32)
+    for r, d in enumerate(extras):
+        order = np.argsort(-x[r, :n], kind="stable")
+        if tied:
+            # the last few candidates (and one key that stays a candidate) share the k-th value
+            x[r, order[top_k - 2:top_k + d]] = x[r, order[top_k - 2]]
+        v_in, v_out = np.float32(x[r, order[top_k + d - 1]]), np.float32(x[r, order[top_k + d]])
+        assert v_out < v_in
+        thr[r] = np.float32((np.float64(v_in) + np.float64(v_out)) / 2)
+        assert int(np.sum(x[r, :n] > thr[r])) == top_k + d
+    wl = W.Workload(name="syn", q=None, kv_fused=np.zeros((1, 1), np.uint8), weights=None, block_tables=None,
+                    seq_lens=np.full(R, n, np.int32), max_seq_len=n, block_size=64, next_n=1,
+                    top_k=top_k, capacity=cap, threshold_recipe="", description="")
+    res = run_select(wl, torch.from_numpy(x).to("cuda"), thr)
+    _check(wl, res, True, scores32=x)
+    assert np.array_equal(res["counters"][:, 0], top_k + np.array(extras))
+
+
 def _oracle_rows(wl, rows):
     ref = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
                                   wl.max_seq_len, rows=rows)
