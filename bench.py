@@ -12,9 +12,9 @@ Prints one JSON line:
   value          pairs/s: sum over rows of visible KV positions, per second
   rows_per_s     rows selected (and finalized) per second
   roofline       the select kernel (the dominant one): algorithmic HBM bytes
-                 per launch over its average launch time, from HIP events on
-                 its stream around the same steps run with the finish stage
-                 off, against 8 TB/s
+                 per launch over its average launch time -- one HIP event pair
+                 on its stream around the same steps run with the finish stage
+                 off, divided by the step count -- against 8 TB/s
   cpu_baseline   the float64 CPU oracle on a bounded sample of the workload
 
     python bench.py [--steps K] [--warmup W] [--workload 3|4|5] [--path fused|unfused]
@@ -179,37 +179,48 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for j in range(args.steps):
-        ev[j][0].record(stream)
-        step(args.warmup + j)
-        ev[j][1].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    ms_step = ms_total / args.steps
+    thr_pristine = torch.from_numpy(np.tile(thr0, (total, 1))).to(dev)
 
+    def reset():
+        cnt_all.zero_()
+        thr_all.copy_(thr_pristine)
+
+    def timed(finish):
+        """Mean time per step over the timed steps: one event pair around all of
+        them on the launch stream (events between steps would add their own
+        gaps)."""
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for j in range(args.steps):
+            step(args.warmup + j, finish)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    ms_step = timed(True)
     assert int(arrivals.abs().sum()) == 0, "arrivals not left zeroed"
     repaired = int((thr_all[-1].cpu().numpy().view(np.int32) != thr0.view(np.int32)).sum())
 
     # the same steps with the finish stage off: the select kernel alone, for
     # its roofline (fresh counters, same KV replicas in the same order)
-    cnt_all.zero_()
-    thr_all.copy_(torch.from_numpy(np.tile(thr0, (total, 1))).to(dev))
+    reset()
     for i in range(args.warmup):
         step(i, finish=False)
-    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    select_ms_mean = timed(False)
+
+    # per-call spread, as context: an event pair around each call
+    reset()
+    for i in range(args.warmup):
+        step(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for j in range(args.steps):
-        sev[j][0].record(stream)
-        step(args.warmup + j, finish=False)
-        sev[j][1].record(stream)
+        ev[j][0].record(stream)
+        step(args.warmup + j)
+        ev[j][1].record(stream)
     torch.cuda.synchronize()
-    select_ms = np.array([a.elapsed_time(b) for a, b in sev])
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
     # one warm (same pool every step) measurement as context
     warm = []
@@ -236,7 +247,7 @@ def main():
         del src, dst
 
     alg = algorithmic_bytes(wl, args.path)
-    mean_launch_s = float(select_ms.mean()) / 1e3
+    mean_launch_s = select_ms_mean / 1e3
     achieved = alg / mean_launch_s / 1e9
     flops = 2.0 * 64 * 128 * pairs
     out = {
@@ -262,12 +273,12 @@ def main():
                      "algorithmic_bytes_per_launch": alg,
                      "kernel": "select (fused logits + candidate/tie select)" if args.path == "fused"
                      else "mqa_logits + select",
-                     "launch_ms": {"mean": float(select_ms.mean()), "p10": float(np.percentile(select_ms, 10)),
-                                   "p50": float(np.percentile(select_ms, 50)),
-                                   "p90": float(np.percentile(select_ms, 90))},
+                     "launch_ms": {"mean": select_ms_mean},
                      "mfma_frac": flops / mean_launch_s / 1e12 / FP8_PEAK_TFLOPS},
-        "call_ms": {"mean": float(launch_ms.mean()), "p50": float(np.percentile(launch_ms, 50)),
-                    "finish_stage_mean": float(launch_ms.mean() - select_ms.mean())},
+        "call_ms": {"mean": ms_step, "finish_stage_mean": ms_step - select_ms_mean,
+                    "per_call_events": {"p10": float(np.percentile(launch_ms, 10)),
+                                        "p50": float(np.percentile(launch_ms, 50)),
+                                        "p90": float(np.percentile(launch_ms, 90))}},
         "warm_ms_per_step": float(np.median(warm)),
         "kernel_src_sha": kernel_hash(),
     }
