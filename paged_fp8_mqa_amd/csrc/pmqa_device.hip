@@ -409,9 +409,8 @@ __device__ __forceinline__ void stream_keys(const Src& src, int k0, int k1, int 
   typename Src::Group ga, gb;
   typename Src::Pages pa = src.pages(key0(0), L);
   typename Src::Pages pb = src.pages(key0(1), L);
-  // the caller's loads (q, weights, thresholds) complete before the loop, so
-  // that inside it every wait is for key loads only
-  wait_vm_done();
+  // (the caller's loads -- q, weights, thresholds -- are older than the key
+  // loads, so the first group's wait covers them too)
   // the scheduling barriers keep the groups' loads in issue order, so the
   // waits for a group count only the loads issued after it
   src.load(ga, pa, key0(0));

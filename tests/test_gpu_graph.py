@@ -1,0 +1,92 @@
+"""HIP-graph capture and replay of the fused select (select kernel, then the
+finish kernel with every row repaired): each replay, with the program's own
+eager calls and synchronisations between replays, gives the eager call's
+results, bit for bit, and the library's state in the workspace carries from
+replay to replay."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_fp8_mqa_amd as pm
+import workloads as W
+from gpu_util import SENTINEL_I32, dev, slot_sets
+
+pytestmark = pytest.mark.gpu
+
+
+def _buffers(wl, thr, ws):
+    R = wl.rows
+    return dict(
+        thr_in=torch.as_tensor(thr).cuda(), thr=torch.empty(R, dtype=torch.float32, device="cuda"),
+        counters=torch.zeros(R, 2, dtype=torch.int32, device="cuda"),
+        cand=torch.full((R, wl.top_k + wl.capacity, 2), SENTINEL_I32, dtype=torch.int32, device="cuda"),
+        arrivals=torch.zeros(wl.batch, dtype=torch.int32, device="cuda"),
+        ranges=torch.zeros(2, R, dtype=torch.int32, device="cuda"),
+        topk=torch.zeros(R, wl.top_k, dtype=torch.int32, device="cuda"), ws=ws)
+
+
+def _call(wl, d, b):
+    # the resets are kernels (a fill and an add), so that a captured graph
+    # holds no memset node
+    b["counters"].zero_()
+    torch.add(b["thr_in"], 0.0, out=b["thr"])
+    pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], wl.max_seq_len, b["thr"], b["counters"],
+                           b["cand"], wl.capacity, wl.top_k, arrivals=b["arrivals"], ranges=b["ranges"],
+                           topk_idx=b["topk"], workspace=b["ws"])
+
+
+def _host(b):
+    torch.cuda.synchronize()
+    return {k: b[k].cpu().numpy() for k in ("thr", "counters", "cand", "arrivals", "ranges", "topk")}
+
+
+def _same(wl, a, b):
+    assert np.array_equal(a["thr"].view(np.int32), b["thr"].view(np.int32)), "thresholds differ"
+    assert np.array_equal(a["counters"], b["counters"]), "counters differ"
+    assert np.array_equal(a["ranges"], b["ranges"]), "ranges differ"
+    assert np.all(b["arrivals"] == 0), "arrivals not left zeroed"
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    for r in range(wl.rows):
+        ra = {"counters": a["counters"], "cand": a["cand"]}
+        rb = {"counters": b["counters"], "cand": b["cand"]}
+        assert slot_sets(ra, r, wl.top_k, wl.capacity) == slot_sets(rb, r, wl.top_k, wl.capacity), f"row {r} slots"
+        k = min(int(ends[r]), wl.top_k)
+        assert set(a["topk"][r, :k].tolist()) == set(b["topk"][r, :k].tolist()), f"row {r} top-k"
+
+
+@pytest.mark.parametrize("mode", ["inf", "mixed"])
+def test_fused_graph_replays_match_eager(mode):
+    wl = W.small_random(61, [3000, 700, 0, 5000], 2, 64, top_k=128, capacity=256)
+    d = dev(wl)
+    ref = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
+                                  wl.max_seq_len)
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    thr = np.zeros(wl.rows, np.float32)
+    for r, e in enumerate(ends):
+        if e:
+            s = np.sort(ref[r, :e].astype(np.float32))[::-1]
+            k = min(int(e), wl.top_k)
+            # "inf": every row repaired; "mixed": even rows repaired, odd rows fit
+            thr[r] = np.inf if (mode == "inf" or r % 2 == 0) else s[k - 1]
+    ws = pm.make_workspace("fused", wl.batch, wl.next_n, wl.max_seq_len)
+    eager = _buffers(wl, thr, ws)
+    _call(wl, d, eager)
+    want = _host(eager)
+
+    graphed = _buffers(wl, thr, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        _call(wl, d, graphed)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graphed["cand"].fill_(SENTINEL_I32)
+        graphed["topk"].fill_(SENTINEL_I32)
+        g.replay()
+        got = _host(graphed)
+        _same(wl, want, got)
+        # the program's own work between replays, on the same workspace
+        _call(wl, d, eager)
+        _same(wl, want, _host(eager))
