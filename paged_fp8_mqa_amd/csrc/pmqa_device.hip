@@ -465,6 +465,15 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// Adds nc candidates and nt ties to a row's (candidate, tie) counter pair with
+// one 64-bit atomic (the pair is 8-byte aligned) and returns the old pair, the
+// first slot of each class.  The low word never carries into the high one:
+// both counts stay below the row's length, under 2^31.
+__device__ __forceinline__ uint64_t reserve_pair(int32_t* pair, int nc, int nt) {
+  const uint64_t add = (static_cast<uint64_t>(static_cast<uint32_t>(nt)) << 32) | static_cast<uint32_t>(nc);
+  return atomicAdd(reinterpret_cast<unsigned long long*>(pair), static_cast<unsigned long long>(add));
+}
+
 // A slot store is an agent-scope (relaxed) atomic store: the L2 of the
 // storing XCD writes it through, so no dirty slot line is left in any XCD's L2.
 // The tile's last CTA (on any XCD) can then read the slots after its acquire,
@@ -791,12 +800,20 @@ __device__ __forceinline__ void few_extra_topk(const int32_t* cand, int32_t* out
   }
   __syncthreads();
   // (LDS reads at clamped indices, unconditional, so that they are all in
-  // flight at once instead of one branch and wait each)
-  uint32_t kv[kPer];
+  // flight at once instead of one branch and wait each; the nu steps a row
+  // needs, out of kPer)
+  const int nu = static_cast<int>(ceil_div(nc, kThreads));
+  uint32_t kv[kPer] = {};
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) kv[u] = key[min(u * kThreads + tid, nc - 1)];
+  for (int u = 0; u < kPer; ++u) {
+    if (u >= nu) break;
+    kv[u] = key[min(u * kThreads + tid, nc - 1)];
+  }
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) kv[u] = radix_key(dec_cand(__uint_as_float(kv[u]), th));
+  for (int u = 0; u < kPer; ++u) {
+    if (u >= nu) break;
+    kv[u] = radix_key(dec_cand(__uint_as_float(kv[u]), th));
+  }
   uint32_t p0 = 0xffffffffu, p1 = 0xffffffffu, p2 = 0xffffffffu;
 #pragma unroll 1
   for (int j = 0; j < d; ++j) {
@@ -805,7 +822,7 @@ __device__ __forceinline__ void few_extra_topk(const int32_t* cand, int32_t* out
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const uint32_t i = static_cast<uint32_t>(u * kThreads + tid);
-      m[u] = (i < static_cast<uint32_t>(nc) && i != p0 && i != p1 && i != p2)
+      m[u] = (u < nu && i < static_cast<uint32_t>(nc) && i != p0 && i != p1 && i != p2)
                  ? ((static_cast<uint64_t>(kv[u]) << 32) | i)
                  : ~0ull;
     }
@@ -826,9 +843,13 @@ __device__ __forceinline__ void few_extra_topk(const int32_t* cand, int32_t* out
   }
   int32_t iv[kPer];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) iv[u] = idx[min(u * kThreads + tid, nc - 1)];
+  for (int u = 0; u < kPer; ++u) {
+    if (u >= nu) break;
+    iv[u] = idx[min(u * kThreads + tid, nc - 1)];
+  }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
+    if (u >= nu) break;
     const uint32_t i = static_cast<uint32_t>(u * kThreads + tid);
     if (i < static_cast<uint32_t>(nc) && i != p0 && i != p1 && i != p2)
       out[i - (i > p0) - (i > p1) - (i > p2)] = iv[u];
@@ -855,19 +876,25 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
     // (the preloaded candidates read from LDS at clamped indices, unconditional)
     const bool lds = nc <= npre;
     for (int i0 = 0; i0 < k; i0 += kPer * kThreads) {
+      const int nu = static_cast<int>(ceil_div(min(k - i0, kPer * kThreads), kThreads));
       int32_t v[kPer];
       if (lds && nc > 0) {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) v[u] = sh.u.fin.idx[min(i0 + u * kThreads + tid, nc - 1)];
+        for (int u = 0; u < kPer; ++u) {
+          if (u >= nu) break;
+          v[u] = sh.u.fin.idx[min(i0 + u * kThreads + tid, nc - 1)];
+        }
       }
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
+        if (u >= nu) break;
         const int i = i0 + u * kThreads + tid;
         if (i < k && (i >= nc || !lds))
           v[u] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
       }
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
+        if (u >= nu) break;
         const int i = i0 + u * kThreads + tid;
         if (i < k) out[i] = v[u];
       }
@@ -1579,6 +1606,7 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     st_wt(ws.hdr() + kHdrMagic, kLayoutMagic);
   }
   uint32_t done_rows = 0;
+  bool published = false;
   for (int r = blockIdx.x; r < s.rows; r += gridDim.x, ++done_rows) {
     const int b = r / NT, t = r - b * NT;
     // the row's first candidate pairs (all of them when it has at most top_k +
@@ -1592,16 +1620,19 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
 #pragma unroll
     for (int u = 0; u < NT; ++u) end[u] = max(0, L - NT + u + 1);
     const int k = min(end[t], s.top_k);
-    if (!(mask & (1u << t)))
+    if (!(mask & (1u << t))) {
       row_outputs<NT>(s, r, k, sh.nc[t], sh.nt[t], sh.thr[t], npre, sh);
-    else if ((mask & ((1u << t) - 1u)) == 0u)
+    } else if ((mask & ((1u << t) - 1u)) == 0u) {
       publish_job<NT>(s, ws, b, end, mask);
+      published = true;
+    }
     __syncthreads();
   }
-  if (done_rows) {
-    wait_vm_done();
-    __syncthreads();
-    if (tid == 0) atomicAdd(ws.hdr() + 2, done_rows);
+  // rows through phase A: the outputs' stores need not have completed (no one
+  // here reads them), only a listed job's entry
+  if (done_rows && tid == 0) {
+    if (published) wait_vm_done();
+    atomicAdd(ws.hdr() + 2, done_rows);
   }
   int idle = 0;
   while (true) {
@@ -1816,22 +1847,16 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
     auto flush = [&](int t) {
       const int r = b * NT + t;
       int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
-      if (ncl[t]) {
-        int base = 0;
-        if (lane == 0) base = atomicAdd(s.counters + 2 * r, ncl[t]);
-        base = __shfl(base, 0);
-        for (int i = lane; i < ncl[t]; i += 64)
-          if (base + i < s.capacity) *reinterpret_cast<int2*>(slots + 2 * (s.top_k + base + i)) = sh.cand[w][t][i];
-        ncl[t] = 0;
-      }
-      if (ntl[t]) {
-        int base = 0;
-        if (lane == 0) base = atomicAdd(s.counters + 2 * r + 1, ntl[t]);
-        base = __shfl(base, 0);
-        for (int i = lane; i < ntl[t]; i += 64)
-          if (base + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - base - i)) = sh.tie[w][t][i];
-        ntl[t] = 0;
-      }
+      uint64_t old = 0;
+      if (lane == 0) old = reserve_pair(s.counters + 2 * r, ncl[t], ntl[t]);
+      const int bc = __shfl(static_cast<int>(static_cast<uint32_t>(old)), 0);
+      const int bt = __shfl(static_cast<int>(static_cast<uint32_t>(old >> 32)), 0);
+      for (int i = lane; i < ncl[t]; i += 64)
+        if (bc + i < s.capacity) *reinterpret_cast<int2*>(slots + 2 * (s.top_k + bc + i)) = sh.cand[w][t][i];
+      for (int i = lane; i < ntl[t]; i += 64)
+        if (bt + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - bt - i)) = sh.tie[w][t][i];
+      ncl[t] = 0;
+      ntl[t] = 0;
     };
     src.init(a, b);
     stream_keys<NT, false>(
@@ -1876,12 +1901,17 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
       }
     }
     __syncthreads();
-    if (threadIdx.x < 2 * NT) {
-      const int t = threadIdx.x >> 1, cls = threadIdx.x & 1;
-      int tot = 0;
+    if (threadIdx.x < NT) {
+      const int t = threadIdx.x;
+      int tc = 0, tt = 0;
 #pragma unroll
-      for (int q = 0; q < kWaves; ++q) tot += sh.count[q][t][cls];
-      sh.base[t][cls] = tot ? atomicAdd(s.counters + 2 * (b * NT + t) + cls, tot) : 0;
+      for (int q = 0; q < kWaves; ++q) {
+        tc += sh.count[q][t][0];
+        tt += sh.count[q][t][1];
+      }
+      const uint64_t old = (tc | tt) ? reserve_pair(s.counters + 2 * (b * NT + t), tc, tt) : 0;
+      sh.base[t][0] = static_cast<int>(static_cast<uint32_t>(old));
+      sh.base[t][1] = static_cast<int>(static_cast<uint32_t>(old >> 32));
     }
     __syncthreads();
 #pragma unroll
