@@ -41,8 +41,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupKeys = 64;                  // keys a wave scores per step
 constexpr int kChunk = kGroupKeys * kWaves * 4;  // keys a CTA scores per chunk
 constexpr int kStageInt4 = 512;  // a wave's KV staging area: 64 keys x 128 bytes
-constexpr int kWaveCand = 256;   // select kernel: a wave's pending candidates per row
-constexpr int kWaveTie = 64;     // select kernel: a wave's pending ties per row
+// Select kernel: a wave's pending candidates and ties per row (smaller for
+// next_n >= 3, whose q operands take LDS instead).
+template <int NT> constexpr int kWaveCand = NT >= 3 ? 64 : 256;
+template <int NT> constexpr int kWaveTie = NT >= 3 ? 32 : 64;
 constexpr int kFewExtra = 3;   // final select by value walk when at most this many keys are left out
 
 struct PagedArgs {
@@ -157,15 +159,14 @@ __device__ __forceinline__ float reduce_scatter4(float x0, float x1, float x2, f
 // row's eight 16-byte columns XOR-swizzled by the row index (so that neither
 // the writes nor the operand reads of 16 rows at one column pile onto one
 // bank), and reads back the 32 bytes of key n its operand needs.
-template <int NT>
-struct KvSource {
+// Page addressing, key loads and the staging of a group's keys into MFMA B
+// operands, shared by the two KV score sources below.
+struct KvStream {
   struct Group {
     v4i raw[8];   // lane's 16 bytes of keys 8i + lane/8, column lane % 8
     float s;
   };
   v4i* stage;           // this wave's 8 KB LDS area: 64 rows of 8 16-byte columns
-  v8i qa[NT][4];        // A operands: rows t, head tiles mt
-  float wt[NT][16];     // weight of head 16*mt + 4*g + i at [4*mt + i]
   const uint8_t* kv;
   const int32_t* bt_row;
   int bs_shift, bs_mask, block_bytes, scale_off;
@@ -174,7 +175,7 @@ struct KvSource {
   // The wave's staging area (kStageInt4 int4 per wave, kWaves waves).
   __device__ __forceinline__ void bind(v4i* lds) { stage = lds + wave_id() * kStageInt4; }
 
-  __device__ __forceinline__ void init(const PagedArgs& a, int b) {
+  __device__ __forceinline__ void init_stream(const PagedArgs& a, int b) {
     lane = lane_id();
     n = lane & 15;
     g = lane >> 4;
@@ -184,19 +185,6 @@ struct KvSource {
     bs_mask = (1 << a.bs_shift) - 1;
     block_bytes = a.block_bytes;
     scale_off = a.scale_off;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int64_t row = static_cast<int64_t>(b) * NT + t;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        qa[t][mt] = load32(a.q + ((row * kHeads + 16 * mt + n) * kDim + 32 * g));
-        const float4 wv = *reinterpret_cast<const float4*>(a.w + row * kHeads + 16 * mt + 4 * g);
-        wt[t][4 * mt + 0] = wv.x;
-        wt[t][4 * mt + 1] = wv.y;
-        wt[t][4 * mt + 2] = wv.z;
-        wt[t][4 * mt + 3] = wv.w;
-      }
-    }
   }
 
   // Pages of the 64 keys at p0 (a multiple of 64, below L): keys p0..p0+31 on
@@ -233,17 +221,14 @@ struct KvSource {
   }
   __device__ __forceinline__ void load(Group& gr, int p0, int L) const { load(gr, pages(p0, L), p0); }
 
-  // E[t] = score of key p0 + lane for row t.  Fixed operation order, shared by
-  // every kernel, so the logits, fused and repair paths agree bit for bit.
-  __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
-    // the group into the staging area, then the operands out of it (LDS
-    // operations of one wave complete in order)
+  // The group into the staging area, then the B operands of its four 16-key
+  // column tiles out of it (LDS operations of one wave complete in order).
+  __device__ __forceinline__ void operands(const Group& gr, v8i (&bk)[4]) const {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = 8 * i + (lane >> 3);
       stage[row * 8 + ((lane & 7) ^ (row & 7))] = gr.raw[i];
     }
-    v8i bk[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 16 * j + n;
@@ -251,6 +236,50 @@ struct KvSource {
       const v4i hi = stage[row * 8 + ((2 * g + 1) ^ (row & 7))];
       bk[j] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
+  }
+};
+
+// The in-lane epilogue of one MFMA result: the weighted sum of the ReLU of
+// this lane's four heads, added to sum in head order.  Both score sources use
+// it in the same order (head tiles mt = 0..3, then i = 0..3 within a tile), so
+// they give the same bits.
+__device__ __forceinline__ float head_sum(v4f acc, float4 w, float sum) {
+  sum = __builtin_fmaf(relu(acc[0]), w.x, sum);
+  sum = __builtin_fmaf(relu(acc[1]), w.y, sum);
+  sum = __builtin_fmaf(relu(acc[2]), w.z, sum);
+  return __builtin_fmaf(relu(acc[3]), w.w, sum);
+}
+
+// Scores computed from the paged KV pool, the A operands (q) and the lane's 16
+// weights per row held in VGPRs (next_n up to 2, and the repair).
+template <int NT>
+struct QLds;
+
+template <int NT>
+struct KvSource : KvStream {
+  v8i qa[NT][4];        // A operands: rows t, head tiles mt
+  float4 wt[NT][4];     // weights of heads 16*mt + 4*g .. +3
+
+  __device__ __forceinline__ void bind_q(QLds<NT>*) {}
+
+  __device__ __forceinline__ void init(const PagedArgs& a, int b) {
+    init_stream(a, b);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = static_cast<int64_t>(b) * NT + t;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        qa[t][mt] = load32(a.q + ((row * kHeads + 16 * mt + n) * kDim + 32 * g));
+        wt[t][mt] = *reinterpret_cast<const float4*>(a.w + row * kHeads + 16 * mt + 4 * g);
+      }
+    }
+  }
+
+  // E[t] = score of key p0 + lane for row t.  Fixed operation order, shared by
+  // every kernel, so the logits, fused and repair paths agree bit for bit.
+  __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
+    v8i bk[4];
+    operands(gr, bk);
     float part[NT][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -265,12 +294,106 @@ struct KvSource {
       for (int t = 0; t < NT; ++t) {
         float sum = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sum = __builtin_fmaf(relu(acc[t][mt][i]), wt[t][4 * mt + i], sum);
+        for (int mt = 0; mt < 4; ++mt) sum = head_sum(acc[t][mt], wt[t][mt], sum);
         part[t][j] = sum;
       }
     }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) E[t] = reduce_scatter4(part[t][0], part[t][1], part[t][2], part[t][3], g) * gr.s;
+  }
+};
+
+// CTA-shared LDS copy of a request's q operands and weights for KvSourceQ: q of
+// row t, head tile mt, half h (16 bytes) for lane l at q[t][mt][h][l]; the
+// weights of heads 16*mt + 4*g .. +3 at w[t][mt][g].
+template <int NT>
+struct QLds {
+  v4i q[NT][4][2][64];
+  float4 w[NT][4][4];
+};
+
+// Scores computed from the paged KV pool with the A operands (q) and weights
+// read from LDS per head tile (next_n of 3 and 4): holding 32 VGPRs of q and
+// 16 of weights per row left those variants one wave per SIMD; from LDS they
+// fit two.  Same operation order as KvSource, so the same bits.
+template <int NT>
+struct KvSourceQ : KvStream {
+  QLds<NT>* ql;
+
+  __device__ __forceinline__ void bind_q(QLds<NT>* q_area) { ql = q_area; }
+
+  // Every thread of the CTA calls it (it ends with a barrier).
+  __device__ __forceinline__ void init(const PagedArgs& a, int b) {
+    init_stream(a, b);
+    const int tid = threadIdx.x;
+    // (t, mt, h, l) -> bytes 32*(l/16) + 16*h of head 16*mt + l%16 of row t
+    for (int e = tid; e < NT * 4 * 2 * 64; e += kThreads) {
+      const int l = e & 63, h = (e >> 6) & 1, mt = (e >> 7) & 3, t = e >> 9;
+      const int64_t row = static_cast<int64_t>(b) * NT + t;
+      (&ql->q[0][0][0][0])[e] =
+          *reinterpret_cast<const v4i*>(a.q + (row * kHeads + 16 * mt + (l & 15)) * kDim + 32 * (l >> 4) + 16 * h);
+    }
+    for (int e = tid; e < NT * 16; e += kThreads) {
+      const int t = e >> 4, head4 = e & 15;  // heads 4*head4 .. +3
+      (&ql->w[0][0][0])[e] = *reinterpret_cast<const float4*>(a.w + (static_cast<int64_t>(b) * NT + t) * kHeads + 4 * head4);
+    }
+    __syncthreads();
+  }
+
+  struct Pipe {
+    v8i qa[3];
+    float4 wv[3];
+    v4f acc[2][4];
+  };
+  template <int k>
+  __device__ __forceinline__ void ld(Pipe& p) const {
+    constexpr int t = k >> 2, mt = k & 3;
+    const v4i lo = ql->q[t][mt][0][lane];
+    const v4i hi = ql->q[t][mt][1][lane];
+    p.qa[k % 3] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    p.wv[k % 3] = ql->w[t][mt][g];
+  }
+  template <int k>
+  __device__ __forceinline__ void mm(Pipe& p, const v8i (&bk)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p.acc[k & 1][j] = mfma_fp8(p.qa[k % 3], bk[j]);
+  }
+  template <int k>
+  __device__ __forceinline__ void steps(Pipe& p, const v8i (&bk)[4], float (&part)[NT][4]) const {
+    if constexpr (k < 4 * NT) {
+      if constexpr (k + 1 < 4 * NT) mm<k + 1>(p, bk);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (k + 2 < 4 * NT) ld<k + 2>(p);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[k >> 2][j] = head_sum(p.acc[k & 1][j], p.wv[k % 3], part[k >> 2][j]);
+      // (keeps the steps in this order: left to itself the scheduler hoists
+      // every LDS read to the top and runs out of registers)
+      __builtin_amdgcn_sched_barrier(0);
+      steps<k + 1>(p, bk, part);
+    }
+  }
+
+  __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
+    v8i bk[4];
+    operands(gr, bk);
+    float part[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[t][j] = 0.f;
+    // Software pipeline over the 4*NT (row, head tile) steps k = 4t + mt: the
+    // operands of step k+2 are read from LDS and the MFMAs of step k+1 issued
+    // before the epilogue of step k (operands triple-, accumulators
+    // double-buffered), so LDS latency, MFMA latency and the epilogue overlap.
+    // The steps are generated at compile time, so every buffer index is a
+    // constant and the buffers live in registers.
+    Pipe p;
+    ld<0>(p);
+    ld<1>(p);
+    mm<0>(p, bk);
+    __builtin_amdgcn_sched_barrier(0);
+    steps<0>(p, bk, part);
 #pragma unroll
     for (int t = 0; t < NT; ++t) E[t] = reduce_scatter4(part[t][0], part[t][1], part[t][2], part[t][3], g) * gr.s;
   }
@@ -291,6 +414,7 @@ struct LogitsSource {
   uint32_t mask;
 
   __device__ __forceinline__ void bind(v4i*) {}
+  __device__ __forceinline__ void bind_q(QLds<NT>*) {}
   __device__ __forceinline__ void init(const LogitsArgs& a, int b) {
     lane = lane_id();
     ld = a.ld;
@@ -525,8 +649,8 @@ struct CtaShared {
 // their KV staging areas fit on a compute unit).
 template <int NT>
 struct MainShared {
-  int2 cand[kWaves][NT][kWaveCand];
-  int2 tie[kWaves][NT][kWaveTie];
+  int2 cand[kWaves][NT][kWaveCand<NT>];
+  int2 tie[kWaves][NT][kWaveTie<NT>];
   int32_t count[kWaves][NT][2];  // the waves' list lengths at the end
   int32_t base[NT][2];           // the CTA's slot bases per row and class
 };
@@ -1793,15 +1917,14 @@ __device__ __forceinline__ void for_each_segment(const int32_t* seq_lens, int64_
 
 // Waves per SIMD each variant is built for (VGPR budget 512 / waves).
 template <int NT>
-constexpr int kFusedWaves = NT == 1 ? 3 : (NT == 2 ? 2 : 1);
+constexpr int kFusedWaves = NT == 1 ? 3 : 2;
 
 
-template <int NT>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
-logits_kernel(PagedArgs a, float* out, int64_t ld) {
-  __shared__ v4i stage[kWaves * kStageInt4];
-  KvSource<NT> src;
+template <int NT, class Src>
+__device__ __forceinline__ void logits_body(const PagedArgs& a, float* out, int64_t ld, v4i* stage, QLds<NT>* ql) {
+  Src src;
   src.bind(stage);
+  src.bind_q(ql);
   const int lane = lane_id();
   for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kLogitsKeysPerCta, false,
                    [&](int b, int L, int k0, int k1, int) {
@@ -1817,6 +1940,18 @@ logits_kernel(PagedArgs a, float* out, int64_t ld) {
   });
 }
 
+template <int NT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
+logits_kernel(PagedArgs a, float* out, int64_t ld) {
+  __shared__ v4i stage[kWaves * kStageInt4];
+  if constexpr (NT >= 3) {
+    __shared__ QLds<NT> ql;
+    logits_body<NT, KvSourceQ<NT>>(a, out, ld, stage, &ql);
+  } else {
+    logits_body<NT, KvSource<NT>>(a, out, ld, stage, nullptr);
+  }
+}
+
 // The select kernels' CTA body: score keys [k0, k1) of the CTA's request and
 // select each wave's 64-key groups straight from the scores in registers onto
 // the wave's own lists, which reach the slots when nearly full (one counter
@@ -1824,10 +1959,12 @@ logits_kernel(PagedArgs a, float* out, int64_t ld) {
 // CTA, after the only barrier).  Whatever follows -- fit test,
 // repair, ranges, Top-k -- is the finish kernel's.
 template <int NT, int kKeysPerCta, class Src, class Args>
-__device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, MainShared<NT>& sh, v4i* stage) {
+__device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, MainShared<NT>& sh, v4i* stage,
+                                            QLds<NT>* ql) {
   if (s.ws) prepare_workspace<NT>(s, a.batch);
   Src src;
   src.bind(stage);
+  src.bind_q(ql);
   const int lane = lane_id();
   const int w = wave_id();
   for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kKeysPerCta, true,
@@ -1876,7 +2013,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
             const uint64_t mt = __ballot(tie);
             const int nc = __popcll(mc);
             const int nt = __popcll(mt);
-            if (ncl[t] + nc > kWaveCand || ntl[t] + nt > kWaveTie) {
+            if (ncl[t] + nc > kWaveCand<NT> || ntl[t] + nt > kWaveTie<NT>) {
               flush(t);
               flushed = true;
             }
@@ -1936,13 +2073,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
 fused_kernel(PagedArgs a, SelectArgs s) {
   __shared__ MainShared<NT> sh;
   __shared__ v4i stage[kWaves * kStageInt4];
-  select_body<NT, kFusedKeysPerCta, KvSource<NT>>(a, s, sh, stage);
+  if constexpr (NT >= 3) {
+    __shared__ QLds<NT> ql;
+    select_body<NT, kFusedKeysPerCta, KvSourceQ<NT>>(a, s, sh, stage, &ql);
+  } else {
+    select_body<NT, kFusedKeysPerCta, KvSource<NT>>(a, s, sh, stage, nullptr);
+  }
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectArgs s) {
   __shared__ MainShared<NT> sh;
-  select_body<NT, kSelectKeysPerCta, LogitsSource<NT>>(a, s, sh, nullptr);
+  select_body<NT, kSelectKeysPerCta, LogitsSource<NT>>(a, s, sh, nullptr, nullptr);
 }
 
 // For next_n = 1 two CTAs fit on a compute unit (by LDS and, capped here, by

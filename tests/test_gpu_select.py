@@ -265,3 +265,28 @@ def test_workspace_reused_across_batch_sizes():
         sb = gpu_util.SelectBuffers(wl.rows, wl.batch, wl.top_k, wl.capacity, thr, workspace=ws)
         pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], wl.max_seq_len, **sb.kwargs())
         _check(wl, sb.host(), True, scores64=ref, tau=tau)
+
+
+@pytest.mark.parametrize("next_n", [1, 2, 3, 4])
+def test_repair_rescore_bits_equal_logits_kernel(next_n):
+    """The fused repair scores a repaired request again (q and weights in
+    registers) and keeps the scores in the workspace's score buffer; they are
+    the logits kernel's bits (q and weights from LDS for next_n >= 3)."""
+    wl = W.small_random(71 + next_n, [3000, 5000, 700, 1], next_n, 64, top_k=128, capacity=256)
+    d = dev(wl)
+    out, _ = run_logits(wl, d)
+    logits = out.cpu().numpy()
+    ws = pm.make_workspace("fused", wl.batch, wl.next_n, wl.max_seq_len)
+    import gpu_util
+    thr = np.full(wl.rows, np.inf, np.float32)  # every row with keys is repaired
+    sb = gpu_util.SelectBuffers(wl.rows, wl.batch, wl.top_k, wl.capacity, thr, workspace=ws)
+    pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], wl.max_seq_len, **sb.kwargs())
+    sb.host()
+    stride = -(-wl.max_seq_len // 64) * 64
+    state = ws.numel() - wl.rows * stride * 4
+    assert state == pm.workspace_bytes("indexer_topk", wl.batch, wl.next_n, wl.max_seq_len)
+    scores = ws[state:].view(torch.float32).view(wl.rows, stride).cpu().numpy()
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    for r, e in enumerate(ends):
+        a, b = scores[r, :e].view(np.int32), logits[r, :e].view(np.int32)
+        assert np.array_equal(a, b), f"row {r}: {int(np.sum(a != b))} of {e} scores differ in their bits"
