@@ -447,6 +447,11 @@ struct LogitsSource {
 #pragma unroll
     for (int t = 0; t < NT; ++t) E[t] = gr.v[t];
   }
+  // Row t's score of key p (clamped to L - 1; jobs exist only for L >= 1).
+  __device__ __forceinline__ float value(int t, int p, int L) const {
+    const float* a = rows + t * ld + max(0, min(p, L - 1));
+    return kShared ? __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(a))) : *a;
+  }
 };
 
 // Scores one chunk [c0, cend) of at most kChunk keys (c0 < cend <= L): wave w
@@ -610,13 +615,12 @@ __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
 }
 
 
-// Shared memory of a CTA: a union of the scores of the chunk being selected,
-// per-row radix histograms (repair passes) and one row's keys (final radix
-// selects), which are live at different times.
+// Shared memory of a finish-kernel CTA: a union of the per-row radix
+// histograms (repair passes) and one row's keys (final selects), which are
+// live at different times.
 template <int NT>
 struct CtaShared {
   union {
-    float score[NT][kChunk];        // the chunk being selected
     uint32_t hist[NT][kRadixBins];  // per-row radix histograms
     struct {
       alignas(16) uint32_t hist[kRadixBins];
@@ -654,79 +658,6 @@ struct MainShared {
   int32_t count[kWaves][NT][2];  // the waves' list lengths at the end
   int32_t base[NT][2];           // the CTA's slot bases per row and class
 };
-
-// Candidate / tie append of one scored chunk [c0, cend) held in sh.u.score, for
-// the rows in row_mask.  Each wave counts its 256 keys with ballots; one
-// thread per row adds the CTA's totals to cnt[2t], cnt[2t+1] (global counters,
-// or the LDS counters of a repairing CTA) with one atomic per class, and the
-// waves then store their slots at the returned base plus their prefix.
-template <int NT, class Sh>
-__device__ __forceinline__ void select_chunk(const SelectArgs& s, int b, int c0, int cend, const float (&thr)[NT],
-                             const int (&end)[NT], Sh& sh, int32_t* cnt, uint32_t row_mask) {
-  const int w = wave_id();
-  const int lane = lane_id();
-  const int tid = threadIdx.x;
-  const int stride = s.top_k + s.capacity;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (!(row_mask & (1u << t))) continue;
-    const int lim = min(cend, end[t]);
-    const float th = thr[t];
-    int nc = 0, ntie = 0;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = 256 * w + 64 * it + lane;
-      const float e = sh.u.score[t][i];
-      const bool valid = c0 + i < lim;
-      nc += __popcll(__ballot(valid && (e > th)));
-      ntie += __popcll(__ballot(valid && !(e > th) && !(e < th)));
-    }
-    if (lane == 0) {
-      sh.wcnt[t][w][0] = nc;
-      sh.wcnt[t][w][1] = ntie;
-    }
-  }
-  __syncthreads();
-  if (tid < NT && (row_mask & (1u << tid))) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      int tot = 0;
-#pragma unroll
-      for (int q = 0; q < kWaves; ++q) tot += sh.wcnt[tid][q][c];
-      int base = tot ? atomicAdd(cnt + 2 * tid + c, tot) : 0;
-#pragma unroll
-      for (int q = 0; q < kWaves; ++q) {
-        sh.wbase[tid][q][c] = base;
-        base += sh.wcnt[tid][q][c];
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (!(row_mask & (1u << t))) continue;
-    const int lim = min(cend, end[t]);
-    const float th = thr[t];
-    int32_t* slots = s.candidates + static_cast<int64_t>(b * NT + t) * stride * 2;
-    int rc = sh.wbase[t][w][0], rt = sh.wbase[t][w][1];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = 256 * w + 64 * it + lane;
-      const float e = sh.u.score[t][i];
-      const bool valid = c0 + i < lim;
-      const bool cand = valid && (e > th);
-      const bool tie = valid && !(e > th) && !(e < th);
-      const uint64_t mc = __ballot(cand);
-      const uint64_t mt = __ballot(tie);
-      const int kc = rc + lanes_below(mc);
-      const int kt = rt + lanes_below(mt);
-      if (cand && kc < s.capacity) store_pair(slots + 2 * (s.top_k + kc), c0 + i, enc_cand(e, th));
-      if (tie && kt < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - kt), c0 + i, e - th);
-      rc += __popcll(mc);
-      rt += __popcll(mt);
-    }
-  }
-}
 
 // One wave finds the digit holding the krem-th largest entry of hist[0..nb) and
 // the rank left inside it, and returns both in every lane.  The histogram's
@@ -1270,37 +1201,38 @@ __device__ __forceinline__ void publish_job(const SelectArgs& s, const Ws& ws, i
   }
 }
 
-// Stage 4 on one scored chunk (scores in sh.u.score): keys of the repaired rows
-// above the bucket are appended as candidates (raw scores; re-encoded once the
-// threshold is known), keys inside it go to the row's bucket buffer.
-template <int NT>
-__device__ __forceinline__ void collect_chunk(const SelectArgs& s, const Ws& ws, int b, int c0, int cend, const int (&end)[NT],
-                              const uint32_t (&pfx)[NT], int known, CtaShared<NT>& sh, uint32_t mask) {
+// Stages 4 and 5 on one whole item of scores held in registers (v[t][u] is row
+// t's score of key c0 + 64*(w + 4u) + lane, for the rows in mask): every key
+// below min(cend, end[t]) is classified by cls(t, score) -> 0 (none), 1 or 2;
+// each wave counts its keys of both classes with ballots, one thread per row
+// reserves the CTA's slots with one atomic per class (add1(t, n), add2(t, n)
+// return the first), and the keys go to put(t, class, position, key, score).
+template <int NT, int kU, class Cls, class Add1, class Add2, class Put>
+__device__ __forceinline__ void append_item(int c0, int cend, const int (&end)[NT], uint32_t mask,
+                                            const float (&v)[NT][kU], CtaShared<NT>& sh, Cls&& cls, Add1&& add1,
+                                            Add2&& add2, Put&& put) {
   const int w = wave_id();
   const int lane = lane_id();
   const int tid = threadIdx.x;
-  const int stride = s.top_k + s.capacity;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (!(mask & (1u << t))) continue;
     const int lim = min(cend, end[t]);
-    int na = 0, ni = 0;
+    int n1 = 0, n2 = 0;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = 256 * w + 64 * it + lane;
-      const bool valid = c0 + i < lim;
-      const uint32_t top = radix_key(sh.u.score[t][i]) >> (32 - known);
-      na += __popcll(__ballot(valid && top > pfx[t]));
-      ni += __popcll(__ballot(valid && top == pfx[t]));
+    for (int u = 0; u < kU; ++u) {
+      const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
+      const int c = p < lim ? cls(t, v[t][u]) : 0;
+      n1 += __popcll(__ballot(c == 1));
+      n2 += __popcll(__ballot(c == 2));
     }
     if (lane == 0) {
-      sh.wcnt[t][w][0] = na;
-      sh.wcnt[t][w][1] = ni;
+      sh.wcnt[t][w][0] = n1;
+      sh.wcnt[t][w][1] = n2;
     }
   }
   __syncthreads();
   if (tid < NT && (mask & (1u << tid))) {
-    const int r = b * NT + tid;
     int tot[2] = {0, 0};
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) {
@@ -1308,8 +1240,8 @@ __device__ __forceinline__ void collect_chunk(const SelectArgs& s, const Ws& ws,
       tot[1] += sh.wcnt[tid][q][1];
     }
     int base[2];
-    base[0] = tot[0] ? atomicAdd(s.counters + 2 * r, tot[0]) : 0;
-    base[1] = tot[1] ? static_cast<int>(atomicAdd(ws.row(r) + 3, static_cast<uint32_t>(tot[1]))) : 0;
+    base[0] = tot[0] ? add1(tid, tot[0]) : 0;
+    base[1] = tot[1] ? add2(tid, tot[1]) : 0;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) {
       sh.wbase[tid][q][0] = base[0];
@@ -1322,27 +1254,18 @@ __device__ __forceinline__ void collect_chunk(const SelectArgs& s, const Ws& ws,
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (!(mask & (1u << t))) continue;
-    const int r = b * NT + t;
     const int lim = min(cend, end[t]);
-    int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
-    int32_t* bucket = ws.bucket(r);
-    int ra = sh.wbase[t][w][0], ri = sh.wbase[t][w][1];
+    int r1 = sh.wbase[t][w][0], r2 = sh.wbase[t][w][1];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = 256 * w + 64 * it + lane;
-      const float e = sh.u.score[t][i];
-      const bool valid = c0 + i < lim;
-      const uint32_t top = radix_key(e) >> (32 - known);
-      const bool above = valid && top > pfx[t];
-      const bool in = valid && top == pfx[t];
-      const uint64_t ma = __ballot(above);
-      const uint64_t mi = __ballot(in);
-      const int ka = ra + lanes_below(ma);
-      const int ki = ri + lanes_below(mi);
-      if (above && ka < s.capacity) store_pair(slots + 2 * (s.top_k + ka), c0 + i, e);
-      if (in && ki < kFinalizeLds) store_pair(bucket + 2 * ki, c0 + i, e);
-      ra += __popcll(ma);
-      ri += __popcll(mi);
+    for (int u = 0; u < kU; ++u) {
+      const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
+      const int c = p < lim ? cls(t, v[t][u]) : 0;
+      const uint64_t m1 = __ballot(c == 1);
+      const uint64_t m2 = __ballot(c == 2);
+      if (c == 1) put(t, 1, r1 + lanes_below(m1), p, v[t][u]);
+      if (c == 2) put(t, 2, r2 + lanes_below(m2), p, v[t][u]);
+      r1 += __popcll(m1);
+      r2 += __popcll(m2);
     }
   }
 }
@@ -1438,19 +1361,38 @@ __device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, i
   const int krem = static_cast<int>(ld_ag(row + 1));
   const int nabove = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
   int32_t* bucket = ws.bucket(r);
-  uint32_t* keys = sh.u.fin.key;
-  #pragma unroll 1
-  for (int i = tid; i < nin; i += kThreads) keys[i] = radix_key(__int_as_float(bucket[2 * i + 1]));
+  // the bucket's (index, score bits) pairs into LDS, all of a thread's loads in
+  // flight at once (the radix keys are derived from the bits where needed)
+  constexpr int kPer = kFinalizeLds / kThreads;
+  uint32_t* bits = sh.u.fin.key;
+  int32_t* idxs = sh.u.fin.idx;
+  {
+    int2 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kThreads + tid;
+      if (i < nin) v[u] = *reinterpret_cast<const int2*>(bucket + 2 * i);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kThreads + tid;
+      if (i < nin) {
+        idxs[i] = v[u].x;
+        bits[i] = static_cast<uint32_t>(v[u].y);
+      }
+    }
+  }
   __syncthreads();
-  cta_radix_select([&](int i) { return keys[i]; }, nin, krem, sh.u.fin.hist, sh);
+  auto key_of = [&](int i) { return radix_key(__uint_as_float(bits[i])); };
+  cta_radix_select(key_of, nin, krem, sh.u.fin.hist, sh);
   const uint32_t kstar = sh.pfx[0];
   const float t2 = key_to_float(kstar);
   int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
   #pragma unroll 1
   for (int i = tid; i < nin; i += kThreads) {
-    const uint32_t key = keys[i];
-    const int32_t idx = bucket[2 * i];
-    const float e = __int_as_float(bucket[2 * i + 1]);
+    const uint32_t key = key_of(i);
+    const int32_t idx = idxs[i];
+    const float e = __uint_as_float(bits[i]);
     if (key > kstar) {
       const int k = nabove + atomicAdd(&sh.pos[0], 1);
       if (k < s.capacity) store_pair(slots + 2 * (s.top_k + k), idx, enc_cand(e, t2));
@@ -1459,10 +1401,21 @@ __device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, i
       if (k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), idx, e - t2);
     }
   }
-  #pragma unroll 1
-  for (int i = tid; i < min(nabove, s.capacity); i += kThreads) {
-    int32_t* sl = slots + 2 * (s.top_k + i);
-    store_pair(sl, sl[0], enc_cand(__int_as_float(sl[1]), t2));
+  // the candidates collected above the bucket (raw scores) re-encoded against
+  // the new threshold, all of a thread's loads in flight at once
+  const int nabove_kept = min(nabove, s.capacity);
+  for (int i0 = 0; i0 < nabove_kept; i0 += kPer * kThreads) {
+    int2 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      if (i < nabove_kept) v[u] = *reinterpret_cast<const int2*>(slots + 2 * (s.top_k + i));
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      if (i < nabove_kept) store_pair(slots + 2 * (s.top_k + i), v[u].x, enc_cand(__int_as_float(v[u].y), t2));
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -1598,6 +1551,18 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
       src.init(a, b);
     const int c0 = idx * kSelectItemKeys;
     const int cend = min(c0 + kSelectItemKeys, L);
+    // The item's scores of the repaired rows, all loaded at once: wave w's
+    // group u holds keys c0 + 64*(w + 4u) .. +63 (chunk u / 4 of kChunk keys,
+    // as score_chunk lays a chunk out).
+    constexpr int kU = kSelectItemKeys / (kGroupKeys * kWaves);
+    const int w = wave_id();
+    float v[NT][kU];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (!(mask & (1u << t))) continue;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[t][u] = src.value(t, c0 + kGroupKeys * (w + kWaves * u) + lane, L);
+    }
     if (stage < kStageCollect) {
       // histogram straight from the scores in registers
       const int pass = stage - kStageHist0;
@@ -1606,35 +1571,52 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
       const uint32_t low = (1u << bits) - 1u;
       for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
       __syncthreads();
-      for (int c = c0; c < cend; c += kChunk) {
-        const int ce = min(c + kChunk, cend);
-        score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
-          const int p = p0 + lane;
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            if (!(mask & (1u << t)) || p >= min(ce, end[t])) continue;
-            const uint32_t key = radix_key(E[t]);
-            if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
-            atomicAdd(&sh.u.hist[t][(key >> shift) & low], 1u);
-          }
-        });
+      for (int t = 0; t < NT; ++t) {
+        if (!(mask & (1u << t))) continue;
+        const int lim = min(cend, end[t]);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
+          if (p >= lim) continue;
+          const uint32_t key = radix_key(v[t][u]);
+          if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
+          atomicAdd(&sh.u.hist[t][(key >> shift) & low], 1u);
+        }
       }
       __syncthreads();
       flush_hist<NT>(ws, b, pass, mask, idx % kHistCopies, sh);
+    } else if (stage == kStageCollect) {
+      // keys above the bucket become candidates (raw scores; re-encoded once
+      // the threshold is known), keys inside it go to the row's bucket buffer
+      const int stride = s.top_k + s.capacity;
+      append_item<NT, kU>(
+          c0, cend, end, mask, v, sh,
+          [&](int t, float e) {
+            const uint32_t top = radix_key(e) >> (32 - known);
+            return top > pfx[t] ? 1 : (top == pfx[t] ? 2 : 0);
+          },
+          [&](int t, int n) { return atomicAdd(s.counters + 2 * (b * NT + t), n); },
+          [&](int t, int n) { return static_cast<int>(atomicAdd(ws.row(b * NT + t) + 3, static_cast<uint32_t>(n))); },
+          [&](int t, int c, int k, int p, float e) {
+            if (c == 1 && k < s.capacity)
+              store_pair(s.candidates + (static_cast<int64_t>(b * NT + t) * stride + s.top_k + k) * 2, p, e);
+            if (c == 2 && k < kFinalizeLds) store_pair(ws.bucket(b * NT + t) + 2 * k, p, e);
+          });
     } else {
-      for (int c = c0; c < cend; c += kChunk) {
-        const int ce = min(c + kChunk, cend);
-        score_chunk<NT>(src, c, ce, L, [&](int p0, const float(&E)[NT]) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) sh.u.score[t][p0 - c + lane] = E[t];
-        });
-        __syncthreads();
-        if (stage == kStageCollect)
-          collect_chunk<NT>(s, ws, b, c, ce, end, pfx, known, sh, mask);
-        else
-          select_chunk<NT>(s, b, c, ce, thr2, end, sh, s.counters + 2 * b * NT, mask);
-        __syncthreads();
-      }
+      // select again at the now exact threshold
+      const int stride = s.top_k + s.capacity;
+      int32_t* cnt = s.counters + 2 * b * NT;
+      append_item<NT, kU>(
+          c0, cend, end, mask, v, sh,
+          [&](int t, float e) { return e > thr2[t] ? 1 : (!(e < thr2[t]) ? 2 : 0); },
+          [&](int t, int n) { return atomicAdd(cnt + 2 * t, n); },
+          [&](int t, int n) { return atomicAdd(cnt + 2 * t + 1, n); },
+          [&](int t, int c, int k, int p, float e) {
+            int32_t* slots = s.candidates + static_cast<int64_t>(b * NT + t) * stride * 2;
+            if (c == 1 && k < s.capacity) store_pair(slots + 2 * (s.top_k + k), p, enc_cand(e, thr2[t]));
+            if (c == 2 && k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), p, e - thr2[t]);
+          });
     }
   }
   wait_vm_done();
