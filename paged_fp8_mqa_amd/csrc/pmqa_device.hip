@@ -454,49 +454,6 @@ struct LogitsSource {
   }
 };
 
-// Scores one chunk [c0, cend) of at most kChunk keys (c0 < cend <= L): wave w
-// takes the groups at c0 + 64*(w + 4i), i = 0..3, double-buffered so the next
-// group's loads are in flight while the current one is scored.  f(p0, E) runs
-// for the groups below cend; the loads of a group past cend re-read the
-// chunk's first group.
-template <int NT, class Src, class F>
-__device__ __forceinline__ void score_chunk(const Src& src, int c0, int cend, int L, F&& f) {
-  const int w = wave_id();
-  int p[4];
-  bool v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = c0 + kGroupKeys * (w + kWaves * i);
-    v[i] = q < cend;
-    p[i] = v[i] ? q : c0;
-  }
-  typename Src::Group ga, gb;
-  src.load(ga, p[0], L);
-  src.load(gb, p[1], L);
-  if (v[0]) {
-    float E[NT];
-    src.score(ga, E);
-    f(p[0], E);
-  }
-  src.load(ga, p[2], L);
-  if (v[1]) {
-    float E[NT];
-    src.score(gb, E);
-    f(p[1], E);
-  }
-  src.load(gb, p[3], L);
-  if (v[2]) {
-    float E[NT];
-    src.score(ga, E);
-    f(p[2], E);
-  }
-  if (v[3]) {
-    float E[NT];
-    src.score(gb, E);
-    f(p[3], E);
-  }
-}
-
 // Wave priority from the fraction of the range done: the waves of the CTAs
 // that share a compute unit start together, and the issue arbiter favours the
 // oldest waves among those of equal priority; waves that are further along
@@ -1552,8 +1509,7 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
     const int c0 = idx * kSelectItemKeys;
     const int cend = min(c0 + kSelectItemKeys, L);
     // The item's scores of the repaired rows, all loaded at once: wave w's
-    // group u holds keys c0 + 64*(w + 4u) .. +63 (chunk u / 4 of kChunk keys,
-    // as score_chunk lays a chunk out).
+    // group u holds keys c0 + 64*(w + 4u) .. +63.
     constexpr int kU = kSelectItemKeys / (kGroupKeys * kWaves);
     const int w = wave_id();
     float v[NT][kU];
