@@ -46,6 +46,12 @@ constexpr int kStageInt4 = 512;  // a wave's KV staging area: 64 keys x 128 byte
 template <int NT> constexpr int kWaveCand = NT >= 3 ? 64 : 256;
 template <int NT> constexpr int kWaveTie = NT >= 3 ? 32 : 64;
 constexpr int kFewExtra = 3;   // final select by value walk when at most this many keys are left out
+// Phase A: the candidate pairs of a row that waves 1-3 preload (pair
+// u * kPreThreads + tid - 64 in unit u of thread tid >= 64); wave 0 loads the
+// fit test's words and counts the row, with no pair load ahead of its atomic.
+constexpr int kPreUnits = 16;
+constexpr int kPreThreads = kThreads - 64;
+constexpr int kPreCap = kPreUnits * kPreThreads;
 
 struct PagedArgs {
   const uint8_t* q;
@@ -995,12 +1001,12 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
 
 // Fit test of tile b (its request's length at *len) from its counters: fills
 // sh.nc, sh.nt, sh.thr and sh.len and returns the mask of rows that do not
-// fit.  With npre > 0 it also loads the first npre candidate pairs of row
-// r_pre into sh.u.fin.idx / sh.u.fin.key (index, score bits), as
-// finalize_topk takes them.  All of these loads are issued together.
+// fit.  It also loads the first npre <= kPreCap candidate pairs of row r_pre
+// (index, score bits) into the registers of waves 1-3: pair u * kPreThreads +
+// tid - 64 into pre[u].  All of these loads are issued together.
 template <int NT>
 __device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, const int32_t* len, int b, CtaShared<NT>& sh,
-                                             int r_pre = 0, int npre = 0) {
+                                             int r_pre, int npre, int2 (&pre)[kPreUnits]) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.repair_mask = 0u;
   int nc = 0, nt = 0, L = 0;
@@ -1012,23 +1018,12 @@ __device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, const int32_t*
     th = s.thresholds[r];
     L = *len;
   }
-  if (npre) {
-    constexpr int kPer = kFinalizeLds / kThreads;
-    const int32_t* cand = s.candidates + (static_cast<int64_t>(r_pre) * (s.top_k + s.capacity) + s.top_k) * 2;
-    int2 v[kPer];
+  const int32_t* cand = s.candidates + (static_cast<int64_t>(r_pre) * (s.top_k + s.capacity) + s.top_k) * 2;
+  const int pt = tid - 64;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kThreads + tid;
-      if (i < npre) v[u] = *reinterpret_cast<const int2*>(cand + 2 * i);
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kThreads + tid;
-      if (i < npre) {
-        sh.u.fin.idx[i] = v[u].x;
-        sh.u.fin.key[i] = static_cast<uint32_t>(v[u].y);
-      }
-    }
+  for (int u = 0; u < kPreUnits; ++u) {
+    const int i = u * kPreThreads + pt;
+    pre[u] = pt >= 0 && i < npre ? *reinterpret_cast<const int2*>(cand + 2 * i) : int2{0, 0};
   }
   __syncthreads();
   if (tid < NT) {
@@ -1044,6 +1039,90 @@ __device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, const int32_t*
   return sh.repair_mask;
 }
 
+// Top-k of a fitting row with d = nc - k in 1 .. kFewExtra extra candidates,
+// all of them in phase A's registers (pre[u] is pair u * kPreThreads + tid -
+// 64 in waves 1-3, nc <= kPreCap): all but the d smallest (by radix key, ties by
+// slot position).  Each of the d rounds finds the smallest pair not yet left
+// out with a tree over the thread's pairs, the wavefront minimum (DPP) and
+// the four waves' minima exchanged through LDS; the indices are then written
+// in slot order shifted past the left-out positions, so the stores stay
+// coalesced.  Every bound here is uniform, so the per-unit steps are scalar
+// branches over straight-line code with constant register indices.
+template <int NT>
+__device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, int k, int nc,
+                                                    const int2 (&pre)[kPreUnits], CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = wave_id();
+  k = __builtin_amdgcn_readfirstlane(k);
+  nc = __builtin_amdgcn_readfirstlane(nc);
+  const int d = nc - k;
+  int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
+  // (order key << 32) | position, all ones past nc (and in wave 0).  The
+  // stored candidate scores order as the scores do (the encoding maps (t, 2t]
+  // onto (0, t] and keeps the rest, with t > 0; ties stay ties), and none is
+  // NaN (a NaN never compares above a threshold), so the order key is the
+  // stored bits' radix key with -0 taken as +0: no decoding.
+  uint64_t key[kPreUnits];
+  const bool has = tid >= 64;  // a thread of waves 1-3
+  const int pt = tid - 64;
+  const int nu = static_cast<int>(ceil_div(nc, kPreThreads));  // units in use (uniform)
+#pragma unroll
+  for (int u = 0; u < kPreUnits; ++u) {
+    key[u] = ~0ull;
+    if (u < nu) {
+      const int i = u * kPreThreads + pt;
+      uint32_t b = static_cast<uint32_t>(pre[u].y);
+      b = b == 0x80000000u ? 0u : b;
+      b ^= static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u;
+      key[u] = has && i < nc ? (static_cast<uint64_t>(b) << 32) | static_cast<uint32_t>(i) : ~0ull;
+    }
+  }
+  uint32_t p[kFewExtra];
+#pragma unroll
+  for (int j = 0; j < kFewExtra; ++j) p[j] = 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < kFewExtra; ++j) {
+    if (j >= d) break;
+    uint64_t m[kPreUnits];
+#pragma unroll
+    for (int u = 0; u < kPreUnits; ++u) m[u] = key[u];
+#pragma unroll
+    for (int h = kPreUnits / 2; h > 0; h >>= 1)
+#pragma unroll
+      for (int u = 0; u < h; ++u) m[u] = min(m[u], m[u + h]);
+    const uint64_t wm = __ockl_wfred_min_u64(m[0]);
+    if (lane == 0) sh.low[j][w] = wm;
+    __syncthreads();
+    uint64_t g = sh.low[j][0];
+#pragma unroll
+    for (int q = 1; q < kWaves; ++q) g = min(g, sh.low[j][q]);
+    p[j] = static_cast<uint32_t>(g);
+    // the pair left out no longer competes
+#pragma unroll
+    for (int u = 0; u < kPreUnits; ++u)
+      if (u < nu) key[u] = key[u] == g ? ~0ull : key[u];
+  }
+  // (positions before the first left-out one already hold their index: the
+  // select kernel wrote candidate j < top_k to entry j)
+#pragma unroll
+  for (int u = 0; u < kPreUnits; ++u) {
+    const int i = u * kPreThreads + pt;
+    if (u < nu && has && i < nc) {
+      const uint32_t iu = static_cast<uint32_t>(i);
+      bool kept = true;
+      uint32_t shift = 0;
+#pragma unroll
+      for (int j = 0; j < kFewExtra; ++j) {
+        kept = kept && iu != p[j];
+        shift += (p[j] != 0xffffffffu && iu > p[j]) ? 1u : 0u;
+      }
+      if (kept && shift) out[i - shift] = pre[u].x;
+    }
+  }
+  for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
+}
+
 // ranges and Top-k finalize of row r (k = min(e_r, top_k)) from its final
 // candidate count nc, tie count nt and threshold th (the first npre candidate
 // pairs possibly loaded already, as finalize_topk takes them).
@@ -1056,6 +1135,49 @@ __device__ __forceinline__ void row_outputs(const SelectArgs& s, int r, int k, i
   }
   if (s.topk_idx) finalize_topk<NT>(s, r, k, nc, th, npre, sh);
   __syncthreads();
+}
+
+// Phase A's outputs of a fitting row, its first npre candidate pairs loading
+// into the registers of waves 1-3 (pre[u] = pair u * kPreThreads + tid - 64).  A row with exactly k
+// candidates has its Top-k from the select kernel already (entries past k
+// aside) and waits for none of these loads.
+template <int NT>
+__device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int k, int nc, int nt, float th, int npre,
+                                                const int2 (&pre)[kPreUnits], CtaShared<NT>& sh) {
+  const bool exact = nc == k;
+  const bool few = nc > k && nc - k <= kFewExtra && nc <= npre;
+  if (!s.topk_idx || exact || few) {
+    if (s.topk_idx && exact) {
+      int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
+      for (int i = k + threadIdx.x; i < s.top_k; i += kThreads) out[i] = -1;
+    } else if (s.topk_idx) {
+      // waves 1-3: their pairs in at once (the compiler would otherwise wait
+      // for all earlier memory operations before each store it predicates);
+      // wave 0 holds no pairs and has no store outstanding here but, in the
+      // CTA with the last count, the done flags'
+      if (threadIdx.x >= 64) wait_vm_done();
+      few_extra_from_regs<NT>(s, r, k, nc, pre, sh);
+    }
+    if (threadIdx.x == 0) {
+      s.ranges[r] = s.top_k - min(nt, s.top_k);
+      s.ranges[s.rows + r] = s.top_k + min(nc, s.capacity);
+    }
+    __syncthreads();
+    return;
+  }
+  // the pairs into LDS, where finalize_topk takes them (one wait for all)
+  const int tid = threadIdx.x;
+  wait_vm_done();
+#pragma unroll
+  for (int u = 0; u < kPreUnits; ++u) {
+    const int i = u * kPreThreads + tid - 64;
+    if (tid >= 64 && i < npre) {
+      sh.u.fin.idx[i] = pre[u].x;
+      sh.u.fin.key[i] = static_cast<uint32_t>(pre[u].y);
+    }
+  }
+  __syncthreads();
+  row_outputs<NT>(s, r, k, nc, nt, th, npre, sh);
 }
 
 // ---------------------------------------------------------------- finish
@@ -1109,13 +1231,21 @@ constexpr uint32_t kLayoutMagic = 0x41514d50u;
 struct Ws {
   uint32_t* base;
   int batch, rows;
-  // [0] job list entries reserved, [2] rows through phase A, [3..5] the
-  // layout of the last finish kernel (the select kernel clears [0..2] and the
-  // list before each finish kernel)
+  // [0,1] the progress word (below), [3..5] the layout of the last finish
+  // kernel (the select kernel clears [0..2], the flags and the list before
+  // each finish kernel)
   __device__ uint32_t* hdr() const { return base; }
-  __device__ uint32_t* list(int j) const { return base + 16 + j; }  // tile + 1, 0 until written
+  // rows through phase A (low half) and job list entries reserved (high half)
+  __device__ uint64_t* progress() const { return reinterpret_cast<uint64_t*>(base); }
+  // copy i of the done flag: 0 while phase A runs, then 1 + the number of jobs
+  // listed (the waiting CTAs poll copy blockIdx % kDoneFlags, 256 bytes apart,
+  // so their polls spread over many lines instead of queueing on one)
+  __device__ uint32_t* flag(int i) const { return base + 16 + kDoneFlagStride * i; }
+  __device__ uint32_t* list(int j) const { return base + 16 + kDoneFlags * kDoneFlagStride + j; }  // tile + 1, 0 until written
   // [0,1] claim word, [2] row mask, [3 + stage] items done in the stage
-  __device__ uint32_t* job(int b) const { return base + 16 + job_list_words(batch) + kJobWords * b; }
+  __device__ uint32_t* job(int b) const {
+    return base + 16 + kDoneFlags * kDoneFlagStride + job_list_words(batch) + kJobWords * b;
+  }
   __device__ uint64_t* claim(int b) const { return reinterpret_cast<uint64_t*>(job(b)); }
   // [0] digit prefix [1] rank left [2] bits known [3] bucket count
   __device__ uint32_t* row(int r) const { return job(batch) + kRowWords * r; }
@@ -1153,8 +1283,24 @@ __device__ __forceinline__ void publish_job(const SelectArgs& s, const Ws& ws, i
   wait_vm_done();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t j = atomicAdd(ws.hdr(), 1u);
-    st_wt(ws.list(static_cast<int>(j)), static_cast<uint32_t>(b + 1));
+    const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.progress()), 1ull << 32);
+    st_wt(ws.list(static_cast<int>(old >> 32)), static_cast<uint32_t>(b + 1));
+  }
+}
+
+// One row through phase A: the count (thread 0, after every store that lists
+// a job of the CTA has completed); it returns the progress word before it.
+__device__ __forceinline__ uint64_t count_row(const Ws& ws) {
+  return atomicAdd(reinterpret_cast<unsigned long long*>(ws.progress()), 1ull);
+}
+
+// Thread 0, with count_row's result: the count of the last row sets every copy
+// of the done flag to 1 + the jobs listed (final by then: each publisher lists
+// its job before it counts its row).
+__device__ __forceinline__ void flag_if_last(const Ws& ws, uint64_t old) {
+  if (static_cast<uint32_t>(old) + 1u == static_cast<uint32_t>(ws.rows)) {
+    const uint32_t v = static_cast<uint32_t>(old >> 32) + 1u;
+    for (int i = 0; i < kDoneFlags; ++i) st_wt(ws.flag(i), v);
   }
 }
 
@@ -1602,8 +1748,9 @@ __device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idl
   if (wave_id() == 0) {
     const int lane = lane_id();
     // (a workspace that was not left zeroed gives wrong results, not stray accesses)
-    const int njobs = min(static_cast<int>(ld_ag(ws.hdr())), ws.batch);
-    bool pending = ld_ag(ws.hdr() + 2) < static_cast<uint32_t>(ws.rows);
+    const uint32_t fl = ld_ag(ws.flag(static_cast<int>(blockIdx.x % kDoneFlags)));
+    const int njobs = fl ? min(static_cast<int>(fl - 1u), ws.batch) : 0;
+    bool pending = fl == 0u;  // phase A still running
     int got = -1, stage = 0, idx = 0;
     for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
       const int j = j0 + lane;
@@ -1667,35 +1814,41 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     st_wt(ws.hdr() + kHdrNextN, static_cast<uint32_t>(NT));
     st_wt(ws.hdr() + kHdrMagic, kLayoutMagic);
   }
-  uint32_t done_rows = 0;
-  bool published = false;
-  for (int r = blockIdx.x; r < s.rows; r += gridDim.x, ++done_rows) {
+  bool saw_repair = false;
+  for (int r = blockIdx.x; r < s.rows; r += gridDim.x) {
     const int b = r / NT, t = r - b * NT;
     // the row's first candidate pairs (all of them when it has at most top_k +
     // kFewExtra) are loaded together with the fit test's inputs
-    const int npre = s.topk_idx ? min(min(s.capacity, s.top_k + kFewExtra), kFinalizeLds) : 0;
+    const int npre = s.topk_idx ? min(min(s.capacity, s.top_k + kFewExtra), kPreCap) : 0;
+    int2 pre[kPreUnits];
     // every CTA working on a row of tile b finds the same mask; the one with
     // its lowest row publishes the job
-    const uint32_t mask = tile_fit<NT>(s, a.seq_lens + static_cast<int64_t>(b) * a.sl_stride, b, sh, r, npre);
+    const uint32_t mask = tile_fit<NT>(s, a.seq_lens + static_cast<int64_t>(b) * a.sl_stride, b, sh, r, npre, pre);
     const int L = sh.len;
     int end[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) end[u] = max(0, L - NT + u + 1);
     const int k = min(end[t], s.top_k);
+    saw_repair = saw_repair || mask != 0u;
+    // The row is through phase A once its fit is decided (and its job, if it
+    // publishes one, listed): the CTAs waiting for repair items leave as soon
+    // as every row is, while the fitting rows' outputs are still being written.
     if (!(mask & (1u << t))) {
-      row_outputs<NT>(s, r, k, sh.nc[t], sh.nt[t], sh.thr[t], npre, sh);
-    } else if ((mask & ((1u << t) - 1u)) == 0u) {
-      publish_job<NT>(s, ws, b, end, mask);
-      published = true;
+      // (wave 0 has no pair load in flight: its count returns after one round trip)
+      if (tid == 0) flag_if_last(ws, count_row(ws));
+      row_outputs_pre<NT>(s, r, k, sh.nc[t], sh.nt[t], sh.thr[t], npre, pre, sh);
+    } else {
+      if ((mask & ((1u << t) - 1u)) == 0u) publish_job<NT>(s, ws, b, end, mask);
+      if (tid == 0) {
+        wait_vm_done();  // the job's list entry first
+        flag_if_last(ws, count_row(ws));
+      }
     }
     __syncthreads();
   }
-  // rows through phase A: the outputs' stores need not have completed (no one
-  // here reads them), only a listed job's entry
-  if (done_rows && tid == 0) {
-    if (published) wait_vm_done();
-    atomicAdd(ws.hdr() + 2, done_rows);
-  }
+  // With at least as many CTAs without rows as with, those are the repair's
+  // hands: a CTA whose rows all fit leaves without polling for items.
+  if (!saw_repair && blockIdx.x < s.rows && 2 * static_cast<int64_t>(s.rows) <= gridDim.x) return;
   int idle = 0;
   while (true) {
     claim_item<NT, kFused>(a, ws, idle, sh);
@@ -1737,8 +1890,10 @@ __device__ __forceinline__ void prepare_workspace(const SelectArgs& s, int batch
          i += static_cast<int64_t>(gridDim.x) * kThreads)
       s.ws[16 + i] = 0u;
   } else if (blockIdx.x == 0) {
-    // the job list (the claim words a late claim attempt incremented sit where
-    // this call's jobs are, and each publish rewrites its job's)
+    // the done flags and the job list (the claim words a late claim attempt
+    // incremented sit where this call's jobs are, and each publish rewrites
+    // its job's)
+    for (int i = tid; i < kDoneFlags; i += kThreads) *ws.flag(i) = 0u;
     for (int i = tid; i < job_list_words(batch); i += kThreads) *ws.list(i) = 0u;
   }
   if (blockIdx.x == 0 && tid < 3) s.ws[tid] = 0u;
@@ -1890,6 +2045,22 @@ logits_kernel(PagedArgs a, float* out, int64_t ld) {
   }
 }
 
+// A wave's n candidate pairs of row r into slots top_k + base + i (those past
+// the capacity dropped).  With a Top-k output, candidate j < top_k also writes
+// its index to topk_idx[r][j]: a row that ends with exactly k candidates then
+// already holds its Top-k in slot order, which the finish kernel keeps; in
+// every other case the finish kernel rewrites entries 0 .. top_k - 1.
+__device__ __forceinline__ void store_cands(const SelectArgs& s, int r, int base, const int2* list, int n) {
+  int32_t* slots = s.candidates + (static_cast<int64_t>(r) * (s.top_k + s.capacity) + s.top_k) * 2;
+  int32_t* out = s.topk_idx ? s.topk_idx + static_cast<int64_t>(r) * s.top_k : nullptr;
+  for (int i = lane_id(); i < n; i += 64) {
+    const int j = base + i;
+    const int2 e = list[i];
+    if (j < s.capacity) *reinterpret_cast<int2*>(slots + 2 * j) = e;
+    if (out && j < s.top_k) out[j] = e.x;
+  }
+}
+
 // The select kernels' CTA body: score keys [k0, k1) of the CTA's request and
 // select each wave's 64-key groups straight from the scores in registers onto
 // the wave's own lists, which reach the slots when nearly full (one counter
@@ -1926,8 +2097,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
       if (lane == 0) old = reserve_pair(s.counters + 2 * r, ncl[t], ntl[t]);
       const int bc = __shfl(static_cast<int>(static_cast<uint32_t>(old)), 0);
       const int bt = __shfl(static_cast<int>(static_cast<uint32_t>(old >> 32)), 0);
-      for (int i = lane; i < ncl[t]; i += 64)
-        if (bc + i < s.capacity) *reinterpret_cast<int2*>(slots + 2 * (s.top_k + bc + i)) = sh.cand[w][t][i];
+      store_cands(s, r, bc, sh.cand[w][t], ncl[t]);
       for (int i = lane; i < ntl[t]; i += 64)
         if (bt + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - bt - i)) = sh.tie[w][t][i];
       ncl[t] = 0;
@@ -1997,8 +2167,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
         bt += sh.count[q][t][1];
       }
       int32_t* slots = s.candidates + static_cast<int64_t>(b * NT + t) * (s.top_k + s.capacity) * 2;
-      for (int i = lane; i < ncl[t]; i += 64)
-        if (bc + i < s.capacity) *reinterpret_cast<int2*>(slots + 2 * (s.top_k + bc + i)) = sh.cand[w][t][i];
+      store_cands(s, b * NT + t, bc, sh.cand[w][t], ncl[t]);
       for (int i = lane; i < ntl[t]; i += 64)
         if (bt + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - bt - i)) = sh.tie[w][t][i];
     }

@@ -19,6 +19,8 @@ constexpr int kHistCopies = 8;          // repair workspace: copies of a row's r
 constexpr int kFinalizeLds = 4096;      // keys a CTA keeps in LDS for a final radix select
 constexpr int kJobWords = 16;           // repair workspace: words per tile job
 constexpr int kRowWords = 16;           // repair workspace: words per row state
+constexpr int kDoneFlags = 64;          // repair workspace: copies of the end-of-phase-A flag
+constexpr int kDoneFlagStride = 64;     // repair workspace: words between two copies (256 bytes)
 constexpr int kRescoreItemKeys = 2048;  // keys per repair item recomputed from the KV pages
 constexpr int kSelectItemKeys = 4096;   // keys per repair item read back as scores
 
@@ -30,11 +32,12 @@ constexpr int64_t job_list_words(int64_t batch) { return (batch + 15) / 16 * 16;
 // Floats per row of the fused repair's score buffer (256-byte rows).
 constexpr int64_t score_stride(int64_t max_context) { return ceil_div(max_context, 64) * 64; }
 
-// Repair workspace: a header, the job list, one job per tile, and per row its
-// state, kHistCopies copies of a radix histogram and a bucket buffer of (index,
-// score) pairs; this much is the finish stage's state (in words).
+// Repair workspace: a header, kDoneFlags copies of a flag, the job list, one
+// job per tile, and per row its state, kHistCopies copies of a radix histogram
+// and a bucket buffer of (index, score) pairs; this much is the finish stage's
+// state (in words).
 constexpr int64_t workspace_state_words(int64_t batch, int64_t rows) {
-  return 16 + job_list_words(batch) + kJobWords * batch +
+  return 16 + kDoneFlags * kDoneFlagStride + job_list_words(batch) + kJobWords * batch +
          (kRowWords + kHistCopies * kRadixBins + 2 * kFinalizeLds) * rows;
 }
 
