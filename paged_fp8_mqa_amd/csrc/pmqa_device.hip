@@ -607,7 +607,9 @@ struct CtaShared {
   int32_t pos[2];
   int32_t job[3];      // claimed repair item: tile (or -1: none open, -2: leave), stage, index
   int32_t next_stage;
-  uint64_t low[kFewExtra][kWaves];  // few_extra_topk: each wave's smallest (key, position) pair per round
+  // few_extra_topk: each wave's smallest (key, position) pair per round;
+  // few_extra_from_regs: each wave's smallest packed keys
+  uint64_t low[kFewExtra][kWaves];
 };
 
 // Shared memory of a select kernel CTA: each wave's candidate and tie lists,
@@ -1039,69 +1041,112 @@ __device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, const int32_t*
   return sh.repair_mask;
 }
 
-// Top-k of a fitting row with d = nc - k in 1 .. kFewExtra extra candidates,
-// all of them in phase A's registers (pre[u] is pair u * kPreThreads + tid -
-// 64 in waves 1-3, nc <= kPreCap): all but the d smallest (by radix key, ties by
-// slot position).  Each of the d rounds finds the smallest pair not yet left
-// out with a tree over the thread's pairs, the wavefront minimum (DPP) and
-// the four waves' minima exchanged through LDS; the indices are then written
-// in slot order shifted past the left-out positions, so the stores stay
-// coalesced.  Every bound here is uniform, so the per-unit steps are scalar
-// branches over straight-line code with constant register indices.
-template <int NT>
+// The D smallest of a set of doubles, kept sorted in m[0..D-1]; kFewBig pads.
+constexpr double kFewBig = 1152921504606846976.0;  // 2^60, above every packed key
+template <int D>
+struct Smallest {
+  double m[D];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int j = 0; j < D; ++j) m[j] = kFewBig;
+  }
+  __device__ __forceinline__ void insert(double x) {
+    if constexpr (D >= 3) m[2] = fmin(m[2], fmax(m[1], x));
+    if constexpr (D >= 2) m[1] = fmin(m[1], fmax(m[0], x));
+    m[0] = fmin(m[0], x);
+  }
+  // The D smallest of the union with another sorted set o: the j-th smallest
+  // of two sorted lists is the least of the maxima of their (i, j - i) prefixes.
+  __device__ __forceinline__ void merge(const Smallest& o) {
+    const double a1 = m[0], a2 = o.m[0];
+    if constexpr (D >= 3) m[2] = fmin(fmin(m[2], o.m[2]), fmin(fmax(a1, o.m[1]), fmax(m[1], a2)));
+    if constexpr (D >= 2) m[1] = fmin(fmax(a1, a2), fmin(m[1], o.m[1]));
+    m[0] = fmin(a1, a2);
+  }
+};
+
+// Lane l's double from the lane the DPP control Ctrl names (kFewBig where it
+// names none, or in a row outside RowMask).
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(kFewBig));
+  const int lo = __builtin_amdgcn_update_dpp(static_cast<int>(static_cast<uint32_t>(b)),
+                                             static_cast<int>(static_cast<uint32_t>(u)), Ctrl, RowMask, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(static_cast<int>(static_cast<uint32_t>(b >> 32)),
+                                             static_cast<int>(static_cast<uint32_t>(u >> 32)), Ctrl, RowMask, 0xf, false);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                                     static_cast<uint32_t>(lo)));
+}
+template <int Ctrl, int RowMask, int D>
+__device__ __forceinline__ void dpp_merge(Smallest<D>& x) {
+  Smallest<D> o;
+#pragma unroll
+  for (int j = 0; j < D; ++j) o.m[j] = dpp_f64<Ctrl, RowMask>(x.m[j]);
+  x.merge(o);
+}
+
+// Top-k of a fitting row with D = nc - k in 1 .. kFewExtra extra candidates,
+// all of them in the registers of waves 1-3 (pre[u] is pair u * kPreThreads +
+// tid - 64, nc <= kPreCap): all but the D smallest, by score and then slot
+// position.  Each pair becomes one exact double, order key * 4096 + position
+// (below 2^44).  The stored candidate scores order as the scores do (the
+// encoding maps (t, 2t] onto (0, t] and keeps the rest, with t > 0; ties stay
+// ties) and none is NaN (a NaN never compares above a threshold), so the order
+// key is the stored bits' radix key with -0 taken as +0.  One pass: each
+// thread keeps its D smallest, a DPP reduction leaves the wave's in lane 63,
+// and the four waves' are merged through LDS.  The indices are then written in
+// slot order shifted past the left-out positions, so the stores stay coalesced.
+template <int NT, int D>
 __device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, int k, int nc,
                                                     const int2 (&pre)[kPreUnits], CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
-  const int lane = lane_id();
   const int w = wave_id();
-  k = __builtin_amdgcn_readfirstlane(k);
-  nc = __builtin_amdgcn_readfirstlane(nc);
-  const int d = nc - k;
   int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
-  // (order key << 32) | position, all ones past nc (and in wave 0).  The
-  // stored candidate scores order as the scores do (the encoding maps (t, 2t]
-  // onto (0, t] and keeps the rest, with t > 0; ties stay ties), and none is
-  // NaN (a NaN never compares above a threshold), so the order key is the
-  // stored bits' radix key with -0 taken as +0: no decoding.
-  uint64_t key[kPreUnits];
   const bool has = tid >= 64;  // a thread of waves 1-3
   const int pt = tid - 64;
   const int nu = static_cast<int>(ceil_div(nc, kPreThreads));  // units in use (uniform)
+  Smallest<D> sm;
+  sm.init();
 #pragma unroll
   for (int u = 0; u < kPreUnits; ++u) {
-    key[u] = ~0ull;
     if (u < nu) {
       const int i = u * kPreThreads + pt;
       uint32_t b = static_cast<uint32_t>(pre[u].y);
       b = b == 0x80000000u ? 0u : b;
       b ^= static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u;
-      key[u] = has && i < nc ? (static_cast<uint64_t>(b) << 32) | static_cast<uint32_t>(i) : ~0ull;
+      if (has && i < nc) sm.insert(__builtin_fma(static_cast<double>(b), 4096.0, static_cast<double>(i)));
     }
   }
-  uint32_t p[kFewExtra];
+  // the wave's D smallest into lane 63
+  dpp_merge<0x111, 0xf>(sm);  // row_shr:1
+  dpp_merge<0x112, 0xf>(sm);  // row_shr:2
+  dpp_merge<0x114, 0xf>(sm);  // row_shr:4
+  dpp_merge<0x118, 0xf>(sm);  // row_shr:8
+  dpp_merge<0x142, 0xa>(sm);  // row_bcast:15
+  dpp_merge<0x143, 0xc>(sm);  // row_bcast:31
+  double* xw = reinterpret_cast<double*>(&sh.low[0][0]);  // the waves' sets (8-byte aligned)
+  static_assert(kFewExtra * kWaves >= D * kWaves, "room for every wave's set");
+  if (lane_id() == 63) {
 #pragma unroll
-  for (int j = 0; j < kFewExtra; ++j) p[j] = 0xffffffffu;
+    for (int j = 0; j < D; ++j) xw[D * w + j] = sm.m[j];
+  }
+  __syncthreads();
+  Smallest<D> all;
 #pragma unroll
-  for (int j = 0; j < kFewExtra; ++j) {
-    if (j >= d) break;
-    uint64_t m[kPreUnits];
+  for (int j = 0; j < D; ++j) all.m[j] = xw[D + j];  // wave 0 holds none
 #pragma unroll
-    for (int u = 0; u < kPreUnits; ++u) m[u] = key[u];
+  for (int q = 2; q < kWaves; ++q) {
+    Smallest<D> o;
 #pragma unroll
-    for (int h = kPreUnits / 2; h > 0; h >>= 1)
+    for (int j = 0; j < D; ++j) o.m[j] = xw[D * q + j];
+    all.merge(o);
+  }
+  uint32_t p[D];  // the left-out slot positions
 #pragma unroll
-      for (int u = 0; u < h; ++u) m[u] = min(m[u], m[u + h]);
-    const uint64_t wm = __ockl_wfred_min_u64(m[0]);
-    if (lane == 0) sh.low[j][w] = wm;
-    __syncthreads();
-    uint64_t g = sh.low[j][0];
-#pragma unroll
-    for (int q = 1; q < kWaves; ++q) g = min(g, sh.low[j][q]);
-    p[j] = static_cast<uint32_t>(g);
-    // the pair left out no longer competes
-#pragma unroll
-    for (int u = 0; u < kPreUnits; ++u)
-      if (u < nu) key[u] = key[u] == g ? ~0ull : key[u];
+  for (int j = 0; j < D; ++j) {
+    const double v = all.m[j];
+    p[j] = static_cast<uint32_t>(v - 4096.0 * floor(v * (1.0 / 4096.0)));
   }
   // (positions before the first left-out one already hold their index: the
   // select kernel wrote candidate j < top_k to entry j)
@@ -1113,9 +1158,9 @@ __device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, 
       bool kept = true;
       uint32_t shift = 0;
 #pragma unroll
-      for (int j = 0; j < kFewExtra; ++j) {
+      for (int j = 0; j < D; ++j) {
         kept = kept && iu != p[j];
-        shift += (p[j] != 0xffffffffu && iu > p[j]) ? 1u : 0u;
+        shift += iu > p[j] ? 1u : 0u;
       }
       if (kept && shift) out[i - shift] = pre[u].x;
     }
@@ -1156,7 +1201,10 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
       // wave 0 holds no pairs and has no store outstanding here but, in the
       // CTA with the last count, the done flags'
       if (threadIdx.x >= 64) wait_vm_done();
-      few_extra_from_regs<NT>(s, r, k, nc, pre, sh);
+      static_assert(kFewExtra == 3, "one instance per count of extra candidates");
+      if (nc - k == 1) few_extra_from_regs<NT, 1>(s, r, k, nc, pre, sh);
+      else if (nc - k == 2) few_extra_from_regs<NT, 2>(s, r, k, nc, pre, sh);
+      else few_extra_from_regs<NT, 3>(s, r, k, nc, pre, sh);
     }
     if (threadIdx.x == 0) {
       s.ranges[r] = s.top_k - min(nt, s.top_k);
