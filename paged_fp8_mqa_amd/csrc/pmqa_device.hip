@@ -90,6 +90,8 @@ struct SelectArgs {
   int64_t ws_words;     // its size in 32-bit words
   float* scores;        // fused repair: the workspace's score buffer, row r at scores + r * score_ld
   int64_t score_ld;
+  float* keep;          // fused select: the main pass writes every score here too (the score
+                        // buffer, next_n >= 2), or null
   int32_t capacity;
   int32_t top_k;
   int32_t rows;
@@ -1432,28 +1434,35 @@ __device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws
   const int bits = pass_bits(pass);
   const int nb = 1 << bits;
   // each row's histogram: the sum of its copies, which are cleared for the next
-  // pass (all of a thread's loads in flight at once)
+  // pass.  Every row's copies are loaded together (kHistCopies * nb / kThreads
+  // words a thread and row), so the sum costs one round trip, not one per row
+  // and half histogram.
+  constexpr int kJ = kRadixBins / kThreads;  // bins of a thread
+  uint32_t v[NT][kJ][kHistCopies];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(mask & (1u << t))) continue;
+    const uint32_t* gh = ws.hist(b * NT + t, 0);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int c = 0; c < kHistCopies; ++c)
+        v[t][j][c] = j * kThreads < nb ? ld_ag(gh + c * kRadixBins + j * kThreads + tid) : 0u;
+  }
+#pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (!(mask & (1u << t))) continue;
     uint32_t* gh = ws.hist(b * NT + t, 0);
-    constexpr int kJ = kRadixBins / kThreads / 2;  // bins of a thread per half
-#pragma unroll 1
-    for (int i0 = 0; i0 < nb; i0 += kJ * kThreads) {
-      uint32_t v[kJ][kHistCopies];
 #pragma unroll
-      for (int j = 0; j < kJ; ++j)
+    for (int j = 0; j < kJ; ++j) {
+      if (j * kThreads >= nb) continue;
+      uint32_t sum = 0u;
 #pragma unroll
-        for (int c = 0; c < kHistCopies; ++c) v[j][c] = ld_ag(gh + c * kRadixBins + i0 + j * kThreads + tid);
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        uint32_t sum = 0u;
-#pragma unroll
-        for (int c = 0; c < kHistCopies; ++c) {
-          sum += v[j][c];
-          if (v[j][c]) st_wt(gh + c * kRadixBins + i0 + j * kThreads + tid, 0u);
-        }
-        sh.u.hist[t][i0 + j * kThreads + tid] = sum;
+      for (int c = 0; c < kHistCopies; ++c) {
+        sum += v[t][j][c];
+        if (v[t][j][c]) st_wt(gh + c * kRadixBins + j * kThreads + tid, 0u);
       }
+      sh.u.hist[t][j * kThreads + tid] = sum;
     }
   }
   __syncthreads();
@@ -2158,6 +2167,10 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
           // this group's candidates and ties onto the wave's lists, positions
           // from the ballots
           const int p = p0 + lane;
+          if (s.keep && p < k1) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) s.keep[static_cast<int64_t>(b * NT + t) * s.score_ld + p] = E[t];
+          }
           bool flushed = false;
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
@@ -2383,6 +2396,7 @@ SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int
   s.ws_words = s.ws ? static_cast<int64_t>(workspace_bytes / 4) : 0;
   s.scores = s.ws && fused ? reinterpret_cast<float*>(s.ws + workspace_state_words(batch, rows)) : nullptr;
   s.score_ld = score_stride(max_context);
+  s.keep = nullptr;
   s.capacity = cap;
   s.top_k = top_k;
   s.rows = rows;
@@ -2512,11 +2526,28 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
-  const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   batch_size, static_cast<int32_t>(rows), max_context, true, workspace,
-                                   workspace_bytes);
+  SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
+                             batch_size, static_cast<int32_t>(rows), max_context, true, workspace, workspace_bytes);
+  // With next_n >= 2 the main pass also writes every score into the
+  // workspace's score buffer (4 * next_n bytes a key against 132 read), and
+  // the finish stage is the one of a select over a logits matrix, run on that
+  // buffer: a repair then reads 4-byte scores instead of scoring its requests
+  // again from the KV pages (next_n = 1 keeps the re-scoring repair: there
+  // the writes would cost more than the rare repair saves).
+  const bool keep = s.ws && next_n >= 2;
+  if (keep) s.keep = s.scores;
   st = launch_k<FusedK>(next_n, true, hs, a, s);
-  if (st == PMQA_OK && s.ws) st = launch_k<FusedFinishK>(next_n, false, hs, a, s);
+  if (st == PMQA_OK && s.ws) {
+    if (keep) {
+      const LogitsArgs la{s.scores, s.score_ld, seq_lens, seq_lens_stride, batch_size, 0, 1};
+      SelectArgs sf = s;
+      sf.scores = nullptr;
+      sf.keep = nullptr;
+      st = launch_k<SelectFinishK>(next_n, false, hs, la, sf);
+    } else {
+      st = launch_k<FusedFinishK>(next_n, false, hs, a, s);
+    }
+  }
   return st != PMQA_OK ? st : launched();
 }
 

@@ -269,9 +269,10 @@ def test_workspace_reused_across_batch_sizes():
 
 @pytest.mark.parametrize("next_n", [1, 2, 3, 4])
 def test_repair_rescore_bits_equal_logits_kernel(next_n):
-    """The fused repair scores a repaired request again (q and weights in
-    registers) and keeps the scores in the workspace's score buffer; they are
-    the logits kernel's bits (q and weights from LDS for next_n >= 3)."""
+    """The fused select's score buffer holds the logits kernel's bits: for
+    next_n = 1 the repair scores a repaired request again and keeps its scores
+    there, for next_n >= 2 the main pass writes every row's scores there (q and
+    weights from LDS for next_n >= 3)."""
     wl = W.small_random(71 + next_n, [3000, 5000, 700, 1], next_n, 64, top_k=128, capacity=256)
     d = dev(wl)
     out, _ = run_logits(wl, d)
