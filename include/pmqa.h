@@ -169,19 +169,22 @@ pmqa_status pmqa_mqa_logits(
  *                repair job for its rows that do not fit (per-row radix
  *                histogram passes, then a collect pass into a per-row bucket
  *                buffer, or an exact re-select), split into items of a few
- *                thousand keys run grid-wide.  The fused select's repair
- *                computes a repaired row's scores once, in its first pass, and
- *                keeps them in the workspace for the later passes.  Calls that
- *                share a workspace must not run concurrently.
+ *                thousand keys run grid-wide.  The fused select keeps scores
+ *                in the workspace's score buffer: with next_n = 1 its repair
+ *                computes a repaired row's scores once, in its first pass, for
+ *                the later passes; with next_n >= 2 the select kernel writes
+ *                every row's scores there and the repair reads them as the
+ *                repair of pmqa_indexer_topk reads its logits matrix.  Calls
+ *                that share a workspace must not run concurrently.
  */
 
 /* Bytes of the finish-stage workspace of entry point `which` (1
  * pmqa_indexer_topk, 2 pmqa_fused_logits_select) for batch_size requests of
- * next_n rows and max_context keys: the finish stage's state (about 41 KB per
+ * next_n rows and max_context keys: the finish stage's state (about 98 KB per
  * row), plus for the fused select a score buffer of
- * round_up(max_context, 64) floats per row, where the repair keeps the scores
- * of the rows it repairs.  Returns 0 for an unknown `which` or a negative
- * size. */
+ * round_up(max_context, 64) floats per row (the scores of the repaired rows
+ * with next_n = 1, of every row with next_n >= 2).  Returns 0 for an unknown
+ * `which` or a negative size. */
 size_t pmqa_workspace_bytes(int32_t which, int32_t batch_size, int32_t next_n, int32_t max_context);
 
 pmqa_status pmqa_check_select_args(
