@@ -222,6 +222,26 @@ def test_fused_large_batch_grid():
     _check(wl, fused, True, scores64=ref, tau=tau, rows=rows)
 
 
+def test_fused_large_batch_fitting_rows():
+    """More rows than the finish kernel has CTAs, thresholds at each row's k-th
+    score: most rows fit (their Top-k from the select kernel's slots, or with a
+    few extra candidates left out), several rows per finish CTA, every row
+    counted through phase A before the waiting CTAs leave."""
+    rng = np.random.default_rng(8)
+    seq = [int(x) for x in rng.integers(0, 1500, size=1100)]
+    wl = W.small_random(43, seq, 1, 64, top_k=32, capacity=64)
+    ref, tau = _oracle_rows(wl, None)
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    thr = _sigma_thresholds(ref, ends, wl.top_k, "kth")
+    d = dev(wl)
+    fused = run_fused(wl, d, thr)
+    _check(wl, fused, True, scores64=ref, tau=tau)
+    assert np.sum(fused["thr"].view(np.int32) == thr.view(np.int32)) > wl.rows // 2  # most rows fit
+    out, _ = run_logits(wl, d)
+    unf = run_select(wl, out, thr, max_context=wl.max_seq_len)
+    _same(wl, fused, unf)
+
+
 def test_fused_repeated_calls_reuse_arrivals():
     wl = W.small_random(41, [3000, 5000], 2, 64, top_k=128, capacity=256)
     ref, tau = _oracle_rows(wl, None)
