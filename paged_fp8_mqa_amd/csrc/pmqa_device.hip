@@ -1927,8 +1927,9 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
   }
 }
 
-// Run by the select kernel, before any finish kernel of this call: the finish
-// stage's header and job list start empty.  Between calls the workspace holds
+// Run by every CTA of the select kernel after its keys (so before any finish
+// kernel of this call): the finish stage's header, done flags and job list
+// start empty.  Between calls the workspace holds
 // only zeros in its state words (every job clears its own) -- except where a
 // call laid it out differently: the fused repair's score buffer starts right
 // after the state words, so another batch size or next_n puts state words
@@ -2127,7 +2128,6 @@ __device__ __forceinline__ void store_cands(const SelectArgs& s, int r, int base
 template <int NT, int kKeysPerCta, class Src, class Args>
 __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, MainShared<NT>& sh, v4i* stage,
                                             QLds<NT>* ql) {
-  if (s.ws) prepare_workspace<NT>(s, a.batch);
   Src src;
   src.bind(stage);
   src.bind_q(ql);
@@ -2233,6 +2233,9 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
         if (bt + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - bt - i)) = sh.tie[w][t][i];
     }
   });
+  // (last: its layout check is a load the CTA's start would otherwise wait
+  // for before it reads the lengths; the finish kernel starts after this one)
+  if (s.ws) prepare_workspace<NT>(s, a.batch);
 }
 
 
