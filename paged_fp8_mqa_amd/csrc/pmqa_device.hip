@@ -46,10 +46,12 @@ constexpr int kStageInt4 = 512;  // a wave's KV staging area: 64 keys x 128 byte
 template <int NT> constexpr int kWaveCand = NT >= 3 ? 64 : 256;
 template <int NT> constexpr int kWaveTie = NT >= 3 ? 32 : 64;
 constexpr int kFewExtra = 3;   // final select by value walk when at most this many keys are left out
-// Phase A: the candidate pairs of a row that every thread preloads (pair
-// u * kThreads + tid in unit u of thread tid).
+// Phase A: the candidate pairs of a row that waves 1-3 preload (pair
+// u * kPreThreads + tid - 64 in unit u of thread tid >= 64); wave 0 loads the
+// fit test's words and counts the row, with no pair load ahead of its atomic.
 constexpr int kPreUnits = 16;
-constexpr int kPreCap = kPreUnits * kThreads;
+constexpr int kPreThreads = kThreads - 64;
+constexpr int kPreCap = kPreUnits * kPreThreads;
 
 struct PagedArgs {
   const uint8_t* q;
@@ -1004,8 +1006,8 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
 // Fit test of tile b (its request's length at *len) from its counters: fills
 // sh.nc, sh.nt, sh.thr and sh.len and returns the mask of rows that do not
 // fit.  It also loads the first npre <= kPreCap candidate pairs of row r_pre
-// (index, score bits) into registers: pair u * kThreads + tid into pre[u].
-// All of these loads are issued together.
+// (index, score bits) into the registers of waves 1-3: pair u * kPreThreads +
+// tid - 64 into pre[u].  All of these loads are issued together.
 template <int NT>
 __device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, const int32_t* len, int b, CtaShared<NT>& sh,
                                              int r_pre, int npre, int2 (&pre)[kPreUnits]) {
@@ -1021,10 +1023,11 @@ __device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, const int32_t*
     L = *len;
   }
   const int32_t* cand = s.candidates + (static_cast<int64_t>(r_pre) * (s.top_k + s.capacity) + s.top_k) * 2;
+  const int pt = tid - 64;
 #pragma unroll
   for (int u = 0; u < kPreUnits; ++u) {
-    const int i = u * kThreads + tid;
-    pre[u] = i < npre ? *reinterpret_cast<const int2*>(cand + 2 * i) : int2{0, 0};
+    const int i = u * kPreThreads + pt;
+    pre[u] = pt >= 0 && i < npre ? *reinterpret_cast<const int2*>(cand + 2 * i) : int2{0, 0};
   }
   __syncthreads();
   if (tid < NT) {
@@ -1086,8 +1089,8 @@ __device__ __forceinline__ void dpp_merge(Smallest<D>& x) {
 }
 
 // Top-k of a fitting row with D = nc - k in 1 .. kFewExtra extra candidates,
-// all of them in registers (pre[u] is pair u * kThreads + tid, nc <= kPreCap):
-// all but the D smallest, by score and then slot
+// all of them in the registers of waves 1-3 (pre[u] is pair u * kPreThreads +
+// tid - 64, nc <= kPreCap): all but the D smallest, by score and then slot
 // position.  Each pair becomes one exact double, order key * 4096 + position
 // (below 2^44).  The stored candidate scores order as the scores do (the
 // encoding maps (t, 2t] onto (0, t] and keeps the rest, with t > 0; ties stay
@@ -1095,26 +1098,26 @@ __device__ __forceinline__ void dpp_merge(Smallest<D>& x) {
 // key is the stored bits' radix key with -0 taken as +0.  One pass: each
 // thread keeps its D smallest, a DPP reduction leaves the wave's in lane 63,
 // and the four waves' are merged through LDS.  The indices are then written in
-// slot order shifted past the left-out positions, so the stores stay coalesced
-// (units wholly before the first left-out slot are skipped: the select kernel
-// wrote their indices already).
+// slot order shifted past the left-out positions, so the stores stay coalesced.
 template <int NT, int D>
 __device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, int k, int nc,
                                                     const int2 (&pre)[kPreUnits], CtaShared<NT>& sh) {
   const int tid = threadIdx.x;
   const int w = wave_id();
   int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
-  const int nu = static_cast<int>(ceil_div(nc, kThreads));  // units in use (uniform)
+  const bool has = tid >= 64;  // a thread of waves 1-3
+  const int pt = tid - 64;
+  const int nu = static_cast<int>(ceil_div(nc, kPreThreads));  // units in use (uniform)
   Smallest<D> sm;
   sm.init();
 #pragma unroll
   for (int u = 0; u < kPreUnits; ++u) {
     if (u < nu) {
-      const int i = u * kThreads + tid;
+      const int i = u * kPreThreads + pt;
       uint32_t b = static_cast<uint32_t>(pre[u].y);
       b = b == 0x80000000u ? 0u : b;
       b ^= static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u;
-      if (i < nc) sm.insert(__builtin_fma(static_cast<double>(b), 4096.0, static_cast<double>(i)));
+      if (has && i < nc) sm.insert(__builtin_fma(static_cast<double>(b), 4096.0, static_cast<double>(i)));
     }
   }
   // the wave's D smallest into lane 63
@@ -1133,28 +1136,26 @@ __device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, 
   __syncthreads();
   Smallest<D> all;
 #pragma unroll
-  for (int j = 0; j < D; ++j) all.m[j] = xw[j];
+  for (int j = 0; j < D; ++j) all.m[j] = xw[D + j];  // wave 0 holds none
 #pragma unroll
-  for (int q = 1; q < kWaves; ++q) {
+  for (int q = 2; q < kWaves; ++q) {
     Smallest<D> o;
 #pragma unroll
     for (int j = 0; j < D; ++j) o.m[j] = xw[D * q + j];
     all.merge(o);
   }
   uint32_t p[D];  // the left-out slot positions
-  uint32_t pmin = 0xffffffffu;
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     const double v = all.m[j];
-    p[j] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v - 4096.0 * floor(v * (1.0 / 4096.0))));
-    pmin = min(pmin, p[j]);
+    p[j] = static_cast<uint32_t>(v - 4096.0 * floor(v * (1.0 / 4096.0)));
   }
   // (positions before the first left-out one already hold their index: the
   // select kernel wrote candidate j < top_k to entry j)
 #pragma unroll
   for (int u = 0; u < kPreUnits; ++u) {
-    const int i = u * kThreads + tid;
-    if (u < nu && static_cast<uint32_t>((u + 1) * kThreads) > pmin + 1u && i < nc) {
+    const int i = u * kPreThreads + pt;
+    if (u < nu && has && i < nc) {
       const uint32_t iu = static_cast<uint32_t>(i);
       bool kept = true;
       uint32_t shift = 0;
@@ -1184,7 +1185,7 @@ __device__ __forceinline__ void row_outputs(const SelectArgs& s, int r, int k, i
 }
 
 // Phase A's outputs of a fitting row, its first npre candidate pairs loading
-// into registers (pre[u] = pair u * kThreads + tid).  A row with exactly k
+// into the registers of waves 1-3 (pre[u] = pair u * kPreThreads + tid - 64).  A row with exactly k
 // candidates has its Top-k from the select kernel already (entries past k
 // aside) and waits for none of these loads.
 template <int NT>
@@ -1197,9 +1198,11 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
       int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
       for (int i = k + threadIdx.x; i < s.top_k; i += kThreads) out[i] = -1;
     } else if (s.topk_idx) {
-      // the pairs in at once (the compiler would otherwise wait for all
-      // earlier memory operations before each store it predicates)
-      wait_vm_done();
+      // waves 1-3: their pairs in at once (the compiler would otherwise wait
+      // for all earlier memory operations before each store it predicates);
+      // wave 0 holds no pairs and has no store outstanding here but, in the
+      // CTA with the last count, the done flags'
+      if (threadIdx.x >= 64) wait_vm_done();
       static_assert(kFewExtra == 3, "one instance per count of extra candidates");
       if (nc - k == 1) few_extra_from_regs<NT, 1>(s, r, k, nc, pre, sh);
       else if (nc - k == 2) few_extra_from_regs<NT, 2>(s, r, k, nc, pre, sh);
@@ -1217,8 +1220,8 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
   wait_vm_done();
 #pragma unroll
   for (int u = 0; u < kPreUnits; ++u) {
-    const int i = u * kThreads + tid;
-    if (i < npre) {
+    const int i = u * kPreThreads + tid - 64;
+    if (tid >= 64 && i < npre) {
       sh.u.fin.idx[i] = pre[u].x;
       sh.u.fin.key[i] = static_cast<uint32_t>(pre[u].y);
     }
@@ -1856,47 +1859,6 @@ __device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idl
   __syncthreads();
 }
 
-// Every row's fit from the select kernel's final counters, read by every CTA
-// of the finish kernel (rows u * kThreads + tid, with their requests' lengths):
-// all CTAs read the same words, so they all find the same answer.  When every
-// row fits there is no repair: no CTA counts rows, writes the done flags or
-// waits for items, and the CTAs without rows leave after this one round trip.
-// Loads first (peek_rows), the test once they are in (peek_fit), so that a CTA
-// with rows has them in flight together with its fit test's loads.
-constexpr int kPeekUnits = 4;  // up to kPeekUnits * kThreads rows; more: counts and flags decide
-struct Peek {
-  int nc[kPeekUnits], nt[kPeekUnits], L[kPeekUnits];
-};
-template <int NT, class Args>
-__device__ __forceinline__ void peek_rows(const Args& a, const SelectArgs& s, Peek& pk) {
-#pragma unroll
-  for (int u = 0; u < kPeekUnits; ++u) {
-    const int r = u * kThreads + static_cast<int>(threadIdx.x);
-    pk.nc[u] = 0;
-    pk.nt[u] = 0;
-    pk.L[u] = 0;
-    if (r < s.rows) {
-      pk.nc[u] = s.counters[2 * r];
-      pk.nt[u] = s.counters[2 * r + 1];
-      pk.L[u] = a.seq_lens[static_cast<int64_t>(r / NT) * a.sl_stride];
-    }
-  }
-}
-template <int NT>
-__device__ __forceinline__ bool peek_fit(const SelectArgs& s, const Peek& pk) {
-  if (s.rows > kPeekUnits * kThreads) return false;  // (uniform)
-  bool fit = true;
-#pragma unroll
-  for (int u = 0; u < kPeekUnits; ++u) {
-    const int r = u * kThreads + static_cast<int>(threadIdx.x);
-    if (r < s.rows) {
-      const int k = min(max(0, pk.L[u] - NT + r % NT + 1), s.top_k);
-      fit = fit && pk.nc[u] <= s.capacity && pk.nc[u] + min(pk.nt[u], s.top_k) >= k;
-    }
-  }
-  return __syncthreads_and(fit) != 0;
-}
-
 // The finish kernel's CTA body: phase A over this CTA's rows, then repair
 // items until nothing is left.
 template <int NT, bool kFused, class Args>
@@ -1909,9 +1871,6 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     st_wt(ws.hdr() + kHdrNextN, static_cast<uint32_t>(NT));
     st_wt(ws.hdr() + kHdrMagic, kLayoutMagic);
   }
-  Peek pk;
-  peek_rows<NT>(a, s, pk);
-  bool no_repair = false, decided = false;  // (uniform)
   bool saw_repair = false;
   for (int r = blockIdx.x; r < s.rows; r += gridDim.x) {
     const int b = r / NT, t = r - b * NT;
@@ -1928,16 +1887,12 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     for (int u = 0; u < NT; ++u) end[u] = max(0, L - NT + u + 1);
     const int k = min(end[t], s.top_k);
     saw_repair = saw_repair || mask != 0u;
-    if (!decided) {
-      no_repair = peek_fit<NT>(s, pk);
-      decided = true;
-    }
     // The row is through phase A once its fit is decided (and its job, if it
     // publishes one, listed): the CTAs waiting for repair items leave as soon
     // as every row is, while the fitting rows' outputs are still being written.
     if (!(mask & (1u << t))) {
-      // (with no repair nobody waits for the count)
-      if (!no_repair && tid == 0) flag_if_last(ws, count_row(ws));
+      // (wave 0 has no pair load in flight: its count returns after one round trip)
+      if (tid == 0) flag_if_last(ws, count_row(ws));
       row_outputs_pre<NT>(s, r, k, sh.nc[t], sh.nt[t], sh.thr[t], npre, pre, sh);
     } else {
       if ((mask & ((1u << t) - 1u)) == 0u) publish_job<NT>(s, ws, b, end, mask);
@@ -1948,8 +1903,6 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     }
     __syncthreads();
   }
-  if (!decided) no_repair = peek_fit<NT>(s, pk);
-  if (no_repair) return;
   // With at least as many CTAs without rows as with, those are the repair's
   // hands: a CTA whose rows all fit leaves without polling for items.
   if (!saw_repair && blockIdx.x < s.rows && 2 * static_cast<int64_t>(s.rows) <= gridDim.x) return;
