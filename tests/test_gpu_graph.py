@@ -55,9 +55,12 @@ def _same(wl, a, b):
         assert set(a["topk"][r, :k].tolist()) == set(b["topk"][r, :k].tolist()), f"row {r} top-k"
 
 
+@pytest.mark.parametrize("next_n", [1, 2])
 @pytest.mark.parametrize("mode", ["inf", "mixed"])
-def test_fused_graph_replays_match_eager(mode):
-    wl = W.small_random(61, [3000, 700, 0, 5000], 2, 64, top_k=128, capacity=256)
+def test_fused_graph_replays_match_eager(mode, next_n):
+    """next_n = 1: the repair scores its rows again from the KV pages; next_n = 2:
+    the select kernel keeps every score and the repair reads them."""
+    wl = W.small_random(61, [3000, 700, 0, 5000], next_n, 64, top_k=128, capacity=256)
     d = dev(wl)
     ref = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
                                   wl.max_seq_len)
