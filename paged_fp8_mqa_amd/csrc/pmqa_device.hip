@@ -1258,11 +1258,11 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
 // found; if every row's bucket fits the bucket buffer the job moves to stage 4,
 // if every key bit is known to stage 5, else to the next pass; stages 4 and 5
 // lead to stage 6.  An item is
-// claimed by a 64-bit fetch-and-add on the job's (stage, next item) word: a
-// returned index below the stage's item count is the caller's item, a larger
-// one claims nothing.  Whoever completes a stage's last item runs the stage
-// change, which rewrites the word to (next stage, 0), or after stage 6 clears
-// the job's words.  A CTA with no open item waits (a bounded number of polls)
+// claimed by a 64-bit fetch-and-add on one of the job's kClaimWords (stage,
+// next) words, word q handing out items q, q + kClaimWords, ...: an item below
+// the stage's item count is the caller's, a larger one claims nothing.
+// Whoever completes a stage's last item runs the stage change, which rewrites
+// the words to (next stage, 0), or after stage 6 clears the job's words.  A CTA with no open item waits (a bounded number of polls)
 // while some CTA is still in phase A, a listed job is not yet written, or a job
 // is in a stage before 6 (its change opens new items), and leaves otherwise;
 // the wait only adds hands, since each job is carried to its end by the CTA that
@@ -1270,6 +1270,7 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
 // atomic (write-through) stores or atomic adds and read with agent-scope atomic
 // loads.  A job's last step clears its words; the select kernel clears the
 // header and the job list at its start, when no finish kernel can be running.
+constexpr int kClaimWords = 4;  // claim words per repair job
 constexpr int kStageHist0 = 1;
 constexpr int kStageCollect = 4;
 constexpr int kStageSelect = 5;
@@ -1277,6 +1278,7 @@ constexpr int kStageRows = 6;
 constexpr int kIdlePolls = 20000;  // bound on a CTA's polls without an item
 constexpr int kHdrBatch = 3, kHdrNextN = 4, kHdrMagic = 5;  // header words of the layout record
 constexpr uint32_t kLayoutMagic = 0x41514d50u;
+static_assert(2 * kClaimWords + 1 + 6 < kJobWords, "a job's claim words, mask and per-stage counts");
 
 struct Ws {
   uint32_t* base;
@@ -1292,11 +1294,17 @@ struct Ws {
   // so their polls spread over many lines instead of queueing on one)
   __device__ uint32_t* flag(int i) const { return base + 16 + kDoneFlagStride * i; }
   __device__ uint32_t* list(int j) const { return base + 16 + kDoneFlags * kDoneFlagStride + j; }  // tile + 1, 0 until written
-  // [0,1] claim word, [2] row mask, [3 + stage] items done in the stage
+  // [2q, 2q + 1] claim word q < kClaimWords, [2 kClaimWords] row mask,
+  // [2 kClaimWords + 1 + stage] items done in the stage
   __device__ uint32_t* job(int b) const {
     return base + 16 + kDoneFlags * kDoneFlagStride + job_list_words(batch) + kJobWords * b;
   }
-  __device__ uint64_t* claim(int b) const { return reinterpret_cast<uint64_t*>(job(b)); }
+  // Claim word q hands out items q, q + kClaimWords, ... of the job's stage: a
+  // CTA claims from word blockIdx % kClaimWords, so the atomics of a stage's
+  // claims spread over kClaimWords words instead of queueing on one.
+  __device__ uint64_t* claim(int b, int q) const { return reinterpret_cast<uint64_t*>(job(b) + 2 * q); }
+  __device__ uint32_t* mask_word(int b) const { return job(b) + 2 * kClaimWords; }
+  __device__ uint32_t* done_word(int b, int stage) const { return job(b) + 2 * kClaimWords + 1 + stage; }
   // [0] digit prefix [1] rank left [2] bits known [3] bucket count
   __device__ uint32_t* row(int r) const { return job(batch) + kRowWords * r; }
   // copy c of row r's radix histogram (items add into copy idx % kHistCopies,
@@ -1321,15 +1329,13 @@ __device__ __forceinline__ int stage_items(int stage, int L) {
 }
 
 // Phase A hands the rows of tile b in `mask` to phase B: their state words and
-// the claim word first, then (once those are complete) the list entry.
+// the claim words first, then (once those are complete) the list entry.
 template <int NT>
 __device__ __forceinline__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int (&end)[NT], uint32_t mask) {
   const int tid = threadIdx.x;
   if (tid < NT && (mask & (1u << tid))) st_wt(ws.row(b * NT + tid) + 1, static_cast<uint32_t>(min(end[tid], s.top_k)));
-  if (tid == 0) {
-    st_wt(ws.job(b) + 2, mask);
-    st_wt64(ws.claim(b), static_cast<uint64_t>(kStageHist0) << 32);
-  }
+  if (tid == 0) st_wt(ws.mask_word(b), mask);
+  if (tid < kClaimWords) st_wt64(ws.claim(b, tid), static_cast<uint64_t>(kStageHist0) << 32);
   wait_vm_done();
   __syncthreads();
   if (tid == 0) {
@@ -1502,7 +1508,7 @@ __device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws
   }
   wait_vm_done();
   __syncthreads();
-  if (tid == 0) st_wt64(ws.claim(b), static_cast<uint64_t>(next) << 32);
+  if (tid < kClaimWords) st_wt64(ws.claim(b, tid), static_cast<uint64_t>(next) << 32);
 }
 
 // Row r after the collect stage: its exact k-th largest key among its bucket
@@ -1678,7 +1684,7 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
                          CtaShared<NT>& sh, v4i* lds) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const uint32_t mask = ld_ag(ws.job(b) + 2);
+  const uint32_t mask = ld_ag(ws.mask_word(b));
   int end[NT];
   uint32_t pfx[NT];
   float thr2[NT];
@@ -1781,19 +1787,19 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
   wait_vm_done();
   __syncthreads();
   if (tid == 0)
-    sh.is_last = atomicAdd(ws.job(b) + 3 + stage, 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
+    sh.is_last = atomicAdd(ws.done_word(b, stage), 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
   __syncthreads();
   if (!sh.is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (stage < kStageCollect) {
     job_next_stage<NT>(s, ws, b, stage - kStageHist0, mask, sh);
   } else if (stage < kStageRows) {
-    if (tid == 0) st_wt64(ws.claim(b), static_cast<uint64_t>(kStageRows) << 32);
+    if (tid < kClaimWords) st_wt64(ws.claim(b, tid), static_cast<uint64_t>(kStageRows) << 32);
   } else {
     // the job is done: its words cleared for the next call (all but the claim
-    // word, which late claim attempts may still increment; the next publish of
-    // the tile rewrites it)
-    if (tid >= 2 && tid < kJobWords) st_wt(ws.job(b) + tid, 0u);
+    // words, which late claim attempts may still increment; the next publish
+    // of the tile rewrites them)
+    if (tid >= 2 * kClaimWords && tid < kJobWords) st_wt(ws.job(b) + tid, 0u);
   }
 }
 
@@ -1809,6 +1815,7 @@ __device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idl
     const int njobs = fl ? min(static_cast<int>(fl - 1u), ws.batch) : 0;
     bool pending = fl == 0u;  // phase A still running
     int got = -1, stage = 0, idx = 0;
+    const int q = static_cast<int>(blockIdx.x % kClaimWords);  // this CTA's claim word
     for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
       const int j = j0 + lane;
       int b = 0, len = 0;
@@ -1819,13 +1826,14 @@ __device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idl
         unwritten = e == 0u;
         if (!unwritten) {
           b = min(static_cast<int>(e) - 1, ws.batch - 1);
-          w = ld_ag64(ws.claim(b));
+          w = ld_ag64(ws.claim(b, q));
           len = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
         }
       }
       const uint32_t st = static_cast<uint32_t>(w >> 32);
       const bool open = st >= kStageHist0 && st <= kStageRows &&
-                        static_cast<uint32_t>(w) < static_cast<uint32_t>(stage_items<NT, kFused>(static_cast<int>(st), len));
+                        q + kClaimWords * static_cast<uint64_t>(static_cast<uint32_t>(w)) <
+                            static_cast<uint64_t>(stage_items<NT, kFused>(static_cast<int>(st), len));
       pending = pending || __ballot(unwritten || (st >= kStageHist0 && st < kStageRows)) != 0;
       uint64_t m = __ballot(open);
       const int rot = static_cast<int>(blockIdx.x & 63);  // spread CTAs over the open jobs
@@ -1836,12 +1844,12 @@ __device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idl
         const int bl = __shfl(b, l);
         const int ll = __shfl(len, l);
         unsigned long long old = 0;
-        if (lane == 0) old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.claim(bl)), 1ull);
+        if (lane == 0) old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.claim(bl, q)), 1ull);
         old = __shfl(old, 0);
         const uint32_t st2 = static_cast<uint32_t>(old >> 32);
-        const uint32_t i2 = static_cast<uint32_t>(old);
+        const uint64_t i2 = q + kClaimWords * static_cast<uint64_t>(static_cast<uint32_t>(old));
         if (st2 >= kStageHist0 && st2 <= kStageRows &&
-            i2 < static_cast<uint32_t>(stage_items<NT, kFused>(static_cast<int>(st2), ll))) {
+            i2 < static_cast<uint64_t>(stage_items<NT, kFused>(static_cast<int>(st2), ll))) {
           got = bl;
           stage = static_cast<int>(st2);
           idx = static_cast<int>(i2);
