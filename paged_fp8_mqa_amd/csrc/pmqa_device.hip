@@ -26,6 +26,7 @@
 #include <cstdlib>
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "pmqa_internal.h"
@@ -549,14 +550,21 @@ __device__ __forceinline__ float enc_cand(float s, float t) { return (t > 0.f &&
 __device__ __forceinline__ float dec_cand(float v, float t) { return (t > 0.f && v <= t) ? v + t : v; }
 
 // Order-preserving radix key: larger score -> larger key, -0 == +0, NaN -> 0.
+// A positive score (or zero) maps to its magnitude bits with the top bit set,
+// a negative one to 2^31 minus its magnitude bits, a NaN (magnitude bits above
+// those of infinity) to 0 -- integer operations only, with no compare, so that
+// the keys of several scores compute side by side.
 __device__ __forceinline__ uint32_t radix_key(float x) {
-  if (x != x) return 0u;
-  const uint32_t u = x == 0.f ? 0u : __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t mag = u & 0x7fffffffu;
+  const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31);
+  const uint32_t key = (neg & (0x80000000u - mag)) | (~neg & (mag | 0x80000000u));
+  const uint32_t nan = static_cast<uint32_t>(static_cast<int32_t>(0x7f800000u - mag) >> 31);
+  return key & ~nan;
 }
 __device__ __forceinline__ float key_to_float(uint32_t k) {
   if (k == 0u) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : (0x80000000u | (0x80000000u - k)));
 }
 
 // Adds nc candidates and nt ties to a row's (candidate, tie) counter pair with
@@ -579,6 +587,16 @@ __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(slot), packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
+// Candidates above the final digit a local repair keeps in LDS (enough for
+// k <= kAboveLds: fewer than k keys lie above the digit holding the k-th).
+constexpr int kAboveLds = 2048;
+
+// Longest request (in keys) whose rows a finish CTA over stored scores repairs
+// by itself: one CTA's sweeps cost about 1 us per thousand keys, while the
+// grid-wide repair costs about 100 us however long the request (measured on
+// 44K- to 62K-key rows, local wins; on 131K-key rows, the jobs).
+constexpr int kLocalRepairKeys = 65536;
 
 // Shared memory of a finish-kernel CTA: a union of the per-row radix
 // histograms (repair passes) and one row's keys (final selects), which are
@@ -1236,9 +1254,11 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
 // kernel on the same stream, so it starts with every slot and counter of the
 // main pass in memory and the memory system idle.  Phase A: CTA i takes rows
 // i, i + grid, ...: the fit test of the row's tile, then either the row's
-// ranges and exact Top-k or, from the CTA with the tile's first row that does
-// not fit, a repair job: the mask of those rows, their state words, and the
-// tile appended to the job list.  Phase B: every CTA runs
+// ranges and exact Top-k, or, for a row that does not fit, over stored scores
+// of a request of at most kLocalRepairKeys keys, the row's repair by this CTA
+// alone (local_repair_row), or else, from the CTA with the tile's first row
+// that does not fit, a repair job: the mask of those rows, their state words,
+// and the tile appended to the job list.  Phase B: every CTA runs
 // repair items.  A job runs in stages, each split into items of a few thousand
 // keys of the request:
 //   stages 1-3  radix histogram pass 0/1/2 (11/11/10 bits) of the repaired
@@ -1867,6 +1887,325 @@ __device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idl
   __syncthreads();
 }
 
+// One key of a sweep batch: its position, score, and 1 if it is below the
+// row's end (0 for the clamped loads past it).
+struct SweepKey {
+  int p;
+  float e;
+  uint32_t ok;
+};
+
+// Sweeps keys [0, end) of one stored score row in batches: batch(at, J) gets a
+// thread's J keys of the batch as at(0..J-1).  Where the row is 16-byte
+// aligned: 16-byte loads, kSweepVec per thread per batch, the next batch's
+// loads issued before the current batch is worked through, and the keys past
+// the last whole quad in one more batch (J = 1); otherwise 4-byte loads,
+// kSweepLoads per thread per batch, all in flight at once.  Every thread of
+// the CTA runs every batch (a batch may synchronise the CTA); nothing at or
+// past end is read.
+constexpr int kSweepVec = 16;
+constexpr int kSweepLoads = 32;
+template <class B>
+__device__ __forceinline__ void sweep_row(const float* row, int end, B&& batch) {
+  const int tid = threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0u) {
+    const v4f* row4 = reinterpret_cast<const v4f*>(row);
+    const int n4 = end / 4;
+    constexpr int kStep = kSweepVec * kThreads;
+    v4f cur[kSweepVec], nxt[kSweepVec];
+    if (n4 > 0) {
+#pragma unroll
+      for (int u = 0; u < kSweepVec; ++u) cur[u] = row4[min(u * kThreads + tid, n4 - 1)];
+    }
+    #pragma unroll 1
+    for (int c0 = 0; c0 < n4; c0 += kStep) {
+      const bool more = c0 + kStep < n4;
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < kSweepVec; ++u) nxt[u] = row4[min(c0 + kStep + u * kThreads + tid, n4 - 1)];
+      }
+      batch(
+          [&](int j) {
+            const int i = c0 + (j >> 2) * kThreads + tid;
+            return SweepKey{4 * i + (j & 3), cur[j >> 2][j & 3], i < n4 ? 1u : 0u};
+          },
+          std::integral_constant<int, 4 * kSweepVec>{});
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < kSweepVec; ++u) cur[u] = nxt[u];
+      }
+    }
+    if (4 * n4 < end) {
+      const int p = 4 * n4 + tid;
+      const float e = row[min(p, end - 1)];
+      batch([&](int) { return SweepKey{p, e, p < end ? 1u : 0u}; }, std::integral_constant<int, 1>{});
+    }
+    return;
+  }
+  #pragma unroll 1
+  for (int c0 = 0; c0 < end; c0 += kSweepLoads * kThreads) {
+    float v[kSweepLoads];
+#pragma unroll
+    for (int u = 0; u < kSweepLoads; ++u) v[u] = row[min(c0 + u * kThreads + tid, end - 1)];
+    batch(
+        [&](int j) {
+          const int p = c0 + j * kThreads + tid;
+          return SweepKey{p, v[j], p < end ? 1u : 0u};
+        },
+        std::integral_constant<int, kSweepLoads>{});
+  }
+}
+
+// Appends a sweep batch's keys of class 1 and 2 (cls(score) -> 0, 1 or 2) in
+// whole-CTA order: each thread counts its keys of both classes (packed in one
+// word, class 2 in the high half: a batch holds fewer than 2^16 keys), one
+// CTA-wide exclusive scan of the counts places each thread's keys after the
+// running totals sh.pos[0..1], and each thread passes its keys, in order, to
+// put(class, position, key, score).  Two barriers a batch; the loads already
+// issued for the next batch complete before the stores.
+template <int NT, int J, class At, class Cls, class Put>
+__device__ __forceinline__ void append_batch(At&& at, Cls&& cls, Put&& put, CtaShared<NT>& sh) {
+  static_assert(J * kThreads < 65536, "class counts of a batch fit 16 bits");
+  const int w = wave_id();
+  const int lane = lane_id();
+  uint32_t cnt = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const SweepKey k = at(j);
+    const int c = k.ok ? cls(k.e) : 0;
+    cnt += (c == 1 ? 1u : 0u) + (c == 2 ? 0x10000u : 0u);
+  }
+  uint32_t incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sh.wtot[w] = incl;
+  __syncthreads();
+  uint32_t below = 0u, tot = 0u;
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) {
+    if (q < w) below += sh.wtot[q];
+    tot += sh.wtot[q];
+  }
+  const int p1 = sh.pos[0], p2 = sh.pos[1];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    sh.pos[0] = p1 + static_cast<int>(tot & 0xffffu);
+    sh.pos[1] = p2 + static_cast<int>(tot >> 16);
+  }
+  const uint32_t excl = below + incl - cnt;
+  int r1 = p1 + static_cast<int>(excl & 0xffffu), r2 = p2 + static_cast<int>(excl >> 16);
+  // one wait for every load in flight (the next batch's included): the
+  // compiler would otherwise wait for some before each predicated store
+  wait_vm_done();
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const SweepKey k = at(j);
+    const int c = k.ok ? cls(k.e) : 0;
+    if (c == 1) put(1, r1, k.p, k.e);
+    if (c == 2) put(2, r2, k.p, k.e);
+    r1 += c == 1 ? 1 : 0;
+    r2 += c == 2 ? 1 : 0;
+  }
+}
+
+// radix_key's mapping in straight-line vector integer operations (the
+// compiler would turn the C form back into compares, which serialise on one
+// condition register): the key of a positive score, or of a negative one,
+// picked by the sign mask, then cleared for a NaN.
+__device__ __forceinline__ uint32_t radix_key_alu(float x) {
+  uint32_t key, mag, t0, t1;
+  asm("v_and_b32 %[mag], 0x7fffffff, %[u]\n\t"
+      "v_ashrrev_i32 %[t0], 31, %[u]\n\t"
+      "v_sub_u32 %[t1], 0x80000000, %[mag]\n\t"
+      "v_or_b32 %[key], 0x80000000, %[mag]\n\t"
+      "v_bfi_b32 %[key], %[t0], %[t1], %[key]\n\t"
+      "v_sub_u32 %[t1], 0x7f800000, %[mag]\n\t"
+      "v_ashrrev_i32 %[t1], 31, %[t1]\n\t"
+      "v_bfi_b32 %[key], %[t1], 0, %[key]"
+      : [key] "=&v"(key), [mag] "=&v"(mag), [t0] "=&v"(t0), [t1] "=&v"(t1)
+      : [u] "v"(__float_as_uint(x)));
+  return key;
+}
+
+// 1 if x == 0, else 0, without a compare.
+__device__ __forceinline__ uint32_t is_zero_alu(uint32_t x) {
+  uint32_t r;
+  asm("v_min_u32 %0, 1, %1\n\t"
+      "v_sub_u32 %0, 1, %0"
+      : "=&v"(r)
+      : "v"(x));
+  return r;
+}
+
+// Repair of row r by this CTA alone, from its stored scores row[0, end): the
+// exact k-th largest key (1 <= k <= end) by LDS radix histogram sweeps (11, 11
+// and 10 bits from the top).  As soon as the digit holding it holds at most
+// kFinalizeLds keys, one collect sweep keeps the digit's keys in LDS, where a
+// radix select finds the exact key, and the keys above the digit as
+// candidates (in LDS too when k <= kAboveLds), stored against that key;
+// after the third histogram the row is selected again at the exact score
+// instead.  Then the row's counters, threshold, ranges and Top-k.  No other
+// CTA takes part, so no repair state is shared.
+template <int NT>
+__device__ __forceinline__ void local_repair_row(const SelectArgs& s, const float* row, int r, int end, int k,
+                                                 CtaShared<NT>& sh) {
+  const int tid = threadIdx.x;
+  uint32_t* hist = sh.u.fin.hist;
+  int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
+  // the candidates above the final digit: (key index, score bits) (only the
+  // finish kernel over stored scores has this area)
+  __shared__ int2 above[kAboveLds];
+  uint32_t pf = 0u, krem = static_cast<uint32_t>(k);
+  int known = 0;
+  float t2 = 0.f;
+  for (int pass = 0;; ++pass) {
+    const int shift = pass_shift(pass);
+    const int bits = pass_bits(pass);
+    const uint32_t low = (1u << bits) - 1u;
+    #pragma unroll 1
+    for (int i = tid; i < kRadixBins; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+    // every key adds to its digit's bin, 1 if it has the known prefix, else 0
+    // (no branch per key, so that the keys' instructions interleave)
+    const int above_shift = pass == 0 ? 31 : shift + bits;
+    const uint32_t want = pass == 0 ? 0u : pf;
+    const uint32_t keep_mask = pass == 0 ? 0u : ~0u;
+    sweep_row(row, end, [&](auto at, auto nj) {
+#pragma unroll
+      for (int j = 0; j < decltype(nj)::value; ++j) {
+        const SweepKey k = at(j);
+        const uint32_t key = radix_key_alu(k.e);
+        const uint32_t in = k.ok & is_zero_alu(((key >> above_shift) ^ want) & keep_mask);
+        atomicAdd(&hist[(key >> shift) & low], in);
+      }
+    });
+    __syncthreads();
+    uint32_t d, rem;
+    cta_find_digit(hist, 1 << bits, krem, sh, d, rem);
+    const uint32_t in_digit = hist[d];
+    pf = pass == 0 ? d : ((pf << bits) | d);
+    krem = rem;
+    known += bits;
+    if (tid == 0) {
+      sh.pos[0] = 0;
+      sh.pos[1] = 0;
+    }
+    __syncthreads();
+    if (known == 32) {
+      // every bit known: select again at the exact score
+      t2 = key_to_float(pf);
+      sweep_row(row, end, [&](auto at, auto nj) {
+        append_batch<NT, decltype(nj)::value>(
+            at, [&](float e) { return e > t2 ? 1 : (!(e < t2) ? 2 : 0); },
+            [&](int c, int i, int p, float e) {
+              if (c == 1 && i < s.capacity) store_pair(slots + 2 * (s.top_k + i), p, enc_cand(e, t2));
+              if (c == 2 && i < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - i), p, e - t2);
+            },
+            sh);
+      });
+      break;
+    }
+    if (in_digit <= static_cast<uint32_t>(kFinalizeLds)) {
+      // collect: the digit's keys go to LDS, keys above it become candidates:
+      // kept in LDS too while k <= kAboveLds (stored once the exact score is
+      // known), else stored with their raw scores and re-encoded afterwards
+      const uint32_t top_pf = pf;
+      const int drop = 32 - known;
+      const bool above_lds = k <= kAboveLds;
+      auto put = [&](int c, int i, int p, float e) {
+        if (c == 1 && above_lds) above[i] = make_int2(p, __float_as_int(e));
+        if (c == 1 && !above_lds && i < s.capacity) store_pair(slots + 2 * (s.top_k + i), p, e);
+        if (c == 2 && i < kFinalizeLds) {
+          sh.u.fin.key[i] = __float_as_uint(e);
+          sh.u.fin.idx[i] = p;
+        }
+      };
+      // The digit's keys are [lo, hi) = [top_pf, top_pf + 1) << drop.  Where lo
+      // is the key of a number (not of the NaN-only low keys), the classes
+      // follow from two float compares: key(e) >= K exactly when e >= the
+      // float of key K (a NaN float for hi past the largest number's key
+      // leaves class 1 empty, as it is).
+      const uint64_t lo = static_cast<uint64_t>(top_pf) << drop;
+      if (lo >= 0x00800000u) {
+        const float lb = key_to_float(static_cast<uint32_t>(lo));
+        const uint64_t hi = lo + (uint64_t{1} << drop);
+        const float ub = hi > 0xffffffffu ? __uint_as_float(0x7fc00000u) : key_to_float(static_cast<uint32_t>(hi));
+        sweep_row(row, end, [&](auto at, auto nj) {
+          append_batch<NT, decltype(nj)::value>(
+              at, [&](float e) { return e >= ub ? 1 : (e >= lb ? 2 : 0); }, put, sh);
+        });
+      } else {
+        sweep_row(row, end, [&](auto at, auto nj) {
+          append_batch<NT, decltype(nj)::value>(
+              at,
+              [&](float e) {
+                const uint32_t top = radix_key_alu(e) >> drop;
+                return top > top_pf ? 1 : (top == top_pf ? 2 : 0);
+              },
+              put, sh);
+        });
+      }
+      __syncthreads();
+      const int nabove = sh.pos[0];
+      const int nin = min(sh.pos[1], kFinalizeLds);
+      __syncthreads();
+      auto key_of = [&](int i) { return radix_key(__uint_as_float(sh.u.fin.key[i])); };
+      cta_radix_select(key_of, nin, static_cast<int>(krem), hist, sh);  // resets sh.pos
+      const uint32_t kstar = sh.pfx[0];
+      t2 = key_to_float(kstar);
+      #pragma unroll 1
+      for (int i = tid; i < nin; i += kThreads) {
+        const uint32_t key = key_of(i);
+        const float e = __uint_as_float(sh.u.fin.key[i]);
+        if (key > kstar) {
+          const int c = nabove + atomicAdd(&sh.pos[0], 1);
+          if (c < s.capacity) store_pair(slots + 2 * (s.top_k + c), sh.u.fin.idx[i], enc_cand(e, t2));
+        } else if (key == kstar) {
+          const int c = atomicAdd(&sh.pos[1], 1);
+          if (c < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - c), sh.u.fin.idx[i], e - t2);
+        }
+      }
+      // the candidates above the digit, encoded against the exact score: from
+      // LDS, or the raw ones read back from L2 once this CTA's stores complete
+      const int nkeep = min(nabove, s.capacity);
+      if (above_lds) {
+        #pragma unroll 1
+        for (int i = tid; i < nkeep; i += kThreads) {
+          const int2 v = above[i];
+          store_pair(slots + 2 * (s.top_k + i), v.x, enc_cand(__int_as_float(v.y), t2));
+        }
+      } else {
+        wait_vm_done();
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        #pragma unroll 1
+        for (int i = tid; i < nkeep; i += kThreads) {
+          const int2 v = *reinterpret_cast<const int2*>(slots + 2 * (s.top_k + i));
+          store_pair(slots + 2 * (s.top_k + i), v.x, enc_cand(__int_as_float(v.y), t2));
+        }
+      }
+      if (tid == 0) sh.pos[0] += nabove;
+      break;
+    }
+  }
+  // the slot stores complete (and this CTA's view of the slots is refreshed)
+  // before the Top-k reads them back
+  wait_vm_done();
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int nc = sh.pos[0], nt = sh.pos[1];
+  __syncthreads();
+  if (tid == 0) {
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, static_cast<uint32_t>(nc));
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(nt));
+    st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
+  }
+  row_outputs<NT>(s, r, k, nc, nt, t2, 0, sh);
+}
+
 // The finish kernel's CTA body: phase A over this CTA's rows, then repair
 // items until nothing is left.
 template <int NT, bool kFused, class Args>
@@ -1894,7 +2233,11 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
 #pragma unroll
     for (int u = 0; u < NT; ++u) end[u] = max(0, L - NT + u + 1);
     const int k = min(end[t], s.top_k);
-    saw_repair = saw_repair || mask != 0u;
+    // Stored scores of requests up to kLocalRepairKeys keys: each CTA repairs
+    // its own rows (the same decision for every row of a tile); longer ones,
+    // and the re-scoring repair, run as jobs.
+    const bool local = !kFused && L <= kLocalRepairKeys;
+    saw_repair = saw_repair || (mask != 0u && !local);
     // The row is through phase A once its fit is decided (and its job, if it
     // publishes one, listed): the CTAs waiting for repair items leave as soon
     // as every row is, while the fitting rows' outputs are still being written.
@@ -1902,6 +2245,13 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
       // (wave 0 has no pair load in flight: its count returns after one round trip)
       if (tid == 0) flag_if_last(ws, count_row(ws));
       row_outputs_pre<NT>(s, r, k, sh.nc[t], sh.nt[t], sh.thr[t], npre, pre, sh);
+    } else if (local) {
+      // counted first: the CTAs waiting for jobs need not wait for the repair
+      if (tid == 0) flag_if_last(ws, count_row(ws));
+      if constexpr (!kFused) {
+        if (k > 0) local_repair_row<NT>(s, a.logits + static_cast<int64_t>(r) * a.ld, r, end[t], k, sh);
+        else row_outputs<NT>(s, r, k, 0, 0, sh.thr[t], 0, sh);
+      }
     } else {
       if ((mask & ((1u << t) - 1u)) == 0u) publish_job<NT>(s, ws, b, end, mask);
       if (tid == 0) {
@@ -1912,7 +2262,8 @@ __device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, 
     __syncthreads();
   }
   // With at least as many CTAs without rows as with, those are the repair's
-  // hands: a CTA whose rows all fit leaves without polling for items.
+  // hands: a CTA whose rows all fit (or were repaired here) leaves without
+  // polling for items.
   if (!saw_repair && blockIdx.x < s.rows && 2 * static_cast<int64_t>(s.rows) <= gridDim.x) return;
   int idle = 0;
   while (true) {

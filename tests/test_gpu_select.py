@@ -115,6 +115,29 @@ def test_indexer_topk_few_extra_candidates(tied):
     assert np.array_equal(res["counters"][:, 0], top_k + np.array(extras))
 
 
+@pytest.mark.parametrize("mode", ["low", "inf"])
+def test_indexer_topk_repair_heavy_ties(mode):
+    """Repaired rows whose k-th largest score is shared by thousands of keys (more
+    than a final in-LDS select holds), so that the repair needs every key bit
+    before it selects the row again; rows aligned and not (odd row stride)."""
+    top_k, cap, n = 2048, 4096, 20000
+    R = 3
+    g = np.random.default_rng(91)
+    x = (g.normal(size=(R, n + 1)) * 4).astype(np.float32)
+    for r in range(R):
+        order = np.argsort(-x[r, :n], kind="stable")
+        tie = order[1500:1500 + 6000]          # the k-th position falls inside this block
+        x[r, tie] = x[r, order[1500]]
+    x[:, n] = np.nan
+    thr = np.full(R, -np.inf if mode == "low" else np.inf, np.float32)
+    wl = W.Workload(name="syn", q=None, kv_fused=np.zeros((1, 1), np.uint8), weights=None, block_tables=None,
+                    seq_lens=np.full(R, n, np.int32), max_seq_len=n, block_size=64, next_n=1,
+                    top_k=top_k, capacity=cap, threshold_recipe="", description="")
+    res = run_select(wl, torch.from_numpy(x).to("cuda"), thr)
+    _check(wl, res, True, scores32=x)
+    assert np.all(res["counters"][:, 1] >= 6000 - 1)
+
+
 def _oracle_rows(wl, rows):
     ref = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
                                   wl.max_seq_len, rows=rows)
