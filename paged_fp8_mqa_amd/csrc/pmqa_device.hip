@@ -1961,9 +1961,12 @@ __device__ __forceinline__ void sweep_row(const float* row, int end, B&& batch) 
 // word, class 2 in the high half: a batch holds fewer than 2^16 keys), one
 // CTA-wide exclusive scan of the counts places each thread's keys after the
 // running totals sh.pos[0..1], and each thread passes its keys, in order, to
-// put(class, position, key, score).  Two barriers a batch; the loads already
-// issued for the next batch complete before the stores.
-template <int NT, int J, class At, class Cls, class Put>
+// put(class, position, key, score) (with kEvery, every key is passed, class 0
+// included, and put writes without a branch: on a lone wave per SIMD each
+// branch per key costs more than the key's arithmetic).  cls must not branch
+// either.  Two barriers a batch; the loads already issued for the next batch
+// complete before the stores.
+template <int NT, int J, bool kEvery = false, class At, class Cls, class Put>
 __device__ __forceinline__ void append_batch(At&& at, Cls&& cls, Put&& put, CtaShared<NT>& sh) {
   static_assert(J * kThreads < 65536, "class counts of a batch fit 16 bits");
   const int w = wave_id();
@@ -1972,7 +1975,7 @@ __device__ __forceinline__ void append_batch(At&& at, Cls&& cls, Put&& put, CtaS
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const SweepKey k = at(j);
-    const int c = k.ok ? cls(k.e) : 0;
+    const int c = cls(k.e) & -static_cast<int>(k.ok);
     cnt += (c == 1 ? 1u : 0u) + (c == 2 ? 0x10000u : 0u);
   }
   uint32_t incl = cnt;
@@ -2003,9 +2006,13 @@ __device__ __forceinline__ void append_batch(At&& at, Cls&& cls, Put&& put, CtaS
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const SweepKey k = at(j);
-    const int c = k.ok ? cls(k.e) : 0;
-    if (c == 1) put(1, r1, k.p, k.e);
-    if (c == 2) put(2, r2, k.p, k.e);
+    const int c = cls(k.e) & -static_cast<int>(k.ok);
+    if constexpr (kEvery) {
+      put(c, c == 1 ? r1 : r2, k.p, k.e);  // every key, no branch (put ignores class 0)
+    } else {
+      if (c == 1) put(1, r1, k.p, k.e);
+      if (c == 2) put(2, r2, k.p, k.e);
+    }
     r1 += c == 1 ? 1 : 0;
     r2 += c == 2 ? 1 : 0;
   }
@@ -2055,9 +2062,12 @@ __device__ __forceinline__ void local_repair_row(const SelectArgs& s, const floa
   const int tid = threadIdx.x;
   uint32_t* hist = sh.u.fin.hist;
   int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
-  // the candidates above the final digit: (key index, score bits) (only the
-  // finish kernel over stored scores has this area)
-  __shared__ int2 above[kAboveLds];
+  // the candidates above the final digit and the digit's keys: (key index,
+  // score bits), each with one spare entry per lane that takes the writes of
+  // the keys of other classes (only the finish kernel over stored scores has
+  // these areas)
+  __shared__ int2 above[kAboveLds + 64];
+  __shared__ int2 digit_keys[kFinalizeLds + 64];
   uint32_t pf = 0u, krem = static_cast<uint32_t>(k);
   int known = 0;
   float t2 = 0.f;
@@ -2118,10 +2128,15 @@ __device__ __forceinline__ void local_repair_row(const SelectArgs& s, const floa
       auto put = [&](int c, int i, int p, float e) {
         if (c == 1 && above_lds) above[i] = make_int2(p, __float_as_int(e));
         if (c == 1 && !above_lds && i < s.capacity) store_pair(slots + 2 * (s.top_k + i), p, e);
-        if (c == 2 && i < kFinalizeLds) {
-          sh.u.fin.key[i] = __float_as_uint(e);
-          sh.u.fin.idx[i] = p;
-        }
+        if (c == 2 && i < kFinalizeLds) digit_keys[i] = make_int2(p, __float_as_int(e));
+      };
+      // both classes to LDS, written by every lane for every key (a key of
+      // another class, or past an area's end, to the lane's spare entry)
+      const int lane = lane_id();
+      auto put_every = [&](int c, int i, int p, float e) {
+        const int2 v = make_int2(p, __float_as_int(e));
+        above[c == 1 && i < kAboveLds ? i : kAboveLds + lane] = v;
+        digit_keys[c == 2 && i < kFinalizeLds ? i : kFinalizeLds + lane] = v;
       };
       // The digit's keys are [lo, hi) = [top_pf, top_pf + 1) << drop.  Where lo
       // is the key of a number (not of the NaN-only low keys), the classes
@@ -2133,10 +2148,13 @@ __device__ __forceinline__ void local_repair_row(const SelectArgs& s, const floa
         const float lb = key_to_float(static_cast<uint32_t>(lo));
         const uint64_t hi = lo + (uint64_t{1} << drop);
         const float ub = hi > 0xffffffffu ? __uint_as_float(0x7fc00000u) : key_to_float(static_cast<uint32_t>(hi));
-        sweep_row(row, end, [&](auto at, auto nj) {
-          append_batch<NT, decltype(nj)::value>(
-              at, [&](float e) { return e >= ub ? 1 : (e >= lb ? 2 : 0); }, put, sh);
-        });
+        // class 1 above the digit, 2 inside it: 2 (e >= lb) - (e >= ub), no branch
+        auto cls = [&](float e) { return 2 * static_cast<int>(e >= lb) - static_cast<int>(e >= ub); };
+        if (above_lds) {
+          sweep_row(row, end, [&](auto at, auto nj) { append_batch<NT, decltype(nj)::value, true>(at, cls, put_every, sh); });
+        } else {
+          sweep_row(row, end, [&](auto at, auto nj) { append_batch<NT, decltype(nj)::value>(at, cls, put, sh); });
+        }
       } else {
         sweep_row(row, end, [&](auto at, auto nj) {
           append_batch<NT, decltype(nj)::value>(
@@ -2152,20 +2170,21 @@ __device__ __forceinline__ void local_repair_row(const SelectArgs& s, const floa
       const int nabove = sh.pos[0];
       const int nin = min(sh.pos[1], kFinalizeLds);
       __syncthreads();
-      auto key_of = [&](int i) { return radix_key(__uint_as_float(sh.u.fin.key[i])); };
+      auto key_of = [&](int i) { return radix_key(__int_as_float(digit_keys[i].y)); };
       cta_radix_select(key_of, nin, static_cast<int>(krem), hist, sh);  // resets sh.pos
       const uint32_t kstar = sh.pfx[0];
       t2 = key_to_float(kstar);
       #pragma unroll 1
       for (int i = tid; i < nin; i += kThreads) {
         const uint32_t key = key_of(i);
-        const float e = __uint_as_float(sh.u.fin.key[i]);
+        const int2 v = digit_keys[i];
+        const float e = __int_as_float(v.y);
         if (key > kstar) {
           const int c = nabove + atomicAdd(&sh.pos[0], 1);
-          if (c < s.capacity) store_pair(slots + 2 * (s.top_k + c), sh.u.fin.idx[i], enc_cand(e, t2));
+          if (c < s.capacity) store_pair(slots + 2 * (s.top_k + c), v.x, enc_cand(e, t2));
         } else if (key == kstar) {
           const int c = atomicAdd(&sh.pos[1], 1);
-          if (c < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - c), sh.u.fin.idx[i], e - t2);
+          if (c < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - c), v.x, e - t2);
         }
       }
       // the candidates above the digit, encoded against the exact score: from
