@@ -138,6 +138,29 @@ def test_indexer_topk_repair_heavy_ties(mode):
     assert np.all(res["counters"][:, 1] >= 6000 - 1)
 
 
+@pytest.mark.parametrize("mode", ["low", "inf", "sigma"])
+def test_indexer_topk_repair_large_k(mode):
+    """Repaired rows with k above 2048 (the candidates above the final digit
+    stored raw, then re-encoded, instead of kept in LDS), on aligned and
+    unaligned rows, with and without ties at the k-th score."""
+    top_k, cap, n = 3000, 6000, 12000
+    R = 4
+    g = np.random.default_rng(123)
+    x = (g.normal(size=(R, n + 3)) * 4).astype(np.float32)
+    for r in (1, 3):
+        order = np.argsort(-x[r, :n], kind="stable")
+        x[r, order[2900:3100]] = x[r, order[2900]]   # ties across the k-th position
+    x[:, n:] = np.nan
+    ends = oracle.row_ends(np.full(R, n), 1)
+    thr = _thresholds(mode, x, ends, top_k, 5) if mode == "sigma" else \
+        np.full(R, -np.inf if mode == "low" else np.inf, np.float32)
+    wl = W.Workload(name="syn", q=None, kv_fused=np.zeros((1, 1), np.uint8), weights=None, block_tables=None,
+                    seq_lens=np.full(R, n, np.int32), max_seq_len=n, block_size=64, next_n=1,
+                    top_k=top_k, capacity=cap, threshold_recipe="", description="")
+    res = run_select(wl, torch.from_numpy(x).to("cuda"), thr)
+    _check(wl, res, True, scores32=x)
+
+
 def _oracle_rows(wl, rows):
     ref = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
                                   wl.max_seq_len, rows=rows)
