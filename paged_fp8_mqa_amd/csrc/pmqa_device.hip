@@ -1903,7 +1903,7 @@ struct SweepKey {
 // kSweepLoads per thread per batch, all in flight at once.  Every thread of
 // the CTA runs every batch (a batch may synchronise the CTA); nothing at or
 // past end is read.
-constexpr int kSweepVec = 16;
+constexpr int kSweepVec = 8;
 constexpr int kSweepLoads = 32;
 template <class B>
 __device__ __forceinline__ void sweep_row(const float* row, int end, B&& batch) {
