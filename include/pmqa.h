@@ -218,9 +218,9 @@ pmqa_status pmqa_indexer_topk(
  * arithmetic, bit for bit) and selects them without storing the scores; the
  * repair recomputes the scores of the request it repairs.  Arguments as in
  * pmqa_mqa_logits (minus out/out_stride/max_seq_len) and the select arguments
- * above; block_table_width >= ceil(max_context / block_size) ("the block table
- * must cover it", page "flashinfer.sdsa.indexer_threshold_select",
- * max_context).
+ * above; block_table_width >= ceil(max_context / block_size) (the table has
+ * to reach max_context keys: page "flashinfer.sdsa.indexer_threshold_select",
+ * Parameters: max_context).
  */
 pmqa_status pmqa_check_fused_args(
     const uint8_t* q, const uint8_t* kv_fused, const float* weights,

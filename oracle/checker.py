@@ -16,7 +16,7 @@ expect a complaint.
 """
 import numpy as np
 
-from .select import classify, decode_slot, fits, kth_largest, radix_key, select_with_repair
+from .select import classify, decode_slots, fits, kth_largest, radix_key, select_with_repair
 
 F32 = np.float32
 
@@ -36,8 +36,16 @@ def read_slots(cand_row: np.ndarray, top_k: int, capacity: int, n_cand: int, n_t
 
 
 def check_row(r, *, e_r, top_k, capacity, threshold_in, threshold_out, counters, cand_row,
-              rng, topk_row, repair, scores32=None, scores64=None, tau=0.0, untouched_slots=None):
-    """Violations (a list of strings, empty when the row is correct)."""
+              rng, topk_row, repair, scores32=None, scores64=None, tau=0.0, untouched_slots=None,
+              stats=None):
+    """Violations (a list of strings, empty when the row is correct).
+
+    untouched_slots: the int32 value every slot word held before the call; a
+    row whose threshold did not change (or that sees no key) must then hold it
+    in every slot outside its ranges (nothing else is written there).
+    stats: a dict that collects, over the rows checked against float64 scores,
+    how the k-th/(k+1)-th gap compares with tau (see exact_set_when_gapped).
+    """
     errs = []
     n_cand, n_tie = int(counters[0]), int(counters[1])
     if n_cand < 0 or n_tie < 0:
@@ -56,8 +64,8 @@ def check_row(r, *, e_r, top_k, capacity, threshold_in, threshold_out, counters,
         return errs
     if np.unique(idx).size != idx.size:
         errs.append(f"row {r}: duplicate slot index")
-    dec_c = np.array([decode_slot(_bits_to_f32(v), t_out, False) for v in cands[:, 1]], dtype=np.float32)
-    dec_t = np.array([decode_slot(_bits_to_f32(v), t_out, True) for v in ties[:, 1]], dtype=np.float32)
+    dec_c = decode_slots(np.ascontiguousarray(cands[:, 1]).view(np.float32), t_out, False)
+    dec_t = decode_slots(np.ascontiguousarray(ties[:, 1]).view(np.float32), t_out, True)
     if dec_c.size and not np.all(dec_c > t_out):
         errs.append(f"row {r}: stored candidate not above threshold")
     if dec_t.size and not np.all((dec_t == t_out) | np.isnan(dec_t)):
@@ -66,6 +74,12 @@ def check_row(r, *, e_r, top_k, capacity, threshold_in, threshold_out, counters,
         exp = (top_k - min(n_tie, top_k), top_k + min(n_cand, capacity))
         if (int(rng[0]), int(rng[1])) != exp:
             errs.append(f"row {r}: ranges {tuple(int(x) for x in rng)} != {exp}")
+    unchanged = F32(threshold_in).view(np.int32) == t_out.view(np.int32)
+    if untouched_slots is not None and (unchanged or e_r == 0):
+        lo, hi = top_k - min(n_tie, top_k), top_k + min(n_cand, capacity)
+        outside = np.concatenate([cand_row[:lo].ravel(), cand_row[hi:].ravel()])
+        if np.any(outside != np.int32(untouched_slots)):
+            errs.append(f"row {r}: a slot outside [{lo},{hi}) was written")
 
     if scores32 is not None:
         s = np.asarray(scores32, dtype=np.float32)[:e_r]
@@ -79,7 +93,7 @@ def check_row(r, *, e_r, top_k, capacity, threshold_in, threshold_out, counters,
         if cands.size:
             if not np.all(cmask[cands[:, 0]]):
                 errs.append(f"row {r}: stored candidate index is not a candidate")
-            want = np.array([F32(s[i]) for i in cands[:, 0]], dtype=np.float32)
+            want = s[cands[:, 0]].astype(np.float32)
             if not np.array_equal(dec_c.view(np.int32), want.view(np.int32)):
                 errs.append(f"row {r}: candidate score bits differ from the scores read")
         if ties.size and not np.all(tmask[ties[:, 0]]):
@@ -114,7 +128,13 @@ def check_row(r, *, e_r, top_k, capacity, threshold_in, threshold_out, counters,
     if topk_row is not None:
         errs += check_topk_against_slots(r, topk_row, cands, dec_c, ties, k, top_k, n_cand)
         if scores64 is not None and k > 0:
-            errs += check_set_rule(r, topk_row[:k], np.asarray(scores64, dtype=np.float64)[:e_r], k, tau)
+            s64 = np.asarray(scores64, dtype=np.float64)[:e_r]
+            errs += check_set_rule(r, topk_row[:k], s64, k, tau)
+            ex = exact_set_when_gapped(topk_row[:k], s64, k, tau)
+            if ex is False:
+                errs.append(f"row {r}: gap above 2 tau but the set is not the exact sort prefix")
+            if stats is not None:
+                gap_stats(stats, topk_row[:k], s64, k, tau)
     return errs
 
 
@@ -167,6 +187,25 @@ def check_set_rule(r, got, s64, k, tau):
     if not gs <= allowed:
         errs.append(f"row {r}: set holds {len(gs - allowed)} keys below sigma_k - 2 tau")
     return errs
+
+
+def gap_stats(stats, got, s64, k, tau):
+    """Counts, per row, where the k-th/(k+1)-th gap lies against tau, and how
+    often the set is the exact sort prefix in each band: "gap>2tau" (the sound
+    form of the north-star rule; must be exact), "tau<gap<=2tau" (the literal
+    form: exact unless the GPU's own rounding swapped the two), "gap<=tau"
+    (tie membership only), "all" (k = row length: every key)."""
+    if k >= s64.size:
+        band = "all"
+    else:
+        srt = np.sort(s64)[::-1]
+        gap = srt[k - 1] - srt[k]
+        band = "gap>2tau" if gap > 2 * tau else ("tau<gap<=2tau" if gap > tau else "gap<=tau")
+    ref = set(np.argsort(-s64, kind="stable")[:k].tolist())
+    exact = set(int(x) for x in got) == ref
+    d = stats.setdefault(band, [0, 0])
+    d[0] += 1
+    d[1] += int(exact)
 
 
 def exact_set_when_gapped(got, s64, k, tau):

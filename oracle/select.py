@@ -81,10 +81,11 @@ def topk_indices(scores64, k: int):
 
 
 def encode_candidate(score, threshold):
-    """Stored value of a candidate (reading of "its score less the threshold where
-    that is exact (scores at most twice it), which keeps their order"): s - t
-    when t > 0 and s <= 2t (exact by Sterbenz' lemma, since t < s <= 2t), else s.
-    The map is increasing in s, so it keeps the candidates' order.
+    """Stored value of a candidate.  The page's sentence on the stored score bits
+    (indexer_threshold_select, description paragraph 2) is garbled; the reading
+    taken: the difference s - t is stored where it is exact, i.e. when t > 0 and
+    s <= 2t (exact by Sterbenz' lemma, since t < s <= 2t), else s itself.  The
+    map is increasing in s, so it keeps the candidates' order.
     Parity unpinned: the pages give no value to check it against."""
     s = F32(score)
     t = F32(threshold)
@@ -110,6 +111,18 @@ def decode_slot(value, threshold, is_tie: bool):
     if t > 0 and v <= t:
         return F32(v + t)
     return v
+
+
+def decode_slots(values, threshold, is_tie: bool):
+    """decode_slot over an array of stored float32 values (same arithmetic,
+    element by element)."""
+    v = np.asarray(values, dtype=np.float32)
+    t = F32(threshold)
+    if is_tie:
+        return np.where(np.isnan(v), F32(np.nan), t).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        shifted = (v + t).astype(np.float32)
+    return np.where((t > 0) & (v <= t), shifted, v).astype(np.float32)
 
 
 def threshold_select(scores, row_end: int, threshold, top_k: int, capacity: int):

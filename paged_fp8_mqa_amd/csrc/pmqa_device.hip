@@ -2206,6 +2206,9 @@ __device__ __forceinline__ void local_repair_row(const SelectArgs& s, const floa
           store_pair(slots + 2 * (s.top_k + i), v.x, enc_cand(__int_as_float(v.y), t2));
         }
       }
+      // every wave's digit-key appends above are done before the count moves
+      // (a late wave's atomicAdd on sh.pos[0] would otherwise race with it)
+      __syncthreads();
       if (tid == 0) sh.pos[0] += nabove;
       break;
     }

@@ -27,3 +27,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    import report
+    if report.GAP_STATS or report.LINES:
+        terminalreporter.write_sep("-", "parity figures")
+        for line in report.LINES:
+            terminalreporter.write_line(line)
+        if report.GAP_STATS:
+            terminalreporter.write_line(
+                "Top-k sets vs the oracle, by the k-th/(k+1)-th gap against tau_r "
+                "[rows, rows equal to the exact sort prefix]: " + str(report.GAP_STATS))

@@ -1,8 +1,7 @@
-"""HIP-graph capture and replay of the fused select (select kernel, then the
-finish kernel with every row repaired): each replay, with the program's own
-eager calls and synchronisations between replays, gives the eager call's
-results, bit for bit, and the library's state in the workspace carries from
-replay to replay."""
+"""HIP-graph capture and replay of the fused select: each replay, with the
+program's own eager calls and synchronisations between replays, gives the
+eager call's results, bit for bit; replays with new seq_lens and thresholds
+written into the captured buffers follow the new inputs."""
 import numpy as np
 import pytest
 import torch
@@ -26,14 +25,14 @@ def _buffers(wl, thr, ws):
         topk=torch.zeros(R, wl.top_k, dtype=torch.int32, device="cuda"), ws=ws)
 
 
-def _call(wl, d, b):
+def _call(wl, d, b, sl=None):
     # the resets are kernels (a fill and an add), so that a captured graph
     # holds no memset node
     b["counters"].zero_()
     torch.add(b["thr_in"], 0.0, out=b["thr"])
-    pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], wl.max_seq_len, b["thr"], b["counters"],
-                           b["cand"], wl.capacity, wl.top_k, arrivals=b["arrivals"], ranges=b["ranges"],
-                           topk_idx=b["topk"], workspace=b["ws"])
+    pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"] if sl is None else sl, wl.max_seq_len,
+                           b["thr"], b["counters"], b["cand"], wl.capacity, wl.top_k, arrivals=b["arrivals"],
+                           ranges=b["ranges"], topk_idx=b["topk"], workspace=b["ws"])
 
 
 def _host(b):
@@ -41,18 +40,94 @@ def _host(b):
     return {k: b[k].cpu().numpy() for k in ("thr", "counters", "cand", "arrivals", "ranges", "topk")}
 
 
-def _same(wl, a, b):
+def _same(wl, a, b, seq_lens=None):
     assert np.array_equal(a["thr"].view(np.int32), b["thr"].view(np.int32)), "thresholds differ"
     assert np.array_equal(a["counters"], b["counters"]), "counters differ"
     assert np.array_equal(a["ranges"], b["ranges"]), "ranges differ"
     assert np.all(b["arrivals"] == 0), "arrivals not left zeroed"
-    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    ends = oracle.row_ends(wl.seq_lens if seq_lens is None else seq_lens, wl.next_n)
     for r in range(wl.rows):
         ra = {"counters": a["counters"], "cand": a["cand"]}
         rb = {"counters": b["counters"], "cand": b["cand"]}
         assert slot_sets(ra, r, wl.top_k, wl.capacity) == slot_sets(rb, r, wl.top_k, wl.capacity), f"row {r} slots"
         k = min(int(ends[r]), wl.top_k)
         assert set(a["topk"][r, :k].tolist()) == set(b["topk"][r, :k].tolist()), f"row {r} top-k"
+
+
+def _thresholds(wl, seq_lens, mode, rng):
+    """Per-row thresholds from the oracle's scores at these lengths: "inf" repairs
+    every row, "mixed" repairs the even rows and puts the odd ones at their k-th
+    score, "jitter" moves each k-th score by a random amount (some rows fit,
+    some do not)."""
+    ref = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, seq_lens, wl.block_size,
+                                  wl.max_seq_len)
+    ends = oracle.row_ends(seq_lens, wl.next_n)
+    thr = np.zeros(wl.rows, np.float32)
+    for r, e in enumerate(ends):
+        if e:
+            s = np.sort(ref[r, :e].astype(np.float32))[::-1]
+            k = min(int(e), wl.top_k)
+            if mode == "inf" or (mode == "mixed" and r % 2 == 0):
+                thr[r] = np.inf
+            elif mode == "mixed":
+                thr[r] = s[k - 1]
+            else:
+                thr[r] = s[min(int(e) - 1, max(0, k - 1 + int(rng.integers(-20, 20))))]
+    return ref, thr
+
+
+def _check_oracle(wl, got, ref, seq_lens):
+    from oracle.checker import check_row
+    tau = oracle.row_tolerance(wl.q, wl.kv_fused, wl.weights, wl.block_tables, seq_lens, wl.block_size)
+    ends = oracle.row_ends(seq_lens, wl.next_n)
+    errs = []
+    for r in range(wl.rows):
+        errs += check_row(r, e_r=int(ends[r]), top_k=wl.top_k, capacity=wl.capacity, threshold_in=got["thr_in"][r],
+                          threshold_out=got["thr"][r], counters=got["counters"][r], cand_row=got["cand"][r],
+                          rng=got["ranges"][:, r], topk_row=got["topk"][r], repair=True, scores64=ref[r],
+                          tau=float(tau[r]))
+    assert not errs, "\n".join(errs[:10])
+
+
+@pytest.mark.parametrize("next_n", [1, 2, 4])
+def test_fused_graph_replays_with_changed_inputs(next_n):
+    """One capture, replayed with new seq_lens and new thresholds written into the
+    captured buffers between replays (the grid's split of the batch is made on
+    the device from seq_lens at each replay): every replay equals an eager call
+    on the same inputs and passes the oracle's checks, and arrivals stays
+    zeroed."""
+    base = [3000, 700, 0, 5000]
+    wl = W.small_random(62 + next_n, base, next_n, 64, top_k=128, capacity=256)
+    d = dev(wl)
+    rng = np.random.default_rng(next_n)
+    ws = pm.make_workspace("fused", wl.batch, wl.next_n, wl.max_seq_len)
+    sl_g = torch.from_numpy(wl.seq_lens.copy()).cuda()
+    graphed = _buffers(wl, np.zeros(wl.rows, np.float32), ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        _call(wl, d, graphed, sl=sl_g)
+    torch.cuda.synchronize()
+    # each variant keeps every length within the request's own pages
+    variants = [(base, "mixed"), ([2500, 1, 0, 4990], "inf"), ([3000, 0, 0, 64], "jitter"),
+                ([1, 700, 0, 5000], "jitter"), (base, "inf")]
+    for lens, mode in variants:
+        lens = np.array(lens, np.int32)
+        ref, thr = _thresholds(wl, lens, mode, rng)
+        sl_g.copy_(torch.from_numpy(lens))
+        graphed["thr_in"].copy_(torch.from_numpy(thr))
+        graphed["cand"].fill_(SENTINEL_I32)
+        graphed["topk"].fill_(SENTINEL_I32)
+        torch.cuda.synchronize()
+        g.replay()
+        got = _host(graphed)
+        got["thr_in"] = thr
+        eager = _buffers(wl, thr, ws)
+        _call(wl, d, eager, sl=torch.from_numpy(lens).cuda())
+        want = _host(eager)
+        _same(wl, want, got, seq_lens=lens)
+        _check_oracle(wl, got, ref, lens)
 
 
 @pytest.mark.parametrize("next_n", [1, 2])

@@ -8,6 +8,7 @@ import torch
 import oracle
 import workloads as W
 from gpu_util import SENTINEL_F32_BITS, dev, run_logits
+from report import LINES
 
 pytestmark = pytest.mark.gpu
 
@@ -122,14 +123,10 @@ def test_logits_strided_views():
 
 
 @pytest.mark.parametrize("cfg", [3, 4, 5])
-def test_logits_large_configs_sampled(cfg):
+def test_logits_large_configs(cfg):
+    """Every row and every visible column of the large workloads within tau_r of
+    the float64 oracle; untouched columns and empty requests keep the sentinel."""
     wl = W.make(cfg)
     out, _ = run_logits(wl, dev(wl))
-    rng = np.random.default_rng(cfg)
-    rows = sorted(set(rng.choice(wl.rows, size=3, replace=False).tolist()) | {wl.rows - 1})
-    _check_logits(wl, out, rows=rows)
-    # every row: finite over its visible range, untouched past its written columns
-    got = out.cpu().numpy()
-    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
-    for r in range(wl.rows):
-        assert np.all(np.isfinite(got[r, :ends[r]]))
+    worst = _check_logits(wl, out)
+    LINES.append(f"{wl.name}: worst |logit err| / tau_r over all rows = {worst:.3g}")

@@ -8,13 +8,22 @@ import torch
 import oracle
 import paged_fp8_mqa_amd as pm
 import workloads as W
-from gpu_util import dev, golden_thresholds, run_fused, run_logits, run_select, slot_sets
+from gpu_util import SENTINEL_I32, dev, golden_thresholds, run_fused, run_logits, run_select, slot_sets
 from oracle.checker import check_row
 
 pytestmark = pytest.mark.gpu
 
 
-def _check(wl, res, repair, scores32=None, scores64=None, tau=None, rows=None, capacity=None):
+from report import GAP_STATS
+
+
+def _check(wl, res, repair, scores32=None, scores64=None, tau=None, rows=None, capacity=None, untouched=True,
+           stats=None):
+    """Every row (or the given rows) against the select contract, and against the
+    oracle's scores when given: exact float32 scores (the unfused select reads
+    them) or float64 ones within tau_r.  With fresh sentinel-filled slots
+    (untouched), slots outside the ranges of rows that were not repaired must
+    still hold the sentinel."""
     cap = wl.capacity if capacity is None else capacity
     ends = oracle.row_ends(wl.seq_lens, wl.next_n)
     errs = []
@@ -25,7 +34,9 @@ def _check(wl, res, repair, scores32=None, scores64=None, tau=None, rows=None, c
             rng=None if res["ranges"] is None else res["ranges"][:, r],
             topk_row=None if res["topk"] is None else res["topk"][r], repair=repair,
             scores32=None if scores32 is None else scores32[r],
-            scores64=None if scores64 is None else scores64[r], tau=0.0 if tau is None else float(tau[r]))
+            scores64=None if scores64 is None else scores64[r], tau=0.0 if tau is None else float(tau[r]),
+            untouched_slots=SENTINEL_I32 if untouched else None,
+            stats=GAP_STATS if stats is None else stats)
     if res["arrivals"] is not None:
         assert np.all(res["arrivals"] == 0), "arrivals not left zeroed"
     assert not errs, "\n".join(errs[:20])
@@ -233,22 +244,39 @@ def _same(wl, a, b, capacity=None):
 
 @pytest.mark.parametrize("cfg", [3, 4, 5])
 def test_fused_large_configs(cfg):
+    """Every row of the large workloads against the float64 oracle (contract,
+    counts within tau, candidate scores, repaired thresholds, the Top-k set
+    rule), in the launch configuration the benchmark times."""
     wl = W.make(cfg)
     gold, thr = golden_thresholds(cfg)
     assert gold["fingerprint"] == W.fingerprint(wl), "input generator drifted from the golden thresholds"
     d = dev(wl)
+    ref, tau = _oracle_rows(wl, None)
     res = run_fused(wl, d, thr)
-    _check(wl, res, True)                               # contract on every row
-    rng = np.random.default_rng(cfg)
-    rows = sorted(set(rng.choice(wl.rows, size=2, replace=False).tolist()) | {0, wl.rows - 1})
-    rows = [r for r in rows if gold["row_ends"][r] > 0]
-    ref, tau = _oracle_rows(wl, rows)
-    _check(wl, res, True, scores64=ref, tau=tau, rows=rows)
+    _check(wl, res, True, scores64=ref, tau=tau)
     if cfg == 5:
         assert np.sum(res["thr"].view(np.int32) != thr.view(np.int32)) >= 7   # the too-high rows repaired
         res2 = run_fused(wl, d, thr, capacity=wl.top_k - 1)
-        _check(wl, res2, True, capacity=wl.top_k - 1)
-        _check(wl, res2, True, scores64=ref, tau=tau, rows=rows, capacity=wl.top_k - 1)
+        _check(wl, res2, True, scores64=ref, tau=tau, capacity=wl.top_k - 1)
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_unfused_large_configs(cfg):
+    """mqa_logits then indexer_topk on the large workloads: the select exactly
+    against the oracle's select over the GPU's own float32 logits, every row
+    against the float64 oracle within tau, and bit for bit equal to the fused
+    path."""
+    wl = W.make(cfg)
+    gold, thr = golden_thresholds(cfg)
+    d = dev(wl)
+    out, _ = run_logits(wl, d)
+    logits = out.cpu().numpy()
+    unf = run_select(wl, out, thr)
+    _check(wl, unf, True, scores32=logits)
+    ref, tau = _oracle_rows(wl, None)
+    _check(wl, unf, True, scores64=ref, tau=tau)
+    fused = run_fused(wl, d, thr)
+    _same(wl, fused, unf)
 
 
 def test_fused_large_batch_grid():
@@ -302,7 +330,7 @@ def test_fused_repeated_calls_reuse_arrivals():
         sb.thr.copy_(sb.thr_in)
         pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], wl.max_seq_len, **sb.kwargs())
         h = sb.host()
-        _check(wl, h, True, scores64=ref, tau=tau)
+        _check(wl, h, True, scores64=ref, tau=tau, untouched=False)
         if first is None:
             first = h
         else:
@@ -330,7 +358,7 @@ def test_workspace_reused_across_batch_sizes():
         d = dev(wl)
         sb = gpu_util.SelectBuffers(wl.rows, wl.batch, wl.top_k, wl.capacity, thr, workspace=ws)
         pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], wl.max_seq_len, **sb.kwargs())
-        _check(wl, sb.host(), True, scores64=ref, tau=tau)
+        _check(wl, sb.host(), True, scores64=ref, tau=tau, untouched=False)
 
 
 @pytest.mark.parametrize("next_n", [1, 2, 3, 4])

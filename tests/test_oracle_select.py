@@ -236,3 +236,55 @@ def test_set_rule():
     assert check_set_rule(0, [0, 1, 2, 3], s, 4, 0.0) == []
     assert check_set_rule(0, [0, 1, 2, 4], s, 4, 0.0) == []   # equal scores: either tie member
     assert check_set_rule(0, [0, 1, 3, 4], s, 4, 0.6) == []   # within 2 tau of sigma_k
+
+
+def test_decode_slots_matches_scalar_decode():
+    g = np.random.default_rng(12)
+    vals = np.concatenate([g.normal(size=200).astype(np.float32) * 5,
+                           np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 3e38, 1e-38], np.float32)])
+    for t in [F32(1.5), F32(-2.0), F32(0.0), F32(3e38), F32(np.inf), F32(-np.inf)]:
+        for tie in (False, True):
+            want = np.array([S.decode_slot(v, t, tie) for v in vals], np.float32)
+            got = S.decode_slots(vals, t, tie)
+            assert np.array_equal(want.view(np.int32), got.view(np.int32)), (t, tie)
+
+
+def test_mutation_stray_slot_write():
+    """A write into a slot outside a row's ranges (rows not repaired, or empty)
+    is reported when the slots' prior contents are known."""
+    SENT = -0x21524111
+    scores, ends, thr, out, top_k, cap = _setup(seed=6, repair=False)
+    for r in range(len(ends)):
+        lo = top_k - min(int(out["counters"][r, 1]), top_k)
+        hi = top_k + min(int(out["counters"][r, 0]), cap)
+        out["candidates"][r, :lo] = SENT
+        out["candidates"][r, hi:] = SENT
+
+    def errs(o):
+        e = []
+        for r in range(len(ends)):
+            e += check_row(r, e_r=ends[r], top_k=top_k, capacity=cap, threshold_in=thr[r],
+                           threshold_out=o["thresholds"][r], counters=o["counters"][r],
+                           cand_row=o["candidates"][r], rng=None, topk_row=None, repair=False,
+                           scores32=scores[r], untouched_slots=SENT)
+        return e
+    assert errs(out) == []
+    for r in (0, 3):   # a row with slots in use, and the empty one
+        bad = {k: v.copy() for k, v in out.items()}
+        bad["candidates"][r, -1] = (0, 0)
+        assert errs(bad), f"stray write in row {r} not reported"
+
+
+def test_gap_stats_bands():
+    from oracle.checker import gap_stats, exact_set_when_gapped
+    s = np.array([9.0, 8.0, 5.0, 4.99, 1.0])
+    st = {}
+    gap_stats(st, [0, 1], s, 2, 1.0)        # gap 3 > 2 tau: exact
+    gap_stats(st, [0, 2, 1], s, 3, 0.004)   # gap 0.01 > 2 tau
+    gap_stats(st, [0, 1, 3], s, 3, 0.008)   # tau < gap 0.01 <= 2 tau, swapped: not exact
+    gap_stats(st, [0, 1, 2], s, 3, 0.02)    # gap <= tau
+    gap_stats(st, [0, 1, 2, 3, 4], s, 5, 0.1)
+    assert st == {"gap>2tau": [2, 2], "tau<gap<=2tau": [1, 0], "gap<=tau": [1, 1], "all": [1, 1]}
+    assert exact_set_when_gapped([0, 1], s, 2, 1.0) is True
+    assert exact_set_when_gapped([0, 2], s, 2, 1.0) is False
+    assert exact_set_when_gapped([0, 1, 3], s, 3, 0.008) is None
