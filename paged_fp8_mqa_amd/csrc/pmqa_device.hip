@@ -84,18 +84,18 @@ struct SelectArgs {
   float* thresholds;
   int32_t* counters;
   int32_t* candidates;
-  int32_t* arrivals;
+  int32_t* arrivals;    // [batch] per-tile arrival counters (with the finish stage), else null
   int32_t* ranges;
   int32_t* topk_idx;
-  uint32_t* ws;         // finish-stage workspace (with arrivals)
-  int64_t ws_words;     // its size in 32-bit words
-  float* scores;        // fused repair: the workspace's score buffer, row r at scores + r * score_ld
+  uint32_t* ws;         // workspace (with arrivals), else null
+  int32_t* ovf;         // its overflow pairs, row r at ovf + r * 2 * kOverflowPairs (null without)
+  float* scores;        // fused repair: the workspace's score rows, row r at scores + r * score_ld
   int64_t score_ld;
-  float* keep;          // fused select: the main pass writes every score here too (the score
-                        // buffer, next_n >= 2), or null
   int32_t capacity;
   int32_t top_k;
   int32_t rows;
+  int32_t resident;     // 1 when every CTA of the launch fits on the device at once (CTAs
+                        // without work then wait a while for repair items before they leave)
 };
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -588,29 +588,9 @@ __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
 }
 
 
-// Candidates above the final digit a local repair keeps in LDS (enough for
-// k <= kAboveLds: fewer than k keys lie above the digit holding the k-th).
-constexpr int kAboveLds = 2048;
-
-// Longest request (in keys) whose rows a finish CTA over stored scores repairs
-// by itself: one CTA's sweeps cost about 1 us per thousand keys, while the
-// grid-wide repair costs about 100 us however long the request (measured on
-// 44K- to 62K-key rows, local wins; on 131K-key rows, the jobs).
-constexpr int kLocalRepairKeys = 65536;
-
-// Shared memory of a finish-kernel CTA: a union of the per-row radix
-// histograms (repair passes) and one row's keys (final selects), which are
-// live at different times.
+// Control words of a CTA's finish work (fit test, repair items, row outputs).
 template <int NT>
-struct CtaShared {
-  union {
-    uint32_t hist[NT][kRadixBins];  // per-row radix histograms
-    struct {
-      alignas(16) uint32_t hist[kRadixBins];
-      uint32_t key[kFinalizeLds];
-      int32_t idx[kFinalizeLds];
-    } fin;                          // one row's keys (and key indices) for a final radix select
-  } u;
+struct Ctl {
   uint32_t wtot[kWaves];
   uint32_t dig[2];
   int32_t wcnt[NT][kWaves][2];
@@ -622,6 +602,7 @@ struct CtaShared {
   int32_t nt[NT];
   float thr[NT];
   uint32_t repair_mask;
+  uint32_t stored_mask;
   int32_t len;
   int32_t is_last;
   int32_t pos[2];
@@ -631,6 +612,37 @@ struct CtaShared {
   // few_extra_from_regs: each wave's smallest packed keys
   uint64_t low[kFewExtra][kWaves];
 };
+
+// The finish work's view of a CTA's LDS: per-row radix histograms (rh, NT of
+// them) and, at the same place, one row's radix histogram (fh) with up to
+// fin_cap keys or score bits (fk) and key indices (fi) for a final select --
+// live at different times -- and the control words (c) in an area of their own.
+template <int NT>
+struct Sh {
+  uint32_t (*rh)[kRadixBins];
+  uint32_t* fh;
+  uint32_t* fk;
+  int32_t* fi;
+  int fin_cap;
+  Ctl<NT>* c;
+};
+
+// Bytes of the finish area for fin_cap final-select entries (at least NT per-row histograms).
+__host__ __device__ constexpr int fin_area_bytes(int nt, int fin_cap) {
+  return 4 * kRadixBins + 8 * fin_cap > 4 * nt * kRadixBins ? 4 * kRadixBins + 8 * fin_cap : 4 * nt * kRadixBins;
+}
+
+template <int NT>
+__device__ __forceinline__ Sh<NT> make_sh(char* lds, int fin_cap, int ctl_off) {
+  Sh<NT> v;
+  v.rh = reinterpret_cast<uint32_t(*)[kRadixBins]>(lds);
+  v.fh = reinterpret_cast<uint32_t*>(lds);
+  v.fk = v.fh + kRadixBins;
+  v.fi = reinterpret_cast<int32_t*>(v.fk + fin_cap);
+  v.fin_cap = fin_cap;
+  v.c = reinterpret_cast<Ctl<NT>*>(lds + ctl_off);
+  return v;
+}
 
 // Shared memory of a select kernel CTA: each wave's candidate and tie lists,
 // per row, of (key index, stored score bits) pairs not yet written to the
@@ -642,6 +654,32 @@ struct MainShared {
   int2 tie[kWaves][NT][kWaveTie<NT>];
   int32_t count[kWaves][NT][2];  // the waves' list lengths at the end
   int32_t base[NT][2];           // the CTA's slot bases per row and class
+};
+
+// LDS of a select launch, one buffer seen three ways: the main pass (KV
+// staging area, q operands for next_n >= 3, the waves' candidate and tie
+// lists), a re-scoring repair item (the same staging area and q operands,
+// packed first-pass histograms where the lists were), and the finish view
+// (row histograms or one row's final-select keys from offset 0, over the
+// staging area); the finish's control words sit after all of them.
+template <int NT, bool kFused>
+struct Layout {
+  static constexpr int kStageBytes = kFused ? kWaves * kStageInt4 * 16 : 0;
+  static constexpr int kQBytes = (kFused && NT >= 3) ? static_cast<int>(sizeof(QLds<NT>)) : 0;
+  static constexpr int kListOff = kStageBytes + kQBytes;
+  static constexpr int kMainEnd = kListOff + static_cast<int>(sizeof(MainShared<NT>));
+  static constexpr int kRescoreEnd = kListOff + NT * 2048;
+  // the largest final select (a multiple of 256 entries, at least kFinalizeLds)
+  // whose area fits where the main pass's buffers are; the select over a
+  // logits matrix keeps kFinalizeLds
+  static constexpr int kFinCap =
+      !kFused ? kFinalizeLds
+              : ((kMainEnd - 4 * kRadixBins) / 8 / 256 * 256 < kFinalizeLds ? kFinalizeLds
+                                                                               : (kMainEnd - 4 * kRadixBins) / 8 / 256 * 256);
+  static constexpr int kFinEnd = fin_area_bytes(NT, kFinCap);
+  static constexpr int kCtlOff =
+      ((kMainEnd > kFinEnd ? (kMainEnd > kRescoreEnd ? kMainEnd : kRescoreEnd) : (kFinEnd > kRescoreEnd ? kFinEnd : kRescoreEnd)) + 15) / 16 * 16;
+  static constexpr int kBytes = kCtlOff + static_cast<int>(sizeof(Ctl<NT>));
 };
 
 // One wave finds the digit holding the krem-th largest entry of hist[0..nb) and
@@ -684,9 +722,11 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_
   *rem = r;
 }
 
-// Radix pass layout: 11 bits, 11 bits, 10 bits from the top of the key.
-__device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
-__device__ __forceinline__ int pass_bits(int pass) { return pass == 2 ? 10 : 11; }
+// Radix pass layout: 10 bits, 11 bits, 11 bits from the top of the key (the
+// first pass's 1024 bins fit a re-scoring item's histograms beside the KV
+// staging area and the q operands).
+__device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 22 : (pass == 1 ? 11 : 0); }
+__device__ __forceinline__ int pass_bits(int pass) { return pass == 0 ? 10 : 11; }
 
 // The digit of hist[0..nb) (nb = 1024 or 2048, 16-byte aligned) holding the
 // krem-th largest entry, and the rank left inside it, found by the whole CTA:
@@ -695,7 +735,7 @@ __device__ __forceinline__ int pass_bits(int pass) { return pass == 2 ? 10 : 11;
 // thread whose bins reach krem walks them.  The histogram's total is at least
 // krem.  Returns the same values in every thread.
 template <int NT>
-__device__ __forceinline__ void cta_find_digit(const uint32_t* hist, int nb, uint32_t krem, CtaShared<NT>& sh,
+__device__ __forceinline__ void cta_find_digit(const uint32_t* hist, int nb, uint32_t krem, const Sh<NT>& sh,
                                                uint32_t& digit, uint32_t& rem) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -715,38 +755,38 @@ __device__ __forceinline__ void cta_find_digit(const uint32_t* hist, int nb, uin
     const uint32_t y = __shfl_down(incl, off);
     if (lane + off < 64) incl += y;
   }
-  if (lane == 0) sh.wtot[w] = incl;
+  if (lane == 0) sh.c->wtot[w] = incl;
   if (tid == 0) {
-    sh.dig[0] = 0u;
-    sh.dig[1] = 0u;
+    sh.c->dig[0] = 0u;
+    sh.c->dig[1] = 0u;
   }
   __syncthreads();
   uint32_t above = incl - local;
-  for (int q = w + 1; q < kWaves; ++q) above += sh.wtot[q];
+  for (int q = w + 1; q < kWaves; ++q) above += sh.c->wtot[q];
   if (above < krem && krem <= above + local) {
     uint32_t acc = above;
     bool found = false;
 #pragma unroll
     for (int i = 7; i >= 0; --i) {
       if (!found && i < per && acc + h[i] >= krem) {
-        sh.dig[0] = static_cast<uint32_t>(tid * per + i);
-        sh.dig[1] = krem - acc;
+        sh.c->dig[0] = static_cast<uint32_t>(tid * per + i);
+        sh.c->dig[1] = krem - acc;
         found = true;
       }
       if (i < per) acc += h[i];
     }
   }
   __syncthreads();
-  digit = sh.dig[0];
-  rem = sh.dig[1];
+  digit = sh.c->dig[0];
+  rem = sh.c->dig[1];
 }
 
 // The k-th largest of n radix keys key_of(0..n) (1 <= k <= n), by a 3-pass
 // LDS radix select over `hist` (kRadixBins words, 16-byte aligned).  Leaves the
-// key in sh.pfx[0] and, in sh.krem[0], how many entries equal to it the k
-// largest hold; resets sh.pos[0..1] for the caller.
+// key in sh.c->pfx[0] and, in sh.c->krem[0], how many entries equal to it the k
+// largest hold; resets sh.c->pos[0..1] for the caller.
 template <int NT, class KeyOf>
-__device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, CtaShared<NT>& sh) {
+__device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   uint32_t pf = 0u, krem = static_cast<uint32_t>(k);
   for (int pass = 0; pass < 3; ++pass) {
@@ -768,10 +808,10 @@ __device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, u
     krem = rem;
   }
   if (tid == 0) {
-    sh.pfx[0] = pf;
-    sh.krem[0] = krem;
-    sh.pos[0] = 0;
-    sh.pos[1] = 0;
+    sh.c->pfx[0] = pf;
+    sh.c->krem[0] = krem;
+    sh.c->pos[0] = 0;
+    sh.c->pos[1] = 0;
   }
   __syncthreads();
 }
@@ -779,7 +819,7 @@ __device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, u
 // CTA-wide exclusive prefix sums of a and b over the threads in order (two
 // barriers).
 template <int NT>
-__device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, CtaShared<NT>& sh) {
+__device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, const Sh<NT>& sh) {
   const int lane = lane_id();
   const int w = wave_id();
   uint32_t ia = a, ib = b;  // inclusive within the wave
@@ -793,21 +833,21 @@ __device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, Ct
   }
   __syncthreads();
   if (lane == 63) {
-    sh.wtot[w] = ia;
-    sh.wcnt[0][w][0] = static_cast<int32_t>(ib);
+    sh.c->wtot[w] = ia;
+    sh.c->wcnt[0][w][0] = static_cast<int32_t>(ib);
   }
   __syncthreads();
   uint32_t ba = 0u, bb = 0u;
   for (int q = 0; q < w; ++q) {
-    ba += sh.wtot[q];
-    bb += static_cast<uint32_t>(sh.wcnt[0][q][0]);
+    ba += sh.c->wtot[q];
+    bb += static_cast<uint32_t>(sh.c->wcnt[0][q][0]);
   }
   a = ba + ia - a;
   b = bb + ib - b;
 }
 
 // Top-k of a row whose nc candidates exceed k by d = nc - k <= kFewExtra (the
-// pairs of the slots below npre already in sh.u.fin.idx / sh.u.fin.key): the
+// pairs of the slots below npre already in sh.fi / sh.fk): the
 // d smallest candidates (by radix key, ties by slot position) are left out
 // and every other candidate's index is written in slot order.  Each of the d
 // rounds finds the smallest pair not yet left out: a tree over each thread's
@@ -816,11 +856,11 @@ __device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, Ct
 // left-out positions before it, so the stores stay coalesced.
 template <int NT>
 __device__ __forceinline__ void few_extra_topk(const int32_t* cand, int32_t* out, int nc, int d, float th, int npre,
-                                               CtaShared<NT>& sh) {
+                                               const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   constexpr int kPer = kFinalizeLds / kThreads;
-  uint32_t* key = sh.u.fin.key;
-  int32_t* idx = sh.u.fin.idx;
+  uint32_t* key = sh.fk;
+  int32_t* idx = sh.fi;
   if (npre < nc) {
     // the pairs not in LDS yet, all of a thread's loads in flight
     int2 v[kPer];
@@ -871,11 +911,11 @@ __device__ __forceinline__ void few_extra_topk(const int32_t* cand, int32_t* out
 #pragma unroll
       for (int u = 0; u < w; ++u) m[u] = min(m[u], m[u + w]);
     const uint64_t wm = __ockl_wfred_min_u64(m[0]);
-    if (lane_id() == 0) sh.low[j][wave_id()] = wm;
+    if (lane_id() == 0) sh.c->low[j][wave_id()] = wm;
     __syncthreads();
-    uint64_t g = sh.low[j][0];
+    uint64_t g = sh.c->low[j][0];
 #pragma unroll
-    for (int q = 1; q < kWaves; ++q) g = min(g, sh.low[j][q]);
+    for (int q = 1; q < kWaves; ++q) g = min(g, sh.c->low[j][q]);
     const uint32_t pj = static_cast<uint32_t>(g);
     if (j == 0) p0 = pj;
     else if (j == 1) p1 = pj;
@@ -902,10 +942,10 @@ __device__ __forceinline__ void few_extra_topk(const int32_t* cand, int32_t* out
 // candidates by decoded score -- all but the few smallest when at most
 // kFewExtra are left out, else by a 3-pass radix select over keys kept in LDS
 // (read from the slots once).  Entries past k are -1.  The first npre
-// candidate pairs may be in sh.u.fin.idx / sh.u.fin.key already.
+// candidate pairs may be in sh.fi / sh.fk already.
 template <int NT>
 __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, int npre,
-                                              CtaShared<NT>& sh) {
+                                              const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   constexpr int kPer = kFinalizeLds / kThreads;
   const int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
@@ -922,7 +962,7 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
           if (u >= nu) break;
-          v[u] = sh.u.fin.idx[min(i0 + u * kThreads + tid, nc - 1)];
+          v[u] = sh.fi[min(i0 + u * kThreads + tid, nc - 1)];
         }
       }
 #pragma unroll
@@ -946,9 +986,9 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
     return;
   }
   const bool in_lds = nc <= kFinalizeLds;
-  uint32_t* hist = sh.u.fin.hist;
-  uint32_t* keys = sh.u.fin.key;
-  int32_t* idx = sh.u.fin.idx;
+  uint32_t* hist = sh.fh;
+  uint32_t* keys = sh.fk;
+  int32_t* idx = sh.fi;
   const int32_t* cand = slots + 2 * s.top_k;
   if (in_lds) {
     // (index, score) pairs into LDS, all of a thread's loads in flight at once
@@ -975,8 +1015,8 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
     return in_lds ? keys[i] : radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
   };
   cta_radix_select(key_of, nc, k, hist, sh);
-  const uint32_t kstar = sh.pfx[0];
-  const int n_eq = static_cast<int>(sh.krem[0]);
+  const uint32_t kstar = sh.c->pfx[0];
+  const int n_eq = static_cast<int>(sh.c->krem[0]);
   const int n_gt = k - n_eq;
   if (in_lds) {
     // each thread's keys above k* (and equal to it) counted, one CTA-wide
@@ -1012,53 +1052,45 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
   for (int i = tid; i < nc; i += kThreads) {
     const uint32_t key = key_of(i);
     if (key > kstar) {
-      out[atomicAdd(&sh.pos[0], 1)] = cand[2 * i];
+      out[atomicAdd(&sh.c->pos[0], 1)] = cand[2 * i];
     } else if (key == kstar) {
-      const int e = atomicAdd(&sh.pos[1], 1);
+      const int e = atomicAdd(&sh.c->pos[1], 1);
       if (e < n_eq) out[n_gt + e] = cand[2 * i];
     }
   }
   __syncthreads();
 }
 
-// Fit test of tile b (its request's length at *len) from its counters: fills
-// sh.nc, sh.nt, sh.thr and sh.len and returns the mask of rows that do not
-// fit.  It also loads the first npre <= kPreCap candidate pairs of row r_pre
-// (index, score bits) into the registers of waves 1-3: pair u * kPreThreads +
-// tid - 64 into pre[u].  All of these loads are issued together.
+// Fit test of tile b (request length L) by the tile's last CTA, from the final
+// counters (every CTA of the tile counted its keys before it arrived): fills
+// sh.c->nc, nt, thr and len, and the masks of the rows that do not fit --
+// stored_mask: rows whose candidates past the capacity all sit in the
+// workspace's overflow area (at most overflow pairs) and in LDS (at most
+// fin_cap), re-selected from those candidates alone; repair_mask: the other
+// rows, whose keys are swept again.
 template <int NT>
-__device__ __forceinline__ uint32_t tile_fit(const SelectArgs& s, const int32_t* len, int b, CtaShared<NT>& sh,
-                                             int r_pre, int npre, int2 (&pre)[kPreUnits]) {
+__device__ __forceinline__ void tile_fit(const SelectArgs& s, int b, int L, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
-  if (tid == 0) sh.repair_mask = 0u;
-  int nc = 0, nt = 0, L = 0;
-  float th = 0.f;
+  if (tid == 0) {
+    sh.c->repair_mask = 0u;
+    sh.c->stored_mask = 0u;
+    sh.c->len = L;
+  }
+  __syncthreads();
   if (tid < NT) {
     const int r = b * NT + tid;
-    nc = __hip_atomic_load(s.counters + 2 * r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    nt = __hip_atomic_load(s.counters + 2 * r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    th = s.thresholds[r];
-    L = *len;
-  }
-  const int32_t* cand = s.candidates + (static_cast<int64_t>(r_pre) * (s.top_k + s.capacity) + s.top_k) * 2;
-  const int pt = tid - 64;
-#pragma unroll
-  for (int u = 0; u < kPreUnits; ++u) {
-    const int i = u * kPreThreads + pt;
-    pre[u] = pt >= 0 && i < npre ? *reinterpret_cast<const int2*>(cand + 2 * i) : int2{0, 0};
-  }
-  __syncthreads();
-  if (tid < NT) {
+    const int nc = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+    const int nt = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
+    const float th = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
     const int k = min(max(0, L - NT + tid + 1), s.top_k);
     const bool fit = nc <= s.capacity && nc + min(nt, s.top_k) >= k;
-    sh.nc[tid] = nc;
-    sh.nt[tid] = nt;
-    sh.thr[tid] = th;
-    if (tid == 0) sh.len = L;
-    if (!fit) atomicOr(&sh.repair_mask, 1u << tid);
+    const bool stored = nc > s.capacity && nc >= k && nc - s.capacity <= kOverflowPairs && nc <= sh.fin_cap;
+    sh.c->nc[tid] = nc;
+    sh.c->nt[tid] = nt;
+    sh.c->thr[tid] = th;
+    if (!fit) atomicOr(stored ? &sh.c->stored_mask : &sh.c->repair_mask, 1u << tid);
   }
   __syncthreads();
-  return sh.repair_mask;
 }
 
 // The D smallest of a set of doubles, kept sorted in m[0..D-1]; kFewBig pads.
@@ -1119,7 +1151,7 @@ __device__ __forceinline__ void dpp_merge(Smallest<D>& x) {
 // slot order shifted past the left-out positions, so the stores stay coalesced.
 template <int NT, int D>
 __device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, int k, int nc,
-                                                    const int2 (&pre)[kPreUnits], CtaShared<NT>& sh) {
+                                                    const int2 (&pre)[kPreUnits], const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   const int w = wave_id();
   int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
@@ -1145,7 +1177,7 @@ __device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, 
   dpp_merge<0x118, 0xf>(sm);  // row_shr:8
   dpp_merge<0x142, 0xa>(sm);  // row_bcast:15
   dpp_merge<0x143, 0xc>(sm);  // row_bcast:31
-  double* xw = reinterpret_cast<double*>(&sh.low[0][0]);  // the waves' sets (8-byte aligned)
+  double* xw = reinterpret_cast<double*>(&sh.c->low[0][0]);  // the waves' sets (8-byte aligned)
   static_assert(kFewExtra * kWaves >= D * kWaves, "room for every wave's set");
   if (lane_id() == 63) {
 #pragma unroll
@@ -1193,7 +1225,7 @@ __device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, 
 // pairs possibly loaded already, as finalize_topk takes them).
 template <int NT>
 __device__ __forceinline__ void row_outputs(const SelectArgs& s, int r, int k, int nc, int nt, float th, int npre,
-                                            CtaShared<NT>& sh) {
+                                            const Sh<NT>& sh) {
   if (threadIdx.x == 0) {
     s.ranges[r] = s.top_k - min(nt, s.top_k);
     s.ranges[s.rows + r] = s.top_k + min(nc, s.capacity);
@@ -1208,7 +1240,7 @@ __device__ __forceinline__ void row_outputs(const SelectArgs& s, int r, int k, i
 // aside) and waits for none of these loads.
 template <int NT>
 __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int k, int nc, int nt, float th, int npre,
-                                                const int2 (&pre)[kPreUnits], CtaShared<NT>& sh) {
+                                                const int2 (&pre)[kPreUnits], const Sh<NT>& sh) {
   const bool exact = nc == k;
   const bool few = nc > k && nc - k <= kFewExtra && nc <= npre;
   if (!s.topk_idx || exact || few) {
@@ -1240,8 +1272,8 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
   for (int u = 0; u < kPreUnits; ++u) {
     const int i = u * kPreThreads + tid - 64;
     if (tid >= 64 && i < npre) {
-      sh.u.fin.idx[i] = pre[u].x;
-      sh.u.fin.key[i] = static_cast<uint32_t>(pre[u].y);
+      sh.fi[i] = pre[u].x;
+      sh.fk[i] = static_cast<uint32_t>(pre[u].y);
     }
   }
   __syncthreads();
@@ -1250,131 +1282,146 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
 
 // ---------------------------------------------------------------- finish
 
-// Each tile is finished by a second kernel, launched right after the select
-// kernel on the same stream, so it starts with every slot and counter of the
-// main pass in memory and the memory system idle.  Phase A: CTA i takes rows
-// i, i + grid, ...: the fit test of the row's tile, then either the row's
-// ranges and exact Top-k, or, for a row that does not fit, over stored scores
-// of a request of at most kLocalRepairKeys keys, the row's repair by this CTA
-// alone (local_repair_row), or else, from the CTA with the tile's first row
-// that does not fit, a repair job: the mask of those rows, their state words,
-// and the tile appended to the job list.  Phase B: every CTA runs
-// repair items.  A job runs in stages, each split into items of a few thousand
-// keys of the request:
-//   stages 1-3  radix histogram pass 0/1/2 (11/11/10 bits) of the repaired
-//               rows' keys, into per-row global histograms;
-//   stage 4     collect: keys above the selected bucket become candidates
-//               (stored raw), keys inside it go to a per-row bucket buffer;
-//   stage 5     select again at the now exact k-th largest score;
-//   stage 6     one item per row: for a collected row, the exact k-th largest
-//               key from its bucket (the bucket's keys appended, the collected
-//               candidates re-encoded against it), then the row's ranges and
-//               Top-k.
-// The fused repair computes the scores from the KV pages once, in stage 1, and
-// keeps the repaired rows' scores in the workspace's score buffer; its later
-// stages read them back (4 bytes a key instead of 132), as the repair of a
-// select over a logits matrix reads the matrix.
+// The finish stage runs in the select launch itself.  Each CTA, once its keys
+// are selected, arrives on its tile's arrival counter (an atomic add, after
+// its slot stores and counter updates have completed: those are agent-scope
+// write-through stores and atomics, so no dirty line of them stays in the
+// storing XCD's L2).  The CTA that brings the count to the tile's number of
+// CTAs is the tile's last: it re-zeroes the counter, takes an agent-scope
+// acquire and runs the fit test on the final counters (page
+// "flashinfer.sdsa.indexer_threshold_select", description paragraph 3 and
+// parameter arrivals).  A tile whose rows all fit is finished at once (one
+// row: by the last CTA itself; more rows: one row item each, the last CTA
+// taking the first).  Rows that do not fit are repaired:
+//   * a row whose candidates all sit in its slots and the workspace's overflow
+//     area is selected again from those candidates alone (its k-th largest
+//     candidate becomes its threshold; every key at or above it is one of
+//     them), in its row item;
+//   * the other rows' keys are swept again by a repair job, in stages split
+//     into items of a few thousand keys that every CTA of the launch may run:
+//       stages 1-3  radix histogram pass 0/1/2 (10/11/11 bits) of the repaired
+//                   rows' keys, into per-row global histograms (the fused
+//                   select computes the scores again in stage 1 and keeps the
+//                   repaired rows' scores in the workspace's score rows for
+//                   the later stages; the select over a logits matrix reads
+//                   the matrix);
+//       stage 4     collect: keys above the selected bucket become candidates
+//                   (stored raw), keys inside it go to the row's bucket;
+//       stage 5     select again at the now exact k-th largest score;
+//       stage 6     one item per row: a collected row's exact k-th largest key
+//                   from its bucket, then every row's ranges and Top-k.
 // After a histogram pass the digit holding each row's k-th largest key is
-// found; if every row's bucket fits the bucket buffer the job moves to stage 4,
-// if every key bit is known to stage 5, else to the next pass; stages 4 and 5
-// lead to stage 6.  An item is
+// found; if every row's bucket fits the bucket area the job moves to stage 4,
+// if every key bit is known to stage 5, else to the next pass.  An item is
 // claimed by a 64-bit fetch-and-add on one of the job's kClaimWords (stage,
 // next) words, word q handing out items q, q + kClaimWords, ...: an item below
 // the stage's item count is the caller's, a larger one claims nothing.
-// Whoever completes a stage's last item runs the stage change, which rewrites
-// the words to (next stage, 0), or after stage 6 clears the job's words.  A CTA with no open item waits (a bounded number of polls)
-// while some CTA is still in phase A, a listed job is not yet written, or a job
-// is in a stage before 6 (its change opens new items), and leaves otherwise;
-// the wait only adds hands, since each job is carried to its end by the CTA that
-// completes each of its stages.  Shared words are written with agent-scope
-// atomic (write-through) stores or atomic adds and read with agent-scope atomic
-// loads.  A job's last step clears its words; the select kernel clears the
-// header and the job list at its start, when no finish kernel can be running.
+// Whoever completes a stage's last item runs the stage change.  After its own
+// keys (and its tile's finish, if last) a CTA claims items; with none open it
+// waits, for a bounded time, while some tile has not been through its fit test
+// or a job is before its last stage (only when every CTA of the launch is
+// resident: otherwise waiting CTAs could keep others from starting), and
+// leaves otherwise: each job is carried to its end by the CTAs that complete
+// its stages, so nothing depends on the waiting.  The last CTA to leave clears
+// the header, the flags and the job list for the next call.
 constexpr int kClaimWords = 4;  // claim words per repair job
 constexpr int kStageHist0 = 1;
 constexpr int kStageCollect = 4;
 constexpr int kStageSelect = 5;
 constexpr int kStageRows = 6;
-constexpr int kIdlePolls = 20000;  // bound on a CTA's polls without an item
-constexpr int kHdrBatch = 3, kHdrNextN = 4, kHdrMagic = 5;  // header words of the layout record
-constexpr uint32_t kLayoutMagic = 0x41514d50u;
+constexpr uint64_t kIdleTicks = 20000;  // s_memrealtime ticks (100 MHz) a CTA waits without an item: 200 us
 static_assert(2 * kClaimWords + 1 + 6 < kJobWords, "a job's claim words, mask and per-stage counts");
 
 struct Ws {
   uint32_t* base;
   int batch, rows;
-  // [0,1] the progress word (below), [3..5] the layout of the last finish
-  // kernel (the select kernel clears [0..2], the flags and the list before
-  // each finish kernel)
+  // [0,1] progress: tiles through their fit test (low half) and jobs listed
+  // (high half); [2] CTAs that have left
   __device__ uint32_t* hdr() const { return base; }
-  // rows through phase A (low half) and job list entries reserved (high half)
   __device__ uint64_t* progress() const { return reinterpret_cast<uint64_t*>(base); }
-  // copy i of the done flag: 0 while phase A runs, then 1 + the number of jobs
-  // listed (the waiting CTAs poll copy blockIdx % kDoneFlags, 256 bytes apart,
-  // so their polls spread over many lines instead of queueing on one)
-  __device__ uint32_t* flag(int i) const { return base + 16 + kDoneFlagStride * i; }
-  __device__ uint32_t* list(int j) const { return base + 16 + kDoneFlags * kDoneFlagStride + j; }  // tile + 1, 0 until written
-  // [2q, 2q + 1] claim word q < kClaimWords, [2 kClaimWords] row mask,
+  // copy i of the done flag: 0 while a tile is before its fit test, then 1 +
+  // the number of jobs listed (the waiting CTAs poll copy blockIdx % kDoneFlags,
+  // 256 bytes apart, so their polls spread over many lines)
+  __device__ uint32_t* flag(int i) const { return base + kHdrWords + kDoneFlagStride * i; }
+  __device__ uint32_t* list(int j) const { return base + kHdrWords + kDoneFlags * kDoneFlagStride + j; }  // tile + 1
+  __device__ WsLayout lay() const { return workspace_layout(batch, rows, 0, false); }
+  // [2q, 2q + 1] claim word q < kClaimWords, [2 kClaimWords] row masks (the
+  // swept rows, and in bits 8.. the rows re-selected from their candidates),
   // [2 kClaimWords + 1 + stage] items done in the stage
-  __device__ uint32_t* job(int b) const {
-    return base + 16 + kDoneFlags * kDoneFlagStride + job_list_words(batch) + kJobWords * b;
-  }
-  // Claim word q hands out items q, q + kClaimWords, ... of the job's stage: a
-  // CTA claims from word blockIdx % kClaimWords, so the atomics of a stage's
-  // claims spread over kClaimWords words instead of queueing on one.
+  __device__ uint32_t* job(int b) const { return base + lay().jobs + kJobWords * b; }
   __device__ uint64_t* claim(int b, int q) const { return reinterpret_cast<uint64_t*>(job(b) + 2 * q); }
   __device__ uint32_t* mask_word(int b) const { return job(b) + 2 * kClaimWords; }
   __device__ uint32_t* done_word(int b, int stage) const { return job(b) + 2 * kClaimWords + 1 + stage; }
-  // [0] digit prefix [1] rank left [2] bits known [3] bucket count
-  __device__ uint32_t* row(int r) const { return job(batch) + kRowWords * r; }
+  // per row: [0] digit prefix [1] rank left [2] bits known [3] bucket count
+  __device__ uint32_t* row(int r) const { return base + lay().row_state + kRowWords * r; }
   // copy c of row r's radix histogram (items add into copy idx % kHistCopies,
   // which spreads the atomics of a pass over kHistCopies times more lines)
   __device__ uint32_t* hist(int r, int c) const {
-    return job(batch) + kRowWords * rows + static_cast<int64_t>(kRadixBins) * (kHistCopies * r + c);
+    return base + lay().hist + static_cast<int64_t>(kRadixBins) * (kHistCopies * r + c);
   }
   __device__ int32_t* bucket(int r) const {
-    return reinterpret_cast<int32_t*>(job(batch) + (kRowWords + kHistCopies * kRadixBins) * rows) +
-           static_cast<int64_t>(2) * kFinalizeLds * r;
+    return reinterpret_cast<int32_t*>(base + lay().bucket) + 2 * static_cast<int64_t>(kBucketPairs) * r;
+  }
+  __device__ int32_t* overflow(int r) const {
+    return reinterpret_cast<int32_t*>(base + lay().overflow) + 2 * static_cast<int64_t>(kOverflowPairs) * r;
   }
 };
 
 // Items of a stage of a request of L keys: kRescoreItemKeys keys when the
 // scores are computed from the KV pages (stage 1 of the fused repair), else
 // kSelectItemKeys keys read back from a score row; one per row in stage 6.
+// Keys of a repair item over stored scores (fewer for next_n >= 3, whose
+// items hold every repaired row's scores in registers at once).
+template <int NT>
+constexpr int kItemKeys = NT >= 3 ? kSelectItemKeys / 2 : kSelectItemKeys;
+
 template <int NT, bool kFused>
 __device__ __forceinline__ int stage_items(int stage, int L) {
   if (stage == kStageRows) return NT;
-  const int keys = (kFused && stage == kStageHist0) ? kRescoreItemKeys : kSelectItemKeys;
+  const int keys = (kFused && stage == kStageHist0) ? kRescoreItemKeys : kItemKeys<NT>;
   return max(1, static_cast<int>(ceil_div(L, keys)));
 }
 
-// Phase A hands the rows of tile b in `mask` to phase B: their state words and
-// the claim words first, then (once those are complete) the list entry.
+// The tile's last CTA lists tile b's job: the swept rows' state words and
+// histograms set up, the row masks, the per-stage counts cleared and the claim
+// words opened at `stage` (with item 0 kept back for the caller when self0),
+// then -- once all of that is complete -- the list entry.
 template <int NT>
-__device__ __forceinline__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int (&end)[NT], uint32_t mask) {
+__device__ __forceinline__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int (&end)[NT],
+                                            uint32_t sweep, uint32_t stored, int stage, bool self0) {
   const int tid = threadIdx.x;
-  if (tid < NT && (mask & (1u << tid))) st_wt(ws.row(b * NT + tid) + 1, static_cast<uint32_t>(min(end[tid], s.top_k)));
-  if (tid == 0) st_wt(ws.mask_word(b), mask);
-  if (tid < kClaimWords) st_wt64(ws.claim(b, tid), static_cast<uint64_t>(kStageHist0) << 32);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(sweep & (1u << t))) continue;
+    uint32_t* h = ws.hist(b * NT + t, 0);
+    for (int i = tid; i < kHistCopies * kRadixBins; i += kThreads) st_wt(h + i, 0u);
+  }
+  if (tid < NT && (sweep & (1u << tid))) {
+    uint32_t* row = ws.row(b * NT + tid);
+    st_wt(row + 0, 0u);
+    st_wt(row + 1, static_cast<uint32_t>(min(end[tid], s.top_k)));
+    st_wt(row + 2, 0u);
+    st_wt(row + 3, 0u);
+  }
+  if (tid == 64) st_wt(ws.mask_word(b), sweep | (stored << 8));
+  if (tid >= 128 && tid < 128 + kStageRows) st_wt(ws.done_word(b, tid - 127), 0u);
+  if (tid >= 192 && tid < 192 + kClaimWords)
+    st_wt64(ws.claim(b, tid - 192), (static_cast<uint64_t>(stage) << 32) | ((self0 && tid == 192) ? 1u : 0u));
   wait_vm_done();
   __syncthreads();
   if (tid == 0) {
     const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.progress()), 1ull << 32);
     st_wt(ws.list(static_cast<int>(old >> 32)), static_cast<uint32_t>(b + 1));
+    wait_vm_done();  // the list entry before the tile is counted
   }
 }
 
-// One row through phase A: the count (thread 0, after every store that lists
-// a job of the CTA has completed); it returns the progress word before it.
-__device__ __forceinline__ uint64_t count_row(const Ws& ws) {
-  return atomicAdd(reinterpret_cast<unsigned long long*>(ws.progress()), 1ull);
-}
-
-// Thread 0, with count_row's result: the count of the last row sets every copy
-// of the done flag to 1 + the jobs listed (final by then: each publisher lists
-// its job before it counts its row).
-__device__ __forceinline__ void flag_if_last(const Ws& ws, uint64_t old) {
-  if (static_cast<uint32_t>(old) + 1u == static_cast<uint32_t>(ws.rows)) {
+// Thread 0: tile b through its fit test (after its job, if any, is listed);
+// the count that completes the batch sets every copy of the done flag to 1 +
+// the jobs listed (final by then: each tile lists its job before it counts).
+__device__ __forceinline__ void count_tile(const Ws& ws) {
+  const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.progress()), 1ull);
+  if (static_cast<uint32_t>(old) + 1u == static_cast<uint32_t>(ws.batch)) {
     const uint32_t v = static_cast<uint32_t>(old >> 32) + 1u;
     for (int i = 0; i < kDoneFlags; ++i) st_wt(ws.flag(i), v);
   }
@@ -1388,7 +1435,7 @@ __device__ __forceinline__ void flag_if_last(const Ws& ws, uint64_t old) {
 // return the first), and the keys go to put(t, class, position, key, score).
 template <int NT, int kU, class Cls, class Add1, class Add2, class Put>
 __device__ __forceinline__ void append_item(int c0, int cend, const int (&end)[NT], uint32_t mask,
-                                            const float (&v)[NT][kU], CtaShared<NT>& sh, Cls&& cls, Add1&& add1,
+                                            const float (&v)[NT][kU], const Sh<NT>& sh, Cls&& cls, Add1&& add1,
                                             Add2&& add2, Put&& put) {
   const int w = wave_id();
   const int lane = lane_id();
@@ -1406,8 +1453,8 @@ __device__ __forceinline__ void append_item(int c0, int cend, const int (&end)[N
       n2 += __popcll(__ballot(c == 2));
     }
     if (lane == 0) {
-      sh.wcnt[t][w][0] = n1;
-      sh.wcnt[t][w][1] = n2;
+      sh.c->wcnt[t][w][0] = n1;
+      sh.c->wcnt[t][w][1] = n2;
     }
   }
   __syncthreads();
@@ -1415,18 +1462,18 @@ __device__ __forceinline__ void append_item(int c0, int cend, const int (&end)[N
     int tot[2] = {0, 0};
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) {
-      tot[0] += sh.wcnt[tid][q][0];
-      tot[1] += sh.wcnt[tid][q][1];
+      tot[0] += sh.c->wcnt[tid][q][0];
+      tot[1] += sh.c->wcnt[tid][q][1];
     }
     int base[2];
     base[0] = tot[0] ? add1(tid, tot[0]) : 0;
     base[1] = tot[1] ? add2(tid, tot[1]) : 0;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) {
-      sh.wbase[tid][q][0] = base[0];
-      sh.wbase[tid][q][1] = base[1];
-      base[0] += sh.wcnt[tid][q][0];
-      base[1] += sh.wcnt[tid][q][1];
+      sh.c->wbase[tid][q][0] = base[0];
+      sh.c->wbase[tid][q][1] = base[1];
+      base[0] += sh.c->wcnt[tid][q][0];
+      base[1] += sh.c->wcnt[tid][q][1];
     }
   }
   __syncthreads();
@@ -1434,7 +1481,7 @@ __device__ __forceinline__ void append_item(int c0, int cend, const int (&end)[N
   for (int t = 0; t < NT; ++t) {
     if (!(mask & (1u << t))) continue;
     const int lim = min(cend, end[t]);
-    int r1 = sh.wbase[t][w][0], r2 = sh.wbase[t][w][1];
+    int r1 = sh.c->wbase[t][w][0], r2 = sh.c->wbase[t][w][1];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
@@ -1452,7 +1499,7 @@ __device__ __forceinline__ void append_item(int c0, int cend, const int (&end)[N
 // Stage change after histogram pass `pass` of tile b's job (run by the CTA that
 // completed the pass's last item).
 template <int NT>
-__device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws, int b, int pass, uint32_t mask, CtaShared<NT>& sh) {
+__device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws, int b, int pass, uint32_t mask, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   const int wave = wave_id();
   const int lane = lane_id();
@@ -1460,35 +1507,29 @@ __device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws
   const int bits = pass_bits(pass);
   const int nb = 1 << bits;
   // each row's histogram: the sum of its copies, which are cleared for the next
-  // pass.  Every row's copies are loaded together (kHistCopies * nb / kThreads
-  // words a thread and row), so the sum costs one round trip, not one per row
-  // and half histogram.
+  // pass.  A row's copies are loaded together (kHistCopies * nb / kThreads
+  // words a thread), so the sum costs one round trip per row.
   constexpr int kJ = kRadixBins / kThreads;  // bins of a thread
-  uint32_t v[NT][kJ][kHistCopies];
-#pragma unroll
+#pragma unroll 1
   for (int t = 0; t < NT; ++t) {
     if (!(mask & (1u << t))) continue;
-    const uint32_t* gh = ws.hist(b * NT + t, 0);
+    uint32_t* gh = ws.hist(b * NT + t, 0);
+    uint32_t v[kJ][kHistCopies];
 #pragma unroll
     for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int c = 0; c < kHistCopies; ++c)
-        v[t][j][c] = j * kThreads < nb ? ld_ag(gh + c * kRadixBins + j * kThreads + tid) : 0u;
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (!(mask & (1u << t))) continue;
-    uint32_t* gh = ws.hist(b * NT + t, 0);
+        v[j][c] = j * kThreads < nb ? ld_ag(gh + c * kRadixBins + j * kThreads + tid) : 0u;
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       if (j * kThreads >= nb) continue;
       uint32_t sum = 0u;
 #pragma unroll
       for (int c = 0; c < kHistCopies; ++c) {
-        sum += v[t][j][c];
-        if (v[t][j][c]) st_wt(gh + c * kRadixBins + j * kThreads + tid, 0u);
+        sum += v[j][c];
+        if (v[j][c]) st_wt(gh + c * kRadixBins + j * kThreads + tid, 0u);
       }
-      sh.u.hist[t][j * kThreads + tid] = sum;
+      sh.rh[t][j * kThreads + tid] = sum;
     }
   }
   __syncthreads();
@@ -1496,11 +1537,11 @@ __device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws
     uint32_t* row = ws.row(b * NT + wave);
     const uint32_t pfx = ld_ag(row + 0);
     uint32_t d = 0, rem = 0;
-    find_digit(sh.u.hist[wave], nb, ld_ag(row + 1), &d, &rem);
+    find_digit(sh.rh[wave], nb, ld_ag(row + 1), &d, &rem);
     if (lane == 0) {
-      sh.pfx[wave] = pass == 0 ? d : ((pfx << bits) | d);
-      sh.krem[wave] = rem;
-      sh.cnt[wave][0] = static_cast<int32_t>(sh.u.hist[wave][d]);
+      sh.c->pfx[wave] = pass == 0 ? d : ((pfx << bits) | d);
+      sh.c->krem[wave] = rem;
+      sh.c->cnt[wave][0] = static_cast<int32_t>(sh.rh[wave][d]);
     }
   }
   __syncthreads();
@@ -1508,23 +1549,23 @@ __device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws
   if (tid == 0) {
     bool small = true;
     for (int t = 0; t < NT; ++t)
-      if ((mask & (1u << t)) && sh.cnt[t][0] > kFinalizeLds) small = false;
-    sh.next_stage = known == 32 ? kStageSelect : (small ? kStageCollect : kStageHist0 + pass + 1);
+      if ((mask & (1u << t)) && sh.c->cnt[t][0] > kBucketPairs) small = false;
+    sh.c->next_stage = known == 32 ? kStageSelect : (small ? kStageCollect : kStageHist0 + pass + 1);
   }
   __syncthreads();
-  const int next = sh.next_stage;
+  const int next = sh.c->next_stage;
   if (tid < NT && (mask & (1u << tid))) {
     const int r = b * NT + tid;
     uint32_t* row = ws.row(r);
-    st_wt(row + 0, sh.pfx[tid]);
-    st_wt(row + 1, sh.krem[tid]);
+    st_wt(row + 0, sh.c->pfx[tid]);
+    st_wt(row + 1, sh.c->krem[tid]);
     st_wt(row + 2, static_cast<uint32_t>(known));
     if (next >= kStageCollect) {
       st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, 0u);
       st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, 0u);
       st_wt(row + 3, 0u);
     }
-    if (next == kStageSelect) st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(key_to_float(sh.pfx[tid])));
+    if (next == kStageSelect) st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(key_to_float(sh.c->pfx[tid])));
   }
   wait_vm_done();
   __syncthreads();
@@ -1534,24 +1575,25 @@ __device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws
 // Row r after the collect stage: its exact k-th largest key among its bucket
 // (kept in LDS), the bucket's candidates and ties appended, the raw candidates
 // re-encoded against the new threshold.  Leaves the row's final candidate and
-// tie counts and threshold in sh.nc[0], sh.nt[0], sh.thr[0] (and in counters
+// tie counts and threshold in sh.c->nc[0], sh.c->nt[0], sh.c->thr[0] (and in counters
 // and thresholds).
 template <int NT>
-__device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, int r, CtaShared<NT>& sh) {
+__device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, int r, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   const int stride = s.top_k + s.capacity;
   uint32_t* row = ws.row(r);
-  // the bucket holds the keys of one digit, at most kFinalizeLds by the stage
+  // the bucket holds the keys of one digit, at most kBucketPairs by the stage
   // change's test
-  const int nin = min(static_cast<int>(ld_ag(row + 3)), kFinalizeLds);
+  const int nin = min(static_cast<int>(ld_ag(row + 3)), kBucketPairs);
+  static_assert(kBucketPairs <= kFinalizeLds, "a bucket fits the final select's LDS");
   const int krem = static_cast<int>(ld_ag(row + 1));
   const int nabove = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
   int32_t* bucket = ws.bucket(r);
   // the bucket's (index, score bits) pairs into LDS, all of a thread's loads in
   // flight at once (the radix keys are derived from the bits where needed)
   constexpr int kPer = kFinalizeLds / kThreads;
-  uint32_t* bits = sh.u.fin.key;
-  int32_t* idxs = sh.u.fin.idx;
+  uint32_t* bits = sh.fk;
+  int32_t* idxs = sh.fi;
   {
     int2 v[kPer];
 #pragma unroll
@@ -1570,8 +1612,8 @@ __device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, i
   }
   __syncthreads();
   auto key_of = [&](int i) { return radix_key(__uint_as_float(bits[i])); };
-  cta_radix_select(key_of, nin, krem, sh.u.fin.hist, sh);
-  const uint32_t kstar = sh.pfx[0];
+  cta_radix_select(key_of, nin, krem, sh.fh, sh);
+  const uint32_t kstar = sh.c->pfx[0];
   const float t2 = key_to_float(kstar);
   int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
   #pragma unroll 1
@@ -1580,10 +1622,10 @@ __device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, i
     const int32_t idx = idxs[i];
     const float e = __uint_as_float(bits[i]);
     if (key > kstar) {
-      const int k = nabove + atomicAdd(&sh.pos[0], 1);
+      const int k = nabove + atomicAdd(&sh.c->pos[0], 1);
       if (k < s.capacity) store_pair(slots + 2 * (s.top_k + k), idx, enc_cand(e, t2));
     } else if (key == kstar) {
-      const int k = atomicAdd(&sh.pos[1], 1);
+      const int k = atomicAdd(&sh.c->pos[1], 1);
       if (k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), idx, e - t2);
     }
   }
@@ -1605,76 +1647,209 @@ __device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, i
   }
   __syncthreads();
   if (tid == 0) {
-    const int nc = nabove + sh.pos[0], nt = sh.pos[1];
+    const int nc = nabove + sh.c->pos[0], nt = sh.c->pos[1];
     st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, static_cast<uint32_t>(nc));
     st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(nt));
     st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
-    sh.nc[0] = nc;
-    sh.nt[0] = nt;
-    sh.thr[0] = t2;
+    sh.c->nc[0] = nc;
+    sh.c->nt[0] = nt;
+    sh.c->thr[0] = t2;
   }
   // this CTA's slot stores complete before the Top-k reads the slots back
   wait_vm_done();
   __syncthreads();
 }
 
-// Stage 6 item t of tile b's job: row t, if repaired, resolved (after a
-// collect) and given its ranges and Top-k.  The row's state words are cleared
-// for the next call.
+// Row r (k = min(e_r, top_k) >= 1) re-selected from its candidates alone: all
+// n_cand of them are kept -- the first `capacity` in its slots (encoded against
+// the old threshold), the rest in the workspace's overflow area -- and every
+// key at or above its k-th largest candidate is a candidate (it scores above
+// the old threshold).  The k-th largest candidate score, radix-selected in
+// LDS, becomes the row's threshold; the candidates above it and those equal
+// to it are stored again as the row's candidates and ties, and its counters,
+// threshold, ranges and Top-k written.  (Scores are NaN-free by precondition,
+// so no key outside the candidates is a tie at the new threshold.)
 template <int NT>
-__device__ __forceinline__ void row_end_item(const SelectArgs& s, const Ws& ws, int b, int L, int t, uint32_t mask,
-                             CtaShared<NT>& sh) {
-  if (!(mask & (1u << t))) return;
+__device__ __forceinline__ void stored_resolve(const SelectArgs& s, const Ws& ws, int r, int k, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
-  const int r = b * NT + t;
-  // the collect stage's stores (other CTAs, written through) become visible
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (ld_ag(ws.row(r) + 2) < 32u) {
-    resolve_row<NT>(s, ws, r, sh);
-  } else {
-    // stage 5 selected the row again at its exact threshold
-    if (tid == 0) {
-      sh.nc[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
-      sh.nt[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
-      sh.thr[0] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
-    }
-    __syncthreads();
+  if (tid == 0) {
+    sh.c->nc[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+    sh.c->thr[0] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
   }
-  const int k = min(max(0, L - NT + t + 1), s.top_k);
-  row_outputs<NT>(s, r, k, sh.nc[0], sh.nt[0], sh.thr[0], 0, sh);
-  if (tid < 4) st_wt(ws.row(r) + tid, 0u);
+  __syncthreads();
+  const int n = sh.c->nc[0];  // capacity < n <= fin_cap, n - capacity <= kOverflowPairs, n >= k
+  const float th = sh.c->thr[0];
+  const int cap = s.capacity;
+  int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + cap) * 2;
+  const int32_t* cand = slots + 2 * s.top_k;
+  const int32_t* ovf = ws.overflow(r);
+  // every candidate's (index, score bits) into LDS, eight loads of a thread in flight at once
+  constexpr int kBatch = 8;
+  for (int i0 = 0; i0 < n; i0 += kBatch * kThreads) {
+    int2 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      if (i < n) v[u] = *reinterpret_cast<const int2*>(i < cap ? cand + 2 * i : ovf + 2 * (i - cap));
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      if (i < n) {
+        sh.fi[i] = v[u].x;
+        sh.fk[i] = __float_as_uint(dec_cand(__int_as_float(v[u].y), th));
+      }
+    }
+  }
+  __syncthreads();
+  auto key_of = [&](int i) { return radix_key(__uint_as_float(sh.fk[i])); };
+  cta_radix_select(key_of, n, k, sh.fh, sh);
+  const uint32_t kstar = sh.c->pfx[0];
+  const float t2 = key_to_float(kstar);
+  // each thread's keys above k* and equal to it counted, one CTA-wide exclusive
+  // scan of the counts, then every thread writes at its offsets
+  uint32_t gt = 0u, eq = 0u;
+  for (int i = tid; i < n; i += kThreads) {
+    const uint32_t key = key_of(i);
+    gt += key > kstar ? 1u : 0u;
+    eq += key == kstar ? 1u : 0u;
+  }
+  uint32_t og = gt, oe = eq;
+  cta_exclusive_scan2(og, oe, sh);
+  uint32_t n_gt = 0u, n_eq = 0u;  // the totals: the last thread's offsets plus its counts
+  if (tid == kThreads - 1) {
+    sh.c->pos[0] = static_cast<int>(og + gt);
+    sh.c->pos[1] = static_cast<int>(oe + eq);
+  }
+  __syncthreads();
+  n_gt = static_cast<uint32_t>(sh.c->pos[0]);
+  n_eq = static_cast<uint32_t>(sh.c->pos[1]);
+  int32_t* out = s.topk_idx ? s.topk_idx + static_cast<int64_t>(r) * s.top_k : nullptr;
+  for (int i = tid; i < n; i += kThreads) {
+    const uint32_t key = key_of(i);
+    const int32_t idx = sh.fi[i];
+    const float e = __uint_as_float(sh.fk[i]);
+    if (key > kstar) {
+      if (static_cast<int>(og) < cap) store_pair(slots + 2 * (s.top_k + og), idx, enc_cand(e, t2));
+      if (out) st_wt(reinterpret_cast<uint32_t*>(out + og), static_cast<uint32_t>(idx));
+      ++og;
+    } else if (key == kstar) {
+      if (static_cast<int>(oe) < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - oe), idx, e - t2);
+      if (out && n_gt + oe < static_cast<uint32_t>(k)) st_wt(reinterpret_cast<uint32_t*>(out + n_gt + oe), static_cast<uint32_t>(idx));
+      ++oe;
+    }
+  }
+  if (out)
+    for (int i = k + tid; i < s.top_k; i += kThreads) st_wt(reinterpret_cast<uint32_t*>(out + i), 0xffffffffu);
+  if (tid == 0) {
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, n_gt);
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, n_eq);
+    st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
+    s.ranges[r] = s.top_k - min(static_cast<int>(n_eq), s.top_k);
+    s.ranges[s.rows + r] = s.top_k + min(static_cast<int>(n_gt), cap);
+  }
+  __syncthreads();
 }
 
-// Adds the LDS histograms sh.u.hist of pass `pass` of the rows in `mask` to
+// Ranges and exact Top-k of a fitting row r (k = min(e_r, top_k)): its counts
+// and threshold, and its first candidate pairs in the registers of waves 1-3
+// (all of them when it has at most top_k + kFewExtra), loaded in one round trip.
+template <int NT>
+__device__ __forceinline__ void fit_row_outputs(const SelectArgs& s, int r, int k, const Sh<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int npre = s.topk_idx ? min(min(s.capacity, s.top_k + kFewExtra), kPreCap) : 0;
+  if (tid == 0) {
+    sh.c->nc[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+    sh.c->nt[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
+    sh.c->thr[0] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
+  }
+  const int32_t* cand = s.candidates + (static_cast<int64_t>(r) * (s.top_k + s.capacity) + s.top_k) * 2;
+  const int pt = tid - 64;
+  int2 pre[kPreUnits];
+#pragma unroll
+  for (int u = 0; u < kPreUnits; ++u) {
+    const int i = u * kPreThreads + pt;
+    pre[u] = pt >= 0 && i < npre ? *reinterpret_cast<const int2*>(cand + 2 * i) : int2{0, 0};
+  }
+  __syncthreads();
+  row_outputs_pre<NT>(s, r, k, sh.c->nc[0], sh.c->nt[0], sh.c->thr[0], npre, pre, sh);
+}
+
+// Stage-6 item t of tile b's job: row t given its ranges and Top-k -- a swept
+// row after its bucket is resolved (or after stage 5 selected it again), a
+// stored row after its re-selection from its candidates, a fitting row from
+// its slots.  A swept row's state words are cleared for the next call.
+template <int NT>
+__device__ __forceinline__ void row_item(const SelectArgs& s, const Ws& ws, int b, int L, int t, uint32_t masks,
+                                         const Sh<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int r = b * NT + t;
+  const int k = min(max(0, L - NT + t + 1), s.top_k);
+  if (masks & (1u << t)) {
+    if (ld_ag(ws.row(r) + 2) < 32u) {
+      resolve_row<NT>(s, ws, r, sh);
+    } else {
+      // stage 5 selected the row again at its exact threshold
+      if (tid == 0) {
+        sh.c->nc[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+        sh.c->nt[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
+        sh.c->thr[0] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
+      }
+      __syncthreads();
+    }
+    row_outputs<NT>(s, r, k, sh.c->nc[0], sh.c->nt[0], sh.c->thr[0], 0, sh);
+    if (tid < 4) st_wt(ws.row(r) + tid, 0u);
+  } else if ((masks >> 8) & (1u << t)) {
+    stored_resolve<NT>(s, ws, r, k, sh);
+  } else {
+    fit_row_outputs<NT>(s, r, k, sh);
+  }
+}
+
+// Adds the LDS histograms sh.rh of pass `pass` of the rows in `mask` to
 // copy `copy` of their global histograms (nonzero bins only).
 template <int NT>
 __device__ __forceinline__ void flush_hist(const Ws& ws, int b, int pass, uint32_t mask, int copy,
-                                           CtaShared<NT>& sh) {
+                                           const Sh<NT>& sh) {
   const int nb = 1 << pass_bits(pass);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (!(mask & (1u << t))) continue;
     uint32_t* gh = ws.hist(b * NT + t, copy);
     for (int i = threadIdx.x; i < nb; i += kThreads) {
-      const uint32_t h = sh.u.hist[t][i];
+      const uint32_t h = sh.rh[t][i];
       if (h) atomicAdd(gh + i, h);
     }
   }
 }
 
+// LDS areas a re-scoring item uses beside the finish view: the KV staging
+// area, the q operands (next_n >= 3) and NT packed first-pass histograms
+// (1024 bins as 512 words of two 16-bit counts: an item has at most
+// kRescoreItemKeys < 65536 keys per row).
+template <int NT>
+struct RescoreLds {
+  v4i* stage;
+  QLds<NT>* ql;
+  uint32_t* ph;
+};
+
 // Stage 1 of the fused repair, item idx: keys [c0, c1) of request b scored
-// again from the KV pages (the select kernel's loop and arithmetic, so the
-// scores are the same bits), the repaired rows' scores written to the score
-// buffer for the later passes, and their first radix histogram pass.
+// again from the KV pages (the select's loop and arithmetic, so the scores are
+// the same bits), the repaired rows' scores written to the score rows for the
+// later passes, and their first radix histogram pass.
 template <int NT>
 __device__ __forceinline__ void rescore_item(const PagedArgs& a, const SelectArgs& s, const Ws& ws, int b, int L, int idx,
-                             uint32_t mask, const int (&end)[NT], CtaShared<NT>& sh, v4i* lds) {
+                                             uint32_t mask, const int (&end)[NT], const RescoreLds<NT>& rl) {
   const int lane = lane_id();
+  const int tid = threadIdx.x;
   const int shift = pass_shift(0);
-  for (int i = threadIdx.x; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
+  constexpr int kWords = (1 << 10) / 2;
+  for (int i = tid; i < NT * kWords; i += kThreads) rl.ph[i] = 0u;
   __syncthreads();
-  KvSource<NT> src;
-  src.bind(lds);
+  typename std::conditional<(NT >= 3), KvSourceQ<NT>, KvSource<NT>>::type src;
+  src.bind(rl.stage);
+  src.bind_q(rl.ql);
   src.init(a, b);
   float* rows = s.scores + static_cast<int64_t>(b) * NT * s.score_ld;
   const int c0 = idx * kRescoreItemKeys;
@@ -1687,12 +1862,23 @@ __device__ __forceinline__ void rescore_item(const PagedArgs& a, const SelectArg
         for (int t = 0; t < NT; ++t) {
           if (!(mask & (1u << t)) || p >= end[t]) continue;
           st_wt(reinterpret_cast<uint32_t*>(rows + t * s.score_ld + p), __float_as_uint(E[t]));
-          atomicAdd(&sh.u.hist[t][radix_key(E[t]) >> shift], 1u);
+          const uint32_t bin = radix_key(E[t]) >> shift;
+          atomicAdd(&rl.ph[t * kWords + (bin >> 1)], 1u << (16 * (bin & 1u)));
         }
       },
       [](int, int) {});
   __syncthreads();
-  flush_hist<NT>(ws, b, 0, mask, idx % kHistCopies, sh);
+  const int copy = idx % kHistCopies;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!(mask & (1u << t))) continue;
+    uint32_t* gh = ws.hist(b * NT + t, copy);
+    for (int i = tid; i < kWords; i += kThreads) {
+      const uint32_t h = rl.ph[t * kWords + i];
+      if (h & 0xffffu) atomicAdd(gh + 2 * i, h & 0xffffu);
+      if (h >> 16) atomicAdd(gh + 2 * i + 1, h >> 16);
+    }
+  }
 }
 
 // Repair item `idx` of stage `stage` of tile b's job: its keys' scores (read
@@ -1701,10 +1887,14 @@ __device__ __forceinline__ void rescore_item(const PagedArgs& a, const SelectArg
 // the stage bookkeeping.
 template <int NT, bool kFused, class Args>
 __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b, int L, int stage, int idx,
-                         CtaShared<NT>& sh, v4i* lds) {
+                                         const Sh<NT>& sh, const RescoreLds<NT>& rl) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const uint32_t mask = ld_ag(ws.mask_word(b));
+  // the stores of the CTAs that ran the tile's main pass and the job's earlier
+  // stages (written through, before their counts) become visible
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const uint32_t masks = ld_ag(ws.mask_word(b));
+  const uint32_t mask = masks & 0xffu;  // the swept rows
   int end[NT];
   uint32_t pfx[NT];
   float thr2[NT];
@@ -1720,12 +1910,12 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
   }
   bool done = false;
   if (stage == kStageRows) {
-    row_end_item<NT>(s, ws, b, L, idx, mask, sh);
+    row_item<NT>(s, ws, b, L, idx, masks, sh);
     done = true;
   }
   if constexpr (kFused) {
     if (stage == kStageHist0) {
-      rescore_item<NT>(a, s, ws, b, L, idx, mask, end, sh, lds);
+      rescore_item<NT>(a, s, ws, b, L, idx, mask, end, rl);
       done = true;
     }
   }
@@ -1735,11 +1925,11 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
       src.init_rows(s.scores + static_cast<int64_t>(b) * NT * s.score_ld, s.score_ld, mask);
     else
       src.init(a, b);
-    const int c0 = idx * kSelectItemKeys;
-    const int cend = min(c0 + kSelectItemKeys, L);
+    const int c0 = idx * kItemKeys<NT>;
+    const int cend = min(c0 + kItemKeys<NT>, L);
     // The item's scores of the repaired rows, all loaded at once: wave w's
     // group u holds keys c0 + 64*(w + 4u) .. +63.
-    constexpr int kU = kSelectItemKeys / (kGroupKeys * kWaves);
+    constexpr int kU = kItemKeys<NT> / (kGroupKeys * kWaves);
     const int w = wave_id();
     float v[NT][kU];
 #pragma unroll
@@ -1754,7 +1944,7 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
       const int shift = pass_shift(pass);
       const int bits = pass_bits(pass);
       const uint32_t low = (1u << bits) - 1u;
-      for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.u.hist[0][0])[i] = 0u;
+      for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.rh[0][0])[i] = 0u;
       __syncthreads();
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -1766,7 +1956,7 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
           if (p >= lim) continue;
           const uint32_t key = radix_key(v[t][u]);
           if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
-          atomicAdd(&sh.u.hist[t][(key >> shift) & low], 1u);
+          atomicAdd(&sh.rh[t][(key >> shift) & low], 1u);
         }
       }
       __syncthreads();
@@ -1786,7 +1976,7 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
           [&](int t, int c, int k, int p, float e) {
             if (c == 1 && k < s.capacity)
               store_pair(s.candidates + (static_cast<int64_t>(b * NT + t) * stride + s.top_k + k) * 2, p, e);
-            if (c == 2 && k < kFinalizeLds) store_pair(ws.bucket(b * NT + t) + 2 * k, p, e);
+            if (c == 2 && k < kBucketPairs) store_pair(ws.bucket(b * NT + t) + 2 * k, p, e);
           });
     } else {
       // select again at the now exact threshold
@@ -1807,9 +1997,9 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
   wait_vm_done();
   __syncthreads();
   if (tid == 0)
-    sh.is_last = atomicAdd(ws.done_word(b, stage), 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
+    sh.c->is_last = atomicAdd(ws.done_word(b, stage), 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
   __syncthreads();
-  if (!sh.is_last) return;
+  if (!sh.c->is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (stage < kStageCollect) {
     job_next_stage<NT>(s, ws, b, stage - kStageHist0, mask, sh);
@@ -1823,17 +2013,19 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
   }
 }
 
-// Wave 0 claims an item of a listed job; the result goes to sh.job: (tile,
+// Wave 0 claims an item of a listed job; the result goes to sh.c->job: (tile,
 // stage, item), tile -1 when none is open but more may open, -2 when the CTA
-// should leave.
+// should leave.  `since` is when the CTA last had an item (s_memrealtime).
 template <int NT, bool kFused, class Args>
-__device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idle, CtaShared<NT>& sh) {
+__device__ __forceinline__ void claim_item(const Args& a, const SelectArgs& s, const Ws& ws, uint64_t since,
+                                           const Sh<NT>& sh) {
   if (wave_id() == 0) {
     const int lane = lane_id();
-    // (a workspace that was not left zeroed gives wrong results, not stray accesses)
+    // (a workspace whose header was not left zeroed gives wrong results, not stray accesses)
     const uint32_t fl = ld_ag(ws.flag(static_cast<int>(blockIdx.x % kDoneFlags)));
-    const int njobs = fl ? min(static_cast<int>(fl - 1u), ws.batch) : 0;
-    bool pending = fl == 0u;  // phase A still running
+    const int njobs = fl ? min(static_cast<int>(fl - 1u), ws.batch)
+                         : min(static_cast<int>(ld_ag64(ws.progress()) >> 32), ws.batch);
+    bool pending = fl == 0u;  // a tile is still before its fit test
     int got = -1, stage = 0, idx = 0;
     const int q = static_cast<int>(blockIdx.x % kClaimWords);  // this CTA's claim word
     for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
@@ -1877,466 +2069,101 @@ __device__ __forceinline__ void claim_item(const Args& a, const Ws& ws, int& idl
         }
       }
     }
-    if (got < 0 && (!pending || ++idle > kIdlePolls)) got = -2;
+    if (got < 0 && (!pending || !s.resident || __builtin_amdgcn_s_memrealtime() - since > kIdleTicks)) got = -2;
     if (lane == 0) {
-      sh.job[0] = got;
-      sh.job[1] = stage;
-      sh.job[2] = idx;
+      sh.c->job[0] = got;
+      sh.c->job[1] = stage;
+      sh.c->job[2] = idx;
     }
   }
   __syncthreads();
 }
 
-// One key of a sweep batch: its position, score, and 1 if it is below the
-// row's end (0 for the clamped loads past it).
-struct SweepKey {
-  int p;
-  float e;
-  uint32_t ok;
-};
-
-// Sweeps keys [0, end) of one stored score row in batches: batch(at, J) gets a
-// thread's J keys of the batch as at(0..J-1).  Where the row is 16-byte
-// aligned: 16-byte loads, kSweepVec per thread per batch, the next batch's
-// loads issued before the current batch is worked through, and the keys past
-// the last whole quad in one more batch (J = 1); otherwise 4-byte loads,
-// kSweepLoads per thread per batch, all in flight at once.  Every thread of
-// the CTA runs every batch (a batch may synchronise the CTA); nothing at or
-// past end is read.
-constexpr int kSweepVec = 8;
-constexpr int kSweepLoads = 32;
-template <class B>
-__device__ __forceinline__ void sweep_row(const float* row, int end, B&& batch) {
-  const int tid = threadIdx.x;
-  if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0u) {
-    const v4f* row4 = reinterpret_cast<const v4f*>(row);
-    const int n4 = end / 4;
-    constexpr int kStep = kSweepVec * kThreads;
-    v4f cur[kSweepVec], nxt[kSweepVec];
-    if (n4 > 0) {
-#pragma unroll
-      for (int u = 0; u < kSweepVec; ++u) cur[u] = row4[min(u * kThreads + tid, n4 - 1)];
-    }
-    #pragma unroll 1
-    for (int c0 = 0; c0 < n4; c0 += kStep) {
-      const bool more = c0 + kStep < n4;
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < kSweepVec; ++u) nxt[u] = row4[min(c0 + kStep + u * kThreads + tid, n4 - 1)];
-      }
-      batch(
-          [&](int j) {
-            const int i = c0 + (j >> 2) * kThreads + tid;
-            return SweepKey{4 * i + (j & 3), cur[j >> 2][j & 3], i < n4 ? 1u : 0u};
-          },
-          std::integral_constant<int, 4 * kSweepVec>{});
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < kSweepVec; ++u) cur[u] = nxt[u];
-      }
-    }
-    if (4 * n4 < end) {
-      const int p = 4 * n4 + tid;
-      const float e = row[min(p, end - 1)];
-      batch([&](int) { return SweepKey{p, e, p < end ? 1u : 0u}; }, std::integral_constant<int, 1>{});
-    }
-    return;
-  }
-  #pragma unroll 1
-  for (int c0 = 0; c0 < end; c0 += kSweepLoads * kThreads) {
-    float v[kSweepLoads];
-#pragma unroll
-    for (int u = 0; u < kSweepLoads; ++u) v[u] = row[min(c0 + u * kThreads + tid, end - 1)];
-    batch(
-        [&](int j) {
-          const int p = c0 + j * kThreads + tid;
-          return SweepKey{p, v[j], p < end ? 1u : 0u};
-        },
-        std::integral_constant<int, kSweepLoads>{});
-  }
-}
-
-// Appends a sweep batch's keys of class 1 and 2 (cls(score) -> 0, 1 or 2) in
-// whole-CTA order: each thread counts its keys of both classes (packed in one
-// word, class 2 in the high half: a batch holds fewer than 2^16 keys), one
-// CTA-wide exclusive scan of the counts places each thread's keys after the
-// running totals sh.pos[0..1], and each thread passes its keys, in order, to
-// put(class, position, key, score) (with kEvery, every key is passed, class 0
-// included, and put writes without a branch: on a lone wave per SIMD each
-// branch per key costs more than the key's arithmetic).  cls must not branch
-// either.  Two barriers a batch; the loads already issued for the next batch
-// complete before the stores.
-template <int NT, int J, bool kEvery = false, class At, class Cls, class Put>
-__device__ __forceinline__ void append_batch(At&& at, Cls&& cls, Put&& put, CtaShared<NT>& sh) {
-  static_assert(J * kThreads < 65536, "class counts of a batch fit 16 bits");
-  const int w = wave_id();
-  const int lane = lane_id();
-  uint32_t cnt = 0u;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const SweepKey k = at(j);
-    const int c = cls(k.e) & -static_cast<int>(k.ok);
-    cnt += (c == 1 ? 1u : 0u) + (c == 2 ? 0x10000u : 0u);
-  }
-  uint32_t incl = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) sh.wtot[w] = incl;
-  __syncthreads();
-  uint32_t below = 0u, tot = 0u;
-#pragma unroll
-  for (int q = 0; q < kWaves; ++q) {
-    if (q < w) below += sh.wtot[q];
-    tot += sh.wtot[q];
-  }
-  const int p1 = sh.pos[0], p2 = sh.pos[1];
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    sh.pos[0] = p1 + static_cast<int>(tot & 0xffffu);
-    sh.pos[1] = p2 + static_cast<int>(tot >> 16);
-  }
-  const uint32_t excl = below + incl - cnt;
-  int r1 = p1 + static_cast<int>(excl & 0xffffu), r2 = p2 + static_cast<int>(excl >> 16);
-  // one wait for every load in flight (the next batch's included): the
-  // compiler would otherwise wait for some before each predicated store
-  wait_vm_done();
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const SweepKey k = at(j);
-    const int c = cls(k.e) & -static_cast<int>(k.ok);
-    if constexpr (kEvery) {
-      put(c, c == 1 ? r1 : r2, k.p, k.e);  // every key, no branch (put ignores class 0)
-    } else {
-      if (c == 1) put(1, r1, k.p, k.e);
-      if (c == 2) put(2, r2, k.p, k.e);
-    }
-    r1 += c == 1 ? 1 : 0;
-    r2 += c == 2 ? 1 : 0;
-  }
-}
-
-// radix_key's mapping in straight-line vector integer operations (the
-// compiler would turn the C form back into compares, which serialise on one
-// condition register): the key of a positive score, or of a negative one,
-// picked by the sign mask, then cleared for a NaN.
-__device__ __forceinline__ uint32_t radix_key_alu(float x) {
-  uint32_t key, mag, t0, t1;
-  asm("v_and_b32 %[mag], 0x7fffffff, %[u]\n\t"
-      "v_ashrrev_i32 %[t0], 31, %[u]\n\t"
-      "v_sub_u32 %[t1], 0x80000000, %[mag]\n\t"
-      "v_or_b32 %[key], 0x80000000, %[mag]\n\t"
-      "v_bfi_b32 %[key], %[t0], %[t1], %[key]\n\t"
-      "v_sub_u32 %[t1], 0x7f800000, %[mag]\n\t"
-      "v_ashrrev_i32 %[t1], 31, %[t1]\n\t"
-      "v_bfi_b32 %[key], %[t1], 0, %[key]"
-      : [key] "=&v"(key), [mag] "=&v"(mag), [t0] "=&v"(t0), [t1] "=&v"(t1)
-      : [u] "v"(__float_as_uint(x)));
-  return key;
-}
-
-// 1 if x == 0, else 0, without a compare.
-__device__ __forceinline__ uint32_t is_zero_alu(uint32_t x) {
-  uint32_t r;
-  asm("v_min_u32 %0, 1, %1\n\t"
-      "v_sub_u32 %0, 1, %0"
-      : "=&v"(r)
-      : "v"(x));
-  return r;
-}
-
-// Repair of row r by this CTA alone, from its stored scores row[0, end): the
-// exact k-th largest key (1 <= k <= end) by LDS radix histogram sweeps (11, 11
-// and 10 bits from the top).  As soon as the digit holding it holds at most
-// kFinalizeLds keys, one collect sweep keeps the digit's keys in LDS, where a
-// radix select finds the exact key, and the keys above the digit as
-// candidates (in LDS too when k <= kAboveLds), stored against that key;
-// after the third histogram the row is selected again at the exact score
-// instead.  Then the row's counters, threshold, ranges and Top-k.  No other
-// CTA takes part, so no repair state is shared.
-template <int NT>
-__device__ __forceinline__ void local_repair_row(const SelectArgs& s, const float* row, int r, int end, int k,
-                                                 CtaShared<NT>& sh) {
-  const int tid = threadIdx.x;
-  uint32_t* hist = sh.u.fin.hist;
-  int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
-  // the candidates above the final digit and the digit's keys: (key index,
-  // score bits), each with one spare entry per lane that takes the writes of
-  // the keys of other classes (only the finish kernel over stored scores has
-  // these areas)
-  __shared__ int2 above[kAboveLds + 64];
-  __shared__ int2 digit_keys[kFinalizeLds + 64];
-  uint32_t pf = 0u, krem = static_cast<uint32_t>(k);
-  int known = 0;
-  float t2 = 0.f;
-  for (int pass = 0;; ++pass) {
-    const int shift = pass_shift(pass);
-    const int bits = pass_bits(pass);
-    const uint32_t low = (1u << bits) - 1u;
-    #pragma unroll 1
-    for (int i = tid; i < kRadixBins; i += kThreads) hist[i] = 0u;
-    __syncthreads();
-    // every key adds to its digit's bin, 1 if it has the known prefix, else 0
-    // (no branch per key, so that the keys' instructions interleave)
-    const int above_shift = pass == 0 ? 31 : shift + bits;
-    const uint32_t want = pass == 0 ? 0u : pf;
-    const uint32_t keep_mask = pass == 0 ? 0u : ~0u;
-    sweep_row(row, end, [&](auto at, auto nj) {
-#pragma unroll
-      for (int j = 0; j < decltype(nj)::value; ++j) {
-        const SweepKey k = at(j);
-        const uint32_t key = radix_key_alu(k.e);
-        const uint32_t in = k.ok & is_zero_alu(((key >> above_shift) ^ want) & keep_mask);
-        atomicAdd(&hist[(key >> shift) & low], in);
-      }
-    });
-    __syncthreads();
-    uint32_t d, rem;
-    cta_find_digit(hist, 1 << bits, krem, sh, d, rem);
-    const uint32_t in_digit = hist[d];
-    pf = pass == 0 ? d : ((pf << bits) | d);
-    krem = rem;
-    known += bits;
-    if (tid == 0) {
-      sh.pos[0] = 0;
-      sh.pos[1] = 0;
-    }
-    __syncthreads();
-    if (known == 32) {
-      // every bit known: select again at the exact score
-      t2 = key_to_float(pf);
-      sweep_row(row, end, [&](auto at, auto nj) {
-        append_batch<NT, decltype(nj)::value>(
-            at, [&](float e) { return e > t2 ? 1 : (!(e < t2) ? 2 : 0); },
-            [&](int c, int i, int p, float e) {
-              if (c == 1 && i < s.capacity) store_pair(slots + 2 * (s.top_k + i), p, enc_cand(e, t2));
-              if (c == 2 && i < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - i), p, e - t2);
-            },
-            sh);
-      });
-      break;
-    }
-    if (in_digit <= static_cast<uint32_t>(kFinalizeLds)) {
-      // collect: the digit's keys go to LDS, keys above it become candidates:
-      // kept in LDS too while k <= kAboveLds (stored once the exact score is
-      // known), else stored with their raw scores and re-encoded afterwards
-      const uint32_t top_pf = pf;
-      const int drop = 32 - known;
-      const bool above_lds = k <= kAboveLds;
-      auto put = [&](int c, int i, int p, float e) {
-        if (c == 1 && above_lds) above[i] = make_int2(p, __float_as_int(e));
-        if (c == 1 && !above_lds && i < s.capacity) store_pair(slots + 2 * (s.top_k + i), p, e);
-        if (c == 2 && i < kFinalizeLds) digit_keys[i] = make_int2(p, __float_as_int(e));
-      };
-      // both classes to LDS, written by every lane for every key (a key of
-      // another class, or past an area's end, to the lane's spare entry)
-      const int lane = lane_id();
-      auto put_every = [&](int c, int i, int p, float e) {
-        const int2 v = make_int2(p, __float_as_int(e));
-        above[c == 1 && i < kAboveLds ? i : kAboveLds + lane] = v;
-        digit_keys[c == 2 && i < kFinalizeLds ? i : kFinalizeLds + lane] = v;
-      };
-      // The digit's keys are [lo, hi) = [top_pf, top_pf + 1) << drop.  Where lo
-      // is the key of a number (not of the NaN-only low keys), the classes
-      // follow from two float compares: key(e) >= K exactly when e >= the
-      // float of key K (a NaN float for hi past the largest number's key
-      // leaves class 1 empty, as it is).
-      const uint64_t lo = static_cast<uint64_t>(top_pf) << drop;
-      if (lo >= 0x00800000u) {
-        const float lb = key_to_float(static_cast<uint32_t>(lo));
-        const uint64_t hi = lo + (uint64_t{1} << drop);
-        const float ub = hi > 0xffffffffu ? __uint_as_float(0x7fc00000u) : key_to_float(static_cast<uint32_t>(hi));
-        // class 1 above the digit, 2 inside it: 2 (e >= lb) - (e >= ub), no branch
-        auto cls = [&](float e) { return 2 * static_cast<int>(e >= lb) - static_cast<int>(e >= ub); };
-        if (above_lds) {
-          sweep_row(row, end, [&](auto at, auto nj) { append_batch<NT, decltype(nj)::value, true>(at, cls, put_every, sh); });
-        } else {
-          sweep_row(row, end, [&](auto at, auto nj) { append_batch<NT, decltype(nj)::value>(at, cls, put, sh); });
-        }
-      } else {
-        sweep_row(row, end, [&](auto at, auto nj) {
-          append_batch<NT, decltype(nj)::value>(
-              at,
-              [&](float e) {
-                const uint32_t top = radix_key_alu(e) >> drop;
-                return top > top_pf ? 1 : (top == top_pf ? 2 : 0);
-              },
-              put, sh);
-        });
-      }
-      __syncthreads();
-      const int nabove = sh.pos[0];
-      const int nin = min(sh.pos[1], kFinalizeLds);
-      __syncthreads();
-      auto key_of = [&](int i) { return radix_key(__int_as_float(digit_keys[i].y)); };
-      cta_radix_select(key_of, nin, static_cast<int>(krem), hist, sh);  // resets sh.pos
-      const uint32_t kstar = sh.pfx[0];
-      t2 = key_to_float(kstar);
-      #pragma unroll 1
-      for (int i = tid; i < nin; i += kThreads) {
-        const uint32_t key = key_of(i);
-        const int2 v = digit_keys[i];
-        const float e = __int_as_float(v.y);
-        if (key > kstar) {
-          const int c = nabove + atomicAdd(&sh.pos[0], 1);
-          if (c < s.capacity) store_pair(slots + 2 * (s.top_k + c), v.x, enc_cand(e, t2));
-        } else if (key == kstar) {
-          const int c = atomicAdd(&sh.pos[1], 1);
-          if (c < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - c), v.x, e - t2);
-        }
-      }
-      // the candidates above the digit, encoded against the exact score: from
-      // LDS, or the raw ones read back from L2 once this CTA's stores complete
-      const int nkeep = min(nabove, s.capacity);
-      if (above_lds) {
-        #pragma unroll 1
-        for (int i = tid; i < nkeep; i += kThreads) {
-          const int2 v = above[i];
-          store_pair(slots + 2 * (s.top_k + i), v.x, enc_cand(__int_as_float(v.y), t2));
-        }
-      } else {
-        wait_vm_done();
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        #pragma unroll 1
-        for (int i = tid; i < nkeep; i += kThreads) {
-          const int2 v = *reinterpret_cast<const int2*>(slots + 2 * (s.top_k + i));
-          store_pair(slots + 2 * (s.top_k + i), v.x, enc_cand(__int_as_float(v.y), t2));
-        }
-      }
-      // every wave's digit-key appends above are done before the count moves
-      // (a late wave's atomicAdd on sh.pos[0] would otherwise race with it)
-      __syncthreads();
-      if (tid == 0) sh.pos[0] += nabove;
-      break;
-    }
-  }
-  // the slot stores complete (and this CTA's view of the slots is refreshed)
-  // before the Top-k reads them back
-  wait_vm_done();
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int nc = sh.pos[0], nt = sh.pos[1];
-  __syncthreads();
-  if (tid == 0) {
-    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, static_cast<uint32_t>(nc));
-    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(nt));
-    st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
-  }
-  row_outputs<NT>(s, r, k, nc, nt, t2, 0, sh);
-}
-
-// The finish kernel's CTA body: phase A over this CTA's rows, then repair
-// items until nothing is left.
+// After its own keys (and its tile's fit test, if it was the last): repair
+// items until nothing is left, then the CTA leaves; the last to leave clears
+// the header, the done flags and the job list for the next call.
 template <int NT, bool kFused, class Args>
-__device__ __forceinline__ void finish_body(const Args& a, const SelectArgs& s, CtaShared<NT>& sh, v4i* lds) {
-  const Ws ws{s.ws, a.batch, s.rows};
+__device__ __forceinline__ void work_loop(const Args& a, const SelectArgs& s, char* lds) {
+  using Lay = Layout<NT, kFused>;
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid == 0) {
-    // the layout this call's state words use (read by the next select kernel)
-    st_wt(ws.hdr() + kHdrBatch, static_cast<uint32_t>(a.batch));
-    st_wt(ws.hdr() + kHdrNextN, static_cast<uint32_t>(NT));
-    st_wt(ws.hdr() + kHdrMagic, kLayoutMagic);
-  }
-  bool saw_repair = false;
-  for (int r = blockIdx.x; r < s.rows; r += gridDim.x) {
-    const int b = r / NT, t = r - b * NT;
-    // the row's first candidate pairs (all of them when it has at most top_k +
-    // kFewExtra) are loaded together with the fit test's inputs
-    const int npre = s.topk_idx ? min(min(s.capacity, s.top_k + kFewExtra), kPreCap) : 0;
-    int2 pre[kPreUnits];
-    // every CTA working on a row of tile b finds the same mask; the one with
-    // its lowest row publishes the job
-    const uint32_t mask = tile_fit<NT>(s, a.seq_lens + static_cast<int64_t>(b) * a.sl_stride, b, sh, r, npre, pre);
-    const int L = sh.len;
-    int end[NT];
-#pragma unroll
-    for (int u = 0; u < NT; ++u) end[u] = max(0, L - NT + u + 1);
-    const int k = min(end[t], s.top_k);
-    // Stored scores of requests up to kLocalRepairKeys keys: each CTA repairs
-    // its own rows (the same decision for every row of a tile); longer ones,
-    // and the re-scoring repair, run as jobs.
-    const bool local = !kFused && L <= kLocalRepairKeys;
-    saw_repair = saw_repair || (mask != 0u && !local);
-    // The row is through phase A once its fit is decided (and its job, if it
-    // publishes one, listed): the CTAs waiting for repair items leave as soon
-    // as every row is, while the fitting rows' outputs are still being written.
-    if (!(mask & (1u << t))) {
-      // (wave 0 has no pair load in flight: its count returns after one round trip)
-      if (tid == 0) flag_if_last(ws, count_row(ws));
-      row_outputs_pre<NT>(s, r, k, sh.nc[t], sh.nt[t], sh.thr[t], npre, pre, sh);
-    } else if (local) {
-      // counted first: the CTAs waiting for jobs need not wait for the repair
-      if (tid == 0) flag_if_last(ws, count_row(ws));
-      if constexpr (!kFused) {
-        if (k > 0) local_repair_row<NT>(s, a.logits + static_cast<int64_t>(r) * a.ld, r, end[t], k, sh);
-        else row_outputs<NT>(s, r, k, 0, 0, sh.thr[t], 0, sh);
-      }
-    } else {
-      if ((mask & ((1u << t) - 1u)) == 0u) publish_job<NT>(s, ws, b, end, mask);
-      if (tid == 0) {
-        wait_vm_done();  // the job's list entry first
-        flag_if_last(ws, count_row(ws));
-      }
-    }
-    __syncthreads();
-  }
-  // With at least as many CTAs without rows as with, those are the repair's
-  // hands: a CTA whose rows all fit (or were repaired here) leaves without
-  // polling for items.
-  if (!saw_repair && blockIdx.x < s.rows && 2 * static_cast<int64_t>(s.rows) <= gridDim.x) return;
-  int idle = 0;
+  uint64_t since = __builtin_amdgcn_s_memrealtime();
+  int polls = 0;
   while (true) {
-    claim_item<NT, kFused>(a, ws, idle, sh);
-    const int b = sh.job[0];
-    const int stage = sh.job[1];
-    const int idx = sh.job[2];
+    // the LDS views and the workspace rebuilt from opaque bases in every
+    // round, so that no address derived from them is hoisted out of the loop
+    // (the compiler would keep hundreds of them live across the items, and
+    // spill them)
+    char* base = lds;
+    asm volatile("" : "+v"(base));
+    uint32_t* wsb = s.ws;
+    asm volatile("" : "+s"(wsb));
+    const Ws ws{wsb, a.batch, s.rows};
+    const Sh<NT> sh = make_sh<NT>(base, Lay::kFinCap, Lay::kCtlOff);
+    const RescoreLds<NT> rl{reinterpret_cast<v4i*>(base), reinterpret_cast<QLds<NT>*>(base + Lay::kStageBytes),
+                            reinterpret_cast<uint32_t*>(base + Lay::kListOff)};
+    claim_item<NT, kFused>(a, s, ws, since, sh);
+    const int b = sh.c->job[0];
+    const int stage = sh.c->job[1];
+    const int idx = sh.c->job[2];
     __syncthreads();
     if (b == -2) break;
     if (b < 0) {
       // back off (up to about half a microsecond between polls), so that
       // waiting CTAs keep their loads off the job words the working ones update
-      for (int i = 0; i < min(idle, 4); ++i) __builtin_amdgcn_s_sleep(4);
+      ++polls;
+      for (int i = 0; i < min(polls, 4); ++i) __builtin_amdgcn_s_sleep(4);
       continue;
     }
-    idle = 0;
+    polls = 0;
     const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
-    run_item<NT, kFused>(a, s, ws, b, L, stage, idx, sh, lds);
+    run_item<NT, kFused>(a, s, ws, b, L, stage, idx, sh, rl);
     __syncthreads();
+    since = __builtin_amdgcn_s_memrealtime();
+  }
+  const Ws ws{s.ws, a.batch, s.rows};
+  if (tid == 0) {
+    const uint32_t old = atomicAdd(ws.hdr() + 2, 1u);
+    if (old + 1u == gridDim.x) {
+      // every other CTA has left: nothing reads the header any more
+      const int njobs = min(static_cast<int>(ld_ag64(ws.progress()) >> 32), ws.batch);
+      for (int j = 0; j < njobs; ++j) st_wt(ws.list(j), 0u);
+      for (int i = 0; i < kDoneFlags; ++i) st_wt(ws.flag(i), 0u);
+      st_wt64(ws.progress(), 0ull);
+      st_wt(ws.hdr() + 2, 0u);
+    }
   }
 }
 
-// Run by every CTA of the select kernel after its keys (so before any finish
-// kernel of this call): the finish stage's header, done flags and job list
-// start empty.  Between calls the workspace holds
-// only zeros in its state words (every job clears its own) -- except where a
-// call laid it out differently: the fused repair's score buffer starts right
-// after the state words, so another batch size or next_n puts state words
-// where an earlier call kept scores.  The header records the layout the last
-// finish kernel used (written by that kernel, so every CTA here reads the same
-// value); when this call's layout differs, all CTAs clear its state words.
-template <int NT>
-__device__ __forceinline__ void prepare_workspace(const SelectArgs& s, int batch) {
-  const Ws ws{s.ws, batch, s.rows};
-  const bool same = s.ws[kHdrMagic] == kLayoutMagic && s.ws[kHdrBatch] == static_cast<uint32_t>(batch) &&
-                    s.ws[kHdrNextN] == static_cast<uint32_t>(NT);
+// The tile's last CTA: arrivals[b] back to zero, the fit test, and then the
+// rows: finished here (one row, no sweep), or a job listed (the first row item
+// kept for this CTA when no sweep comes first); then the tile is counted.
+template <int NT, bool kFused, class Args>
+__device__ __forceinline__ void tile_finish(const Args& a, const SelectArgs& s, int b, int L, const Sh<NT>& sh,
+                                            const RescoreLds<NT>& rl) {
+  const Ws ws{s.ws, a.batch, s.rows};
   const int tid = threadIdx.x;
-  if (!same) {
-    const int64_t n = workspace_state_words(batch, s.rows) - 16;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + tid; i < n;
-         i += static_cast<int64_t>(gridDim.x) * kThreads)
-      s.ws[16 + i] = 0u;
-  } else if (blockIdx.x == 0) {
-    // the done flags and the job list (the claim words a late claim attempt
-    // incremented sit where this call's jobs are, and each publish rewrites
-    // its job's)
-    for (int i = tid; i < kDoneFlags; i += kThreads) *ws.flag(i) = 0u;
-    for (int i = tid; i < job_list_words(batch); i += kThreads) *ws.list(i) = 0u;
+  if (tid == 0) st_wt(reinterpret_cast<uint32_t*>(s.arrivals) + b, 0u);
+  tile_fit<NT>(s, b, L, sh);
+  const uint32_t sweep = sh.c->repair_mask;
+  const uint32_t stored = sh.c->stored_mask;
+  int end[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) end[t] = max(0, L - NT + t + 1);
+  if (NT == 1 && sweep == 0u) {
+    if (tid == 0) count_tile(ws);
+    const int k = min(end[0], s.top_k);
+    if (stored) stored_resolve<NT>(s, ws, b, k, sh);
+    else fit_row_outputs<NT>(s, b, k, sh);
+    return;
   }
-  if (blockIdx.x == 0 && tid < 3) s.ws[tid] = 0u;
+  const bool self0 = sweep == 0u;
+  publish_job<NT>(s, ws, b, end, sweep, stored, self0 ? kStageRows : kStageHist0, self0);
+  if (tid == 0) count_tile(ws);
+  __syncthreads();
+  if (self0) run_item<NT, kFused>(a, s, ws, b, L, kStageRows, 0, sh, rl);
 }
+
+
 
 // ---------------------------------------------------------------- work items
 
@@ -2360,19 +2187,24 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Calls seg(b, L, k0, k1, ctas) for the request b this CTA works on, with
-// [k0, k1) the keys of b it handles and ctas the number of CTAs that handle b
-// (the arrivals b's tile waits for).  Uniform across the CTA.
-template <class F>
-__device__ __forceinline__ void for_each_segment(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
-                                                 int per_request, int keys_per_cta, bool empty_group, F&& seg) {
+// The request b this CTA works on, [k0, k1) the keys of b it handles and ctas
+// the number of CTAs that handle b (the arrivals b's tile waits for); ok is
+// false for a CTA without work.  Uniform across the CTA.
+struct Segment {
+  int b, L, k0, k1, ctas;
+  bool ok;
+};
+
+__device__ __forceinline__ Segment find_segment(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
+                                                int per_request, int keys_per_cta, bool empty_group) {
+  Segment sg{0, 0, 0, 0, 0, false};
   if (!locate) {
     const int b = blockIdx.x / per_request;
     const int c = blockIdx.x % per_request;
     const int L = seq_lens[static_cast<int64_t>(b) * sl_stride];
     const int n = L > 0 ? static_cast<int>(ceil_div(L, keys_per_cta)) : (empty_group ? 1 : 0);
-    if (c < n) seg(b, L, c * keys_per_cta, min((c + 1) * keys_per_cta, L), n);
-    return;
+    if (c < n) sg = Segment{b, L, c * keys_per_cta, min((c + 1) * keys_per_cta, L), n, true};
+    return sg;
   }
   const int lane = lane_id();
   if (batch <= 64) {
@@ -2400,9 +2232,9 @@ __device__ __forceinline__ void for_each_segment(const int32_t* seq_lens, int64_
       const int p = static_cast<int>(i - uniform64(__shfl(a0, l)));
       const int k0 = static_cast<int>(static_cast<int64_t>(p) * gg / n) * kGroupKeys;
       const int k1 = min(static_cast<int>(static_cast<int64_t>(p + 1) * gg / n) * kGroupKeys, LL);
-      seg(bb, LL, k0, max(k0, k1), n);
+      sg = Segment{bb, LL, k0, max(k0, k1), n, true};
     }
-    return;
+    return sg;
   }
   int64_t N = 0;  // groups in all
   for (int b0 = 0; b0 < batch; b0 += 64) {
@@ -2438,11 +2270,20 @@ __device__ __forceinline__ void for_each_segment(const int32_t* seq_lens, int64_
       const int p = static_cast<int>(i - uniform64(__shfl(a0, l)));
       const int k0 = static_cast<int>(static_cast<int64_t>(p) * gg / n) * kGroupKeys;
       const int k1 = min(static_cast<int>(static_cast<int64_t>(p + 1) * gg / n) * kGroupKeys, LL);
-      seg(bb, LL, k0, max(k0, k1), n);
-      return;
+      return Segment{bb, LL, k0, max(k0, k1), n, true};
     }
     before += uniform64(__shfl(incl, 63));
   }
+  return sg;
+}
+
+// Calls seg(b, L, k0, k1, ctas) for this CTA's segment, if it has one (one
+// call site, so the body is inlined once).
+template <class F>
+__device__ __forceinline__ void for_each_segment(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
+                                                 int per_request, int keys_per_cta, bool empty_group, F&& seg) {
+  const Segment sg = find_segment(seq_lens, sl_stride, batch, locate, per_request, keys_per_cta, empty_group);
+  if (sg.ok) seg(sg.b, sg.L, sg.k0, sg.k1, sg.ctas);
 }
 
 // ---------------------------------------------------------------- kernels
@@ -2484,38 +2325,56 @@ logits_kernel(PagedArgs a, float* out, int64_t ld) {
   }
 }
 
-// A wave's n candidate pairs of row r into slots top_k + base + i (those past
-// the capacity dropped).  With a Top-k output, candidate j < top_k also writes
-// its index to topk_idx[r][j]: a row that ends with exactly k candidates then
-// already holds its Top-k in slot order, which the finish kernel keeps; in
-// every other case the finish kernel rewrites entries 0 .. top_k - 1.
+// A wave's n candidate pairs of row r into slots top_k + base + i, those past
+// the capacity into the workspace's overflow area (while it has room; without
+// a workspace they are dropped), all with agent-scope write-through stores
+// (the tile's last CTA, on any XCD, reads them).  With a Top-k output,
+// candidate j < top_k also writes its key index to topk_idx[r][j]: a row that
+// ends with exactly k candidates then already holds its Top-k in slot order;
+// every other row's finish rewrites entries 0 .. top_k - 1.
 __device__ __forceinline__ void store_cands(const SelectArgs& s, int r, int base, const int2* list, int n) {
   int32_t* slots = s.candidates + (static_cast<int64_t>(r) * (s.top_k + s.capacity) + s.top_k) * 2;
+  int32_t* ovf = s.ovf ? s.ovf + 2 * static_cast<int64_t>(kOverflowPairs) * r : nullptr;
   int32_t* out = s.topk_idx ? s.topk_idx + static_cast<int64_t>(r) * s.top_k : nullptr;
   for (int i = lane_id(); i < n; i += 64) {
     const int j = base + i;
     const int2 e = list[i];
-    if (j < s.capacity) *reinterpret_cast<int2*>(slots + 2 * j) = e;
-    if (out && j < s.top_k) out[j] = e.x;
+    if (j < s.capacity) store_pair(slots + 2 * j, e.x, __int_as_float(e.y));
+    else if (ovf && j - s.capacity < kOverflowPairs) store_pair(ovf + 2 * (j - s.capacity), e.x, __int_as_float(e.y));
+    if (out && j < s.top_k) st_wt(reinterpret_cast<uint32_t*>(out + j), static_cast<uint32_t>(e.x));
   }
 }
 
-// The select kernels' CTA body: score keys [k0, k1) of the CTA's request and
-// select each wave's 64-key groups straight from the scores in registers onto
-// the wave's own lists, which reach the slots when nearly full (one counter
-// atomic per list) and at the end (one atomic per row and class for the whole
-// CTA, after the only barrier).  Whatever follows -- fit test,
-// repair, ranges, Top-k -- is the finish kernel's.
-template <int NT, int kKeysPerCta, class Src, class Args>
-__device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, MainShared<NT>& sh, v4i* stage,
-                                            QLds<NT>* ql) {
+// A wave's n tie pairs of row r into slots top_k - 1 - base - i (those past
+// top_k dropped), written through.
+__device__ __forceinline__ void store_ties(const SelectArgs& s, int r, int base, const int2* list, int n) {
+  int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
+  for (int i = lane_id(); i < n; i += 64)
+    if (base + i < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - base - i), list[i].x, __int_as_float(list[i].y));
+}
+
+// The select launch's CTA body: score keys [k0, k1) of the CTA's request (or
+// read them from a logits matrix) and select each wave's 64-key groups straight
+// from the scores in registers onto the wave's own lists, which reach the slots
+// when nearly full (one counter atomic per list) and at the end (one atomic
+// per row and class for the whole CTA).  With arrivals, the CTA then arrives
+// on its tile, the tile's last CTA runs the fit test and the rows' finish, and
+// every CTA runs repair items until none is left.
+template <int NT, bool kFused, int kKeysPerCta, class Src, class Args>
+__device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, char* lds) {
+  using Lay = Layout<NT, kFused>;
+  MainShared<NT>& ms = *reinterpret_cast<MainShared<NT>*>(lds + Lay::kListOff);
+  v4i* stage = reinterpret_cast<v4i*>(lds);
+  QLds<NT>* ql = reinterpret_cast<QLds<NT>*>(lds + Lay::kStageBytes);
+  const Sh<NT> sh = make_sh<NT>(lds, Lay::kFinCap, Lay::kCtlOff);
+  const RescoreLds<NT> rl{stage, ql, reinterpret_cast<uint32_t*>(lds + Lay::kListOff)};
   Src src;
   src.bind(stage);
   src.bind_q(ql);
   const int lane = lane_id();
   const int w = wave_id();
   for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kKeysPerCta, true,
-                   [&](int b, int L, int k0, int k1, int) {
+                   [&](int b, int L, int k0, int k1, int nctas) {
     float thr[NT];
     int lim[NT];
     int ncl[NT], ntl[NT];  // entries in this wave's lists (wave-uniform)
@@ -2526,18 +2385,16 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
       ncl[t] = 0;
       ntl[t] = 0;
     }
-    // A wave's list of row t into the row's slots: one atomic per class for
-    // the base, then the pairs at base + i (dropped past the slots).
+    // A wave's list of row t into the row's slots: one atomic on the row's
+    // counter pair for both bases, then the pairs at base + i.
     auto flush = [&](int t) {
       const int r = b * NT + t;
-      int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
       uint64_t old = 0;
       if (lane == 0) old = reserve_pair(s.counters + 2 * r, ncl[t], ntl[t]);
       const int bc = __shfl(static_cast<int>(static_cast<uint32_t>(old)), 0);
       const int bt = __shfl(static_cast<int>(static_cast<uint32_t>(old >> 32)), 0);
-      store_cands(s, r, bc, sh.cand[w][t], ncl[t]);
-      for (int i = lane; i < ntl[t]; i += 64)
-        if (bt + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - bt - i)) = sh.tie[w][t][i];
+      store_cands(s, r, bc, ms.cand[w][t], ncl[t]);
+      store_ties(s, r, bt, ms.tie[w][t], ntl[t]);
       ncl[t] = 0;
       ntl[t] = 0;
     };
@@ -2548,10 +2405,6 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
           // this group's candidates and ties onto the wave's lists, positions
           // from the ballots
           const int p = p0 + lane;
-          if (s.keep && p < k1) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) s.keep[static_cast<int64_t>(b * NT + t) * s.score_ld + p] = E[t];
-          }
           bool flushed = false;
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
@@ -2567,8 +2420,8 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
               flush(t);
               flushed = true;
             }
-            if (cand) sh.cand[w][t][ncl[t] + lanes_below(mc)] = int2{p, __float_as_int(enc_cand(e, thr[t]))};
-            if (tie) sh.tie[w][t][ntl[t] + lanes_below(mt)] = int2{p, __float_as_int(e - thr[t])};
+            if (cand) ms.cand[w][t][ncl[t] + lanes_below(mc)] = int2{p, __float_as_int(enc_cand(e, thr[t]))};
+            if (tie) ms.tie[w][t][ntl[t] + lanes_below(mt)] = int2{p, __float_as_int(e - thr[t])};
             ncl[t] += nc;
             ntl[t] += nt;
           }
@@ -2583,8 +2436,8 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
     if (lane == 0) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        sh.count[w][t][0] = ncl[t];
-        sh.count[w][t][1] = ntl[t];
+        ms.count[w][t][0] = ncl[t];
+        ms.count[w][t][1] = ntl[t];
       }
     }
     __syncthreads();
@@ -2593,67 +2446,66 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
       int tc = 0, tt = 0;
 #pragma unroll
       for (int q = 0; q < kWaves; ++q) {
-        tc += sh.count[q][t][0];
-        tt += sh.count[q][t][1];
+        tc += ms.count[q][t][0];
+        tt += ms.count[q][t][1];
       }
       const uint64_t old = (tc | tt) ? reserve_pair(s.counters + 2 * (b * NT + t), tc, tt) : 0;
-      sh.base[t][0] = static_cast<int>(static_cast<uint32_t>(old));
-      sh.base[t][1] = static_cast<int>(static_cast<uint32_t>(old >> 32));
+      ms.base[t][0] = static_cast<int>(static_cast<uint32_t>(old));
+      ms.base[t][1] = static_cast<int>(static_cast<uint32_t>(old >> 32));
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      int bc = sh.base[t][0], bt = sh.base[t][1];
+      int bc = ms.base[t][0], bt = ms.base[t][1];
       for (int q = 0; q < w; ++q) {
-        bc += sh.count[q][t][0];
-        bt += sh.count[q][t][1];
+        bc += ms.count[q][t][0];
+        bt += ms.count[q][t][1];
       }
-      int32_t* slots = s.candidates + static_cast<int64_t>(b * NT + t) * (s.top_k + s.capacity) * 2;
-      store_cands(s, b * NT + t, bc, sh.cand[w][t], ncl[t]);
-      for (int i = lane; i < ntl[t]; i += 64)
-        if (bt + i < s.top_k) *reinterpret_cast<int2*>(slots + 2 * (s.top_k - 1 - bt - i)) = sh.tie[w][t][i];
+      const int r = b * NT + t;
+      store_cands(s, r, bc, ms.cand[w][t], ncl[t]);
+      store_ties(s, r, bt, ms.tie[w][t], ntl[t]);
+    }
+    if (!s.ws) return;
+    // arrival: this CTA's stores and counts are complete (written through)
+    // before its count on the tile; the CTA that completes the count is last
+    wait_vm_done();
+    __syncthreads();
+    if (threadIdx.x == 0) sh.c->is_last = atomicAdd(s.arrivals + b, 1) + 1 == nctas;
+    __syncthreads();
+    if (sh.c->is_last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      tile_finish<NT, kFused>(a, s, b, L, sh, rl);
     }
   });
-  // (last: its layout check is a load the CTA's start would otherwise wait
-  // for before it reads the lengths; the finish kernel starts after this one)
-  if (s.ws) prepare_workspace<NT>(s, a.batch);
-}
-
-
-template <int NT>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
-fused_kernel(PagedArgs a, SelectArgs s) {
-  __shared__ MainShared<NT> sh;
-  __shared__ v4i stage[kWaves * kStageInt4];
-  if constexpr (NT >= 3) {
-    __shared__ QLds<NT> ql;
-    select_body<NT, kFusedKeysPerCta, KvSourceQ<NT>>(a, s, sh, stage, &ql);
-  } else {
-    select_body<NT, kFusedKeysPerCta, KvSource<NT>>(a, s, sh, stage, nullptr);
+  if (s.ws) {
+    __syncthreads();
+    work_loop<NT, kFused>(a, s, lds);
   }
 }
 
 template <int NT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
+fused_kernel(PagedArgs a, SelectArgs s) {
+  using Lay = Layout<NT, true>;
+  __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
+  if constexpr (NT >= 3)
+    select_body<NT, true, kFusedKeysPerCta, KvSourceQ<NT>>(a, s, lds);
+  else
+    select_body<NT, true, kFusedKeysPerCta, KvSource<NT>>(a, s, lds);
+}
+
+template <int NT>
 __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectArgs s) {
-  __shared__ MainShared<NT> sh;
-  select_body<NT, kSelectKeysPerCta, LogitsSource<NT>>(a, s, sh, nullptr, nullptr);
+  using Lay = Layout<NT, false>;
+  __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
+  select_body<NT, false, kSelectKeysPerCta, LogitsSource<NT>>(a, s, lds);
 }
 
-// For next_n = 1 two CTAs fit on a compute unit (by LDS and, capped here, by
-// registers).
-template <int NT>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1, 8)))
-fused_finish_kernel(PagedArgs a, SelectArgs s) {
-  __shared__ CtaShared<NT> sh;
-  __shared__ v4i stage[kWaves * kStageInt4];
-  finish_body<NT, true>(a, s, sh, stage);
-}
-
-template <int NT>
-__global__ void __launch_bounds__(kThreads) select_finish_kernel(LogitsArgs a, SelectArgs s) {
-  __shared__ CtaShared<NT> sh;
-  finish_body<NT, false>(a, s, sh, nullptr);
-}
+// LDS of the fused launches: 2 CTAs per compute unit for next_n >= 2, 3 for next_n = 1.
+static_assert(3 * Layout<1, true>::kBytes <= 160 * 1024, "three next_n = 1 CTAs per compute unit");
+static_assert(2 * Layout<2, true>::kBytes <= 160 * 1024, "two next_n = 2 CTAs per compute unit");
+static_assert(2 * Layout<3, true>::kBytes <= 160 * 1024, "two next_n = 3 CTAs per compute unit");
+static_assert(2 * Layout<4, true>::kBytes <= 160 * 1024, "two next_n = 4 CTAs per compute unit");
 
 // ---------------------------------------------------------------- host side
 
@@ -2768,7 +2620,7 @@ int resident_ctas(const void* fn) {
 
 SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int32_t top_k, int32_t* arr,
                        int32_t* ranges, int32_t* topk, int32_t batch, int32_t rows, int32_t max_context, bool fused,
-                       void* workspace, size_t workspace_bytes) {
+                       void* workspace) {
   SelectArgs s;
   s.thresholds = thr;
   s.counters = cnt;
@@ -2777,41 +2629,44 @@ SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int
   s.ranges = ranges;
   s.topk_idx = topk;
   s.ws = arr ? static_cast<uint32_t*>(workspace) : nullptr;
-  s.ws_words = s.ws ? static_cast<int64_t>(workspace_bytes / 4) : 0;
-  s.scores = s.ws && fused ? reinterpret_cast<float*>(s.ws + workspace_state_words(batch, rows)) : nullptr;
+  const WsLayout lay = workspace_layout(batch, rows, max_context, fused);
+  s.ovf = s.ws ? reinterpret_cast<int32_t*>(s.ws + lay.overflow) : nullptr;
+  s.scores = s.ws && fused ? reinterpret_cast<float*>(s.ws + lay.scores) : nullptr;
   s.score_ld = score_stride(max_context);
-  s.keep = nullptr;
   s.capacity = cap;
   s.top_k = top_k;
   s.rows = rows;
+  s.resident = 0;
   return s;
 }
 
 pmqa_status launched() { return hipGetLastError() == hipSuccess ? PMQA_OK : PMQA_ERR_LAUNCH; }
 
-
-// One launch of K<nt> with scoring arguments `a` first.  A main kernel runs the
-// located grid -- as many CTAs as fit on the device at once, but at most 15/8
-// per compute unit -- when that is at least twice the batch, else
-// a.per_request CTAs per request (PMQA_ERR_SHAPE if that grid is too large); a
-// finish kernel always runs as many CTAs as fit.  (The cap: on the 64-request
-// decode batch 480 CTAs stream 2.7 us faster than the 768 that fit, whose
-// third CTA on each compute unit gets its first keys some 15 us after the
-// first and finishes last; 432 and fewer are slower again.)
+// One launch of K<nt>.  The located grid -- as many CTAs as fit on the device
+// at once, but at most 15/8 per compute unit -- runs when that is at least
+// twice the batch, else a.per_request CTAs per request (PMQA_ERR_SHAPE if that
+// grid is too large).  (The cap: on the 64-request decode batch 480 CTAs
+// stream 2.7 us faster than the 768 that fit, whose third CTA on each compute
+// unit gets its first keys some 15 us after the first and finishes last; 432
+// and fewer are slower again.)  A select launch learns whether all of its CTAs
+// fit on the device at once (only then do CTAs without work wait for repair
+// items).
 template <template <int> class K, class A, class... Rest>
-pmqa_status launch_k(int nt, bool main, hipStream_t st, A a, Rest... rest) {
+pmqa_status launch_k(int nt, hipStream_t st, A a, Rest... rest) {
   pmqa_status status = PMQA_OK;
   auto go = [&](auto fn) {
-    int64_t g = resident_ctas(reinterpret_cast<const void*>(fn));
-    if (main) {
-      g = std::min<int64_t>(g, static_cast<int64_t>(device_cus()) * 15 / 8);
-      a.locate = g >= 2 * static_cast<int64_t>(a.batch);
-      if (!a.locate) g = static_cast<int64_t>(a.per_request) * a.batch;
-      if (g > 0x7fffffff) {
-        status = PMQA_ERR_SHAPE;
-        return;
-      }
+    const int64_t fit = resident_ctas(reinterpret_cast<const void*>(fn));
+    int64_t g = std::min<int64_t>(fit, static_cast<int64_t>(device_cus()) * 15 / 8);
+    a.locate = g >= 2 * static_cast<int64_t>(a.batch);
+    if (!a.locate) g = static_cast<int64_t>(a.per_request) * a.batch;
+    if (g > 0x7fffffff) {
+      status = PMQA_ERR_SHAPE;
+      return;
     }
+    auto mark = [&](auto& x) {
+      if constexpr (std::is_same<std::decay_t<decltype(x)>, SelectArgs>::value) x.resident = g <= fit ? 1 : 0;
+    };
+    (mark(rest), ...);
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st, a, rest...);
   };
   switch (nt) {
@@ -2826,8 +2681,6 @@ pmqa_status launch_k(int nt, bool main, hipStream_t st, A a, Rest... rest) {
 template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT>; };
 template <int NT> struct FusedK { static constexpr auto fn = fused_kernel<NT>; };
 template <int NT> struct SelectK { static constexpr auto fn = select_kernel<NT>; };
-template <int NT> struct FusedFinishK { static constexpr auto fn = fused_finish_kernel<NT>; };
-template <int NT> struct SelectFinishK { static constexpr auto fn = select_finish_kernel<NT>; };
 
 }  // namespace
 }  // namespace pmqa
@@ -2856,7 +2709,7 @@ pmqa_status pmqa_mqa_logits(const uint8_t* q, const uint8_t* kv_fused, const flo
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
-  st = launch_k<LogitsK>(next_n, true, hs, a, out, out_stride);
+  st = launch_k<LogitsK>(next_n, hs, a, out, out_stride);
   return st != PMQA_OK ? st : launched();
 }
 
@@ -2879,10 +2732,8 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
   if (st != PMQA_OK) return st;
   const LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, 0, static_cast<int32_t>(gx)};
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                                   batch_size, static_cast<int32_t>(rows), max_context, false, workspace,
-                                   workspace_bytes);
-  st = launch_k<SelectK>(next_n, true, hs, a, s);
-  if (st == PMQA_OK && s.ws) st = launch_k<SelectFinishK>(next_n, false, hs, a, s);
+                                   batch_size, static_cast<int32_t>(rows), max_context, false, workspace);
+  st = launch_k<SelectK>(next_n, hs, a, s);
   return st != PMQA_OK ? st : launched();
 }
 
@@ -2910,28 +2761,9 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
-  SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
-                             batch_size, static_cast<int32_t>(rows), max_context, true, workspace, workspace_bytes);
-  // With next_n >= 2 the main pass also writes every score into the
-  // workspace's score buffer (4 * next_n bytes a key against 132 read), and
-  // the finish stage is the one of a select over a logits matrix, run on that
-  // buffer: a repair then reads 4-byte scores instead of scoring its requests
-  // again from the KV pages (next_n = 1 keeps the re-scoring repair: there
-  // the writes would cost more than the rare repair saves).
-  const bool keep = s.ws && next_n >= 2;
-  if (keep) s.keep = s.scores;
-  st = launch_k<FusedK>(next_n, true, hs, a, s);
-  if (st == PMQA_OK && s.ws) {
-    if (keep) {
-      const LogitsArgs la{s.scores, s.score_ld, seq_lens, seq_lens_stride, batch_size, 0, 1};
-      SelectArgs sf = s;
-      sf.scores = nullptr;
-      sf.keep = nullptr;
-      st = launch_k<SelectFinishK>(next_n, false, hs, la, sf);
-    } else {
-      st = launch_k<FusedFinishK>(next_n, false, hs, a, s);
-    }
-  }
+  const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
+                                   batch_size, static_cast<int32_t>(rows), max_context, true, workspace);
+  st = launch_k<FusedK>(next_n, hs, a, s);
   return st != PMQA_OK ? st : launched();
 }
 

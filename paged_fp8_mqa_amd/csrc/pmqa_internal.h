@@ -14,11 +14,14 @@ constexpr int kLogitsKeysPerCta = 1024;
 constexpr int kFusedKeysPerCta = 1024;
 constexpr int kSelectKeysPerCta = 4096;
 constexpr int kOutColumnGranule = 256;  // padded_seq_len rounding
-constexpr int kRadixBins = 2048;        // 11-bit radix digits: 11 + 11 + 10
-constexpr int kHistCopies = 8;          // repair workspace: copies of a row's radix histogram
+constexpr int kRadixBins = 2048;        // radix digits: 10 + 11 + 11 bits from the top
+constexpr int kHistCopies = 4;          // repair workspace: copies of a row's radix histogram
 constexpr int kFinalizeLds = 4096;      // keys a CTA keeps in LDS for a final radix select
+constexpr int kBucketPairs = 4096;      // repair workspace: a row's bucket of keys at the k-th digit
+constexpr int kOverflowPairs = 8192;    // repair workspace: a row's candidates past its capacity
 constexpr int kJobWords = 16;           // repair workspace: words per tile job
 constexpr int kRowWords = 16;           // repair workspace: words per row state
+constexpr int kHdrWords = 64;           // repair workspace: header words
 constexpr int kDoneFlags = 64;          // repair workspace: copies of the end-of-phase-A flag
 constexpr int kDoneFlagStride = 64;     // repair workspace: words between two copies (256 bytes)
 constexpr int kRescoreItemKeys = 2048;  // keys per repair item recomputed from the KV pages
@@ -32,20 +35,32 @@ constexpr int64_t job_list_words(int64_t batch) { return (batch + 15) / 16 * 16;
 // Floats per row of the fused repair's score buffer (256-byte rows).
 constexpr int64_t score_stride(int64_t max_context) { return ceil_div(max_context, 64) * 64; }
 
-// Repair workspace: a header, kDoneFlags copies of a flag, the job list, one
-// job per tile, and per row its state, kHistCopies copies of a radix histogram
-// and a bucket buffer of (index, score) pairs; this much is the finish stage's
-// state (in words).
-constexpr int64_t workspace_state_words(int64_t batch, int64_t rows) {
-  return 16 + kDoneFlags * kDoneFlagStride + job_list_words(batch) + kJobWords * batch +
-         (kRowWords + kHistCopies * kRadixBins + 2 * kFinalizeLds) * rows;
+// Workspace of the select entry points, in 32-bit words and in this order: a
+// header and the copies of the phase-A flag (zero between calls: the last CTA
+// of each call to leave clears them), the job list, one job per tile, then per
+// row -- each kind in an array of its own -- the state words, kHistCopies
+// radix histograms, the bucket of keys at the k-th digit and the candidates
+// past the capacity (kOverflowPairs pairs); the fused select adds a score row
+// of score_stride(max_context) floats per row, written only for rows whose
+// repair sweeps their keys again.
+struct WsLayout {
+  int64_t hdr, list, jobs, row_state, hist, bucket, overflow, scores, end;
+};
+constexpr WsLayout workspace_layout(int64_t batch, int64_t rows, int64_t max_context, bool fused) {
+  WsLayout l{};
+  l.hdr = 0;
+  l.list = kHdrWords + kDoneFlags * kDoneFlagStride;
+  l.jobs = l.list + job_list_words(batch);
+  l.row_state = l.jobs + kJobWords * batch;
+  l.hist = l.row_state + kRowWords * rows;
+  l.bucket = l.hist + static_cast<int64_t>(kHistCopies) * kRadixBins * rows;
+  l.overflow = l.bucket + 2 * static_cast<int64_t>(kBucketPairs) * rows;
+  l.scores = l.overflow + 2 * static_cast<int64_t>(kOverflowPairs) * rows;
+  l.end = l.scores + (fused ? rows * score_stride(max_context) : 0);
+  return l;
 }
-
-// The whole workspace in words: the fused select's repair adds a score buffer
-// of score_stride(max_context) floats per row (the scores of a repaired row,
-// computed once from the KV pages and read back by the later passes).
 constexpr int64_t workspace_words(int64_t batch, int64_t rows, int64_t max_context, bool fused) {
-  return workspace_state_words(batch, rows) + (fused ? rows * score_stride(max_context) : 0);
+  return workspace_layout(batch, rows, max_context, fused).end;
 }
 
 }  // namespace pmqa
