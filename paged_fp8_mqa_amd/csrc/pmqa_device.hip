@@ -46,13 +46,6 @@ constexpr int kStageInt4 = 512;  // a wave's KV staging area: 64 keys x 128 byte
 // next_n >= 3, whose q operands take LDS instead).
 template <int NT> constexpr int kWaveCand = NT >= 3 ? 64 : 256;
 template <int NT> constexpr int kWaveTie = NT >= 3 ? 32 : 64;
-constexpr int kFewExtra = 3;   // final select by value walk when at most this many keys are left out
-// Phase A: the candidate pairs of a row that waves 1-3 preload (pair
-// u * kPreThreads + tid - 64 in unit u of thread tid >= 64); wave 0 loads the
-// fit test's words and counts the row, with no pair load ahead of its atomic.
-constexpr int kPreUnits = 16;
-constexpr int kPreThreads = kThreads - 64;
-constexpr int kPreCap = kPreUnits * kPreThreads;
 
 struct PagedArgs {
   const uint8_t* q;
@@ -89,6 +82,8 @@ struct SelectArgs {
   int32_t* topk_idx;
   uint32_t* ws;         // workspace (with arrivals), else null
   int32_t* ovf;         // its overflow pairs, row r at ovf + r * 2 * kOverflowPairs (null without)
+  int32_t* nearp;       // its near-band pairs, row r at nearp + r * 2 * kNearPairs (null without)
+  uint32_t* nearc;      // row r's near-band count at nearc[r * kRowWords] (a row state word)
   float* scores;        // fused repair: the workspace's score rows, row r at scores + r * score_ld
   int64_t score_ld;
   int32_t capacity;
@@ -111,6 +106,29 @@ extern "C" __device__ uint64_t __ockl_wfred_min_u64(uint64_t);
 
 // s_waitcnt vmcnt(0): this wave's loads and stores have completed.
 __device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Optional event trace (built only with PMQA_TRACE defined; the product build
+// compiles every trace point to nothing): thread 0 of each of the first
+// kTraceCtas CTAs records up to kTraceSlots events (kind, two small
+// arguments, s_memrealtime) at g_trace[cta * kTraceSlots + i], read back with
+// pmqa_trace_read.
+#ifdef PMQA_TRACE
+constexpr int kTraceCtas = 2048;
+constexpr int kTraceSlots = 64;
+__device__ uint64_t g_trace[kTraceCtas * kTraceSlots];
+__device__ __forceinline__ void trace_event(int* n, int kind, int x, int y) {
+  if (threadIdx.x == 0 && blockIdx.x < kTraceCtas && *n < kTraceSlots) {
+    const uint64_t t = __builtin_amdgcn_s_memrealtime();
+    g_trace[blockIdx.x * kTraceSlots + *n] = (static_cast<uint64_t>(kind & 0xff) << 56) |
+                                            (static_cast<uint64_t>(x & 0xffff) << 40) |
+                                            (static_cast<uint64_t>(y & 0xff) << 32) | (t & 0xffffffffu);
+    ++*n;
+  }
+}
+#define PMQA_TR(sh, kind, x, y) trace_event(&(sh).c->trace_n, (kind), (x), (y))
+#else
+#define PMQA_TR(sh, kind, x, y) ((void)0)
+#endif
 
 // Words shared between the CTAs of one kernel (on any XCD) are written with
 // agent-scope atomic stores, which the storing XCD's L2 writes through, and
@@ -281,6 +299,18 @@ struct KvSource : KvStream {
         qa[t][mt] = load32(a.q + ((row * kHeads + 16 * mt + n) * kDim + 32 * g));
         wt[t][mt] = *reinterpret_cast<const float4*>(a.w + row * kHeads + 16 * mt + 4 * g);
       }
+    }
+  }
+
+  // One row's operands (NT == 1): absolute row r = b * next_n + t of q and the
+  // weights, with the stream of request b (the repair's scoring of one row).
+  __device__ __forceinline__ void init_row(const PagedArgs& a, int b, int64_t r) {
+    static_assert(NT == 1, "one row");
+    init_stream(a, b);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      qa[0][mt] = load32(a.q + ((r * kHeads + 16 * mt + n) * kDim + 32 * g));
+      wt[0][mt] = *reinterpret_cast<const float4*>(a.w + r * kHeads + 16 * mt + 4 * g);
     }
   }
 
@@ -567,6 +597,14 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : (0x80000000u | (0x80000000u - k)));
 }
 
+// The lower end of a threshold's near band: kNearBand radix keys below it
+// (about 2^-8 of its magnitude), at least -inf; a NaN threshold has none.
+__device__ __forceinline__ float near_floor(float t) {
+  const uint32_t k = radix_key(t);
+  if (k == 0u) return t;
+  return key_to_float(k > 0x00800000u + kNearBand ? k - kNearBand : 0x00800000u);
+}
+
 // Adds nc candidates and nt ties to a row's (candidate, tie) counter pair with
 // one 64-bit atomic (the pair is 8-byte aligned) and returns the old pair, the
 // first slot of each class.  The low word never carries into the high one:
@@ -600,6 +638,7 @@ struct Ctl {
   int32_t cnt[NT][2];
   int32_t nc[NT];
   int32_t nt[NT];
+  int32_t nn[NT];
   float thr[NT];
   uint32_t repair_mask;
   uint32_t stored_mask;
@@ -608,9 +647,7 @@ struct Ctl {
   int32_t pos[2];
   int32_t job[3];      // claimed repair item: tile (or -1: none open, -2: leave), stage, index
   int32_t next_stage;
-  // few_extra_topk: each wave's smallest (key, position) pair per round;
-  // few_extra_from_regs: each wave's smallest packed keys
-  uint64_t low[kFewExtra][kWaves];
+  int32_t trace_n;  // events recorded by this CTA (trace builds only)
 };
 
 // The finish work's view of a CTA's LDS: per-row radix histograms (rh, NT of
@@ -652,8 +689,8 @@ template <int NT>
 struct MainShared {
   int2 cand[kWaves][NT][kWaveCand<NT>];
   int2 tie[kWaves][NT][kWaveTie<NT>];
-  int32_t count[kWaves][NT][2];  // the waves' list lengths at the end
-  int32_t base[NT][2];           // the CTA's slot bases per row and class
+  int32_t count[kWaves][NT][3];  // the waves' candidates, ties and near-band keys at the end
+  int32_t base[NT][3];           // the CTA's bases per row and class
 };
 
 // LDS of a select launch, one buffer seen three ways: the main pass (KV
@@ -789,6 +826,7 @@ template <int NT, class KeyOf>
 __device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, uint32_t* hist, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   uint32_t pf = 0u, krem = static_cast<uint32_t>(k);
+#pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass_shift(pass);
     const int bits = pass_bits(pass);
@@ -796,10 +834,33 @@ __device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, u
     for (int i = tid; i < kRadixBins; i += kThreads) hist[i] = 0u;
     __syncthreads();
     #pragma unroll 1
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t key = key_of(i);
-      if (pass > 0 && (key >> (shift + bits)) != pf) continue;
-      atomicAdd(&hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
+    for (int i0 = 0; i0 < n; i0 += 4 * kThreads) {
+      // four keys a thread per round, their LDS reads in flight together (the
+      // loop bound is uniform, so that the wave's ballots see every lane)
+      uint32_t key[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        key[u] = i < n ? key_of(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        const bool in = i < n && (pass == 0 || (key[u] >> (shift + bits)) == pf);
+        const uint32_t bin = (key[u] >> shift) & ((1u << bits) - 1u);
+        // lanes in the bin of the wave's first counted lane add once, together
+        // (thousands of equal scores would otherwise serialise on one LDS word)
+        const uint64_t act = __ballot(in);
+        if (act) {
+          const uint32_t lead = __builtin_amdgcn_readlane(bin, __ffsll(static_cast<long long>(act)) - 1);
+          const uint64_t same = __ballot(in && bin == lead);
+          if (in && bin == lead) {
+            if (lanes_below(same) == 0) atomicAdd(&hist[lead], static_cast<uint32_t>(__popcll(same)));
+          } else if (in) {
+            atomicAdd(&hist[bin], 1u);
+          }
+        }
+      }
     }
     __syncthreads();
     uint32_t d, rem;
@@ -846,216 +907,130 @@ __device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, co
   b = bb + ib - b;
 }
 
-// Top-k of a row whose nc candidates exceed k by d = nc - k <= kFewExtra (the
-// pairs of the slots below npre already in sh.fi / sh.fk): the
-// d smallest candidates (by radix key, ties by slot position) are left out
-// and every other candidate's index is written in slot order.  Each of the d
-// rounds finds the smallest pair not yet left out: a tree over each thread's
-// keys, the wavefront minimum (DPP), and the four waves' minima exchanged
-// through LDS with one barrier; the output then shifts each index past the
-// left-out positions before it, so the stores stay coalesced.
-template <int NT>
-__device__ __forceinline__ void few_extra_topk(const int32_t* cand, int32_t* out, int nc, int d, float th, int npre,
-                                               const Sh<NT>& sh) {
+// ---------------------------------------------------------------- row finish
+
+// A row's final select works on n (key index, score bits) pairs: pair_of(i)
+// returns pair i (from LDS -- sh.fi, sh.fk -- or from where they lie).
+// Loads pairs [0, n) -- the first n1 from `a`, the rest from `b` -- into LDS,
+// the score bits passed through dec(bits); sixteen loads a thread in flight.
+template <int NT, class Dec>
+__device__ __forceinline__ void load_pairs(const int32_t* a, int n1, const int32_t* b, int n, Dec&& dec,
+                                           const Sh<NT>& sh) {
   const int tid = threadIdx.x;
-  constexpr int kPer = kFinalizeLds / kThreads;
-  uint32_t* key = sh.fk;
-  int32_t* idx = sh.fi;
-  if (npre < nc) {
-    // the pairs not in LDS yet, all of a thread's loads in flight
-    int2 v[kPer];
+#pragma unroll 1
+  for (int i0 = 0; i0 < n; i0 += 16 * kThreads) {
+    int2 v[16];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kThreads + tid;
-      if (i >= npre && i < nc) v[u] = *reinterpret_cast<const int2*>(cand + 2 * i);
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      if (i < n) v[u] = *reinterpret_cast<const int2*>(i < n1 ? a + 2 * i : b + 2 * (i - n1));
     }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kThreads + tid;
-      if (i >= npre && i < nc) {
-        idx[i] = v[u].x;
-        key[i] = static_cast<uint32_t>(v[u].y);
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      if (i < n) {
+        sh.fi[i] = v[u].x;
+        sh.fk[i] = dec(static_cast<uint32_t>(v[u].y));
       }
     }
-  }
-  __syncthreads();
-  // (LDS reads at clamped indices, unconditional, so that they are all in
-  // flight at once instead of one branch and wait each; the nu steps a row
-  // needs, out of kPer)
-  const int nu = static_cast<int>(ceil_div(nc, kThreads));
-  uint32_t kv[kPer] = {};
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    if (u >= nu) break;
-    kv[u] = key[min(u * kThreads + tid, nc - 1)];
-  }
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    if (u >= nu) break;
-    kv[u] = radix_key(dec_cand(__uint_as_float(kv[u]), th));
-  }
-  uint32_t p0 = 0xffffffffu, p1 = 0xffffffffu, p2 = 0xffffffffu;
-#pragma unroll 1
-  for (int j = 0; j < d; ++j) {
-    // this thread's smallest pair still in, by a tree over its keys
-    uint64_t m[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const uint32_t i = static_cast<uint32_t>(u * kThreads + tid);
-      m[u] = (u < nu && i < static_cast<uint32_t>(nc) && i != p0 && i != p1 && i != p2)
-                 ? ((static_cast<uint64_t>(kv[u]) << 32) | i)
-                 : ~0ull;
-    }
-#pragma unroll
-    for (int w = kPer / 2; w > 0; w >>= 1)
-#pragma unroll
-      for (int u = 0; u < w; ++u) m[u] = min(m[u], m[u + w]);
-    const uint64_t wm = __ockl_wfred_min_u64(m[0]);
-    if (lane_id() == 0) sh.c->low[j][wave_id()] = wm;
-    __syncthreads();
-    uint64_t g = sh.c->low[j][0];
-#pragma unroll
-    for (int q = 1; q < kWaves; ++q) g = min(g, sh.c->low[j][q]);
-    const uint32_t pj = static_cast<uint32_t>(g);
-    if (j == 0) p0 = pj;
-    else if (j == 1) p1 = pj;
-    else p2 = pj;
-  }
-  int32_t iv[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    if (u >= nu) break;
-    iv[u] = idx[min(u * kThreads + tid, nc - 1)];
-  }
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    if (u >= nu) break;
-    const uint32_t i = static_cast<uint32_t>(u * kThreads + tid);
-    if (i < static_cast<uint32_t>(nc) && i != p0 && i != p1 && i != p2)
-      out[i - (i > p0) - (i > p1) - (i > p2)] = iv[u];
   }
   __syncthreads();
 }
 
-// Exact Top-k of one fitting row from its slots: every candidate when there are
-// at most k, topped up with ties from the tie slots; otherwise the k largest
-// candidates by decoded score -- all but the few smallest when at most
-// kFewExtra are left out, else by a 3-pass radix select over keys kept in LDS
-// (read from the slots once).  Entries past k are -1.  The first npre
-// candidate pairs may be in sh.fi / sh.fk already.
+// Where a final select's pairs lie: in LDS (sh.fi, sh.fk, already decoded),
+// or in memory at g, their stored values encoded as candidates against th
+// when dec is set.  One descriptor for every caller, so that the select's
+// code exists once.
+struct PairSrc {
+  const int32_t* g;
+  float th;
+  int dec;
+  int lds;
+};
+
 template <int NT>
-__device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k, int nc, float th, int npre,
-                                              const Sh<NT>& sh) {
-  const int tid = threadIdx.x;
-  constexpr int kPer = kFinalizeLds / kThreads;
-  const int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
-  int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
-  for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
-  if (nc <= k) {
-    // every candidate, then ties; all of a thread's loads in flight at once
-    // (the preloaded candidates read from LDS at clamped indices, unconditional)
-    const bool lds = nc <= npre;
-    for (int i0 = 0; i0 < k; i0 += kPer * kThreads) {
-      const int nu = static_cast<int>(ceil_div(min(k - i0, kPer * kThreads), kThreads));
-      int32_t v[kPer];
-      if (lds && nc > 0) {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-          if (u >= nu) break;
-          v[u] = sh.fi[min(i0 + u * kThreads + tid, nc - 1)];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        if (u >= nu) break;
-        const int i = i0 + u * kThreads + tid;
-        if (i < k && (i >= nc || !lds))
-          v[u] = i < nc ? slots[2 * (s.top_k + i)] : slots[2 * (s.top_k - 1 - (i - nc))];
-      }
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        if (u >= nu) break;
-        const int i = i0 + u * kThreads + tid;
-        if (i < k) out[i] = v[u];
-      }
-    }
-    return;
-  }
-  if (nc - k <= kFewExtra && nc <= kFinalizeLds) {
-    few_extra_topk<NT>(slots + 2 * s.top_k, out, nc, nc - k, th, npre, sh);
-    return;
-  }
-  const bool in_lds = nc <= kFinalizeLds;
-  uint32_t* hist = sh.fh;
-  uint32_t* keys = sh.fk;
-  int32_t* idx = sh.fi;
-  const int32_t* cand = slots + 2 * s.top_k;
-  if (in_lds) {
-    // (index, score) pairs into LDS, all of a thread's loads in flight at once
-    constexpr int kPer = kFinalizeLds / kThreads;
-    for (int i0 = 0; i0 < nc; i0 += kPer * kThreads) {
-      int2 v[kPer];
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int i = i0 + u * kThreads + tid;
-        if (i < nc) v[u] = *reinterpret_cast<const int2*>(cand + 2 * i);
-      }
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int i = i0 + u * kThreads + tid;
-        if (i < nc) {
-          keys[i] = radix_key(dec_cand(__int_as_float(v[u].y), th));
-          idx[i] = v[u].x;
-        }
-      }
-    }
-    __syncthreads();
-  }
-  auto key_of = [&](int i) -> uint32_t {
-    return in_lds ? keys[i] : radix_key(dec_cand(__int_as_float(cand[2 * i + 1]), th));
-  };
-  cta_radix_select(key_of, nc, k, hist, sh);
+__device__ __forceinline__ int2 pair_at(const PairSrc& ps, int i, const Sh<NT>& sh) {
+  if (ps.lds) return make_int2(sh.fi[i], static_cast<int>(sh.fk[i]));
+  int2 p = *reinterpret_cast<const int2*>(ps.g + 2 * i);
+  if (ps.dec) p.y = __float_as_int(dec_cand(__int_as_float(p.y), ps.th));
+  return p;
+}
+
+// The k-th largest key k* of n pairs (1 <= k <= n) by an LDS radix select,
+// then each thread's pairs above k* and equal to it (i = tid, tid + kThreads,
+// ...) counted and placed by one CTA-wide exclusive scan: og and oe are the
+// thread's first ranks in each class, n_gt and n_eq the class sizes.  The
+// caller then walks its pairs in the same order, handing out ranks og++ and
+// oe++.
+template <int NT>
+__device__ __forceinline__ uint32_t kth_scan(const PairSrc& ps, int n, int k, const Sh<NT>& sh, uint32_t& og,
+                                             uint32_t& oe, int& n_gt, int& n_eq) {
+  auto key_of = [&](int i) { return radix_key(__int_as_float(pair_at<NT>(ps, i, sh).y)); };
+  cta_radix_select(key_of, n, k, sh.fh, sh);
   const uint32_t kstar = sh.c->pfx[0];
-  const int n_eq = static_cast<int>(sh.c->krem[0]);
-  const int n_gt = k - n_eq;
-  if (in_lds) {
-    // each thread's keys above k* (and equal to it) counted, one CTA-wide
-    // exclusive scan of the counts, then every thread writes at its offsets
-    constexpr int kPer = kFinalizeLds / kThreads;
-    uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kThreads + tid;
-      if (i < nc) {
-        gt += keys[i] > kstar ? 1u : 0u;
-        eq += keys[i] == kstar ? 1u : 0u;
-      }
-    }
-    uint32_t og = gt, oe = eq;
-    cta_exclusive_scan2(og, oe, sh);
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kThreads + tid;
-      if (i < nc) {
-        if (keys[i] > kstar) {
-          out[og++] = idx[i];
-        } else if (keys[i] == kstar) {
-          if (static_cast<int>(oe) < n_eq) out[n_gt + oe] = idx[i];
-          ++oe;
-        }
-      }
-    }
-    __syncthreads();
-    return;
-  }
-  #pragma unroll 1
-  for (int i = tid; i < nc; i += kThreads) {
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll 1
+  for (int i = threadIdx.x; i < n; i += kThreads) {
     const uint32_t key = key_of(i);
-    if (key > kstar) {
-      out[atomicAdd(&sh.c->pos[0], 1)] = cand[2 * i];
-    } else if (key == kstar) {
-      const int e = atomicAdd(&sh.c->pos[1], 1);
-      if (e < n_eq) out[n_gt + e] = cand[2 * i];
+    gt += key > kstar ? 1u : 0u;
+    eq += key == kstar ? 1u : 0u;
+  }
+  og = gt;
+  oe = eq;
+  cta_exclusive_scan2(og, oe, sh);
+  if (threadIdx.x == kThreads - 1) {
+    sh.c->pos[0] = static_cast<int>(og + gt);
+    sh.c->pos[1] = static_cast<int>(oe + eq);
+  }
+  __syncthreads();
+  n_gt = sh.c->pos[0];
+  n_eq = sh.c->pos[1];
+  return kstar;
+}
+
+// Ranges and exact Top-k of a fitting row r (k = min(e_r, top_k)) with nc
+// candidates, nt ties and threshold th: all candidates when there are at most
+// k of them, completed with ties from the tie slots (cands_out: the candidates'
+// indices are in topk_idx already, as the main pass writes candidate j < top_k
+// to entry j), else the k largest candidates by decoded score.  Entries past k
+// are -1.
+template <int NT>
+__device__ __forceinline__ void fit_row_outputs(const SelectArgs& s, int r, int k, int nc, int nt, float th,
+                                                bool cands_out, const Sh<NT>& sh) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s.ranges[r] = s.top_k - min(nt, s.top_k);
+    s.ranges[s.rows + r] = s.top_k + min(nc, s.capacity);
+  }
+  if (s.topk_idx) {
+    const int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
+    const int32_t* cand = slots + 2 * s.top_k;
+    int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
+    for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
+    if (nc <= k) {
+#pragma unroll 1
+      for (int i = (cands_out ? nc : 0) + tid; i < k; i += kThreads)
+        out[i] = i < nc ? cand[2 * i] : slots[2 * (s.top_k - 1 - (i - nc))];
+    } else {
+      // nc <= capacity (the row fits)
+      const bool lds = nc <= sh.fin_cap;
+      if (lds)
+        load_pairs<NT>(cand, nc, cand, nc, [&](uint32_t b) { return __float_as_uint(dec_cand(__uint_as_float(b), th)); },
+                       sh);
+      const PairSrc ps{cand, th, 1, lds ? 1 : 0};
+      auto pair_of = [&](int i) { return pair_at<NT>(ps, i, sh); };
+      PMQA_TR(sh, 19, nc, 0);
+      uint32_t og, oe;
+      int n_gt, n_eq;
+      const uint32_t kstar = kth_scan<NT>(ps, nc, k, sh, og, oe, n_gt, n_eq);
+      PMQA_TR(sh, 20, 0, 0);
+#pragma unroll 1
+      for (int i = tid; i < nc; i += kThreads) {
+        const int2 p = pair_of(i);
+        const uint32_t key = radix_key(__int_as_float(p.y));
+        if (key > kstar) out[og++] = p.x;
+        else if (key == kstar && n_gt + static_cast<int>(oe) < k) out[n_gt + oe++] = p.x;
+      }
     }
   }
   __syncthreads();
@@ -1063,11 +1038,12 @@ __device__ __forceinline__ void finalize_topk(const SelectArgs& s, int r, int k,
 
 // Fit test of tile b (request length L) by the tile's last CTA, from the final
 // counters (every CTA of the tile counted its keys before it arrived): fills
-// sh.c->nc, nt, thr and len, and the masks of the rows that do not fit --
-// stored_mask: rows whose candidates past the capacity all sit in the
-// workspace's overflow area (at most overflow pairs) and in LDS (at most
-// fin_cap), re-selected from those candidates alone; repair_mask: the other
-// rows, whose keys are swept again.
+// sh.c->nc, nt, nn (near-band keys), thr and len, and the masks of the rows
+// that do not fit -- stored_mask: rows whose k-th largest score is among pairs
+// that are all kept (every candidate, in the slots and the overflow area; or,
+// short of k candidates, every candidate, tie and near-band key) and that fit
+// in LDS, re-selected from those pairs alone; repair_mask: the other rows,
+// whose keys are swept again.
 template <int NT>
 __device__ __forceinline__ void tile_fit(const SelectArgs& s, int b, int L, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
@@ -1081,203 +1057,22 @@ __device__ __forceinline__ void tile_fit(const SelectArgs& s, int b, int L, cons
     const int r = b * NT + tid;
     const int nc = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
     const int nt = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
+    const int nn = s.nearc ? static_cast<int>(ld_ag(s.nearc + static_cast<int64_t>(r) * kRowWords)) : 0;
     const float th = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
     const int k = min(max(0, L - NT + tid + 1), s.top_k);
     const bool fit = nc <= s.capacity && nc + min(nt, s.top_k) >= k;
-    const bool stored = nc > s.capacity && nc >= k && nc - s.capacity <= kOverflowPairs && nc <= sh.fin_cap;
+    const bool kept = nc <= s.capacity + kOverflowPairs;
+    const bool stored =
+        kept && (nc >= k ? nc <= sh.fin_cap
+                         : (s.nearp && nt <= s.top_k && nn <= kNearPairs && nc + nt + nn >= k &&
+                            nc + nt + nn <= sh.fin_cap));
     sh.c->nc[tid] = nc;
     sh.c->nt[tid] = nt;
+    sh.c->nn[tid] = nn;
     sh.c->thr[tid] = th;
     if (!fit) atomicOr(stored ? &sh.c->stored_mask : &sh.c->repair_mask, 1u << tid);
   }
   __syncthreads();
-}
-
-// The D smallest of a set of doubles, kept sorted in m[0..D-1]; kFewBig pads.
-constexpr double kFewBig = 1152921504606846976.0;  // 2^60, above every packed key
-template <int D>
-struct Smallest {
-  double m[D];
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int j = 0; j < D; ++j) m[j] = kFewBig;
-  }
-  __device__ __forceinline__ void insert(double x) {
-    if constexpr (D >= 3) m[2] = fmin(m[2], fmax(m[1], x));
-    if constexpr (D >= 2) m[1] = fmin(m[1], fmax(m[0], x));
-    m[0] = fmin(m[0], x);
-  }
-  // The D smallest of the union with another sorted set o: the j-th smallest
-  // of two sorted lists is the least of the maxima of their (i, j - i) prefixes.
-  __device__ __forceinline__ void merge(const Smallest& o) {
-    const double a1 = m[0], a2 = o.m[0];
-    if constexpr (D >= 3) m[2] = fmin(fmin(m[2], o.m[2]), fmin(fmax(a1, o.m[1]), fmax(m[1], a2)));
-    if constexpr (D >= 2) m[1] = fmin(fmax(a1, a2), fmin(m[1], o.m[1]));
-    m[0] = fmin(a1, a2);
-  }
-};
-
-// Lane l's double from the lane the DPP control Ctrl names (kFewBig where it
-// names none, or in a row outside RowMask).
-template <int Ctrl, int RowMask>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(kFewBig));
-  const int lo = __builtin_amdgcn_update_dpp(static_cast<int>(static_cast<uint32_t>(b)),
-                                             static_cast<int>(static_cast<uint32_t>(u)), Ctrl, RowMask, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(static_cast<int>(static_cast<uint32_t>(b >> 32)),
-                                             static_cast<int>(static_cast<uint32_t>(u >> 32)), Ctrl, RowMask, 0xf, false);
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
-                                                     static_cast<uint32_t>(lo)));
-}
-template <int Ctrl, int RowMask, int D>
-__device__ __forceinline__ void dpp_merge(Smallest<D>& x) {
-  Smallest<D> o;
-#pragma unroll
-  for (int j = 0; j < D; ++j) o.m[j] = dpp_f64<Ctrl, RowMask>(x.m[j]);
-  x.merge(o);
-}
-
-// Top-k of a fitting row with D = nc - k in 1 .. kFewExtra extra candidates,
-// all of them in the registers of waves 1-3 (pre[u] is pair u * kPreThreads +
-// tid - 64, nc <= kPreCap): all but the D smallest, by score and then slot
-// position.  Each pair becomes one exact double, order key * 4096 + position
-// (below 2^44).  The stored candidate scores order as the scores do (the
-// encoding maps (t, 2t] onto (0, t] and keeps the rest, with t > 0; ties stay
-// ties) and none is NaN (a NaN never compares above a threshold), so the order
-// key is the stored bits' radix key with -0 taken as +0.  One pass: each
-// thread keeps its D smallest, a DPP reduction leaves the wave's in lane 63,
-// and the four waves' are merged through LDS.  The indices are then written in
-// slot order shifted past the left-out positions, so the stores stay coalesced.
-template <int NT, int D>
-__device__ __forceinline__ void few_extra_from_regs(const SelectArgs& s, int r, int k, int nc,
-                                                    const int2 (&pre)[kPreUnits], const Sh<NT>& sh) {
-  const int tid = threadIdx.x;
-  const int w = wave_id();
-  int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
-  const bool has = tid >= 64;  // a thread of waves 1-3
-  const int pt = tid - 64;
-  const int nu = static_cast<int>(ceil_div(nc, kPreThreads));  // units in use (uniform)
-  Smallest<D> sm;
-  sm.init();
-#pragma unroll
-  for (int u = 0; u < kPreUnits; ++u) {
-    if (u < nu) {
-      const int i = u * kPreThreads + pt;
-      uint32_t b = static_cast<uint32_t>(pre[u].y);
-      b = b == 0x80000000u ? 0u : b;
-      b ^= static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u;
-      if (has && i < nc) sm.insert(__builtin_fma(static_cast<double>(b), 4096.0, static_cast<double>(i)));
-    }
-  }
-  // the wave's D smallest into lane 63
-  dpp_merge<0x111, 0xf>(sm);  // row_shr:1
-  dpp_merge<0x112, 0xf>(sm);  // row_shr:2
-  dpp_merge<0x114, 0xf>(sm);  // row_shr:4
-  dpp_merge<0x118, 0xf>(sm);  // row_shr:8
-  dpp_merge<0x142, 0xa>(sm);  // row_bcast:15
-  dpp_merge<0x143, 0xc>(sm);  // row_bcast:31
-  double* xw = reinterpret_cast<double*>(&sh.c->low[0][0]);  // the waves' sets (8-byte aligned)
-  static_assert(kFewExtra * kWaves >= D * kWaves, "room for every wave's set");
-  if (lane_id() == 63) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) xw[D * w + j] = sm.m[j];
-  }
-  __syncthreads();
-  Smallest<D> all;
-#pragma unroll
-  for (int j = 0; j < D; ++j) all.m[j] = xw[D + j];  // wave 0 holds none
-#pragma unroll
-  for (int q = 2; q < kWaves; ++q) {
-    Smallest<D> o;
-#pragma unroll
-    for (int j = 0; j < D; ++j) o.m[j] = xw[D * q + j];
-    all.merge(o);
-  }
-  uint32_t p[D];  // the left-out slot positions
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const double v = all.m[j];
-    p[j] = static_cast<uint32_t>(v - 4096.0 * floor(v * (1.0 / 4096.0)));
-  }
-  // (positions before the first left-out one already hold their index: the
-  // select kernel wrote candidate j < top_k to entry j)
-#pragma unroll
-  for (int u = 0; u < kPreUnits; ++u) {
-    const int i = u * kPreThreads + pt;
-    if (u < nu && has && i < nc) {
-      const uint32_t iu = static_cast<uint32_t>(i);
-      bool kept = true;
-      uint32_t shift = 0;
-#pragma unroll
-      for (int j = 0; j < D; ++j) {
-        kept = kept && iu != p[j];
-        shift += iu > p[j] ? 1u : 0u;
-      }
-      if (kept && shift) out[i - shift] = pre[u].x;
-    }
-  }
-  for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
-}
-
-// ranges and Top-k finalize of row r (k = min(e_r, top_k)) from its final
-// candidate count nc, tie count nt and threshold th (the first npre candidate
-// pairs possibly loaded already, as finalize_topk takes them).
-template <int NT>
-__device__ __forceinline__ void row_outputs(const SelectArgs& s, int r, int k, int nc, int nt, float th, int npre,
-                                            const Sh<NT>& sh) {
-  if (threadIdx.x == 0) {
-    s.ranges[r] = s.top_k - min(nt, s.top_k);
-    s.ranges[s.rows + r] = s.top_k + min(nc, s.capacity);
-  }
-  if (s.topk_idx) finalize_topk<NT>(s, r, k, nc, th, npre, sh);
-  __syncthreads();
-}
-
-// Phase A's outputs of a fitting row, its first npre candidate pairs loading
-// into the registers of waves 1-3 (pre[u] = pair u * kPreThreads + tid - 64).  A row with exactly k
-// candidates has its Top-k from the select kernel already (entries past k
-// aside) and waits for none of these loads.
-template <int NT>
-__device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int k, int nc, int nt, float th, int npre,
-                                                const int2 (&pre)[kPreUnits], const Sh<NT>& sh) {
-  const bool exact = nc == k;
-  const bool few = nc > k && nc - k <= kFewExtra && nc <= npre;
-  if (!s.topk_idx || exact || few) {
-    if (s.topk_idx && exact) {
-      int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
-      for (int i = k + threadIdx.x; i < s.top_k; i += kThreads) out[i] = -1;
-    } else if (s.topk_idx) {
-      // waves 1-3: their pairs in at once (the compiler would otherwise wait
-      // for all earlier memory operations before each store it predicates);
-      // wave 0 holds no pairs and has no store outstanding here but, in the
-      // CTA with the last count, the done flags'
-      if (threadIdx.x >= 64) wait_vm_done();
-      static_assert(kFewExtra == 3, "one instance per count of extra candidates");
-      if (nc - k == 1) few_extra_from_regs<NT, 1>(s, r, k, nc, pre, sh);
-      else if (nc - k == 2) few_extra_from_regs<NT, 2>(s, r, k, nc, pre, sh);
-      else few_extra_from_regs<NT, 3>(s, r, k, nc, pre, sh);
-    }
-    if (threadIdx.x == 0) {
-      s.ranges[r] = s.top_k - min(nt, s.top_k);
-      s.ranges[s.rows + r] = s.top_k + min(nc, s.capacity);
-    }
-    __syncthreads();
-    return;
-  }
-  // the pairs into LDS, where finalize_topk takes them (one wait for all)
-  const int tid = threadIdx.x;
-  wait_vm_done();
-#pragma unroll
-  for (int u = 0; u < kPreUnits; ++u) {
-    const int i = u * kPreThreads + tid - 64;
-    if (tid >= 64 && i < npre) {
-      sh.fi[i] = pre[u].x;
-      sh.fk[i] = static_cast<uint32_t>(pre[u].y);
-    }
-  }
-  __syncthreads();
-  row_outputs<NT>(s, r, k, nc, nt, th, npre, sh);
 }
 
 // ---------------------------------------------------------------- finish
@@ -1317,33 +1112,27 @@ __device__ __forceinline__ void row_outputs_pre(const SelectArgs& s, int r, int 
 // next) words, word q handing out items q, q + kClaimWords, ...: an item below
 // the stage's item count is the caller's, a larger one claims nothing.
 // Whoever completes a stage's last item runs the stage change.  After its own
-// keys (and its tile's finish, if last) a CTA claims items; with none open it
-// waits, for a bounded time, while some tile has not been through its fit test
-// or a job is before its last stage (only when every CTA of the launch is
-// resident: otherwise waiting CTAs could keep others from starting), and
-// leaves otherwise: each job is carried to its end by the CTAs that complete
-// its stages, so nothing depends on the waiting.  The last CTA to leave clears
-// the header, the flags and the job list for the next call.
+// keys (and its tile's finish, if last) a CTA claims items, scanning every
+// tile's claim words; with none open it waits -- for a bounded time while a
+// job is before its last stage (its next stage opens more items), briefly
+// otherwise (tiles still finishing their keys may publish some) -- and only
+// when every CTA of the launch is resident (otherwise waiting CTAs could keep
+// others from starting); then it leaves.  Each job is carried to its end by
+// the CTAs that complete its stages, so nothing depends on the waiting, and
+// no word outside the jobs is shared, so nothing needs clearing between calls:
+// a finished job's claim words hand out no item.
 constexpr int kClaimWords = 4;  // claim words per repair job
 constexpr int kStageHist0 = 1;
 constexpr int kStageCollect = 4;
 constexpr int kStageSelect = 5;
 constexpr int kStageRows = 6;
-constexpr uint64_t kIdleTicks = 20000;  // s_memrealtime ticks (100 MHz) a CTA waits without an item: 200 us
+constexpr uint64_t kIdleTicks = 20000;  // s_memrealtime ticks (100 MHz) a CTA waits for a pending job: 200 us
+constexpr uint64_t kLingerTicks = 400;  // and without one: 4 us
 static_assert(2 * kClaimWords + 1 + 6 < kJobWords, "a job's claim words, mask and per-stage counts");
 
 struct Ws {
   uint32_t* base;
   int batch, rows;
-  // [0,1] progress: tiles through their fit test (low half) and jobs listed
-  // (high half); [2] CTAs that have left
-  __device__ uint32_t* hdr() const { return base; }
-  __device__ uint64_t* progress() const { return reinterpret_cast<uint64_t*>(base); }
-  // copy i of the done flag: 0 while a tile is before its fit test, then 1 +
-  // the number of jobs listed (the waiting CTAs poll copy blockIdx % kDoneFlags,
-  // 256 bytes apart, so their polls spread over many lines)
-  __device__ uint32_t* flag(int i) const { return base + kHdrWords + kDoneFlagStride * i; }
-  __device__ uint32_t* list(int j) const { return base + kHdrWords + kDoneFlags * kDoneFlagStride + j; }  // tile + 1
   __device__ WsLayout lay() const { return workspace_layout(batch, rows, 0, false); }
   // [2q, 2q + 1] claim word q < kClaimWords, [2 kClaimWords] row masks (the
   // swept rows, and in bits 8.. the rows re-selected from their candidates),
@@ -1352,7 +1141,8 @@ struct Ws {
   __device__ uint64_t* claim(int b, int q) const { return reinterpret_cast<uint64_t*>(job(b) + 2 * q); }
   __device__ uint32_t* mask_word(int b) const { return job(b) + 2 * kClaimWords; }
   __device__ uint32_t* done_word(int b, int stage) const { return job(b) + 2 * kClaimWords + 1 + stage; }
-  // per row: [0] digit prefix [1] rank left [2] bits known [3] bucket count
+  // per row: [0] digit prefix [1] rank left [2] bits known [3] bucket count [4] near-band
+  // keys (counted by the main pass, cleared when the row is finished)
   __device__ uint32_t* row(int r) const { return base + lay().row_state + kRowWords * r; }
   // copy c of row r's radix histogram (items add into copy idx % kHistCopies,
   // which spreads the atomics of a pass over kHistCopies times more lines)
@@ -1382,10 +1172,11 @@ __device__ __forceinline__ int stage_items(int stage, int L) {
   return max(1, static_cast<int>(ceil_div(L, keys)));
 }
 
-// The tile's last CTA lists tile b's job: the swept rows' state words and
-// histograms set up, the row masks, the per-stage counts cleared and the claim
-// words opened at `stage` (with item 0 kept back for the caller when self0),
-// then -- once all of that is complete -- the list entry.
+// The tile's last CTA publishes tile b's job: the swept rows' state words and
+// histograms set up, the row masks and the per-stage counts cleared, and --
+// once all of that is complete -- the claim words opened at `stage` (with item
+// 0 kept back for the caller when self0).  Claimers find the job by its claim
+// words, so no other word changes hands.
 template <int NT>
 __device__ __forceinline__ void publish_job(const SelectArgs& s, const Ws& ws, int b, const int (&end)[NT],
                                             uint32_t sweep, uint32_t stored, int stage, bool self0) {
@@ -1405,95 +1196,66 @@ __device__ __forceinline__ void publish_job(const SelectArgs& s, const Ws& ws, i
   }
   if (tid == 64) st_wt(ws.mask_word(b), sweep | (stored << 8));
   if (tid >= 128 && tid < 128 + kStageRows) st_wt(ws.done_word(b, tid - 127), 0u);
-  if (tid >= 192 && tid < 192 + kClaimWords)
-    st_wt64(ws.claim(b, tid - 192), (static_cast<uint64_t>(stage) << 32) | ((self0 && tid == 192) ? 1u : 0u));
   wait_vm_done();
   __syncthreads();
-  if (tid == 0) {
-    const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.progress()), 1ull << 32);
-    st_wt(ws.list(static_cast<int>(old >> 32)), static_cast<uint32_t>(b + 1));
-    wait_vm_done();  // the list entry before the tile is counted
-  }
+  if (tid < kClaimWords)
+    st_wt64(ws.claim(b, tid), (static_cast<uint64_t>(stage) << 32) | ((self0 && tid == 0) ? 1u : 0u));
 }
 
-// Thread 0: tile b through its fit test (after its job, if any, is listed);
-// the count that completes the batch sets every copy of the done flag to 1 +
-// the jobs listed (final by then: each tile lists its job before it counts).
-__device__ __forceinline__ void count_tile(const Ws& ws) {
-  const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.progress()), 1ull);
-  if (static_cast<uint32_t>(old) + 1u == static_cast<uint32_t>(ws.batch)) {
-    const uint32_t v = static_cast<uint32_t>(old >> 32) + 1u;
-    for (int i = 0; i < kDoneFlags; ++i) st_wt(ws.flag(i), v);
-  }
-}
-
-// Stages 4 and 5 on one whole item of scores held in registers (v[t][u] is row
-// t's score of key c0 + 64*(w + 4u) + lane, for the rows in mask): every key
-// below min(cend, end[t]) is classified by cls(t, score) -> 0 (none), 1 or 2;
-// each wave counts its keys of both classes with ballots, one thread per row
-// reserves the CTA's slots with one atomic per class (add1(t, n), add2(t, n)
-// return the first), and the keys go to put(t, class, position, key, score).
+// Stages 4 and 5 on one row of one item, its scores in registers (v[u] is the
+// score of key c0 + 64*(w + 4u) + lane): every key below lim is classified by
+// cls(score) -> 0 (none), 1 or 2; each wave counts its keys of both classes
+// with ballots, thread 0 reserves the CTA's positions with one atomic per
+// class (add1(n), add2(n) return the first), and the keys go to put(class,
+// position, key, score).
 template <int NT, int kU, class Cls, class Add1, class Add2, class Put>
-__device__ __forceinline__ void append_item(int c0, int cend, const int (&end)[NT], uint32_t mask,
-                                            const float (&v)[NT][kU], const Sh<NT>& sh, Cls&& cls, Add1&& add1,
-                                            Add2&& add2, Put&& put) {
+__device__ __forceinline__ void append_row(int c0, int lim, const float (&v)[kU], const Sh<NT>& sh, Cls&& cls,
+                                           Add1&& add1, Add2&& add2, Put&& put) {
   const int w = wave_id();
   const int lane = lane_id();
-  const int tid = threadIdx.x;
+  int n1 = 0, n2 = 0;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (!(mask & (1u << t))) continue;
-    const int lim = min(cend, end[t]);
-    int n1 = 0, n2 = 0;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
-      const int c = p < lim ? cls(t, v[t][u]) : 0;
-      n1 += __popcll(__ballot(c == 1));
-      n2 += __popcll(__ballot(c == 2));
-    }
-    if (lane == 0) {
-      sh.c->wcnt[t][w][0] = n1;
-      sh.c->wcnt[t][w][1] = n2;
-    }
+  for (int u = 0; u < kU; ++u) {
+    const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
+    const int c = p < lim ? cls(v[u]) : 0;
+    n1 += __popcll(__ballot(c == 1));
+    n2 += __popcll(__ballot(c == 2));
+  }
+  if (lane == 0) {
+    sh.c->wcnt[0][w][0] = n1;
+    sh.c->wcnt[0][w][1] = n2;
   }
   __syncthreads();
-  if (tid < NT && (mask & (1u << tid))) {
+  if (threadIdx.x == 0) {
     int tot[2] = {0, 0};
-#pragma unroll
     for (int q = 0; q < kWaves; ++q) {
-      tot[0] += sh.c->wcnt[tid][q][0];
-      tot[1] += sh.c->wcnt[tid][q][1];
+      tot[0] += sh.c->wcnt[0][q][0];
+      tot[1] += sh.c->wcnt[0][q][1];
     }
     int base[2];
-    base[0] = tot[0] ? add1(tid, tot[0]) : 0;
-    base[1] = tot[1] ? add2(tid, tot[1]) : 0;
-#pragma unroll
+    base[0] = tot[0] ? add1(tot[0]) : 0;
+    base[1] = tot[1] ? add2(tot[1]) : 0;
     for (int q = 0; q < kWaves; ++q) {
-      sh.c->wbase[tid][q][0] = base[0];
-      sh.c->wbase[tid][q][1] = base[1];
-      base[0] += sh.c->wcnt[tid][q][0];
-      base[1] += sh.c->wcnt[tid][q][1];
+      sh.c->wbase[0][q][0] = base[0];
+      sh.c->wbase[0][q][1] = base[1];
+      base[0] += sh.c->wcnt[0][q][0];
+      base[1] += sh.c->wcnt[0][q][1];
     }
   }
   __syncthreads();
+  int r1 = sh.c->wbase[0][w][0], r2 = sh.c->wbase[0][w][1];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (!(mask & (1u << t))) continue;
-    const int lim = min(cend, end[t]);
-    int r1 = sh.c->wbase[t][w][0], r2 = sh.c->wbase[t][w][1];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
-      const int c = p < lim ? cls(t, v[t][u]) : 0;
-      const uint64_t m1 = __ballot(c == 1);
-      const uint64_t m2 = __ballot(c == 2);
-      if (c == 1) put(t, 1, r1 + lanes_below(m1), p, v[t][u]);
-      if (c == 2) put(t, 2, r2 + lanes_below(m2), p, v[t][u]);
-      r1 += __popcll(m1);
-      r2 += __popcll(m2);
-    }
+  for (int u = 0; u < kU; ++u) {
+    const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
+    const int c = p < lim ? cls(v[u]) : 0;
+    const uint64_t m1 = __ballot(c == 1);
+    const uint64_t m2 = __ballot(c == 2);
+    if (c == 1) put(1, r1 + lanes_below(m1), p, v[u]);
+    if (c == 2) put(2, r2 + lanes_below(m2), p, v[u]);
+    r1 += __popcll(m1);
+    r2 += __popcll(m2);
   }
+  __syncthreads();
 }
 
 // Stage change after histogram pass `pass` of tile b's job (run by the CTA that
@@ -1573,86 +1335,54 @@ __device__ __forceinline__ void job_next_stage(const SelectArgs& s, const Ws& ws
 }
 
 // Row r after the collect stage: its exact k-th largest key among its bucket
-// (kept in LDS), the bucket's candidates and ties appended, the raw candidates
-// re-encoded against the new threshold.  Leaves the row's final candidate and
-// tie counts and threshold in sh.c->nc[0], sh.c->nt[0], sh.c->thr[0] (and in counters
-// and thresholds).
+// (in LDS when it fits, else read from L2 by every pass) becomes its
+// threshold; the bucket's keys above it and equal to it are appended as
+// candidates (after the nabove collected above the bucket) and ties, the
+// collected candidates (stored raw) re-encoded against it.  Writes the row's
+// counters and threshold and returns them in sh.c->nc[0], nt[0], thr[0].
 template <int NT>
 __device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, int r, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
-  const int stride = s.top_k + s.capacity;
   uint32_t* row = ws.row(r);
-  // the bucket holds the keys of one digit, at most kBucketPairs by the stage
-  // change's test
   const int nin = min(static_cast<int>(ld_ag(row + 3)), kBucketPairs);
-  static_assert(kBucketPairs <= kFinalizeLds, "a bucket fits the final select's LDS");
   const int krem = static_cast<int>(ld_ag(row + 1));
   const int nabove = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
-  int32_t* bucket = ws.bucket(r);
-  // the bucket's (index, score bits) pairs into LDS, all of a thread's loads in
-  // flight at once (the radix keys are derived from the bits where needed)
-  constexpr int kPer = kFinalizeLds / kThreads;
-  uint32_t* bits = sh.fk;
-  int32_t* idxs = sh.fi;
-  {
-    int2 v[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kThreads + tid;
-      if (i < nin) v[u] = *reinterpret_cast<const int2*>(bucket + 2 * i);
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kThreads + tid;
-      if (i < nin) {
-        idxs[i] = v[u].x;
-        bits[i] = static_cast<uint32_t>(v[u].y);
-      }
-    }
-  }
-  __syncthreads();
-  auto key_of = [&](int i) { return radix_key(__uint_as_float(bits[i])); };
-  cta_radix_select(key_of, nin, krem, sh.fh, sh);
-  const uint32_t kstar = sh.c->pfx[0];
+  const int32_t* bucket = ws.bucket(r);
+  const bool lds = nin <= sh.fin_cap;
+  if (lds) load_pairs<NT>(bucket, nin, bucket, nin, [](uint32_t b) { return b; }, sh);
+  const PairSrc ps{bucket, 0.f, 0, lds ? 1 : 0};
+  auto pair_of = [&](int i) { return pair_at<NT>(ps, i, sh); };
+  uint32_t og, oe;
+  int n_gt, n_eq;
+  const uint32_t kstar = kth_scan<NT>(ps, nin, krem, sh, og, oe, n_gt, n_eq);
   const float t2 = key_to_float(kstar);
-  int32_t* slots = s.candidates + static_cast<int64_t>(r) * stride * 2;
-  #pragma unroll 1
+  int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
+#pragma unroll 1
   for (int i = tid; i < nin; i += kThreads) {
-    const uint32_t key = key_of(i);
-    const int32_t idx = idxs[i];
-    const float e = __uint_as_float(bits[i]);
+    const int2 p = pair_of(i);
+    const float e = __int_as_float(p.y);
+    const uint32_t key = radix_key(e);
     if (key > kstar) {
-      const int k = nabove + atomicAdd(&sh.c->pos[0], 1);
-      if (k < s.capacity) store_pair(slots + 2 * (s.top_k + k), idx, enc_cand(e, t2));
+      const int c = nabove + static_cast<int>(og++);
+      if (c < s.capacity) store_pair(slots + 2 * (s.top_k + c), p.x, enc_cand(e, t2));
     } else if (key == kstar) {
-      const int k = atomicAdd(&sh.c->pos[1], 1);
-      if (k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), idx, e - t2);
+      const int c = static_cast<int>(oe++);
+      if (c < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - c), p.x, e - t2);
     }
   }
-  // the candidates collected above the bucket (raw scores) re-encoded against
-  // the new threshold, all of a thread's loads in flight at once
-  const int nabove_kept = min(nabove, s.capacity);
-  for (int i0 = 0; i0 < nabove_kept; i0 += kPer * kThreads) {
-    int2 v[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = i0 + u * kThreads + tid;
-      if (i < nabove_kept) v[u] = *reinterpret_cast<const int2*>(slots + 2 * (s.top_k + i));
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = i0 + u * kThreads + tid;
-      if (i < nabove_kept) store_pair(slots + 2 * (s.top_k + i), v[u].x, enc_cand(__int_as_float(v[u].y), t2));
-    }
+  // the candidates collected above the bucket (raw scores) re-encoded
+#pragma unroll 1
+  for (int i = tid; i < min(nabove, s.capacity); i += kThreads) {
+    const int2 p = *reinterpret_cast<const int2*>(slots + 2 * (s.top_k + i));
+    store_pair(slots + 2 * (s.top_k + i), p.x, enc_cand(__int_as_float(p.y), t2));
   }
-  __syncthreads();
   if (tid == 0) {
-    const int nc = nabove + sh.c->pos[0], nt = sh.c->pos[1];
+    const int nc = nabove + n_gt;
     st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, static_cast<uint32_t>(nc));
-    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(nt));
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(n_eq));
     st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
     sh.c->nc[0] = nc;
-    sh.c->nt[0] = nt;
+    sh.c->nt[0] = n_eq;
     sh.c->thr[0] = t2;
   }
   // this CTA's slot stores complete before the Top-k reads the slots back
@@ -1660,119 +1390,96 @@ __device__ __forceinline__ void resolve_row(const SelectArgs& s, const Ws& ws, i
   __syncthreads();
 }
 
-// Row r (k = min(e_r, top_k) >= 1) re-selected from its candidates alone: all
-// n_cand of them are kept -- the first `capacity` in its slots (encoded against
-// the old threshold), the rest in the workspace's overflow area -- and every
-// key at or above its k-th largest candidate is a candidate (it scores above
-// the old threshold).  The k-th largest candidate score, radix-selected in
-// LDS, becomes the row's threshold; the candidates above it and those equal
-// to it are stored again as the row's candidates and ties, and its counters,
-// threshold, ranges and Top-k written.  (Scores are NaN-free by precondition,
-// so no key outside the candidates is a tie at the new threshold.)
+// Row r (k = min(e_r, top_k) >= 1) selected again from its kept pairs alone.
+// With at least k candidates, all nc of them are kept -- the first `capacity`
+// in its slots (encoded against the old threshold), the rest in the overflow
+// area -- and every key at or above the k-th largest candidate is one of them
+// (it scores above the old threshold).  With fewer, the kept pairs are every
+// candidate, every tie (in the tie slots) and every key of the near band just
+// below the threshold (raw, in the near area), which holds the k-th largest:
+// every key at or above it is one of them.  The k-th largest kept score,
+// radix-selected in LDS, becomes the row's threshold; the kept pairs above it
+// and equal to it are stored again as the row's candidates and ties, and its
+// counters, threshold, ranges and Top-k written.  (Scores are NaN-free by
+// precondition, so no key outside them is a tie at the new threshold.)
 template <int NT>
-__device__ __forceinline__ void stored_resolve(const SelectArgs& s, const Ws& ws, int r, int k, const Sh<NT>& sh) {
+__device__ __forceinline__ void stored_resolve(const SelectArgs& s, int r, int k, int nc, int nt, int nn, float th,
+                                               const Sh<NT>& sh) {
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    sh.c->nc[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
-    sh.c->thr[0] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
-  }
-  __syncthreads();
-  const int n = sh.c->nc[0];  // capacity < n <= fin_cap, n - capacity <= kOverflowPairs, n >= k
-  const float th = sh.c->thr[0];
   const int cap = s.capacity;
   int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + cap) * 2;
   const int32_t* cand = slots + 2 * s.top_k;
-  const int32_t* ovf = ws.overflow(r);
-  // every candidate's (index, score bits) into LDS, eight loads of a thread in flight at once
-  constexpr int kBatch = 8;
-  for (int i0 = 0; i0 < n; i0 += kBatch * kThreads) {
-    int2 v[kBatch];
+  const int32_t* ovf = s.ovf + 2 * static_cast<int64_t>(kOverflowPairs) * r;
+  const int32_t* nearp = s.nearp + 2 * static_cast<int64_t>(kNearPairs) * r;
+  const int n = nc >= k ? nc : nc + nt + nn;  // <= fin_cap
+  // every kept pair into LDS with its score, eight loads a thread in flight
+#pragma unroll 1
+  for (int i0 = 0; i0 < n; i0 += 8 * kThreads) {
+    int2 v[8];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * kThreads + tid;
-      if (i < n) v[u] = *reinterpret_cast<const int2*>(i < cap ? cand + 2 * i : ovf + 2 * (i - cap));
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * kThreads + tid;
       if (i < n) {
+        const int32_t* src = i < nc ? (i < cap ? cand + 2 * i : ovf + 2 * (i - cap))
+                                    : (i < nc + nt ? slots + 2 * (s.top_k - 1 - (i - nc)) : nearp + 2 * (i - nc - nt));
+        v[u] = *reinterpret_cast<const int2*>(src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      if (i < n) {
+        const float x = __int_as_float(v[u].y);
+        const float e = i < nc ? dec_cand(x, th) : (i < nc + nt ? x + th : x);
         sh.fi[i] = v[u].x;
-        sh.fk[i] = __float_as_uint(dec_cand(__int_as_float(v[u].y), th));
+        sh.fk[i] = __float_as_uint(e);
       }
     }
   }
   __syncthreads();
-  auto key_of = [&](int i) { return radix_key(__uint_as_float(sh.fk[i])); };
-  cta_radix_select(key_of, n, k, sh.fh, sh);
-  const uint32_t kstar = sh.c->pfx[0];
+  const PairSrc ps{nullptr, 0.f, 0, 1};
+  auto pair_of = [&](int i) { return pair_at<NT>(ps, i, sh); };
+  uint32_t og, oe;
+  int n_gt, n_eq;
+  const uint32_t kstar = kth_scan<NT>(ps, n, k, sh, og, oe, n_gt, n_eq);
   const float t2 = key_to_float(kstar);
-  // each thread's keys above k* and equal to it counted, one CTA-wide exclusive
-  // scan of the counts, then every thread writes at its offsets
-  uint32_t gt = 0u, eq = 0u;
-  for (int i = tid; i < n; i += kThreads) {
-    const uint32_t key = key_of(i);
-    gt += key > kstar ? 1u : 0u;
-    eq += key == kstar ? 1u : 0u;
-  }
-  uint32_t og = gt, oe = eq;
-  cta_exclusive_scan2(og, oe, sh);
-  uint32_t n_gt = 0u, n_eq = 0u;  // the totals: the last thread's offsets plus its counts
-  if (tid == kThreads - 1) {
-    sh.c->pos[0] = static_cast<int>(og + gt);
-    sh.c->pos[1] = static_cast<int>(oe + eq);
-  }
-  __syncthreads();
-  n_gt = static_cast<uint32_t>(sh.c->pos[0]);
-  n_eq = static_cast<uint32_t>(sh.c->pos[1]);
   int32_t* out = s.topk_idx ? s.topk_idx + static_cast<int64_t>(r) * s.top_k : nullptr;
+#pragma unroll 1
   for (int i = tid; i < n; i += kThreads) {
-    const uint32_t key = key_of(i);
-    const int32_t idx = sh.fi[i];
-    const float e = __uint_as_float(sh.fk[i]);
+    const int2 p = pair_of(i);
+    const float e = __int_as_float(p.y);
+    const uint32_t key = radix_key(e);
     if (key > kstar) {
-      if (static_cast<int>(og) < cap) store_pair(slots + 2 * (s.top_k + og), idx, enc_cand(e, t2));
-      if (out) st_wt(reinterpret_cast<uint32_t*>(out + og), static_cast<uint32_t>(idx));
+      if (static_cast<int>(og) < cap) store_pair(slots + 2 * (s.top_k + og), p.x, enc_cand(e, t2));
+      if (out) out[og] = p.x;
       ++og;
     } else if (key == kstar) {
-      if (static_cast<int>(oe) < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - oe), idx, e - t2);
-      if (out && n_gt + oe < static_cast<uint32_t>(k)) st_wt(reinterpret_cast<uint32_t*>(out + n_gt + oe), static_cast<uint32_t>(idx));
+      if (static_cast<int>(oe) < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - oe), p.x, e - t2);
+      if (out && n_gt + static_cast<int>(oe) < k) out[n_gt + oe] = p.x;
       ++oe;
     }
   }
   if (out)
-    for (int i = k + tid; i < s.top_k; i += kThreads) st_wt(reinterpret_cast<uint32_t*>(out + i), 0xffffffffu);
+    for (int i = k + tid; i < s.top_k; i += kThreads) out[i] = -1;
   if (tid == 0) {
-    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, n_gt);
-    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, n_eq);
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r, static_cast<uint32_t>(n_gt));
+    st_wt(reinterpret_cast<uint32_t*>(s.counters) + 2 * r + 1, static_cast<uint32_t>(n_eq));
     st_wt(reinterpret_cast<uint32_t*>(s.thresholds) + r, __float_as_uint(t2));
-    s.ranges[r] = s.top_k - min(static_cast<int>(n_eq), s.top_k);
-    s.ranges[s.rows + r] = s.top_k + min(static_cast<int>(n_gt), cap);
+    s.ranges[r] = s.top_k - min(n_eq, s.top_k);
+    s.ranges[s.rows + r] = s.top_k + min(n_gt, cap);
   }
   __syncthreads();
 }
 
-// Ranges and exact Top-k of a fitting row r (k = min(e_r, top_k)): its counts
-// and threshold, and its first candidate pairs in the registers of waves 1-3
-// (all of them when it has at most top_k + kFewExtra), loaded in one round trip.
+// Row r of a tile with final counters (nc, nt), nn near-band keys and
+// threshold th: its ranges and Top-k when it fits, its re-selection from its
+// kept pairs when it is a stored row; its near-band count is left zeroed.
 template <int NT>
-__device__ __forceinline__ void fit_row_outputs(const SelectArgs& s, int r, int k, const Sh<NT>& sh) {
-  const int tid = threadIdx.x;
-  const int npre = s.topk_idx ? min(min(s.capacity, s.top_k + kFewExtra), kPreCap) : 0;
-  if (tid == 0) {
-    sh.c->nc[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
-    sh.c->nt[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
-    sh.c->thr[0] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
-  }
-  const int32_t* cand = s.candidates + (static_cast<int64_t>(r) * (s.top_k + s.capacity) + s.top_k) * 2;
-  const int pt = tid - 64;
-  int2 pre[kPreUnits];
-#pragma unroll
-  for (int u = 0; u < kPreUnits; ++u) {
-    const int i = u * kPreThreads + pt;
-    pre[u] = pt >= 0 && i < npre ? *reinterpret_cast<const int2*>(cand + 2 * i) : int2{0, 0};
-  }
-  __syncthreads();
-  row_outputs_pre<NT>(s, r, k, sh.c->nc[0], sh.c->nt[0], sh.c->thr[0], npre, pre, sh);
+__device__ __forceinline__ void unswept_row(const SelectArgs& s, int r, int k, int nc, int nt, int nn, float th,
+                                            bool stored, const Sh<NT>& sh) {
+  if (threadIdx.x == 0 && s.nearc) st_wt(s.nearc + static_cast<int64_t>(r) * kRowWords, 0u);
+  if (stored) stored_resolve<NT>(s, r, k, nc, nt, nn, th, sh);
+  else fit_row_outputs<NT>(s, r, k, nc, nt, th, true, sh);
 }
 
 // Stage-6 item t of tile b's job: row t given its ranges and Top-k -- a swept
@@ -1781,45 +1488,51 @@ __device__ __forceinline__ void fit_row_outputs(const SelectArgs& s, int r, int 
 // its slots.  A swept row's state words are cleared for the next call.
 template <int NT>
 __device__ __forceinline__ void row_item(const SelectArgs& s, const Ws& ws, int b, int L, int t, uint32_t masks,
-                                         const Sh<NT>& sh) {
+                                         int nc, int nt, int nn, float th, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   const int r = b * NT + t;
   const int k = min(max(0, L - NT + t + 1), s.top_k);
   if (masks & (1u << t)) {
     if (ld_ag(ws.row(r) + 2) < 32u) {
       resolve_row<NT>(s, ws, r, sh);
-    } else {
-      // stage 5 selected the row again at its exact threshold
-      if (tid == 0) {
-        sh.c->nc[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
-        sh.c->nt[0] = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
-        sh.c->thr[0] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
-      }
-      __syncthreads();
+      nc = sh.c->nc[0];
+      nt = sh.c->nt[0];
+      th = sh.c->thr[0];
     }
-    row_outputs<NT>(s, r, k, sh.c->nc[0], sh.c->nt[0], sh.c->thr[0], 0, sh);
-    if (tid < 4) st_wt(ws.row(r) + tid, 0u);
-  } else if ((masks >> 8) & (1u << t)) {
-    stored_resolve<NT>(s, ws, r, k, sh);
+    // (after a stage-5 select the slots were written by the items: visible
+    // after the item's acquire; after a resolve this CTA wrote them)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    fit_row_outputs<NT>(s, r, k, nc, nt, th, false, sh);
+    if (tid < 5) st_wt(ws.row(r) + tid, 0u);  // (word 4: the near-band count)
   } else {
-    fit_row_outputs<NT>(s, r, k, sh);
+    unswept_row<NT>(s, r, k, nc, nt, nn, th, ((masks >> 8) & (1u << t)) != 0, sh);
   }
 }
 
-// Adds the LDS histograms sh.rh of pass `pass` of the rows in `mask` to
-// copy `copy` of their global histograms (nonzero bins only).
-template <int NT>
-__device__ __forceinline__ void flush_hist(const Ws& ws, int b, int pass, uint32_t mask, int copy,
-                                           const Sh<NT>& sh) {
-  const int nb = 1 << pass_bits(pass);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (!(mask & (1u << t))) continue;
-    uint32_t* gh = ws.hist(b * NT + t, copy);
-    for (int i = threadIdx.x; i < nb; i += kThreads) {
-      const uint32_t h = sh.rh[t][i];
-      if (h) atomicAdd(gh + i, h);
-    }
+// The bookkeeping after item idx of stage `stage` of tile b's job: the item is
+// counted, and whoever completes the stage's last item runs the stage change
+// (or, after the last stage, clears the job's words).
+template <int NT, bool kFused>
+__device__ __forceinline__ void item_done(const SelectArgs& s, const Ws& ws, int b, int L, int stage, uint32_t mask,
+                                          const Sh<NT>& sh) {
+  const int tid = threadIdx.x;
+  wait_vm_done();
+  __syncthreads();
+  PMQA_TR(sh, 11, 0, stage);
+  if (tid == 0)
+    sh.c->is_last = atomicAdd(ws.done_word(b, stage), 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
+  __syncthreads();
+  PMQA_TR(sh, 12, sh.c->is_last, stage);
+  if (!sh.c->is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (stage < kStageCollect) {
+    job_next_stage<NT>(s, ws, b, stage - kStageHist0, mask, sh);
+  } else if (stage < kStageRows) {
+    if (tid < kClaimWords) st_wt64(ws.claim(b, tid), static_cast<uint64_t>(kStageRows) << 32);
+  } else {
+    // the job is done: all of its words cleared for the next call (a late claim
+    // attempt then adds to a word of stage 0, which hands out nothing)
+    if (tid < kJobWords) st_wt(ws.job(b) + tid, 0u);
   }
 }
 
@@ -1840,34 +1553,57 @@ struct RescoreLds {
 // later passes, and their first radix histogram pass.
 template <int NT>
 __device__ __forceinline__ void rescore_item(const PagedArgs& a, const SelectArgs& s, const Ws& ws, int b, int L, int idx,
-                                             uint32_t mask, const int (&end)[NT], const RescoreLds<NT>& rl) {
+                                             uint32_t mask, const int (&end)[NT], const RescoreLds<NT>& rl,
+                                             const Sh<NT>& sh) {
   const int lane = lane_id();
   const int tid = threadIdx.x;
   const int shift = pass_shift(0);
   constexpr int kWords = (1 << 10) / 2;
   for (int i = tid; i < NT * kWords; i += kThreads) rl.ph[i] = 0u;
   __syncthreads();
-  typename std::conditional<(NT >= 3), KvSourceQ<NT>, KvSource<NT>>::type src;
-  src.bind(rl.stage);
-  src.bind_q(rl.ql);
-  src.init(a, b);
   float* rows = s.scores + static_cast<int64_t>(b) * NT * s.score_ld;
   const int c0 = idx * kRescoreItemKeys;
   const int c1 = min(c0 + kRescoreItemKeys, L);
-  stream_keys<NT, false>(
-      src, c0, c1, L,
-      [&](int, int p0, const float(&E)[NT]) {
-        const int p = p0 + lane;
+  auto add = [&](int t, int p, float e) {
+    st_wt(reinterpret_cast<uint32_t*>(rows + t * s.score_ld + p), __float_as_uint(e));
+    const uint32_t bin = radix_key(e) >> shift;
+    atomicAdd(&rl.ph[t * kWords + (bin >> 1)], 1u << (16 * (bin & 1u)));
+  };
+  if (NT > 1 && __popc(mask) == 1) {
+    // one row repaired: only its scores are computed (the same operations, so
+    // the same bits, as the row's scores in the tile's scoring)
+    const int t1 = __ffs(static_cast<int>(mask)) - 1;
+    int e1 = 0;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (!(mask & (1u << t)) || p >= end[t]) continue;
-          st_wt(reinterpret_cast<uint32_t*>(rows + t * s.score_ld + p), __float_as_uint(E[t]));
-          const uint32_t bin = radix_key(E[t]) >> shift;
-          atomicAdd(&rl.ph[t * kWords + (bin >> 1)], 1u << (16 * (bin & 1u)));
-        }
-      },
-      [](int, int) {});
+    for (int t = 0; t < NT; ++t)
+      if (t == t1) e1 = end[t];
+    KvSource<1> src;
+    src.bind(rl.stage);
+    src.init_row(a, b, static_cast<int64_t>(b) * NT + t1);
+    stream_keys<1, false>(
+        src, c0, c1, L,
+        [&](int, int p0, const float(&E)[1]) {
+          const int p = p0 + lane;
+          if (p < e1) add(t1, p, E[0]);
+        },
+        [](int, int) {});
+  } else {
+    typename std::conditional<(NT >= 3), KvSourceQ<NT>, KvSource<NT>>::type src;
+    src.bind(rl.stage);
+    src.bind_q(rl.ql);
+    src.init(a, b);
+    stream_keys<NT, false>(
+        src, c0, c1, L,
+        [&](int, int p0, const float(&E)[NT]) {
+          const int p = p0 + lane;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            if ((mask & (1u << t)) && p < end[t]) add(t, p, E[t]);
+        },
+        [](int, int) {});
+  }
   __syncthreads();
+  PMQA_TR(sh, 18, 0, 0);
   const int copy = idx % kHistCopies;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -1882,9 +1618,9 @@ __device__ __forceinline__ void rescore_item(const PagedArgs& a, const SelectArg
 }
 
 // Repair item `idx` of stage `stage` of tile b's job: its keys' scores (read
-// back from the logits matrix or the score buffer, or for stage 1 of the fused
-// repair computed again), then their histogram, collect or select pass, then
-// the stage bookkeeping.
+// back from the logits matrix or the score rows, or for stage 1 of the fused
+// repair computed again), then their histogram, collect or select pass; or a
+// row item; then the stage bookkeeping.
 template <int NT, bool kFused, class Args>
 __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, const Ws& ws, int b, int L, int stage, int idx,
                                          const Sh<NT>& sh, const RescoreLds<NT>& rl) {
@@ -1893,29 +1629,44 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
   // the stores of the CTAs that ran the tile's main pass and the job's earlier
   // stages (written through, before their counts) become visible
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // the job's masks and every row's state words, all loaded at once
   const uint32_t masks = ld_ag(ws.mask_word(b));
-  const uint32_t mask = masks & 0xffu;  // the swept rows
   int end[NT];
-  uint32_t pfx[NT];
+  uint32_t pfx[NT], kn[NT];
   float thr2[NT];
-  int known = 0;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     end[t] = max(0, L - NT + t + 1);
     const int r = b * NT + t;
-    const bool m = (mask & (1u << t)) != 0;
-    pfx[t] = m ? ld_ag(ws.row(r) + 0) : 0u;
-    thr2[t] = m ? __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r)) : 0.f;
-    if (m) known = static_cast<int>(ld_ag(ws.row(r) + 2));
+    pfx[t] = ld_ag(ws.row(r) + 0);
+    kn[t] = ld_ag(ws.row(r) + 2);
+    thr2[t] = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
   }
+  // a row item's counts, in the same round trip
+  int nc = 0, nt = 0, nn = 0;
+  if (stage == kStageRows) {
+    const int r = b * NT + idx;
+    nc = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+    nt = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
+    nn = s.nearc ? static_cast<int>(ld_ag(s.nearc + static_cast<int64_t>(r) * kRowWords)) : 0;
+  }
+  const uint32_t mask = masks & 0xffu;  // the swept rows
+  int known = 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (mask & (1u << t)) known = static_cast<int>(kn[t]);
   bool done = false;
   if (stage == kStageRows) {
-    row_item<NT>(s, ws, b, L, idx, masks, sh);
+    float th = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (t == idx) th = thr2[t];
+    row_item<NT>(s, ws, b, L, idx, masks, nc, nt, nn, th, sh);
     done = true;
   }
   if constexpr (kFused) {
     if (stage == kStageHist0) {
-      rescore_item<NT>(a, s, ws, b, L, idx, mask, end, rl);
+      rescore_item<NT>(a, s, ws, b, L, idx, mask, end, rl, sh);
       done = true;
     }
   }
@@ -1927,149 +1678,141 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
       src.init(a, b);
     const int c0 = idx * kItemKeys<NT>;
     const int cend = min(c0 + kItemKeys<NT>, L);
-    // The item's scores of the repaired rows, all loaded at once: wave w's
-    // group u holds keys c0 + 64*(w + 4u) .. +63.
+    // one repaired row at a time: its item scores all loaded at once (wave w's
+    // group u holds keys c0 + 64*(w + 4u) .. +63), then its pass
     constexpr int kU = kItemKeys<NT> / (kGroupKeys * kWaves);
     const int w = wave_id();
-    float v[NT][kU];
-#pragma unroll
+#pragma unroll 1
     for (int t = 0; t < NT; ++t) {
       if (!(mask & (1u << t))) continue;
+      const int r = b * NT + t;
+      uint32_t pf = 0u;
+      float th2 = 0.f;
+      int lim = 0;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) v[t][u] = src.value(t, c0 + kGroupKeys * (w + kWaves * u) + lane, L);
-    }
-    if (stage < kStageCollect) {
-      // histogram straight from the scores in registers
-      const int pass = stage - kStageHist0;
-      const int shift = pass_shift(pass);
-      const int bits = pass_bits(pass);
-      const uint32_t low = (1u << bits) - 1u;
-      for (int i = tid; i < NT * kRadixBins; i += kThreads) (&sh.rh[0][0])[i] = 0u;
-      __syncthreads();
+      for (int u = 0; u < NT; ++u)
+        if (u == t) {
+          pf = pfx[u];
+          th2 = thr2[u];
+          lim = min(cend, end[u]);
+        }
+      float v[kU];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (!(mask & (1u << t))) continue;
-        const int lim = min(cend, end[t]);
+      for (int u = 0; u < kU; ++u) v[u] = src.value(t, c0 + kGroupKeys * (w + kWaves * u) + lane, L);
+      PMQA_TR(sh, 9, 0, stage);
+      if (stage < kStageCollect) {
+        // histogram straight from the scores in registers
+        const int pass = stage - kStageHist0;
+        const int shift = pass_shift(pass);
+        const int bits = pass_bits(pass);
+        const uint32_t low = (1u << bits) - 1u;
+        uint32_t* h = sh.rh[0];
+        for (int i = tid; i < (1 << bits); i += kThreads) h[i] = 0u;
+        __syncthreads();
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
           const int p = c0 + kGroupKeys * (w + kWaves * u) + lane;
-          if (p >= lim) continue;
-          const uint32_t key = radix_key(v[t][u]);
-          if (pass > 0 && (key >> (shift + bits)) != pfx[t]) continue;
-          atomicAdd(&sh.rh[t][(key >> shift) & low], 1u);
+          const uint32_t key = radix_key(v[u]);
+          const bool in = p < lim && (pass == 0 || (key >> (shift + bits)) == pf);
+          if (in) atomicAdd(&h[(key >> shift) & low], 1u);
         }
+        __syncthreads();
+        PMQA_TR(sh, 10, 0, stage);
+        uint32_t* gh = ws.hist(r, idx % kHistCopies);
+        for (int i = tid; i < (1 << bits); i += kThreads) {
+          const uint32_t x = h[i];
+          if (x) atomicAdd(gh + i, x);
+        }
+        __syncthreads();
+      } else if (stage == kStageCollect) {
+        // keys above the bucket become candidates (raw scores; re-encoded once
+        // the threshold is known), keys inside it go to the row's bucket
+        int32_t* cslots = s.candidates + (static_cast<int64_t>(r) * (s.top_k + s.capacity) + s.top_k) * 2;
+        int32_t* bucket = ws.bucket(r);
+        append_row<NT, kU>(
+            c0, lim, v, sh,
+            [&](float e) {
+              const uint32_t top = radix_key(e) >> (32 - known);
+              return top > pf ? 1 : (top == pf ? 2 : 0);
+            },
+            [&](int n) { return atomicAdd(s.counters + 2 * r, n); },
+            [&](int n) { return static_cast<int>(atomicAdd(ws.row(r) + 3, static_cast<uint32_t>(n))); },
+            [&](int c, int k, int p, float e) {
+              if (c == 1 && k < s.capacity) store_pair(cslots + 2 * k, p, e);
+              if (c == 2 && k < kBucketPairs) store_pair(bucket + 2 * k, p, e);
+            });
+      } else {
+        // select again at the now exact threshold
+        int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
+        append_row<NT, kU>(
+            c0, lim, v, sh, [&](float e) { return e > th2 ? 1 : (!(e < th2) ? 2 : 0); },
+            [&](int n) { return atomicAdd(s.counters + 2 * r, n); },
+            [&](int n) { return atomicAdd(s.counters + 2 * r + 1, n); },
+            [&](int c, int k, int p, float e) {
+              if (c == 1 && k < s.capacity) store_pair(slots + 2 * (s.top_k + k), p, enc_cand(e, th2));
+              if (c == 2 && k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), p, e - th2);
+            });
       }
-      __syncthreads();
-      flush_hist<NT>(ws, b, pass, mask, idx % kHistCopies, sh);
-    } else if (stage == kStageCollect) {
-      // keys above the bucket become candidates (raw scores; re-encoded once
-      // the threshold is known), keys inside it go to the row's bucket buffer
-      const int stride = s.top_k + s.capacity;
-      append_item<NT, kU>(
-          c0, cend, end, mask, v, sh,
-          [&](int t, float e) {
-            const uint32_t top = radix_key(e) >> (32 - known);
-            return top > pfx[t] ? 1 : (top == pfx[t] ? 2 : 0);
-          },
-          [&](int t, int n) { return atomicAdd(s.counters + 2 * (b * NT + t), n); },
-          [&](int t, int n) { return static_cast<int>(atomicAdd(ws.row(b * NT + t) + 3, static_cast<uint32_t>(n))); },
-          [&](int t, int c, int k, int p, float e) {
-            if (c == 1 && k < s.capacity)
-              store_pair(s.candidates + (static_cast<int64_t>(b * NT + t) * stride + s.top_k + k) * 2, p, e);
-            if (c == 2 && k < kBucketPairs) store_pair(ws.bucket(b * NT + t) + 2 * k, p, e);
-          });
-    } else {
-      // select again at the now exact threshold
-      const int stride = s.top_k + s.capacity;
-      int32_t* cnt = s.counters + 2 * b * NT;
-      append_item<NT, kU>(
-          c0, cend, end, mask, v, sh,
-          [&](int t, float e) { return e > thr2[t] ? 1 : (!(e < thr2[t]) ? 2 : 0); },
-          [&](int t, int n) { return atomicAdd(cnt + 2 * t, n); },
-          [&](int t, int n) { return atomicAdd(cnt + 2 * t + 1, n); },
-          [&](int t, int c, int k, int p, float e) {
-            int32_t* slots = s.candidates + static_cast<int64_t>(b * NT + t) * stride * 2;
-            if (c == 1 && k < s.capacity) store_pair(slots + 2 * (s.top_k + k), p, enc_cand(e, thr2[t]));
-            if (c == 2 && k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), p, e - thr2[t]);
-          });
     }
   }
-  wait_vm_done();
-  __syncthreads();
-  if (tid == 0)
-    sh.c->is_last = atomicAdd(ws.done_word(b, stage), 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
-  __syncthreads();
-  if (!sh.c->is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (stage < kStageCollect) {
-    job_next_stage<NT>(s, ws, b, stage - kStageHist0, mask, sh);
-  } else if (stage < kStageRows) {
-    if (tid < kClaimWords) st_wt64(ws.claim(b, tid), static_cast<uint64_t>(kStageRows) << 32);
-  } else {
-    // the job is done: its words cleared for the next call (all but the claim
-    // words, which late claim attempts may still increment; the next publish
-    // of the tile rewrites them)
-    if (tid >= 2 * kClaimWords && tid < kJobWords) st_wt(ws.job(b) + tid, 0u);
-  }
+  item_done<NT, kFused>(s, ws, b, L, stage, mask, sh);
 }
 
-// Wave 0 claims an item of a listed job; the result goes to sh.c->job: (tile,
-// stage, item), tile -1 when none is open but more may open, -2 when the CTA
-// should leave.  `since` is when the CTA last had an item (s_memrealtime).
+// Wave 0 claims an item of a published job; the result goes to sh.c->job:
+// (tile, stage, item), tile -1 when none is open but more may open, -2 when
+// the CTA should leave.  `since` is when the CTA last had work (s_memrealtime).
 template <int NT, bool kFused, class Args>
 __device__ __forceinline__ void claim_item(const Args& a, const SelectArgs& s, const Ws& ws, uint64_t since,
                                            const Sh<NT>& sh) {
   if (wave_id() == 0) {
     const int lane = lane_id();
-    // (a workspace whose header was not left zeroed gives wrong results, not stray accesses)
-    const uint32_t fl = ld_ag(ws.flag(static_cast<int>(blockIdx.x % kDoneFlags)));
-    const int njobs = fl ? min(static_cast<int>(fl - 1u), ws.batch)
-                         : min(static_cast<int>(ld_ag64(ws.progress()) >> 32), ws.batch);
-    bool pending = fl == 0u;  // a tile is still before its fit test
+    bool pending = false;  // a job before its last stage
     int got = -1, stage = 0, idx = 0;
-    const int q = static_cast<int>(blockIdx.x % kClaimWords);  // this CTA's claim word
-    for (int j0 = 0; j0 < njobs && got < 0; j0 += 64) {
-      const int j = j0 + lane;
-      int b = 0, len = 0;
-      uint64_t w = 0;
-      bool unwritten = false;
-      if (j < njobs) {
-        const uint32_t e = ld_ag(ws.list(j));
-        unwritten = e == 0u;
-        if (!unwritten) {
-          b = min(static_cast<int>(e) - 1, ws.batch - 1);
+    const int q0 = static_cast<int>(blockIdx.x % kClaimWords);  // this CTA's first claim word
+    const int rot = static_cast<int>((blockIdx.x / kClaimWords) & 63);  // spread CTAs over the open jobs
+    // every claim word of every job, the CTA's own word first (any CTA can
+    // take any item, so no item waits for a CTA that has left)
+    for (int qi = 0; qi < kClaimWords && got < 0; ++qi) {
+      const int q = (q0 + qi) % kClaimWords;
+      for (int j0 = 0; j0 < ws.batch && got < 0; j0 += 64) {
+        const int b = j0 + lane;
+        int len = 0;
+        uint64_t w = 0;
+        if (b < ws.batch) {
           w = ld_ag64(ws.claim(b, q));
           len = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
         }
-      }
-      const uint32_t st = static_cast<uint32_t>(w >> 32);
-      const bool open = st >= kStageHist0 && st <= kStageRows &&
-                        q + kClaimWords * static_cast<uint64_t>(static_cast<uint32_t>(w)) <
-                            static_cast<uint64_t>(stage_items<NT, kFused>(static_cast<int>(st), len));
-      pending = pending || __ballot(unwritten || (st >= kStageHist0 && st < kStageRows)) != 0;
-      uint64_t m = __ballot(open);
-      const int rot = static_cast<int>(blockIdx.x & 63);  // spread CTAs over the open jobs
-      while (m) {
-        const uint64_t hi = m & (~0ull << rot);
-        const int l = __ffsll(static_cast<long long>(hi ? hi : m)) - 1;
-        m &= ~(1ull << l);
-        const int bl = __shfl(b, l);
-        const int ll = __shfl(len, l);
-        unsigned long long old = 0;
-        if (lane == 0) old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.claim(bl, q)), 1ull);
-        old = __shfl(old, 0);
-        const uint32_t st2 = static_cast<uint32_t>(old >> 32);
-        const uint64_t i2 = q + kClaimWords * static_cast<uint64_t>(static_cast<uint32_t>(old));
-        if (st2 >= kStageHist0 && st2 <= kStageRows &&
-            i2 < static_cast<uint64_t>(stage_items<NT, kFused>(static_cast<int>(st2), ll))) {
-          got = bl;
-          stage = static_cast<int>(st2);
-          idx = static_cast<int>(i2);
-          break;
+        const uint32_t st = static_cast<uint32_t>(w >> 32);
+        const bool open = st >= kStageHist0 && st <= kStageRows &&
+                          q + kClaimWords * static_cast<uint64_t>(static_cast<uint32_t>(w)) <
+                              static_cast<uint64_t>(stage_items<NT, kFused>(static_cast<int>(st), len));
+        pending = pending || __ballot(st >= kStageHist0 && st < kStageRows) != 0;
+        uint64_t m = __ballot(open);
+        while (m) {
+          const uint64_t hi = m & (~0ull << rot);
+          const int l = __ffsll(static_cast<long long>(hi ? hi : m)) - 1;
+          m &= ~(1ull << l);
+          const int bl = j0 + l;
+          const int ll = __shfl(len, l);
+          unsigned long long old = 0;
+          if (lane == 0) old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.claim(bl, q)), 1ull);
+          old = __shfl(old, 0);
+          const uint32_t st2 = static_cast<uint32_t>(old >> 32);
+          const uint64_t i2 = q + kClaimWords * static_cast<uint64_t>(static_cast<uint32_t>(old));
+          if (st2 >= kStageHist0 && st2 <= kStageRows &&
+              i2 < static_cast<uint64_t>(stage_items<NT, kFused>(static_cast<int>(st2), ll))) {
+            got = bl;
+            stage = static_cast<int>(st2);
+            idx = static_cast<int>(i2);
+            break;
+          }
         }
       }
     }
-    if (got < 0 && (!pending || !s.resident || __builtin_amdgcn_s_memrealtime() - since > kIdleTicks)) got = -2;
+    if (got < 0) {
+      const uint64_t idle = __builtin_amdgcn_s_memrealtime() - since;
+      if (!s.resident || idle > (pending ? kIdleTicks : kLingerTicks)) got = -2;
+    }
     if (lane == 0) {
       sh.c->job[0] = got;
       sh.c->job[1] = stage;
@@ -2080,13 +1823,13 @@ __device__ __forceinline__ void claim_item(const Args& a, const SelectArgs& s, c
 }
 
 // After its own keys (and its tile's fit test, if it was the last): repair
-// items until nothing is left, then the CTA leaves; the last to leave clears
-// the header, the done flags and the job list for the next call.
+// items until nothing is left, then the CTA leaves.
 template <int NT, bool kFused, class Args>
-__device__ __forceinline__ void work_loop(const Args& a, const SelectArgs& s, char* lds) {
+__device__ __forceinline__ void work_loop(const Args& a, const SelectArgs& s, char* lds, bool linger) {
   using Lay = Layout<NT, kFused>;
-  const int tid = threadIdx.x;
-  uint64_t since = __builtin_amdgcn_s_memrealtime();
+  // (a CTA that has just finished its tile does not linger for items to come:
+  // the CTAs still finishing their keys will)
+  uint64_t since = __builtin_amdgcn_s_memrealtime() - (linger ? 0 : kLingerTicks);
   int polls = 0;
   while (true) {
     // the LDS views and the workspace rebuilt from opaque bases in every
@@ -2106,7 +1849,10 @@ __device__ __forceinline__ void work_loop(const Args& a, const SelectArgs& s, ch
     const int stage = sh.c->job[1];
     const int idx = sh.c->job[2];
     __syncthreads();
-    if (b == -2) break;
+    if (b == -2) {
+      PMQA_TR(sh, 8, polls, 0);
+      break;
+    }
     if (b < 0) {
       // back off (up to about half a microsecond between polls), so that
       // waiting CTAs keep their loads off the job words the working ones update
@@ -2115,28 +1861,18 @@ __device__ __forceinline__ void work_loop(const Args& a, const SelectArgs& s, ch
       continue;
     }
     polls = 0;
+    PMQA_TR(sh, 6, b, stage);
     const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
     run_item<NT, kFused>(a, s, ws, b, L, stage, idx, sh, rl);
     __syncthreads();
+    PMQA_TR(sh, 7, idx, stage);
     since = __builtin_amdgcn_s_memrealtime();
-  }
-  const Ws ws{s.ws, a.batch, s.rows};
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(ws.hdr() + 2, 1u);
-    if (old + 1u == gridDim.x) {
-      // every other CTA has left: nothing reads the header any more
-      const int njobs = min(static_cast<int>(ld_ag64(ws.progress()) >> 32), ws.batch);
-      for (int j = 0; j < njobs; ++j) st_wt(ws.list(j), 0u);
-      for (int i = 0; i < kDoneFlags; ++i) st_wt(ws.flag(i), 0u);
-      st_wt64(ws.progress(), 0ull);
-      st_wt(ws.hdr() + 2, 0u);
-    }
   }
 }
 
 // The tile's last CTA: arrivals[b] back to zero, the fit test, and then the
-// rows: finished here (one row, no sweep), or a job listed (the first row item
-// kept for this CTA when no sweep comes first); then the tile is counted.
+// rows: finished here (one row, no sweep), or a job published (the first row
+// item kept for this CTA when no sweep comes first).
 template <int NT, bool kFused, class Args>
 __device__ __forceinline__ void tile_finish(const Args& a, const SelectArgs& s, int b, int L, const Sh<NT>& sh,
                                             const RescoreLds<NT>& rl) {
@@ -2146,21 +1882,23 @@ __device__ __forceinline__ void tile_finish(const Args& a, const SelectArgs& s, 
   tile_fit<NT>(s, b, L, sh);
   const uint32_t sweep = sh.c->repair_mask;
   const uint32_t stored = sh.c->stored_mask;
+  PMQA_TR(sh, 4, sweep, stored);
   int end[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) end[t] = max(0, L - NT + t + 1);
   if (NT == 1 && sweep == 0u) {
-    if (tid == 0) count_tile(ws);
     const int k = min(end[0], s.top_k);
-    if (stored) stored_resolve<NT>(s, ws, b, k, sh);
-    else fit_row_outputs<NT>(s, b, k, sh);
+    unswept_row<NT>(s, b, k, sh.c->nc[0], sh.c->nt[0], sh.c->nn[0], sh.c->thr[0], stored != 0u, sh);
     return;
   }
   const bool self0 = sweep == 0u;
   publish_job<NT>(s, ws, b, end, sweep, stored, self0 ? kStageRows : kStageHist0, self0);
-  if (tid == 0) count_tile(ws);
-  __syncthreads();
-  if (self0) run_item<NT, kFused>(a, s, ws, b, L, kStageRows, 0, sh, rl);
+  if (self0) {
+    // the first row item, with the counts the fit test loaded
+    unswept_row<NT>(s, b * NT, min(end[0], s.top_k), sh.c->nc[0], sh.c->nt[0], sh.c->nn[0], sh.c->thr[0],
+                    (stored & 1u) != 0u, sh);
+    item_done<NT, kFused>(s, ws, b, L, kStageRows, 0u, sh);
+  }
 }
 
 
@@ -2345,12 +2083,34 @@ __device__ __forceinline__ void store_cands(const SelectArgs& s, int r, int base
   }
 }
 
-// A wave's n tie pairs of row r into slots top_k - 1 - base - i (those past
-// top_k dropped), written through.
-__device__ __forceinline__ void store_ties(const SelectArgs& s, int r, int base, const int2* list, int n) {
+// A wave's n pairs of row r from its tie list -- ties (stored value 0 or NaN)
+// into slots top_k - 1 - bt - i (those past top_k dropped), near-band keys
+// (below the threshold th; stored value e - th < 0, exact) with their raw
+// scores into the workspace's near area at bn + i (those past it dropped) --
+// written through.
+__device__ __forceinline__ void store_ties(const SelectArgs& s, int r, int bt, int bn, float th, const int2* list,
+                                           int n) {
   int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
-  for (int i = lane_id(); i < n; i += 64)
-    if (base + i < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - base - i), list[i].x, __int_as_float(list[i].y));
+  int32_t* nearp = s.nearp ? s.nearp + 2 * static_cast<int64_t>(kNearPairs) * r : nullptr;
+  const int lane = lane_id();
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const int2 e = i < n ? list[i] : int2{0, 0};
+    const float v = __int_as_float(e.y);
+    const bool near = i < n && v != 0.f && v == v;
+    const uint64_t mt = __ballot(i < n && !near);
+    const uint64_t mn = __ballot(near);
+    if (i < n && !near) {
+      const int j = bt + lanes_below(mt);
+      if (j < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - j), e.x, v);
+    }
+    if (near) {
+      const int j = bn + lanes_below(mn);
+      if (nearp && j < kNearPairs) store_pair(nearp + 2 * j, e.x, v + th);
+    }
+    bt += __popcll(mt);
+    bn += __popcll(mn);
+  }
 }
 
 // The select launch's CTA body: score keys [k0, k1) of the CTA's request (or
@@ -2373,30 +2133,44 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
   src.bind_q(ql);
   const int lane = lane_id();
   const int w = wave_id();
+  if (threadIdx.x == 0) sh.c->trace_n = 0;
+  bool was_last = false;  // this CTA finished its tile
   for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kKeysPerCta, true,
                    [&](int b, int L, int k0, int k1, int nctas) {
-    float thr[NT];
+    PMQA_TR(sh, 1, b, nctas);
+    float thr[NT], tlo[NT];
     int lim[NT];
-    int ncl[NT], ntl[NT];  // entries in this wave's lists (wave-uniform)
+    int ncl[NT], ntl[NT], nnl[NT];  // this wave's list entries: candidates, tie list (ties and near band), near band
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       thr[t] = s.thresholds[b * NT + t];
+      // with a workspace, the keys in a narrow band just below the threshold
+      // are kept too (a repair that needs a few more keys than the candidates
+      // and ties then finds them there); they share the tie list
+      tlo[t] = s.nearp ? near_floor(thr[t]) : thr[t];
       lim[t] = min(k1, max(0, L - NT + t + 1));
       ncl[t] = 0;
       ntl[t] = 0;
+      nnl[t] = 0;
     }
-    // A wave's list of row t into the row's slots: one atomic on the row's
-    // counter pair for both bases, then the pairs at base + i.
+    // A wave's lists of row t out: one atomic on the row's counter pair for
+    // the candidate and tie bases (one more for the near band), then the pairs.
     auto flush = [&](int t) {
       const int r = b * NT + t;
       uint64_t old = 0;
-      if (lane == 0) old = reserve_pair(s.counters + 2 * r, ncl[t], ntl[t]);
+      uint32_t nb = 0;
+      if (lane == 0) {
+        old = reserve_pair(s.counters + 2 * r, ncl[t], ntl[t] - nnl[t]);
+        if (nnl[t]) nb = atomicAdd(s.nearc + static_cast<int64_t>(r) * kRowWords, static_cast<uint32_t>(nnl[t]));
+      }
       const int bc = __shfl(static_cast<int>(static_cast<uint32_t>(old)), 0);
       const int bt = __shfl(static_cast<int>(static_cast<uint32_t>(old >> 32)), 0);
+      const int bn = __shfl(static_cast<int>(nb), 0);
       store_cands(s, r, bc, ms.cand[w][t], ncl[t]);
-      store_ties(s, r, bt, ms.tie[w][t], ntl[t]);
+      store_ties(s, r, bt, bn, thr[t], ms.tie[w][t], ntl[t]);
       ncl[t] = 0;
       ntl[t] = 0;
+      nnl[t] = 0;
     };
     src.init(a, b);
     stream_keys<NT, false>(
@@ -2411,11 +2185,12 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
             const float e = E[t];
             const bool vis = p < lim[t];
             const bool cand = vis && e > thr[t];
-            const bool tie = vis && !(e > thr[t]) && !(e < thr[t]);
+            const bool tie = vis && !(e > thr[t]) && !(e < tlo[t]);  // a tie, or in the near band
             const uint64_t mc = __ballot(cand);
             const uint64_t mt = __ballot(tie);
             const int nc = __popcll(mc);
             const int nt = __popcll(mt);
+            const int nn = mt ? __popcll(__ballot(tie && e < thr[t])) : 0;
             if (ncl[t] + nc > kWaveCand<NT> || ntl[t] + nt > kWaveTie<NT>) {
               flush(t);
               flushed = true;
@@ -2424,6 +2199,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
             if (tie) ms.tie[w][t][ntl[t] + lanes_below(mt)] = int2{p, __float_as_int(e - thr[t])};
             ncl[t] += nc;
             ntl[t] += nt;
+            nnl[t] += nn;
           }
           // a flush's stores and atomics complete here, so that the loop's
           // waits keep counting only key loads
@@ -2437,34 +2213,42 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         ms.count[w][t][0] = ncl[t];
-        ms.count[w][t][1] = ntl[t];
+        ms.count[w][t][1] = ntl[t] - nnl[t];
+        ms.count[w][t][2] = nnl[t];
       }
     }
     __syncthreads();
     if (threadIdx.x < NT) {
       const int t = threadIdx.x;
-      int tc = 0, tt = 0;
+      int tc = 0, tt = 0, tn = 0;
 #pragma unroll
       for (int q = 0; q < kWaves; ++q) {
         tc += ms.count[q][t][0];
         tt += ms.count[q][t][1];
+        tn += ms.count[q][t][2];
       }
-      const uint64_t old = (tc | tt) ? reserve_pair(s.counters + 2 * (b * NT + t), tc, tt) : 0;
+      const int r = b * NT + t;
+      const uint64_t old = (tc | tt) ? reserve_pair(s.counters + 2 * r, tc, tt) : 0;
       ms.base[t][0] = static_cast<int>(static_cast<uint32_t>(old));
       ms.base[t][1] = static_cast<int>(static_cast<uint32_t>(old >> 32));
+      ms.base[t][2] = tn ? static_cast<int>(atomicAdd(s.nearc + static_cast<int64_t>(r) * kRowWords,
+                                                      static_cast<uint32_t>(tn)))
+                         : 0;
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      int bc = ms.base[t][0], bt = ms.base[t][1];
+      int bc = ms.base[t][0], bt = ms.base[t][1], bn = ms.base[t][2];
       for (int q = 0; q < w; ++q) {
         bc += ms.count[q][t][0];
         bt += ms.count[q][t][1];
+        bn += ms.count[q][t][2];
       }
       const int r = b * NT + t;
       store_cands(s, r, bc, ms.cand[w][t], ncl[t]);
-      store_ties(s, r, bt, ms.tie[w][t], ntl[t]);
+      store_ties(s, r, bt, bn, thr[t], ms.tie[w][t], ntl[t]);
     }
+    PMQA_TR(sh, 2, b, 0);
     if (!s.ws) return;
     // arrival: this CTA's stores and counts are complete (written through)
     // before its count on the tile; the CTA that completes the count is last
@@ -2472,14 +2256,17 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
     __syncthreads();
     if (threadIdx.x == 0) sh.c->is_last = atomicAdd(s.arrivals + b, 1) + 1 == nctas;
     __syncthreads();
-    if (sh.c->is_last) {
+    PMQA_TR(sh, 3, b, sh.c->is_last);
+    was_last = sh.c->is_last != 0;
+    if (was_last) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       tile_finish<NT, kFused>(a, s, b, L, sh, rl);
+      PMQA_TR(sh, 5, b, 0);
     }
   });
   if (s.ws) {
     __syncthreads();
-    work_loop<NT, kFused>(a, s, lds);
+    work_loop<NT, kFused>(a, s, lds, !was_last);
   }
 }
 
@@ -2631,6 +2418,8 @@ SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int
   s.ws = arr ? static_cast<uint32_t*>(workspace) : nullptr;
   const WsLayout lay = workspace_layout(batch, rows, max_context, fused);
   s.ovf = s.ws ? reinterpret_cast<int32_t*>(s.ws + lay.overflow) : nullptr;
+  s.nearp = s.ws ? reinterpret_cast<int32_t*>(s.ws + lay.near) : nullptr;
+  s.nearc = s.ws ? s.ws + lay.row_state + 4 : nullptr;
   s.scores = s.ws && fused ? reinterpret_cast<float*>(s.ws + lay.scores) : nullptr;
   s.score_ld = score_stride(max_context);
   s.capacity = cap;
@@ -2676,6 +2465,41 @@ pmqa_status launch_k(int nt, hipStream_t st, A a, Rest... rest) {
     default: go(K<4>::fn); break;
   }
   return status;
+}
+
+// Zeroes words [0, n) of a workspace (a kernel, not a memset: callers may
+// capture the call in a graph).
+__global__ void __launch_bounds__(kThreads) clear_words_kernel(uint32_t* w, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+    w[i] = 0u;
+}
+
+// Every state word of the workspace (jobs, row states, histograms) is back to
+// zero when a call ends, but where they lie depends on the batch and next_n of
+// the call.  The library remembers the layout each workspace was last used
+// with and, when a call lays it out otherwise, clears the new layout's state
+// words first (one more launch on the same stream).
+pmqa_status prepare_workspace(void* ws, int64_t batch, int64_t rows, int64_t max_context, bool fused,
+                              hipStream_t st) {
+  static std::mutex mu;
+  static std::map<void*, std::vector<int64_t>> last;
+  const std::vector<int64_t> key{batch, rows};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = last.find(ws);
+    if (it == last.end()) {
+      last[ws] = key;  // first use: zeroed by the caller
+      return PMQA_OK;
+    }
+    if (it->second == key) return PMQA_OK;
+    it->second = key;
+  }
+  const int64_t n = workspace_layout(batch, rows, max_context, fused).bucket;  // jobs, row states, histograms
+  const int64_t g = std::min<int64_t>(1024, ceil_div(n, kThreads));
+  hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st,
+                     static_cast<uint32_t*>(ws), n);
+  return launched();
 }
 
 template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT>; };
@@ -2733,7 +2557,8 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
   const LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, 0, static_cast<int32_t>(gx)};
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
                                    batch_size, static_cast<int32_t>(rows), max_context, false, workspace);
-  st = launch_k<SelectK>(next_n, hs, a, s);
+  if (s.ws) st = prepare_workspace(workspace, batch_size, rows, max_context, false, hs);
+  if (st == PMQA_OK) st = launch_k<SelectK>(next_n, hs, a, s);
   return st != PMQA_OK ? st : launched();
 }
 
@@ -2763,8 +2588,19 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
                                  seq_lens_stride, block_size, batch_size, gx);
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
                                    batch_size, static_cast<int32_t>(rows), max_context, true, workspace);
-  st = launch_k<FusedK>(next_n, hs, a, s);
+  if (s.ws) st = prepare_workspace(workspace, batch_size, rows, max_context, true, hs);
+  if (st == PMQA_OK) st = launch_k<FusedK>(next_n, hs, a, s);
   return st != PMQA_OK ? st : launched();
 }
+
+#ifdef PMQA_TRACE
+int32_t pmqa_trace_read(void* host, size_t bytes) {
+  const size_t n = std::min(bytes, sizeof(g_trace));
+  if (hipMemcpyFromSymbol(host, HIP_SYMBOL(g_trace), n, 0, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  static const std::vector<uint64_t> zero(sizeof(g_trace) / sizeof(uint64_t), 0);
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_trace), zero.data(), sizeof(g_trace), 0, hipMemcpyHostToDevice) != hipSuccess) return -1;
+  return static_cast<int32_t>(n);
+}
+#endif
 
 }  // extern "C"

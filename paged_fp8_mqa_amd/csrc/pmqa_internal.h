@@ -17,45 +17,42 @@ constexpr int kOutColumnGranule = 256;  // padded_seq_len rounding
 constexpr int kRadixBins = 2048;        // radix digits: 10 + 11 + 11 bits from the top
 constexpr int kHistCopies = 4;          // repair workspace: copies of a row's radix histogram
 constexpr int kFinalizeLds = 4096;      // keys a CTA keeps in LDS for a final radix select
-constexpr int kBucketPairs = 4096;      // repair workspace: a row's bucket of keys at the k-th digit
+constexpr int kBucketPairs = 16384;     // repair workspace: a row's bucket of keys at the k-th digit
 constexpr int kOverflowPairs = 8192;    // repair workspace: a row's candidates past its capacity
+constexpr int kNearPairs = 4096;        // repair workspace: a row's keys just below its threshold
+constexpr uint32_t kNearBand = 1u << 15;  // the band below a threshold, in radix-key units (about 2^-8 of it)
 constexpr int kJobWords = 16;           // repair workspace: words per tile job
 constexpr int kRowWords = 16;           // repair workspace: words per row state
-constexpr int kHdrWords = 64;           // repair workspace: header words
-constexpr int kDoneFlags = 64;          // repair workspace: copies of the end-of-phase-A flag
-constexpr int kDoneFlagStride = 64;     // repair workspace: words between two copies (256 bytes)
 constexpr int kRescoreItemKeys = 2048;  // keys per repair item recomputed from the KV pages
 constexpr int kSelectItemKeys = 4096;   // keys per repair item read back as scores
 
 constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Repair job list: one word per tile, rounded up to keep the jobs 64-byte aligned.
-constexpr int64_t job_list_words(int64_t batch) { return (batch + 15) / 16 * 16; }
-
 // Floats per row of the fused repair's score buffer (256-byte rows).
 constexpr int64_t score_stride(int64_t max_context) { return ceil_div(max_context, 64) * 64; }
 
-// Workspace of the select entry points, in 32-bit words and in this order: a
-// header and the copies of the phase-A flag (zero between calls: the last CTA
-// of each call to leave clears them), the job list, one job per tile, then per
-// row -- each kind in an array of its own -- the state words, kHistCopies
-// radix histograms, the bucket of keys at the k-th digit and the candidates
-// past the capacity (kOverflowPairs pairs); the fused select adds a score row
-// of score_stride(max_context) floats per row, written only for rows whose
-// repair sweeps their keys again.
+// Workspace of the select entry points, in 32-bit words and in this order:
+// one job per tile, then per row -- each kind in an array of its own -- the
+// state words, kHistCopies radix histograms, the bucket of keys at the k-th
+// digit, the candidates past the capacity (kOverflowPairs pairs) and the keys
+// just below the threshold (kNearPairs pairs); the fused
+// select adds a score row of score_stride(max_context) floats per row, written
+// only for rows whose repair sweeps their keys again.  A job's claim words are
+// written by the job's publisher; every other word is set up before it is read
+// in the call that reads it, so the workspace needs zeroing only before its
+// first use.
 struct WsLayout {
-  int64_t hdr, list, jobs, row_state, hist, bucket, overflow, scores, end;
+  int64_t jobs, row_state, hist, bucket, overflow, near, scores, end;
 };
 constexpr WsLayout workspace_layout(int64_t batch, int64_t rows, int64_t max_context, bool fused) {
   WsLayout l{};
-  l.hdr = 0;
-  l.list = kHdrWords + kDoneFlags * kDoneFlagStride;
-  l.jobs = l.list + job_list_words(batch);
+  l.jobs = 0;
   l.row_state = l.jobs + kJobWords * batch;
   l.hist = l.row_state + kRowWords * rows;
   l.bucket = l.hist + static_cast<int64_t>(kHistCopies) * kRadixBins * rows;
   l.overflow = l.bucket + 2 * static_cast<int64_t>(kBucketPairs) * rows;
-  l.scores = l.overflow + 2 * static_cast<int64_t>(kOverflowPairs) * rows;
+  l.near = l.overflow + 2 * static_cast<int64_t>(kOverflowPairs) * rows;
+  l.scores = l.near + 2 * static_cast<int64_t>(kNearPairs) * rows;
   l.end = l.scores + (fused ? rows * score_stride(max_context) : 0);
   return l;
 }

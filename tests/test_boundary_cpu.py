@@ -68,7 +68,7 @@ def logits_args(**kw):
             a["D"], a["bs"], a["nb"], a["msl"], a["out"], a["outs"]]
 
 
-WS = 1 << 20
+WS = 1 << 23
 
 
 def select_args(**kw):
