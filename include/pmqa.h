@@ -55,7 +55,8 @@ typedef enum pmqa_status {
   PMQA_ERR_ALIGN = 5,       /* a pointer is not aligned as its entry point requires */
   PMQA_ERR_OVERFLOW = 6,    /* an output offset would not fit the 32-bit range */
   PMQA_ERR_LAUNCH = 7,      /* the HIP launch failed (no device, bad stream, ...) */
-  PMQA_ERR_CONTENT = 8      /* PMQA_VALIDATE=1 found a device-content precondition violated */
+  PMQA_ERR_CONTENT = 8,     /* PMQA_VALIDATE=1 found a device-content precondition violated */
+  PMQA_ERR_SCRATCH = 9      /* the call needs more workspace than the library's static scratch holds */
 } pmqa_status;
 
 /* Static string naming a status; never NULL. */
@@ -243,6 +244,41 @@ pmqa_status pmqa_fused_logits_select(
     int32_t capacity, int32_t top_k,
     int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pmqa_fused_logits_select_noalloc -- pmqa_fused_logits_select for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels, with the
+ * finish-stage workspace taken from a static device array of
+ * PMQA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on until the process ends.  The call itself allocates nothing.
+ *
+ *   Arguments and outputs as in pmqa_fused_logits_select, without workspace
+ *   and workspace_bytes.  The caller still owns and passes every input and
+ *   output buffer (thresholds, counters and arrivals zeroed as there).
+ *   PMQA_ERR_SCRATCH: with arrivals, pmqa_workspace_bytes(2, batch_size,
+ *   next_n, max_context) exceeds PMQA_NOALLOC_SCRATCH_BYTES (e.g. 32 requests
+ *   of next_n 4 over 65536 keys need about 64 MiB and fit; 64 such
+ *   requests do not);
+ *   nothing is launched.  The scratch is cleared by the library on its first
+ *   use on a device and whenever a call lays it out for another batch_size or
+ *   next_n (one extra fill kernel on the stream); otherwise each call leaves
+ *   it as the next call needs it.  All calls on one device share its scratch:
+ *   calls that overlap on a device (two streams, two threads) race and give
+ *   undefined results.  PMQA_VALIDATE is not honoured here (its check copies
+ *   to host memory).
+ */
+#define PMQA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+pmqa_status pmqa_fused_logits_select_noalloc(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_context,
+    float* thresholds, int32_t* counters, int32_t* candidates,
+    int32_t capacity, int32_t top_k,
+    int32_t* arrivals, int32_t* ranges, int32_t* topk_idx, void* stream);
 
 /* Keys scored per CTA by the logits/fused kernels and selected per CTA by the
  * indexer_topk kernel (at most batch_size x ceil(max_context / keys) CTAs). */

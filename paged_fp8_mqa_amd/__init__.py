@@ -14,6 +14,8 @@ Entry points mirror the C ABI in include/pmqa.h:
   fused_logits_select(q, kv_fused, weights, block_tables, seq_lens, max_context,
                thresholds, counters, candidates, capacity, top_k,
                arrivals=None, ranges=None, topk_idx=None, workspace=None)
+  fused_logits_select_noalloc(...)  as fused_logits_select, without workspace:
+               the library's static scratch (NOALLOC_SCRATCH_BYTES) serves
   make_workspace(which, batch_size, next_n, max_context)
                -> zeroed finish-stage workspace (required with arrivals)
 """
@@ -24,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpmqa.so"
 
 STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_NULL", 2: "PMQA_ERR_SHAPE", 3: "PMQA_ERR_STRIDE",
           4: "PMQA_ERR_UNSUPPORTED", 5: "PMQA_ERR_ALIGN", 6: "PMQA_ERR_OVERFLOW",
-          7: "PMQA_ERR_LAUNCH", 8: "PMQA_ERR_CONTENT"}
+          7: "PMQA_ERR_LAUNCH", 8: "PMQA_ERR_CONTENT", 9: "PMQA_ERR_SCRATCH"}
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -46,7 +48,10 @@ SIGNATURES = {
     "pmqa_indexer_topk": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT + [_P], ctypes.c_int),
     "pmqa_check_fused_args": (_PAGED + [_I32] + _SELECT_OUT, ctypes.c_int),
     "pmqa_fused_logits_select": (_PAGED + [_I32] + _SELECT_OUT + [_P], ctypes.c_int),
+    "pmqa_fused_logits_select_noalloc": (_PAGED + [_I32] + _SELECT_OUT[:-2] + [_P], ctypes.c_int),
 }
+
+NOALLOC_SCRATCH_BYTES = 96 << 20  # PMQA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -178,3 +183,14 @@ def fused_logits_select(q, kv_fused, weights, block_tables, seq_lens, max_contex
                                           *_select_out(thresholds, counters, candidates, capacity, top_k,
                                                        arrivals, ranges, topk_idx, workspace), _stream(stream)),
            "pmqa_fused_logits_select")
+
+
+def fused_logits_select_noalloc(q, kv_fused, weights, block_tables, seq_lens, max_context, thresholds, counters,
+                                candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None,
+                                block_size=None, stream=None):
+    """fused_logits_select with the library's static scratch as its workspace
+    (nothing is allocated; calls that overlap on one device race)."""
+    args, B, nn = _paged(q, kv_fused, weights, block_tables, seq_lens, block_size)
+    out = _select_out(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx, None)[:-2]
+    _check(lib().pmqa_fused_logits_select_noalloc(*args, int(max_context), *out, _stream(stream)),
+           "pmqa_fused_logits_select_noalloc")

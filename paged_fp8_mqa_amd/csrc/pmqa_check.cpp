@@ -72,6 +72,7 @@ const char* pmqa_status_string(int status) {
     case PMQA_ERR_OVERFLOW: return "PMQA_ERR_OVERFLOW: an output offset exceeds the 32-bit range";
     case PMQA_ERR_LAUNCH: return "PMQA_ERR_LAUNCH: the HIP launch failed";
     case PMQA_ERR_CONTENT: return "PMQA_ERR_CONTENT: PMQA_VALIDATE found a device-content precondition violated";
+    case PMQA_ERR_SCRATCH: return "PMQA_ERR_SCRATCH: the call needs more workspace than the static scratch holds";
     default: return "PMQA: unknown status";
   }
 }

@@ -2479,9 +2479,10 @@ __global__ void __launch_bounds__(kThreads) clear_words_kernel(uint32_t* w, int6
 // zero when a call ends, but where they lie depends on the batch and next_n of
 // the call.  The library remembers the layout each workspace was last used
 // with and, when a call lays it out otherwise, clears the new layout's state
-// words first (one more launch on the same stream).
+// words first (one more launch on the same stream); with clear_first_use it
+// does so also the first time it sees the workspace.
 pmqa_status prepare_workspace(void* ws, int64_t batch, int64_t rows, int64_t max_context, bool fused,
-                              hipStream_t st) {
+                              hipStream_t st, bool clear_first_use) {
   static std::mutex mu;
   static std::map<void*, std::vector<int64_t>> last;
   const std::vector<int64_t> key{batch, rows};
@@ -2489,17 +2490,52 @@ pmqa_status prepare_workspace(void* ws, int64_t batch, int64_t rows, int64_t max
     std::lock_guard<std::mutex> lock(mu);
     auto it = last.find(ws);
     if (it == last.end()) {
-      last[ws] = key;  // first use: zeroed by the caller
-      return PMQA_OK;
+      last[ws] = key;  // first use: zeroed by the caller, or cleared here
+      if (!clear_first_use) return PMQA_OK;
+    } else {
+      if (it->second == key) return PMQA_OK;
+      it->second = key;
     }
-    if (it->second == key) return PMQA_OK;
-    it->second = key;
   }
   const int64_t n = workspace_layout(batch, rows, max_context, fused).bucket;  // jobs, row states, histograms
   const int64_t g = std::min<int64_t>(1024, ceil_div(n, kThreads));
   hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st,
                      static_cast<uint32_t*>(ws), n);
   return launched();
+}
+
+// The finish-stage workspace of pmqa_fused_logits_select_noalloc, for callers
+// that cannot allocate.  Every device the library runs on holds its own copy
+// from the code object's load until the process ends.  Host code never passes
+// the array's name to a kernel or a copy (on the host it is only a stand-in
+// for the symbol): it uses the device address scratch_address() looked up.
+constexpr size_t kScratchBytes = PMQA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
+
+// Device address of `scratch` on device `dev`, looked up once per device with
+// that device current; nullptr if the lookup fails.
+void* scratch_address(int dev) {
+  static std::mutex mu;
+  static std::map<int, void*> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  cache[dev] = p;
+  return p;
 }
 
 template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT>; };
@@ -2557,19 +2593,25 @@ pmqa_status pmqa_indexer_topk(const float* logits, int64_t logits_stride, const 
   const LogitsArgs a{logits, logits_stride, seq_lens, seq_lens_stride, batch_size, 0, static_cast<int32_t>(gx)};
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
                                    batch_size, static_cast<int32_t>(rows), max_context, false, workspace);
-  if (s.ws) st = prepare_workspace(workspace, batch_size, rows, max_context, false, hs);
+  if (s.ws) st = prepare_workspace(workspace, batch_size, rows, max_context, false, hs, false);
   if (st == PMQA_OK) st = launch_k<SelectK>(next_n, hs, a, s);
   return st != PMQA_OK ? st : launched();
 }
 
-pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
-                                     const int32_t* block_tables, int64_t block_table_stride,
-                                     int32_t block_table_width, const int32_t* seq_lens, int64_t seq_lens_stride,
-                                     int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
-                                     int32_t block_size, int64_t num_blocks, int32_t max_context,
-                                     float* thresholds, int32_t* counters, int32_t* candidates, int32_t capacity,
-                                     int32_t top_k, int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pmqa_fused_logits_select with a choice: scratch_mode marks the library's
+// static scratch as the workspace (cleared on its first use per device, no
+// PMQA_VALIDATE host copies).
+pmqa_status fused_select(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+                         const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+                         const int32_t* seq_lens, int64_t seq_lens_stride, int32_t batch_size, int32_t next_n,
+                         int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                         int32_t max_context, float* thresholds, int32_t* counters, int32_t* candidates,
+                         int32_t capacity, int32_t top_k, int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
+                         void* workspace, size_t workspace_bytes, void* stream, bool scratch_mode) {
   pmqa_status st = pmqa_check_fused_args(q, kv_fused, weights, block_tables, block_table_stride,
                                          block_table_width, seq_lens, seq_lens_stride, batch_size, next_n,
                                          num_heads, head_dim, block_size, num_blocks, max_context, thresholds,
@@ -2581,16 +2623,64 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
   const int64_t gx = std::max<int64_t>(1, ceil_div(max_context, kFusedKeysPerCta));
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int64_t rows = static_cast<int64_t>(batch_size) * next_n;
-  st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_context, block_tables, block_table_stride,
-                        block_table_width, block_size, num_blocks, counters, rows, arrivals);
-  if (st != PMQA_OK) return st;
+  if (!scratch_mode) {
+    st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_context, block_tables, block_table_stride,
+                          block_table_width, block_size, num_blocks, counters, rows, arrivals);
+    if (st != PMQA_OK) return st;
+  }
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
   const SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx,
                                    batch_size, static_cast<int32_t>(rows), max_context, true, workspace);
-  if (s.ws) st = prepare_workspace(workspace, batch_size, rows, max_context, true, hs);
+  if (s.ws) st = prepare_workspace(workspace, batch_size, rows, max_context, true, hs, scratch_mode);
   if (st == PMQA_OK) st = launch_k<FusedK>(next_n, hs, a, s);
   return st != PMQA_OK ? st : launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+                                     const int32_t* block_tables, int64_t block_table_stride,
+                                     int32_t block_table_width, const int32_t* seq_lens, int64_t seq_lens_stride,
+                                     int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+                                     int32_t block_size, int64_t num_blocks, int32_t max_context,
+                                     float* thresholds, int32_t* counters, int32_t* candidates, int32_t capacity,
+                                     int32_t top_k, int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return fused_select(q, kv_fused, weights, block_tables, block_table_stride, block_table_width, seq_lens,
+                      seq_lens_stride, batch_size, next_n, num_heads, head_dim, block_size, num_blocks, max_context,
+                      thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx, workspace,
+                      workspace_bytes, stream, false);
+}
+
+pmqa_status pmqa_fused_logits_select_noalloc(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+                                             const int32_t* block_tables, int64_t block_table_stride,
+                                             int32_t block_table_width, const int32_t* seq_lens,
+                                             int64_t seq_lens_stride, int32_t batch_size, int32_t next_n,
+                                             int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                             int64_t num_blocks, int32_t max_context, float* thresholds,
+                                             int32_t* counters, int32_t* candidates, int32_t capacity, int32_t top_k,
+                                             int32_t* arrivals, int32_t* ranges, int32_t* topk_idx, void* stream) {
+  void* ws = nullptr;
+  size_t bytes = 0;
+  if (arrivals) {
+    // an invalid size gives 0 here and its own status from the argument check
+    if (pmqa_workspace_bytes(2, batch_size, next_n, max_context) > kScratchBytes) return PMQA_ERR_SCRATCH;
+    int dev = 0;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return PMQA_ERR_LAUNCH;
+    }
+    ws = scratch_address(dev);
+    if (!ws) return PMQA_ERR_LAUNCH;
+    bytes = kScratchBytes;
+  }
+  return fused_select(q, kv_fused, weights, block_tables, block_table_stride, block_table_width, seq_lens,
+                      seq_lens_stride, batch_size, next_n, num_heads, head_dim, block_size, num_blocks, max_context,
+                      thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx, ws, bytes,
+                      stream, true);
 }
 
 #ifdef PMQA_TRACE
