@@ -385,3 +385,34 @@ def test_repair_rescore_bits_equal_logits_kernel(next_n):
     for r, e in enumerate(ends):
         a, b = scores[r, :e].view(np.int32), logits[r, :e].view(np.int32)
         assert np.array_equal(a, b), f"row {r}: {int(np.sum(a != b))} of {e} scores differ in their bits"
+
+
+@pytest.mark.parametrize("next_n", [1, 2, 4])
+def test_fused_writes_no_scores_when_rows_fit(next_n):
+    """No score matrix in the fused path: with every row fitting (each
+    threshold below the row's k-th score by more than the logits error, and
+    room for every key above it), the score buffer at the end of the fused
+    workspace keeps a sentinel in every byte, and no row is repaired."""
+    wl = W.small_random(70 + next_n, [5000, 9000, 0, 3000], next_n, 64, top_k=256, capacity=1024)
+    ref, tau = _oracle_rows(wl, None)
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    thr = np.full(wl.rows, np.inf, np.float32)
+    for r, e in enumerate(ends):
+        if e == 0:
+            continue
+        s = np.sort(ref[r, :e])[::-1]
+        k = min(int(e), wl.top_k)
+        thr[r] = np.float32(s[k - 1] - 3 * tau[r])
+        assert np.sum(ref[r, :e] > thr[r] - tau[r]) <= wl.capacity, "test input: too many keys near the threshold"
+    import gpu_util
+    nbytes = pm.workspace_bytes("fused", wl.batch, wl.next_n, wl.max_seq_len)
+    score_bytes = wl.rows * (-(-wl.max_seq_len // 64) * 64) * 4
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    ws[nbytes - score_bytes:] = 0xA5
+    sb = gpu_util.SelectBuffers(wl.rows, wl.batch, wl.top_k, wl.capacity, thr, workspace=ws)
+    d = dev(wl)
+    pm.fused_logits_select(d["q"], d["kv"], d["w"], d["bt"], d["sl"], wl.max_seq_len, **sb.kwargs())
+    res = sb.host()
+    _check(wl, res, False, scores64=ref, tau=tau)
+    tail = ws[nbytes - score_bytes:].cpu().numpy()
+    assert np.all(tail == 0xA5), f"{int(np.sum(tail != 0xA5))} score-buffer bytes written"
