@@ -93,6 +93,43 @@ struct SelectArgs {
                         // without work then wait a while for repair items before they leave)
 };
 
+// Address-space views.  A generic pointer passed through in_global() is known
+// to the compiler to address global memory, and one derived from an LdsByte
+// pointer to address LDS, so their accesses compile to global_* and ds_*
+// instructions rather than flat_* ones (which wait on both the vector-memory
+// and the LDS counters, and reach LDS through the vector-memory path).
+typedef __attribute__((address_space(3))) char LdsByte;
+typedef __attribute__((address_space(1))) char GlobalByte;
+template <class T>
+__device__ __forceinline__ T* in_global(T* p) {
+  return (T*)((GlobalByte*)((char*)p));
+}
+
+__device__ __forceinline__ void global_view(PagedArgs& a) {
+  a.q = in_global(a.q);
+  a.kv = in_global(a.kv);
+  a.w = in_global(a.w);
+  a.bt = in_global(a.bt);
+  a.seq_lens = in_global(a.seq_lens);
+}
+__device__ __forceinline__ void global_view(LogitsArgs& a) {
+  a.logits = in_global(a.logits);
+  a.seq_lens = in_global(a.seq_lens);
+}
+__device__ __forceinline__ void global_view(SelectArgs& s) {
+  s.thresholds = in_global(s.thresholds);
+  s.counters = in_global(s.counters);
+  s.candidates = in_global(s.candidates);
+  s.arrivals = in_global(s.arrivals);
+  s.ranges = in_global(s.ranges);
+  s.topk_idx = in_global(s.topk_idx);
+  s.ws = in_global(s.ws);
+  s.ovf = in_global(s.ovf);
+  s.nearp = in_global(s.nearp);
+  s.nearc = in_global(s.nearc);
+  s.scores = in_global(s.scores);
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -103,6 +140,11 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 // Wavefront minimum (the device library's DPP reduction); every lane gets it.
 extern "C" __device__ uint64_t __ockl_wfred_min_u64(uint64_t);
+// Wavefront min / max / prefix sum by DPP lane moves (the device library's
+// reductions and scans; no LDS round trips).
+extern "C" __device__ uint32_t __ockl_wfred_min_u32(uint32_t);
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
+extern "C" __device__ uint32_t __ockl_wfscan_add_u32(uint32_t, bool inclusive);
 
 // s_waitcnt vmcnt(0): this wave's loads and stores have completed.
 __device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -116,16 +158,23 @@ __device__ __forceinline__ void wait_vm_done() { __builtin_amdgcn_s_waitcnt(0x0F
 constexpr int kTraceCtas = 2048;
 constexpr int kTraceSlots = 64;
 __device__ uint64_t g_trace[kTraceCtas * kTraceSlots];
-__device__ __forceinline__ void trace_event(int* n, int kind, int x, int y) {
-  if (threadIdx.x == 0 && blockIdx.x < kTraceCtas && *n < kTraceSlots) {
+// events are kept in the CTA's control words and written out when it ends, so
+// that the trace adds no global stores for later barriers to wait on
+template <class C>
+__device__ __forceinline__ void trace_event(C* c, int kind, int x, int y) {
+  if (threadIdx.x == 0 && c->trace_n < kTraceSlots) {
     const uint64_t t = __builtin_amdgcn_s_memrealtime();
-    g_trace[blockIdx.x * kTraceSlots + *n] = (static_cast<uint64_t>(kind & 0xff) << 56) |
-                                            (static_cast<uint64_t>(x & 0xffff) << 40) |
-                                            (static_cast<uint64_t>(y & 0xff) << 32) | (t & 0xffffffffu);
-    ++*n;
+    c->trace_ev[c->trace_n] = (static_cast<uint64_t>(kind & 0xff) << 56) | (static_cast<uint64_t>(x & 0xffff) << 40) |
+                              (static_cast<uint64_t>(y & 0xff) << 32) | (t & 0xffffffffu);
+    ++c->trace_n;
   }
 }
-#define PMQA_TR(sh, kind, x, y) trace_event(&(sh).c->trace_n, (kind), (x), (y))
+template <class C>
+__device__ __forceinline__ void trace_flush(C* c) {
+  if (threadIdx.x == 0 && blockIdx.x < kTraceCtas)
+    for (int i = 0; i < c->trace_n; ++i) g_trace[blockIdx.x * kTraceSlots + i] = c->trace_ev[i];
+}
+#define PMQA_TR(sh, kind, x, y) trace_event((sh).c, (kind), (x), (y))
 #else
 #define PMQA_TR(sh, kind, x, y) ((void)0)
 #endif
@@ -133,17 +182,37 @@ __device__ __forceinline__ void trace_event(int* n, int kind, int x, int y) {
 // Words shared between the CTAs of one kernel (on any XCD) are written with
 // agent-scope atomic stores, which the storing XCD's L2 writes through, and
 // read with agent-scope atomic loads.
+typedef __attribute__((address_space(1))) uint32_t GlobalU32;
+typedef __attribute__((address_space(1))) uint64_t GlobalU64;
+typedef __attribute__((address_space(3))) uint32_t LdsU32;
+typedef __attribute__((address_space(3))) int32_t LdsI32;
 __device__ __forceinline__ uint32_t ld_ag(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((const GlobalU32*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_ag64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((const GlobalU64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_wt(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((GlobalU32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_wt64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((GlobalU64*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A slot pair (key index, score bits) from global memory, as one 8-byte load.
+__device__ __forceinline__ int2 ld_pair(const int32_t* p) {
+  const uint64_t v = *(const GlobalU64*)p;
+  return make_int2(static_cast<int>(static_cast<uint32_t>(v)), static_cast<int>(static_cast<uint32_t>(v >> 32)));
+}
+
+// Agent-scope atomic adds on global memory; they return the old value.
+__device__ __forceinline__ uint32_t add_ag(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add((GlobalU32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t add_ag(int32_t* p, int32_t v) {
+  return static_cast<int32_t>(add_ag(reinterpret_cast<uint32_t*>(p), static_cast<uint32_t>(v)));
+}
+__device__ __forceinline__ uint64_t add_ag64(uint64_t* p, uint64_t v) {
+  return __hip_atomic_fetch_add((GlobalU64*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
@@ -611,7 +680,7 @@ __device__ __forceinline__ float near_floor(float t) {
 // both counts stay below the row's length, under 2^31.
 __device__ __forceinline__ uint64_t reserve_pair(int32_t* pair, int nc, int nt) {
   const uint64_t add = (static_cast<uint64_t>(static_cast<uint32_t>(nt)) << 32) | static_cast<uint32_t>(nc);
-  return atomicAdd(reinterpret_cast<unsigned long long*>(pair), static_cast<unsigned long long>(add));
+  return add_ag64(reinterpret_cast<uint64_t*>(pair), add);
 }
 
 // A slot store is an agent-scope (relaxed) atomic store: the L2 of the
@@ -622,7 +691,7 @@ __device__ __forceinline__ uint64_t reserve_pair(int32_t* pair, int nc, int nt) 
 // costs on every CTA.
 __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
   const uint64_t packed = (static_cast<uint64_t>(__float_as_uint(v)) << 32) | static_cast<uint32_t>(idx);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(slot), packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((GlobalU64*)slot, packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 
@@ -630,6 +699,9 @@ __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
 template <int NT>
 struct Ctl {
   uint32_t wtot[kWaves];
+  uint32_t wmin[kWaves];
+  uint32_t wmax[kWaves];
+  uint32_t sink[64];  // a final select's discarded histogram adds, one word per lane
   uint32_t dig[2];
   int32_t wcnt[NT][kWaves][2];
   int32_t wbase[NT][kWaves][2];
@@ -648,6 +720,9 @@ struct Ctl {
   int32_t job[3];      // claimed repair item: tile (or -1: none open, -2: leave), stage, index
   int32_t next_stage;
   int32_t trace_n;  // events recorded by this CTA (trace builds only)
+#ifdef PMQA_TRACE
+  uint64_t trace_ev[kTraceSlots];
+#endif
 };
 
 // The finish work's view of a CTA's LDS: per-row radix histograms (rh, NT of
@@ -772,41 +847,45 @@ __device__ __forceinline__ int pass_bits(int pass) { return pass == 0 ? 10 : 11;
 // thread whose bins reach krem walks them.  The histogram's total is at least
 // krem.  Returns the same values in every thread.
 template <int NT>
-__device__ __forceinline__ void cta_find_digit(const uint32_t* hist, int nb, uint32_t krem, const Sh<NT>& sh,
-                                               uint32_t& digit, uint32_t& rem) {
+__device__ __forceinline__ void cta_find_digit(uint32_t* hist, int nb, uint32_t krem, const Sh<NT>& sh,
+                                               uint32_t& digit, uint32_t& rem, bool zero_after = false) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = wave_id();
   const int per = nb / kThreads;  // 4 or 8
+  // thread t holds the per bins below nb - per * t, so that a prefix sum over
+  // the threads in order counts from the top bin down
+  const int b0 = nb - per * (tid + 1);
   uint32_t h[8];
-  const uint4 lo = *reinterpret_cast<const uint4*>(hist + tid * per);
-  const uint4 hi = per == 8 ? *reinterpret_cast<const uint4*>(hist + tid * per + 4) : uint4{0u, 0u, 0u, 0u};
+  const uint4 lo = *reinterpret_cast<const uint4*>(hist + b0);
+  const uint4 hi = per == 8 ? *reinterpret_cast<const uint4*>(hist + b0 + 4) : uint4{0u, 0u, 0u, 0u};
   h[0] = lo.x; h[1] = lo.y; h[2] = lo.z; h[3] = lo.w;
   h[4] = hi.x; h[5] = hi.y; h[6] = hi.z; h[7] = hi.w;
   uint32_t local = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) local += h[i];
-  uint32_t incl = local;  // over lanes >= this lane
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(incl, off);
-    if (lane + off < 64) incl += y;
-  }
-  if (lane == 0) sh.c->wtot[w] = incl;
+  const uint32_t incl = __ockl_wfscan_add_u32(local, true);  // this and the earlier lanes: higher bins
+  if (lane == 63) sh.c->wtot[w] = incl;
   if (tid == 0) {
     sh.c->dig[0] = 0u;
     sh.c->dig[1] = 0u;
   }
   __syncthreads();
+  // every bin is read: the histogram can be cleared for a next pass (cleared
+  // by the barrier below)
+  if (zero_after) {
+    reinterpret_cast<uint4*>(hist + b0)[0] = uint4{0u, 0u, 0u, 0u};
+    if (per == 8) reinterpret_cast<uint4*>(hist + b0)[1] = uint4{0u, 0u, 0u, 0u};
+  }
   uint32_t above = incl - local;
-  for (int q = w + 1; q < kWaves; ++q) above += sh.c->wtot[q];
+  for (int q = 0; q < w; ++q) above += sh.c->wtot[q];
   if (above < krem && krem <= above + local) {
     uint32_t acc = above;
     bool found = false;
 #pragma unroll
     for (int i = 7; i >= 0; --i) {
       if (!found && i < per && acc + h[i] >= krem) {
-        sh.c->dig[0] = static_cast<uint32_t>(tid * per + i);
+        sh.c->dig[0] = static_cast<uint32_t>(b0 + i);
         sh.c->dig[1] = krem - acc;
         found = true;
       }
@@ -833,6 +912,7 @@ __device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, u
     #pragma unroll 1
     for (int i = tid; i < kRadixBins; i += kThreads) hist[i] = 0u;
     __syncthreads();
+    PMQA_TR(sh, 21, n, pass);
     #pragma unroll 1
     for (int i0 = 0; i0 < n; i0 += 4 * kThreads) {
       // four keys a thread per round, their LDS reads in flight together (the
@@ -863,8 +943,10 @@ __device__ __forceinline__ void cta_radix_select(KeyOf&& key_of, int n, int k, u
       }
     }
     __syncthreads();
+    PMQA_TR(sh, 22, 0, pass);
     uint32_t d, rem;
     cta_find_digit(hist, 1 << bits, krem, sh, d, rem);
+    PMQA_TR(sh, 23, 0, pass);
     pf = pass == 0 ? d : ((pf << bits) | d);
     krem = rem;
   }
@@ -883,15 +965,8 @@ template <int NT>
 __device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, const Sh<NT>& sh) {
   const int lane = lane_id();
   const int w = wave_id();
-  uint32_t ia = a, ib = b;  // inclusive within the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t ya = __shfl_up(ia, off), yb = __shfl_up(ib, off);
-    if (lane >= off) {
-      ia += ya;
-      ib += yb;
-    }
-  }
+  const uint32_t ia = __ockl_wfscan_add_u32(a, true);  // inclusive within the wave
+  const uint32_t ib = __ockl_wfscan_add_u32(b, true);
   __syncthreads();
   if (lane == 63) {
     sh.c->wtot[w] = ia;
@@ -905,6 +980,101 @@ __device__ __forceinline__ void cta_exclusive_scan2(uint32_t& a, uint32_t& b, co
   }
   a = ba + ia - a;
   b = bb + ib - b;
+}
+
+// The k-th largest (1 <= k <= n <= fin_cap) of the radix keys of the score
+// bits in LDS (sh.fk[0 .. n)), by radix select over the bits where the keys
+// differ: their common prefix (from the least and greatest key) is skipped,
+// then 11-bit digits from the top of the rest, one histogram pass each (two
+// for keys spread over at most 22 bits; none when all are equal).  Each pass
+// reads the keys in runs of four per thread (one 16-byte LDS read), two runs
+// at a time (the reads past n stay inside the final-select area and are not
+// counted).
+template <int NT>
+__device__ __forceinline__ uint32_t lds_select(int n, int k, const Sh<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = wave_id();
+  constexpr int kPer = 4;  // keys a thread takes per run: one 16-byte LDS read
+  constexpr int kRun = kPer * kThreads;
+  typedef uint32_t U32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) U32x4 LdsU32x4;
+  auto run = [&](int c, uint32_t (&x)[kPer]) {
+    const U32x4 a = *(const LdsU32x4*)((LdsByte*)((char*)(sh.fk + c * kRun + kPer * tid)));
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) x[u] = radix_key(__uint_as_float(a[u]));
+  };
+  uint32_t* hist = sh.fh;
+  // the first pass's histogram cleared by the same barrier as the extremes
+  for (int i = tid; i < kRadixBins / 4; i += kThreads) reinterpret_cast<uint4*>(hist)[i] = uint4{0u, 0u, 0u, 0u};
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll 1
+  for (int c = 0; c * kRun < n; ++c) {
+    uint32_t x[kPer];
+    run(c, x);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const bool in = c * kRun + kPer * tid + u < n;
+      mn = min(mn, in ? x[u] : 0xffffffffu);
+      mx = max(mx, in ? x[u] : 0u);
+    }
+  }
+  mn = __ockl_wfred_min_u32(mn);
+  mx = __ockl_wfred_max_u32(mx);
+  if (lane == 0) {
+    sh.c->wmin[w] = mn;
+    sh.c->wmax[w] = mx;
+  }
+  __syncthreads();
+  mn = sh.c->wmin[0];
+  mx = sh.c->wmax[0];
+#pragma unroll
+  for (int q = 1; q < kWaves; ++q) {
+    mn = min(mn, sh.c->wmin[q]);
+    mx = max(mx, sh.c->wmax[q]);
+  }
+  PMQA_TR(sh, 21, n, 0);
+  int hi = mn == mx ? 0 : 32 - __clz(static_cast<int>(mn ^ mx));  // the low bits where keys differ
+  uint32_t pf = hi == 32 ? 0u : mn >> hi;                          // the bits above them, shared
+  uint32_t krem = static_cast<uint32_t>(k);
+  uint32_t* sink = sh.c->sink + lane;
+#pragma unroll 1
+  while (hi > 0) {
+    const int shift = hi > 11 ? hi - 11 : 0;
+    const int bits = hi - shift;
+    const uint32_t high = hi == 32 ? 0u : ~0u << hi;  // the bits decided so far, and their value
+    const uint32_t want = hi == 32 ? 0u : pf << hi;
+    const uint32_t low = (1u << bits) - 1u;
+    // two runs at a time, their reads in flight together
+#pragma unroll 1
+    for (int c = 0; c * kRun < n; c += 2) {
+      uint32_t x[2 * kPer];
+      uint32_t(&x0)[kPer] = *reinterpret_cast<uint32_t(*)[kPer]>(x);
+      uint32_t(&x1)[kPer] = *reinterpret_cast<uint32_t(*)[kPer]>(x + kPer);
+      run(c, x0);
+      run(c + 1, x1);
+      // one LDS add per key, every lane: keys outside the pass (or past n) add
+      // to the lane's own sink word, so that no lane masking separates the adds
+      uint32_t* at[2 * kPer];
+#pragma unroll
+      for (int u = 0; u < 2 * kPer; ++u) {
+        const int i = (c + u / kPer) * kRun + kPer * tid + u % kPer;
+        const bool in = i < n && (x[u] & high) == want;
+        at[u] = in ? hist + ((x[u] >> shift) & low) : sink;
+      }
+#pragma unroll
+      for (int u = 0; u < 2 * kPer; ++u) atomicAdd(at[u], 1u);
+    }
+    __syncthreads();
+    PMQA_TR(sh, 22, hi, 0);
+    uint32_t d, rem;
+    cta_find_digit(hist, kRadixBins, krem, sh, d, rem, shift > 0);
+    PMQA_TR(sh, 23, 0, 0);
+    pf = (pf << bits) | d;
+    krem = rem;
+    hi = shift;
+  }
+  return pf;
 }
 
 // ---------------------------------------------------------------- row finish
@@ -923,14 +1093,14 @@ __device__ __forceinline__ void load_pairs(const int32_t* a, int n1, const int32
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int i = i0 + u * kThreads + tid;
-      if (i < n) v[u] = *reinterpret_cast<const int2*>(i < n1 ? a + 2 * i : b + 2 * (i - n1));
+      if (i < n) v[u] = ld_pair(i < n1 ? a + 2 * i : b + 2 * (i - n1));
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int i = i0 + u * kThreads + tid;
       if (i < n) {
-        sh.fi[i] = v[u].x;
-        sh.fk[i] = dec(static_cast<uint32_t>(v[u].y));
+        ((LdsI32*)sh.fi)[i] = v[u].x;
+        ((LdsU32*)sh.fk)[i] = dec(static_cast<uint32_t>(v[u].y));
       }
     }
   }
@@ -950,8 +1120,8 @@ struct PairSrc {
 
 template <int NT>
 __device__ __forceinline__ int2 pair_at(const PairSrc& ps, int i, const Sh<NT>& sh) {
-  if (ps.lds) return make_int2(sh.fi[i], static_cast<int>(sh.fk[i]));
-  int2 p = *reinterpret_cast<const int2*>(ps.g + 2 * i);
+  if (ps.lds) return make_int2(((const LdsI32*)sh.fi)[i], static_cast<int>(((const LdsU32*)sh.fk)[i]));
+  int2 p = ld_pair(ps.g + 2 * i);
   if (ps.dec) p.y = __float_as_int(dec_cand(__int_as_float(p.y), ps.th));
   return p;
 }
@@ -966,8 +1136,13 @@ template <int NT>
 __device__ __forceinline__ uint32_t kth_scan(const PairSrc& ps, int n, int k, const Sh<NT>& sh, uint32_t& og,
                                              uint32_t& oe, int& n_gt, int& n_eq) {
   auto key_of = [&](int i) { return radix_key(__int_as_float(pair_at<NT>(ps, i, sh).y)); };
-  cta_radix_select(key_of, n, k, sh.fh, sh);
-  const uint32_t kstar = sh.c->pfx[0];
+  uint32_t kstar;
+  if (ps.lds) {
+    kstar = lds_select<NT>(n, k, sh);
+  } else {
+    cta_radix_select(key_of, n, k, sh.fh, sh);
+    kstar = sh.c->pfx[0];
+  }
   uint32_t gt = 0u, eq = 0u;
 #pragma unroll 1
   for (int i = threadIdx.x; i < n; i += kThreads) {
@@ -975,6 +1150,7 @@ __device__ __forceinline__ uint32_t kth_scan(const PairSrc& ps, int n, int k, co
     gt += key > kstar ? 1u : 0u;
     eq += key == kstar ? 1u : 0u;
   }
+  PMQA_TR(sh, 24, 0, 0);
   og = gt;
   oe = eq;
   cta_exclusive_scan2(og, oe, sh);
@@ -1520,7 +1696,7 @@ __device__ __forceinline__ void item_done(const SelectArgs& s, const Ws& ws, int
   __syncthreads();
   PMQA_TR(sh, 11, 0, stage);
   if (tid == 0)
-    sh.c->is_last = atomicAdd(ws.done_word(b, stage), 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
+    sh.c->is_last = add_ag(ws.done_word(b, stage), 1u) + 1 == static_cast<uint32_t>(stage_items<NT, kFused>(stage, L));
   __syncthreads();
   PMQA_TR(sh, 12, sh.c->is_last, stage);
   if (!sh.c->is_last) return;
@@ -1611,8 +1787,8 @@ __device__ __forceinline__ void rescore_item(const PagedArgs& a, const SelectArg
     uint32_t* gh = ws.hist(b * NT + t, copy);
     for (int i = tid; i < kWords; i += kThreads) {
       const uint32_t h = rl.ph[t * kWords + i];
-      if (h & 0xffffu) atomicAdd(gh + 2 * i, h & 0xffffu);
-      if (h >> 16) atomicAdd(gh + 2 * i + 1, h >> 16);
+      if (h & 0xffffu) add_ag(gh + 2 * i, h & 0xffffu);
+      if (h >> 16) add_ag(gh + 2 * i + 1, h >> 16);
     }
   }
 }
@@ -1721,7 +1897,7 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
         uint32_t* gh = ws.hist(r, idx % kHistCopies);
         for (int i = tid; i < (1 << bits); i += kThreads) {
           const uint32_t x = h[i];
-          if (x) atomicAdd(gh + i, x);
+          if (x) add_ag(gh + i, x);
         }
         __syncthreads();
       } else if (stage == kStageCollect) {
@@ -1735,8 +1911,8 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
               const uint32_t top = radix_key(e) >> (32 - known);
               return top > pf ? 1 : (top == pf ? 2 : 0);
             },
-            [&](int n) { return atomicAdd(s.counters + 2 * r, n); },
-            [&](int n) { return static_cast<int>(atomicAdd(ws.row(r) + 3, static_cast<uint32_t>(n))); },
+            [&](int n) { return add_ag(s.counters + 2 * r, n); },
+            [&](int n) { return static_cast<int>(add_ag(ws.row(r) + 3, static_cast<uint32_t>(n))); },
             [&](int c, int k, int p, float e) {
               if (c == 1 && k < s.capacity) store_pair(cslots + 2 * k, p, e);
               if (c == 2 && k < kBucketPairs) store_pair(bucket + 2 * k, p, e);
@@ -1746,8 +1922,8 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
         int32_t* slots = s.candidates + static_cast<int64_t>(r) * (s.top_k + s.capacity) * 2;
         append_row<NT, kU>(
             c0, lim, v, sh, [&](float e) { return e > th2 ? 1 : (!(e < th2) ? 2 : 0); },
-            [&](int n) { return atomicAdd(s.counters + 2 * r, n); },
-            [&](int n) { return atomicAdd(s.counters + 2 * r + 1, n); },
+            [&](int n) { return add_ag(s.counters + 2 * r, n); },
+            [&](int n) { return add_ag(s.counters + 2 * r + 1, n); },
             [&](int c, int k, int p, float e) {
               if (c == 1 && k < s.capacity) store_pair(slots + 2 * (s.top_k + k), p, enc_cand(e, th2));
               if (c == 2 && k < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - k), p, e - th2);
@@ -1795,7 +1971,7 @@ __device__ __forceinline__ void claim_item(const Args& a, const SelectArgs& s, c
           const int bl = j0 + l;
           const int ll = __shfl(len, l);
           unsigned long long old = 0;
-          if (lane == 0) old = atomicAdd(reinterpret_cast<unsigned long long*>(ws.claim(bl, q)), 1ull);
+          if (lane == 0) old = add_ag64(reinterpret_cast<uint64_t*>(ws.claim(bl, q)), 1ull);
           old = __shfl(old, 0);
           const uint32_t st2 = static_cast<uint32_t>(old >> 32);
           const uint64_t i2 = q + kClaimWords * static_cast<uint64_t>(static_cast<uint32_t>(old));
@@ -1836,10 +2012,12 @@ __device__ __forceinline__ void work_loop(const Args& a, const SelectArgs& s, ch
     // round, so that no address derived from them is hoisted out of the loop
     // (the compiler would keep hundreds of them live across the items, and
     // spill them)
-    char* base = lds;
-    asm volatile("" : "+v"(base));
-    uint32_t* wsb = s.ws;
-    asm volatile("" : "+s"(wsb));
+    uint32_t lo = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LdsByte*)lds));
+    asm volatile("" : "+v"(lo));
+    char* base = (char*)((LdsByte*)lo);
+    uint64_t wv = reinterpret_cast<uint64_t>(s.ws);
+    asm volatile("" : "+s"(wv));
+    uint32_t* wsb = in_global(reinterpret_cast<uint32_t*>(wv));
     const Ws ws{wsb, a.batch, s.rows};
     const Sh<NT> sh = make_sh<NT>(base, Lay::kFinCap, Lay::kCtlOff);
     const RescoreLds<NT> rl{reinterpret_cast<v4i*>(base), reinterpret_cast<QLds<NT>*>(base + Lay::kStageBytes),
@@ -2055,6 +2233,8 @@ template <int NT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
 logits_kernel(PagedArgs a, float* out, int64_t ld) {
   __shared__ v4i stage[kWaves * kStageInt4];
+  global_view(a);
+  out = in_global(out);
   if constexpr (NT >= 3) {
     __shared__ QLds<NT> ql;
     logits_body<NT, KvSourceQ<NT>>(a, out, ld, stage, &ql);
@@ -2161,7 +2341,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
       uint32_t nb = 0;
       if (lane == 0) {
         old = reserve_pair(s.counters + 2 * r, ncl[t], ntl[t] - nnl[t]);
-        if (nnl[t]) nb = atomicAdd(s.nearc + static_cast<int64_t>(r) * kRowWords, static_cast<uint32_t>(nnl[t]));
+        if (nnl[t]) nb = add_ag(s.nearc + static_cast<int64_t>(r) * kRowWords, static_cast<uint32_t>(nnl[t]));
       }
       const int bc = __shfl(static_cast<int>(static_cast<uint32_t>(old)), 0);
       const int bt = __shfl(static_cast<int>(static_cast<uint32_t>(old >> 32)), 0);
@@ -2231,7 +2411,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
       const uint64_t old = (tc | tt) ? reserve_pair(s.counters + 2 * r, tc, tt) : 0;
       ms.base[t][0] = static_cast<int>(static_cast<uint32_t>(old));
       ms.base[t][1] = static_cast<int>(static_cast<uint32_t>(old >> 32));
-      ms.base[t][2] = tn ? static_cast<int>(atomicAdd(s.nearc + static_cast<int64_t>(r) * kRowWords,
+      ms.base[t][2] = tn ? static_cast<int>(add_ag(s.nearc + static_cast<int64_t>(r) * kRowWords,
                                                       static_cast<uint32_t>(tn)))
                          : 0;
     }
@@ -2254,7 +2434,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
     // before its count on the tile; the CTA that completes the count is last
     wait_vm_done();
     __syncthreads();
-    if (threadIdx.x == 0) sh.c->is_last = atomicAdd(s.arrivals + b, 1) + 1 == nctas;
+    if (threadIdx.x == 0) sh.c->is_last = add_ag(s.arrivals + b, 1) + 1 == nctas;
     __syncthreads();
     PMQA_TR(sh, 3, b, sh.c->is_last);
     was_last = sh.c->is_last != 0;
@@ -2275,16 +2455,23 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
 fused_kernel(PagedArgs a, SelectArgs s) {
   using Lay = Layout<NT, true>;
   __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
+  global_view(a);
+  global_view(s);
   if constexpr (NT >= 3)
     select_body<NT, true, kFusedKeysPerCta, KvSourceQ<NT>>(a, s, lds);
   else
     select_body<NT, true, kFusedKeysPerCta, KvSource<NT>>(a, s, lds);
+#ifdef PMQA_TRACE
+  trace_flush(reinterpret_cast<Ctl<NT>*>(lds + Lay::kCtlOff));
+#endif
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectArgs s) {
   using Lay = Layout<NT, false>;
   __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
+  global_view(a);
+  global_view(s);
   select_body<NT, false, kSelectKeysPerCta, LogitsSource<NT>>(a, s, lds);
 }
 
