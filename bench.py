@@ -1,23 +1,27 @@
 """Benchmark of the paged FP8 MQA logits + threshold Top-k select hot path.
 
 One step = one pmqa_fused_logits_select call over the whole batch of a
-synthetic workload: the select kernel (logits and candidate/tie select) and
-the finish kernel (fit test, repair, ranges and exact Top-k), with every input
-already resident in HBM.  Each step gets its own pre-zeroed counters and
-pristine thresholds (prepared before the timed region) and cycles through
-`--replicas` copies of the KV pool, so no step finds its pool in the 256 MiB
-Infinity Cache.
+synthetic workload: one kernel launch that scores every visible (row, KV
+position) pair, selects candidates and ties against the row thresholds, and
+finishes every tile (fit test, radix-select repair, ranges and exact Top-k),
+with every input already resident in HBM.  Each step gets its own pre-zeroed
+counters and pristine thresholds (prepared before the timed region) and cycles
+through `--replicas` copies of the KV pool, so no step finds its pool in the
+256 MiB Infinity Cache.
 
 Prints one JSON line:
   value          pairs/s: sum over rows of visible KV positions, per second
   rows_per_s     rows selected (and finalized) per second
-  roofline       the select kernel (the dominant one): algorithmic HBM bytes
-                 per launch over its average launch time -- one HIP event pair
-                 on its stream around the same steps run with the finish stage
-                 off, divided by the step count -- against 8 TB/s
+  roofline       the call's kernel (the only launch of a step): algorithmic HBM
+                 bytes per launch over its average launch time -- one HIP event
+                 pair on the launch stream around the timed steps, divided by
+                 the step count -- against 8 TB/s; traffic from the committed
+                 rocprofv3 FETCH_SIZE / WRITE_SIZE summary when it was taken on
+                 this kernel source
   cpu_baseline   the float64 CPU oracle on a bounded sample of the workload
 
     python bench.py [--steps K] [--warmup W] [--workload 3|4|5] [--path fused|unfused]
+                    [--main-leg]   also time the same kernel without the finish stage
 """
 import argparse
 import hashlib
@@ -128,6 +132,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for HBM counter calibration)")
+    ap.add_argument("--main-leg", action="store_true",
+                    help="also time the steps without the finish stage (the main pass alone; another launch "
+                         "configuration of the same kernel, so it stays out of the default run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -202,12 +209,14 @@ def main():
     assert int(arrivals.abs().sum()) == 0, "arrivals not left zeroed"
     repaired = int((thr_all[-1].cpu().numpy().view(np.int32) != thr0.view(np.int32)).sum())
 
-    # the same steps with the finish stage off: the select kernel alone, for
-    # its roofline (fresh counters, same KV replicas in the same order)
-    reset()
-    for i in range(args.warmup):
-        step(i, finish=False)
-    select_ms_mean = timed(False)
+    main_ms_mean = None
+    if args.main_leg:
+        # the same steps with the finish stage off: the main pass alone (fresh
+        # counters, same KV replicas in the same order)
+        reset()
+        for i in range(args.warmup):
+            step(i, finish=False)
+        main_ms_mean = timed(False)
 
     # per-call spread, as context: an event pair around each call
     reset()
@@ -222,18 +231,6 @@ def main():
     torch.cuda.synchronize()
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
-    # one warm (same pool every step) measurement as context
-    warm = []
-    thr_dev = torch.from_numpy(thr0).to(dev)
-    for j in range(5):
-        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cnt_all[0].zero_()
-        thr_all[0].copy_(thr_dev)
-        a.record(stream)
-        step(0)
-        b_.record(stream)
-        torch.cuda.synchronize()
-        warm.append(a.elapsed_time(b_))
 
     if args.calib_copy_mib:
         # a plain elementwise kernel that reads and writes exactly calib_copy_mib MiB
@@ -250,7 +247,6 @@ def main():
     call_s = ms_step / 1e3
     achieved = alg / call_s / 1e9
     flops = 2.0 * 64 * 128 * pairs
-    sel_s = select_ms_mean / 1e3
     out = {
         "metric": METRIC,
         "value": pairs / (ms_step / 1e3),
@@ -272,18 +268,20 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(args.workload, args.path),
                      "algorithmic_bytes_per_launch": alg,
-                     "kernel": "whole call (every kernel of one step)",
-                     "launch_ms": {"mean": ms_step},
-                     "mfma_frac": flops / call_s / 1e12 / FP8_PEAK_TFLOPS,
-                     "select_kernel": {"ms": select_ms_mean, "frac": alg / sel_s / 1e9 / HBM_PEAK_GBS,
-                                       "mfma_frac": flops / sel_s / 1e12 / FP8_PEAK_TFLOPS}},
-        "call_ms": {"mean": ms_step, "finish_stage_mean": ms_step - select_ms_mean,
-                    "per_call_events": {"p10": float(np.percentile(launch_ms, 10)),
-                                        "p50": float(np.percentile(launch_ms, 50)),
-                                        "p90": float(np.percentile(launch_ms, 90))}},
-        "warm_ms_per_step": float(np.median(warm)),
+                     "kernel": ("fused_kernel<%d>" % wl.next_n) if args.path == "fused"
+                               else "logits_kernel + select_kernel",
+                     "launch_us": ms_step * 1e3,
+                     "mfma_frac": flops / call_s / 1e12 / FP8_PEAK_TFLOPS},
+        "call_us": {"mean": ms_step * 1e3,
+                    "per_call_events": {"p10": float(np.percentile(launch_ms, 10)) * 1e3,
+                                        "p50": float(np.percentile(launch_ms, 50)) * 1e3,
+                                        "p90": float(np.percentile(launch_ms, 90)) * 1e3}},
         "kernel_src_sha": kernel_hash(),
     }
+    if main_ms_mean is not None:
+        out["main_pass_us"] = main_ms_mean * 1e3
+        out["finish_stage_us"] = (ms_step - main_ms_mean) * 1e3
+        out["main_pass_frac"] = alg / (main_ms_mean / 1e3) / 1e9 / HBM_PEAK_GBS
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, thr0, args.cpu_seconds)
     else:
