@@ -702,6 +702,8 @@ struct Ctl {
   uint32_t wmin[kWaves];
   uint32_t wmax[kWaves];
   uint32_t sink[64];  // a final select's discarded histogram adds, one word per lane
+  uint64_t wmin64[2][kWaves];  // few-extra rounds: each wave's least (key, slot), double-buffered
+  uint32_t left_out[8];        // few-extra rounds: the left-out slots
   uint32_t dig[2];
   int32_t wcnt[NT][kWaves][2];
   int32_t wbase[NT][kWaves][2];
@@ -1164,6 +1166,71 @@ __device__ __forceinline__ uint32_t kth_scan(const PairSrc& ps, int n, int k, co
   return kstar;
 }
 
+// Top-k of a fitting row with a few candidates past k (1 <= nc - k <=
+// kFewExtra, nc <= kFewPer * kThreads): every candidate but the nc - k
+// smallest, by stored score and then slot.  The stored candidate values order
+// as the scores do (the encoding maps (t, 2t] onto (0, t] and keeps the rest,
+// with t > 0), so their radix keys are the order.  Thread t holds the keys of
+// slots t + kThreads * u in registers; each round takes the CTA's least (key, slot)
+// among those not yet left out (a wavefront minimum, then the four waves'
+// through LDS; one barrier a round).  The kept indices are then written in
+// slot order shifted past the left-out slots -- entries before the first
+// left-out slot already hold their index (the main pass writes candidate
+// j < top_k to entry j).
+constexpr int kFewExtra = 8;  // at most the control words' left_out entries
+constexpr int kFewPer = 16;
+
+template <int NT>
+__device__ __forceinline__ void few_extra_topk(const SelectArgs& s, int r, int k, int nc, const Sh<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int32_t* cand = s.candidates + (static_cast<int64_t>(r) * (s.top_k + s.capacity) + s.top_k) * 2;
+  int32_t* out = s.topk_idx + static_cast<int64_t>(r) * s.top_k;
+  const int d = nc - k;
+  uint32_t key[kFewPer];
+#pragma unroll
+  for (int u = 0; u < kFewPer; ++u) {
+    key[u] = 0xffffffffu;  // above every radix key (+inf's is 0xff800000)
+    if (u * kThreads < nc) {
+      const int i = u * kThreads + tid;
+      const uint32_t v = *(const GlobalU32*)(cand + 2 * min(i, nc - 1) + 1);
+      if (i < nc) key[u] = radix_key(__uint_as_float(v));
+    }
+  }
+  uint32_t gone = 0u;  // this thread's left-out units
+#pragma unroll 1
+  for (int j = 0; j < d; ++j) {
+    uint64_t m = ~0ull;
+#pragma unroll
+    for (int u = 0; u < kFewPer; ++u) {
+      const uint64_t v = (static_cast<uint64_t>(key[u]) << 32) | static_cast<uint32_t>(u * kThreads + tid);
+      if (!((gone >> u) & 1u)) m = min(m, v);
+    }
+    m = __ockl_wfred_min_u64(m);
+    if (lane == 0) sh.c->wmin64[j & 1][w] = m;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) m = min(m, sh.c->wmin64[j & 1][q]);
+    const uint32_t slot = static_cast<uint32_t>(m);
+    if (tid == 0) sh.c->left_out[j] = slot;
+    if (static_cast<int>(slot % kThreads) == tid) gone |= 1u << (slot / kThreads);
+  }
+  __syncthreads();
+  uint32_t first = 0xffffffffu;
+  for (int j = 0; j < d; ++j) first = min(first, sh.c->left_out[j]);
+#pragma unroll
+  for (int u = 0; u < kFewPer; ++u) {
+    const uint32_t i = static_cast<uint32_t>(u * kThreads + tid);
+    if (u * kThreads < nc && i < static_cast<uint32_t>(nc) && !((gone >> u) & 1u) &&
+        (i > first || i >= static_cast<uint32_t>(s.top_k))) {
+      uint32_t shift = 0u;
+      for (int j = 0; j < d; ++j) shift += sh.c->left_out[j] < i ? 1u : 0u;
+      out[i - shift] = *(const GlobalU32*)(cand + 2 * i);  // the slot's key index, read again
+    }
+  }
+}
+
 // Ranges and exact Top-k of a fitting row r (k = min(e_r, top_k)) with nc
 // candidates, nt ties and threshold th: all candidates when there are at most
 // k of them, completed with ties from the tie slots (cands_out: the candidates'
@@ -1187,6 +1254,10 @@ __device__ __forceinline__ void fit_row_outputs(const SelectArgs& s, int r, int 
 #pragma unroll 1
       for (int i = (cands_out ? nc : 0) + tid; i < k; i += kThreads)
         out[i] = i < nc ? cand[2 * i] : slots[2 * (s.top_k - 1 - (i - nc))];
+    } else if (NT == 1 && cands_out && nc - k <= kFewExtra && nc <= kFewPer * kThreads) {
+      // (next_n = 1 only: in the kernels for more rows the extra registers
+      // cost the main loop more than this path saves)
+      few_extra_topk<NT>(s, r, k, nc, sh);
     } else {
       // nc <= capacity (the row fits)
       const bool lds = nc <= sh.fin_cap;
@@ -2015,9 +2086,11 @@ __device__ __forceinline__ void work_loop(const Args& a, const SelectArgs& s, ch
     uint32_t lo = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LdsByte*)lds));
     asm volatile("" : "+v"(lo));
     char* base = (char*)((LdsByte*)lo);
-    uint64_t wv = reinterpret_cast<uint64_t>(s.ws);
-    asm volatile("" : "+s"(wv));
-    uint32_t* wsb = in_global(reinterpret_cast<uint32_t*>(wv));
+    const uint64_t wv = reinterpret_cast<uint64_t>(s.ws);
+    uint32_t wlo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(wv));
+    uint32_t whi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(wv >> 32));
+    asm volatile("" : "+s"(wlo), "+s"(whi));
+    uint32_t* wsb = in_global(reinterpret_cast<uint32_t*>((static_cast<uint64_t>(whi) << 32) | wlo));
     const Ws ws{wsb, a.batch, s.rows};
     const Sh<NT> sh = make_sh<NT>(base, Lay::kFinCap, Lay::kCtlOff);
     const RescoreLds<NT> rl{reinterpret_cast<v4i*>(base), reinterpret_cast<QLds<NT>*>(base + Lay::kStageBytes),
