@@ -14,9 +14,10 @@
  *   - All buffer pointers are DEVICE pointers on the device that owns `stream`
  *     (a hipStream_t; NULL is the null stream).  The caller owns every buffer:
  *     the library never allocates, frees or synchronises the host, and each
- *     call is one kernel launch on `stream`, two for a select with arrivals
- *     (the select kernel, then the finish kernel), with no host round trip
- *     (so it can be captured in a HIP graph).
+ *     call is one kernel launch on `stream` with no host round trip (so it can
+ *     be captured in a HIP graph).  A select call whose workspace was last laid
+ *     out for another batch_size or next_n first launches one small kernel that
+ *     clears the workspace's state words.
  *   - Rows: R = batch_size * next_n, row r = b*next_n + t pairs with q[b, t].
  *     Row r sees KV positions 0 .. e_r - 1 with e_r = seq_lens[b] - next_n + t + 1
  *     (at least 0): slot t = next_n-1 is the newest draft position and sees the
@@ -141,15 +142,19 @@ pmqa_status pmqa_mqa_logits(
  *                (exact, and order-keeping), else s; for a tie s - t.
  *   capacity     >= 0 candidate slots per row.
  *   top_k        >= 1; also the number of tie slots.
- *   arrivals     [batch_size] int32 or NULL: the per-tile arrival counters of
- *                the pages' calling convention.  Non-NULL turns on the finish
- *                stage: every row that does not fit (n_cand > capacity or
- *                n_cand + min(n_tie, top_k) < min(e_r, top_k)) is selected again
- *                at its radix-selected min(e_r, top_k)-th largest score (with
- *                capacity >= top_k - 1 every row then fits), and ranges and
- *                topk_idx are written.  This implementation finishes the tiles
- *                in a second kernel on the same stream, so the buffer is never
- *                read or written (it stays zeroed).  With NULL no repair runs and
+ *   arrivals     [batch_size] int32 or NULL, zeroed by the caller once and
+ *                left zeroed by every call: the per-tile arrival counters.  A
+ *                tile is one request's next_n rows.  Each CTA that scores a
+ *                share of a tile's keys counts itself on arrivals[b] once its
+ *                candidate and tie stores are complete; the CTA that completes
+ *                the count sets it back to zero and finishes the tile in the
+ *                same launch.  Finishing means: every row that does not fit
+ *                (n_cand > capacity or n_cand + min(n_tie, top_k) <
+ *                min(e_r, top_k)) is selected again at its radix-selected
+ *                min(e_r, top_k)-th largest score (with capacity >= top_k - 1
+ *                every row then fits), and ranges and topk_idx are written.  A
+ *                repair too large for one CTA becomes items that the launch's
+ *                other CTAs claim.  With NULL no repair runs and
  *                ranges/topk_idx must be NULL.
  *   ranges       [2, R] int32, required with arrivals, output: slots
  *                [ranges[0][r], ranges[1][r]) hold the row's ties and candidates
@@ -162,30 +167,27 @@ pmqa_status pmqa_mqa_logits(
  *   workspace    pmqa_workspace_bytes(which, batch_size, next_n, max_context)
  *                bytes of device memory, 8-byte aligned, required with arrivals
  *                (NULL without).  Zeroed by the caller before its first use;
- *                after that the library keeps state in it from call to call,
- *                so the caller leaves it alone (zeroing it again is harmless).
- *                It holds the finish stage, a second kernel launched by the
- *                same call on the same stream with as many CTAs as fit on the
- *                device: each tile's fit test, then ranges and Top-k, or a
- *                repair job for its rows that do not fit (per-row radix
- *                histogram passes, then a collect pass into a per-row bucket
- *                buffer, or an exact re-select), split into items of a few
- *                thousand keys run grid-wide.  The fused select keeps scores
- *                in the workspace's score buffer: with next_n = 1 its repair
- *                computes a repaired row's scores once, in its first pass, for
- *                the later passes; with next_n >= 2 the select kernel writes
- *                every row's scores there and the repair reads them as the
- *                repair of pmqa_indexer_topk reads its logits matrix.  Calls
- *                that share a workspace must not run concurrently.
+ *                after that the library keeps state in it from call to call, so
+ *                the caller leaves it alone (zeroing it again is harmless).
+ *                Every call leaves its state words (tile jobs, row states,
+ *                radix histograms) back at zero; a call laid out for another
+ *                batch_size or next_n clears them first (above).  It also holds
+ *                per row a bucket of keys at the k-th digit, the candidates past
+ *                capacity (up to 8192 per row, so a row with too many
+ *                candidates is re-selected from its stored pairs without a
+ *                sweep), and the keys in a narrow band just below the
+ *                threshold (up to 4096 per row, for rows a few keys short).
+ *                The fused select adds a score buffer of round_up(max_context,
+ *                64) floats per row, written only for rows whose repair sweeps
+ *                their keys again: no score matrix is written for fitting rows.
+ *                Calls that share a workspace must not run concurrently.
  */
 
 /* Bytes of the finish-stage workspace of entry point `which` (1
  * pmqa_indexer_topk, 2 pmqa_fused_logits_select) for batch_size requests of
- * next_n rows and max_context keys: the finish stage's state (about 98 KB per
- * row), plus for the fused select a score buffer of
- * round_up(max_context, 64) floats per row (the scores of the repaired rows
- * with next_n = 1, of every row with next_n >= 2).  Returns 0 for an unknown
- * `which` or a negative size. */
+ * next_n rows and max_context keys: 64 bytes per tile, about 256 KB of state
+ * per row, plus for the fused select a score buffer of round_up(max_context,
+ * 64) floats per row.  Returns 0 for an unknown `which` or a negative size. */
 size_t pmqa_workspace_bytes(int32_t which, int32_t batch_size, int32_t next_n, int32_t max_context);
 
 pmqa_status pmqa_check_select_args(
@@ -216,8 +218,8 @@ pmqa_status pmqa_indexer_topk(
 /*
  * pmqa_fused_logits_select -- logits and select in one launch: each CTA scores
  * its share of a request's keys exactly as pmqa_mqa_logits does (same
- * arithmetic, bit for bit) and selects them without storing the scores; the
- * repair recomputes the scores of the request it repairs.  Arguments as in
+ * arithmetic, bit for bit) and selects them without storing the scores; a
+ * repair that sweeps a tile's keys again recomputes their scores.  Arguments as in
  * pmqa_mqa_logits (minus out/out_stride/max_seq_len) and the select arguments
  * above; block_table_width >= ceil(max_context / block_size) (the table has
  * to reach max_context keys: page "flashinfer.sdsa.indexer_threshold_select",
