@@ -20,7 +20,7 @@ Prints one JSON line:
                  this kernel source
   cpu_baseline   the float64 CPU oracle on a bounded sample of the workload
 
-    python bench.py [--steps K] [--warmup W] [--workload 3|4|5] [--path fused|unfused]
+    python bench.py [--steps K] [--warmup W] [--workload 3|4|5|prefill] [--path fused|unfused]
                     [--main-leg]   also time the same kernel without the finish stage
 """
 import argparse
@@ -120,12 +120,111 @@ def cpu_baseline(wl, thresholds, budget_s):
             "sample": f"first {reqs} of {wl.batch} requests of {wl.name} ({pairs} pairs, {rows} rows) in {dt:.1f}s"}
 
 
+def bench_prefill(args, dev):
+    """The prefill chunk through pmqa_prefill_select: one launch per step over
+    prefill-shaped rows (tiles of 4 rows of one request, causal row ends).  Its
+    keys (2.3 MB) stay in the caches across the tiles that share a request, so
+    the bound is the FP8 MFMA work, 16384 FLOP per (row, key) pair."""
+    wl = W.prefill_chunk()
+    d = json.load(open(os.path.join(GOLDEN, "thresholds_prefill_chunk.json")))
+    if d["fingerprint"] != W.prefill_fingerprint(wl):
+        raise SystemExit("prefill workload does not match its stored thresholds (generator drift)")
+    thr0 = np.array(d["threshold_bits"], dtype=np.int32).view(np.float32)
+    R, T = wl.rows, wl.tiles
+    pairs = int(np.maximum(wl.row_ends, 0).astype(np.int64).sum())
+    q = torch.from_numpy(wl.q).to(dev)
+    w = torch.from_numpy(wl.weights).to(dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    treq = torch.from_numpy(wl.tile_requests).to(dev)
+    re_ = torch.from_numpy(wl.row_ends).to(dev)
+    kv = torch.from_numpy(wl.kv_fused).to(dev).view(wl.num_blocks, wl.block_size, 1, 132)
+    total = args.warmup + args.steps
+    thr_all = torch.from_numpy(np.tile(thr0, (total, 1))).to(dev)
+    cnt_all = torch.zeros(total, R, 2, dtype=torch.int32, device=dev)
+    cand = torch.empty(R, wl.top_k + wl.capacity, 2, dtype=torch.int32, device=dev)
+    arrivals = torch.zeros(T, dtype=torch.int32, device=dev)
+    ranges = torch.empty(2, R, dtype=torch.int32, device=dev)
+    topk = torch.empty(R, wl.top_k, dtype=torch.int32, device=dev)
+    ws = pm.make_workspace("fused", T, wl.tile_rows, wl.max_context, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        pm.prefill_select(q, kv, w, bt, treq, re_, wl.tile_rows, wl.max_context, thr_all[i], cnt_all[i], cand,
+                          wl.capacity, wl.top_k, arrivals, ranges, topk, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for j in range(args.steps):
+        step(args.warmup + j)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    assert int(arrivals.abs().sum()) == 0, "arrivals not left zeroed"
+    repaired = int((thr_all[-1].cpu().numpy().view(np.int32) != thr0.view(np.int32)).sum())
+    flops = 2.0 * 64 * 128 * pairs
+    tflops = flops / (ms_step / 1e3) / 1e12
+    kv_bytes = int(wl.seq_lens.astype(np.int64).sum()) * 132
+    out = {
+        "metric": METRIC, "value": pairs / (ms_step / 1e3), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3 x fp8_e4m3 -> f32", "data": "synthetic (seeded generators, workloads/)",
+        "config": {"workload": wl.name, "path": "prefill", "tiles": T, "tile_rows": wl.tile_rows, "rows": R,
+                   "pairs": pairs, "top_k": wl.top_k, "capacity": wl.capacity, "block_size": wl.block_size,
+                   "parallelism": "single GPU"},
+        "rows_per_s": R / (ms_step / 1e3),
+        "repaired_rows": repaired,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP8_PEAK_TFLOPS, "traffic": None, "kernel": "fused_kernel<4>",
+                     "launch_us": ms_step * 1e3, "flop_per_launch": flops,
+                     "kv_bytes_per_launch_once": kv_bytes},
+        "kernel_src_sha": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = prefill_cpu_baseline(wl, thr0, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def prefill_cpu_baseline(wl, thresholds, budget_s):
+    """The oracle on the first tiles of the prefill chunk, until about budget_s
+    seconds of CPU work."""
+    import oracle
+    from oracle.select import select_with_repair
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    pairs = rows = tiles = 0
+    t0 = time.perf_counter()
+    for i in range(wl.tiles):
+        rs = list(range(i * wl.tile_rows, (i + 1) * wl.tile_rows))
+        sc = oracle.prefill_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.tile_requests, wl.row_ends,
+                                   wl.tile_rows, wl.block_size, wl.max_context, rows=rs)
+        for r in rs:
+            e = int(wl.row_ends[r])
+            if e > 0:
+                select_with_repair(sc[r, :e].astype(np.float32), e, thresholds[r], wl.top_k, wl.capacity)
+                pairs += e
+                rows += 1
+        tiles += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": int(cores), "kind": "oracle", "rows_per_s": rows / dt,
+            "sample": f"first {tiles} of {wl.tiles} tiles of {wl.name} ({pairs} pairs, {rows} rows) in {dt:.1f}s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5])
+    ap.add_argument("--workload", default="4", choices=["3", "4", "5", "prefill"])
     ap.add_argument("--path", default="fused", choices=["fused", "unfused"])
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -142,6 +241,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     pm.lib()
+    if args.workload == "prefill":
+        return bench_prefill(args, dev)
+    args.workload = int(args.workload)
 
     wl = W.make(args.workload)
     thr0 = load_thresholds(args.workload, wl)

@@ -248,6 +248,55 @@ pmqa_status pmqa_fused_logits_select(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pmqa_prefill_select -- the fused select over prefill-shaped rows (page
+ * "flashinfer.sdsa.indexer_threshold_select", the signature and the
+ * parameters row_ends and tile_requests): rows come in query tiles of
+ * tile_rows rows that all belong to one request, each row has its own key
+ * end, and several tiles may share a request (the causal rows of a prompt).
+ * The pages build 128-row tiles for their hardware's matrix tile; here a tile
+ * is the 1 to 4 rows whose scores share one pass over the request's keys, as
+ * the next_n rows of a decode request do (the same kernels).
+ *
+ *   q            [num_tiles*tile_rows, num_heads, head_dim] e4m3fn bytes, row
+ *                r = tile*tile_rows + t, contiguous, 16-byte aligned.
+ *   weights      [num_tiles*tile_rows, num_heads] f32.
+ *   block_tables int32 [num_requests rows of block_table_stride], as in
+ *                pmqa_mqa_logits; block_table_width >= ceil(max_context /
+ *                block_size).
+ *   tile_requests int32 [num_tiles]: tile i's request, a row of block_tables.
+ *   row_ends     int32 [num_tiles*tile_rows]: row r sees keys p < row_ends[r]
+ *                of its tile's request (0 <= row_ends[r] <= max_context; a row
+ *                with 0 sees nothing).  A tile streams keys up to its largest
+ *                row end, so that many of its request's keys must be valid.
+ *   Row r's score at key p is the pmqa_mqa_logits formula with q[r] and
+ *   weights[r]; the select arguments are those of pmqa_fused_logits_select
+ *   with e_r = row_ends[r], batch_size = num_tiles and next_n = tile_rows
+ *   (arrivals [num_tiles]; workspace pmqa_workspace_bytes(2, num_tiles,
+ *   tile_rows, max_context) bytes).
+ *   Errors as in pmqa_fused_logits_select; PMQA_VALIDATE=1 also checks
+ *   row_ends and tile_requests against max_context and num_requests.
+ */
+pmqa_status pmqa_check_prefill_args(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width, int32_t num_requests,
+    const int32_t* tile_requests, const int32_t* row_ends, int32_t num_tiles, int32_t tile_rows,
+    int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_context,
+    const float* thresholds, const int32_t* counters, const int32_t* candidates,
+    int32_t capacity, int32_t top_k,
+    const int32_t* arrivals, const int32_t* ranges, const int32_t* topk_idx,
+    const void* workspace, size_t workspace_bytes);
+
+pmqa_status pmqa_prefill_select(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width, int32_t num_requests,
+    const int32_t* tile_requests, const int32_t* row_ends, int32_t num_tiles, int32_t tile_rows,
+    int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_context,
+    float* thresholds, int32_t* counters, int32_t* candidates,
+    int32_t capacity, int32_t top_k,
+    int32_t* arrivals, int32_t* ranges, int32_t* topk_idx,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pmqa_fused_logits_select_noalloc -- pmqa_fused_logits_select for callers
  * that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): the same kernels, with the

@@ -16,6 +16,11 @@ Entry points mirror the C ABI in include/pmqa.h:
                arrivals=None, ranges=None, topk_idx=None, workspace=None)
   fused_logits_select_noalloc(...)  as fused_logits_select, without workspace:
                the library's static scratch (NOALLOC_SCRATCH_BYTES) serves
+  prefill_select(q, kv_fused, weights, block_tables, tile_requests, row_ends, tile_rows,
+               max_context, thresholds, counters, candidates, capacity, top_k,
+               arrivals=None, ranges=None, topk_idx=None, workspace=None)
+               the fused select over prefill-shaped rows (query tiles of tile_rows
+               rows of one request each, explicit row ends)
   make_workspace(which, batch_size, next_n, max_context)
                -> zeroed finish-stage workspace (required with arrivals)
 """
@@ -35,6 +40,9 @@ _SZ = ctypes.c_size_t
 
 _PAGED = [_P, _P, _P, _P, _I64, _I32, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64]
 _SELECT_OUT = [_P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ]
+# q, kv, weights, block_tables, stride, width, num_requests, tile_requests, row_ends, num_tiles, tile_rows,
+# heads, dim, block_size, num_blocks, max_context
+_PREFILL = [_P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32]
 SIGNATURES = {
     "pmqa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pmqa_version": ([], _I32),
@@ -49,6 +57,8 @@ SIGNATURES = {
     "pmqa_check_fused_args": (_PAGED + [_I32] + _SELECT_OUT, ctypes.c_int),
     "pmqa_fused_logits_select": (_PAGED + [_I32] + _SELECT_OUT + [_P], ctypes.c_int),
     "pmqa_fused_logits_select_noalloc": (_PAGED + [_I32] + _SELECT_OUT[:-2] + [_P], ctypes.c_int),
+    "pmqa_check_prefill_args": (_PREFILL + _SELECT_OUT, ctypes.c_int),
+    "pmqa_prefill_select": (_PREFILL + _SELECT_OUT + [_P], ctypes.c_int),
 }
 
 NOALLOC_SCRATCH_BYTES = 96 << 20  # PMQA_NOALLOC_SCRATCH_BYTES
@@ -194,3 +204,39 @@ def fused_logits_select_noalloc(q, kv_fused, weights, block_tables, seq_lens, ma
     out = _select_out(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx, None)[:-2]
     _check(lib().pmqa_fused_logits_select_noalloc(*args, int(max_context), *out, _stream(stream)),
            "pmqa_fused_logits_select_noalloc")
+
+
+def prefill_select(q, kv_fused, weights, block_tables, tile_requests, row_ends, tile_rows, max_context, thresholds,
+                   counters, candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None, workspace=None,
+                   block_size=None, stream=None):
+    """The fused select over prefill-shaped rows: q [rows, H, D] (or [tiles,
+    tile_rows, H, D]), tile i's rows on request tile_requests[i], row r seeing
+    keys below row_ends[r].  With arrivals ([tiles]), pass a workspace from
+    make_workspace("fused", tiles, tile_rows, max_context)."""
+    if q.dim() == 4:
+        q = q.reshape(-1, q.shape[2], q.shape[3])
+    R, H, D = q.shape
+    if kv_fused.dim() == 4:
+        bs = kv_fused.shape[1]
+    else:
+        if block_size is None:
+            raise ValueError("block_size is needed for a 2-D kv_fused")
+        bs = block_size
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be 2-D with contiguous rows")
+    if not q.is_contiguous() or not weights.is_contiguous() or not kv_fused.is_contiguous():
+        raise ValueError("q, weights and kv_fused must be contiguous")
+    if not tile_requests.is_contiguous() or not row_ends.is_contiguous():
+        raise ValueError("tile_requests and row_ends must be contiguous")
+    T = int(tile_rows)
+    if T < 1 or R % T:
+        raise ValueError("rows must be a multiple of tile_rows")
+    tiles = R // T
+    if tile_requests.numel() != tiles or row_ends.numel() != R:
+        raise ValueError("tile_requests must hold one entry per tile and row_ends one per row")
+    args = [_ptr(q), _ptr(kv_fused), _ptr(weights), _ptr(block_tables), block_tables.stride(0),
+            block_tables.shape[1], block_tables.shape[0], _ptr(tile_requests), _ptr(row_ends), tiles, T, H, D, bs,
+            kv_fused.shape[0], int(max_context)]
+    _check(lib().pmqa_prefill_select(*args, *_select_out(thresholds, counters, candidates, capacity, top_k,
+                                                        arrivals, ranges, topk_idx, workspace), _stream(stream)),
+           "pmqa_prefill_select")

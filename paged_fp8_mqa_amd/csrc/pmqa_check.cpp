@@ -170,4 +170,25 @@ pmqa_status pmqa_check_fused_args(const uint8_t* q, const uint8_t* kv_fused, con
   return PMQA_OK;
 }
 
+pmqa_status pmqa_check_prefill_args(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+                                    const int32_t* block_tables, int64_t block_table_stride,
+                                    int32_t block_table_width, int32_t num_requests,
+                                    const int32_t* tile_requests, const int32_t* row_ends, int32_t num_tiles,
+                                    int32_t tile_rows, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                    int64_t num_blocks, int32_t max_context, const float* thresholds,
+                                    const int32_t* counters, const int32_t* candidates, int32_t capacity,
+                                    int32_t top_k, const int32_t* arrivals, const int32_t* ranges,
+                                    const int32_t* topk_idx, const void* workspace, size_t workspace_bytes) {
+  // the fused select's checks, with the row ends in place of the lengths
+  pmqa_status st = pmqa_check_fused_args(q, kv_fused, weights, block_tables, block_table_stride, block_table_width,
+                                         row_ends, 1, num_tiles, tile_rows, num_heads, head_dim, block_size,
+                                         num_blocks, max_context, thresholds, counters, candidates, capacity, top_k,
+                                         arrivals, ranges, topk_idx, workspace, workspace_bytes);
+  if (st != PMQA_OK || num_tiles == 0) return st;
+  if (num_requests < 1) return PMQA_ERR_SHAPE;
+  if (!tile_requests) return PMQA_ERR_NULL;
+  if (!aligned(tile_requests, 4)) return PMQA_ERR_ALIGN;
+  return PMQA_OK;
+}
+
 }  // extern "C"

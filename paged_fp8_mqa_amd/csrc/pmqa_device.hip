@@ -61,6 +61,10 @@ struct PagedArgs {
   int32_t batch;
   int32_t locate;       // balanced grid over all requests' keys (else per_request CTAs per request)
   int32_t per_request;
+  // prefill-shaped rows (both null for decode rows): tile b's rows b*NT + t
+  // see keys below row_ends[b*NT + t] of request tile_req[b]
+  const int32_t* row_ends;
+  const int32_t* tile_req;
 };
 
 struct LogitsArgs {
@@ -91,6 +95,7 @@ struct SelectArgs {
   int32_t rows;
   int32_t resident;     // 1 when every CTA of the launch fits on the device at once (CTAs
                         // without work then wait a while for repair items before they leave)
+  const int32_t* row_ends;  // prefill-shaped rows: each row's key end (null: derived from the length)
 };
 
 // Address-space views.  A generic pointer passed through in_global() is known
@@ -111,6 +116,8 @@ __device__ __forceinline__ void global_view(PagedArgs& a) {
   a.w = in_global(a.w);
   a.bt = in_global(a.bt);
   a.seq_lens = in_global(a.seq_lens);
+  a.row_ends = in_global(a.row_ends);
+  a.tile_req = in_global(a.tile_req);
 }
 __device__ __forceinline__ void global_view(LogitsArgs& a) {
   a.logits = in_global(a.logits);
@@ -128,6 +135,33 @@ __device__ __forceinline__ void global_view(SelectArgs& s) {
   s.nearp = in_global(s.nearp);
   s.nearc = in_global(s.nearc);
   s.scores = in_global(s.scores);
+  s.row_ends = in_global(s.row_ends);
+}
+
+// The keys tile b streams: its request's length for decode rows, the largest
+// of its rows' ends for prefill-shaped rows.
+template <int NT>
+__device__ __forceinline__ int tile_keys(const PagedArgs& a, int b) {
+  if (a.row_ends) {
+    int m = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) m = max(m, a.row_ends[static_cast<int64_t>(b) * NT + t]);
+    return m;
+  }
+  return a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+}
+template <int NT>
+__device__ __forceinline__ int tile_keys(const LogitsArgs& a, int b) {
+  return a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+}
+
+// Row t of tile b (L keys streamed) sees keys below its end: L - NT + t + 1
+// for decode rows (page "flashinfer.attn_scores", Note), row_ends[r] for
+// prefill-shaped rows (page "flashinfer.sdsa.indexer_threshold_select",
+// Parameters: row_ends).
+template <int NT>
+__device__ __forceinline__ int row_end(const SelectArgs& s, int b, int L, int t) {
+  return s.row_ends ? max(0, s.row_ends[static_cast<int64_t>(b) * NT + t]) : max(0, L - NT + t + 1);
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -276,7 +310,8 @@ struct KvStream {
     n = lane & 15;
     g = lane >> 4;
     kv = a.kv;
-    bt_row = a.bt + static_cast<int64_t>(b) * a.bt_stride;
+    const int req = a.tile_req ? a.tile_req[b] : b;
+    bt_row = a.bt + static_cast<int64_t>(req) * a.bt_stride;
     bs_shift = a.bs_shift;
     bs_mask = (1 << a.bs_shift) - 1;
     block_bytes = a.block_bytes;
@@ -1138,31 +1173,39 @@ template <int NT>
 __device__ __forceinline__ uint32_t kth_scan(const PairSrc& ps, int n, int k, const Sh<NT>& sh, uint32_t& og,
                                              uint32_t& oe, int& n_gt, int& n_eq) {
   auto key_of = [&](int i) { return radix_key(__int_as_float(pair_at<NT>(ps, i, sh).y)); };
-  uint32_t kstar;
-  if (ps.lds) {
-    kstar = lds_select<NT>(n, k, sh);
-  } else {
-    cta_radix_select(key_of, n, k, sh.fh, sh);
-    kstar = sh.c->pfx[0];
-  }
-  uint32_t gt = 0u, eq = 0u;
+  uint32_t kstar = 0u;
+  // The class counts check the k-th key found: fewer than k keys above it and
+  // at least k at or above it.  Should the prefix-skipping select ever miss
+  // that, the three fixed passes select again over the same keys.
 #pragma unroll 1
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const uint32_t key = key_of(i);
-    gt += key > kstar ? 1u : 0u;
-    eq += key == kstar ? 1u : 0u;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (ps.lds && attempt == 0) {
+      kstar = lds_select<NT>(n, k, sh);
+    } else {
+      cta_radix_select(key_of, n, k, sh.fh, sh);
+      kstar = sh.c->pfx[0];
+    }
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll 1
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const uint32_t key = key_of(i);
+      gt += key > kstar ? 1u : 0u;
+      eq += key == kstar ? 1u : 0u;
+    }
+    PMQA_TR(sh, 24, 0, 0);
+    og = gt;
+    oe = eq;
+    cta_exclusive_scan2(og, oe, sh);
+    if (threadIdx.x == kThreads - 1) {
+      sh.c->pos[0] = static_cast<int>(og + gt);
+      sh.c->pos[1] = static_cast<int>(oe + eq);
+    }
+    __syncthreads();
+    n_gt = sh.c->pos[0];
+    n_eq = sh.c->pos[1];
+    if (!ps.lds || (n_gt < k && k <= n_gt + n_eq)) break;
+    PMQA_TR(sh, 25, n_gt, 0);
   }
-  PMQA_TR(sh, 24, 0, 0);
-  og = gt;
-  oe = eq;
-  cta_exclusive_scan2(og, oe, sh);
-  if (threadIdx.x == kThreads - 1) {
-    sh.c->pos[0] = static_cast<int>(og + gt);
-    sh.c->pos[1] = static_cast<int>(oe + eq);
-  }
-  __syncthreads();
-  n_gt = sh.c->pos[0];
-  n_eq = sh.c->pos[1];
   return kstar;
 }
 
@@ -1306,7 +1349,7 @@ __device__ __forceinline__ void tile_fit(const SelectArgs& s, int b, int L, cons
     const int nt = static_cast<int>(ld_ag(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
     const int nn = s.nearc ? static_cast<int>(ld_ag(s.nearc + static_cast<int64_t>(r) * kRowWords)) : 0;
     const float th = __uint_as_float(ld_ag(reinterpret_cast<const uint32_t*>(s.thresholds) + r));
-    const int k = min(max(0, L - NT + tid + 1), s.top_k);
+    const int k = min(row_end<NT>(s, b, L, tid), s.top_k);
     const bool fit = nc <= s.capacity && nc + min(nt, s.top_k) >= k;
     const bool kept = nc <= s.capacity + kOverflowPairs;
     const bool stored =
@@ -1738,7 +1781,7 @@ __device__ __forceinline__ void row_item(const SelectArgs& s, const Ws& ws, int 
                                          int nc, int nt, int nn, float th, const Sh<NT>& sh) {
   const int tid = threadIdx.x;
   const int r = b * NT + t;
-  const int k = min(max(0, L - NT + t + 1), s.top_k);
+  const int k = min(row_end<NT>(s, b, L, t), s.top_k);
   if (masks & (1u << t)) {
     if (ld_ag(ws.row(r) + 2) < 32u) {
       resolve_row<NT>(s, ws, r, sh);
@@ -1883,7 +1926,7 @@ __device__ __forceinline__ void run_item(const Args& a, const SelectArgs& s, con
   float thr2[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    end[t] = max(0, L - NT + t + 1);
+    end[t] = row_end<NT>(s, b, L, t);
     const int r = b * NT + t;
     pfx[t] = ld_ag(ws.row(r) + 0);
     kn[t] = ld_ag(ws.row(r) + 2);
@@ -2027,7 +2070,7 @@ __device__ __forceinline__ void claim_item(const Args& a, const SelectArgs& s, c
         uint64_t w = 0;
         if (b < ws.batch) {
           w = ld_ag64(ws.claim(b, q));
-          len = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+          len = tile_keys<NT>(a, b);
         }
         const uint32_t st = static_cast<uint32_t>(w >> 32);
         const bool open = st >= kStageHist0 && st <= kStageRows &&
@@ -2113,7 +2156,7 @@ __device__ __forceinline__ void work_loop(const Args& a, const SelectArgs& s, ch
     }
     polls = 0;
     PMQA_TR(sh, 6, b, stage);
-    const int L = a.seq_lens[static_cast<int64_t>(b) * a.sl_stride];
+    const int L = tile_keys<NT>(a, b);
     run_item<NT, kFused>(a, s, ws, b, L, stage, idx, sh, rl);
     __syncthreads();
     PMQA_TR(sh, 7, idx, stage);
@@ -2136,7 +2179,7 @@ __device__ __forceinline__ void tile_finish(const Args& a, const SelectArgs& s, 
   PMQA_TR(sh, 4, sweep, stored);
   int end[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) end[t] = max(0, L - NT + t + 1);
+  for (int t = 0; t < NT; ++t) end[t] = row_end<NT>(s, b, L, t);
   if (NT == 1 && sweep == 0u) {
     const int k = min(end[0], s.top_k);
     unswept_row<NT>(s, b, k, sh.c->nc[0], sh.c->nt[0], sh.c->nn[0], sh.c->thr[0], stored != 0u, sh);
@@ -2184,13 +2227,14 @@ struct Segment {
   bool ok;
 };
 
-__device__ __forceinline__ Segment find_segment(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
-                                                int per_request, int keys_per_cta, bool empty_group) {
+template <class LenF>
+__device__ __forceinline__ Segment find_segment(LenF&& len_of, int batch, bool locate, int per_request,
+                                                int keys_per_cta, bool empty_group) {
   Segment sg{0, 0, 0, 0, 0, false};
   if (!locate) {
     const int b = blockIdx.x / per_request;
     const int c = blockIdx.x % per_request;
-    const int L = seq_lens[static_cast<int64_t>(b) * sl_stride];
+    const int L = len_of(b);
     const int n = L > 0 ? static_cast<int>(ceil_div(L, keys_per_cta)) : (empty_group ? 1 : 0);
     if (c < n) sg = Segment{b, L, c * keys_per_cta, min((c + 1) * keys_per_cta, L), n, true};
     return sg;
@@ -2198,7 +2242,7 @@ __device__ __forceinline__ Segment find_segment(const int32_t* seq_lens, int64_t
   const int lane = lane_id();
   if (batch <= 64) {
     // one load of the lengths, kept in registers for both scans
-    const int L = lane < batch ? seq_lens[static_cast<int64_t>(lane) * sl_stride] : 0;
+    const int L = lane < batch ? len_of(lane) : 0;
     const int g = lane < batch ? groups_of(L, empty_group) : 0;
     int64_t incl = g;
 #pragma unroll
@@ -2228,7 +2272,7 @@ __device__ __forceinline__ Segment find_segment(const int32_t* seq_lens, int64_t
   int64_t N = 0;  // groups in all
   for (int b0 = 0; b0 < batch; b0 += 64) {
     const int b = b0 + lane;
-    int64_t n = b < batch ? groups_of(seq_lens[static_cast<int64_t>(b) * sl_stride], empty_group) : 0;
+    int64_t n = b < batch ? groups_of(len_of(b), empty_group) : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
     N += uniform64(n);
@@ -2240,7 +2284,7 @@ __device__ __forceinline__ Segment find_segment(const int32_t* seq_lens, int64_t
   int64_t before = 0;  // groups of the requests before this block of 64
   for (int b0 = 0; b0 < batch; b0 += 64) {
     const int b = b0 + lane;
-    const int L = b < batch ? seq_lens[static_cast<int64_t>(b) * sl_stride] : 0;
+    const int L = b < batch ? len_of(b) : 0;
     const int g = b < batch ? groups_of(L, empty_group) : 0;
     int64_t incl = g;
 #pragma unroll
@@ -2268,10 +2312,10 @@ __device__ __forceinline__ Segment find_segment(const int32_t* seq_lens, int64_t
 
 // Calls seg(b, L, k0, k1, ctas) for this CTA's segment, if it has one (one
 // call site, so the body is inlined once).
-template <class F>
-__device__ __forceinline__ void for_each_segment(const int32_t* seq_lens, int64_t sl_stride, int batch, bool locate,
-                                                 int per_request, int keys_per_cta, bool empty_group, F&& seg) {
-  const Segment sg = find_segment(seq_lens, sl_stride, batch, locate, per_request, keys_per_cta, empty_group);
+template <class LenF, class F>
+__device__ __forceinline__ void for_each_segment(LenF&& len_of, int batch, bool locate, int per_request,
+                                                 int keys_per_cta, bool empty_group, F&& seg) {
+  const Segment sg = find_segment(len_of, batch, locate, per_request, keys_per_cta, empty_group);
   if (sg.ok) seg(sg.b, sg.L, sg.k0, sg.k1, sg.ctas);
 }
 
@@ -2288,7 +2332,7 @@ __device__ __forceinline__ void logits_body(const PagedArgs& a, float* out, int6
   src.bind(stage);
   src.bind_q(ql);
   const int lane = lane_id();
-  for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kLogitsKeysPerCta, false,
+  for_each_segment([&](int b) { return tile_keys<NT>(a, b); }, a.batch, a.locate, a.per_request, kLogitsKeysPerCta, false,
                    [&](int b, int L, int k0, int k1, int) {
     src.init(a, b);
     float* row0 = out + static_cast<int64_t>(b) * NT * ld;
@@ -2388,7 +2432,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
   const int w = wave_id();
   if (threadIdx.x == 0) sh.c->trace_n = 0;
   bool was_last = false;  // this CTA finished its tile
-  for_each_segment(a.seq_lens, a.sl_stride, a.batch, a.locate, a.per_request, kKeysPerCta, true,
+  for_each_segment([&](int b) { return tile_keys<NT>(a, b); }, a.batch, a.locate, a.per_request, kKeysPerCta, true,
                    [&](int b, int L, int k0, int k1, int nctas) {
     PMQA_TR(sh, 1, b, nctas);
     float thr[NT], tlo[NT];
@@ -2401,7 +2445,7 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
       // are kept too (a repair that needs a few more keys than the candidates
       // and ties then finds them there); they share the tie list
       tlo[t] = s.nearp ? near_floor(thr[t]) : thr[t];
-      lim[t] = min(k1, max(0, L - NT + t + 1));
+      lim[t] = min(k1, row_end<NT>(s, b, L, t));
       ncl[t] = 0;
       ntl[t] = 0;
       nnl[t] = 0;
@@ -2613,6 +2657,44 @@ pmqa_status validate_content(hipStream_t st, const int32_t* seq_lens, int64_t sl
 }
 
 
+// PMQA_VALIDATE=1 for prefill-shaped rows: every row end within max_context,
+// every tile's request a row of the block table, the table entries a tile
+// reads (its largest row end's pages) valid ids, counters and arrivals zero.
+pmqa_status validate_prefill(hipStream_t st, const int32_t* tile_req, const int32_t* row_ends, int32_t tiles,
+                             int32_t tile_rows, int32_t requests, int32_t max_context, const int32_t* bt,
+                             int64_t bt_stride, int32_t bt_width, int32_t bs, int64_t num_blocks,
+                             const int32_t* counters, const int32_t* arrivals) {
+  if (!validate_enabled() || stream_capturing(st) || tiles == 0) return PMQA_OK;
+  const int64_t rows = static_cast<int64_t>(tiles) * tile_rows;
+  std::vector<int32_t> TR, E, T, C, A;
+  bool ok = copy_span(TR, tile_req, static_cast<int64_t>(tiles), st) && copy_span(E, row_ends, rows, st) &&
+            copy_span(T, bt, static_cast<int64_t>(requests - 1) * bt_stride + bt_width, st) &&
+            copy_span(C, counters, 2 * rows, st);
+  if (arrivals) ok = ok && copy_span(A, arrivals, static_cast<int64_t>(tiles), st);
+  if (!ok || hipStreamSynchronize(st) != hipSuccess) return PMQA_ERR_LAUNCH;
+  for (int32_t b = 0; b < tiles; ++b) {
+    const int32_t req = TR[static_cast<size_t>(b)];
+    if (req < 0 || req >= requests) return PMQA_ERR_CONTENT;
+    int32_t L = 0;
+    for (int32_t t = 0; t < tile_rows; ++t) {
+      const int32_t e = E[static_cast<size_t>(b) * tile_rows + t];
+      if (e < 0 || e > max_context) return PMQA_ERR_CONTENT;
+      L = std::max(L, e);
+    }
+    const int64_t pages = ceil_div(L, bs);
+    if (pages > bt_width) return PMQA_ERR_CONTENT;
+    for (int64_t j = 0; j < pages; ++j) {
+      const int32_t id = T[static_cast<size_t>(req * bt_stride + j)];
+      if (id < 0 || id >= num_blocks) return PMQA_ERR_CONTENT;
+    }
+  }
+  for (int32_t v : C)
+    if (v != 0) return PMQA_ERR_CONTENT;
+  for (int32_t v : A)
+    if (v != 0) return PMQA_ERR_CONTENT;
+  return PMQA_OK;
+}
+
 PagedArgs paged_args(const uint8_t* q, const uint8_t* kv, const float* w, const int32_t* bt,
                      int64_t bt_stride, const int32_t* sl, int64_t sl_stride, int32_t bs, int32_t batch,
                      int64_t per_request) {
@@ -2630,6 +2712,8 @@ PagedArgs paged_args(const uint8_t* q, const uint8_t* kv, const float* w, const 
   a.bs_shift = log2_exact(bs);
   a.block_bytes = bs * (kDim + 4);
   a.scale_off = bs * kDim;
+  a.row_ends = nullptr;
+  a.tile_req = nullptr;
   return a;
 }
 
@@ -2686,15 +2770,17 @@ SelectArgs select_args(float* thr, int32_t* cnt, int32_t* cand, int32_t cap, int
   s.top_k = top_k;
   s.rows = rows;
   s.resident = 0;
+  s.row_ends = nullptr;
   return s;
 }
 
 pmqa_status launched() { return hipGetLastError() == hipSuccess ? PMQA_OK : PMQA_ERR_LAUNCH; }
 
 // One launch of K<nt>.  The located grid -- as many CTAs as fit on the device
-// at once, but at most 15/8 per compute unit -- runs when that is at least
-// twice the batch, else a.per_request CTAs per request (PMQA_ERR_SHAPE if that
-// grid is too large).  (The cap: on the 64-request decode batch 480 CTAs
+// at once, but at most 15/8 per compute unit -- runs when that gives every
+// tile a CTA (256 prefill tiles of 4 rows: 3328 CTAs in waves took 412 us per
+// call against 480 located), else a.per_request CTAs per request
+// (PMQA_ERR_SHAPE if that grid is too large).  (The cap: on the 64-request decode batch 480 CTAs
 // stream 2.7 us faster than the 768 that fit, whose third CTA on each compute
 // unit gets its first keys some 15 us after the first and finishes last; 432
 // and fewer are slower again.)  A select launch learns whether all of its CTAs
@@ -2706,7 +2792,7 @@ pmqa_status launch_k(int nt, hipStream_t st, A a, Rest... rest) {
   auto go = [&](auto fn) {
     const int64_t fit = resident_ctas(reinterpret_cast<const void*>(fn));
     int64_t g = std::min<int64_t>(fit, static_cast<int64_t>(device_cus()) * 15 / 8);
-    a.locate = g >= 2 * static_cast<int64_t>(a.batch);
+    a.locate = g >= static_cast<int64_t>(a.batch);
     if (!a.locate) g = static_cast<int64_t>(a.per_request) * a.batch;
     if (g > 0x7fffffff) {
       status = PMQA_ERR_SHAPE;
@@ -2913,6 +2999,40 @@ pmqa_status pmqa_fused_logits_select(const uint8_t* q, const uint8_t* kv_fused, 
                       seq_lens_stride, batch_size, next_n, num_heads, head_dim, block_size, num_blocks, max_context,
                       thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx, workspace,
                       workspace_bytes, stream, false);
+}
+
+pmqa_status pmqa_prefill_select(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+                                const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+                                int32_t num_requests, const int32_t* tile_requests, const int32_t* row_ends,
+                                int32_t num_tiles, int32_t tile_rows, int32_t num_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, int32_t max_context, float* thresholds,
+                                int32_t* counters, int32_t* candidates, int32_t capacity, int32_t top_k,
+                                int32_t* arrivals, int32_t* ranges, int32_t* topk_idx, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  pmqa_status st = pmqa_check_prefill_args(q, kv_fused, weights, block_tables, block_table_stride, block_table_width,
+                                           num_requests, tile_requests, row_ends, num_tiles, tile_rows, num_heads,
+                                           head_dim, block_size, num_blocks, max_context, thresholds, counters,
+                                           candidates, capacity, top_k, arrivals, ranges, topk_idx, workspace,
+                                           workspace_bytes);
+  if (st != PMQA_OK) return st;
+  if (num_tiles > 65535) return PMQA_ERR_SHAPE;
+  if (num_tiles == 0) return PMQA_OK;
+  const int64_t gx = std::max<int64_t>(1, ceil_div(max_context, kFusedKeysPerCta));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int64_t rows = static_cast<int64_t>(num_tiles) * tile_rows;
+  st = validate_prefill(hs, tile_requests, row_ends, num_tiles, tile_rows, num_requests, max_context, block_tables,
+                        block_table_stride, block_table_width, block_size, num_blocks, counters, arrivals);
+  if (st != PMQA_OK) return st;
+  PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, nullptr, 0, block_size, num_tiles,
+                           gx);
+  a.row_ends = row_ends;
+  a.tile_req = tile_requests;
+  SelectArgs s = select_args(thresholds, counters, candidates, capacity, top_k, arrivals, ranges, topk_idx, num_tiles,
+                             static_cast<int32_t>(rows), max_context, true, workspace);
+  s.row_ends = row_ends;
+  if (s.ws) st = prepare_workspace(workspace, num_tiles, rows, max_context, true, hs, false);
+  if (st == PMQA_OK) st = launch_k<FusedK>(tile_rows, hs, a, s);
+  return st != PMQA_OK ? st : launched();
 }
 
 pmqa_status pmqa_fused_logits_select_noalloc(const uint8_t* q, const uint8_t* kv_fused, const float* weights,

@@ -6,7 +6,10 @@ to be repaired).  This script computes them with the float64 oracle and
 stores them, with sigma_k, sigma_{k+1} and the per-row tolerance, as JSON
 beside it.  It imports only the oracle and the input generators.
 
-    python tests/golden/make_thresholds.py 3 4 5
+    python tests/golden/make_thresholds.py 3 4 5 prefill
+
+"prefill" is the prefill chunk (prefill-shaped rows): each row's threshold
+is its min(row_end, 2048)-th largest score less 1e-3.
 """
 import json
 import os
@@ -83,5 +86,42 @@ def main(cfgs):
         print(f"cfg{cfg}: {wl.rows} rows in {time.time() - t0:.1f}s", flush=True)
 
 
+def prefill_main():
+    t0 = time.time()
+    wl = W.prefill_chunk()
+    s64 = oracle.prefill_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.tile_requests, wl.row_ends,
+                                wl.tile_rows, wl.block_size, wl.max_context)
+    tau = oracle.prefill_tolerance(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.tile_requests, wl.row_ends,
+                                   wl.tile_rows, wl.block_size)
+    thr = np.zeros(wl.rows, np.float32)
+    sig_k = [None] * wl.rows
+    sig_k1 = [None] * wl.rows
+    for r, e in enumerate(wl.row_ends):
+        if e <= 0:
+            continue
+        srt = np.sort(s64[r, :e])[::-1]
+        k = min(int(e), wl.top_k)
+        thr[r] = np.float32(srt[k - 1] - 1e-3)
+        sig_k[r] = float(srt[k - 1])
+        sig_k1[r] = float(srt[k]) if k < e else None
+    doc = {
+        "_about": f"Oracle-computed select thresholds for workload {wl.name}; written by make_thresholds.py",
+        "recipe": "sigma_min(row_end,k)_minus_1e-3",
+        "workload": wl.name,
+        "fingerprint": W.prefill_fingerprint(wl),
+        "threshold_bits": [int(x) for x in thr.view(np.int32)],
+        "sigma_k": sig_k,
+        "sigma_k1": sig_k1,
+        "tau": [float(x) for x in tau],
+        "row_ends": [int(x) for x in wl.row_ends],
+    }
+    with open(os.path.join(HERE, "thresholds_prefill_chunk.json"), "w") as f:
+        json.dump(doc, f, indent=0)
+    print(f"prefill chunk: {wl.rows} rows in {time.time() - t0:.1f}s", flush=True)
+
+
 if __name__ == "__main__":
-    main([int(a) for a in sys.argv[1:]] or [3, 4, 5])
+    args = sys.argv[1:] or ["3", "4", "5"]
+    main([int(a) for a in args if a != "prefill"])
+    if "prefill" in args:
+        prefill_main()

@@ -166,3 +166,37 @@ def test_entry_points_reject_before_launch():
     assert lib.pmqa_fused_logits_select(*fused_args(q=None), None) == NULL
     # a zero batch is a no-op that needs no device either
     assert lib.pmqa_fused_logits_select(*fused_args(B=0), None) == OK
+
+
+def prefill_args(**kw):
+    a = dict(q=P(), kv=P(), w=P(), bt=P(), bts=250, btw=250, nreq=2, treq=P(), re=P(), T=6, tr=4, H=64, D=128,
+             bs=32, nb=500, mc=8000, thr=P(), cnt=P(), cand=P(), cap=512, k=512, arr=P(), rng=P(), topk=P(),
+             ws=P(), wsb=1 << 24)
+    a.update(kw)
+    return [a["q"], a["kv"], a["w"], a["bt"], a["bts"], a["btw"], a["nreq"], a["treq"], a["re"], a["T"], a["tr"],
+            a["H"], a["D"], a["bs"], a["nb"], a["mc"], a["thr"], a["cnt"], a["cand"], a["cap"], a["k"], a["arr"],
+            a["rng"], a["topk"], a["ws"], a["wsb"]]
+
+
+PREFILL_CASES = [
+    ({}, OK),
+    ({"T": 0, "q": None, "treq": None}, OK),
+    ({"treq": None}, NULL), ({"re": None}, NULL), ({"q": None}, NULL), ({"rng": None}, NULL),
+    ({"nreq": 0}, SHAPE), ({"tr": 5}, UNSUP), ({"tr": 0}, UNSUP), ({"btw": 249}, SHAPE), ({"T": -1}, SHAPE),
+    ({"wsb": 100}, SHAPE), ({"treq": P(2)}, ALIGN), ({"re": P(2)}, ALIGN),
+]
+
+
+@pytest.mark.parametrize("kw,want", PREFILL_CASES)
+def test_check_prefill_args(kw, want):
+    assert pm.lib().pmqa_check_prefill_args(*prefill_args(**kw)) == want
+    if want != OK:
+        assert pm.lib().pmqa_prefill_select(*prefill_args(**kw), None) == want
+
+
+def test_prefill_workspace_is_the_fused_layout():
+    """The prefill select's workspace is the fused select's for num_tiles tiles
+    of tile_rows rows: one byte short is rejected."""
+    need = pm.workspace_bytes("fused", 6, 4, 8000)
+    assert pm.lib().pmqa_check_prefill_args(*prefill_args(wsb=need)) == OK
+    assert pm.lib().pmqa_check_prefill_args(*prefill_args(wsb=need - 1)) == SHAPE

@@ -253,6 +253,90 @@ def small_random(seed: int, seq_lens: List[int], next_n: int, block_size: int, t
         threshold_recipe="test", description=f"small random-page workload seed={seed}")
 
 
+@dataclasses.dataclass
+class PrefillWorkload:
+    """Prefill-shaped rows: query tiles of tile_rows rows, each tile on one
+    request (tile_requests), each row with its own key end (row_ends)."""
+    name: str
+    q: np.ndarray              # uint8 [rows, H, D]
+    kv_fused: np.ndarray       # uint8 [num_blocks, bs*(D+4)]
+    weights: np.ndarray        # float32 [rows, H]
+    block_tables: np.ndarray   # int32 [requests, width]
+    seq_lens: np.ndarray       # int32 [requests]: the keys each request holds
+    tile_requests: np.ndarray  # int32 [tiles]
+    row_ends: np.ndarray       # int32 [rows]
+    max_context: int
+    block_size: int
+    tile_rows: int
+    top_k: int
+    capacity: int
+    description: str
+
+    @property
+    def tiles(self) -> int:
+        return int(self.tile_requests.shape[0])
+
+    @property
+    def rows(self) -> int:
+        return int(self.row_ends.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_fused.shape[0])
+
+
+def prefill_random(seed: int, prompts: List[tuple], tile_rows: int, block_size: int, top_k: int, capacity: int,
+                   key_scale: float = 1.0, shuffle_tiles: bool = True, name: Optional[str] = None) -> PrefillWorkload:
+    """Causal prefill rows over random pages.  prompts[i] = (prefix, new):
+    request i holds prefix + new keys, and its j-th new token's row sees keys
+    below prefix + j + 1.  A request's rows fill tiles of tile_rows in order;
+    the last tile is topped up with rows that see nothing.  With shuffle_tiles
+    the tiles of all requests come in random order."""
+    g = torch.Generator().manual_seed(seed)
+    lens = [int(p) + int(n) for p, n in prompts]
+    bs = block_size
+    max_ctx = max(max(lens), 1)
+    width = int(math.ceil(max_ctx / bs))
+    bt, nb, page_of = _random_pool(g, lens, bs, width)
+    values = _e4m3_codes(key_scale * torch.randn(nb, bs, D, generator=g))
+    scales = _uniform(g, (nb, bs), 0.5, 2.0)
+    _poison_tails(values, scales, lens, page_of, bs, nb - 1)
+    tiles = []  # (request, [row ends])
+    for i, (pre, new) in enumerate(prompts):
+        ends = [int(pre) + j + 1 for j in range(int(new))]
+        for t0 in range(0, len(ends), tile_rows):
+            e = ends[t0:t0 + tile_rows]
+            tiles.append((i, e + [0] * (tile_rows - len(e))))
+    if shuffle_tiles and tiles:
+        order = torch.randperm(len(tiles), generator=g).tolist()
+        tiles = [tiles[j] for j in order]
+    R = len(tiles) * tile_rows
+    q = _e4m3_codes(key_scale * torch.randn(R, H, D, generator=g))
+    w = _uniform(g, (R, H), -1.0, 1.0)
+    return PrefillWorkload(
+        name=name or f"prefill_s{seed}", q=q.numpy().copy(), kv_fused=_pack_kv_fused(values, scales),
+        weights=w.numpy().copy(), block_tables=bt, seq_lens=np.array(lens, dtype=np.int32),
+        tile_requests=np.array([t[0] for t in tiles], dtype=np.int32),
+        row_ends=np.array([e for t in tiles for e in t[1]], dtype=np.int32), max_context=max_ctx, block_size=bs,
+        tile_rows=tile_rows, top_k=top_k, capacity=capacity,
+        description=f"causal prefill rows, prompts (prefix, new) = {list(prompts)}, tiles of {tile_rows} rows")
+
+
+def prefill_chunk(seed: int = 1006) -> PrefillWorkload:
+    """A prefill chunk: two requests, 512 new tokens each on cached prefixes of
+    12288 and 4096 keys, tiles of 4 rows in random order, top_k 2048."""
+    return prefill_random(seed, [(12288, 512), (4096, 512)], tile_rows=4, block_size=64, top_k=2048,
+                          capacity=4096, name="prefill_chunk_2x512")
+
+
+def prefill_fingerprint(w: PrefillWorkload) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for a in (w.q, w.kv_fused, w.weights, w.block_tables, w.tile_requests, w.row_ends):
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()[:16]
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
