@@ -120,6 +120,21 @@ def cpu_baseline(wl, thresholds, budget_s):
             "sample": f"first {reqs} of {wl.batch} requests of {wl.name} ({pairs} pairs, {rows} rows) in {dt:.1f}s"}
 
 
+def calibration_copy(args, dev):
+    """With --calib-copy-mib: one plain elementwise kernel that reads and writes
+    exactly that many MiB (torch's same-dtype copy_ may go to a DMA engine
+    instead of a kernel), the yardstick for the HBM byte counters."""
+    if not args.calib_copy_mib:
+        return
+    src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_prefill(args, dev):
     """The prefill chunk through pmqa_prefill_select: one launch per step over
     prefill-shaped rows (tiles of 4 rows of one request, causal row ends).  Its
@@ -164,6 +179,7 @@ def bench_prefill(args, dev):
     ms_step = start.elapsed_time(stop) / args.steps
     assert int(arrivals.abs().sum()) == 0, "arrivals not left zeroed"
     repaired = int((thr_all[-1].cpu().numpy().view(np.int32) != thr0.view(np.int32)).sum())
+    calibration_copy(args, dev)
     flops = 2.0 * 64 * 128 * pairs
     tflops = flops / (ms_step / 1e3) / 1e12
     kv_bytes = int(wl.seq_lens.astype(np.int64).sum()) * 132
@@ -334,16 +350,7 @@ def main():
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
 
-    if args.calib_copy_mib:
-        # a plain elementwise kernel that reads and writes exactly calib_copy_mib MiB
-        # (torch's same-dtype copy_ may go to a DMA engine instead of a kernel)
-        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        torch.bitwise_not(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy(args, dev)
 
     alg = algorithmic_bytes(wl, args.path)
     call_s = ms_step / 1e3

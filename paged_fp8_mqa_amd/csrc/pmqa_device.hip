@@ -795,8 +795,8 @@ __device__ __forceinline__ Sh<NT> make_sh(char* lds, int fin_cap, int ctl_off) {
 
 // Shared memory of a select kernel CTA: each wave's candidate and tie lists,
 // per row, of (key index, stored score bits) pairs not yet written to the
-// row's slots (the finish stage's structures stay out, so that three CTAs and
-// their KV staging areas fit on a compute unit).
+// row's slots (the finish stage's structures stay out, so that the LDS of two
+// CTAs, with their KV staging areas, fits on a compute unit).
 template <int NT>
 struct MainShared {
   int2 cand[kWaves][NT][kWaveCand<NT>];
@@ -2321,9 +2321,13 @@ __device__ __forceinline__ void for_each_segment(LenF&& len_of, int batch, bool 
 
 // ---------------------------------------------------------------- kernels
 
-// Waves per SIMD each variant is built for (VGPR budget 512 / waves).
+// Waves per SIMD each variant is built for (VGPR budget 512 / waves): two for
+// every next_n.  The finish stage's code shares the kernel's register budget;
+// built for three waves (168 VGPRs) the next_n = 1 variant spilled inside its
+// streaming loop and wrote 34 MB of spill lines per call on the 64-request
+// decode batch (9.5 MB at two waves, and 0.8 us faster per call).
 template <int NT>
-constexpr int kFusedWaves = NT == 1 ? 3 : 2;
+constexpr int kFusedWaves = 2;
 
 
 template <int NT, class Src>
@@ -2592,8 +2596,8 @@ __global__ void __launch_bounds__(kThreads) select_kernel(LogitsArgs a, SelectAr
   select_body<NT, false, kSelectKeysPerCta, LogitsSource<NT>>(a, s, lds);
 }
 
-// LDS of the fused launches: 2 CTAs per compute unit for next_n >= 2, 3 for next_n = 1.
-static_assert(3 * Layout<1, true>::kBytes <= 160 * 1024, "three next_n = 1 CTAs per compute unit");
+// LDS of the fused launches: two CTAs per compute unit (the VGPR budget allows two).
+static_assert(2 * Layout<1, true>::kBytes <= 160 * 1024, "two next_n = 1 CTAs per compute unit");
 static_assert(2 * Layout<2, true>::kBytes <= 160 * 1024, "two next_n = 2 CTAs per compute unit");
 static_assert(2 * Layout<3, true>::kBytes <= 160 * 1024, "two next_n = 3 CTAs per compute unit");
 static_assert(2 * Layout<4, true>::kBytes <= 160 * 1024, "two next_n = 4 CTAs per compute unit");
