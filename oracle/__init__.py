@@ -20,5 +20,6 @@ from .layout import (parse_block, gather_request, min_block_table_width,  # noqa
                      padded_seq_len, region2_offset, block_bytes)
 from .logits import paged_mqa_logits, request_scores, row_ends, row_tolerance  # noqa: F401
 from .prefill import prefill_logits, prefill_tolerance  # noqa: F401
+from .dtypes import mqa_logits_dtypes, round_f16  # noqa: F401
 from .select import (classify, fits, kth_largest, topk_indices, threshold_select,  # noqa: F401
                      encode_candidate, encode_tie, decode_slot, select_with_repair)
