@@ -240,13 +240,69 @@ def prefill_cpu_baseline(wl, thresholds, budget_s):
                       f"tiles ({pairs} pairs, {rows} rows) in {dt:.1f}s"}
 
 
+def bench_logits(args, dev):
+    """--path logits: pmqa_mqa_logits(_typed) alone on the workload, with the
+    precisions of --dtypes (output,epi,acc).  HBM-bound: every visible key's
+    132 bytes once per request, q and weights, and the logits written (4 or 2
+    bytes per pair)."""
+    wl = W.make(int(args.workload))
+    names = args.dtypes.split(",")
+    dt = {"f32": torch.float32, "f16": torch.float16}
+    out_dt, epi_dt, acc_dt = (dt[n] for n in names)
+    pairs = int(wl.row_ends().sum())
+    q = torch.from_numpy(wl.q).to(dev)
+    w = torch.from_numpy(wl.weights).to(dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    kv_host = torch.from_numpy(wl.kv_fused)
+    kvs = [kv_host.to(dev).view(wl.num_blocks, wl.block_size, 1, 132) for _ in range(args.replicas)]
+    out = torch.empty(wl.rows, pm.padded_seq_len(wl.max_seq_len), dtype=out_dt, device=dev)
+
+    def step(i):
+        pm.mqa_logits(q, kvs[i % len(kvs)], w, bt, sl, wl.max_seq_len, out=out, output_dtype=out_dt,
+                      epi_dtype=epi_dt, acc_dtype=acc_dt)
+
+    for i in range(args.warmup):
+        step(i)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for j in range(args.steps):
+        step(args.warmup + j)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    out_bytes = 2 if out_dt == torch.float16 else 4
+    alg = int(wl.seq_lens.astype(np.int64).sum()) * 132 + wl.q.nbytes + wl.weights.nbytes + pairs * out_bytes
+    achieved = alg / (ms_step / 1e3) / 1e9
+    line = {
+        "metric": "scored (row,KV position) pairs/sec; % roofline (logits only)",
+        "value": pairs / (ms_step / 1e3), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"fp8_e4m3 x fp8_e4m3 -> acc {names[2]}, epilogue {names[1]}, out {names[0]}",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "path": "logits", "dtypes": {"output": names[0], "epi": names[1],
+                                                                      "acc": names[2]},
+                   "pairs": pairs, "rows": wl.rows, "kv_replicas": args.replicas, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": alg,
+                     "kernel": "logits_kernel<%d>" % wl.next_n, "launch_us": ms_step * 1e3},
+        "kernel_src_sha": kernel_hash(),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="4", choices=["3", "4", "5", "prefill"])
-    ap.add_argument("--path", default="fused", choices=["fused", "unfused"])
+    ap.add_argument("--path", default="fused", choices=["fused", "unfused", "logits"])
+    ap.add_argument("--dtypes", default="f32,f32,f32",
+                    help="--path logits: output,epi,acc precisions, each f32 or f16")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -264,6 +320,8 @@ def main():
     pm.lib()
     if args.workload == "prefill":
         return bench_prefill(args, dev)
+    if args.path == "logits":
+        return bench_logits(args, dev)
     args.workload = int(args.workload)
 
     wl = W.make(args.workload)

@@ -5,6 +5,8 @@
  * Operations (definitions on the pages cited per entry point):
  *   pmqa_mqa_logits           logits[b*next_n+t, p] =
  *                               s_p * sum_h w[b*next_n+t, h] * relu(q[b,t,h,:] . k_p)
+ *   pmqa_mqa_logits_typed     the same with float16 accumulator, epilogue or
+ *                             output options
  *   pmqa_indexer_topk         one-pass threshold select over a logits matrix,
  *                             with last-CTA radix-select repair and Top-k finalize
  *   pmqa_fused_logits_select  both in one pass over the KV pages; no score
@@ -120,6 +122,55 @@ pmqa_status pmqa_mqa_logits(
     int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
     int32_t block_size, int64_t num_blocks, int32_t max_seq_len,
     float* out, int64_t out_stride, void* stream);
+
+/* Element types of pmqa_mqa_logits_typed's precision arguments. */
+typedef enum pmqa_dtype {
+  PMQA_DTYPE_F32 = 0,
+  PMQA_DTYPE_F16 = 1,
+  PMQA_DTYPE_BF16 = 2 /* named so that it can be refused: no FP8 precision takes it */
+} pmqa_dtype;
+
+/*
+ * pmqa_mqa_logits_typed -- pmqa_mqa_logits with the three precisions of page
+ * "flashinfer.attn_scores", fp8_paged_mqa_logits (the formula block and the
+ * parameters output_dtype, epi_dtype, acc_dtype, weights):
+ *
+ *   acc_dtype     each head's dot product q[b,t,h,:] . k_p.  PMQA_DTYPE_F32:
+ *                 as pmqa_mqa_logits.  PMQA_DTYPE_F16: the float32 result of
+ *                 the FP8 matrix instruction is rounded to float16 (nearest
+ *                 even; past 65504 it becomes infinite), the hardware having no
+ *                 FP8 instruction that accumulates in float16.
+ *   epi_dtype     ReLU, the weight multiply, the head sum and the scale
+ *                 multiply.  PMQA_DTYPE_F16: the dot product enters rounded to
+ *                 float16 (so acc_dtype makes no difference), the weights and
+ *                 the scale are rounded to float16, and every product and sum
+ *                 is a float16 operation (packed, two heads at a time), which
+ *                 overflows to infinity past 65504.
+ *   output_dtype  the stored element: PMQA_DTYPE_F32 (4 bytes) or
+ *                 PMQA_DTYPE_F16 (2 bytes, the epilogue's result rounded to
+ *                 nearest even).
+ *
+ * PMQA_DTYPE_BF16, or any other value, for any of the three returns
+ * PMQA_ERR_UNSUPPORTED.  `out` is an array of output_dtype elements, aligned to
+ * one element; out_stride counts elements.  Everything else is as for
+ * pmqa_mqa_logits, which equals this call with all three PMQA_DTYPE_F32.
+ */
+pmqa_status pmqa_check_logits_typed_args(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_seq_len,
+    const void* out, int64_t out_stride, int32_t output_dtype, int32_t epi_dtype, int32_t acc_dtype);
+
+pmqa_status pmqa_mqa_logits_typed(
+    const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_seq_len,
+    void* out, int64_t out_stride, int32_t output_dtype, int32_t epi_dtype, int32_t acc_dtype,
+    void* stream);
 
 /*
  * Select arguments shared by pmqa_indexer_topk and pmqa_fused_logits_select

@@ -7,7 +7,8 @@ PyTorch supplies device memory and the current stream.  Loading fails loudly
 when the library has not been built; there is no fallback.
 
 Entry points mirror the C ABI in include/pmqa.h:
-  mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None)
+  mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None,
+             output_dtype=None, epi_dtype=None, acc_dtype=None)
   indexer_topk(logits, seq_lens, next_n, max_context, thresholds, counters,
                candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None,
                workspace=None)
@@ -52,6 +53,8 @@ SIGNATURES = {
     "pmqa_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
     "pmqa_check_logits_args": (_PAGED + [_I32, _P, _I64], ctypes.c_int),
     "pmqa_mqa_logits": (_PAGED + [_I32, _P, _I64, _P], ctypes.c_int),
+    "pmqa_check_logits_typed_args": (_PAGED + [_I32, _P, _I64, _I32, _I32, _I32], ctypes.c_int),
+    "pmqa_mqa_logits_typed": (_PAGED + [_I32, _P, _I64, _I32, _I32, _I32, _P], ctypes.c_int),
     "pmqa_check_select_args": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT, ctypes.c_int),
     "pmqa_indexer_topk": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT + [_P], ctypes.c_int),
     "pmqa_check_fused_args": (_PAGED + [_I32] + _SELECT_OUT, ctypes.c_int),
@@ -149,17 +152,40 @@ def _paged(q, kv_fused, weights, block_tables, seq_lens, block_size):
             kv_fused.shape[0]], B, nn
 
 
+DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2  # pmqa_dtype
+
+
+def _dtype_code(dt):
+    import torch
+    codes = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
+    if dt not in codes:
+        raise ValueError(f"unsupported dtype {dt}")
+    return codes[dt]
+
+
 def mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None, block_size=None,
-               stream=None):
-    """FP8 paged MQA logits; returns the [B*next_n, max_seq_len] view of `out`."""
+               stream=None, output_dtype=None, epi_dtype=None, acc_dtype=None):
+    """FP8 paged MQA logits; returns the [B*next_n, max_seq_len] view of `out`.
+
+    output_dtype (torch.float32 or torch.float16), epi_dtype and acc_dtype
+    (torch.float32 or torch.float16) select pmqa_mqa_logits_typed; all three
+    float32 (the default) is pmqa_mqa_logits."""
     import torch
     args, B, nn = _paged(q, kv_fused, weights, block_tables, seq_lens, block_size)
+    odt = torch.float32 if output_dtype is None else output_dtype
+    codes = [_dtype_code(odt), _dtype_code(epi_dtype or torch.float32), _dtype_code(acc_dtype or torch.float32)]
     if out is None:
-        out = torch.empty(B * nn, padded_seq_len(max_seq_len), dtype=torch.float32, device=q.device)
+        out = torch.empty(B * nn, padded_seq_len(max_seq_len), dtype=odt, device=q.device)
     if out.stride(1) != 1:
         raise ValueError("out rows must be contiguous")
-    _check(lib().pmqa_mqa_logits(*args, int(max_seq_len), _ptr(out), out.stride(0), _stream(stream)),
-           "pmqa_mqa_logits")
+    if out.dtype != odt:
+        raise ValueError(f"out is {out.dtype}, output_dtype is {odt}")
+    if codes == [DTYPE_F32] * 3:
+        _check(lib().pmqa_mqa_logits(*args, int(max_seq_len), _ptr(out), out.stride(0), _stream(stream)),
+               "pmqa_mqa_logits")
+    else:
+        _check(lib().pmqa_mqa_logits_typed(*args, int(max_seq_len), _ptr(out), out.stride(0), *codes,
+                                           _stream(stream)), "pmqa_mqa_logits_typed")
     return out[: B * nn, :max_seq_len]
 
 

@@ -381,15 +381,100 @@ __device__ __forceinline__ float head_sum(v4f acc, float4 w, float sum) {
   return __builtin_fmaf(relu(acc[3]), w.w, sum);
 }
 
+// The epilogue's precision (page "flashinfer.attn_scores", fp8_paged_mqa_logits,
+// acc_dtype and epi_dtype).  Each policy turns one MFMA result (four heads of
+// one key) into a running partial (head_sum, in head order), and a lane's four
+// column tiles' partials into the score of key p0 + lane (finish: the
+// reduce-scatter over the four lane groups, then the scale multiply).
+//   kEpiF32    float32 throughout (the fused select and pmqa_mqa_logits);
+//   kEpiAcc16  each dot product rounded to float16, then the float32 epilogue;
+//   kEpiF16    the dot products, weights and scale rounded to float16 and
+//              every product and sum a float16 operation, two heads per packed
+//              instruction.
+constexpr int kEpiF32 = 0;
+constexpr int kEpiAcc16 = 1;
+constexpr int kEpiF16 = 2;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef short s2 __attribute__((ext_vector_type(2)));
+
+// max(x, 0) of both halves as a 16-bit integer max on the bit patterns (the
+// float32 relu's rule: a negative sign bit gives +0).
+__device__ __forceinline__ h2 relu2(h2 x) {
+  return __builtin_bit_cast(h2, __builtin_elementwise_max(__builtin_bit_cast(s2, x), s2{0, 0}));
+}
+
+__device__ __forceinline__ _Float16 shfl_xor_h(_Float16 v, int m) {
+  const int x = __shfl_xor(static_cast<int>(__builtin_bit_cast(unsigned short, v)), m);
+  return __builtin_bit_cast(_Float16, static_cast<unsigned short>(x));
+}
+
+template <int kEpi>
+struct Epi {
+  using Acc = float;
+  using W = float4;
+  __device__ static Acc zero() { return 0.f; }
+  __device__ static W weights(float4 w) { return w; }
+  __device__ static float dot(float x) {
+    if constexpr (kEpi == kEpiAcc16) return static_cast<float>(static_cast<_Float16>(x));
+    else return x;
+  }
+  __device__ static Acc head_sum(v4f acc, W w, Acc sum) {
+    if constexpr (kEpi == kEpiF32) {
+      return pmqa::head_sum(acc, w, sum);
+    } else {
+      sum = __builtin_fmaf(relu(dot(acc[0])), w.x, sum);
+      sum = __builtin_fmaf(relu(dot(acc[1])), w.y, sum);
+      sum = __builtin_fmaf(relu(dot(acc[2])), w.z, sum);
+      return __builtin_fmaf(relu(dot(acc[3])), w.w, sum);
+    }
+  }
+  __device__ static float finish(Acc x0, Acc x1, Acc x2, Acc x3, int g, float s) {
+    return reduce_scatter4(x0, x1, x2, x3, g) * s;
+  }
+};
+
+template <>
+struct Epi<kEpiF16> {
+  using Acc = h2;  // two heads' running sums
+  struct W {
+    h2 lo, hi;  // weights of the lane's heads 0-1 and 2-3 of a tile
+  };
+  __device__ static Acc zero() { return h2{0, 0}; }
+  __device__ static W weights(float4 w) {
+    return W{h2{static_cast<_Float16>(w.x), static_cast<_Float16>(w.y)},
+             h2{static_cast<_Float16>(w.z), static_cast<_Float16>(w.w)}};
+  }
+  __device__ static Acc head_sum(v4f acc, W w, Acc sum) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const h2 a01 = relu2(__builtin_convertvector((f2{acc[0], acc[1]}), h2));
+    const h2 a23 = relu2(__builtin_convertvector((f2{acc[2], acc[3]}), h2));
+    sum = __builtin_elementwise_fma(a01, w.lo, sum);
+    return __builtin_elementwise_fma(a23, w.hi, sum);
+  }
+  // the two halves of each tile's partial, then the float32 path's
+  // reduce-scatter in float16, then the scale
+  __device__ static float finish(Acc x0, Acc x1, Acc x2, Acc x3, int g, float s) {
+    const _Float16 y[4] = {x0.x + x0.y, x1.x + x1.y, x2.x + x2.y, x3.x + x3.y};
+    const bool hi2 = (g & 2) != 0;
+    const _Float16 a = (hi2 ? y[2] : y[0]) + shfl_xor_h(hi2 ? y[0] : y[2], 32);
+    const _Float16 b = (hi2 ? y[3] : y[1]) + shfl_xor_h(hi2 ? y[1] : y[3], 32);
+    const bool hi1 = (g & 1) != 0;
+    const _Float16 r = (hi1 ? b : a) + shfl_xor_h(hi1 ? a : b, 16);
+    return static_cast<float>(r * static_cast<_Float16>(s));
+  }
+};
+
 // Scores computed from the paged KV pool, the A operands (q) and the lane's 16
 // weights per row held in VGPRs (next_n up to 2, and the repair).
 template <int NT>
 struct QLds;
 
-template <int NT>
+template <int NT, int kEpi = kEpiF32>
 struct KvSource : KvStream {
-  v8i qa[NT][4];        // A operands: rows t, head tiles mt
-  float4 wt[NT][4];     // weights of heads 16*mt + 4*g .. +3
+  using E = Epi<kEpi>;
+  v8i qa[NT][4];                 // A operands: rows t, head tiles mt
+  typename E::W wt[NT][4];       // weights of heads 16*mt + 4*g .. +3
 
   __device__ __forceinline__ void bind_q(QLds<NT>*) {}
 
@@ -401,7 +486,7 @@ struct KvSource : KvStream {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         qa[t][mt] = load32(a.q + ((row * kHeads + 16 * mt + n) * kDim + 32 * g));
-        wt[t][mt] = *reinterpret_cast<const float4*>(a.w + row * kHeads + 16 * mt + 4 * g);
+        wt[t][mt] = E::weights(*reinterpret_cast<const float4*>(a.w + row * kHeads + 16 * mt + 4 * g));
       }
     }
   }
@@ -414,16 +499,16 @@ struct KvSource : KvStream {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       qa[0][mt] = load32(a.q + ((r * kHeads + 16 * mt + n) * kDim + 32 * g));
-      wt[0][mt] = *reinterpret_cast<const float4*>(a.w + r * kHeads + 16 * mt + 4 * g);
+      wt[0][mt] = E::weights(*reinterpret_cast<const float4*>(a.w + r * kHeads + 16 * mt + 4 * g));
     }
   }
 
-  // E[t] = score of key p0 + lane for row t.  Fixed operation order, shared by
-  // every kernel, so the logits, fused and repair paths agree bit for bit.
-  __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
+  // out[t] = score of key p0 + lane for row t.  Fixed operation order, shared
+  // by every kernel, so the logits, fused and repair paths agree bit for bit.
+  __device__ __forceinline__ void score(const Group& gr, float (&out)[NT]) const {
     v8i bk[4];
     operands(gr, bk);
-    float part[NT][4];
+    typename E::Acc part[NT][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // all of the tile's MFMAs first, into separate accumulators, so their
@@ -435,14 +520,14 @@ struct KvSource : KvStream {
         for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mfma_fp8(qa[t][mt], bk[j]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        float sum = 0.f;
+        typename E::Acc sum = E::zero();
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) sum = head_sum(acc[t][mt], wt[t][mt], sum);
+        for (int mt = 0; mt < 4; ++mt) sum = E::head_sum(acc[t][mt], wt[t][mt], sum);
         part[t][j] = sum;
       }
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) E[t] = reduce_scatter4(part[t][0], part[t][1], part[t][2], part[t][3], g) * gr.s;
+    for (int t = 0; t < NT; ++t) out[t] = E::finish(part[t][0], part[t][1], part[t][2], part[t][3], g, gr.s);
   }
 };
 
@@ -459,8 +544,9 @@ struct QLds {
 // read from LDS per head tile (next_n of 3 and 4): holding 32 VGPRs of q and
 // 16 of weights per row left those variants one wave per SIMD; from LDS they
 // fit two.  Same operation order as KvSource, so the same bits.
-template <int NT>
+template <int NT, int kEpi = kEpiF32>
 struct KvSourceQ : KvStream {
+  using E = Epi<kEpi>;
   QLds<NT>* ql;
 
   __device__ __forceinline__ void bind_q(QLds<NT>* q_area) { ql = q_area; }
@@ -502,14 +588,15 @@ struct KvSourceQ : KvStream {
     for (int j = 0; j < 4; ++j) p.acc[k & 1][j] = mfma_fp8(p.qa[k % 3], bk[j]);
   }
   template <int k>
-  __device__ __forceinline__ void steps(Pipe& p, const v8i (&bk)[4], float (&part)[NT][4]) const {
+  __device__ __forceinline__ void steps(Pipe& p, const v8i (&bk)[4], typename E::Acc (&part)[NT][4]) const {
     if constexpr (k < 4 * NT) {
       if constexpr (k + 1 < 4 * NT) mm<k + 1>(p, bk);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (k + 2 < 4 * NT) ld<k + 2>(p);
       __builtin_amdgcn_sched_barrier(0);
+      const typename E::W wk = E::weights(p.wv[k % 3]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[k >> 2][j] = head_sum(p.acc[k & 1][j], p.wv[k % 3], part[k >> 2][j]);
+      for (int j = 0; j < 4; ++j) part[k >> 2][j] = E::head_sum(p.acc[k & 1][j], wk, part[k >> 2][j]);
       // (keeps the steps in this order: left to itself the scheduler hoists
       // every LDS read to the top and runs out of registers)
       __builtin_amdgcn_sched_barrier(0);
@@ -517,14 +604,14 @@ struct KvSourceQ : KvStream {
     }
   }
 
-  __device__ __forceinline__ void score(const Group& gr, float (&E)[NT]) const {
+  __device__ __forceinline__ void score(const Group& gr, float (&out)[NT]) const {
     v8i bk[4];
     operands(gr, bk);
-    float part[NT][4];
+    typename E::Acc part[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[t][j] = 0.f;
+      for (int j = 0; j < 4; ++j) part[t][j] = E::zero();
     // Software pipeline over the 4*NT (row, head tile) steps k = 4t + mt: the
     // operands of step k+2 are read from LDS and the MFMAs of step k+1 issued
     // before the epilogue of step k (operands triple-, accumulators
@@ -538,7 +625,7 @@ struct KvSourceQ : KvStream {
     __builtin_amdgcn_sched_barrier(0);
     steps<0>(p, bk, part);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) E[t] = reduce_scatter4(part[t][0], part[t][1], part[t][2], part[t][3], g) * gr.s;
+    for (int t = 0; t < NT; ++t) out[t] = E::finish(part[t][0], part[t][1], part[t][2], part[t][3], g, gr.s);
   }
 };
 
@@ -2330,8 +2417,11 @@ template <int NT>
 constexpr int kFusedWaves = 2;
 
 
+// Logits of a request's rows, stored as float32, or as float16 when out16 is
+// set (rounded to nearest even).
 template <int NT, class Src>
-__device__ __forceinline__ void logits_body(const PagedArgs& a, float* out, int64_t ld, v4i* stage, QLds<NT>* ql) {
+__device__ __forceinline__ void logits_body(const PagedArgs& a, void* out, int64_t ld, int out16, v4i* stage,
+                                            QLds<NT>* ql) {
   Src src;
   src.bind(stage);
   src.bind_q(ql);
@@ -2339,28 +2429,34 @@ __device__ __forceinline__ void logits_body(const PagedArgs& a, float* out, int6
   for_each_segment([&](int b) { return tile_keys<NT>(a, b); }, a.batch, a.locate, a.per_request, kLogitsKeysPerCta, false,
                    [&](int b, int L, int k0, int k1, int) {
     src.init(a, b);
-    float* row0 = out + static_cast<int64_t>(b) * NT * ld;
+    const int64_t off = static_cast<int64_t>(b) * NT * ld;
+    float* row0 = in_global(static_cast<float*>(out)) + off;
+    _Float16* row0h = in_global(static_cast<_Float16*>(out)) + off;
     stream_keys<NT, false>(
         src, k0, k1, L,
         [&](int, int p0, const float(&E)[NT]) {
+          if (out16) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t) row0[t * ld + p0 + lane] = E[t];
+            for (int t = 0; t < NT; ++t) row0h[t * ld + p0 + lane] = static_cast<_Float16>(E[t]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) row0[t * ld + p0 + lane] = E[t];
+          }
         },
         [](int, int) {});
   });
 }
 
-template <int NT>
+template <int NT, int kEpi>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
-logits_kernel(PagedArgs a, float* out, int64_t ld) {
+logits_kernel(PagedArgs a, void* out, int64_t ld, int out16) {
   __shared__ v4i stage[kWaves * kStageInt4];
   global_view(a);
-  out = in_global(out);
   if constexpr (NT >= 3) {
     __shared__ QLds<NT> ql;
-    logits_body<NT, KvSourceQ<NT>>(a, out, ld, stage, &ql);
+    logits_body<NT, KvSourceQ<NT, kEpi>>(a, out, ld, out16, stage, &ql);
   } else {
-    logits_body<NT, KvSource<NT>>(a, out, ld, stage, nullptr);
+    logits_body<NT, KvSource<NT, kEpi>>(a, out, ld, out16, stage, nullptr);
   }
 }
 
@@ -2888,7 +2984,9 @@ void* scratch_address(int dev) {
   return p;
 }
 
-template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT>; };
+template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT, kEpiF32>; };
+template <int NT> struct LogitsAcc16K { static constexpr auto fn = logits_kernel<NT, kEpiAcc16>; };
+template <int NT> struct LogitsF16K { static constexpr auto fn = logits_kernel<NT, kEpiF16>; };
 template <int NT> struct FusedK { static constexpr auto fn = fused_kernel<NT>; };
 template <int NT> struct SelectK { static constexpr auto fn = select_kernel<NT>; };
 
@@ -2919,7 +3017,39 @@ pmqa_status pmqa_mqa_logits(const uint8_t* q, const uint8_t* kv_fused, const flo
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
-  st = launch_k<LogitsK>(next_n, hs, a, out, out_stride);
+  st = launch_k<LogitsK>(next_n, hs, a, static_cast<void*>(out), out_stride, 0);
+  return st != PMQA_OK ? st : launched();
+}
+
+pmqa_status pmqa_mqa_logits_typed(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
+                                  const int32_t* block_tables, int64_t block_table_stride,
+                                  int32_t block_table_width, const int32_t* seq_lens, int64_t seq_lens_stride,
+                                  int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+                                  int32_t block_size, int64_t num_blocks, int32_t max_seq_len, void* out,
+                                  int64_t out_stride, int32_t output_dtype, int32_t epi_dtype, int32_t acc_dtype,
+                                  void* stream) {
+  pmqa_status st = pmqa_check_logits_typed_args(q, kv_fused, weights, block_tables, block_table_stride,
+                                                block_table_width, seq_lens, seq_lens_stride, batch_size, next_n,
+                                                num_heads, head_dim, block_size, num_blocks, max_seq_len, out,
+                                                out_stride, output_dtype, epi_dtype, acc_dtype);
+  if (st != PMQA_OK) return st;
+  if (batch_size > 65535) return PMQA_ERR_SHAPE;
+  const int64_t gx = ceil_div(max_seq_len, kLogitsKeysPerCta);
+  if (batch_size == 0 || gx == 0) return PMQA_OK;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_seq_len, block_tables,
+                        block_table_stride, block_table_width, block_size, num_blocks, nullptr, 0, nullptr);
+  if (st != PMQA_OK) return st;
+  const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
+                                 seq_lens_stride, block_size, batch_size, gx);
+  const int out16 = output_dtype == PMQA_DTYPE_F16 ? 1 : 0;
+  // a float16 epilogue starts from float16 dot products: acc_dtype changes nothing then
+  if (epi_dtype == PMQA_DTYPE_F16)
+    st = launch_k<LogitsF16K>(next_n, hs, a, out, out_stride, out16);
+  else if (acc_dtype == PMQA_DTYPE_F16)
+    st = launch_k<LogitsAcc16K>(next_n, hs, a, out, out_stride, out16);
+  else
+    st = launch_k<LogitsK>(next_n, hs, a, out, out_stride, out16);
   return st != PMQA_OK ? st : launched();
 }
 

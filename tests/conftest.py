@@ -34,7 +34,7 @@ def pytest_terminal_summary(terminalreporter):
     if report.GAP_STATS or report.LINES:
         terminalreporter.write_sep("-", "parity figures")
         for line in report.LINES:
-            terminalreporter.write_line(line)
+            terminalreporter.write_line(str(line))
         if report.GAP_STATS:
             terminalreporter.write_line(
                 "Top-k sets vs the oracle, by the k-th/(k+1)-th gap against tau_r "

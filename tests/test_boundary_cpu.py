@@ -110,6 +110,28 @@ def test_check_logits_args(kw, want):
     assert pm.lib().pmqa_check_logits_args(*logits_args(**kw)) == want
 
 
+F32, F16, BF16 = 0, 1, 2
+TYPED_CASES = [
+    ((F32, F32, F32), {}, OK), ((F16, F16, F16), {}, OK), ((F16, F32, F16), {"out": P(2)}, OK),
+    ((F32, F16, F32), {"out": P(2)}, ALIGN), ((F16, F32, F32), {"out": P(1)}, ALIGN),
+    ((BF16, F32, F32), {}, UNSUP), ((F32, BF16, F32), {}, UNSUP), ((F32, F32, BF16), {}, UNSUP),
+    ((F32, F32, 7), {}, UNSUP), ((-1, F32, F32), {}, UNSUP),
+    ((F16, F32, F32), {"outs": 8000}, STRIDE), ((F16, F16, F32), {"q": None}, NULL),
+    ((BF16, F32, F32), {"B": 0}, UNSUP),  # the precisions are checked before the empty-batch shortcut
+]
+
+
+@pytest.mark.parametrize("dtypes,kw,want", TYPED_CASES)
+def test_check_logits_typed_args(dtypes, kw, want):
+    assert pm.lib().pmqa_check_logits_typed_args(*logits_args(**kw), *dtypes) == want
+
+
+def test_typed_logits_rejects_before_launch():
+    lib = pm.lib()
+    assert lib.pmqa_mqa_logits_typed(*logits_args(), BF16, F32, F32, None) == UNSUP
+    assert lib.pmqa_mqa_logits_typed(*logits_args(B=0), F16, F16, F16, None) == OK
+
+
 SELECT_CASES = [
     ({}, OK),
     ({"arr": None, "rng": None, "topk": None, "ws": None, "wsb": 0}, OK),

@@ -253,6 +253,32 @@ def small_random(seed: int, seq_lens: List[int], next_n: int, block_size: int, t
         threshold_recipe="test", description=f"small random-page workload seed={seed}")
 
 
+def small_f16_exact(seed: int, seq_lens: List[int], next_n: int, block_size: int) -> Workload:
+    """Small random-page workload whose logits are exact in float16 arithmetic
+    in any order: q has at most 4 nonzero entries per head, all q and key
+    entries are -1, 0 or 1, weights are +-0.5 or +-1 and scales 0.5, 1 or 2, so
+    every dot product is an integer of magnitude at most 4, every partial sum a
+    multiple of 0.25 below 2^9 in magnitude."""
+    g = torch.Generator().manual_seed(seed)
+    max_len = max(max(seq_lens), 1)
+    bs = block_size
+    width = int(math.ceil(max_len / bs))
+    bt, nb, page_of = _random_pool(g, seq_lens, bs, width)
+    values = _e4m3_codes(torch.randint(-1, 2, (nb, bs, D), generator=g).float())
+    scales = torch.tensor([0.5, 1.0, 2.0])[torch.randint(0, 3, (nb, bs), generator=g)]
+    _poison_tails(values, scales, seq_lens, page_of, bs, nb - 1)
+    qv = torch.zeros(len(seq_lens), next_n, H, D)
+    pos = torch.randint(0, D, (len(seq_lens), next_n, H, 4), generator=g)
+    qv.scatter_(3, pos, torch.randint(-1, 2, (len(seq_lens), next_n, H, 4), generator=g).float())
+    q = _e4m3_codes(qv)
+    w = torch.tensor([-1.0, -0.5, 0.5, 1.0])[torch.randint(0, 4, (len(seq_lens) * next_n, H), generator=g)]
+    return Workload(
+        name=f"f16exact_s{seed}", q=q.numpy().copy(), kv_fused=_pack_kv_fused(values, scales),
+        weights=w.numpy().astype(np.float32).copy(), block_tables=bt, seq_lens=np.array(seq_lens, dtype=np.int32),
+        max_seq_len=max_len, block_size=bs, next_n=next_n, top_k=1, capacity=1, threshold_recipe="test",
+        description=f"float16-exact small workload seed={seed}")
+
+
 @dataclasses.dataclass
 class PrefillWorkload:
     """Prefill-shaped rows: query tiles of tile_rows rows, each tile on one
