@@ -294,15 +294,77 @@ def bench_logits(args, dev):
     print(json.dumps(line), flush=True)
 
 
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
+
+
+def bench_fp4(args, dev):
+    """--path fp4: pmqa_fp4_mqa_logits on the MXFP4 pool of the workload's
+    shape (decode batch 3 or MTP batch 4), with --dtypes output,epi
+    (default bf16,f32).  HBM-bound: every visible key's 68 bytes (64 value
+    bytes, 4 scale bytes) once per request, q and its scales, weights, and the
+    logits written."""
+    wl = W.fp4_config(int(args.workload))
+    names = args.dtypes.split(",") if args.dtypes != "f32,f32,f32" else ["bf16", "f32"]
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    out_dt, epi_dt = dt[names[0]], dt[names[1]]
+    pairs = int(wl.row_ends().sum())
+    q = torch.from_numpy(wl.q).to(dev)
+    qsf = torch.from_numpy(wl.q_sf).to(dev)
+    w = torch.from_numpy(wl.weights).to(dev)
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    kv_host = torch.from_numpy(wl.kv_fused)
+    kvs = [kv_host.to(dev).view(wl.num_blocks, wl.block_size, 1, 68) for _ in range(args.replicas)]
+    out = torch.empty(wl.rows, pm.padded_seq_len(wl.max_seq_len), dtype=out_dt, device=dev)
+
+    def step(i):
+        pm.fp4_mqa_logits(q, qsf, kvs[i % len(kvs)], w, bt, sl, wl.max_seq_len, out=out, output_dtype=out_dt,
+                          epi_dtype=epi_dt)
+
+    for i in range(args.warmup):
+        step(i)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for j in range(args.steps):
+        step(args.warmup + j)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    out_bytes = 4 if out_dt == torch.float32 else 2
+    alg = (int(wl.seq_lens.astype(np.int64).sum()) * 68 + wl.q.nbytes + wl.q_sf.nbytes + wl.weights.nbytes
+           + pairs * out_bytes)
+    achieved = alg / (ms_step / 1e3) / 1e9
+    flops = 2.0 * 64 * 128 * pairs
+    line = {
+        "metric": "scored (row,KV position) pairs/sec; % roofline (MXFP4 logits)",
+        "value": pairs / (ms_step / 1e3), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"mxfp4 x mxfp4 -> f32 acc, epilogue {names[1]}, out {names[0]}",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "path": "fp4", "dtypes": {"output": names[0], "epi": names[1]},
+                   "pairs": pairs, "rows": wl.rows, "kv_replicas": args.replicas, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": alg,
+                     "kernel": "fp4_logits_kernel<%d>" % wl.next_n, "launch_us": ms_step * 1e3,
+                     "mfma_frac": flops / (ms_step / 1e3) / 1e12 / FP4_PEAK_TFLOPS},
+        "kernel_src_sha": kernel_hash(),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="4", choices=["3", "4", "5", "prefill"])
-    ap.add_argument("--path", default="fused", choices=["fused", "unfused", "logits"])
+    ap.add_argument("--path", default="fused", choices=["fused", "unfused", "logits", "fp4"])
     ap.add_argument("--dtypes", default="f32,f32,f32",
-                    help="--path logits: output,epi,acc precisions, each f32 or f16")
+                    help="--path logits: output,epi,acc precisions, each f32 or f16; --path fp4: output,epi, "
+                         "each f32, f16 or bf16 (default bf16,f32)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -322,6 +384,8 @@ def main():
         return bench_prefill(args, dev)
     if args.path == "logits":
         return bench_logits(args, dev)
+    if args.path == "fp4":
+        return bench_fp4(args, dev)
     args.workload = int(args.workload)
 
     wl = W.make(args.workload)

@@ -7,6 +7,8 @@
  *                               s_p * sum_h w[b*next_n+t, h] * relu(q[b,t,h,:] . k_p)
  *   pmqa_mqa_logits_typed     the same with float16 accumulator, epilogue or
  *                             output options
+ *   pmqa_fp4_mqa_logits       the logits of an MXFP4 pool (E2M1 values, UE8M0
+ *                             scales per 32 elements, no per-token scale)
  *   pmqa_indexer_topk         one-pass threshold select over a logits matrix,
  *                             with last-CTA radix-select repair and Top-k finalize
  *   pmqa_fused_logits_select  both in one pass over the KV pages; no score
@@ -127,7 +129,7 @@ pmqa_status pmqa_mqa_logits(
 typedef enum pmqa_dtype {
   PMQA_DTYPE_F32 = 0,
   PMQA_DTYPE_F16 = 1,
-  PMQA_DTYPE_BF16 = 2 /* named so that it can be refused: no FP8 precision takes it */
+  PMQA_DTYPE_BF16 = 2 /* MXFP4 logits only; no FP8 precision takes it */
 } pmqa_dtype;
 
 /*
@@ -171,6 +173,63 @@ pmqa_status pmqa_mqa_logits_typed(
     int32_t block_size, int64_t num_blocks, int32_t max_seq_len,
     void* out, int64_t out_stride, int32_t output_dtype, int32_t epi_dtype, int32_t acc_dtype,
     void* stream);
+
+/*
+ * pmqa_fp4_mqa_logits -- MXFP4 paged MQA logits (page "flashinfer.attn_scores",
+ * fp4_paged_mqa_logits: the formula, its parameters, the kv_fused figure and
+ * the Restrictions):
+ *
+ *   logits[b*next_n+t, p] = sum_h w[b*next_n+t, h] * relu(q^[b,t,h,:] . k^_p)
+ *
+ * with q^ and k^ the dequantised vectors (each element an E2M1 value times the
+ * UE8M0 scale 2^(e-127) of its group of 32) and no per-token scale.
+ *
+ *   q            [batch_size, next_n, num_heads, head_dim/2] bytes, two E2M1
+ *                values per byte (element 2m in the low nibble of byte m),
+ *                contiguous, 16-byte aligned.
+ *   q_sf         [batch_size, next_n, num_heads] int32, contiguous, 4-byte
+ *                aligned: byte k (k-th least significant) is the UE8M0 scale
+ *                of elements [32k, 32k+32) of that (row, head).
+ *   kv_fused     [num_blocks, block_size*(head_dim/2 + head_dim/32)] bytes,
+ *                16-byte aligned.  Block j: bytes [0, block_size*head_dim/2)
+ *                hold the packed values token-major (token i at i*head_dim/2,
+ *                same nibble rule as q); then block_size slots of 4 UE8M0 scale
+ *                bytes (byte k for elements [32k, 32k+32)): slot i holds token
+ *                i, or with kv_sf_interleaved != 0 slot k holds token
+ *                (k % 4) * (block_size / 4) + k / 4.
+ *   weights, block_tables, seq_lens, max_seq_len: as for pmqa_mqa_logits.
+ *   sf_vec_size  must be 32.
+ *   kv_sf_interleaved  0 or 1; 1 only with block_size 128.
+ *   output_dtype PMQA_DTYPE_BF16 (the page's default), PMQA_DTYPE_F32 or
+ *                PMQA_DTYPE_F16; `out` holds such elements, aligned to one,
+ *                out_stride counts them (as for pmqa_mqa_logits_typed).
+ *   epi_dtype    PMQA_DTYPE_F32, PMQA_DTYPE_F16 or PMQA_DTYPE_BF16: the
+ *                precision of ReLU, the weight multiply and the head sum (each
+ *                dot product, accumulated in float32 by the matrix
+ *                instruction, is rounded to it first; the weights are rounded
+ *                to it; every product and sum is rounded).
+ *
+ * Unsupported values (sf_vec_size != 32, interleaved scales with another block
+ * size, another dtype) return PMQA_ERR_UNSUPPORTED.  Output rows, columns and
+ * the empty-request rule are as for pmqa_mqa_logits.
+ */
+pmqa_status pmqa_check_fp4_logits_args(
+    const uint8_t* q, const int32_t* q_sf, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_seq_len,
+    int32_t sf_vec_size, int32_t kv_sf_interleaved,
+    const void* out, int64_t out_stride, int32_t output_dtype, int32_t epi_dtype);
+
+pmqa_status pmqa_fp4_mqa_logits(
+    const uint8_t* q, const int32_t* q_sf, const uint8_t* kv_fused, const float* weights,
+    const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+    const int32_t* seq_lens, int64_t seq_lens_stride,
+    int32_t batch_size, int32_t next_n, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, int32_t max_seq_len,
+    int32_t sf_vec_size, int32_t kv_sf_interleaved,
+    void* out, int64_t out_stride, int32_t output_dtype, int32_t epi_dtype, void* stream);
 
 /*
  * Select arguments shared by pmqa_indexer_topk and pmqa_fused_logits_select

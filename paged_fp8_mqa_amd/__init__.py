@@ -9,6 +9,9 @@ when the library has not been built; there is no fallback.
 Entry points mirror the C ABI in include/pmqa.h:
   mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None,
              output_dtype=None, epi_dtype=None, acc_dtype=None)
+  fp4_mqa_logits(q, q_sf, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None,
+             output_dtype=None, epi_dtype=None, is_kv_sf_interleaved=False)
+               the MXFP4 pool's logits (bfloat16 output by default)
   indexer_topk(logits, seq_lens, next_n, max_context, thresholds, counters,
                candidates, capacity, top_k, arrivals=None, ranges=None, topk_idx=None,
                workspace=None)
@@ -55,6 +58,8 @@ SIGNATURES = {
     "pmqa_mqa_logits": (_PAGED + [_I32, _P, _I64, _P], ctypes.c_int),
     "pmqa_check_logits_typed_args": (_PAGED + [_I32, _P, _I64, _I32, _I32, _I32], ctypes.c_int),
     "pmqa_mqa_logits_typed": (_PAGED + [_I32, _P, _I64, _I32, _I32, _I32, _P], ctypes.c_int),
+    "pmqa_check_fp4_logits_args": ([_P, _P] + _PAGED[1:] + [_I32, _I32, _I32, _P, _I64, _I32, _I32], ctypes.c_int),
+    "pmqa_fp4_mqa_logits": ([_P, _P] + _PAGED[1:] + [_I32, _I32, _I32, _P, _I64, _I32, _I32, _P], ctypes.c_int),
     "pmqa_check_select_args": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT, ctypes.c_int),
     "pmqa_indexer_topk": ([_P, _I64, _P, _I64, _I32, _I32, _I32] + _SELECT_OUT + [_P], ctypes.c_int),
     "pmqa_check_fused_args": (_PAGED + [_I32] + _SELECT_OUT, ctypes.c_int),
@@ -186,6 +191,44 @@ def mqa_logits(q, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=No
     else:
         _check(lib().pmqa_mqa_logits_typed(*args, int(max_seq_len), _ptr(out), out.stride(0), *codes,
                                            _stream(stream)), "pmqa_mqa_logits_typed")
+    return out[: B * nn, :max_seq_len]
+
+
+def fp4_mqa_logits(q, q_sf, kv_fused, weights, block_tables, seq_lens, max_seq_len, out=None, sf_vec_size=32,
+                   output_dtype=None, epi_dtype=None, is_kv_sf_interleaved=False, block_size=None, stream=None):
+    """MXFP4 paged MQA logits; returns the [B*next_n, max_seq_len] view of `out`.
+
+    q uint8 [B, next_n, H, head_dim/2], q_sf int32 [B, next_n, H], kv_fused
+    uint8 [num_blocks, block_size, 1, head_dim/2 + 4] (or 2-D with block_size);
+    output_dtype torch.bfloat16 (default), float32 or float16; epi_dtype
+    torch.float32 (default), float16 or bfloat16."""
+    import torch
+    B, nn, H, half = q.shape
+    if kv_fused.dim() == 4:
+        bs = kv_fused.shape[1]
+    else:
+        if block_size is None:
+            raise ValueError("block_size is needed for a 2-D kv_fused")
+        bs = block_size
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be 2-D with contiguous rows")
+    for name, t in (("q", q), ("q_sf", q_sf), ("weights", weights), ("kv_fused", kv_fused)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    odt = torch.bfloat16 if output_dtype is None else output_dtype
+    edt = torch.float32 if epi_dtype is None else epi_dtype
+    if out is None:
+        out = torch.empty(B * nn, padded_seq_len(max_seq_len), dtype=odt, device=q.device)
+    if out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    if out.dtype != odt:
+        raise ValueError(f"out is {out.dtype}, output_dtype is {odt}")
+    _check(lib().pmqa_fp4_mqa_logits(_ptr(q), _ptr(q_sf), _ptr(kv_fused), _ptr(weights), _ptr(block_tables),
+                                     block_tables.stride(0), block_tables.shape[1], _ptr(seq_lens),
+                                     seq_lens.stride(0), B, nn, H, 2 * half, bs, kv_fused.shape[0],
+                                     int(max_seq_len), int(sf_vec_size), 1 if is_kv_sf_interleaved else 0,
+                                     _ptr(out), out.stride(0), _dtype_code(odt), _dtype_code(edt),
+                                     _stream(stream)), "pmqa_fp4_mqa_logits")
     return out[: B * nn, :max_seq_len]
 
 

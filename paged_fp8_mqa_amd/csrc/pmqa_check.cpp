@@ -130,6 +130,32 @@ pmqa_status pmqa_check_logits_typed_args(const uint8_t* q, const uint8_t* kv_fus
   return PMQA_OK;
 }
 
+pmqa_status pmqa_check_fp4_logits_args(const uint8_t* q, const int32_t* q_sf, const uint8_t* kv_fused,
+                                       const float* weights, const int32_t* block_tables,
+                                       int64_t block_table_stride, int32_t block_table_width,
+                                       const int32_t* seq_lens, int64_t seq_lens_stride, int32_t batch_size,
+                                       int32_t next_n, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                       int64_t num_blocks, int32_t max_seq_len, int32_t sf_vec_size,
+                                       int32_t kv_sf_interleaved, const void* out, int64_t out_stride,
+                                       int32_t output_dtype, int32_t epi_dtype) {
+  pmqa_status st = check_paged_inputs(q, kv_fused, weights, block_tables, block_table_stride,
+                                      block_table_width, seq_lens, seq_lens_stride, batch_size,
+                                      next_n, num_heads, head_dim, block_size, num_blocks);
+  if (st != PMQA_OK) return st;
+  if (sf_vec_size != 32) return PMQA_ERR_UNSUPPORTED;
+  if (kv_sf_interleaved != 0 && (kv_sf_interleaved != 1 || block_size != 128)) return PMQA_ERR_UNSUPPORTED;
+  for (const int32_t d : {output_dtype, epi_dtype})
+    if (d != PMQA_DTYPE_F32 && d != PMQA_DTYPE_F16 && d != PMQA_DTYPE_BF16) return PMQA_ERR_UNSUPPORTED;
+  if (max_seq_len < 0) return PMQA_ERR_SHAPE;
+  if (batch_size == 0) return PMQA_OK;
+  if (!q_sf || !out) return PMQA_ERR_NULL;
+  if (!aligned(q_sf, 4) || !aligned(out, output_dtype == PMQA_DTYPE_F32 ? 4 : 2)) return PMQA_ERR_ALIGN;
+  if (out_stride < pmqa_padded_seq_len(max_seq_len) || out_stride < 0) return PMQA_ERR_STRIDE;
+  const int64_t rows = static_cast<int64_t>(batch_size) * next_n;
+  if (rows * out_stride >= (int64_t(1) << 31)) return PMQA_ERR_OVERFLOW;
+  return PMQA_OK;
+}
+
 pmqa_status pmqa_check_logits_args(const uint8_t* q, const uint8_t* kv_fused, const float* weights,
                                    const int32_t* block_tables, int64_t block_table_stride,
                                    int32_t block_table_width, const int32_t* seq_lens,

@@ -65,6 +65,10 @@ struct PagedArgs {
   // see keys below row_ends[b*NT + t] of request tile_req[b]
   const int32_t* row_ends;
   const int32_t* tile_req;
+  // MXFP4 pools only: q's UE8M0 scales (one int32 of four per (row, head)) and
+  // whether a block's scale slots are interleaved
+  const int32_t* qsf;
+  int32_t sf_inter;
 };
 
 struct LogitsArgs {
@@ -118,6 +122,7 @@ __device__ __forceinline__ void global_view(PagedArgs& a) {
   a.seq_lens = in_global(a.seq_lens);
   a.row_ends = in_global(a.row_ends);
   a.tile_req = in_global(a.tile_req);
+  a.qsf = in_global(a.qsf);
 }
 __device__ __forceinline__ void global_view(LogitsArgs& a) {
   a.logits = in_global(a.logits);
@@ -465,6 +470,38 @@ struct Epi<kEpiF16> {
   }
 };
 
+// bfloat16 epilogue (the MXFP4 logits): the float32 operations with every
+// result rounded to bfloat16 (nearest even): the dot products, the weights,
+// each fused product-and-sum, each partial of the reduce-scatter, the scale
+// multiply.  A fused result rounded from float32 to bfloat16 is rounded twice.
+constexpr int kEpiBf16 = 3;
+
+__device__ __forceinline__ float round_bf16(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
+
+template <>
+struct Epi<kEpiBf16> {
+  using Acc = float;
+  using W = float4;
+  __device__ static Acc zero() { return 0.f; }
+  __device__ static W weights(float4 w) {
+    return float4{round_bf16(w.x), round_bf16(w.y), round_bf16(w.z), round_bf16(w.w)};
+  }
+  __device__ static Acc head_sum(v4f acc, W w, Acc sum) {
+    sum = round_bf16(__builtin_fmaf(relu(round_bf16(acc[0])), w.x, sum));
+    sum = round_bf16(__builtin_fmaf(relu(round_bf16(acc[1])), w.y, sum));
+    sum = round_bf16(__builtin_fmaf(relu(round_bf16(acc[2])), w.z, sum));
+    return round_bf16(__builtin_fmaf(relu(round_bf16(acc[3])), w.w, sum));
+  }
+  __device__ static float finish(Acc x0, Acc x1, Acc x2, Acc x3, int g, float s) {
+    const bool hi2 = (g & 2) != 0;
+    const float a = round_bf16((hi2 ? x2 : x0) + __shfl_xor(hi2 ? x0 : x2, 32));
+    const float b = round_bf16((hi2 ? x3 : x1) + __shfl_xor(hi2 ? x1 : x3, 32));
+    const bool hi1 = (g & 1) != 0;
+    const float r = round_bf16((hi1 ? b : a) + __shfl_xor(hi1 ? a : b, 16));
+    return round_bf16(r * round_bf16(s));
+  }
+};
+
 // Scores computed from the paged KV pool, the A operands (q) and the lane's 16
 // weights per row held in VGPRs (next_n up to 2, and the repair).
 template <int NT>
@@ -626,6 +663,101 @@ struct KvSourceQ : KvStream {
     steps<0>(p, bk, part);
 #pragma unroll
     for (int t = 0; t < NT; ++t) out[t] = E::finish(part[t][0], part[t][1], part[t][2], part[t][3], g, gr.s);
+  }
+};
+
+// Scores of an MXFP4 pool (page "flashinfer.attn_scores", fp4_paged_mqa_logits:
+// the kv_fused figure, q, q_sf and is_kv_sf_interleaved).  A block holds
+// block_size * 64 bytes of packed E2M1 values (token i's 64 bytes at i * 64,
+// element 2m in the low nibble of byte m) and then block_size * 4 UE8M0 scale
+// bytes, token i's at slot i, or with interleaved slots (block size 128) at
+// slot 4 * (i % 32) + i / 32; byte k of a token's four scales is the scale of
+// elements [32k, 32k + 32).  gfx950's block-scaled MFMA takes exactly that:
+// with FP4 operands, lane l of a 16x16x128 step holds 32 elements (16 bytes)
+// of row / column l % 16, K block l / 16, and one scale byte for them.  So a
+// lane loads its 16 bytes of key p0 + 16j + n straight into the B operand of
+// column tile j (each 1 KB run of 16 keys is one wave-wide load), and its scale
+// byte g of the key's four; no LDS staging.  The matrix instruction applies
+// both sides' scales and accumulates in float32; there is no per-token scale.
+struct KvStreamFp4 : KvStream {
+  struct Group {
+    v4i raw[4];       // column tile j: 16 bytes of key p0 + 16j + n, K block g
+    uint32_t sc[4];   // column tile j: the key's four scale bytes
+    float s;          // (unused: no per-token scale)
+  };
+  int sf_inter;
+
+  __device__ __forceinline__ void bind(v4i*) {}
+  __device__ __forceinline__ void bind_q(void*) {}
+
+  __device__ __forceinline__ void load(Group& gr, const Pages& pg, int p0) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint8_t* page = j < 2 ? pg.a : pg.b;
+      const int slot = (p0 + 16 * j + n) & bs_mask;
+      gr.raw[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(page + slot * 64 + 16 * g));
+      const int ss = sf_inter ? 4 * (slot & 31) + (slot >> 5) : slot;
+      gr.sc[j] = *reinterpret_cast<const uint32_t*>(page + scale_off + 4 * ss);
+    }
+    gr.s = 1.f;
+  }
+  __device__ __forceinline__ void load(Group& gr, int p0, int L) const { load(gr, pages(p0, L), p0); }
+};
+
+// One 16x16x128 FP4 x FP4 -> f32 MFMA with UE8M0 scales sa (A) and sb (B):
+// format code 4 (E2M1) for both operands; only the low 4 dwords of each
+// operand are read.
+__device__ __forceinline__ v4f mfma_fp4(v8i a, v8i b, int sa, int sb) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 4, 0, sa, 0, sb);
+}
+
+template <int NT, int kEpi>
+struct KvSourceFp4 : KvStreamFp4 {
+  using E = Epi<kEpi>;
+  v8i qa[NT][4];              // A operands: row t, head tile mt (low 4 dwords)
+  int qs[NT][4];              // their scale bytes: head 16*mt + n, K block g
+  typename E::W wt[NT][4];    // weights of heads 16*mt + 4*g .. +3
+
+  __device__ __forceinline__ void init(const PagedArgs& a, int b) {
+    init_stream(a, b);
+    sf_inter = a.sf_inter;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = static_cast<int64_t>(b) * NT + t;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int64_t head = row * kHeads + 16 * mt + n;
+        const v4i v = *reinterpret_cast<const v4i*>(a.q + head * (kDim / 2) + 16 * g);
+        qa[t][mt] = v8i{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+        qs[t][mt] = (static_cast<uint32_t>(a.qsf[head]) >> (8 * g)) & 0xff;
+        wt[t][mt] = E::weights(*reinterpret_cast<const float4*>(a.w + row * kHeads + 16 * mt + 4 * g));
+      }
+    }
+  }
+
+  // out[t] = score of key p0 + lane for row t.  Per row, the four head tiles'
+  // MFMAs of a column tile and then their epilogue (a row's accumulators at a
+  // time keep the registers within two waves per SIMD).
+  __device__ __forceinline__ void score(const Group& gr, float (&out)[NT]) const {
+    typename E::Acc part[NT][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v8i bk = v8i{gr.raw[j].x, gr.raw[j].y, gr.raw[j].z, gr.raw[j].w, 0, 0, 0, 0};
+      const int sb = (gr.sc[j] >> (8 * g)) & 0xff;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        v4f acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma_fp4(qa[t][mt], bk, qs[t][mt], sb);
+        typename E::Acc sum = E::zero();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sum = E::head_sum(acc[mt], wt[t][mt], sum);
+        part[t][j] = sum;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) out[t] = E::finish(part[t][0], part[t][1], part[t][2], part[t][3], g, 1.f);
   }
 };
 
@@ -2417,11 +2549,15 @@ template <int NT>
 constexpr int kFusedWaves = 2;
 
 
-// Logits of a request's rows, stored as float32, or as float16 when out16 is
-// set (rounded to nearest even).
-template <int NT, class Src>
-__device__ __forceinline__ void logits_body(const PagedArgs& a, void* out, int64_t ld, int out16, v4i* stage,
-                                            QLds<NT>* ql) {
+// Stored logits element: float32, float16 or bfloat16 (rounded to nearest even).
+constexpr int kOutF32 = 0;
+constexpr int kOutF16 = 1;
+constexpr int kOutBf16 = 2;
+
+// Logits of a request's rows, stored as out_type elements.
+template <int NT, class Src, class Q>
+__device__ __forceinline__ void logits_body(const PagedArgs& a, void* out, int64_t ld, int out_type, v4i* stage,
+                                            Q* ql) {
   Src src;
   src.bind(stage);
   src.bind_q(ql);
@@ -2432,12 +2568,16 @@ __device__ __forceinline__ void logits_body(const PagedArgs& a, void* out, int64
     const int64_t off = static_cast<int64_t>(b) * NT * ld;
     float* row0 = in_global(static_cast<float*>(out)) + off;
     _Float16* row0h = in_global(static_cast<_Float16*>(out)) + off;
+    __bf16* row0b = in_global(static_cast<__bf16*>(out)) + off;
     stream_keys<NT, false>(
         src, k0, k1, L,
         [&](int, int p0, const float(&E)[NT]) {
-          if (out16) {
+          if (out_type == kOutF16) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) row0h[t * ld + p0 + lane] = static_cast<_Float16>(E[t]);
+          } else if (out_type == kOutBf16) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) row0b[t * ld + p0 + lane] = static_cast<__bf16>(E[t]);
           } else {
 #pragma unroll
             for (int t = 0; t < NT; ++t) row0[t * ld + p0 + lane] = E[t];
@@ -2449,15 +2589,23 @@ __device__ __forceinline__ void logits_body(const PagedArgs& a, void* out, int64
 
 template <int NT, int kEpi>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<NT>, 8)))
-logits_kernel(PagedArgs a, void* out, int64_t ld, int out16) {
+logits_kernel(PagedArgs a, void* out, int64_t ld, int out_type) {
   __shared__ v4i stage[kWaves * kStageInt4];
   global_view(a);
   if constexpr (NT >= 3) {
     __shared__ QLds<NT> ql;
-    logits_body<NT, KvSourceQ<NT, kEpi>>(a, out, ld, out16, stage, &ql);
+    logits_body<NT, KvSourceQ<NT, kEpi>>(a, out, ld, out_type, stage, &ql);
   } else {
-    logits_body<NT, KvSource<NT, kEpi>>(a, out, ld, out16, stage, nullptr);
+    logits_body<NT, KvSource<NT, kEpi>>(a, out, ld, out_type, stage, static_cast<QLds<NT>*>(nullptr));
   }
+}
+
+// MXFP4 logits: no LDS (the keys go straight from their loads into the MFMA).
+template <int NT, int kEpi>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+fp4_logits_kernel(PagedArgs a, void* out, int64_t ld, int out_type) {
+  global_view(a);
+  logits_body<NT, KvSourceFp4<NT, kEpi>>(a, out, ld, out_type, nullptr, static_cast<void*>(nullptr));
 }
 
 // A wave's n candidate pairs of row r into slots top_k + base + i, those past
@@ -2814,6 +2962,8 @@ PagedArgs paged_args(const uint8_t* q, const uint8_t* kv, const float* w, const 
   a.scale_off = bs * kDim;
   a.row_ends = nullptr;
   a.tile_req = nullptr;
+  a.qsf = nullptr;
+  a.sf_inter = 0;
   return a;
 }
 
@@ -2987,6 +3137,9 @@ void* scratch_address(int dev) {
 template <int NT> struct LogitsK { static constexpr auto fn = logits_kernel<NT, kEpiF32>; };
 template <int NT> struct LogitsAcc16K { static constexpr auto fn = logits_kernel<NT, kEpiAcc16>; };
 template <int NT> struct LogitsF16K { static constexpr auto fn = logits_kernel<NT, kEpiF16>; };
+template <int NT> struct Fp4K { static constexpr auto fn = fp4_logits_kernel<NT, kEpiF32>; };
+template <int NT> struct Fp4F16K { static constexpr auto fn = fp4_logits_kernel<NT, kEpiF16>; };
+template <int NT> struct Fp4Bf16K { static constexpr auto fn = fp4_logits_kernel<NT, kEpiBf16>; };
 template <int NT> struct FusedK { static constexpr auto fn = fused_kernel<NT>; };
 template <int NT> struct SelectK { static constexpr auto fn = select_kernel<NT>; };
 
@@ -3017,7 +3170,7 @@ pmqa_status pmqa_mqa_logits(const uint8_t* q, const uint8_t* kv_fused, const flo
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
-  st = launch_k<LogitsK>(next_n, hs, a, static_cast<void*>(out), out_stride, 0);
+  st = launch_k<LogitsK>(next_n, hs, a, static_cast<void*>(out), out_stride, kOutF32);
   return st != PMQA_OK ? st : launched();
 }
 
@@ -3042,14 +3195,51 @@ pmqa_status pmqa_mqa_logits_typed(const uint8_t* q, const uint8_t* kv_fused, con
   if (st != PMQA_OK) return st;
   const PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens,
                                  seq_lens_stride, block_size, batch_size, gx);
-  const int out16 = output_dtype == PMQA_DTYPE_F16 ? 1 : 0;
+  const int out_type = output_dtype == PMQA_DTYPE_F16 ? kOutF16 : kOutF32;
   // a float16 epilogue starts from float16 dot products: acc_dtype changes nothing then
   if (epi_dtype == PMQA_DTYPE_F16)
-    st = launch_k<LogitsF16K>(next_n, hs, a, out, out_stride, out16);
+    st = launch_k<LogitsF16K>(next_n, hs, a, out, out_stride, out_type);
   else if (acc_dtype == PMQA_DTYPE_F16)
-    st = launch_k<LogitsAcc16K>(next_n, hs, a, out, out_stride, out16);
+    st = launch_k<LogitsAcc16K>(next_n, hs, a, out, out_stride, out_type);
   else
-    st = launch_k<LogitsK>(next_n, hs, a, out, out_stride, out16);
+    st = launch_k<LogitsK>(next_n, hs, a, out, out_stride, out_type);
+  return st != PMQA_OK ? st : launched();
+}
+
+pmqa_status pmqa_fp4_mqa_logits(const uint8_t* q, const int32_t* q_sf, const uint8_t* kv_fused, const float* weights,
+                                const int32_t* block_tables, int64_t block_table_stride, int32_t block_table_width,
+                                const int32_t* seq_lens, int64_t seq_lens_stride, int32_t batch_size,
+                                int32_t next_n, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                int64_t num_blocks, int32_t max_seq_len, int32_t sf_vec_size,
+                                int32_t kv_sf_interleaved, void* out, int64_t out_stride, int32_t output_dtype,
+                                int32_t epi_dtype, void* stream) {
+  pmqa_status st = pmqa_check_fp4_logits_args(q, q_sf, kv_fused, weights, block_tables, block_table_stride,
+                                              block_table_width, seq_lens, seq_lens_stride, batch_size, next_n,
+                                              num_heads, head_dim, block_size, num_blocks, max_seq_len,
+                                              sf_vec_size, kv_sf_interleaved, out, out_stride, output_dtype,
+                                              epi_dtype);
+  if (st != PMQA_OK) return st;
+  if (batch_size > 65535) return PMQA_ERR_SHAPE;
+  const int64_t gx = ceil_div(max_seq_len, kLogitsKeysPerCta);
+  if (batch_size == 0 || gx == 0) return PMQA_OK;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = validate_content(hs, seq_lens, seq_lens_stride, batch_size, max_seq_len, block_tables,
+                        block_table_stride, block_table_width, block_size, num_blocks, nullptr, 0, nullptr);
+  if (st != PMQA_OK) return st;
+  PagedArgs a = paged_args(q, kv_fused, weights, block_tables, block_table_stride, seq_lens, seq_lens_stride,
+                           block_size, batch_size, gx);
+  a.block_bytes = block_size * (kDim / 2 + kDim / 32);
+  a.scale_off = block_size * (kDim / 2);
+  a.qsf = q_sf;
+  a.sf_inter = kv_sf_interleaved ? 1 : 0;
+  const int out_type =
+      output_dtype == PMQA_DTYPE_F16 ? kOutF16 : (output_dtype == PMQA_DTYPE_BF16 ? kOutBf16 : kOutF32);
+  if (epi_dtype == PMQA_DTYPE_F16)
+    st = launch_k<Fp4F16K>(next_n, hs, a, out, out_stride, out_type);
+  else if (epi_dtype == PMQA_DTYPE_BF16)
+    st = launch_k<Fp4Bf16K>(next_n, hs, a, out, out_stride, out_type);
+  else
+    st = launch_k<Fp4K>(next_n, hs, a, out, out_stride, out_type);
   return st != PMQA_OK ? st : launched();
 }
 

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pmqa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pmqa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -124,6 +124,26 @@ TYPED_CASES = [
 @pytest.mark.parametrize("dtypes,kw,want", TYPED_CASES)
 def test_check_logits_typed_args(dtypes, kw, want):
     assert pm.lib().pmqa_check_logits_typed_args(*logits_args(**kw), *dtypes) == want
+
+
+def fp4_args(qsf=P(), sfv=32, inter=0, out_dt=BF16, epi=F32, **kw):
+    a = logits_args(**kw)
+    # q, q_sf, kv, ... max_seq_len, sf_vec_size, interleaved, out, out_stride, output_dtype, epi_dtype
+    return [a[0], qsf] + a[1:15] + [sfv, inter] + a[15:17] + [out_dt, epi]
+
+
+FP4_CASES = [
+    ({}, OK), ({"out_dt": F32}, OK), ({"out_dt": F16, "epi": BF16}, OK), ({"epi": F16, "out": P(2)}, OK),
+    ({"sfv": 16}, UNSUP), ({"inter": 1}, UNSUP), ({"inter": 1, "bs": 128}, OK), ({"inter": 2, "bs": 128}, UNSUP),
+    ({"out_dt": 3}, UNSUP), ({"epi": -1}, UNSUP), ({"qsf": None}, NULL), ({"qsf": P(2)}, ALIGN),
+    ({"out_dt": F32, "out": P(2)}, ALIGN), ({"out": P(1)}, ALIGN), ({"H": 32}, UNSUP), ({"outs": 8000}, STRIDE),
+    ({"B": 0, "qsf": None, "out": None}, OK),
+]
+
+
+@pytest.mark.parametrize("kw,want", FP4_CASES)
+def test_check_fp4_logits_args(kw, want):
+    assert pm.lib().pmqa_check_fp4_logits_args(*fp4_args(**kw)) == want
 
 
 def test_typed_logits_rejects_before_launch():

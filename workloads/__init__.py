@@ -366,6 +366,106 @@ def prefill_fingerprint(w: PrefillWorkload) -> str:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+# ---------------------------------------------------------------- MXFP4 pools
+
+_E2M1_MAGS = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _mx_quantize(x: torch.Tensor):
+    """Synthetic MXFP4 data from float values x [..., 128]: per group of 32 the
+    scale exponent e = ceil(log2(amax / 6)) (so the group's largest magnitude
+    fits the largest E2M1 value), the UE8M0 byte e + 127, and each element the
+    E2M1 code nearest x / 2^e (the lower magnitude on a tie).  Returns (packed
+    uint8 [..., 64] with element 2m in the low nibble of byte m, scale bytes
+    uint8 [..., 4])."""
+    g = x.reshape(*x.shape[:-1], 4, 32)
+    amax = g.abs().amax(dim=-1).clamp_min(2.0 ** -100)
+    e = torch.ceil(torch.log2(amax / 6.0)).clamp(-127, 127)
+    y = g / torch.pow(2.0, e).unsqueeze(-1)
+    mag = (y.abs().unsqueeze(-1) - _E2M1_MAGS).abs().argmin(dim=-1)
+    codes = (mag | ((y < 0) & (mag > 0)).to(torch.int64) * 8).to(torch.uint8).reshape(x.shape)
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed, (e + 127).to(torch.uint8)
+
+
+@dataclasses.dataclass
+class Fp4Workload:
+    """An MXFP4 paged pool (page "flashinfer.attn_scores", fp4_paged_mqa_logits)."""
+    name: str
+    q: np.ndarray              # uint8 [B, next_n, H, 64]
+    q_sf: np.ndarray           # int32 [B, next_n, H] (byte k: group k's scale)
+    kv_fused: np.ndarray       # uint8 [num_blocks, bs*68]
+    weights: np.ndarray        # float32 [B*next_n, H]
+    block_tables: np.ndarray   # int32 [B, width]
+    seq_lens: np.ndarray       # int32 [B]
+    max_seq_len: int
+    block_size: int
+    next_n: int
+    interleaved: bool
+    description: str
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.next_n
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_fused.shape[0])
+
+    def row_ends(self) -> np.ndarray:
+        L = np.repeat(self.seq_lens.astype(np.int64), self.next_n)
+        t = np.tile(np.arange(self.next_n), self.batch)
+        return np.maximum(0, L - self.next_n + t + 1)
+
+
+def fp4_random(seed: int, seq_lens: List[int], next_n: int, block_size: int, interleaved: bool = False,
+               max_seq_len: Optional[int] = None, key_scale: float = 1.0, name: Optional[str] = None) -> Fp4Workload:
+    """MXFP4 pool over random pages: q and keys are Gaussian (key_scale times
+    randn) quantised per group of 32; weights U[-1, 1].  Every token a request
+    does not own (its last page's tail, the poison page) has NaN scale bytes
+    (255), so an over-read shows as NaN.  With interleaved, each block's scale
+    slots are in the interleaved order (slot k holds token (k % 4) * bs/4 + k / 4)."""
+    g = torch.Generator().manual_seed(seed)
+    bs = block_size
+    max_len = max_seq_len if max_seq_len is not None else max(max(seq_lens), 1)
+    width = int(math.ceil(max_len / bs))
+    bt, nb, page_of = _random_pool(g, seq_lens, bs, width)
+    vals, sf = _mx_quantize(key_scale * torch.randn(nb, bs, D, generator=g))
+    for b, L in enumerate(seq_lens):
+        if L % bs and len(page_of[b]):
+            sf[int(page_of[b][-1]), L % bs:] = 255
+    sf[nb - 1] = 255
+    if interleaved:
+        order = torch.tensor([(k % 4) * (bs // 4) + k // 4 for k in range(bs)])
+        sf = sf[:, order]
+    kv = torch.cat([vals.reshape(nb, -1), sf.reshape(nb, -1)], dim=1).numpy().copy()
+    qv, qs = _mx_quantize(key_scale * torch.randn(len(seq_lens), next_n, H, D, generator=g))
+    w = _uniform(g, (len(seq_lens) * next_n, H), -1.0, 1.0)
+    return Fp4Workload(
+        name=name or f"fp4_s{seed}", q=qv.numpy().copy(), q_sf=qs.contiguous().view(torch.int32).squeeze(-1).numpy().copy(),
+        kv_fused=kv, weights=w.numpy().copy(), block_tables=bt, seq_lens=np.array(seq_lens, dtype=np.int32),
+        max_seq_len=max_len, block_size=bs, next_n=next_n, interleaved=interleaved,
+        description=f"MXFP4 random-page pool seed={seed}, bs={bs}, interleaved scales={interleaved}")
+
+
+def fp4_config(i: int) -> Fp4Workload:
+    """MXFP4 pools of the decode batch (3) and the MTP draft batch (4) shapes:
+    the same batch sizes, next_n, block size and length ranges."""
+    if i == 3:
+        g = torch.Generator().manual_seed(1103)
+        return fp4_random(1103, _randint_inclusive(g, 4096, 32768, 64), 1, 64, max_seq_len=32768,
+                          name="cfg3_decode_b64_mxfp4")
+    if i == 4:
+        g = torch.Generator().manual_seed(1104)
+        return fp4_random(1104, _randint_inclusive(g, 16384, 65536, 32), 4, 64, max_seq_len=65536,
+                          name="cfg4_mtp_b32_n4_mxfp4")
+    raise ValueError(f"no MXFP4 configuration {i}")
+
+
 def make(i: int, **kw) -> Workload:
     return CONFIGS[i](**kw)
 
