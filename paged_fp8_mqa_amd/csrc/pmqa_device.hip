@@ -44,8 +44,11 @@ constexpr int kChunk = kGroupKeys * kWaves * 4;  // keys a CTA scores per chunk
 constexpr int kStageInt4 = 512;  // a wave's KV staging area: 64 keys x 128 bytes
 // Select kernel: a wave's pending candidates and ties per row (smaller for
 // next_n >= 3, whose q operands take LDS instead).
-template <int NT> constexpr int kWaveCand = NT >= 3 ? 64 : 256;
-template <int NT> constexpr int kWaveTie = NT >= 3 ? 32 : 64;
+// Entries of a wave's list per row: candidates from the front, ties and
+// near-band keys from the back; a list is flushed when a group's entries would
+// not fit, so an empty list must hold a whole group's (at most 64).
+template <int NT> constexpr int kWaveList = NT >= 3 ? 96 : 320;
+static_assert(kWaveList<3> >= 64, "a group's entries fit an empty list");
 
 struct PagedArgs {
   const uint8_t* q;
@@ -1012,14 +1015,14 @@ __device__ __forceinline__ Sh<NT> make_sh(char* lds, int fin_cap, int ctl_off) {
   return v;
 }
 
-// Shared memory of a select kernel CTA: each wave's candidate and tie lists,
-// per row, of (key index, stored score bits) pairs not yet written to the
-// row's slots (the finish stage's structures stay out, so that the LDS of two
-// CTAs, with their KV staging areas, fits on a compute unit).
+// Shared memory of a select kernel CTA: each wave's list per row of (key
+// index, stored score bits) pairs not yet written to the row's slots --
+// candidates from the front, ties and near-band keys from the back (the finish
+// stage's structures stay out, so that the LDS of two CTAs, with their KV
+// staging areas, fits on a compute unit).
 template <int NT>
 struct MainShared {
-  int2 cand[kWaves][NT][kWaveCand<NT>];
-  int2 tie[kWaves][NT][kWaveTie<NT>];
+  int2 list[kWaves][NT][kWaveList<NT>];
   int32_t count[kWaves][NT][3];  // the waves' candidates, ties and near-band keys at the end
   int32_t base[NT][3];           // the CTA's bases per row and class
 };
@@ -2711,8 +2714,8 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
       const int bc = __shfl(static_cast<int>(static_cast<uint32_t>(old)), 0);
       const int bt = __shfl(static_cast<int>(static_cast<uint32_t>(old >> 32)), 0);
       const int bn = __shfl(static_cast<int>(nb), 0);
-      store_cands(s, r, bc, ms.cand[w][t], ncl[t]);
-      store_ties(s, r, bt, bn, thr[t], ms.tie[w][t], ntl[t]);
+      store_cands(s, r, bc, ms.list[w][t], ncl[t]);
+      store_ties(s, r, bt, bn, thr[t], ms.list[w][t] + kWaveList<NT> - ntl[t], ntl[t]);
       ncl[t] = 0;
       ntl[t] = 0;
       nnl[t] = 0;
@@ -2736,12 +2739,12 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
             const int nc = __popcll(mc);
             const int nt = __popcll(mt);
             const int nn = mt ? __popcll(__ballot(tie && e < thr[t])) : 0;
-            if (ncl[t] + nc > kWaveCand<NT> || ntl[t] + nt > kWaveTie<NT>) {
+            if (ncl[t] + ntl[t] + nc + nt > kWaveList<NT>) {
               flush(t);
               flushed = true;
             }
-            if (cand) ms.cand[w][t][ncl[t] + lanes_below(mc)] = int2{p, __float_as_int(enc_cand(e, thr[t]))};
-            if (tie) ms.tie[w][t][ntl[t] + lanes_below(mt)] = int2{p, __float_as_int(e - thr[t])};
+            if (cand) ms.list[w][t][ncl[t] + lanes_below(mc)] = int2{p, __float_as_int(enc_cand(e, thr[t]))};
+            if (tie) ms.list[w][t][kWaveList<NT> - 1 - (ntl[t] + lanes_below(mt))] = int2{p, __float_as_int(e - thr[t])};
             ncl[t] += nc;
             ntl[t] += nt;
             nnl[t] += nn;
@@ -2790,8 +2793,8 @@ __device__ __forceinline__ void select_body(const Args& a, const SelectArgs& s, 
         bn += ms.count[q][t][2];
       }
       const int r = b * NT + t;
-      store_cands(s, r, bc, ms.cand[w][t], ncl[t]);
-      store_ties(s, r, bt, bn, thr[t], ms.tie[w][t], ntl[t]);
+      store_cands(s, r, bc, ms.list[w][t], ncl[t]);
+      store_ties(s, r, bt, bn, thr[t], ms.list[w][t] + kWaveList<NT> - ntl[t], ntl[t]);
     }
     PMQA_TR(sh, 2, b, 0);
     if (!s.ws) return;

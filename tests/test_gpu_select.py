@@ -416,3 +416,49 @@ def test_fused_writes_no_scores_when_rows_fit(next_n):
     _check(wl, res, False, scores64=ref, tau=tau)
     tail = ws[nbytes - score_bytes:].cpu().numpy()
     assert np.all(tail == 0xA5), f"{int(np.sum(tail != 0xA5))} score-buffer bytes written"
+
+
+def _duplicated_keys(seed, nn):
+    """Two requests whose keys 128..255 (request 0) and 64..191 (request 1) are
+    copies of one key (values and scale): 64-key groups in which every key
+    scores the same for each row."""
+    wl = W.small_random(seed, [1500, 900], nn, 64, top_k=256, capacity=512)
+    kv = wl.kv_fused.copy()
+    bs, D = wl.block_size, 128
+
+    def tok(b, p):
+        return int(wl.block_tables[b, p // bs]), p % bs
+
+    for b, (src, lo, hi) in enumerate([(127, 128, 256), (63, 64, 192)]):
+        ps, ss = tok(b, src)
+        for p in range(lo, hi):
+            pg, sl = tok(b, p)
+            kv[pg, sl * D:(sl + 1) * D] = kv[ps, ss * D:(ss + 1) * D]
+            kv[pg, bs * D + 4 * sl:bs * D + 4 * sl + 4] = kv[ps, bs * D + 4 * ss:bs * D + 4 * ss + 4]
+    wl.kv_fused = kv
+    return wl, [128, 64]
+
+
+@pytest.mark.parametrize("nn", [1, 3, 4])
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_groups_full_of_near_band_keys(nn, path):
+    """Thresholds just above the duplicated keys' common score put 64 near-band
+    keys of every row in each of their groups, more than half a wave's list: the
+    list is flushed before such a group, and every row still matches the
+    oracle (a tie list of 32 entries for next_n 3 and 4 used to take them and
+    write past its end)."""
+    wl, first = _duplicated_keys(40 + nn, nn)
+    s64 = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
+                                  wl.max_seq_len)
+    tau = oracle.row_tolerance(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size)
+    thr = np.zeros(wl.rows, np.float32)
+    for r in range(wl.rows):
+        S = float(s64[r, first[r // nn]])
+        thr[r] = np.float32(S * (1 + 2.0 ** -10) if S > 0 else S * (1 - 2.0 ** -10))
+    d = dev(wl)
+    if path == "fused":
+        res = run_fused(wl, d, thr)
+    else:
+        _, view = run_logits(wl, d)
+        res = run_select(wl, view, thr)
+    _check(wl, res, True, scores64=s64, tau=tau)
