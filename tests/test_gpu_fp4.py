@@ -145,3 +145,13 @@ def test_rejects_unsupported_arguments():
         pm.fp4_mqa_logits(d["q"], d["qsf"], d["kv"], d["w"], d["bt"], d["sl"], 100, is_kv_sf_interleaved=True)
     with pytest.raises(pm.PmqaError):
         pm.fp4_mqa_logits(d["q"], d["qsf"], d["kv"], d["w"], d["bt"], d["sl"], 100, sf_vec_size=16)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_fp4_bench_shapes_all_rows(cfg):
+    """The MXFP4 pools bench.py times (decode batch and MTP batch shapes), in
+    the page's default precisions: every visible logit of every row against the
+    float64 oracle."""
+    wl = W.fp4_config(cfg)
+    worst = _check(wl, _run(wl, _dev(wl), BF16, F32), BF16, F32)
+    LINES.append(f"{wl.name}: worst |logit err| / tol over all rows = {worst:.3g}")

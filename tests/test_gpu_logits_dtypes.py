@@ -165,3 +165,12 @@ def test_overflow_to_infinity(nn):
     assert float(_run(wl, d, F16, F32, F32)[0, 0]) == float("inf")
     for mode in MODES:
         _check(wl, _run(wl, d, *mode), *mode)
+
+
+@pytest.mark.parametrize("mode", [(F16, F16, F16), (F32, F32, F16)])
+def test_typed_bench_shape_all_rows(mode):
+    """The MTP draft batch (32 requests x 4 rows, up to 65536 keys) through the
+    typed logits: every visible logit of every row within the bound."""
+    wl = W.make(4)
+    worst = _check(wl, _run(wl, dev(wl), *mode), *mode)
+    LINES.append(f"{wl.name} typed {'/'.join(NAME[m] for m in mode)}: worst |err| / tol over all rows = {worst:.3g}")
