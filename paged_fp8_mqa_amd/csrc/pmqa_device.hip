@@ -952,6 +952,15 @@ __device__ __forceinline__ void store_pair(int32_t* slot, int idx, float v) {
 }
 
 
+// A slot's final value, written by the row's last writer in the launch and
+// read by nothing after it in the launch: an ordinary (write-back) store.  No
+// other XCD's L2 holds a dirty copy of the line (every earlier slot store was
+// written through), so the write-back at the end of the kernel cannot be
+// overwritten by a stale one.
+__device__ __forceinline__ void store_final(int32_t* slot, int idx, float v) {
+  *(GlobalU64*)slot = (static_cast<uint64_t>(__float_as_uint(v)) << 32) | static_cast<uint32_t>(idx);
+}
+
 // Control words of a CTA's finish work (fit test, repair items, row outputs).
 template <int NT>
 struct Ctl {
@@ -1962,11 +1971,11 @@ __device__ __forceinline__ void stored_resolve(const SelectArgs& s, int r, int k
     const float e = __int_as_float(p.y);
     const uint32_t key = radix_key(e);
     if (key > kstar) {
-      if (static_cast<int>(og) < cap) store_pair(slots + 2 * (s.top_k + og), p.x, enc_cand(e, t2));
+      if (static_cast<int>(og) < cap) store_final(slots + 2 * (s.top_k + og), p.x, enc_cand(e, t2));
       if (out) out[og] = p.x;
       ++og;
     } else if (key == kstar) {
-      if (static_cast<int>(oe) < s.top_k) store_pair(slots + 2 * (s.top_k - 1 - oe), p.x, e - t2);
+      if (static_cast<int>(oe) < s.top_k) store_final(slots + 2 * (s.top_k - 1 - oe), p.x, e - t2);
       if (out && n_gt + static_cast<int>(oe) < k) out[n_gt + oe] = p.x;
       ++oe;
     }
