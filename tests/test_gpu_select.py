@@ -297,10 +297,11 @@ def test_fused_large_batch_grid():
 
 
 def test_fused_large_batch_fitting_rows():
-    """More rows than the finish kernel has CTAs, thresholds at each row's k-th
-    score: most rows fit (their Top-k from the select kernel's slots, or with a
-    few extra candidates left out), several rows per finish CTA, every row
-    counted through phase A before the waiting CTAs leave."""
+    """1100 requests, more tiles than the launch can place with the located
+    grid (a fixed number of CTAs per request instead), thresholds at each
+    row's k-th score: most rows fit (their Top-k from the main pass's slots, or
+    with a few extra candidates left out), and every row matches the oracle and
+    the select over a logits matrix."""
     rng = np.random.default_rng(8)
     seq = [int(x) for x in rng.integers(0, 1500, size=1100)]
     wl = W.small_random(43, seq, 1, 64, top_k=32, capacity=64)
