@@ -242,3 +242,14 @@ def test_prefill_workspace_is_the_fused_layout():
     need = pm.workspace_bytes("fused", 6, 4, 8000)
     assert pm.lib().pmqa_check_prefill_args(*prefill_args(wsb=need)) == OK
     assert pm.lib().pmqa_check_prefill_args(*prefill_args(wsb=need - 1)) == SHAPE
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """The binding has no fallback: with the library missing every entry point
+    raises instead of computing anything."""
+    monkeypatch.setattr(pm, "LIB_PATH", str(tmp_path / "missing" / "libpmqa.so"))
+    monkeypatch.setattr(pm, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        pm.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        pm.padded_seq_len(8000)

@@ -133,8 +133,9 @@ def test_fused_graph_replays_with_changed_inputs(next_n):
 @pytest.mark.parametrize("next_n", [1, 2])
 @pytest.mark.parametrize("mode", ["inf", "mixed"])
 def test_fused_graph_replays_match_eager(mode, next_n):
-    """next_n = 1: the repair scores its rows again from the KV pages; next_n = 2:
-    the select kernel keeps every score and the repair reads them."""
+    """Every row repaired, or the even rows repaired and the odd ones fitting:
+    the swept rows' repair scores their keys again from the KV pages inside the
+    captured launch, replay after replay."""
     wl = W.small_random(61, [3000, 700, 0, 5000], next_n, 64, top_k=128, capacity=256)
     d = dev(wl)
     ref = oracle.paged_mqa_logits(wl.q, wl.kv_fused, wl.weights, wl.block_tables, wl.seq_lens, wl.block_size,
@@ -168,3 +169,100 @@ def test_fused_graph_replays_match_eager(mode, next_n):
         # the program's own work between replays, on the same workspace
         _call(wl, d, eager)
         _same(wl, want, _host(eager))
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_prefill_graph_replays_match_eager():
+    """pmqa_prefill_select captured once and replayed with new thresholds
+    written into the captured buffer: each replay equals an eager call and
+    passes the oracle's checks."""
+    from test_gpu_prefill import _check as pcheck, _dev as pdev, _oracle as poracle, _thresholds as pthr
+    wl = W.prefill_random(71, [(900, 10), (50, 7)], 4, 64, 64, 128)
+    d = pdev(wl)
+    s64, tau = poracle(wl)
+    ws = pm.make_workspace("fused", wl.tiles, wl.tile_rows, wl.max_context)
+
+    def bufs():
+        R = wl.rows
+        return dict(thr_in=torch.zeros(R, dtype=torch.float32, device="cuda"),
+                    thr=torch.empty(R, dtype=torch.float32, device="cuda"),
+                    counters=torch.zeros(R, 2, dtype=torch.int32, device="cuda"),
+                    cand=torch.full((R, wl.top_k + wl.capacity, 2), SENTINEL_I32, dtype=torch.int32, device="cuda"),
+                    arrivals=torch.zeros(wl.tiles, dtype=torch.int32, device="cuda"),
+                    ranges=torch.zeros(2, R, dtype=torch.int32, device="cuda"),
+                    topk=torch.zeros(R, wl.top_k, dtype=torch.int32, device="cuda"), ws=ws)
+
+    def call(b):
+        b["counters"].zero_()
+        torch.add(b["thr_in"], 0.0, out=b["thr"])
+        pm.prefill_select(d["q"], d["kv"], d["w"], d["bt"], d["treq"], d["re"], wl.tile_rows, wl.max_context,
+                          b["thr"], b["counters"], b["cand"], wl.capacity, wl.top_k, b["arrivals"], b["ranges"],
+                          b["topk"], workspace=b["ws"])
+
+    graphed = bufs()
+    g = _capture(lambda: call(graphed))
+    for seed, mode in [(1, "kth"), (2, "mixed"), (3, "inf")]:
+        thr = pthr(wl, s64, mode, seed)
+        graphed["thr_in"].copy_(torch.from_numpy(thr))
+        graphed["cand"].fill_(SENTINEL_I32)
+        torch.cuda.synchronize()
+        g.replay()
+        got = _host(graphed)
+        eager = bufs()
+        eager["thr_in"].copy_(torch.from_numpy(thr))
+        call(eager)
+        want = _host(eager)
+        assert np.array_equal(want["thr"].view(np.int32), got["thr"].view(np.int32))
+        assert np.array_equal(want["counters"], got["counters"]) and np.array_equal(want["ranges"], got["ranges"])
+        assert np.all(got["arrivals"] == 0)
+        for r in range(wl.rows):
+            assert slot_sets(want, r, wl.top_k, wl.capacity) == slot_sets(got, r, wl.top_k, wl.capacity), r
+            assert sorted(want["topk"][r].tolist()) == sorted(got["topk"][r].tolist()), r
+        got["thr_in"] = thr
+        pcheck(wl, got, s64, tau)
+
+
+@pytest.mark.parametrize("which", ["typed", "fp4"])
+def test_logits_graph_replays_match_eager(which):
+    """The float16-option and the MXFP4 logits captured once and replayed with
+    new seq_lens: each replay equals an eager call, bit for bit."""
+    if which == "typed":
+        wl = W.small_random(72, [3000, 700, 0, 5000], 3, 64, top_k=1, capacity=1)
+        d = dev(wl)
+        kw = dict(output_dtype=torch.float16, epi_dtype=torch.float16, acc_dtype=torch.float32)
+        dt = torch.float16
+        run = lambda sl, out: pm.mqa_logits(d["q"], d["kv"], d["w"], d["bt"], sl, wl.max_seq_len, out=out, **kw)
+    else:
+        wl = W.fp4_random(73, [3000, 700, 0, 5000], 2, 64)
+        d = {"q": torch.from_numpy(wl.q).cuda(), "qsf": torch.from_numpy(wl.q_sf).cuda(),
+             "kv": torch.from_numpy(wl.kv_fused).cuda().view(wl.num_blocks, wl.block_size, 1, 68),
+             "w": torch.from_numpy(wl.weights).cuda(), "bt": torch.from_numpy(wl.block_tables).cuda()}
+        dt = torch.bfloat16
+        run = lambda sl, out: pm.fp4_mqa_logits(d["q"], d["qsf"], d["kv"], d["w"], d["bt"], sl, wl.max_seq_len,
+                                                out=out)
+    cols = pm.padded_seq_len(wl.max_seq_len)
+    sl_g = torch.from_numpy(wl.seq_lens.copy()).cuda()
+    out_g = torch.zeros(wl.rows, cols, dtype=dt, device="cuda")
+    g = _capture(lambda: run(sl_g, out_g))
+    for lens in ([3000, 700, 0, 5000], [2500, 1, 0, 4990], [64, 700, 0, 100]):
+        lens = np.array(lens, np.int32)
+        sl_g.copy_(torch.from_numpy(lens))
+        out_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = torch.zeros_like(out_g)
+        run(torch.from_numpy(lens).cuda(), eager)
+        torch.cuda.synchronize()
+        ends = oracle.row_ends(lens, wl.next_n)
+        for r, e in enumerate(ends):
+            assert torch.equal(out_g[r, :e].view(torch.int16), eager[r, :e].view(torch.int16)), (which, r)
