@@ -1680,7 +1680,7 @@ struct Ws {
   }
 };
 
-// Items of a stage of a request of L keys: kRescoreItemKeys keys when the
+// Items of a stage of a request of L keys: rescore_item_keys(L) keys when the
 // scores are computed from the KV pages (stage 1 of the fused repair), else
 // kSelectItemKeys keys read back from a score row; one per row in stage 6.
 // Keys of a repair item over stored scores (fewer for next_n >= 3, whose
@@ -1688,10 +1688,21 @@ struct Ws {
 template <int NT>
 constexpr int kItemKeys = NT >= 3 ? kSelectItemKeys / 2 : kSelectItemKeys;
 
+// Keys of a stage-1 item of a request of L keys: the request in about
+// kRescoreItems items of a multiple of kRescoreItemKeys keys, at most 32768
+// (the items' packed 16-bit histogram counts).  Every item has fixed costs --
+// its claim and completion round trips and its histogram's flush into the
+// row's -- so long requests take long items; short ones still spread over
+// several CTAs.
+__device__ __forceinline__ int rescore_item_keys(int L) {
+  const int per = static_cast<int>(ceil_div(ceil_div(L, kRescoreItems), kRescoreItemKeys)) * kRescoreItemKeys;
+  return min(max(per, kRescoreItemKeys), 32768);
+}
+
 template <int NT, bool kFused>
 __device__ __forceinline__ int stage_items(int stage, int L) {
   if (stage == kStageRows) return NT;
-  const int keys = (kFused && stage == kStageHist0) ? kRescoreItemKeys : kItemKeys<NT>;
+  const int keys = (kFused && stage == kStageHist0) ? rescore_item_keys(L) : kItemKeys<NT>;
   return max(1, static_cast<int>(ceil_div(L, keys)));
 }
 
@@ -2061,8 +2072,8 @@ __device__ __forceinline__ void item_done(const SelectArgs& s, const Ws& ws, int
 
 // LDS areas a re-scoring item uses beside the finish view: the KV staging
 // area, the q operands (next_n >= 3) and NT packed first-pass histograms
-// (1024 bins as 512 words of two 16-bit counts: an item has at most
-// kRescoreItemKeys < 65536 keys per row).
+// (1024 bins as 512 words of two 16-bit counts: an item has at most 32768
+// keys per row).
 template <int NT>
 struct RescoreLds {
   v4i* stage;
@@ -2085,8 +2096,8 @@ __device__ __forceinline__ void rescore_item(const PagedArgs& a, const SelectArg
   for (int i = tid; i < NT * kWords; i += kThreads) rl.ph[i] = 0u;
   __syncthreads();
   float* rows = s.scores + static_cast<int64_t>(b) * NT * s.score_ld;
-  const int c0 = idx * kRescoreItemKeys;
-  const int c1 = min(c0 + kRescoreItemKeys, L);
+  const int c0 = idx * rescore_item_keys(L);
+  const int c1 = min(c0 + rescore_item_keys(L), L);
   auto add = [&](int t, int p, float e) {
     st_wt(reinterpret_cast<uint32_t*>(rows + t * s.score_ld + p), __float_as_uint(e));
     const uint32_t bin = radix_key(e) >> shift;

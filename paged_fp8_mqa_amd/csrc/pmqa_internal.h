@@ -23,7 +23,8 @@ constexpr int kNearPairs = 4096;        // repair workspace: a row's keys just b
 constexpr uint32_t kNearBand = 1u << 15;  // the band below a threshold, in radix-key units (about 2^-8 of it)
 constexpr int kJobWords = 16;           // repair workspace: words per tile job
 constexpr int kRowWords = 16;           // repair workspace: words per row state
-constexpr int kRescoreItemKeys = 2048;  // keys per repair item recomputed from the KV pages
+constexpr int kRescoreItemKeys = 2048;  // granule of the keys per repair item recomputed from the KV pages
+constexpr int kRescoreItems = 16;       // repair items a request's keys are recomputed in (about)
 constexpr int kSelectItemKeys = 4096;   // keys per repair item read back as scores
 
 constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
