@@ -585,11 +585,15 @@ struct QLds {
 // Scores computed from the paged KV pool with the A operands (q) and weights
 // read from LDS per head tile (next_n of 3 and 4): holding 32 VGPRs of q and
 // 16 of weights per row left those variants one wave per SIMD; from LDS they
-// fit two.  Same operation order as KvSource, so the same bits.
-template <int NT, int kEpi = kEpiF32>
+// fit two.  The first kRegRows rows keep their q in VGPRs all the same (only
+// their weights are read from LDS): every 64-key group reads each LDS row's q
+// (8 KB a wave) again, and those reads bound the loop.  Same operation order
+// as KvSource, so the same bits.
+template <int NT, int kEpi = kEpiF32, int kRegRows = 0>
 struct KvSourceQ : KvStream {
   using E = Epi<kEpi>;
   QLds<NT>* ql;
+  v8i qr[kRegRows > 0 ? kRegRows : 1][4];  // A operands of rows t < kRegRows
 
   __device__ __forceinline__ void bind_q(QLds<NT>* q_area) { ql = q_area; }
 
@@ -608,6 +612,12 @@ struct KvSourceQ : KvStream {
       const int t = e >> 4, head4 = e & 15;  // heads 4*head4 .. +3
       (&ql->w[0][0][0])[e] = *reinterpret_cast<const float4*>(a.w + (static_cast<int64_t>(b) * NT + t) * kHeads + 4 * head4);
     }
+#pragma unroll
+    for (int t = 0; t < kRegRows; ++t) {
+      const int64_t row = static_cast<int64_t>(b) * NT + t;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) qr[t][mt] = load32(a.q + ((row * kHeads + 16 * mt + n) * kDim + 32 * g));
+    }
     __syncthreads();
   }
 
@@ -619,15 +629,21 @@ struct KvSourceQ : KvStream {
   template <int k>
   __device__ __forceinline__ void ld(Pipe& p) const {
     constexpr int t = k >> 2, mt = k & 3;
-    const v4i lo = ql->q[t][mt][0][lane];
-    const v4i hi = ql->q[t][mt][1][lane];
-    p.qa[k % 3] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    if constexpr (t >= kRegRows) {
+      const v4i lo = ql->q[t][mt][0][lane];
+      const v4i hi = ql->q[t][mt][1][lane];
+      p.qa[k % 3] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
     p.wv[k % 3] = ql->w[t][mt][g];
   }
   template <int k>
   __device__ __forceinline__ void mm(Pipe& p, const v8i (&bk)[4]) const {
+    constexpr int t = k >> 2, mt = k & 3;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p.acc[k & 1][j] = mfma_fp8(p.qa[k % 3], bk[j]);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (t < kRegRows) p.acc[k & 1][j] = mfma_fp8(qr[t < kRegRows ? t : 0][mt], bk[j]);
+      else p.acc[k & 1][j] = mfma_fp8(p.qa[k % 3], bk[j]);
+    }
   }
   template <int k>
   __device__ __forceinline__ void steps(Pipe& p, const v8i (&bk)[4], typename E::Acc (&part)[NT][4]) const {
@@ -2874,7 +2890,9 @@ fused_kernel(PagedArgs a, SelectArgs s) {
   global_view(a);
   global_view(s);
   if constexpr (NT >= 3)
-    select_body<NT, true, kFusedKeysPerCta, KvSourceQ<NT>>(a, s, lds);
+    // (row 0's q in VGPRs: 2.3 us faster per call on the MTP batch than none,
+    // two rows no faster again; the kernel stays within two waves per SIMD)
+    select_body<NT, true, kFusedKeysPerCta, KvSourceQ<NT, kEpiF32, 1>>(a, s, lds);
   else
     select_body<NT, true, kFusedKeysPerCta, KvSource<NT>>(a, s, lds);
 #ifdef PMQA_TRACE
