@@ -242,6 +242,20 @@ def _same(wl, a, b, capacity=None):
             assert ta == tb, f"row {r}: tie slots differ"
 
 
+def test_swept_rows_of_a_very_long_request():
+    """A 600000-key request beside a short one, next_n 2, every row swept
+    (threshold +inf): the long rows are scored again in repair items of the
+    largest size (32768 keys, the limit of an item's packed 16-bit histogram
+    counts); every row against the float64 oracle."""
+    wl = W.small_random(81, [600000, 3000], 2, 64, top_k=2048, capacity=4096)
+    d = dev(wl)
+    ref, tau = _oracle_rows(wl, None)
+    ends = oracle.row_ends(wl.seq_lens, wl.next_n)
+    thr = _sigma_thresholds(ref, ends, wl.top_k, "inf")
+    res = run_fused(wl, d, thr)
+    _check(wl, res, True, scores64=ref, tau=tau)
+
+
 @pytest.mark.parametrize("cfg", [3, 4, 5])
 def test_fused_large_configs(cfg):
     """Every row of the large workloads against the float64 oracle (contract,
