@@ -170,7 +170,7 @@ def check_topk_against_slots(r, topk_row, cands, dec_c, ties, k, top_k, n_cand):
 
 
 def check_set_rule(r, got, s64, k, tau):
-    """North-star set rule: the set has k members, holds every p with
+    """Top-k set rule of the parity contract: the set has k members, holds every p with
     sigma_p > sigma_k + 2 tau and only p with sigma_p >= sigma_k - 2 tau
     (2 tau: each GPU score may be off by tau).  Exact when the k-th/(k+1)-th
     gap exceeds 2 tau."""
@@ -192,7 +192,7 @@ def check_set_rule(r, got, s64, k, tau):
 def gap_stats(stats, got, s64, k, tau):
     """Counts, per row, where the k-th/(k+1)-th gap lies against tau, and how
     often the set is the exact sort prefix in each band: "gap>2tau" (the sound
-    form of the north-star rule; must be exact), "tau<gap<=2tau" (the literal
+    form of the set rule; must be exact), "tau<gap<=2tau" (the literal
     form: exact unless the GPU's own rounding swapped the two), "gap<=tau"
     (tie membership only), "all" (k = row length: every key)."""
     if k >= s64.size:
@@ -210,7 +210,7 @@ def gap_stats(stats, got, s64, k, tau):
 
 def exact_set_when_gapped(got, s64, k, tau):
     """True when the k-th/(k+1)-th gap exceeds 2 tau and the set is then the exact
-    sort prefix (the strict form of the spec rule)."""
+    sort prefix (the strict form of the set rule)."""
     srt = np.sort(s64)[::-1]
     if k >= s64.size or srt[k - 1] - srt[k] <= 2 * tau:
         return None

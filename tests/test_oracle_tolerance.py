@@ -2,7 +2,7 @@
 
 The bound on a GPU logit's error is 1e-4 * sum_h |w_h| * max_h |q_h . k| per
 row; the per-token scale multiplies every term of a score, so it enters the
-scale (reading of the tolerance in the benchmark spec, with s_p).  Each case below
+scale (this reading of the tolerance includes s_p).  Each case below
 is computed by hand from that rule on inputs where the dots are closed forms
 (all-ones or constant e4m3 vectors), and each is chosen so that one plausible
 mistake in the formula gives another value:
