@@ -259,6 +259,19 @@ __device__ __forceinline__ uint64_t add_ag64(uint64_t* p, uint64_t v) {
   return __hip_atomic_fetch_add((GlobalU64*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A uniform word read by a returning agent-scope atomic (an add of a zero the
+// compiler cannot see, so that it stays an atomic; lane 0 of the wave, every
+// lane active, the value broadcast): performed where the device's atomics
+// are, it returns the word's current value whatever copy of its line a cache
+// may hold.  Slower than an agent-scope load, so kept off the usual paths.
+__device__ __forceinline__ uint32_t rd_cur_wave(const uint32_t* p) {
+  uint32_t z = 0u;
+  asm volatile("" : "+v"(z));
+  uint32_t v = 0u;
+  if ((threadIdx.x & 63) == 0) v = add_ag(const_cast<uint32_t*>(p), z);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const int4 lo = *reinterpret_cast<const int4*>(p);
   const int4 hi = *reinterpret_cast<const int4*>(p + 16);
@@ -2030,9 +2043,18 @@ __device__ __forceinline__ void stored_resolve(const SelectArgs& s, int r, int k
 template <int NT>
 __device__ __forceinline__ void unswept_row(const SelectArgs& s, int r, int k, int nc, int nt, int nn, float th,
                                             bool stored, const Sh<NT>& sh) {
-  if (threadIdx.x == 0 && s.nearc) st_wt(s.nearc + static_cast<int64_t>(r) * kRowWords, 0u);
+  if (stored && nc < k && nc + nt + nn < k) {
+    // A stored row's fit test counted at least k kept pairs, so counts short of
+    // k were not the final ones: they are read again as the words' current
+    // values (the near-band count is cleared only after the select, whose last
+    // barrier every wave passes after these reads).
+    nc = static_cast<int>(rd_cur_wave(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r));
+    nt = static_cast<int>(rd_cur_wave(reinterpret_cast<const uint32_t*>(s.counters) + 2 * r + 1));
+    nn = s.nearc ? static_cast<int>(rd_cur_wave(s.nearc + static_cast<int64_t>(r) * kRowWords)) : 0;
+  }
   if (stored) stored_resolve<NT>(s, r, k, nc, nt, nn, th, sh);
   else fit_row_outputs<NT>(s, r, k, nc, nt, th, true, sh);
+  if (threadIdx.x == 0 && s.nearc) st_wt(s.nearc + static_cast<int64_t>(r) * kRowWords, 0u);
 }
 
 // Stage-6 item t of tile b's job: row t given its ranges and Top-k -- a swept
